@@ -1,0 +1,401 @@
+"""Pins for the CPU oracle, independent of the oracle's own arithmetic.
+
+Each test checks the oracle against something the pages or mathematics fix:
+hand-derived vectors (tests/golden/hand_vectors.json), exact rational
+arithmetic (fractions.Fraction), closed forms, invariants, and library
+routines the oracle does not call (numpy's int64 matmul).  None of these tests
+needs a GPU.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from ternary_weight_linear_forward_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_vectors.json")
+with open(GOLDEN) as f:
+    HV = json.load(f)
+
+
+def f32(x):
+    return np.float32(x)
+
+
+def nearest_f32_check(g: np.float32, exact: Fraction):
+    """g must be the binary32 nearest to 'exact', ties to an even mantissa."""
+    g = np.float32(g)
+    lo = np.nextafter(g, np.float32(-np.inf))
+    hi = np.nextafter(g, np.float32(np.inf))
+    d = abs(Fraction(float(g)) - exact)
+    for nb in (lo, hi):
+        if not np.isfinite(nb):
+            continue
+        dn = abs(Fraction(float(nb)) - exact)
+        assert d <= dn, (g, nb, float(exact))
+        if d == dn:  # a tie: g must carry the even mantissa
+            assert (int(np.array(g).view(np.uint32)) & 1) == 0
+
+
+# --------------------------------------------------------------------------
+# gamma = mean|W|
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(6))
+def test_gamma_is_exact_mean_correctly_rounded(seed):
+    r = synth.rng(seed)
+    n = int(r.integers(1, 300))
+    # mix of magnitudes, including subnormals and wide exponent spread
+    w = (r.standard_normal(n) * np.exp2(r.integers(-140, 60, n))).astype(np.float32)
+    if seed % 2:
+        w[: n // 3] = (r.standard_normal(n // 3) * 1e-44).astype(np.float32)
+    g = oracle.absmean(w)
+    exact = sum(Fraction(float(abs(v))) for v in w) / n
+    nearest_f32_check(g, exact)
+
+
+def test_gamma_tie_to_even_is_exercised():
+    # mean of {1, 1 + 2^-23 * 1} ... build a set whose exact mean is a binary32 midpoint
+    a = f32(1.0)
+    b = np.nextafter(a, f32(2.0))  # 1 + 2^-23
+    # mean(a, b) = 1 + 2^-24: midway between a (even) and b (odd) -> a
+    assert oracle.absmean(np.array([a, b], np.float32)) == a
+    c = np.nextafter(b, f32(2.0))  # 1 + 2^-22 (even mantissa)
+    # mean(b, c) = 1 + 3 * 2^-24: midway between b (odd) and c (even) -> c
+    assert oracle.absmean(np.array([b, c], np.float32)) == c
+
+
+@pytest.mark.parametrize("c", [0.02, 1.0, 3.5e-42, 6.0e37, 0.0])
+def test_gamma_constant_magnitude(c):
+    r = synth.rng(7)
+    w = (np.where(r.random(1000) < 0.5, -1, 1) * f32(c)).astype(np.float32)
+    assert oracle.absmean(w) == f32(c)
+
+
+def test_gamma_permutation_and_power_of_two_scaling():
+    w = synth.latent_weights(64, 96, seed=11)
+    g = oracle.absmean(w)
+    perm = synth.rng(12).permutation(w.size)
+    assert oracle.absmean(w.reshape(-1)[perm]) == g
+    for k in (-20, -3, 1, 7, 30):
+        assert oracle.absmean((w * np.float32(2.0 ** k)).astype(np.float32)) == np.float32(g * 2.0 ** k)
+
+
+def test_gamma_matches_fsum_in_practice():
+    w = synth.latent_weights(200, 300, seed=13)
+    g = oracle.absmean(w)
+    ref = np.float32(math.fsum(float(abs(v)) for v in w.reshape(-1)) / w.size)
+    assert abs(int(np.array(g).view(np.int32)) - int(np.array(ref).view(np.int32))) <= 1
+
+
+def test_gamma_statistics_gaussian():
+    n = 1 << 20
+    w = synth.latent_weights(1024, 1024, seed=14)
+    g = float(oracle.absmean(w))
+    mu = 0.02 * math.sqrt(2 / math.pi)
+    sd = 0.02 * math.sqrt(1 - 2 / math.pi) / math.sqrt(n)
+    assert abs(g - mu) < 5 * sd
+
+
+def test_gamma_rejects_nonfinite():
+    with pytest.raises(oracle.OracleError):
+        oracle.absmean(np.array([1.0, np.inf], np.float32))
+    with pytest.raises(oracle.OracleError):
+        oracle.absmean(np.array([np.nan], np.float32))
+
+
+# --------------------------------------------------------------------------
+# ternarisation
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("key", ["absmean_tie", "absmean_integers", "absmean_mixed"])
+def test_ternarize_hand_vectors(key):
+    v = HV[key]
+    w = np.array(v["W"], np.float32)
+    t, g = oracle.quantize_weights(w)
+    assert g == np.float32(v["gamma"])
+    assert t.tolist() == v["T"]
+
+
+def test_ternarize_invariants():
+    w = synth.latent_weights(128, 256, seed=21)
+    t, g = oracle.quantize_weights(w)
+    assert set(np.unique(t).tolist()) <= {-1, 0, 1}
+    # odd symmetry and scale invariance
+    t_neg, g_neg = oracle.quantize_weights(-w)
+    assert g_neg == g and np.array_equal(t_neg, -t)
+    for k in (-5, 3):
+        t_s, _ = oracle.quantize_weights((w * np.float32(2.0 ** k)).astype(np.float32))
+        assert np.array_equal(t_s, t)
+    # sign agreement and monotonicity in |w|
+    nz = t != 0
+    assert np.all(np.sign(w[nz]) == t[nz])
+    order = np.argsort(np.abs(w).reshape(-1), kind="stable")
+    mags = np.abs(t.reshape(-1)[order])
+    assert np.all(np.diff(mags.astype(np.int16)) >= 0)
+
+
+def test_ternarize_threshold_is_exact_half():
+    # |w|/gamma just above / at / below 0.5 in binary32
+    g = np.float32(1.0)
+    half = np.float32(0.5)
+    above = np.nextafter(half, np.float32(1))
+    below = np.nextafter(half, np.float32(0))
+    w = np.array([half, above, below, -above, -half], np.float32)
+    t = oracle.ternarize(w, g)
+    assert t.tolist() == [0, 1, 0, -1, 0]
+
+
+def test_ternarize_zero_gamma():
+    w = np.zeros(10, np.float32)
+    t, g = oracle.quantize_weights(w)
+    assert g == 0 and not t.any()
+
+
+def test_ternarize_zero_fraction_closed_form():
+    # For Gaussian W, T = 0 iff |w| <= gamma/2 with gamma -> sigma*sqrt(2/pi):
+    # P = erf(1 / (2*sqrt(pi))) = 0.31006.
+    p = math.erf(1 / (2 * math.sqrt(math.pi)))
+    assert abs(p - 0.31006) < 1e-5
+    for shape, seed in (((512, 256), 0), ((2048, 2048), 1)):
+        w = synth.latent_weights(*shape, seed=31 + seed)
+        t, _ = oracle.quantize_weights(w)
+        frac = float((t == 0).mean())
+        sd = math.sqrt(p * (1 - p) / t.size)
+        assert abs(frac - p) < 5 * sd + 2e-4, frac
+
+
+# --------------------------------------------------------------------------
+# packing
+# --------------------------------------------------------------------------
+def test_pack_i2_hand_word():
+    v = HV["pack_i2_word"]
+    t = np.array([v["T"]], np.int8)
+    p = oracle.pack(t, oracle.LAYOUT_I2)
+    assert p.size == 256  # one tile of 16 rows x one 64-weight block x 16 bytes
+    words = p[:16].view("<u4")
+    assert [hex(int(x)) for x in words] == v["chunk_words_hex"]
+    # padding rows 1..15 of the tile: T = 0 everywhere -> 0x55 bytes
+    assert np.all(p[16:] == 0x55)
+
+
+def test_pack_b3_hand_bytes():
+    v = HV["pack_b3_bytes"]
+    for grp, want in zip(v["groups"], v["bytes"]):
+        t = np.array([grp], np.int8)
+        p = oracle.pack(t, oracle.LAYOUT_B3)
+        assert p[0] == want
+        assert np.all(p[1:16] == 121) and np.all(p[16:] == 121)
+
+
+def test_pack_b3_bijection_over_all_groups():
+    groups = np.array(np.meshgrid(*[[-1, 0, 1]] * 5, indexing="ij")).reshape(5, -1).T.astype(np.int8)
+    assert groups.shape == (243, 5)
+    t = groups.reshape(1, -1)  # one row of 1215 weights = 243 groups of 5
+    p = oracle.pack(t, oracle.LAYOUT_B3)
+    KB = (t.shape[1] + 79) // 80
+    codes = []
+    for kb in range(KB):
+        codes.extend(p[kb * 256: kb * 256 + 16].tolist())
+    codes = codes[:243]
+    assert sorted(codes) == list(range(243))
+    # first trit most significant: decode by plain base-3 expansion
+    for g, b in zip(groups, codes):
+        digits = [(b // 3 ** (4 - i)) % 3 - 1 for i in range(5)]
+        assert digits == g.tolist()
+
+
+@pytest.mark.parametrize("layout", [oracle.LAYOUT_I2, oracle.LAYOUT_B3])
+@pytest.mark.parametrize("N,K", [(1, 1), (16, 64), (17, 65), (33, 80), (5, 161), (48, 257)])
+def test_pack_round_trip(layout, N, K):
+    t = synth.ternary_weights(N, K, seed=N * 1000 + K)
+    p = oracle.pack(t, layout)
+    assert np.array_equal(oracle.unpack(p, N, K, layout), t)
+
+
+def test_packed_sizes():
+    assert oracle.packed_bytes(8192, 8192, oracle.LAYOUT_I2) == 8192 * 8192 // 4
+    assert oracle.packed_bytes(3200, 3200, oracle.LAYOUT_I2) == 3200 * 3200 // 4
+    assert oracle.packed_bytes(28672, 8192, oracle.LAYOUT_B3) == 28672 * 103 * 16  # ceil(8192/80) = 103
+    assert oracle.packed_bytes(1, 1, oracle.LAYOUT_I2) == 256
+    assert oracle.packed_bytes(17, 65, oracle.LAYOUT_I2) == 2 * 2 * 256
+
+
+def test_pack_single_weight_position():
+    # one +1 at (n, k) in a zero matrix changes exactly one 2-bit field, the one
+    # named by the layout: chunk ((n/16)*KB + k/64)*256 + (n%16)*16, byte 4*d + j,
+    # bit pair s where k%64 = 16d + 4s + j.
+    N, K = 40, 200
+    KB = (K + 63) // 64
+    zero = oracle.pack(np.zeros((N, K), np.int8), oracle.LAYOUT_I2)
+    for n, k in ((0, 0), (17, 63), (39, 199), (20, 130)):
+        t = np.zeros((N, K), np.int8)
+        t[n, k] = 1
+        p = oracle.pack(t, oracle.LAYOUT_I2)
+        diff = np.nonzero(p != zero)[0]
+        r = k % 64
+        d, s, j = r // 16, (r % 16) // 4, r % 4
+        byte = ((n // 16) * KB + k // 64) * 256 + (n % 16) * 16 + 4 * d + j
+        assert diff.tolist() == [byte]
+        assert (int(p[byte]) >> (2 * s)) & 3 == 2
+
+
+def test_unpack_rejects_unused_code():
+    p = oracle.pack(np.zeros((1, 4), np.int8), oracle.LAYOUT_I2)
+    p[0] = 0xFF
+    with pytest.raises(oracle.OracleError):
+        oracle.unpack(p, 1, 4, oracle.LAYOUT_I2)
+    p = oracle.pack(np.zeros((1, 4), np.int8), oracle.LAYOUT_B3)
+    p[0] = 243
+    with pytest.raises(oracle.OracleError):
+        oracle.unpack(p, 1, 4, oracle.LAYOUT_B3)
+
+
+# --------------------------------------------------------------------------
+# activation quantisation
+# --------------------------------------------------------------------------
+def test_act_quant_hand_vector():
+    v = HV["act_quant_ties"]
+    q, beta = oracle.quantize_act(np.array([v["x"]], np.float32))
+    assert beta[0] == np.float32(v["beta"])
+    assert q[0].tolist() == v["q"]
+
+
+def test_act_quant_invariants():
+    x = synth.activations_f32(32, 500, seed=41)
+    x[3] = 0.0
+    q, beta = oracle.quantize_act(x)
+    assert np.abs(q.astype(np.int16)).max() <= 127
+    assert beta[3] == 0 and not q[3].any()
+    for m in range(32):
+        if beta[m] > 0:
+            i = int(np.argmax(np.abs(x[m])))
+            assert abs(int(q[m, i])) == 127
+            assert beta[m] == np.abs(x[m]).max()
+    qn, bn = oracle.quantize_act(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(bn, beta)
+    for k in (-10, 4):
+        qs, bs = oracle.quantize_act((x * np.float32(2.0 ** k)).astype(np.float32))
+        assert np.array_equal(qs, q)
+        assert np.array_equal(bs, (beta * np.float32(2.0 ** k)).astype(np.float32))
+
+
+def test_act_quant_bf16_input_is_widened_exactly():
+    xb = synth.activations_bf16(4, 64, seed=42)
+    q1, b1 = oracle.quantize_act(xb)
+    q2, b2 = oracle.quantize_act(synth.bf16_bits_to_f32(xb))
+    assert np.array_equal(q1, q2) and np.array_equal(b1, b2)
+
+
+def test_act_quant_error_bound():
+    # |q - x * 127 / beta| <= 0.5 + (rounding of the scale): q is within one
+    # integer of the exact real product, and equals it rounded when far from ties.
+    x = synth.activations_f32(8, 300, seed=43)
+    q, beta = oracle.quantize_act(x)
+    exact = x.astype(np.float64) * 127.0 / beta[:, None].astype(np.float64)
+    assert np.all(np.abs(q - exact) <= 0.5 + 1e-4)
+
+
+# --------------------------------------------------------------------------
+# integer product
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 7), (16, 33, 129), (7, 64, 1000)])
+def test_matmul_equals_numpy_int64(M, N, K):
+    q = synth.int8_activations(M, K, seed=M + N + K)
+    t = synth.ternary_weights(N, K, seed=M * N + K)
+    acc = oracle.matmul(q, t)
+    ref = q.astype(np.int64) @ t.astype(np.int64).T
+    assert np.array_equal(acc, ref)
+
+
+def test_matmul_is_add_sub_of_activations():
+    q = synth.int8_activations(5, 300, seed=51)
+    t = synth.ternary_weights(40, 300, seed=52)
+    acc = oracle.matmul(q, t)
+    qi = q.astype(np.int64)
+    for n in range(t.shape[0]):
+        plus = qi[:, t[n] == 1].sum(axis=1)
+        minus = qi[:, t[n] == -1].sum(axis=1)
+        assert np.array_equal(acc[:, n], plus - minus)
+
+
+def test_matmul_special_cases():
+    q = synth.int8_activations(4, 32, seed=53)
+    ones = np.ones((3, 32), np.int8)
+    assert np.array_equal(oracle.matmul(q, ones), np.repeat(q.astype(np.int64).sum(1)[:, None], 3, 1))
+    eye = np.eye(32, dtype=np.int8)
+    assert np.array_equal(oracle.matmul(q, eye), q.astype(np.int32))
+    assert not oracle.matmul(q, np.zeros((5, 32), np.int8)).any()
+
+
+def test_matmul_through_packed_layouts():
+    q = synth.int8_activations(3, 250, seed=54)
+    t = synth.ternary_weights(20, 250, seed=55)
+    acc = oracle.matmul(q, t)
+    for layout in (oracle.LAYOUT_I2, oracle.LAYOUT_B3):
+        t2 = oracle.unpack(oracle.pack(t, layout), 20, 250, layout)
+        assert np.array_equal(oracle.matmul(q, t2), acc)
+
+
+def test_matmul_overflow_is_detected():
+    # ternary weights keep |acc| <= 127 K, so the guard is exercised with a
+    # non-ternary operand: 127 * 127 * K > 2^31 - 1
+    K = 140000
+    q = np.full((1, K), 127, np.int8)
+    t = np.full((1, K), 127, np.int8)
+    with pytest.raises(oracle.OracleError):
+        oracle.matmul(q, t)
+
+
+# --------------------------------------------------------------------------
+# rescale and output rounding
+# --------------------------------------------------------------------------
+def test_rescale_error_bound_and_zero():
+    r = synth.rng(61)
+    acc = r.integers(-3_000_000, 3_000_000, size=(16, 300)).astype(np.int32)
+    acc[0, :5] = 0
+    beta = (r.random(16) * 50 + 0.1).astype(np.float32)
+    gamma = np.float32(0.0159)
+    y = oracle.rescale(acc, beta, gamma)
+    exact = acc.astype(np.float64) * float(gamma) * beta.astype(np.float64)[:, None] / 127.0
+    ulp = np.spacing(np.abs(y).astype(np.float32)).astype(np.float64)
+    nz = acc != 0
+    assert np.all(np.abs(y[nz] - exact[nz]) <= 2 * ulp[nz])
+    assert np.all(y[0, :5] == 0) and not np.signbit(y[0, :5]).any()
+
+
+def test_bf16_output_ties():
+    v = HV["bf16_ties"]
+    b = oracle.f32_to_bf16(np.array(v["f32"], np.float32))
+    assert [hex(int(x)) for x in b] == [h.replace("0x", "0x") for h in v["bf16_hex"]] or \
+        [int(x) for x in b] == [int(h, 16) for h in v["bf16_hex"]]
+
+
+# --------------------------------------------------------------------------
+# the composed forward
+# --------------------------------------------------------------------------
+def test_forward_hand_vector():
+    v = HV["forward_1x4"]
+    w = np.array(v["W"], np.float32)
+    t, g = oracle.quantize_weights(w)
+    assert t.tolist() == v["T"]
+    out = oracle.forward(t, g, np.array(v["x"], np.float32))
+    assert out["beta"].tolist() == v["beta"]
+    assert out["q"].tolist() == v["q"]
+    assert out["acc"].tolist() == v["acc"]
+    r = np.float32(np.float32(np.float32(0.75) * np.float32(8.0)) / np.float32(127.0))
+    assert out["y"][0, 0] == np.float32(-16.0) * r
+
+
+def test_forward_tracks_the_linear_layer():
+    # Not a parity gate: BitLinear should approximate x @ W^T (LIT-380 Key
+    # takeaways bullet 3 reports perplexity close to FP16); report-level check.
+    w = synth.latent_weights(512, 256, seed=71)
+    x = synth.activations_f32(16, 256, seed=72)
+    t, g = oracle.quantize_weights(w)
+    y = oracle.forward(t, g, x)["y"]
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    corr = np.corrcoef(y.reshape(-1), ref.reshape(-1))[0, 1]
+    assert corr > 0.7
