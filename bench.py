@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Throughput of the BitLinear forward (BitNet b1.58) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the forward over one batch of synthetic inputs: for the
+default workload (the 3B model's decode layers) every layer of the set
+q, k, v, o (3200 x 3200), gate, up (8640 x 3200), down (3200 x 8640) at every
+batch M in {1, 4, 16}: bf16 activations quantised per token to int8, the
+ternary x int8 product from 2-bit packed weights, and the fp32 rescale.
+Weights are ternarised and packed once, before timing (a load-time step; its
+throughput is reported separately under "weight_prep").  Steps rotate over
+copies of the packed weights totalling >= 1 GiB so that neither the L2 nor
+the 256 MB Infinity Cache serves them.  Each step is a captured HIP graph.
+
+One JSON line is printed.  'value' is packed-weight GB/s over the whole step
+(wall clock around K replays); 'roofline' reports the dominant kernel from a
+replay in which every launch of it is bracketed by HIP events; 'cpu_baseline'
+times the CPU oracle on a bounded sample of the same work.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "packed-weight GB/s + effective ternary TOPS per BitLinear (decode GEMV, prefill GEMM)"
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+MALL_DEFEAT_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_3b",
+                    choices=["decode_3b", "prefill_3b", "llama70b_layers", "stack_3b_26"])
+    ap.add_argument("--batches", default=None, help="comma list overriding the workload's batch sizes")
+    ap.add_argument("--layout", default="i2", choices=["i2", "b3"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); this library has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from ternary_weight_linear_forward_amd import bitlinear as bl
+    from ternary_weight_linear_forward_amd import synth, workloads
+
+    wl = workloads.ALL[args.workload]
+    layout = bl.LAYOUT_I2 if args.layout == "i2" else bl.LAYOUT_B3
+    batches = tuple(int(b) for b in args.batches.split(",")) if args.batches else wl.batches
+    dev = torch.device("cuda")
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    print(f"[bench] workload={wl.name} batches={batches} layout={args.layout}", file=sys.stderr, flush=True)
+
+    # ---- weights: quantise + pack on the GPU (timed separately) --------------
+    layers = []
+    prep_ms = 0.0
+    prep_bytes = 0
+    with torch.cuda.stream(stream):
+        for li, layer in enumerate(wl.layers):
+            w = torch.from_numpy(synth.latent_weights(layer.N, layer.K, seed=workloads.seed_for(wl, li, 0))).to(dev)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            T, gamma = bl.quantize_weights(w, stream=stream)
+            P = bl.pack(T, layout, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            prep_ms += e0.elapsed_time(e1)
+            prep_bytes += w.numel() * 4
+            layers.append({"layer": layer, "gamma": gamma, "P": [P]})
+            del w, T
+    set_bytes = sum(L["P"][0].numel() for L in layers)
+    ncopies = max(1, math.ceil(MALL_DEFEAT_BYTES / set_bytes))
+    for L in layers:
+        L["P"] += [L["P"][0].clone() for _ in range(ncopies - 1)]
+    torch.cuda.synchronize()
+    print(f"[bench] packed set {set_bytes/1e6:.1f} MB x {ncopies} copies", file=sys.stderr, flush=True)
+
+    # ---- activations and outputs --------------------------------------------
+    act = synth.activations_student_t_bf16 if wl.act_dist == "student_t" else synth.activations_bf16
+    jobs = []
+    for M in batches:
+        for li, L in enumerate(layers):
+            layer = L["layer"]
+            x = act(M, layer.K, seed=workloads.seed_for(wl, li, 1) + M)
+            xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+            ldq = (layer.K + 63) // 64 * 64
+            jobs.append({
+                "M": M, "L": L, "x": xd,
+                "xq": torch.empty((M, ldq), dtype=torch.int8, device=dev),
+                "beta": torch.empty(M, dtype=torch.float32, device=dev),
+                "y": torch.empty((M, layer.N), dtype=torch.float32, device=dev),
+            })
+    torch.cuda.synchronize()
+
+    def algo_for(M):
+        # the kernel bitlinear_forward picks automatically (mirrors its dispatch)
+        if M <= 16:
+            return bl.ALGO_GEMV_ADDSUB if (layout == bl.LAYOUT_I2 and M <= 4) else bl.ALGO_GEMV_MFMA
+        return bl.ALGO_GEMM_MFMA if layout == bl.LAYOUT_I2 else bl.ALGO_GEMV_MFMA
+
+    def kernel_name(M):
+        a = algo_for(M)
+        if a == bl.ALGO_GEMV_ADDSUB:
+            mt = 1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8 if M <= 8 else 16
+            return f"k_gemv_addsub<{mt}>"
+        if a == bl.ALGO_GEMV_MFMA:
+            return f"k_gemv_mfma<{layout}>"
+        return "k_gemm_mfma_i2"
+
+    def launch_job(j, copy, sidx):
+        L = j["L"]
+        layer = L["layer"]
+        s = stream.cuda_stream
+        st = bl.bitlinear_quantize_act(j["x"].data_ptr(), bl.BF16, j["M"], layer.K, j["x"].stride(0),
+                                       j["xq"].data_ptr(), j["xq"].stride(0), j["beta"].data_ptr(), s)
+        if st:
+            raise bl.BitlinearError(st, "quantize_act")
+        st = bl.bitlinear_forward_algo(L["P"][copy].data_ptr(), layout, L["gamma"].data_ptr(), j["M"], layer.N,
+                                       layer.K, j["xq"].data_ptr(), bl.I8, j["xq"].stride(0), j["beta"].data_ptr(),
+                                       j["y"].data_ptr(), bl.F32, j["y"].stride(0), None, 0, algo_for(j["M"]), s)
+        if st:
+            raise bl.BitlinearError(st, "forward")
+
+    def step(copy):
+        for sidx, j in enumerate(jobs):
+            launch_job(j, copy, sidx)
+
+    # ---- capture one graph per weight copy -----------------------------------
+    graphs = []
+    with torch.cuda.stream(stream):
+        step(0)  # eager warm-up before capture
+        torch.cuda.synchronize()
+        for c in range(ncopies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step(c)
+            graphs.append(g)
+    torch.cuda.synchronize()
+    print(f"[bench] captured {len(graphs)} graphs of {2 * len(jobs)} kernels", file=sys.stderr, flush=True)
+
+    with torch.cuda.stream(stream):
+        for k in range(args.warmup):
+            graphs[k % ncopies].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(args.steps):
+            graphs[(args.warmup + k) % ncopies].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    step_ms = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] timed {args.steps} steps: {step_ms:.4f} ms/step (wall {wall*1e3/args.steps:.4f})",
+          file=sys.stderr, flush=True)
+
+    packed_per_step = sum(j["L"]["P"][0].numel() for j in jobs)
+    ops_per_step = sum(2 * j["M"] * j["L"]["layer"].N * j["L"]["layer"].K for j in jobs)
+    value = packed_per_step / (step_ms * 1e-3) / 1e9
+    tops = ops_per_step / (step_ms * 1e-3) / 1e12
+
+    # ---- roofline: HIP events around every launch of each product kernel -----
+    def gemv_bytes(j):
+        layer = j["L"]["layer"]
+        return j["L"]["P"][0].numel() + j["M"] * layer.K + 4 * j["M"] + 4 + 4 * j["M"] * layer.N
+
+    per_kernel = {}
+    reps = max(1, min(args.steps, ncopies, 4))
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        marks = []
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(50_000_000)  # hold the stream while the host queues every launch
+        for r in range(reps):
+            for sidx, j in enumerate(jobs):
+                L = j["L"]
+                layer = L["layer"]
+                s = stream.cuda_stream
+                bl.bitlinear_quantize_act(j["x"].data_ptr(), bl.BF16, j["M"], layer.K, j["x"].stride(0),
+                                          j["xq"].data_ptr(), j["xq"].stride(0), j["beta"].data_ptr(), s)
+                ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ea.record(stream)
+                bl.bitlinear_forward_algo(L["P"][r % ncopies].data_ptr(), layout, L["gamma"].data_ptr(), j["M"],
+                                          layer.N, layer.K, j["xq"].data_ptr(), bl.I8, j["xq"].stride(0),
+                                          j["beta"].data_ptr(), j["y"].data_ptr(), bl.F32, j["y"].stride(0), None,
+                                          0, algo_for(j["M"]), s)
+                eb.record(stream)
+                marks.append((kernel_name(j["M"]), ea, eb, gemv_bytes(j), 2 * j["M"] * layer.N * layer.K))
+        torch.cuda.synchronize()
+    for name, ea, eb, nbytes, nops in marks:
+        d = per_kernel.setdefault(name, {"ms": 0.0, "bytes": 0, "ops": 0, "launches": 0})
+        d["ms"] += ea.elapsed_time(eb)
+        d["bytes"] += nbytes
+        d["ops"] += nops
+        d["launches"] += 1
+    dom_name, dom = max(per_kernel.items(), key=lambda kv: kv[1]["ms"])
+    avg_us = dom["ms"] / dom["launches"] * 1e3
+    bound = "mfma" if dom_name.startswith("k_gemm") else "hbm"
+    if bound == "hbm":
+        achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = dom["ops"] / (dom["ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                "frac": round(achieved / INT8_PEAK_TOPS, 4)}
+    roof.update({"traffic": None, "kernel": dom_name, "avg_launch_us": round(avg_us, 3),
+                 "launches": dom["launches"],
+                 "algorithmic_bytes_per_launch": dom["bytes"] // dom["launches"]})
+    kernels = {k: {"avg_us": round(v["ms"] / v["launches"] * 1e3, 3),
+                   "GB/s": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1),
+                   "TOPS": round(v["ops"] / (v["ms"] * 1e-3) / 1e12, 2), "launches": v["launches"]}
+               for k, v in per_kernel.items()}
+    print(f"[bench] per-kernel: {json.dumps(kernels)}", file=sys.stderr, flush=True)
+
+    # ---- CPU oracle baseline --------------------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, batches, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "layers": {L["layer"].name: [L["layer"].N, L["layer"].K] for L in layers},
+            "batches": list(batches),
+            "layout": args.layout,
+            "x_dtype": "bf16",
+            "y_dtype": "f32",
+            "weight_copies": ncopies,
+            "graph_replay": True,
+        },
+        "effective_tops": round(tops, 2),
+        "us_per_bitlinear": round(step_ms * 1e3 / len(jobs), 3),
+        "kernels": kernels,
+        "weight_prep": {"GB/s_latent_fp32": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1),
+                        "ms": round(prep_ms, 3)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, batches, seconds):
+    """The CPU oracle, untuned, on a bounded sample of the same work: whole
+    layers of the workload (quantise the activations, exact product, rescale),
+    cycling through the step's (batch, layer) pairs until about 'seconds' of
+    CPU time has passed.  Reported in the same unit (packed-weight GB/s)."""
+    import oracle
+
+    from ternary_weight_linear_forward_amd import synth, workloads
+    from ternary_weight_linear_forward_amd import bitlinear as bl
+
+    act = synth.activations_student_t_bf16 if wl.act_dist == "student_t" else synth.activations_bf16
+    pairs = [(M, li) for M in batches for li in range(len(wl.layers))]
+    tern = {}
+    done_bytes = 0
+    done = []
+    t_total = 0.0
+    i = 0
+    while t_total < seconds and i < 400 * len(pairs):
+        M, li = pairs[i % len(pairs)]
+        layer = wl.layers[li]
+        if li not in tern:
+            w = synth.latent_weights(layer.N, layer.K, seed=workloads.seed_for(wl, li, 0))
+            tern[li] = oracle.quantize_weights(w)
+        t, g = tern[li]
+        x = act(M, layer.K, seed=workloads.seed_for(wl, li, 1) + M)
+        t0 = time.perf_counter()
+        oracle.forward(t, g, x)
+        t_total += time.perf_counter() - t0
+        done_bytes += bl.bitlinear_packed_bytes(layer.N, layer.K, bl.LAYOUT_I2)
+        done.append(f"{layer.name}@M{M}")
+        i += 1
+    return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": oracle.threads_used(),
+            "kind": "oracle",
+            "sample": f"{len(done)} BitLinear forwards ({', '.join(done[:8])}{', ...' if len(done) > 8 else ''}) "
+                      f"in {t_total:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * bitlinear.h -- C ABI of libbitlinear, the BitLinear forward pass of
+ * BitNet b1.58 on AMD Instinct MI355X (gfx950).
+ *
+ * Method (what the sources say):
+ *   - "The Era of 1-bit LLMs: All Large Language Models are in 1.58 Bits",
+ *     Abstract: every weight of a BitNet b1.58 model is ternary, {-1, 0, +1}.
+ *   - LIT-380 record (dmarx anthology), Key takeaways, bullet 1: BitLinear is
+ *     the drop-in replacement of nn.Linear; weights go to {-1, 0, +1} through
+ *     an absmean quantisation function; activations are 8-bit integers.
+ *   - LIT-380, Key takeaways, bullet 4: the matrix product becomes integer
+ *     additions and subtractions, with no multiplications.
+ *   - HackerPapers digest, thread "GPUs Go Brrr": 1.58 bits are 2 bits in
+ *     practice; thread "How to pack ternary numbers in 8-bit bytes": five
+ *     ternary digits fit one byte.
+ * The pages give no formulas; this library fixes the plainest reading:
+ *   gamma   = mean |W| over the whole tensor, exact, rounded once to binary32;
+ *   T       = clamp(rint(W / gamma), -1, +1), IEEE division, ties to even;
+ *   beta_m  = max_k |x_mk| (per token);
+ *   q_mk    = clamp(rint(x_mk * (127 / beta_m)), -127, 127), ties to even;
+ *   acc_mn  = sum_k q_mk * T_nk, exact in int32;
+ *   y_mn    = float(acc_mn) * ((gamma * beta_m) / 127), binary32.
+ *
+ * Conventions for every entry point:
+ *   - Matrices are row-major.  W and T are [N x K] (out x in, like
+ *     nn.Linear.weight), X and Xq are [M x K], Y is [M x N].  "ld*" arguments
+ *     are row strides in elements.
+ *   - All array pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises; it keeps no mutable global state.
+ *   - 'stream' is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it and the call returns before the work finishes.
+ *   - Argument errors are detected on the host before anything is enqueued and
+ *     returned as a status; nothing is launched in that case.  A failed launch
+ *     returns BITLINEAR_ERR_LAUNCH.  The library never prints.
+ *   - Non-finite floating-point inputs are outside the contract.
+ *   - K <= BITLINEAR_MAX_K keeps |acc| < 2^24, so float(acc) is exact.
+ *   - Pointers read with 128-bit loads (P, Xq, ws) must be 16-byte aligned.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITLINEAR_MAX_K 131072
+#define BITLINEAR_MAX_M 65536
+
+typedef enum {
+    BITLINEAR_OK = 0,
+    BITLINEAR_ERR_INVALID_ARG = 1, /* null pointer, bad size, stride, enum or alignment */
+    BITLINEAR_ERR_UNSUPPORTED = 2, /* valid request this build does not implement       */
+    BITLINEAR_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required        */
+    BITLINEAR_ERR_LAUNCH = 4,      /* a kernel launch failed                            */
+    BITLINEAR_ERR_DEVICE = 5       /* no usable gfx950 device on the current HIP device  */
+} bitlinear_status_t;
+
+typedef enum {
+    BITLINEAR_F32 = 0,
+    BITLINEAR_BF16 = 1,
+    BITLINEAR_I8 = 2,
+    BITLINEAR_I32 = 3
+} bitlinear_dtype_t;
+
+typedef enum {
+    BITLINEAR_LAYOUT_I2 = 0, /* 2 bits per weight                     */
+    BITLINEAR_LAYOUT_B3 = 1  /* base 3, 5 weights per byte            */
+} bitlinear_layout_t;
+
+typedef enum {
+    BITLINEAR_ALGO_AUTO = 0,        /* pick by M and layout                                 */
+    BITLINEAR_ALGO_GEMV_ADDSUB = 1, /* vector-ALU add/subtract GEMV, M <= 16                */
+    BITLINEAR_ALGO_GEMV_MFMA = 2,   /* 16-token int8 matrix-core tiles, M <= 16             */
+    BITLINEAR_ALGO_GEMM_MFMA = 3    /* LDS-tiled int8 matrix-core GEMM, any M (i2 layout)   */
+} bitlinear_algo_t;
+
+/* Static description of a status code (never NULL). */
+const char *bitlinear_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int bitlinear_version(void);
+
+/*
+ * Packed layouts (this library's convention; the pages fix none).
+ * Both store code c = T + 1 in {0, 1, 2} and pad with T = 0 (rows up to a
+ * multiple of 16, columns up to a whole k-block).  Rows are grouped in tiles
+ * of 16.  Inside a tile, 16-byte chunks are ordered by k-block, then by row:
+ * the chunk of row n and k-block kb starts at byte
+ *     ((n / 16) * KB + kb) * 256 + (n % 16) * 16.
+ *   I2: a k-block is 64 weights, KB = ceil(K / 64).  Little-endian 32-bit word
+ *       d (0..3) of a chunk holds weights kb*64 + 16d + 4s + j (s, j in 0..3)
+ *       at bits 8j+2s .. 8j+2s+1, so (word >> 2s) & 0x03030303 gives the
+ *       codes of 4 consecutive weights, one per byte.
+ *   B3: a k-block is 80 weights, KB = ceil(K / 80).  Byte i (0..15) of a chunk
+ *       holds weights kb*80 + 5i + t (t = 0..4) as sum_t c_t * 3^(4-t) (first
+ *       weight most significant); values 243..255 never occur.
+ * Returns the byte size of P, or -1 if N, K or layout is invalid.
+ */
+int64_t bitlinear_packed_bytes(int64_t N, int64_t K, int layout);
+
+/* Workspace bytes bitlinear_quantize_weights needs (-1 if N or K is invalid). */
+int64_t bitlinear_quantize_weights_workspace_bytes(int64_t N, int64_t K);
+
+/*
+ * Workspace bytes bitlinear_forward needs for these sizes (-1 if invalid).
+ * Covers the staged int8 activations of the fused quantiser (x_dtype F32 or
+ * BF16) and any split-K partial sums.
+ */
+int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int layout, int x_dtype);
+
+/*
+ * Absmean weight ternarisation (LIT-380 Key takeaways bullet 1).
+ *   W      fp32 [N x K], row stride ldw >= K (device, read-only).
+ *   T      int8 [N x K], row stride K (device, written): values in {-1, 0, +1}.
+ *   gamma  1 fp32 (device, written): the exact mean of |W| rounded once to
+ *          binary32, ties to even.  The sum is exact and order-independent.
+ *   ws     >= bitlinear_quantize_weights_workspace_bytes(N, K) bytes, 16-byte
+ *          aligned; contents on entry are ignored.
+ * Requires N * K < 2^40.  gamma == 0 (all-zero W) gives T = 0.
+ */
+int bitlinear_quantize_weights(const float *W, int64_t N, int64_t K, int64_t ldw, int8_t *T,
+                               float *gamma, void *ws, int64_t ws_bytes, void *stream);
+
+/*
+ * Pack ternary weights T int8 [N x K] (row stride ldt >= K, values in
+ * {-1, 0, +1}) into P (bitlinear_packed_bytes(N, K, layout) bytes, 16-byte
+ * aligned).  Every byte of P is written, padding included.  Values of T
+ * outside {-1, 0, +1} are outside the contract.
+ */
+int bitlinear_pack(const int8_t *T, int64_t N, int64_t K, int64_t ldt, int layout, uint8_t *P,
+                   void *stream);
+
+/*
+ * Per-token absmax int8 activation quantisation (LIT-380 Key takeaways
+ * bullet 1: 8-bit activations).
+ *   X      [M x K], x_dtype F32 or BF16, row stride ldx >= K.
+ *   Xq     int8 [M x K], row stride ldq >= K, 16-byte aligned, ldq % 16 == 0.
+ *          Bytes K .. ldq-1 of every row are written with 0.
+ *   beta   fp32 [M]: beta_m = max_k |x_mk|; a zero row gives beta = 0, q = 0.
+ */
+int bitlinear_quantize_act(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int8_t *Xq,
+                           int64_t ldq, float *beta, void *stream);
+
+/*
+ * BitLinear forward: Y = rescale(quant(X) (x) T^T), T given packed in P.
+ *   P        packed weights of T [N x K] in 'layout' (16-byte aligned).
+ *   gamma    1 fp32 (device): the weight scale returned by quantize_weights.
+ *   X        x_dtype F32 or BF16: quantised per token inside the call (the
+ *            quantiser is fused with the product; its int8 output is staged
+ *            in ws).  x_dtype I8: X is already quantised (16-byte aligned,
+ *            ldx % 16 == 0) and beta_in (fp32 [M], device) gives beta.
+ *   beta_in  required iff x_dtype == I8, else must be NULL.
+ *   Y        [M x N], y_dtype F32, BF16 (round to nearest even), or I32 (the
+ *            exact accumulators acc, no rescale); row stride ldy >= N.
+ *   ws       >= bitlinear_forward_workspace_bytes(M, N, K, layout, x_dtype)
+ *            bytes, 16-byte aligned (may be NULL when that size is 0).
+ * The accumulators are exact; Y in F32 is bit-identical to the binary32
+ * formula above.  Calls that share a workspace must be ordered on one stream.
+ */
+int bitlinear_forward(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                      const void *X, int x_dtype, int64_t ldx, const float *beta_in, void *Y, int y_dtype,
+                      int64_t ldy, void *ws, int64_t ws_bytes, void *stream);
+
+/* Same as bitlinear_forward with an explicit kernel choice (bitlinear_algo_t);
+ * returns BITLINEAR_ERR_UNSUPPORTED if that kernel cannot take these sizes. */
+int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N,
+                           int64_t K, const void *X, int x_dtype, int64_t ldx, const float *beta_in,
+                           void *Y, int y_dtype, int64_t ldy, void *ws, int64_t ws_bytes, int algo,
+                           void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

@@ -1,0 +1,193 @@
+"""ctypes binding of libbitlinear (include/bitlinear.h).
+
+Argument marshalling only: every step of the BitLinear forward runs in the HIP
+kernels of libbitlinear.so.  The ``bitlinear_*`` functions mirror the C entry
+points one to one (device pointers as Python ints, the HIP stream as an int);
+the lower-case helpers below them take torch tensors, allocate outputs with
+torch (device memory and streams are all torch is used for) and call those.
+
+Importing this module raises if the library has not been built: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m ternary_weight_linear_forward_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# --- enums (bitlinear.h) ---------------------------------------------------
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_DEVICE = range(6)
+F32, BF16, I8, I32 = range(4)
+LAYOUT_I2, LAYOUT_B3 = 0, 1
+ALGO_AUTO, ALGO_GEMV_ADDSUB, ALGO_GEMV_MFMA, ALGO_GEMM_MFMA = range(4)
+MAX_K = 131072
+MAX_M = 65536
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+
+_SIGNATURES = {
+    "bitlinear_status_string": ([_INT], ctypes.c_char_p),
+    "bitlinear_version": ([], _INT),
+    "bitlinear_packed_bytes": ([_I64, _I64, _INT], _I64),
+    "bitlinear_quantize_weights_workspace_bytes": ([_I64, _I64], _I64),
+    "bitlinear_forward_workspace_bytes": ([_I64, _I64, _I64, _INT, _INT], _I64),
+    "bitlinear_quantize_weights": ([_P, _I64, _I64, _I64, _P, _P, _P, _I64, _P], _INT),
+    "bitlinear_pack": ([_P, _I64, _I64, _I64, _INT, _P, _P], _INT),
+    "bitlinear_quantize_act": ([_P, _INT, _I64, _I64, _I64, _P, _I64, _P, _P], _INT),
+    "bitlinear_forward": ([_P, _INT, _P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P, _INT, _I64, _P, _I64, _P], _INT),
+    "bitlinear_forward_algo": (
+        [_P, _INT, _P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P, _INT, _I64, _P, _I64, _INT, _P], _INT),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+for _name, (_args, _res) in _SIGNATURES.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+
+class BitlinearError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {bitlinear_status_string(status)} (status {status})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise BitlinearError(status, where)
+
+
+# --- raw C entry points (same names) ----------------------------------------
+def bitlinear_status_string(status: int) -> str:
+    return _lib.bitlinear_status_string(status).decode()
+
+
+def bitlinear_version() -> int:
+    return _lib.bitlinear_version()
+
+
+def bitlinear_packed_bytes(N: int, K: int, layout: int) -> int:
+    return _lib.bitlinear_packed_bytes(N, K, layout)
+
+
+def bitlinear_quantize_weights_workspace_bytes(N: int, K: int) -> int:
+    return _lib.bitlinear_quantize_weights_workspace_bytes(N, K)
+
+
+def bitlinear_forward_workspace_bytes(M: int, N: int, K: int, layout: int, x_dtype: int) -> int:
+    return _lib.bitlinear_forward_workspace_bytes(M, N, K, layout, x_dtype)
+
+
+def bitlinear_quantize_weights(W, N, K, ldw, T, gamma, ws, ws_bytes, stream) -> int:
+    return _lib.bitlinear_quantize_weights(W, N, K, ldw, T, gamma, ws, ws_bytes, stream)
+
+
+def bitlinear_pack(T, N, K, ldt, layout, P, stream) -> int:
+    return _lib.bitlinear_pack(T, N, K, ldt, layout, P, stream)
+
+
+def bitlinear_quantize_act(X, x_dtype, M, K, ldx, Xq, ldq, beta, stream) -> int:
+    return _lib.bitlinear_quantize_act(X, x_dtype, M, K, ldx, Xq, ldq, beta, stream)
+
+
+def bitlinear_forward(P, layout, gamma, M, N, K, X, x_dtype, ldx, beta_in, Y, y_dtype, ldy, ws, ws_bytes,
+                      stream) -> int:
+    return _lib.bitlinear_forward(P, layout, gamma, M, N, K, X, x_dtype, ldx, beta_in, Y, y_dtype, ldy, ws,
+                                  ws_bytes, stream)
+
+
+def bitlinear_forward_algo(P, layout, gamma, M, N, K, X, x_dtype, ldx, beta_in, Y, y_dtype, ldy, ws, ws_bytes,
+                           algo, stream) -> int:
+    return _lib.bitlinear_forward_algo(P, layout, gamma, M, N, K, X, x_dtype, ldx, beta_in, Y, y_dtype, ldy, ws,
+                                       ws_bytes, algo, stream)
+
+
+# --- torch-tensor helpers (allocation + marshalling) ------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    return {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.int32: I32}[t.dtype]
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+def quantize_weights(W, stream=None):
+    """Latent fp32 W [N x K] (cuda) -> (T int8 [N x K], gamma fp32 [1])."""
+    torch = _torch()
+    N, K = W.shape
+    T = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    gamma = torch.empty(1, dtype=torch.float32, device=W.device)
+    nws = bitlinear_quantize_weights_workspace_bytes(N, K)
+    if nws < 0:
+        raise BitlinearError(ERR_INVALID_ARG, "quantize_weights")
+    ws = torch.empty(nws, dtype=torch.uint8, device=W.device)
+    _check(bitlinear_quantize_weights(_ptr(W), N, K, W.stride(0), _ptr(T), _ptr(gamma), _ptr(ws), nws,
+                                      _stream(stream)), "bitlinear_quantize_weights")
+    return T, gamma
+
+
+def pack(T, layout: int = LAYOUT_I2, stream=None):
+    """Ternary int8 T [N x K] (cuda) -> packed uint8 P."""
+    torch = _torch()
+    N, K = T.shape
+    nbytes = bitlinear_packed_bytes(N, K, layout)
+    if nbytes < 0:
+        raise BitlinearError(ERR_INVALID_ARG, "pack")
+    P = torch.empty(nbytes, dtype=torch.uint8, device=T.device)
+    _check(bitlinear_pack(_ptr(T), N, K, T.stride(0), layout, _ptr(P), _stream(stream)), "bitlinear_pack")
+    return P
+
+
+def quantize_act(X, stream=None):
+    """Activations X [M x K] fp32/bf16 (cuda) -> (Xq int8 [M x ldq], beta fp32 [M]); ldq = K rounded up to 16."""
+    torch = _torch()
+    M, K = X.shape
+    ldq = (K + 15) // 16 * 16
+    Xq = torch.empty((M, ldq), dtype=torch.int8, device=X.device)
+    beta = torch.empty(M, dtype=torch.float32, device=X.device)
+    _check(bitlinear_quantize_act(_ptr(X), _dtype_code(X), M, K, X.stride(0), _ptr(Xq), ldq, _ptr(beta),
+                                  _stream(stream)), "bitlinear_quantize_act")
+    return Xq, beta
+
+
+def forward(P, layout: int, gamma, X, N: int, K: int | None = None, beta=None, y_dtype=None, algo: int = ALGO_AUTO,
+            ws=None, out=None, stream=None):
+    """BitLinear forward.  X [M x >=K] fp32/bf16 (quantised inside the call) or
+    int8 (then 'beta' is required).  Returns Y [M x N] (fp32 by default; bf16,
+    or int32 raw accumulators with y_dtype=torch.int32)."""
+    torch = _torch()
+    M = X.shape[0]
+    K = X.shape[1] if K is None else K
+    xdt = _dtype_code(X)
+    if out is None:
+        out = torch.empty((M, N), dtype=y_dtype or torch.float32, device=X.device)
+    nws = bitlinear_forward_workspace_bytes(M, N, K, layout, xdt)
+    if nws < 0:
+        raise BitlinearError(ERR_INVALID_ARG, "forward")
+    if nws > 0 and (ws is None or ws.numel() < nws):
+        ws = torch.empty(nws, dtype=torch.uint8, device=X.device)
+    _check(bitlinear_forward_algo(_ptr(P), layout, _ptr(gamma), M, N, K, _ptr(X), xdt, X.stride(0), _ptr(beta),
+                                  _ptr(out), _dtype_code(out), out.stride(0), _ptr(ws) if nws > 0 else None,
+                                  nws, algo, _stream(stream)), "bitlinear_forward")
+    return out

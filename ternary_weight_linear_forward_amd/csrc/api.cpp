@@ -1,0 +1,232 @@
+// api.cpp -- the C ABI of libbitlinear (declared in include/bitlinear.h).
+// Validates every argument on the host, then enqueues the kernels.  Nothing is
+// launched when validation fails.  No allocation, no synchronisation, no
+// mutable global state.
+#include "bitlinear.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40; // keeps per-exponent sums of |W| below 2^64
+// Largest M the add/subtract GEMV takes when the kernel is chosen automatically.
+constexpr int64_t kAddSubMaxM = 4;
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+int dtype_size(int dt)
+{
+    switch (dt) {
+    case BITLINEAR_F32: return 4;
+    case BITLINEAR_BF16: return 2;
+    case BITLINEAR_I8: return 1;
+    case BITLINEAR_I32: return 4;
+    default: return 0;
+    }
+}
+
+struct Span {
+    uintptr_t lo, hi; // [lo, hi)
+};
+
+Span span_of(const void *p, int64_t rows, int64_t ld, int64_t cols, int elem)
+{
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    uintptr_t bytes = static_cast<uintptr_t>(((rows - 1) * ld + cols) * elem);
+    return {lo, lo + bytes};
+}
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? BITLINEAR_OK : BITLINEAR_ERR_LAUNCH; }
+
+bool valid_layout(int layout) { return layout == BITLINEAR_LAYOUT_I2 || layout == BITLINEAR_LAYOUT_B3; }
+
+// Staged activations of the fused quantiser: Xq [M x round_up(K, 64)] then beta [M].
+int64_t staged_ldq(int64_t K) { return round_up(K, 64); }
+int64_t staged_xq_bytes(int64_t M, int64_t K) { return round_up(M * staged_ldq(K), 256); }
+
+} // namespace
+
+extern "C" {
+
+const char *bitlinear_status_string(int status)
+{
+    switch (status) {
+    case BITLINEAR_OK: return "ok";
+    case BITLINEAR_ERR_INVALID_ARG: return "invalid argument";
+    case BITLINEAR_ERR_UNSUPPORTED: return "unsupported combination of arguments";
+    case BITLINEAR_ERR_WORKSPACE: return "workspace missing or too small";
+    case BITLINEAR_ERR_LAUNCH: return "kernel launch failed";
+    case BITLINEAR_ERR_DEVICE: return "no usable gfx950 device";
+    default: return "unknown status";
+    }
+}
+
+int bitlinear_version(void) { return 100; }
+
+int64_t bitlinear_packed_bytes(int64_t N, int64_t K, int layout)
+{
+    if (N < 1 || K < 1 || K > BITLINEAR_MAX_K || N > kMaxElems || !valid_layout(layout)) return -1;
+    const int64_t NT = (N + 15) / 16;
+    const int64_t KB = layout == BITLINEAR_LAYOUT_I2 ? (K + 63) / 64 : (K + 79) / 80;
+    return NT * KB * 256;
+}
+
+int64_t bitlinear_quantize_weights_workspace_bytes(int64_t N, int64_t K)
+{
+    if (N < 1 || K < 1 || N > kMaxElems / K) return -1;
+    return 256 * 8; // 256 per-exponent uint64 sums
+}
+
+int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int layout, int x_dtype)
+{
+    if (M < 1 || M > BITLINEAR_MAX_M || N < 1 || K < 1 || K > BITLINEAR_MAX_K || !valid_layout(layout))
+        return -1;
+    if (x_dtype == BITLINEAR_I8) return 0;
+    if (x_dtype != BITLINEAR_F32 && x_dtype != BITLINEAR_BF16) return -1;
+    return staged_xq_bytes(M, K) + round_up(4 * M, 256);
+}
+
+int bitlinear_quantize_weights(const float *W, int64_t N, int64_t K, int64_t ldw, int8_t *T, float *gamma,
+                               void *ws, int64_t ws_bytes, void *stream)
+{
+    if (!W || !T || !gamma) return BITLINEAR_ERR_INVALID_ARG;
+    if (N < 1 || K < 1 || ldw < K || N > kMaxElems / K) return BITLINEAR_ERR_INVALID_ARG;
+    const int64_t need = bitlinear_quantize_weights_workspace_bytes(N, K);
+    if (!ws || ws_bytes < need) return BITLINEAR_ERR_WORKSPACE;
+    if (!aligned16(ws) || (reinterpret_cast<uintptr_t>(W) & 3u) || (reinterpret_cast<uintptr_t>(gamma) & 3u))
+        return BITLINEAR_ERR_INVALID_ARG;
+    const Span sw = span_of(W, N, ldw, K, 4), st = span_of(T, N, K, K, 1), sg = span_of(gamma, 1, 1, 1, 4),
+               sws = span_of(ws, 1, need, need, 1);
+    if (overlap(sw, st) || overlap(sw, sg) || overlap(st, sg) || overlap(sws, sw) || overlap(sws, st) ||
+        overlap(sws, sg))
+        return BITLINEAR_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return status_of(bl::launch_quantize_weights(W, N, K, ldw, T, gamma, ws, as_stream(stream)));
+}
+
+int bitlinear_pack(const int8_t *T, int64_t N, int64_t K, int64_t ldt, int layout, uint8_t *P, void *stream)
+{
+    if (!T || !P || !valid_layout(layout)) return BITLINEAR_ERR_INVALID_ARG;
+    if (N < 1 || K < 1 || K > BITLINEAR_MAX_K || ldt < K || N > kMaxElems / K) return BITLINEAR_ERR_INVALID_ARG;
+    if (!aligned16(P)) return BITLINEAR_ERR_INVALID_ARG;
+    const int64_t pb = bitlinear_packed_bytes(N, K, layout);
+    if (overlap(span_of(T, N, ldt, K, 1), span_of(P, 1, pb, pb, 1))) return BITLINEAR_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return status_of(bl::launch_pack(T, N, K, ldt, layout, P, as_stream(stream)));
+}
+
+int bitlinear_quantize_act(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int8_t *Xq,
+                           int64_t ldq, float *beta, void *stream)
+{
+    if (!X || !Xq || !beta) return BITLINEAR_ERR_INVALID_ARG;
+    if (x_dtype != BITLINEAR_F32 && x_dtype != BITLINEAR_BF16) return BITLINEAR_ERR_INVALID_ARG;
+    if (M < 1 || M > BITLINEAR_MAX_M || K < 1 || K > BITLINEAR_MAX_K || ldx < K || ldq < K || ldq % 16)
+        return BITLINEAR_ERR_INVALID_ARG;
+    if (!aligned16(Xq) || (reinterpret_cast<uintptr_t>(X) % dtype_size(x_dtype)) ||
+        (reinterpret_cast<uintptr_t>(beta) & 3u))
+        return BITLINEAR_ERR_INVALID_ARG;
+    const Span sx = span_of(X, M, ldx, K, dtype_size(x_dtype)), sq = span_of(Xq, M, ldq, ldq, 1),
+               sb = span_of(beta, 1, M, M, 4);
+    if (overlap(sx, sq) || overlap(sx, sb) || overlap(sq, sb)) return BITLINEAR_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return status_of(bl::launch_quant_act(X, x_dtype, M, K, ldx, Xq, ldq, beta, as_stream(stream)));
+}
+
+int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                           const void *X, int x_dtype, int64_t ldx, const float *beta_in, void *Y, int y_dtype,
+                           int64_t ldy, void *ws, int64_t ws_bytes, int algo, void *stream)
+{
+    if (!P || !gamma || !X || !Y || !valid_layout(layout)) return BITLINEAR_ERR_INVALID_ARG;
+    if (M < 1 || M > BITLINEAR_MAX_M || N < 1 || N > (int64_t(1) << 31) || K < 1 || K > BITLINEAR_MAX_K)
+        return BITLINEAR_ERR_INVALID_ARG;
+    if (x_dtype != BITLINEAR_F32 && x_dtype != BITLINEAR_BF16 && x_dtype != BITLINEAR_I8)
+        return BITLINEAR_ERR_INVALID_ARG;
+    if (y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_BF16 && y_dtype != BITLINEAR_I32)
+        return BITLINEAR_ERR_INVALID_ARG;
+    if (ldx < K || ldy < N) return BITLINEAR_ERR_INVALID_ARG;
+    if (algo < BITLINEAR_ALGO_AUTO || algo > BITLINEAR_ALGO_GEMM_MFMA) return BITLINEAR_ERR_INVALID_ARG;
+    if ((x_dtype == BITLINEAR_I8) != (beta_in != nullptr)) return BITLINEAR_ERR_INVALID_ARG;
+    if (!aligned16(P) || (reinterpret_cast<uintptr_t>(gamma) & 3u) ||
+        (reinterpret_cast<uintptr_t>(X) % dtype_size(x_dtype)) ||
+        (reinterpret_cast<uintptr_t>(Y) % dtype_size(y_dtype)))
+        return BITLINEAR_ERR_INVALID_ARG;
+    if (x_dtype == BITLINEAR_I8 && (!aligned16(X) || ldx % 16 || (reinterpret_cast<uintptr_t>(beta_in) & 3u)))
+        return BITLINEAR_ERR_INVALID_ARG;
+
+    const int64_t need = bitlinear_forward_workspace_bytes(M, N, K, layout, x_dtype);
+    if (need > 0 && (!ws || ws_bytes < need)) return BITLINEAR_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(ws)) return BITLINEAR_ERR_INVALID_ARG;
+
+    const int64_t pb = bitlinear_packed_bytes(N, K, layout);
+    const Span sp = span_of(P, 1, pb, pb, 1), sx = span_of(X, M, ldx, K, dtype_size(x_dtype)),
+               sy = span_of(Y, M, ldy, N, dtype_size(y_dtype)), sg = span_of(gamma, 1, 1, 1, 4);
+    if (overlap(sy, sp) || overlap(sy, sx) || overlap(sy, sg)) return BITLINEAR_ERR_INVALID_ARG;
+    if (beta_in && overlap(sy, span_of(beta_in, 1, M, M, 4))) return BITLINEAR_ERR_INVALID_ARG;
+    if (need > 0) {
+        const Span sw = span_of(ws, 1, need, need, 1);
+        if (overlap(sw, sp) || overlap(sw, sx) || overlap(sw, sy) || overlap(sw, sg))
+            return BITLINEAR_ERR_INVALID_ARG;
+    }
+
+    if (algo == BITLINEAR_ALGO_AUTO) {
+        if (M <= 16)
+            algo = (layout == BITLINEAR_LAYOUT_I2 && M <= kAddSubMaxM) ? BITLINEAR_ALGO_GEMV_ADDSUB
+                                                                       : BITLINEAR_ALGO_GEMV_MFMA;
+        else
+            algo = layout == BITLINEAR_LAYOUT_I2 ? BITLINEAR_ALGO_GEMM_MFMA : BITLINEAR_ALGO_GEMV_MFMA;
+    }
+    if (algo == BITLINEAR_ALGO_GEMV_ADDSUB && (M > 16 || layout != BITLINEAR_LAYOUT_I2))
+        return BITLINEAR_ERR_UNSUPPORTED;
+    if (algo == BITLINEAR_ALGO_GEMM_MFMA && layout != BITLINEAR_LAYOUT_I2) return BITLINEAR_ERR_UNSUPPORTED;
+
+    (void)hipGetLastError();
+    hipStream_t st = as_stream(stream);
+    bl::GemvArgs a;
+    a.P = P;
+    a.layout = layout;
+    a.gamma = gamma;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.Y = Y;
+    a.y_dtype = y_dtype;
+    a.ldy = ldy;
+    if (x_dtype == BITLINEAR_I8) {
+        a.Xq = static_cast<const int8_t *>(X);
+        a.ldq = ldx;
+        a.beta = beta_in;
+    } else {
+        int8_t *xq = static_cast<int8_t *>(ws);
+        float *beta = reinterpret_cast<float *>(static_cast<char *>(ws) + staged_xq_bytes(M, K));
+        const int64_t ldq = staged_ldq(K);
+        hipError_t e = bl::launch_quant_act(X, x_dtype, M, K, ldx, xq, ldq, beta, st);
+        if (e != hipSuccess) return BITLINEAR_ERR_LAUNCH;
+        a.Xq = xq;
+        a.ldq = ldq;
+        a.beta = beta;
+    }
+    hipError_t e;
+    switch (algo) {
+    case BITLINEAR_ALGO_GEMV_ADDSUB: e = bl::launch_gemv_addsub(a, st); break;
+    case BITLINEAR_ALGO_GEMV_MFMA: e = bl::launch_gemv_mfma(a, st); break;
+    default: e = bl::launch_gemm_mfma(a, st); break;
+    }
+    return status_of(e);
+}
+
+int bitlinear_forward(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                      const void *X, int x_dtype, int64_t ldx, const float *beta_in, void *Y, int y_dtype,
+                      int64_t ldy, void *ws, int64_t ws_bytes, void *stream)
+{
+    return bitlinear_forward_algo(P, layout, gamma, M, N, K, X, x_dtype, ldx, beta_in, Y, y_dtype, ldy, ws,
+                                  ws_bytes, BITLINEAR_ALGO_AUTO, stream);
+}
+
+} // extern "C"

@@ -1,0 +1,84 @@
+// common.h -- device helpers shared by the libbitlinear kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// dtype / layout codes of the C ABI (bitlinear.h).
+enum { DT_F32 = 0, DT_BF16 = 1, DT_I8 = 2, DT_I32 = 3 };
+enum { LAYOUT_I2 = 0, LAYOUT_B3 = 1 };
+
+// A chunk is 16 bytes: one row's weights for one k-block; a tile is 16 rows.
+constexpr int TILE_ROWS = 16;
+constexpr int CHUNK_BYTES = 16;
+constexpr int I2_KBLOCK = 64;
+constexpr int B3_KBLOCK = 80;
+// Word of four "T = 0" codes (c = 1 in every 2-bit field): padding for i2.
+constexpr uint32_t I2_ZERO_WORD = 0x55555555u;
+// Byte of five "T = 0" codes in base 3: 1*81 + 1*27 + 1*9 + 1*3 + 1.
+constexpr uint32_t B3_ZERO_BYTE = 121u;
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b)
+{
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// binary32 -> bfloat16 bits, round to nearest even (finite values).
+__device__ __forceinline__ uint16_t float_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    uint32_t lsb = (u >> 16) & 1u;
+    return static_cast<uint16_t>((u + 0x7fffu + lsb) >> 16);
+}
+
+// Four 2-bit offset codes c in {0,1,2}, one per byte, to signed bytes T = c - 1:
+// c + 0x7f stays below 0x100 in every byte (no carries), and xor 0x80 maps
+// 0x7f, 0x80, 0x81 to 0xff, 0x00, 0x01.
+__device__ __forceinline__ uint32_t codes_to_signed(uint32_t c)
+{
+    return (c + 0x7f7f7f7fu) ^ 0x80808080u;
+}
+
+// The four words of signed weights held in one i2 word (16 weights, natural
+// k order): word s covers weights 4s .. 4s+3 of the word's 16.
+__device__ __forceinline__ v4i i2_word_to_signed16(uint32_t w)
+{
+    v4i r;
+    r[0] = static_cast<int>(codes_to_signed(w & 0x03030303u));
+    r[1] = static_cast<int>(codes_to_signed((w >> 2) & 0x03030303u));
+    r[2] = static_cast<int>(codes_to_signed((w >> 4) & 0x03030303u));
+    r[3] = static_cast<int>(codes_to_signed((w >> 6) & 0x03030303u));
+    return r;
+}
+
+// Per-token rescale factor (gamma * beta) / 127 in binary32.
+__device__ __forceinline__ float token_scale(float gamma, float beta)
+{
+    float gb = gamma * beta;
+    return gb / 127.0f;
+}
+
+// Store one output element: raw accumulator, or float(acc) * r in fp32 / bf16.
+__device__ __forceinline__ void store_out(void *Y, int y_dtype, int64_t ldy, int64_t m, int64_t n, int acc,
+                                          float r)
+{
+    const int64_t idx = m * ldy + n;
+    if (y_dtype == DT_I32) {
+        static_cast<int *>(Y)[idx] = acc;
+    } else {
+        float y = static_cast<float>(acc) * r;
+        if (y_dtype == DT_F32)
+            static_cast<float *>(Y)[idx] = y;
+        else
+            static_cast<uint16_t *>(Y)[idx] = float_to_bf16_rne(y);
+    }
+}
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+} // namespace bl

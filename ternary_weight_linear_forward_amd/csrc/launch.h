@@ -1,0 +1,39 @@
+// launch.h -- host-side launchers of the libbitlinear kernels (internal).
+// Each launcher enqueues its kernels on 'stream' and returns hipGetLastError().
+// Arguments are validated by api.cpp before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+hipError_t launch_quantize_weights(const float *W, int64_t N, int64_t K, int64_t ldw, int8_t *T, float *gamma,
+                                   void *ws, hipStream_t stream);
+
+hipError_t launch_pack(const int8_t *T, int64_t N, int64_t K, int64_t ldt, int layout, uint8_t *P,
+                       hipStream_t stream);
+
+hipError_t launch_quant_act(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int8_t *Xq,
+                            int64_t ldq, float *beta, hipStream_t stream);
+
+// Product + rescale on int8 activations Xq [M x K] (row stride ldq, 16-byte
+// aligned rows) with per-token beta.
+struct GemvArgs {
+    const uint8_t *P;
+    int layout;
+    const float *gamma;
+    int64_t M, N, K;
+    const int8_t *Xq;
+    int64_t ldq;
+    const float *beta;
+    void *Y;
+    int y_dtype;
+    int64_t ldy;
+};
+
+hipError_t launch_gemv_addsub(const GemvArgs &a, hipStream_t stream);
+hipError_t launch_gemv_mfma(const GemvArgs &a, hipStream_t stream);
+hipError_t launch_gemm_mfma(const GemvArgs &a, hipStream_t stream);
+
+} // namespace bl

@@ -1,0 +1,138 @@
+"""The C ABI without a GPU: the library loads, exports every function declared
+in include/bitlinear.h, and rejects invalid arguments on the host before any
+HIP call.  Pointer arguments here are fake addresses that are never touched."""
+import os
+import re
+
+import pytest
+
+from ternary_weight_linear_forward_amd import bitlinear as bl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+A = 0x10000  # 16-byte aligned fake device addresses, far apart
+B = 0x20000000
+C = 0x40000000
+D = 0x60000000
+E = 0x80000000
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    declared = header_functions()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(bl._lib, name), name
+    assert sorted(declared) == sorted(bl.EXPORTED)
+
+
+def test_status_strings_and_version():
+    assert bl.bitlinear_status_string(bl.OK) == "ok"
+    for s in range(1, 6):
+        assert bl.bitlinear_status_string(s) not in ("ok", "unknown status")
+    assert bl.bitlinear_status_string(99) == "unknown status"
+    assert bl.bitlinear_version() >= 100
+
+
+def test_size_queries():
+    assert bl.bitlinear_packed_bytes(3200, 3200, bl.LAYOUT_I2) == 3200 * 3200 // 4
+    assert bl.bitlinear_packed_bytes(28672, 8192, bl.LAYOUT_B3) == 28672 * 103 * 16
+    assert bl.bitlinear_packed_bytes(17, 65, bl.LAYOUT_I2) == 2 * 2 * 256
+    assert bl.bitlinear_packed_bytes(0, 4, bl.LAYOUT_I2) == -1
+    assert bl.bitlinear_packed_bytes(4, bl.MAX_K + 1, bl.LAYOUT_I2) == -1
+    assert bl.bitlinear_packed_bytes(4, 4, 7) == -1
+    assert bl.bitlinear_quantize_weights_workspace_bytes(10, 10) == 2048
+    assert bl.bitlinear_quantize_weights_workspace_bytes(1 << 21, 1 << 20) == -1
+    assert bl.bitlinear_forward_workspace_bytes(16, 100, 100, bl.LAYOUT_I2, bl.I8) == 0
+    assert bl.bitlinear_forward_workspace_bytes(16, 100, 100, bl.LAYOUT_I2, bl.BF16) >= 16 * 100 + 64
+    assert bl.bitlinear_forward_workspace_bytes(16, 100, 100, bl.LAYOUT_I2, bl.I32) == -1
+
+
+def qw(**kw):
+    a = dict(W=A, N=64, K=64, ldw=64, T=B, gamma=C, ws=D, ws_bytes=2048, stream=None)
+    a.update(kw)
+    return bl.bitlinear_quantize_weights(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), bl.ERR_INVALID_ARG), (dict(T=None), bl.ERR_INVALID_ARG), (dict(gamma=None), bl.ERR_INVALID_ARG),
+    (dict(N=0), bl.ERR_INVALID_ARG), (dict(K=-1), bl.ERR_INVALID_ARG), (dict(ldw=63), bl.ERR_INVALID_ARG),
+    (dict(N=1 << 21, K=1 << 20, ldw=1 << 20), bl.ERR_INVALID_ARG),
+    (dict(ws=None), bl.ERR_WORKSPACE), (dict(ws_bytes=2047), bl.ERR_WORKSPACE),
+    (dict(ws=D + 8), bl.ERR_INVALID_ARG), (dict(W=A + 2), bl.ERR_INVALID_ARG),
+    (dict(T=A + 64), bl.ERR_INVALID_ARG),       # T overlaps W
+    (dict(ws=A), bl.ERR_INVALID_ARG),           # workspace overlaps W
+])
+def test_quantize_weights_rejects(kw, status):
+    assert qw(**kw) == status
+
+
+def pk(**kw):
+    a = dict(T=A, N=64, K=64, ldt=64, layout=bl.LAYOUT_I2, P=B, stream=None)
+    a.update(kw)
+    return bl.bitlinear_pack(**a)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=None), dict(P=None), dict(layout=2), dict(N=0), dict(K=0), dict(K=bl.MAX_K + 1, ldt=bl.MAX_K + 1),
+    dict(ldt=10), dict(P=B + 4), dict(P=A + 16),
+])
+def test_pack_rejects(kw):
+    assert pk(**kw) == bl.ERR_INVALID_ARG
+
+
+def qa(**kw):
+    a = dict(X=A, x_dtype=bl.BF16, M=16, K=100, ldx=100, Xq=B, ldq=112, beta=C, stream=None)
+    a.update(kw)
+    return bl.bitlinear_quantize_act(**a)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(X=None), dict(Xq=None), dict(beta=None), dict(x_dtype=bl.I8), dict(x_dtype=bl.I32), dict(M=0),
+    dict(M=bl.MAX_M + 1), dict(K=0), dict(K=bl.MAX_K + 1, ldx=bl.MAX_K + 1, ldq=bl.MAX_K + 16), dict(ldx=99),
+    dict(ldq=104), dict(ldq=96), dict(Xq=B + 8), dict(X=A + 1), dict(beta=C + 2), dict(Xq=A + 32),
+])
+def test_quantize_act_rejects(kw):
+    assert qa(**kw) == bl.ERR_INVALID_ARG
+
+
+def fw(**kw):
+    a = dict(P=A, layout=bl.LAYOUT_I2, gamma=B, M=4, N=64, K=64, X=C, x_dtype=bl.BF16, ldx=64, beta_in=None,
+             Y=D, y_dtype=bl.F32, ldy=64, ws=E, ws_bytes=1 << 20, algo=bl.ALGO_AUTO, stream=None)
+    a.update(kw)
+    return bl.bitlinear_forward_algo(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=None), bl.ERR_INVALID_ARG), (dict(gamma=None), bl.ERR_INVALID_ARG), (dict(X=None), bl.ERR_INVALID_ARG),
+    (dict(Y=None), bl.ERR_INVALID_ARG), (dict(layout=5), bl.ERR_INVALID_ARG), (dict(M=0), bl.ERR_INVALID_ARG),
+    (dict(M=bl.MAX_M + 1), bl.ERR_INVALID_ARG), (dict(N=0), bl.ERR_INVALID_ARG), (dict(K=0), bl.ERR_INVALID_ARG),
+    (dict(K=bl.MAX_K + 1, ldx=bl.MAX_K + 1), bl.ERR_INVALID_ARG), (dict(x_dtype=bl.I32), bl.ERR_INVALID_ARG),
+    (dict(y_dtype=bl.I8), bl.ERR_INVALID_ARG), (dict(ldx=63), bl.ERR_INVALID_ARG), (dict(ldy=63), bl.ERR_INVALID_ARG),
+    (dict(algo=9), bl.ERR_INVALID_ARG), (dict(algo=-1), bl.ERR_INVALID_ARG),
+    (dict(x_dtype=bl.I8), bl.ERR_INVALID_ARG),                      # I8 needs beta_in
+    (dict(beta_in=A + 0x100000), bl.ERR_INVALID_ARG),               # bf16 must not pass beta_in
+    (dict(x_dtype=bl.I8, beta_in=B + 64, ldx=72), bl.ERR_INVALID_ARG),  # I8 rows must be 16-aligned
+    (dict(x_dtype=bl.I8, beta_in=B + 64, X=C + 8), bl.ERR_INVALID_ARG),
+    (dict(P=A + 8), bl.ERR_INVALID_ARG), (dict(Y=D + 2), bl.ERR_INVALID_ARG),
+    (dict(ws=None), bl.ERR_WORKSPACE), (dict(ws_bytes=64), bl.ERR_WORKSPACE), (dict(ws=E + 8), bl.ERR_INVALID_ARG),
+    (dict(Y=C), bl.ERR_INVALID_ARG),                                # Y overlaps X
+    (dict(Y=A), bl.ERR_INVALID_ARG),                                # Y overlaps P
+    (dict(ws=C), bl.ERR_INVALID_ARG),                               # workspace overlaps X
+    (dict(algo=bl.ALGO_GEMV_ADDSUB, M=17), bl.ERR_UNSUPPORTED),
+    (dict(algo=bl.ALGO_GEMV_ADDSUB, layout=bl.LAYOUT_B3), bl.ERR_UNSUPPORTED),
+    (dict(algo=bl.ALGO_GEMM_MFMA, layout=bl.LAYOUT_B3), bl.ERR_UNSUPPORTED),
+])
+def test_forward_rejects(kw, status):
+    assert fw(**kw) == status
+
+
+def test_forward_plain_entry_validates_too():
+    assert bl.bitlinear_forward(None, 0, B, 4, 64, 64, C, bl.BF16, 64, None, D, bl.F32, 64, E, 1 << 20, None) \
+        == bl.ERR_INVALID_ARG

@@ -1,0 +1,115 @@
+"""GPU parity at the full layer sizes of the pages' 3B and 70B models, with the
+kernels the benchmark times (automatic dispatch).  The weight path (gamma, T,
+packed bytes) and the activation quantiser are compared in full; the product
+and rescale on a sample of output columns that the oracle computes one by one,
+plus a property that holds for every element (the fp32 output is the rescale
+of the int32 output)."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from ternary_weight_linear_forward_amd import bitlinear as bl  # noqa: E402
+from ternary_weight_linear_forward_amd import synth, workloads  # noqa: E402
+
+from gpu_helpers import assert_f32_parity, f32_bits, to_dev, to_host  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+LAYOUTS = {"i2": bl.LAYOUT_I2, "b3": bl.LAYOUT_B3}
+_cache = {}
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def prepared(wl, li):
+    """Quantise and pack one layer on the GPU and check it in full against the oracle."""
+    key = (wl.name, li)
+    if key in _cache:
+        return _cache[key]
+    _cache.clear()
+    layer = wl.layers[li]
+    log("prepare", wl.name, layer)
+    w = synth.latent_weights(layer.N, layer.K, seed=workloads.seed_for(wl, li, 0))
+    wd = to_dev(w)
+    T, gamma = bl.quantize_weights(wd)
+    t_ref, g_ref = oracle.quantize_weights(w)
+    assert to_host(gamma).view(np.uint32)[0] == np.array(g_ref, np.float32).view(np.uint32)
+    assert np.array_equal(to_host(T), t_ref)
+    packed = {}
+    for name in wl.layouts:
+        P = bl.pack(T, LAYOUTS[name])
+        assert np.array_equal(to_host(P), oracle.pack(t_ref, LAYOUTS[name])), name
+        packed[name] = P
+    del wd, T
+    _cache[key] = (t_ref, g_ref, gamma, packed)
+    return _cache[key]
+
+
+def check_forward(wl, li, M, layout, act="normal"):
+    layer = wl.layers[li]
+    t_ref, g_ref, gamma, packed = prepared(wl, li)
+    log("forward", wl.name, layer.name, "M", M, layout)
+    seed = workloads.seed_for(wl, li, 1) + M
+    if act == "student_t":
+        x = synth.activations_student_t_bf16(M, layer.K, seed=seed)
+    else:
+        x = synth.activations_bf16(M, layer.K, seed=seed)
+    xd = to_dev(x)
+    P = packed[layout]
+    acc = to_host(bl.forward(P, LAYOUTS[layout], gamma, xd, layer.N, layer.K, y_dtype=torch.int32))
+    y = to_host(bl.forward(P, LAYOUTS[layout], gamma, xd, layer.N, layer.K, y_dtype=torch.float32))
+    q, beta = oracle.quantize_act(x)
+    # sampled columns: both ends, every tile boundary region, random interior
+    r = synth.rng(seed)
+    cols = np.unique(np.concatenate([[0, 15, 16, layer.N - 1], r.integers(0, layer.N, 60)]))
+    acc_ref = oracle.matmul(q, t_ref[cols])
+    assert np.array_equal(acc[:, cols], acc_ref)
+    assert_f32_parity(y[:, cols], oracle.rescale(acc_ref, beta, g_ref))
+    # every element: the fp32 output is the rescale of the exact accumulator
+    assert np.array_equal(f32_bits(y), f32_bits(oracle.rescale(acc, beta, g_ref)))
+    assert np.abs(acc.astype(np.int64)).max() <= 127 * layer.K
+
+
+def test_tiny_config_full_pipeline():
+    """The tiny workload through every entry point, compared in full."""
+    wl = workloads.TINY
+    layer = wl.layers[0]
+    w = synth.latent_weights(layer.N, layer.K, seed=workloads.seed_for(wl, 0, 0))
+    x = synth.activations_f32(wl.batches[0], layer.K, seed=workloads.seed_for(wl, 0, 1))
+    T, gamma = bl.quantize_weights(to_dev(w))
+    t_ref, g_ref = oracle.quantize_weights(w)
+    ref = oracle.forward(t_ref, g_ref, x)
+    assert np.array_equal(to_host(T), t_ref)
+    for name, lay in LAYOUTS.items():
+        P = bl.pack(T, lay)
+        assert np.array_equal(to_host(P), oracle.pack(t_ref, lay))
+        for algo in ((bl.ALGO_AUTO, bl.ALGO_GEMV_MFMA) if name == "b3" else
+                     (bl.ALGO_AUTO, bl.ALGO_GEMV_ADDSUB, bl.ALGO_GEMV_MFMA, bl.ALGO_GEMM_MFMA)):
+            acc = to_host(bl.forward(P, lay, gamma, to_dev(x), layer.N, layer.K, y_dtype=torch.int32, algo=algo))
+            assert np.array_equal(acc, ref["acc"])
+            y = to_host(bl.forward(P, lay, gamma, to_dev(x), layer.N, layer.K, algo=algo))
+            assert_f32_parity(y, ref["y"])
+    Xq, beta = bl.quantize_act(to_dev(x))
+    assert np.array_equal(to_host(Xq)[:, :layer.K], ref["q"])
+    assert np.array_equal(f32_bits(to_host(beta)), f32_bits(ref["beta"]))
+
+
+@pytest.mark.parametrize("li", [0, 4, 6], ids=["q_3200x3200", "gate_8640x3200", "down_3200x8640"])
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_decode_3b(li, M):
+    check_forward(workloads.DECODE_3B, li, M, "i2")
+
+
+@pytest.mark.parametrize("li", [0, 1, 2], ids=["3200x3200", "8640x3200", "3200x8640"])
+def test_prefill_3b(li):
+    check_forward(workloads.PREFILL_3B, li, 2048, "i2", act="student_t")
+
+
+@pytest.mark.parametrize("li", [0, 1, 4, 6], ids=["q_8192", "k_1024x8192", "gate_28672x8192", "down_8192x28672"])
+def test_llama70b(li):
+    for layout in ("i2", "b3"):
+        for M in (1, 16, 64, 176):
+            check_forward(workloads.LAYERS_70B, li, M, layout)

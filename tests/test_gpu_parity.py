@@ -1,0 +1,225 @@
+"""GPU parity: every entry point of libbitlinear against the CPU oracle,
+element by element, on seeded inputs that span several tiles, ragged tails and
+the degenerate cases.  Integer, byte and index outputs must be bit-exact; the
+fp32 output within 1e-5 relative (and, by construction, bit-identical); the
+bf16 output within 2e-2 relative (and identical).  Calls go through the C ABI
+(the ctypes binding)."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from ternary_weight_linear_forward_amd import bitlinear as bl  # noqa: E402
+from ternary_weight_linear_forward_amd import synth  # noqa: E402
+
+from gpu_helpers import (DEV, assert_bf16_parity, assert_f32_parity, f32_bits, to_dev,  # noqa: E402
+                         to_host)
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = {"i2": bl.LAYOUT_I2, "b3": bl.LAYOUT_B3}
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# weight ternarisation
+# ---------------------------------------------------------------------------
+def weight_cases():
+    yield "tiny_512x256", synth.latent_weights(512, 256, seed=1)
+    yield "ragged_17x65", synth.latent_weights(17, 65, seed=2)
+    yield "one", np.array([[0.37]], np.float32)
+    yield "ties", np.array([[0.5, 1.5, -0.5, -1.5, 0.0, 1.0, -1.0, 0.5]], np.float32)
+    yield "zeros", np.zeros((3, 40), np.float32)
+    r = synth.rng(3)
+    w = (r.standard_normal((33, 97)) * np.exp2(r.integers(-140, 40, (33, 97)))).astype(np.float32)
+    yield "wide_exponents", w
+    yield "subnormal", (r.standard_normal((8, 70)) * 1e-42).astype(np.float32)
+    yield "constant", np.where(r.random((20, 30)) < 0.5, -0.02, 0.02).astype(np.float32)
+    yield "rows_3200x3200", synth.latent_weights(3200, 3200, seed=4)
+
+
+@pytest.mark.parametrize("name,w", list(weight_cases()), ids=[c[0] for c in weight_cases()])
+def test_quantize_weights(name, w):
+    log("quantize_weights", name, w.shape)
+    T, gamma = bl.quantize_weights(to_dev(w))
+    torch.cuda.synchronize()
+    t_ref, g_ref = oracle.quantize_weights(w)
+    assert to_host(gamma).view(np.uint32)[0] == np.array(g_ref, np.float32).view(np.uint32)
+    assert np.array_equal(to_host(T), t_ref)
+
+
+def test_quantize_weights_strided():
+    w = synth.latent_weights(40, 200, seed=5)
+    wd = to_dev(w)[:, :150]  # row stride 200, K = 150
+    T, gamma = bl.quantize_weights(wd)
+    t_ref, g_ref = oracle.quantize_weights(np.ascontiguousarray(w[:, :150]))
+    assert to_host(gamma)[0] == g_ref
+    assert np.array_equal(to_host(T), t_ref)
+
+
+# ---------------------------------------------------------------------------
+# packing
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("layout", ["i2", "b3"])
+@pytest.mark.parametrize("N,K", [(1, 1), (16, 64), (17, 65), (33, 80), (48, 257), (100, 1000), (512, 256)])
+def test_pack(layout, N, K):
+    t = synth.ternary_weights(N, K, seed=N * 7 + K)
+    P = bl.pack(to_dev(t), LAYOUTS[layout])
+    assert np.array_equal(to_host(P), oracle.pack(t, LAYOUTS[layout]))
+
+
+def test_pack_strided():
+    t = synth.ternary_weights(20, 300, seed=9)
+    P = bl.pack(to_dev(t)[:, :250], bl.LAYOUT_I2)
+    assert np.array_equal(to_host(P), oracle.pack(np.ascontiguousarray(t[:, :250]), bl.LAYOUT_I2))
+
+
+# ---------------------------------------------------------------------------
+# activation quantisation
+# ---------------------------------------------------------------------------
+def act_cases():
+    yield "f32_16x256", synth.activations_f32(16, 256, seed=11)
+    yield "bf16_16x3200", synth.activations_bf16(16, 3200, seed=12)
+    yield "bf16_ragged_5x77", synth.activations_bf16(5, 77, seed=13)
+    yield "bf16_1x1", synth.activations_bf16(1, 1, seed=14)
+    yield "student_t_64x8640", synth.activations_student_t_bf16(64, 8640, seed=15)
+    x = synth.activations_f32(6, 300, seed=16)
+    x[0] = 0.0                                       # zero row
+    x[1, :7] = [127.0, 2.5, -2.5, 0.5, -0.5, 1.5, -127.0]
+    x[1, 7:] = 0.0                                   # exact ties
+    x[2] = (x[2] * 1e-40).astype(np.float32)         # subnormal row
+    x[3] = np.float32(-3.0)                          # constant row
+    yield "f32_edges", x
+
+
+@pytest.mark.parametrize("name,x", list(act_cases()), ids=[c[0] for c in act_cases()])
+def test_quantize_act(name, x):
+    log("quantize_act", name, x.shape)
+    Xq, beta = bl.quantize_act(to_dev(x))
+    q_ref, b_ref = oracle.quantize_act(x)
+    K = x.shape[1]
+    xq = to_host(Xq)
+    assert np.array_equal(xq[:, :K], q_ref)
+    assert not xq[:, K:].any()
+    assert np.array_equal(f32_bits(to_host(beta)), f32_bits(b_ref))
+
+
+# ---------------------------------------------------------------------------
+# forward: every kernel, several tiles, ragged tails
+# ---------------------------------------------------------------------------
+FWD_SHAPES = [  # (M, N, K)
+    (1, 16, 64), (1, 50, 100), (2, 333, 257), (3, 64, 1000), (4, 130, 3200), (5, 17, 65),
+    (8, 200, 640), (11, 48, 1), (16, 512, 256), (16, 100, 333),
+]
+ALGOS_SMALL = [("addsub", bl.ALGO_GEMV_ADDSUB, "i2"), ("mfma_gemv", bl.ALGO_GEMV_MFMA, "i2"),
+               ("mfma_gemv", bl.ALGO_GEMV_MFMA, "b3"), ("gemm", bl.ALGO_GEMM_MFMA, "i2"),
+               ("auto", bl.ALGO_AUTO, "i2"), ("auto", bl.ALGO_AUTO, "b3")]
+
+
+def run_forward_case(M, N, K, algo, layout, seed, x_kind="bf16", y_kinds=("i32", "f32", "bf16")):
+    t = synth.ternary_weights(N, K, seed=seed)
+    w_scale = np.float32(0.0123)
+    P = to_dev(oracle.pack(t, LAYOUTS[layout]))
+    gamma = to_dev(np.array([w_scale], np.float32))
+    if x_kind == "bf16":
+        x = synth.activations_bf16(M, K, seed=seed + 1)
+    else:
+        x = synth.activations_f32(M, K, seed=seed + 1)
+    ref = oracle.forward(t, w_scale, x)
+    xd = to_dev(x)
+    for yk in y_kinds:
+        ydt = {"i32": torch.int32, "f32": torch.float32, "bf16": torch.bfloat16}[yk]
+        Y = bl.forward(P, LAYOUTS[layout], gamma, xd, N, K, y_dtype=ydt, algo=algo)
+        y = to_host(Y)
+        if yk == "i32":
+            assert np.array_equal(y, ref["acc"]), f"acc mismatch at {np.argwhere(y != ref['acc'])[:5]}"
+        elif yk == "f32":
+            assert_f32_parity(y, ref["y"])
+        else:
+            assert_bf16_parity(y, ref["y"], oracle.f32_to_bf16(ref["y"]))
+
+
+@pytest.mark.parametrize("algo_name,algo,layout", ALGOS_SMALL, ids=[f"{a}-{l}-{c}" for a, c, l in ALGOS_SMALL])
+@pytest.mark.parametrize("M,N,K", FWD_SHAPES)
+def test_forward_small(algo_name, algo, layout, M, N, K):
+    log("forward", algo_name, layout, M, N, K)
+    run_forward_case(M, N, K, algo, layout, seed=M * 10007 + N * 31 + K)
+
+
+@pytest.mark.parametrize("algo_name,algo,layout", [("mfma_gemv", bl.ALGO_GEMV_MFMA, "i2"),
+                                                   ("mfma_gemv", bl.ALGO_GEMV_MFMA, "b3"),
+                                                   ("gemm", bl.ALGO_GEMM_MFMA, "i2")])
+@pytest.mark.parametrize("M,N,K", [(17, 40, 100), (64, 96, 512), (130, 257, 700), (256, 128, 64)])
+def test_forward_many_tokens(algo_name, algo, layout, M, N, K):
+    log("forward", algo_name, layout, M, N, K)
+    run_forward_case(M, N, K, algo, layout, seed=M * 131 + N + K)
+
+
+def test_forward_f32_input_tiny():
+    run_forward_case(16, 512, 256, bl.ALGO_AUTO, "i2", seed=77, x_kind="f32")
+
+
+def test_forward_int8_input():
+    M, N, K = 6, 80, 300
+    t = synth.ternary_weights(N, K, seed=81)
+    x = synth.activations_bf16(M, K, seed=82)
+    ref = oracle.forward(t, np.float32(0.02), x)
+    Xq, beta = bl.quantize_act(to_dev(x))
+    P = to_dev(oracle.pack(t, bl.LAYOUT_I2))
+    gamma = to_dev(np.array([0.02], np.float32))
+    for algo in (bl.ALGO_GEMV_ADDSUB, bl.ALGO_GEMV_MFMA, bl.ALGO_GEMM_MFMA):
+        Y = bl.forward(P, bl.LAYOUT_I2, gamma, Xq, N, K, beta=beta, algo=algo)
+        assert_f32_parity(to_host(Y), ref["y"])
+
+
+def test_forward_degenerate():
+    # zero activations row and all-zero weights
+    M, N, K = 4, 32, 128
+    x = synth.activations_bf16(M, K, seed=91)
+    x[2] = 0
+    t = np.zeros((N, K), np.int8)
+    P = to_dev(oracle.pack(t, bl.LAYOUT_I2))
+    gamma = to_dev(np.array([0.0], np.float32))
+    for algo in (bl.ALGO_GEMV_ADDSUB, bl.ALGO_GEMV_MFMA, bl.ALGO_GEMM_MFMA):
+        y = to_host(bl.forward(P, bl.LAYOUT_I2, gamma, to_dev(x), N, K, algo=algo))
+        assert not y.any() and not np.signbit(y).any()
+    # all +1 weights: the product is the row sum of q
+    t = np.ones((N, K), np.int8)
+    ref = oracle.forward(t, np.float32(1.0), x)
+    P = to_dev(oracle.pack(t, bl.LAYOUT_I2))
+    gamma = to_dev(np.array([1.0], np.float32))
+    for algo in (bl.ALGO_GEMV_ADDSUB, bl.ALGO_GEMV_MFMA, bl.ALGO_GEMM_MFMA):
+        acc = to_host(bl.forward(P, bl.LAYOUT_I2, gamma, to_dev(x), N, K, y_dtype=torch.int32, algo=algo))
+        assert np.array_equal(acc, ref["acc"])
+
+
+def test_forward_strided_output_and_input():
+    M, N, K = 16, 96, 200
+    t = synth.ternary_weights(N, K, seed=95)
+    x = synth.activations_bf16(M, 256, seed=96)
+    ref = oracle.forward(t, np.float32(0.5), np.ascontiguousarray(x[:, :K]))
+    P = to_dev(oracle.pack(t, bl.LAYOUT_I2))
+    gamma = to_dev(np.array([0.5], np.float32))
+    xd = to_dev(x)[:, :K]
+    out = torch.full((M, 128), -7.0, dtype=torch.float32, device=DEV)
+    for algo in (bl.ALGO_GEMV_ADDSUB, bl.ALGO_GEMV_MFMA, bl.ALGO_GEMM_MFMA):
+        bl.forward(P, bl.LAYOUT_I2, gamma, xd, N, K, algo=algo, out=out[:, :N])
+        o = to_host(out)
+        assert_f32_parity(o[:, :N], ref["y"])
+        assert np.all(o[:, N:] == -7.0)
+
+
+def test_forward_deterministic():
+    M, N, K = 16, 1024, 3200
+    t = synth.ternary_weights(N, K, seed=97)
+    x = to_dev(synth.activations_bf16(M, K, seed=98))
+    P = to_dev(oracle.pack(t, bl.LAYOUT_I2))
+    gamma = to_dev(np.array([0.01], np.float32))
+    for algo in (bl.ALGO_GEMV_ADDSUB, bl.ALGO_GEMV_MFMA, bl.ALGO_GEMM_MFMA):
+        a = to_host(bl.forward(P, bl.LAYOUT_I2, gamma, x, N, K, algo=algo))
+        b = to_host(bl.forward(P, bl.LAYOUT_I2, gamma, x, N, K, algo=algo))
+        assert np.array_equal(f32_bits(a), f32_bits(b))
