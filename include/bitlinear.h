@@ -94,8 +94,9 @@ int bitlinear_version(void);
  *       at bits 8j+2s .. 8j+2s+1, so (word >> 2s) & 0x03030303 gives the
  *       codes of 4 consecutive weights, one per byte.
  *   B3: a k-block is 80 weights, KB = ceil(K / 80).  Byte i (0..15) of a chunk
- *       holds weights kb*80 + 5i + t (t = 0..4) as sum_t c_t * 3^(4-t) (first
- *       weight most significant); values 243..255 never occur.
+ *       holds weights kb*80 + 16t + i (t = 0..4) as sum_t c_t * 3^(4-t)
+ *       (t = 0 most significant), so base-3 digit t of the 16 bytes covers 16
+ *       consecutive weights; values 243..255 never occur.
  * Returns the byte size of P, or -1 if N, K or layout is invalid.
  */
 int64_t bitlinear_packed_bytes(int64_t N, int64_t K, int layout);

@@ -165,9 +165,10 @@ int oracle_ternarize(const float *w, int64_t count, float gamma, int8_t *t)
  *
  * "b3" (base 3, 5 weights per byte): a k-block is 80 weights.  The chunk of
  * row n and k-block kb starts at byte ((n/16)*KB3 + kb)*256 + (n%16)*16,
- * KB3 = ceil(K/80).  Its byte i (i = 0..15) holds weights kb*80 + 5i + t
- * (t = 0..4) as sum_t c_t * 3^(4 - t): the first weight is the most
- * significant base-3 digit.  Values 243..255 are never written.
+ * KB3 = ceil(K/80).  Its byte i (i = 0..15) holds the five weights
+ * kb*80 + 16t + i (t = 0..4) as sum_t c_t * 3^(4 - t): weight t = 0 is the
+ * most significant base-3 digit.  So digit t of bytes 0..15 covers 16
+ * consecutive weights.  Values 243..255 are never written.
  */
 static int8_t t_at(const int8_t *t, int64_t N, int64_t K, int64_t n, int64_t k)
 {
@@ -226,7 +227,7 @@ int oracle_pack_b3(const int8_t *t, int64_t N, int64_t K, uint8_t *p)
             for (int i = 0; i < 16; ++i) {
                 unsigned byte = 0;
                 for (int d = 0; d < 5; ++d) {
-                    int8_t v = t_at(t, N, K, n, kb * 80 + 5 * i + d);
+                    int8_t v = t_at(t, N, K, n, kb * 80 + 16 * d + i);
                     if (v < -1 || v > 1) return ORACLE_ERR_ARG;
                     byte = byte * 3 + (unsigned)(v + 1);
                 }
@@ -242,10 +243,10 @@ int oracle_unpack_b3(const uint8_t *p, int64_t N, int64_t K, int8_t *t)
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; ++k) {
             int64_t kb = k / 80, r = k % 80;
-            unsigned byte = p[((n / 16) * KB + kb) * 256 + (n % 16) * 16 + r / 5];
+            unsigned byte = p[((n / 16) * KB + kb) * 256 + (n % 16) * 16 + r % 16];
             if (byte > 242) return ORACLE_ERR_CODE;
             unsigned digit = byte;
-            for (int d = 4; d > (int)(r % 5); --d) digit /= 3;
+            for (int d = 4; d > (int)(r / 16); --d) digit /= 3;
             t[n * K + k] = (int8_t)((int)(digit % 3) - 1);
         }
     return ORACLE_OK;

@@ -184,7 +184,8 @@ def test_pack_i2_hand_word():
 def test_pack_b3_hand_bytes():
     v = HV["pack_b3_bytes"]
     for grp, want in zip(v["groups"], v["bytes"]):
-        t = np.array([grp], np.int8)
+        t = np.zeros((1, 80), np.int8)
+        t[0, [0, 16, 32, 48, 64]] = grp
         p = oracle.pack(t, oracle.LAYOUT_B3)
         assert p[0] == want
         assert np.all(p[1:16] == 121) and np.all(p[16:] == 121)
@@ -193,9 +194,13 @@ def test_pack_b3_hand_bytes():
 def test_pack_b3_bijection_over_all_groups():
     groups = np.array(np.meshgrid(*[[-1, 0, 1]] * 5, indexing="ij")).reshape(5, -1).T.astype(np.int8)
     assert groups.shape == (243, 5)
-    t = groups.reshape(1, -1)  # one row of 1215 weights = 243 groups of 5
+    # group j goes to byte j % 16 of k-block j // 16: weights kb*80 + 16t + i
+    KB = (243 + 15) // 16
+    t = np.zeros((1, KB * 80), np.int8)
+    for j, grp in enumerate(groups):
+        kb, i = divmod(j, 16)
+        t[0, [kb * 80 + 16 * d + i for d in range(5)]] = grp
     p = oracle.pack(t, oracle.LAYOUT_B3)
-    KB = (t.shape[1] + 79) // 80
     codes = []
     for kb in range(KB):
         codes.extend(p[kb * 256: kb * 256 + 16].tolist())
