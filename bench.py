@@ -97,7 +97,7 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] packed set {set_bytes/1e6:.1f} MB x {ncopies} copies", file=sys.stderr, flush=True)
 
-    # ---- activations and outputs --------------------------------------------
+    # ---- activations, outputs, workspaces --------------------------------------
     act = synth.activations_student_t_bf16 if wl.act_dist == "student_t" else synth.activations_bf16
     jobs = []
     for M in batches:
@@ -105,47 +105,27 @@ def main():
             layer = L["layer"]
             x = act(M, layer.K, seed=workloads.seed_for(wl, li, 1) + M)
             xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
-            ldq = (layer.K + 63) // 64 * 64
+            nws = bl.bitlinear_forward_workspace_bytes(M, layer.N, layer.K, layout, bl.BF16)
             jobs.append({
                 "M": M, "L": L, "x": xd,
-                "xq": torch.empty((M, ldq), dtype=torch.int8, device=dev),
-                "beta": torch.empty(M, dtype=torch.float32, device=dev),
+                "ws": torch.empty(max(nws, 16), dtype=torch.uint8, device=dev), "nws": nws,
                 "y": torch.empty((M, layer.N), dtype=torch.float32, device=dev),
             })
     torch.cuda.synchronize()
 
-    def algo_for(M):
-        # the kernel bitlinear_forward picks automatically (mirrors its dispatch)
-        if M <= 16:
-            return bl.ALGO_GEMV_ADDSUB if (layout == bl.LAYOUT_I2 and M <= 4) else bl.ALGO_GEMV_MFMA
-        return bl.ALGO_GEMM_MFMA if layout == bl.LAYOUT_I2 else bl.ALGO_GEMV_MFMA
-
-    def kernel_name(M):
-        a = algo_for(M)
-        if a == bl.ALGO_GEMV_ADDSUB:
-            mt = 1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8 if M <= 8 else 16
-            return f"k_gemv_addsub<{mt}>"
-        if a == bl.ALGO_GEMV_MFMA:
-            return f"k_gemv_mfma<{layout}>"
-        return "k_gemm_mfma_i2"
-
-    def launch_job(j, copy, sidx):
+    def launch_job(j, copy):
+        """The user path: one fused bitlinear_forward (quantiser + product + rescale)."""
         L = j["L"]
         layer = L["layer"]
-        s = stream.cuda_stream
-        st = bl.bitlinear_quantize_act(j["x"].data_ptr(), bl.BF16, j["M"], layer.K, j["x"].stride(0),
-                                       j["xq"].data_ptr(), j["xq"].stride(0), j["beta"].data_ptr(), s)
+        st = bl.bitlinear_forward(L["P"][copy].data_ptr(), layout, L["gamma"].data_ptr(), j["M"], layer.N, layer.K,
+                                  j["x"].data_ptr(), bl.BF16, j["x"].stride(0), None, j["y"].data_ptr(), bl.F32,
+                                  j["y"].stride(0), j["ws"].data_ptr(), j["nws"], stream.cuda_stream)
         if st:
-            raise bl.BitlinearError(st, "quantize_act")
-        st = bl.bitlinear_forward_algo(L["P"][copy].data_ptr(), layout, L["gamma"].data_ptr(), j["M"], layer.N,
-                                       layer.K, j["xq"].data_ptr(), bl.I8, j["xq"].stride(0), j["beta"].data_ptr(),
-                                       j["y"].data_ptr(), bl.F32, j["y"].stride(0), None, 0, algo_for(j["M"]), s)
-        if st:
-            raise bl.BitlinearError(st, "forward")
+            raise bl.BitlinearError(st, "bitlinear_forward")
 
     def step(copy):
-        for sidx, j in enumerate(jobs):
-            launch_job(j, copy, sidx)
+        for j in jobs:
+            launch_job(j, copy)
 
     # ---- capture one graph per weight copy -----------------------------------
     graphs = []
@@ -158,7 +138,7 @@ def main():
                 step(c)
             graphs.append(g)
     torch.cuda.synchronize()
-    print(f"[bench] captured {len(graphs)} graphs of {2 * len(jobs)} kernels", file=sys.stderr, flush=True)
+    print(f"[bench] captured {len(graphs)} graphs of {len(jobs)} forwards", file=sys.stderr, flush=True)
 
     with torch.cuda.stream(stream):
         for k in range(args.warmup):
@@ -182,6 +162,31 @@ def main():
     tops = ops_per_step / (step_ms * 1e-3) / 1e12
 
     # ---- roofline: HIP events around every launch of each product kernel -----
+    # bitlinear_forward runs a quantiser kernel, then the product kernel.  To
+    # time the product kernel alone the same two steps are issued through the
+    # split entry points, in the same way bitlinear_forward dispatches them.
+    def plan(M):
+        if M <= 16 and layout == bl.LAYOUT_I2 and M <= 4:
+            return "rowmajor", bl.ALGO_GEMV_ADDSUB, f"k_gemv_addsub<{1 if M <= 1 else 2 if M <= 2 else 4}>"
+        if M <= 16 or layout == bl.LAYOUT_B3:
+            if M > 4:
+                return "tiled", bl.ALGO_GEMV_MFMA, f"k_gemv_mfma<{layout},tiled>"
+            return "rowmajor", bl.ALGO_GEMV_MFMA, f"k_gemv_mfma<{layout},rowmajor>"
+        return "rowmajor", bl.ALGO_GEMM_MFMA, "k_gemm_mfma_i2"
+
+    for j in jobs:
+        layer = j["L"]["layer"]
+        kind, algo, name = plan(j["M"])
+        j["plan"] = (kind, algo, name)
+        if kind == "tiled":
+            nb = bl.bitlinear_act_tiled_bytes(j["M"], layer.K, layout)
+            j["xq"] = torch.empty(nb, dtype=torch.int8, device=dev)
+            j["ldq"] = 0
+        else:
+            j["ldq"] = (layer.K + 63) // 64 * 64
+            j["xq"] = torch.empty((j["M"], j["ldq"]), dtype=torch.int8, device=dev)
+        j["beta"] = torch.empty(j["M"], dtype=torch.float32, device=dev)
+
     def gemv_bytes(j):
         layer = j["L"]["layer"]
         return j["L"]["P"][0].numel() + j["M"] * layer.K + 4 * j["M"] + 4 + 4 * j["M"] * layer.N
@@ -194,20 +199,30 @@ def main():
         if hasattr(torch.cuda, "_sleep"):
             torch.cuda._sleep(50_000_000)  # hold the stream while the host queues every launch
         for r in range(reps):
-            for sidx, j in enumerate(jobs):
+            for j in jobs:
                 L = j["L"]
                 layer = L["layer"]
+                kind, algo, name = j["plan"]
                 s = stream.cuda_stream
-                bl.bitlinear_quantize_act(j["x"].data_ptr(), bl.BF16, j["M"], layer.K, j["x"].stride(0),
-                                          j["xq"].data_ptr(), j["xq"].stride(0), j["beta"].data_ptr(), s)
+                if kind == "tiled":
+                    bl.bitlinear_quantize_act_tiled(j["x"].data_ptr(), bl.BF16, j["M"], layer.K, j["x"].stride(0),
+                                                    layout, j["xq"].data_ptr(), j["xq"].numel(),
+                                                    j["beta"].data_ptr(), s)
+                    xdt = bl.I8_TILED
+                else:
+                    bl.bitlinear_quantize_act(j["x"].data_ptr(), bl.BF16, j["M"], layer.K, j["x"].stride(0),
+                                              j["xq"].data_ptr(), j["ldq"], j["beta"].data_ptr(), s)
+                    xdt = bl.I8
                 ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 ea.record(stream)
-                bl.bitlinear_forward_algo(L["P"][r % ncopies].data_ptr(), layout, L["gamma"].data_ptr(), j["M"],
-                                          layer.N, layer.K, j["xq"].data_ptr(), bl.I8, j["xq"].stride(0),
-                                          j["beta"].data_ptr(), j["y"].data_ptr(), bl.F32, j["y"].stride(0), None,
-                                          0, algo_for(j["M"]), s)
+                st = bl.bitlinear_forward_algo(L["P"][r % ncopies].data_ptr(), layout, L["gamma"].data_ptr(),
+                                               j["M"], layer.N, layer.K, j["xq"].data_ptr(), xdt, j["ldq"],
+                                               j["beta"].data_ptr(), j["y"].data_ptr(), bl.F32, j["y"].stride(0),
+                                               None, 0, algo, s)
                 eb.record(stream)
-                marks.append((kernel_name(j["M"]), ea, eb, gemv_bytes(j), 2 * j["M"] * layer.N * layer.K))
+                if st:
+                    raise bl.BitlinearError(st, "forward (instrumented)")
+                marks.append((name, ea, eb, gemv_bytes(j), 2 * j["M"] * layer.N * layer.K))
         torch.cuda.synchronize()
     for name, ea, eb, nbytes, nops in marks:
         d = per_kernel.setdefault(name, {"ms": 0.0, "bytes": 0, "ops": 0, "launches": 0})

@@ -60,8 +60,9 @@ typedef enum {
 typedef enum {
     BITLINEAR_F32 = 0,
     BITLINEAR_BF16 = 1,
-    BITLINEAR_I8 = 2,
-    BITLINEAR_I32 = 3
+    BITLINEAR_I8 = 2,      /* int8, row-major                                       */
+    BITLINEAR_I32 = 3,
+    BITLINEAR_I8_TILED = 4 /* int8 in the tiled activation layout (see below)      */
 } bitlinear_dtype_t;
 
 typedef enum {
@@ -72,7 +73,7 @@ typedef enum {
 typedef enum {
     BITLINEAR_ALGO_AUTO = 0,        /* pick by M and layout                                 */
     BITLINEAR_ALGO_GEMV_ADDSUB = 1, /* vector-ALU add/subtract GEMV, M <= 16                */
-    BITLINEAR_ALGO_GEMV_MFMA = 2,   /* 16-token int8 matrix-core tiles, M <= 16             */
+    BITLINEAR_ALGO_GEMV_MFMA = 2,   /* 16-token int8 matrix-core tiles, any M (token groups) */
     BITLINEAR_ALGO_GEMM_MFMA = 3    /* LDS-tiled int8 matrix-core GEMM, any M (i2 layout)   */
 } bitlinear_algo_t;
 
@@ -145,14 +146,44 @@ int bitlinear_quantize_act(const void *X, int x_dtype, int64_t M, int64_t K, int
                            int64_t ldq, float *beta, void *stream);
 
 /*
+ * Tiled activation layout (this library's convention): the int8 activations
+ * as the operands of the matrix-core product, 1 KiB per operand.  With
+ * S = 256 weights per k-step for I2 (320 for B3), F = 4 operands per k-step
+ * for I2 (5 for B3), nsteps = ceil(K / S) and G = ceil(M / 16) token groups,
+ * q[m][k] with m = 16*tg + i, k = s*S + g*(S/4) + 16*d + e (g in 0..3,
+ * d in 0..F-1, e in 0..15) is stored at byte
+ *     (((tg * nsteps + s) * F + d) * 64 + g * 16 + i) * 16 + e
+ * and every byte outside [0, M) x [0, K) is 0.  Size: G * nsteps * F * 1024.
+ * Returns that size, or -1 if an argument is invalid.
+ */
+int64_t bitlinear_act_tiled_bytes(int64_t M, int64_t K, int layout);
+
+/*
+ * Per-token absmax int8 quantisation (as bitlinear_quantize_act) written in
+ * the tiled activation layout for 'layout'.
+ *   Xt     bitlinear_act_tiled_bytes(M, K, layout) bytes, 16-byte aligned;
+ *          every byte is written (padding with 0).
+ *   beta   fp32 [M].
+ * Quantising once and passing Xt to several forwards (x_dtype I8_TILED) lets
+ * BitLinears that share an input (q, k and v, or gate and up) skip the
+ * quantiser.
+ */
+int bitlinear_quantize_act_tiled(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int layout,
+                                 int8_t *Xt, int64_t xt_bytes, float *beta, void *stream);
+
+/*
  * BitLinear forward: Y = rescale(quant(X) (x) T^T), T given packed in P.
  *   P        packed weights of T [N x K] in 'layout' (16-byte aligned).
  *   gamma    1 fp32 (device): the weight scale returned by quantize_weights.
  *   X        x_dtype F32 or BF16: quantised per token inside the call (the
  *            quantiser is fused with the product; its int8 output is staged
  *            in ws).  x_dtype I8: X is already quantised (16-byte aligned,
- *            ldx % 16 == 0) and beta_in (fp32 [M], device) gives beta.
- *   beta_in  required iff x_dtype == I8, else must be NULL.
+ *            ldx % 16 == 0, M rows of ldx bytes readable) and beta_in (fp32
+ *            [M], device) gives beta.  x_dtype I8_TILED: X is
+ *            bitlinear_act_tiled_bytes(M, K, layout) bytes in the tiled
+ *            activation layout of the same 'layout' (ldx is ignored) and
+ *            beta_in gives beta; only the matrix-core GEMV takes it.
+ *   beta_in  required iff x_dtype is I8 or I8_TILED, else must be NULL.
  *   Y        [M x N], y_dtype F32, BF16 (round to nearest even), or I32 (the
  *            exact accumulators acc, no rescale); row stride ldy >= N.
  *   ws       >= bitlinear_forward_workspace_bytes(M, N, K, layout, x_dtype)

@@ -20,11 +20,33 @@ LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m ternary_weight_linear_forward_amd.build`")
 
+# torch wheels bundle their own HIP runtime.  Load it first so that the
+# library's libamdhip64.so.7 dependency binds to that same runtime: two HIP
+# runtimes in one process would not share devices, streams or allocations.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
+
 _lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes_loaded() -> list:
+    try:
+        with open(f"/proc/{os.getpid()}/maps") as f:
+            paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return []
+    return sorted({os.path.realpath(p) for p in paths})
+
+
+if len(_hip_runtimes_loaded()) > 1:
+    raise ImportError("two HIP runtimes are loaded in this process "
+                      f"({', '.join(_hip_runtimes_loaded())}); import torch before loading libbitlinear")
 
 # --- enums (bitlinear.h) ---------------------------------------------------
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_DEVICE = range(6)
-F32, BF16, I8, I32 = range(4)
+F32, BF16, I8, I32, I8_TILED = range(5)
 LAYOUT_I2, LAYOUT_B3 = 0, 1
 ALGO_AUTO, ALGO_GEMV_ADDSUB, ALGO_GEMV_MFMA, ALGO_GEMM_MFMA = range(4)
 MAX_K = 131072
@@ -40,6 +62,8 @@ _SIGNATURES = {
     "bitlinear_packed_bytes": ([_I64, _I64, _INT], _I64),
     "bitlinear_quantize_weights_workspace_bytes": ([_I64, _I64], _I64),
     "bitlinear_forward_workspace_bytes": ([_I64, _I64, _I64, _INT, _INT], _I64),
+    "bitlinear_act_tiled_bytes": ([_I64, _I64, _INT], _I64),
+    "bitlinear_quantize_act_tiled": ([_P, _INT, _I64, _I64, _I64, _INT, _P, _I64, _P, _P], _INT),
     "bitlinear_quantize_weights": ([_P, _I64, _I64, _I64, _P, _P, _P, _I64, _P], _INT),
     "bitlinear_pack": ([_P, _I64, _I64, _I64, _INT, _P, _P], _INT),
     "bitlinear_quantize_act": ([_P, _INT, _I64, _I64, _I64, _P, _I64, _P, _P], _INT),
@@ -85,6 +109,14 @@ def bitlinear_quantize_weights_workspace_bytes(N: int, K: int) -> int:
 
 def bitlinear_forward_workspace_bytes(M: int, N: int, K: int, layout: int, x_dtype: int) -> int:
     return _lib.bitlinear_forward_workspace_bytes(M, N, K, layout, x_dtype)
+
+
+def bitlinear_act_tiled_bytes(M: int, K: int, layout: int) -> int:
+    return _lib.bitlinear_act_tiled_bytes(M, K, layout)
+
+
+def bitlinear_quantize_act_tiled(X, x_dtype, M, K, ldx, layout, Xt, xt_bytes, beta, stream) -> int:
+    return _lib.bitlinear_quantize_act_tiled(X, x_dtype, M, K, ldx, layout, Xt, xt_bytes, beta, stream)
 
 
 def bitlinear_quantize_weights(W, N, K, ldw, T, gamma, ws, ws_bytes, stream) -> int:
@@ -171,15 +203,38 @@ def quantize_act(X, stream=None):
     return Xq, beta
 
 
+def quantize_act_tiled(X, layout: int = LAYOUT_I2, stream=None):
+    """Activations X [M x K] fp32/bf16 (cuda) -> (Xt int8 in the tiled activation layout, beta fp32 [M])."""
+    torch = _torch()
+    M, K = X.shape
+    nbytes = bitlinear_act_tiled_bytes(M, K, layout)
+    if nbytes < 0:
+        raise BitlinearError(ERR_INVALID_ARG, "quantize_act_tiled")
+    Xt = torch.empty(nbytes, dtype=torch.int8, device=X.device)
+    beta = torch.empty(M, dtype=torch.float32, device=X.device)
+    _check(bitlinear_quantize_act_tiled(_ptr(X), _dtype_code(X), M, K, X.stride(0), layout, _ptr(Xt), nbytes,
+                                        _ptr(beta), _stream(stream)), "bitlinear_quantize_act_tiled")
+    return Xt, beta
+
+
 def forward(P, layout: int, gamma, X, N: int, K: int | None = None, beta=None, y_dtype=None, algo: int = ALGO_AUTO,
             ws=None, out=None, stream=None):
     """BitLinear forward.  X [M x >=K] fp32/bf16 (quantised inside the call) or
     int8 (then 'beta' is required).  Returns Y [M x N] (fp32 by default; bf16,
     or int32 raw accumulators with y_dtype=torch.int32)."""
     torch = _torch()
-    M = X.shape[0]
-    K = X.shape[1] if K is None else K
-    xdt = _dtype_code(X)
+    tiled = X.dim() == 1 and X.dtype == torch.int8
+    if tiled:
+        if K is None or beta is None:
+            raise ValueError("tiled activations need K and beta")
+        M = beta.numel()
+        xdt = I8_TILED
+        ldx = 0
+    else:
+        M = X.shape[0]
+        K = X.shape[1] if K is None else K
+        xdt = _dtype_code(X)
+        ldx = X.stride(0)
     if out is None:
         out = torch.empty((M, N), dtype=y_dtype or torch.float32, device=X.device)
     nws = bitlinear_forward_workspace_bytes(M, N, K, layout, xdt)
@@ -187,7 +242,7 @@ def forward(P, layout: int, gamma, X, N: int, K: int | None = None, beta=None, y
         raise BitlinearError(ERR_INVALID_ARG, "forward")
     if nws > 0 and (ws is None or ws.numel() < nws):
         ws = torch.empty(nws, dtype=torch.uint8, device=X.device)
-    _check(bitlinear_forward_algo(_ptr(P), layout, _ptr(gamma), M, N, K, _ptr(X), xdt, X.stride(0), _ptr(beta),
+    _check(bitlinear_forward_algo(_ptr(P), layout, _ptr(gamma), M, N, K, _ptr(X), xdt, ldx, _ptr(beta),
                                   _ptr(out), _dtype_code(out), out.stride(0), _ptr(ws) if nws > 0 else None,
                                   nws, algo, _stream(stream)), "bitlinear_forward")
     return out

@@ -18,63 +18,252 @@ __device__ __forceinline__ float load_x(const void *X, int64_t idx)
         return bf16_bits_to_float(static_cast<const uint16_t *>(X)[idx]);
 }
 
-__device__ __forceinline__ float block_max_256(float v, float *red)
+__device__ __forceinline__ float block_max(float v, float *red)
 {
     for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    const int nw = blockDim.x >> 6;
     if (lane_id() == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
-    float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float r = red[0];
+    for (int w = 1; w < nw; ++w) r = fmaxf(r, red[w]);
     __syncthreads();
     return r;
 }
 
-__device__ __forceinline__ int quant_one(float x, float s)
+__device__ __forceinline__ uint32_t quant_one(float x, float s)
 {
     float r = __builtin_rintf(x * s);
     r = r > 127.0f ? 127.0f : r;
     r = r < -127.0f ? -127.0f : r;
-    return static_cast<int>(r);
+    return static_cast<uint32_t>(static_cast<int>(r)) & 0xffu;
 }
 
-// One workgroup of 256 threads per token row; a thread handles groups of
-// 4 consecutive elements and writes them as one 32-bit word.
+// Generic path: one workgroup per token row; a thread handles groups of 4
+// consecutive elements and writes them as one 32-bit word.
 template <int XDT>
 __global__ __launch_bounds__(256) void k_quant_act(const void *__restrict__ X, int64_t K, int64_t ldx,
                                                    int8_t *__restrict__ Xq, int64_t ldq,
                                                    float *__restrict__ beta)
 {
-    __shared__ float red[4];
+    __shared__ float red[16];
     const int64_t m = blockIdx.x;
     const int64_t base = m * ldx;
     float amax = 0.0f;
-    for (int64_t k = threadIdx.x; k < K; k += 256) amax = fmaxf(amax, fabsf(load_x<XDT>(X, base + k)));
-    const float b = block_max_256(amax, red);
+    for (int64_t k = threadIdx.x; k < K; k += blockDim.x) amax = fmaxf(amax, fabsf(load_x<XDT>(X, base + k)));
+    const float b = block_max(amax, red);
     const float s = b > 0.0f ? 127.0f / b : 0.0f;
     uint32_t *qrow = reinterpret_cast<uint32_t *>(Xq + m * ldq);
     const int64_t nwords = ldq / 4;
-    for (int64_t w = threadIdx.x; w < nwords; w += 256) {
+    for (int64_t w = threadIdx.x; w < nwords; w += blockDim.x) {
         uint32_t packed = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             int64_t k = 4 * w + j;
-            int q = k < K ? quant_one(load_x<XDT>(X, base + k), s) : 0;
-            packed |= (static_cast<uint32_t>(q) & 0xffu) << (8 * j);
+            uint32_t q = k < K ? quant_one(load_x<XDT>(X, base + k), s) : 0u;
+            packed |= q << (8 * j);
         }
         qrow[w] = packed;
     }
     if (threadIdx.x == 0) beta[m] = b;
 }
 
+// Vector path (16-byte aligned rows, K a multiple of the vector width): every
+// thread issues all its 16-byte loads of the row first (one memory round
+// trip), keeps them in registers for the max and for the rounding.
+template <int XDT, int VPT>
+__global__ __launch_bounds__(256) void k_quant_act_vec(const void *__restrict__ X, int64_t K, int64_t ldx,
+                                                       int8_t *__restrict__ Xq, int64_t ldq,
+                                                       float *__restrict__ beta)
+{
+    constexpr int EPV = XDT == DT_F32 ? 4 : 8; // elements per 16-byte vector
+    __shared__ float red[16];
+    const int64_t m = blockIdx.x;
+    const int64_t nvec = K / EPV;
+    const uint4 *row = reinterpret_cast<const uint4 *>(static_cast<const char *>(X) +
+                                                       m * ldx * (XDT == DT_F32 ? 4 : 2));
+    uint4 v[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int64_t vi = threadIdx.x + static_cast<int64_t>(j) * blockDim.x;
+        v[j] = vi < nvec ? row[vi] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (XDT == DT_F32) {
+                amax = fmaxf(amax, fabsf(__uint_as_float(u[e])));
+            } else {
+                amax = fmaxf(amax, fabsf(__uint_as_float(u[e] << 16)));
+                amax = fmaxf(amax, fabsf(__uint_as_float(u[e] & 0xffff0000u)));
+            }
+        }
+    }
+    const float b = block_max(amax, red);
+    const float s = b > 0.0f ? 127.0f / b : 0.0f;
+    int8_t *qrow = Xq + m * ldq;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int64_t vi = threadIdx.x + static_cast<int64_t>(j) * blockDim.x;
+        if (vi >= nvec) continue;
+        const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        if constexpr (XDT == DT_F32) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w |= quant_one(__uint_as_float(u[e]), s) << (8 * e);
+            reinterpret_cast<uint32_t *>(qrow)[vi] = w;
+        } else {
+            uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                w0 |= quant_one(__uint_as_float(u[e] << 16), s) << (16 * e);
+                w0 |= quant_one(__uint_as_float(u[e] & 0xffff0000u), s) << (16 * e + 8);
+                w1 |= quant_one(__uint_as_float(u[e + 2] << 16), s) << (16 * e);
+                w1 |= quant_one(__uint_as_float(u[e + 2] & 0xffff0000u), s) << (16 * e + 8);
+            }
+            reinterpret_cast<uint2 *>(qrow)[vi] = make_uint2(w0, w1);
+        }
+    }
+    // zero the row padding [K, ldq)
+    for (int64_t k = K + 4 * threadIdx.x; k < ldq; k += 4 * blockDim.x)
+        *reinterpret_cast<uint32_t *>(qrow + k) = 0u;
+    if (threadIdx.x == 0) beta[m] = b;
+}
+
+template <int XDT>
+static bool launch_vec(const void *X, int64_t M, int64_t K, int64_t ldx, int8_t *Xq, int64_t ldq, float *beta,
+                       hipStream_t stream)
+{
+    constexpr int EPV = XDT == DT_F32 ? 4 : 8;
+    constexpr int ES = XDT == DT_F32 ? 4 : 2;
+    if (K % EPV || (ldx * ES) % 16 || (reinterpret_cast<uintptr_t>(X) & 15)) return false;
+    const int64_t vpt = (K / EPV + 255) / 256;
+    dim3 grid(static_cast<unsigned>(M)), block(256);
+    if (vpt <= 1) hipLaunchKernelGGL((k_quant_act_vec<XDT, 1>), grid, block, 0, stream, X, K, ldx, Xq, ldq, beta);
+    else if (vpt <= 2) hipLaunchKernelGGL((k_quant_act_vec<XDT, 2>), grid, block, 0, stream, X, K, ldx, Xq, ldq, beta);
+    else if (vpt <= 4) hipLaunchKernelGGL((k_quant_act_vec<XDT, 4>), grid, block, 0, stream, X, K, ldx, Xq, ldq, beta);
+    else if (vpt <= 8) hipLaunchKernelGGL((k_quant_act_vec<XDT, 8>), grid, block, 0, stream, X, K, ldx, Xq, ldq, beta);
+    else if (vpt <= 16) hipLaunchKernelGGL((k_quant_act_vec<XDT, 16>), grid, block, 0, stream, X, K, ldx, Xq, ldq, beta);
+    else return false;
+    return true;
+}
+
 hipError_t launch_quant_act(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int8_t *Xq,
                             int64_t ldq, float *beta, hipStream_t stream)
 {
-    if (x_dtype == DT_F32)
-        hipLaunchKernelGGL(k_quant_act<DT_F32>, dim3(static_cast<unsigned>(M)), dim3(256), 0, stream, X, K, ldx, Xq,
-                           ldq, beta);
-    else
-        hipLaunchKernelGGL(k_quant_act<DT_BF16>, dim3(static_cast<unsigned>(M)), dim3(256), 0, stream, X, K, ldx, Xq,
-                           ldq, beta);
+    bool done = x_dtype == DT_F32 ? launch_vec<DT_F32>(X, M, K, ldx, Xq, ldq, beta, stream)
+                                  : launch_vec<DT_BF16>(X, M, K, ldx, Xq, ldq, beta, stream);
+    if (!done) {
+        if (x_dtype == DT_F32)
+            hipLaunchKernelGGL(k_quant_act<DT_F32>, dim3(static_cast<unsigned>(M)), dim3(256), 0, stream, X, K, ldx,
+                               Xq, ldq, beta);
+        else
+            hipLaunchKernelGGL(k_quant_act<DT_BF16>, dim3(static_cast<unsigned>(M)), dim3(256), 0, stream, X, K, ldx,
+                               Xq, ldq, beta);
+    }
     return hipGetLastError();
+}
+
+} // namespace bl
+
+namespace bl {
+
+// Tiled activation layout (bitlinear.h): one workgroup per token row m of the
+// G*16 padded rows.  A thread owns whole 16-element pieces of the row (16
+// consecutive k: one 16-byte operand slice), loads them all before the max,
+// then quantises from registers and stores each piece with one 16-byte store.
+template <int XDT, int PPT>
+__global__ __launch_bounds__(256) void k_quant_act_tiled(const void *__restrict__ X, int64_t M, int64_t K,
+                                                         int64_t ldx, int layout, int64_t nsteps,
+                                                         int8_t *__restrict__ Xt, float *__restrict__ beta)
+{
+    constexpr int ES = XDT == DT_F32 ? 4 : 2;
+    __shared__ float red[16];
+    const int64_t m = blockIdx.x;
+    const int64_t step_k = layout == LAYOUT_I2 ? 256 : 320, kblk = step_k / 4, nmf = layout == LAYOUT_I2 ? 4 : 5;
+    const int64_t npieces = nsteps * step_k / 16;
+    const int64_t tg = m / 16, i = m % 16;
+    const bool live_row = m < M;
+    const char *row = static_cast<const char *>(X) + (live_row ? m : 0) * ldx * ES;
+    const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
+    float v[PPT][16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        const int64_t p = threadIdx.x + static_cast<int64_t>(j) * blockDim.x;
+        const int64_t k0 = 16 * p;
+        if (live_row && p < npieces && k0 + 16 <= K && vec) {
+            if constexpr (XDT == DT_F32) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint4 u = reinterpret_cast<const uint4 *>(row + k0 * 4)[q];
+                    v[j][4 * q] = __uint_as_float(u.x); v[j][4 * q + 1] = __uint_as_float(u.y);
+                    v[j][4 * q + 2] = __uint_as_float(u.z); v[j][4 * q + 3] = __uint_as_float(u.w);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const uint4 u = reinterpret_cast<const uint4 *>(row + k0 * 2)[q];
+                    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[j][8 * q + 2 * e] = __uint_as_float(w[e] << 16);
+                        v[j][8 * q + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                v[j][e] = (live_row && p < npieces && k0 + e < K) ? load_x<XDT>(X, m * ldx + k0 + e) : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
+    }
+    const float b = block_max(amax, red);
+    const float s = b > 0.0f ? 127.0f / b : 0.0f;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        const int64_t p = threadIdx.x + static_cast<int64_t>(j) * blockDim.x;
+        if (p >= npieces) break;
+        const int64_t k0 = 16 * p;
+        const int64_t st = k0 / step_k, r = k0 % step_k, g = r / kblk, d = (r % kblk) / 16;
+        uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) w[e / 4] |= quant_one(v[j][e], s) << (8 * (e % 4));
+        const int64_t off = (((tg * nsteps + st) * nmf + d) * 64 + g * 16 + i) * 16;
+        *reinterpret_cast<uint4 *>(Xt + off) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    if (threadIdx.x == 0 && live_row) beta[m] = b;
+}
+
+template <int XDT>
+static bool launch_tiled_ppt(const void *X, int64_t M, int64_t K, int64_t ldx, int layout, int8_t *Xt, float *beta,
+                             hipStream_t stream)
+{
+    const int64_t nsteps = tiled_nsteps(K, layout);
+    const int64_t npieces = nsteps * tiled_step_k(layout) / 16;
+    const int64_t ppt = (npieces + 255) / 256;
+    dim3 grid(static_cast<unsigned>((M + 15) / 16 * 16)), block(256);
+#define BL_TILED(N) hipLaunchKernelGGL((k_quant_act_tiled<XDT, N>), grid, block, 0, stream, X, M, K, ldx, layout, nsteps, Xt, beta)
+    if (ppt <= 1) BL_TILED(1);
+    else if (ppt <= 2) BL_TILED(2);
+    else if (ppt <= 4) BL_TILED(4);
+    else if (ppt <= 8) BL_TILED(8);
+    else if (ppt <= 16) BL_TILED(16);
+    else return false;
+#undef BL_TILED
+    return true;
+}
+
+hipError_t launch_quant_act_tiled(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int layout,
+                                  int8_t *Xt, float *beta, hipStream_t stream)
+{
+    const bool ok = x_dtype == DT_F32 ? launch_tiled_ppt<DT_F32>(X, M, K, ldx, layout, Xt, beta, stream)
+                                      : launch_tiled_ppt<DT_BF16>(X, M, K, ldx, layout, Xt, beta, stream);
+    return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 
 } // namespace bl

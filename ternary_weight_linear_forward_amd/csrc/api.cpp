@@ -26,6 +26,7 @@ int dtype_size(int dt)
     case BITLINEAR_BF16: return 2;
     case BITLINEAR_I8: return 1;
     case BITLINEAR_I32: return 4;
+    case BITLINEAR_I8_TILED: return 1;
     default: return 0;
     }
 }
@@ -47,9 +48,16 @@ int status_of(hipError_t e) { return e == hipSuccess ? BITLINEAR_OK : BITLINEAR_
 
 bool valid_layout(int layout) { return layout == BITLINEAR_LAYOUT_I2 || layout == BITLINEAR_LAYOUT_B3; }
 
-// Staged activations of the fused quantiser: Xq [M x round_up(K, 64)] then beta [M].
+// Staged activations of the fused quantiser: row-major Xq [M x round_up(K, 64)]
+// or the tiled layout, whichever is larger, then beta [M].
 int64_t staged_ldq(int64_t K) { return round_up(K, 64); }
-int64_t staged_xq_bytes(int64_t M, int64_t K) { return round_up(M * staged_ldq(K), 256); }
+constexpr int64_t kTiledMaxK = 65536; // the tiled quantiser keeps a row's pieces in registers
+int64_t staged_xq_bytes(int64_t M, int64_t K, int layout)
+{
+    int64_t rm = M * staged_ldq(K);
+    int64_t tl = K <= kTiledMaxK ? bl::tiled_bytes(M, K, layout) : 0;
+    return round_up(rm > tl ? rm : tl, 256);
+}
 
 } // namespace
 
@@ -88,9 +96,15 @@ int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int l
 {
     if (M < 1 || M > BITLINEAR_MAX_M || N < 1 || K < 1 || K > BITLINEAR_MAX_K || !valid_layout(layout))
         return -1;
-    if (x_dtype == BITLINEAR_I8) return 0;
+    if (x_dtype == BITLINEAR_I8 || x_dtype == BITLINEAR_I8_TILED) return 0;
     if (x_dtype != BITLINEAR_F32 && x_dtype != BITLINEAR_BF16) return -1;
-    return staged_xq_bytes(M, K) + round_up(4 * M, 256);
+    return staged_xq_bytes(M, K, layout) + round_up(4 * M, 256);
+}
+
+int64_t bitlinear_act_tiled_bytes(int64_t M, int64_t K, int layout)
+{
+    if (M < 1 || M > BITLINEAR_MAX_M || K < 1 || K > BITLINEAR_MAX_K || !valid_layout(layout)) return -1;
+    return bl::tiled_bytes(M, K, layout);
 }
 
 int bitlinear_quantize_weights(const float *W, int64_t N, int64_t K, int64_t ldw, int8_t *T, float *gamma,
@@ -139,6 +153,25 @@ int bitlinear_quantize_act(const void *X, int x_dtype, int64_t M, int64_t K, int
     return status_of(bl::launch_quant_act(X, x_dtype, M, K, ldx, Xq, ldq, beta, as_stream(stream)));
 }
 
+int bitlinear_quantize_act_tiled(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int layout,
+                                 int8_t *Xt, int64_t xt_bytes, float *beta, void *stream)
+{
+    if (!X || !Xt || !beta || !valid_layout(layout)) return BITLINEAR_ERR_INVALID_ARG;
+    if (x_dtype != BITLINEAR_F32 && x_dtype != BITLINEAR_BF16) return BITLINEAR_ERR_INVALID_ARG;
+    if (M < 1 || M > BITLINEAR_MAX_M || K < 1 || K > BITLINEAR_MAX_K || ldx < K) return BITLINEAR_ERR_INVALID_ARG;
+    const int64_t need = bl::tiled_bytes(M, K, layout);
+    if (xt_bytes < need) return BITLINEAR_ERR_INVALID_ARG;
+    if (!aligned16(Xt) || (reinterpret_cast<uintptr_t>(X) % dtype_size(x_dtype)) ||
+        (reinterpret_cast<uintptr_t>(beta) & 3u))
+        return BITLINEAR_ERR_INVALID_ARG;
+    const Span sx = span_of(X, M, ldx, K, dtype_size(x_dtype)), st = span_of(Xt, 1, need, need, 1),
+               sb = span_of(beta, 1, M, M, 4);
+    if (overlap(sx, st) || overlap(sx, sb) || overlap(st, sb)) return BITLINEAR_ERR_INVALID_ARG;
+    if (K > kTiledMaxK) return BITLINEAR_ERR_UNSUPPORTED;
+    (void)hipGetLastError();
+    return status_of(bl::launch_quant_act_tiled(X, x_dtype, M, K, ldx, layout, Xt, beta, as_stream(stream)));
+}
+
 int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
                            const void *X, int x_dtype, int64_t ldx, const float *beta_in, void *Y, int y_dtype,
                            int64_t ldy, void *ws, int64_t ws_bytes, int algo, void *stream)
@@ -146,18 +179,22 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
     if (!P || !gamma || !X || !Y || !valid_layout(layout)) return BITLINEAR_ERR_INVALID_ARG;
     if (M < 1 || M > BITLINEAR_MAX_M || N < 1 || N > (int64_t(1) << 31) || K < 1 || K > BITLINEAR_MAX_K)
         return BITLINEAR_ERR_INVALID_ARG;
-    if (x_dtype != BITLINEAR_F32 && x_dtype != BITLINEAR_BF16 && x_dtype != BITLINEAR_I8)
+    if (x_dtype != BITLINEAR_F32 && x_dtype != BITLINEAR_BF16 && x_dtype != BITLINEAR_I8 &&
+        x_dtype != BITLINEAR_I8_TILED)
         return BITLINEAR_ERR_INVALID_ARG;
+    const bool x_int8 = x_dtype == BITLINEAR_I8 || x_dtype == BITLINEAR_I8_TILED;
     if (y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_BF16 && y_dtype != BITLINEAR_I32)
         return BITLINEAR_ERR_INVALID_ARG;
-    if (ldx < K || ldy < N) return BITLINEAR_ERR_INVALID_ARG;
+    if ((x_dtype != BITLINEAR_I8_TILED && ldx < K) || ldy < N) return BITLINEAR_ERR_INVALID_ARG;
     if (algo < BITLINEAR_ALGO_AUTO || algo > BITLINEAR_ALGO_GEMM_MFMA) return BITLINEAR_ERR_INVALID_ARG;
-    if ((x_dtype == BITLINEAR_I8) != (beta_in != nullptr)) return BITLINEAR_ERR_INVALID_ARG;
+    if (x_int8 != (beta_in != nullptr)) return BITLINEAR_ERR_INVALID_ARG;
     if (!aligned16(P) || (reinterpret_cast<uintptr_t>(gamma) & 3u) ||
         (reinterpret_cast<uintptr_t>(X) % dtype_size(x_dtype)) ||
         (reinterpret_cast<uintptr_t>(Y) % dtype_size(y_dtype)))
         return BITLINEAR_ERR_INVALID_ARG;
     if (x_dtype == BITLINEAR_I8 && (!aligned16(X) || ldx % 16 || (reinterpret_cast<uintptr_t>(beta_in) & 3u)))
+        return BITLINEAR_ERR_INVALID_ARG;
+    if (x_dtype == BITLINEAR_I8_TILED && (!aligned16(X) || (reinterpret_cast<uintptr_t>(beta_in) & 3u)))
         return BITLINEAR_ERR_INVALID_ARG;
 
     const int64_t need = bitlinear_forward_workspace_bytes(M, N, K, layout, x_dtype);
@@ -165,7 +202,9 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
     if (need > 0 && !aligned16(ws)) return BITLINEAR_ERR_INVALID_ARG;
 
     const int64_t pb = bitlinear_packed_bytes(N, K, layout);
-    const Span sp = span_of(P, 1, pb, pb, 1), sx = span_of(X, M, ldx, K, dtype_size(x_dtype)),
+    const int64_t xt = bl::tiled_bytes(M, K, layout);
+    const Span sp = span_of(P, 1, pb, pb, 1),
+               sx = x_dtype == BITLINEAR_I8_TILED ? span_of(X, 1, xt, xt, 1) : span_of(X, M, ldx, K, dtype_size(x_dtype)),
                sy = span_of(Y, M, ldy, N, dtype_size(y_dtype)), sg = span_of(gamma, 1, 1, 1, 4);
     if (overlap(sy, sp) || overlap(sy, sx) || overlap(sy, sg)) return BITLINEAR_ERR_INVALID_ARG;
     if (beta_in && overlap(sy, span_of(beta_in, 1, M, M, 4))) return BITLINEAR_ERR_INVALID_ARG;
@@ -176,7 +215,9 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
     }
 
     if (algo == BITLINEAR_ALGO_AUTO) {
-        if (M <= 16)
+        if (x_dtype == BITLINEAR_I8_TILED)
+            algo = BITLINEAR_ALGO_GEMV_MFMA;
+        else if (M <= 16)
             algo = (layout == BITLINEAR_LAYOUT_I2 && M <= kAddSubMaxM) ? BITLINEAR_ALGO_GEMV_ADDSUB
                                                                        : BITLINEAR_ALGO_GEMV_MFMA;
         else
@@ -185,6 +226,7 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
     if (algo == BITLINEAR_ALGO_GEMV_ADDSUB && (M > 16 || layout != BITLINEAR_LAYOUT_I2))
         return BITLINEAR_ERR_UNSUPPORTED;
     if (algo == BITLINEAR_ALGO_GEMM_MFMA && layout != BITLINEAR_LAYOUT_I2) return BITLINEAR_ERR_UNSUPPORTED;
+    if (x_dtype == BITLINEAR_I8_TILED && algo != BITLINEAR_ALGO_GEMV_MFMA) return BITLINEAR_ERR_UNSUPPORTED;
 
     (void)hipGetLastError();
     hipStream_t st = as_stream(stream);
@@ -198,19 +240,31 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
     a.Y = Y;
     a.y_dtype = y_dtype;
     a.ldy = ldy;
-    if (x_dtype == BITLINEAR_I8) {
+    a.tiled = false;
+    if (x_int8) {
         a.Xq = static_cast<const int8_t *>(X);
         a.ldq = ldx;
         a.beta = beta_in;
+        a.tiled = x_dtype == BITLINEAR_I8_TILED;
     } else {
         int8_t *xq = static_cast<int8_t *>(ws);
-        float *beta = reinterpret_cast<float *>(static_cast<char *>(ws) + staged_xq_bytes(M, K));
-        const int64_t ldq = staged_ldq(K);
-        hipError_t e = bl::launch_quant_act(X, x_dtype, M, K, ldx, xq, ldq, beta, st);
+        float *beta = reinterpret_cast<float *>(static_cast<char *>(ws) + staged_xq_bytes(M, K, layout));
+        // The matrix-core GEMV reads tiled activations when a token group has
+        // more than a few live rows (with few rows the clamped row-major reads
+        // touch few cache lines).
+        const bool tiled = algo == BITLINEAR_ALGO_GEMV_MFMA && M > 4 && K <= kTiledMaxK;
+        hipError_t e;
+        if (tiled) {
+            e = bl::launch_quant_act_tiled(X, x_dtype, M, K, ldx, layout, xq, beta, st);
+            a.ldq = 0;
+        } else {
+            a.ldq = staged_ldq(K);
+            e = bl::launch_quant_act(X, x_dtype, M, K, ldx, xq, a.ldq, beta, st);
+        }
         if (e != hipSuccess) return BITLINEAR_ERR_LAUNCH;
         a.Xq = xq;
-        a.ldq = ldq;
         a.beta = beta;
+        a.tiled = tiled;
     }
     hipError_t e;
     switch (algo) {

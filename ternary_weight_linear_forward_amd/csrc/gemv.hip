@@ -4,21 +4,24 @@
 // LIT-380 record (dmarx anthology), Key takeaways, bullet 4: with ternary
 // weights the product needs only additions and subtractions.  The same
 // record's closing section notes that on stock GPUs the memory saving is what
-// survives: this path streams 2 bits per weight from HBM and is bound by it.
+// survives: this path streams 2 bits (i2) or 1.6 bits (b3) per weight from HBM
+// and is bound by it.
 //
 // Two kernels:
-//  * k_gemv_addsub: vector-ALU add/subtract.  A lane owns one weight row; the
-//    activation words are wave-uniform (scalar registers).  The offset code
-//    c = T + 1 in {0, 1, 2} goes through v_dot4_i32_i8: sum_k c*q adds q where
-//    T = 0, adds 2q where T = +1, adds nothing where T = -1; subtracting
-//    sum_k q afterwards leaves sum_{T=+1} q - sum_{T=-1} q exactly.
-//  * k_gemv_mfma: tiles of 16 tokens x 16 rows x 64 weights on the int8 matrix
-//    cores, weights unpacked in registers to signed bytes.  Used where the
-//    vector ALU cannot keep up with HBM (more than a few tokens).
+//  * k_gemv_mfma: tiles of 16 tokens x 16 rows on the int8 matrix cores
+//    (v_mfma_i32_16x16x64_i8), the packed weights unpacked in registers to
+//    signed bytes.  Waves issue all loads of a batch of k-steps before their
+//    first MFMA, so many HBM round trips overlap.
+//  * k_gemv_addsub: vector-ALU add/subtract.  A lane owns one weight row and
+//    the activation words are wave-uniform.  The offset code c = T + 1 in
+//    {0, 1, 2} goes through v_dot4_i32_i8: sum_k c*q adds q where T = 0, 2q
+//    where T = +1 and nothing where T = -1; subtracting sum_k q leaves
+//    sum_{T=+1} q - sum_{T=-1} q exactly.
 #include "common.h"
 #include "launch.h"
 
 namespace bl {
+
 
 // 16 int8 activations q[m][k0 .. k0+15] as one MFMA operand; zero outside
 // [0, M) x [0, K).  Rows of Xq are 16-byte aligned and k0 % 16 == 0.
@@ -39,107 +42,364 @@ __device__ __forceinline__ v4i load_a16(const int8_t *__restrict__ Xq, int64_t l
     return r;
 }
 
+// Signed weights of one i2 word (16 weights, natural k order).  v_perm_b32
+// with selector bytes c in {0, 1, 2} picks byte c of 0x000100ff: -1, 0, +1.
+__device__ __forceinline__ v4i i2_word_signed(uint32_t w)
+{
+    v4i r;
+    r[0] = static_cast<int>(__builtin_amdgcn_perm(0u, 0x000100ffu, w & 0x03030303u));
+    r[1] = static_cast<int>(__builtin_amdgcn_perm(0u, 0x000100ffu, (w >> 2) & 0x03030303u));
+    r[2] = static_cast<int>(__builtin_amdgcn_perm(0u, 0x000100ffu, (w >> 4) & 0x03030303u));
+    r[3] = static_cast<int>(__builtin_amdgcn_perm(0u, 0x000100ffu, (w >> 6) & 0x03030303u));
+    return r;
+}
+
+// Base-3 digit t (t = 0 most significant) of each byte of a b3 word, as signed
+// bytes digit - 1.  Two bytes per 16-bit lane: floor(b / 3^(4-t)) is
+// (b * m) >> s with (m, s) = (203, 14), (19, 9), (57, 9), (171, 9) for
+// t = 0..3, exact for every b <= 242 with b * m < 2^16; digit t is
+// H_t - 3 H_(t-1) with H_t = floor(b / 3^(4-t)).
+struct B3Digits {
+    uint32_t d[5];
+};
+
+__device__ __forceinline__ uint32_t pk_mul_u16(uint32_t a, uint32_t b)
+{
+    typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+    v2u16 x = __builtin_bit_cast(v2u16, a), y = __builtin_bit_cast(v2u16, b);
+    return __builtin_bit_cast(uint32_t, static_cast<v2u16>(x * y));
+}
+
+__device__ __forceinline__ uint32_t pk_shr_u16(uint32_t a, int s)
+{
+    typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+    v2u16 x = __builtin_bit_cast(v2u16, a);
+    v2u16 sh = {static_cast<unsigned short>(s), static_cast<unsigned short>(s)};
+    return __builtin_bit_cast(uint32_t, static_cast<v2u16>(x >> sh));
+}
+
+__device__ __forceinline__ uint32_t pk_sub_u16(uint32_t a, uint32_t b)
+{
+    typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+    v2u16 x = __builtin_bit_cast(v2u16, a), y = __builtin_bit_cast(v2u16, b);
+    return __builtin_bit_cast(uint32_t, static_cast<v2u16>(x - y));
+}
+
+// digits of the two bytes held in the 16-bit lanes of 'b' (each <= 242)
+__device__ __forceinline__ void b3_digits_pair(uint32_t b, uint32_t c[5])
+{
+    const uint32_t h0 = pk_shr_u16(pk_mul_u16(b, 0x00cb00cbu), 14); // b / 81
+    const uint32_t h1 = pk_shr_u16(pk_mul_u16(b, 0x00130013u), 9);  // b / 27
+    const uint32_t h2 = pk_shr_u16(pk_mul_u16(b, 0x00390039u), 9);  // b / 9
+    const uint32_t h3 = pk_shr_u16(pk_mul_u16(b, 0x00ab00abu), 9);  // b / 3
+    c[0] = h0;
+    c[1] = pk_sub_u16(h1, pk_mul_u16(h0, 0x00030003u));
+    c[2] = pk_sub_u16(h2, pk_mul_u16(h1, 0x00030003u));
+    c[3] = pk_sub_u16(h3, pk_mul_u16(h2, 0x00030003u));
+    c[4] = pk_sub_u16(b, pk_mul_u16(h3, 0x00030003u));
+}
+
+__device__ __forceinline__ B3Digits b3_word_signed(uint32_t w)
+{
+    uint32_t lo[5], hi[5];
+    b3_digits_pair(w & 0x00ff00ffu, lo);        // bytes 0 and 2
+    b3_digits_pair((w >> 8) & 0x00ff00ffu, hi); // bytes 1 and 3
+    B3Digits r;
+#pragma unroll
+    for (int t = 0; t < 5; ++t) r.d[t] = __builtin_amdgcn_perm(0u, 0x000100ffu, lo[t] | (hi[t] << 8));
+    return r;
+}
+
 // ---------------------------------------------------------------------------
-// MFMA GEMV: one workgroup = one 16-row tile x one group of 16 tokens; its four
-// waves take the k-steps (4 k-blocks = 256 weights) round-robin and reduce
-// through LDS.  In a k-step, lane l (i = l % 16, g = l / 16) loads the 16-byte
-// chunk of row 16*tile + i at k-block 4*step + g; MFMA number d (i2: word d,
-// 16 weights; b3: base-3 digit d of the 16 bytes) pairs it with the matching
-// 16 activations of token i.
+// MFMA GEMV.  A k-step is 4 consecutive k-blocks (i2: 256 weights, b3: 320).
+// In a k-step, lane l (i = l % 16, g = l / 16) holds the 16-byte chunk of row
+// 16*tile + i at k-block 4*step + g.  i2: MFMA d (0..3) multiplies word d
+// (16 weights) with activations kb*64 + 16d .. +15 of token i; b3: MFMA t
+// (0..4) multiplies base-3 digit t of the 16 bytes with activations
+// kb*80 + 16t .. +15.
+//
+// A workgroup owns TW consecutive row tiles and has KS waves; wave w takes
+// the k-steps w, w + KS, ... of all TW tiles, SB steps at a time: it issues
+// the loads of SB steps (SB activation operands, SB x TW weight chunks) before
+// the first MFMA, and reuses each activation operand for the TW tiles.  With
+// up to 16 waves per CU this keeps ~100 KB of weights in flight per CU.  The
+// KS partial tiles are summed through LDS; wave t < TW writes tile t.
 // ---------------------------------------------------------------------------
 template <int LAYOUT>
-__global__ __launch_bounds__(256) void k_gemv_mfma(const uint8_t *__restrict__ P, int64_t KB, int64_t NT,
-                                                   const float *__restrict__ gamma_p,
-                                                   const int8_t *__restrict__ Xq, int64_t ldq,
-                                                   const float *__restrict__ beta, int64_t M, int64_t N,
-                                                   int64_t K, void *__restrict__ Y, int y_dtype, int64_t ldy)
+struct StepShape;
+template <>
+struct StepShape<LAYOUT_I2> {
+    static constexpr int NMF = 4, KBLK = 64;
+};
+template <>
+struct StepShape<LAYOUT_B3> {
+    static constexpr int NMF = 5, KBLK = 80;
+};
+
+// One k-step of TW tiles: unpack the weight chunks and accumulate.
+template <int LAYOUT, int TW, int NMF>
+__device__ __forceinline__ void gemv_step(const uint4 (&b)[TW], const v4i (&a)[NMF], v4i (&acc)[TW])
 {
-    __shared__ v4i red[4][64];
-    const int wave = wave_id(), lane = lane_id();
-    const int i = lane & 15, g = lane >> 4;
-    const int64_t tile = blockIdx.x;
-    const int64_t m = static_cast<int64_t>(blockIdx.y) * 16 + i; // token of the A operand
-    const uint8_t *ptile = P + tile * KB * 256;
-    const int64_t nsteps = (KB + 3) / 4;
-    v4i acc = {0, 0, 0, 0};
-    for (int64_t s = wave; s < nsteps; s += 4) {
-        const int64_t kb = 4 * s + g;
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+        const uint32_t wd[4] = {b[t].x, b[t].y, b[t].z, b[t].w};
         if constexpr (LAYOUT == LAYOUT_I2) {
-            uint4 w = make_uint4(I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD);
-            if (kb < KB) w = *reinterpret_cast<const uint4 *>(ptile + kb * 256 + i * 16);
-            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                v4i a = load_a16(Xq, ldq, m, M, K, kb * 64 + 16 * d);
-                v4i b = i2_word_to_signed16(wd[d]);
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
-            }
+            for (int d = 0; d < 4; ++d)
+                acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d], i2_word_signed(wd[d]), acc[t], 0, 0, 0);
         } else {
-            uint4 w = make_uint4(0x79797979u, 0x79797979u, 0x79797979u, 0x79797979u); // 121 = all T = 0
-            if (kb < KB) w = *reinterpret_cast<const uint4 *>(ptile + kb * 256 + i * 16);
-            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-            // digit t of byte j holds weight kb*80 + 5j + t
+            B3Digits dg[4];
 #pragma unroll
-            for (int t = 0; t < 5; ++t) {
-                uint32_t bw[4] = {0, 0, 0, 0}, aw[4] = {0, 0, 0, 0};
-                const uint32_t div = t == 0 ? 81u : t == 1 ? 27u : t == 2 ? 9u : t == 3 ? 3u : 1u;
+            for (int q = 0; q < 4; ++q) dg[q] = b3_word_signed(wd[q]);
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    uint32_t byte = (wd[j / 4] >> (8 * (j % 4))) & 0xffu;
-                    uint32_t digit = (byte / div) % 3u;
-                    bw[j / 4] |= ((digit + 0xffu) & 0xffu) << (8 * (j % 4)); // digit - 1 as a byte
-                    int64_t k = kb * 80 + 5 * j + t;
-                    if (m < M && k < K)
-                        aw[j / 4] |= (static_cast<uint32_t>(Xq[m * ldq + k]) & 0xffu) << (8 * (j % 4));
-                }
-                v4i a = {static_cast<int>(aw[0]), static_cast<int>(aw[1]), static_cast<int>(aw[2]),
-                         static_cast<int>(aw[3])};
-                v4i b = {static_cast<int>(bw[0]), static_cast<int>(bw[1]), static_cast<int>(bw[2]),
-                         static_cast<int>(bw[3])};
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+            for (int d = 0; d < 5; ++d) {
+                v4i bt = {static_cast<int>(dg[0].d[d]), static_cast<int>(dg[1].d[d]), static_cast<int>(dg[2].d[d]),
+                          static_cast<int>(dg[3].d[d])};
+                acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d], bt, acc[t], 0, 0, 0);
             }
         }
     }
-    red[wave][lane] = acc;
-    __syncthreads();
-    if (wave != 0) return;
-    v4i tot = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
-    // D layout: lane l holds rows (tokens) 4g + r, column (weight row) i.
-    const float gamma = *gamma_p;
-    const int64_t n = tile * 16 + i;
+}
+
+template <int LAYOUT, int TW, int SB, bool TILED>
+__global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ P, int64_t KB, int64_t NT,
+                                                    const float *__restrict__ gamma_p,
+                                                    const int8_t *__restrict__ Xq, int64_t ldq,
+                                                    const float *__restrict__ beta, int64_t M, int64_t N,
+                                                    int64_t K, void *__restrict__ Y, int y_dtype, int64_t ldy)
+{
+    using S = StepShape<LAYOUT>;
+    constexpr int NMF = S::NMF, KBLK = S::KBLK;
+    constexpr int STEP_K = 4 * KBLK; // weights per k-step
+    __shared__ v4i red[TW][16][64];
+    const int KS = blockDim.x >> 6;
+    const int wave = wave_id(), lane = lane_id();
+    const int i = lane & 15, g = lane >> 4;
+    const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * TW;
+    const int64_t nsteps = (KB + 3) / 4;
+    // Row-major activations: k-steps whose activations all lie inside K run
+    // without bounds checks, the last partial one is checked.  Tiled
+    // activations are zero-padded, so every k-step runs unchecked: a weight
+    // chunk past the last k-block (address clamped) meets zero activations.
+    const int64_t nfull = TILED ? nsteps : K / STEP_K;
+    const uint4 zero_chunk = LAYOUT == LAYOUT_I2 ? make_uint4(I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD)
+                                                 : make_uint4(0x79797979u, 0x79797979u, 0x79797979u, 0x79797979u);
+    // Tokens past M and tiles past NT read valid rows (clamped); their results are never stored.
+    const int64_t m_a = static_cast<int64_t>(blockIdx.y) * 16 + i;
+    const int8_t *xrow = TILED ? Xq + (static_cast<int64_t>(blockIdx.y) * nsteps * NMF * 64 + lane) * 16
+                               : Xq + (m_a < M ? m_a : M - 1) * ldq + g * KBLK;
+    const uint8_t *ptile[TW];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int64_t mm = static_cast<int64_t>(blockIdx.y) * 16 + 4 * g + r;
-        if (mm < M && n < N) store_out(Y, y_dtype, ldy, mm, n, tot[r], token_scale(gamma, beta[mm]));
+    for (int t = 0; t < TW; ++t) {
+        const int64_t tt = tile0 + t < NT ? tile0 + t : NT - 1;
+        ptile[t] = P + tt * KB * 256;
+    }
+    const uint32_t lane_off = static_cast<uint32_t>(g) * 256u + static_cast<uint32_t>(i) * 16u;
+    const uint32_t last_kb_off = static_cast<uint32_t>(KB - 1) * 256u + static_cast<uint32_t>(i) * 16u;
+
+    v4i acc[TW];
+#pragma unroll
+    for (int t = 0; t < TW; ++t) acc[t] = v4i{0, 0, 0, 0};
+
+    // Software-pipelined: the loads of the next batch are in flight while the
+    // current batch is unpacked and multiplied.
+    const int64_t stride = static_cast<int64_t>(KS) * SB;
+    auto load_batch = [&](int64_t s0, uint4 (&b)[SB][TW], v4i (&a)[SB][NMF]) {
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            int64_t s = s0 + static_cast<int64_t>(j) * KS;
+            s = s < nfull ? s : nfull - 1; // a clamped duplicate is never accumulated
+            uint32_t off = static_cast<uint32_t>(s) * 1024u + lane_off;
+            if (TILED) off = 4 * s + g < KB ? off : last_kb_off;
+#pragma unroll
+            for (int t = 0; t < TW; ++t) b[j][t] = *reinterpret_cast<const uint4 *>(ptile[t] + off);
+#pragma unroll
+            for (int d = 0; d < NMF; ++d)
+                a[j][d] = TILED ? *reinterpret_cast<const v4i *>(xrow + (s * NMF + d) * 1024)
+                                : *reinterpret_cast<const v4i *>(xrow + s * STEP_K + 16 * d);
+        }
+    };
+    auto compute_batch = [&](int64_t s0, const uint4 (&b)[SB][TW], const v4i (&a)[SB][NMF]) {
+#pragma unroll
+        for (int j = 0; j < SB; ++j)
+            if (s0 + static_cast<int64_t>(j) * KS < nfull) gemv_step<LAYOUT, TW, NMF>(b[j], a[j], acc);
+    };
+    if (wave < nfull) {
+        uint4 b0[SB][TW], b1[SB][TW];
+        v4i a0[SB][NMF], a1[SB][NMF];
+        int64_t s0 = wave;
+        load_batch(s0, b0, a0);
+        while (true) {
+            const int64_t s1 = s0 + stride;
+            if (s1 < nfull) load_batch(s1, b1, a1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_batch(s0, b0, a0);
+            if (s1 >= nfull) break;
+            const int64_t s2 = s1 + stride;
+            if (s2 < nfull) load_batch(s2, b0, a0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_batch(s1, b1, a1);
+            if (s2 >= nfull) break;
+            s0 = s2;
+        }
+    }
+    // the partial k-step of row-major activations, bounds-checked
+    if (!TILED && nfull < nsteps && wave == static_cast<int>(nfull % KS)) {
+        const int64_t kb = 4 * nfull + g;
+        uint4 b[TW];
+        v4i a[NMF];
+#pragma unroll
+        for (int t = 0; t < TW; ++t)
+            b[t] = kb < KB ? *reinterpret_cast<const uint4 *>(ptile[t] + kb * 256 + i * 16) : zero_chunk;
+#pragma unroll
+        for (int d = 0; d < NMF; ++d) a[d] = load_a16(Xq, ldq, m_a, M, K, kb * KBLK + 16 * d);
+        gemv_step<LAYOUT, TW, NMF>(b, a, acc);
+    }
+
+#pragma unroll
+    for (int t = 0; t < TW; ++t) red[t][wave][lane] = acc[t];
+    __syncthreads();
+    const float gamma = *gamma_p;
+    // tile t is finished by wave t % KS (KS may be smaller than TW)
+    for (int t = wave; t < TW; t += KS) {
+        const int64_t tile = tile0 + t;
+        if (tile >= NT) break;
+        v4i tot = red[t][0][lane];
+        for (int w = 1; w < KS; ++w) tot += red[t][w][lane];
+        // D layout: lane l holds tokens 4g + rr of this token group, weight row i of the tile.
+        const int64_t n = tile * 16 + i;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int64_t mm = static_cast<int64_t>(blockIdx.y) * 16 + 4 * g + rr;
+            if (mm < M && n < N) store_out(Y, y_dtype, ldy, mm, n, tot[rr], token_scale(gamma, beta[mm]));
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Add/subtract GEMV: one workgroup = 64 weight rows (4 tiles), lane l owns row
-// 16*(4*blockIdx.x + l/16) + l%16; wave w takes k-blocks w, w+4, ...  For a
-// k-block the 16 code words of the lane's row are formed once and dotted with
-// the 16 activation words of each token (the same for the whole wave).
+// Persistent MFMA GEMV for large layers.  About one workgroup per CU, KS
+// waves; wave w owns the k-steps w, w + KS, ... (at most SPW of them): it loads
+// their activation operands into registers once and then streams the packed
+// weights of its workgroup's row tiles blockIdx.x + t * gridDim.x
+// (t < TMAX), keeping one accumulator per tile, with a ring of D tiles in
+// flight.  No barrier until every tile is done; then the KS partials of every
+// tile meet in LDS and the 4 x TMAX output groups are summed by different
+// waves.  Activations cross L2 once per CU instead of once per tile.
+// ---------------------------------------------------------------------------
+template <int LAYOUT, int SPW, int TMAX, bool TILED>
+__global__ __launch_bounds__(1024) void k_gemv_persist(const uint8_t *__restrict__ P, int64_t KB, int64_t NT,
+                                                       const float *__restrict__ gamma_p,
+                                                       const int8_t *__restrict__ Xq, int64_t ldq,
+                                                       const float *__restrict__ beta, int64_t M, int64_t N,
+                                                       int64_t K, void *__restrict__ Y, int y_dtype, int64_t ldy)
+{
+    using S = StepShape<LAYOUT>;
+    constexpr int NMF = S::NMF, KBLK = S::KBLK;
+    constexpr int D = SPW >= 4 ? 2 : (SPW >= 2 ? 3 : 4);
+    extern __shared__ int red_dyn[]; // [TMAX][KS][4][64]
+    const int KS = blockDim.x >> 6;
+    const int wave = wave_id(), lane = lane_id();
+    const int i = lane & 15, g = lane >> 4;
+    const int64_t nsteps = (KB + 3) / 4;
+    const int64_t m_a = static_cast<int64_t>(blockIdx.y) * 16 + i;
+    const int64_t G = gridDim.x;
+    const int ntiles = static_cast<int>((NT - blockIdx.x + G - 1) / G); // tiles of this workgroup (<= TMAX)
+
+    // activation operands of this wave's k-steps, loaded once (zero past K)
+    v4i a[SPW][NMF];
+    uint32_t boff[SPW]; // byte offset of this lane's weight chunk in a tile, per k-step
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+        const int64_t s = wave + static_cast<int64_t>(j) * KS;
+        const int64_t kb = 4 * s + g;
+        boff[j] = static_cast<uint32_t>(kb < KB ? kb : KB - 1) * 256u + static_cast<uint32_t>(i) * 16u;
+#pragma unroll
+        for (int d = 0; d < NMF; ++d) {
+            if (s >= nsteps)
+                a[j][d] = v4i{0, 0, 0, 0};
+            else if (TILED)
+                a[j][d] = *reinterpret_cast<const v4i *>(
+                    Xq + (((static_cast<int64_t>(blockIdx.y) * nsteps + s) * NMF + d) * 64 + lane) * 16);
+            else
+                a[j][d] = load_a16(Xq, ldq, m_a, M, K, kb * KBLK + 16 * d);
+        }
+    }
+    auto load_tile = [&](int t, uint4 (&b)[SPW]) {
+        const int64_t tile = blockIdx.x + t * G;
+        const uint8_t *pt = P + (tile < NT ? tile : NT - 1) * KB * 256;
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) b[j] = *reinterpret_cast<const uint4 *>(pt + boff[j]);
+    };
+
+    v4i acc[TMAX];
+    uint4 b[D][SPW];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) acc[t] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < D; ++t)
+        if (t < ntiles) load_tile(t, b[t]);
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+        if (t >= ntiles) break;
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+            if (wave + static_cast<int64_t>(j) * KS >= nsteps) break;
+            const uint4 bj[1] = {b[t % D][j]};
+            v4i accs[1] = {acc[t]};
+            gemv_step<LAYOUT, 1, NMF>(bj, a[j], accs);
+            acc[t] = accs[0];
+        }
+        if (t + D < ntiles) load_tile(t + D, b[t % D]);
+    }
+    int *red = red_dyn;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+        if (t >= ntiles) break;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) red[((t * KS + wave) * 4 + rr) * 64 + lane] = acc[t][rr];
+    }
+    __syncthreads();
+    const float gamma = *gamma_p;
+    // output group (t, rr): tokens 4g + rr of this token group, weight row i of tile t
+    for (int task = wave; task < ntiles * 4; task += KS) {
+        const int t = task >> 2, rr = task & 3;
+        int tot = 0;
+        for (int w = 0; w < KS; ++w) tot += red[((t * KS + w) * 4 + rr) * 64 + lane];
+        const int64_t n = (blockIdx.x + t * G) * 16 + i;
+        const int64_t mm = static_cast<int64_t>(blockIdx.y) * 16 + 4 * g + rr;
+        if (mm < M && n < N) store_out(Y, y_dtype, ldy, mm, n, tot, token_scale(gamma, beta[mm]));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Add/subtract GEMV: a workgroup owns 64 weight rows (4 tiles), lane l owns
+// row 16*(4*blockIdx.x + l/16) + l%16; wave w of W takes k-blocks w, w+W, ...,
+// loading up to 4 of them before it computes.  For a k-block the 16 code
+// words of the lane's row are formed once and dotted with the 16 activation
+// words of each token, which are the same for the whole wave.
 // ---------------------------------------------------------------------------
 template <int MT>
-__global__ __launch_bounds__(256) void k_gemv_addsub(const uint8_t *__restrict__ P, int64_t KB, int64_t NT,
-                                                     const float *__restrict__ gamma_p,
-                                                     const int8_t *__restrict__ Xq, int64_t ldq,
-                                                     const float *__restrict__ beta, int64_t M, int64_t N,
-                                                     int64_t K, void *__restrict__ Y, int y_dtype, int64_t ldy)
+__global__ __launch_bounds__(1024) void k_gemv_addsub(const uint8_t *__restrict__ P, int64_t KB, int64_t NT,
+                                                      const float *__restrict__ gamma_p,
+                                                      const int8_t *__restrict__ Xq, int64_t ldq,
+                                                      const float *__restrict__ beta, int64_t M, int64_t N,
+                                                      int64_t K, void *__restrict__ Y, int y_dtype, int64_t ldy)
 {
-    __shared__ int red[4][MT][64];
-    __shared__ int qsum_part[4][MT];
+    constexpr int DEPTH = 4;
+    __shared__ int red[16][MT][64];
+    __shared__ int qsum_part[16][MT];
+    const int W = blockDim.x >> 6;
     const int wave = wave_id(), lane = lane_id();
     const int64_t tile = 4 * static_cast<int64_t>(blockIdx.x) + (lane >> 4);
     const int r = lane & 15;
 
-    // sum_k q[m][k] for the correction of the offset codes
+    // sum_k q[m][k], for the correction of the offset codes
     {
         int part[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) part[t] = 0;
         const int64_t nwords = (K + 3) / 4;
-        for (int64_t wi = threadIdx.x; wi < nwords; wi += 256) {
+        for (int64_t wi = threadIdx.x; wi < nwords; wi += blockDim.x) {
             const int64_t k = 4 * wi;
 #pragma unroll
             for (int t = 0; t < MT; ++t)
@@ -166,41 +426,52 @@ __global__ __launch_bounds__(256) void k_gemv_addsub(const uint8_t *__restrict__
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[t] = 0;
     const int64_t KBF = K / 64; // k-blocks whose 64 activations are all in range
-    for (int64_t kb = wave; kb < KB; kb += 4) {
-        uint4 w = make_uint4(I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD);
-        if (tile < NT) w = *reinterpret_cast<const uint4 *>(P + (tile * KB + kb) * 256 + r * 16);
-        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-        uint32_t c[16];
+    const uint8_t *prow = P + tile * KB * 256 + r * 16;
+    for (int64_t kb0 = wave; kb0 < KB; kb0 += static_cast<int64_t>(W) * DEPTH) {
+        uint4 wv[DEPTH];
 #pragma unroll
-        for (int d = 0; d < 4; ++d)
+        for (int j = 0; j < DEPTH; ++j) {
+            const int64_t kb = kb0 + static_cast<int64_t>(j) * W;
+            wv[j] = (tile < NT && kb < KB) ? *reinterpret_cast<const uint4 *>(prow + kb * 256)
+                                           : make_uint4(I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD);
+        }
 #pragma unroll
-            for (int s = 0; s < 4; ++s) c[4 * d + s] = (wd[d] >> (2 * s)) & 0x03030303u;
+        for (int j = 0; j < DEPTH; ++j) {
+            const int64_t kb = kb0 + static_cast<int64_t>(j) * W;
+            if (kb >= KB) break;
+            const uint32_t wd[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
+            uint32_t c[16];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            if (t >= M) break;
-            const int8_t *qp = Xq + t * ldq + kb * 64;
-            uint32_t qd[16];
-            if (kb < KBF) {
-                const uint4 *q4 = reinterpret_cast<const uint4 *>(qp);
+            for (int d = 0; d < 4; ++d)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    uint4 x = q4[v];
-                    qd[4 * v] = x.x; qd[4 * v + 1] = x.y; qd[4 * v + 2] = x.z; qd[4 * v + 3] = x.w;
-                }
-            } else {
+                for (int s = 0; s < 4; ++s) c[4 * d + s] = (wd[d] >> (2 * s)) & 0x03030303u;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    uint32_t word = 0;
-                    for (int j = 0; j < 4; ++j) {
-                        int64_t k = kb * 64 + 4 * v + j;
-                        if (k < K) word |= (static_cast<uint32_t>(qp[4 * v + j]) & 0xffu) << (8 * j);
+            for (int t = 0; t < MT; ++t) {
+                if (t >= M) break;
+                const int8_t *qp = Xq + t * ldq + kb * 64;
+                uint32_t qd[16];
+                if (kb < KBF) {
+                    const uint4 *q4 = reinterpret_cast<const uint4 *>(qp);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        uint4 x = q4[v];
+                        qd[4 * v] = x.x; qd[4 * v + 1] = x.y; qd[4 * v + 2] = x.z; qd[4 * v + 3] = x.w;
                     }
-                    qd[v] = word;
-                }
-            }
+                } else {
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                acc[t] = __builtin_amdgcn_sdot4(static_cast<int>(c[j]), static_cast<int>(qd[j]), acc[t], false);
+                    for (int v = 0; v < 16; ++v) {
+                        uint32_t word = 0;
+                        for (int jj = 0; jj < 4; ++jj) {
+                            int64_t k = kb * 64 + 4 * v + jj;
+                            if (k < K) word |= (static_cast<uint32_t>(qp[4 * v + jj]) & 0xffu) << (8 * jj);
+                        }
+                        qd[v] = word;
+                    }
+                }
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj)
+                    acc[t] = __builtin_amdgcn_sdot4(static_cast<int>(c[jj]), static_cast<int>(qd[jj]), acc[t], false);
+            }
         }
     }
 #pragma unroll
@@ -212,32 +483,111 @@ __global__ __launch_bounds__(256) void k_gemv_addsub(const uint8_t *__restrict__
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         if (t >= M) break;
-        int total = red[0][t][lane] + red[1][t][lane] + red[2][t][lane] + red[3][t][lane];
-        int qs = qsum_part[0][t] + qsum_part[1][t] + qsum_part[2][t] + qsum_part[3][t];
+        int total = 0, qs = 0;
+        for (int w = 0; w < W; ++w) {
+            total += red[w][t][lane];
+            qs += qsum_part[w][t];
+        }
         if (n < N) store_out(Y, y_dtype, ldy, t, n, total - qs, token_scale(gamma, beta[t]));
     }
 }
 
-hipError_t launch_gemv_mfma(const GemvArgs &a, hipStream_t stream)
+// Shape choice of the MFMA GEMV: TW tiles per workgroup (reuse of each
+// activation operand, worth it when many tokens make the activations a large
+// share of the L2 -> CU traffic) and KS waves per workgroup (enough waves to
+// cover the chip: about 16 per CU).
+template <int LAYOUT, int TW>
+static void launch_mfma_tw(const GemvArgs &a, int64_t KB, int64_t NT, int64_t nsteps, hipStream_t stream)
+{
+    const int64_t groups = (NT + TW - 1) / TW;
+    const int64_t tgroups = (a.M + 15) / 16;
+    const int64_t want_waves = 256 * 16;
+    int64_t KS = (want_waves + groups * tgroups - 1) / (groups * tgroups);
+    KS = KS < 1 ? 1 : KS;
+    KS = KS > 16 ? 16 : KS;
+    KS = KS > nsteps ? nsteps : KS;
+    dim3 grid(static_cast<unsigned>(groups), static_cast<unsigned>(tgroups));
+    dim3 block(static_cast<unsigned>(KS * 64));
+    constexpr int SB = 1;
+    if (a.tiled)
+        hipLaunchKernelGGL((k_gemv_mfma<LAYOUT, TW, SB, true>), grid, block, 0, stream, a.P, KB, NT, a.gamma, a.Xq,
+                           a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
+    else
+        hipLaunchKernelGGL((k_gemv_mfma<LAYOUT, TW, SB, false>), grid, block, 0, stream, a.P, KB, NT, a.gamma, a.Xq,
+                           a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
+}
+
+template <int LAYOUT, int SPW>
+static void launch_persist(const GemvArgs &a, int64_t KB, int64_t NT, int64_t KS, hipStream_t stream)
+{
+    constexpr int TMAX = SPW >= 4 ? 4 : 8;
+    const int64_t tgroups = (a.M + 15) / 16;
+    // about one workgroup per CU in total, at most TMAX tiles each
+    int64_t wgs = 256 / tgroups;
+    const int64_t min_wgs = (NT + TMAX - 1) / TMAX;
+    wgs = wgs < min_wgs ? min_wgs : wgs;
+    wgs = wgs > NT ? NT : wgs;
+    const size_t lds = static_cast<size_t>(TMAX) * KS * 4 * 64 * sizeof(int);
+    dim3 grid(static_cast<unsigned>(wgs), static_cast<unsigned>(tgroups)), block(static_cast<unsigned>(KS * 64));
+    // more than 64 KiB of dynamic LDS must be allowed explicitly (a host-side
+    // function attribute; nothing is enqueued)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv_persist<LAYOUT, SPW, TMAX, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv_persist<LAYOUT, SPW, TMAX, false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (a.tiled)
+        hipLaunchKernelGGL((k_gemv_persist<LAYOUT, SPW, TMAX, true>), grid, block, lds, stream, a.P, KB, NT, a.gamma,
+                           a.Xq, a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
+    else
+        hipLaunchKernelGGL((k_gemv_persist<LAYOUT, SPW, TMAX, false>), grid, block, lds, stream, a.P, KB, NT, a.gamma,
+                           a.Xq, a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
+}
+
+template <int LAYOUT>
+static void launch_mfma_layout(const GemvArgs &a, hipStream_t stream)
 {
     const int64_t NT = (a.N + 15) / 16;
-    const int64_t KB = a.layout == LAYOUT_I2 ? (a.K + 63) / 64 : (a.K + 79) / 80;
-    dim3 grid(static_cast<unsigned>(NT), static_cast<unsigned>((a.M + 15) / 16));
-    if (a.layout == LAYOUT_I2)
-        hipLaunchKernelGGL(k_gemv_mfma<LAYOUT_I2>, grid, dim3(256), 0, stream, a.P, KB, NT, a.gamma, a.Xq, a.ldq,
-                           a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
+    const int64_t KB = LAYOUT == LAYOUT_I2 ? (a.K + 63) / 64 : (a.K + 79) / 80;
+    const int64_t nsteps = (KB + 3) / 4;
+    // Large layers: persistent workgroups with register-resident activations,
+    // when every CU gets at least two row tiles and the k-steps fit 16 waves x 4.
+    const int64_t tgroups = (a.M + 15) / 16;
+    if (NT >= 512 * tgroups && nsteps <= 64) {
+        const int64_t KS = nsteps < 16 ? nsteps : 16;
+        const int64_t spw = (nsteps + KS - 1) / KS;
+        if (spw <= 1) launch_persist<LAYOUT, 1>(a, KB, NT, KS, stream);
+        else if (spw <= 2) launch_persist<LAYOUT, 2>(a, KB, NT, KS, stream);
+        else launch_persist<LAYOUT, 4>(a, KB, NT, KS, stream);
+        return;
+    }
+    // Reuse each activation operand over several tiles when there are many
+    // tokens (the activations are then a large share of the L2 -> CU traffic)
+    // and enough tiles to keep every CU busy.
+    if (a.M > 4 && NT >= 1024)
+        launch_mfma_tw<LAYOUT, 4>(a, KB, NT, nsteps, stream);
+    else if (a.M > 4 && NT >= 512)
+        launch_mfma_tw<LAYOUT, 2>(a, KB, NT, nsteps, stream);
     else
-        hipLaunchKernelGGL(k_gemv_mfma<LAYOUT_B3>, grid, dim3(256), 0, stream, a.P, KB, NT, a.gamma, a.Xq, a.ldq,
-                           a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
+        launch_mfma_tw<LAYOUT, 1>(a, KB, NT, nsteps, stream);
+}
+
+hipError_t launch_gemv_mfma(const GemvArgs &a, hipStream_t stream)
+{
+    if (a.layout == LAYOUT_I2)
+        launch_mfma_layout<LAYOUT_I2>(a, stream);
+    else
+        launch_mfma_layout<LAYOUT_B3>(a, stream);
     return hipGetLastError();
 }
 
 template <int MT>
 static void launch_addsub_mt(const GemvArgs &a, int64_t KB, int64_t NT, hipStream_t stream)
 {
+    int64_t W = (KB + 3) / 4;
+    W = W < 1 ? 1 : (W > 16 ? 16 : W);
     dim3 grid(static_cast<unsigned>((NT + 3) / 4));
-    hipLaunchKernelGGL(k_gemv_addsub<MT>, grid, dim3(256), 0, stream, a.P, KB, NT, a.gamma, a.Xq, a.ldq, a.beta,
-                       a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
+    hipLaunchKernelGGL(k_gemv_addsub<MT>, grid, dim3(static_cast<unsigned>(W * 64)), 0, stream, a.P, KB, NT, a.gamma,
+                       a.Xq, a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
 }
 
 hipError_t launch_gemv_addsub(const GemvArgs &a, hipStream_t stream)

@@ -17,6 +17,18 @@ hipError_t launch_pack(const int8_t *T, int64_t N, int64_t K, int64_t ldt, int l
 hipError_t launch_quant_act(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int8_t *Xq,
                             int64_t ldq, float *beta, hipStream_t stream);
 
+// Tiled activation layout: see bitlinear_act_tiled_bytes in bitlinear.h.
+inline int64_t tiled_step_k(int layout) { return layout == 0 ? 256 : 320; }
+inline int64_t tiled_nmf(int layout) { return layout == 0 ? 4 : 5; }
+inline int64_t tiled_nsteps(int64_t K, int layout) { return (K + tiled_step_k(layout) - 1) / tiled_step_k(layout); }
+inline int64_t tiled_bytes(int64_t M, int64_t K, int layout)
+{
+    return (M + 15) / 16 * tiled_nsteps(K, layout) * tiled_nmf(layout) * 1024;
+}
+
+hipError_t launch_quant_act_tiled(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int layout,
+                                  int8_t *Xt, float *beta, hipStream_t stream);
+
 // Product + rescale on int8 activations Xq [M x K] (row stride ldq, 16-byte
 // aligned rows) with per-token beta.
 struct GemvArgs {
@@ -26,6 +38,7 @@ struct GemvArgs {
     int64_t M, N, K;
     const int8_t *Xq;
     int64_t ldq;
+    bool tiled; // Xq holds the tiled activation layout (ldq unused)
     const float *beta;
     void *Y;
     int y_dtype;

@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void k_pack_i2(const int8_t *__restrict__ T, i
 }
 
 // b3 packing: one thread per (row n, 80-weight block kb); byte i holds
-// weights 5i .. 5i+4 of the block as a base-3 number, first weight most significant.
+// weights 16t + i (t = 0..4) of the block as a base-3 number, t = 0 most significant.
 __global__ __launch_bounds__(256) void k_pack_b3(const int8_t *__restrict__ T, int64_t N, int64_t K,
                                                  int64_t ldt, int64_t KB, int64_t nchunks,
                                                  uint8_t *__restrict__ P)
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void k_pack_b3(const int8_t *__restrict__ T, i
     for (int i = 0; i < 16; ++i) {
         uint32_t b = 0;
         for (int t = 0; t < 5; ++t) {
-            int64_t k = kb * 80 + 5 * i + t;
+            int64_t k = kb * 80 + 16 * t + i;
             int v = (n < N && k < K) ? T[n * ldt + k] : 0;
             b = b * 3u + static_cast<uint32_t>(v + 1);
         }

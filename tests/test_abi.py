@@ -133,6 +133,57 @@ def test_forward_rejects(kw, status):
     assert fw(**kw) == status
 
 
+def test_tiled_sizes():
+    # I2: 256 weights and 4 operands per k-step; B3: 320 and 5; 1 KiB per operand
+    assert bl.bitlinear_act_tiled_bytes(16, 3200, bl.LAYOUT_I2) == 1 * 13 * 4 * 1024
+    assert bl.bitlinear_act_tiled_bytes(17, 3200, bl.LAYOUT_I2) == 2 * 13 * 4 * 1024
+    assert bl.bitlinear_act_tiled_bytes(1, 8192, bl.LAYOUT_B3) == 1 * 26 * 5 * 1024
+    assert bl.bitlinear_act_tiled_bytes(0, 64, bl.LAYOUT_I2) == -1
+    assert bl.bitlinear_act_tiled_bytes(4, 64, 3) == -1
+
+
+def qt(**kw):
+    a = dict(X=A, x_dtype=bl.BF16, M=16, K=256, ldx=256, layout=bl.LAYOUT_I2, Xt=B, xt_bytes=4096, beta=C,
+             stream=None)
+    a.update(kw)
+    return bl.bitlinear_quantize_act_tiled(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), bl.ERR_INVALID_ARG), (dict(Xt=None), bl.ERR_INVALID_ARG), (dict(beta=None), bl.ERR_INVALID_ARG),
+    (dict(layout=9), bl.ERR_INVALID_ARG), (dict(x_dtype=bl.I8), bl.ERR_INVALID_ARG), (dict(M=0), bl.ERR_INVALID_ARG),
+    (dict(ldx=255), bl.ERR_INVALID_ARG), (dict(xt_bytes=4095), bl.ERR_INVALID_ARG), (dict(Xt=B + 4), bl.ERR_INVALID_ARG),
+    (dict(Xt=A + 64), bl.ERR_INVALID_ARG),
+    (dict(K=70000, ldx=70000, xt_bytes=1 << 30), bl.ERR_UNSUPPORTED),
+])
+def test_quantize_act_tiled_rejects(kw, status):
+    assert qt(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x_dtype=bl.I8_TILED), bl.ERR_INVALID_ARG),                                   # needs beta_in
+    (dict(x_dtype=bl.I8_TILED, beta_in=B + 64, X=C + 8), bl.ERR_INVALID_ARG),          # alignment
+    (dict(x_dtype=bl.I8_TILED, beta_in=B + 64, algo=bl.ALGO_GEMV_ADDSUB), bl.ERR_UNSUPPORTED),
+    (dict(x_dtype=bl.I8_TILED, beta_in=B + 64, algo=bl.ALGO_GEMM_MFMA), bl.ERR_UNSUPPORTED),
+    (dict(x_dtype=bl.I8_TILED, beta_in=B + 64, Y=C), bl.ERR_INVALID_ARG),              # Y overlaps X
+])
+def test_forward_tiled_rejects(kw, status):
+    assert fw(**kw) == status
+
+
 def test_forward_plain_entry_validates_too():
     assert bl.bitlinear_forward(None, 0, B, 4, 64, 64, C, bl.BF16, 64, None, D, bl.F32, 64, E, 1 << 20, None) \
         == bl.ERR_INVALID_ARG
+
+
+def test_one_hip_runtime_when_loaded_first():
+    """Importing the binding before anything else must still leave a single
+    HIP runtime in the process (torch bundles its own libamdhip64)."""
+    import subprocess
+    import sys
+    code = ("from ternary_weight_linear_forward_amd import bitlinear as bl\n"
+            "import torch\n"
+            "rt = bl._hip_runtimes_loaded()\n"
+            "assert len(rt) == 1, rt\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]

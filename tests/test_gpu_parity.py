@@ -108,6 +108,52 @@ def test_quantize_act(name, x):
     assert np.array_equal(f32_bits(to_host(beta)), f32_bits(b_ref))
 
 
+def untile(xt: np.ndarray, M: int, K: int, layout: str) -> np.ndarray:
+    """Read q[m][k] back out of the tiled activation layout (the byte formula of
+    bitlinear_act_tiled_bytes), and check that every other byte is zero."""
+    S, F = (256, 4) if layout == "i2" else (320, 5)
+    nsteps = -(-K // S)
+    G = -(-M // 16)
+    m = np.arange(G * 16)[:, None]
+    k = np.arange(nsteps * S)[None, :]
+    s, r = k // S, k % S
+    g, r2 = r // (S // 4), r % (S // 4)
+    d, e = r2 // 16, r2 % 16
+    off = ((((m // 16) * nsteps + s) * F + d) * 64 + g * 16 + (m % 16)) * 16 + e
+    full = xt[off]
+    assert off.size == xt.size and np.unique(off).size == off.size
+    assert not full[M:, :].any() and not full[:, K:].any()
+    return full[:M, :K]
+
+
+@pytest.mark.parametrize("layout", ["i2", "b3"])
+@pytest.mark.parametrize("M,K,kind", [(16, 256, "f32"), (5, 3200, "bf16"), (20, 333, "bf16"), (1, 80, "f32"),
+                                      (33, 8192, "bf16"), (3, 28672, "bf16")])
+def test_quantize_act_tiled(layout, M, K, kind):
+    log("quantize_act_tiled", layout, M, K, kind)
+    x = synth.activations_f32(M, K, seed=M + K) if kind == "f32" else synth.activations_bf16(M, K, seed=M + K)
+    Xt, beta = bl.quantize_act_tiled(to_dev(x), LAYOUTS[layout])
+    q_ref, b_ref = oracle.quantize_act(x)
+    assert np.array_equal(untile(to_host(Xt), M, K, layout), q_ref)
+    assert np.array_equal(f32_bits(to_host(beta)), f32_bits(b_ref))
+
+
+@pytest.mark.parametrize("layout", ["i2", "b3"])
+@pytest.mark.parametrize("M,N,K", [(16, 512, 256), (7, 100, 333), (40, 260, 700), (1, 48, 3200)])
+def test_forward_tiled_input(layout, M, N, K):
+    log("forward tiled", layout, M, N, K)
+    t = synth.ternary_weights(N, K, seed=N + K)
+    x = synth.activations_bf16(M, K, seed=M * 3 + K)
+    ref = oracle.forward(t, np.float32(0.03), x)
+    P = to_dev(oracle.pack(t, LAYOUTS[layout]))
+    gamma = to_dev(np.array([0.03], np.float32))
+    Xt, beta = bl.quantize_act_tiled(to_dev(x), LAYOUTS[layout])
+    acc = to_host(bl.forward(P, LAYOUTS[layout], gamma, Xt, N, K, beta=beta, y_dtype=torch.int32))
+    assert np.array_equal(acc, ref["acc"])
+    y = to_host(bl.forward(P, LAYOUTS[layout], gamma, Xt, N, K, beta=beta))
+    assert_f32_parity(y, ref["y"])
+
+
 # ---------------------------------------------------------------------------
 # forward: every kernel, several tiles, ragged tails
 # ---------------------------------------------------------------------------
@@ -157,6 +203,15 @@ def test_forward_small(algo_name, algo, layout, M, N, K):
 def test_forward_many_tokens(algo_name, algo, layout, M, N, K):
     log("forward", algo_name, layout, M, N, K)
     run_forward_case(M, N, K, algo, layout, seed=M * 131 + N + K)
+
+
+@pytest.mark.parametrize("layout", ["i2", "b3"])
+@pytest.mark.parametrize("M,N,K", [(20, 16400, 300), (64, 16390, 70), (16, 8200, 100), (5, 16384, 1000)])
+def test_forward_wide_short(layout, M, N, K):
+    """Many row tiles and few k-steps: a workgroup owns several tiles and may
+    have fewer waves than tiles."""
+    log("forward wide", layout, M, N, K)
+    run_forward_case(M, N, K, bl.ALGO_GEMV_MFMA, layout, seed=M + N + K, y_kinds=("i32", "f32"))
 
 
 def test_forward_f32_input_tiny():
