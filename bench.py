@@ -166,8 +166,6 @@ def main():
     # time the product kernel alone the same two steps are issued through the
     # split entry points, in the same way bitlinear_forward dispatches them.
     def plan(M):
-        if M <= 16 and layout == bl.LAYOUT_I2 and M <= 4:
-            return "rowmajor", bl.ALGO_GEMV_ADDSUB, f"k_gemv_addsub<{1 if M <= 1 else 2 if M <= 2 else 4}>"
         if M <= 16 or layout == bl.LAYOUT_B3:
             if M > 4:
                 return "tiled", bl.ALGO_GEMV_MFMA, f"k_gemv_mfma<{layout},tiled>"

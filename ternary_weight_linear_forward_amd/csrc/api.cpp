@@ -12,8 +12,12 @@
 namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40; // keeps per-exponent sums of |W| below 2^64
-// Largest M the add/subtract GEMV takes when the kernel is chosen automatically.
-constexpr int64_t kAddSubMaxM = 4;
+// Largest M the add/subtract GEMV takes when the kernel is chosen
+// automatically.  Measured on MI355X the matrix-core GEMV is faster at every M
+// (the vector ALU reaches 4 int8 MACs per lane-cycle, the matrix core takes the
+// MACs off it), so automatic dispatch never picks add/subtract; it stays
+// available as BITLINEAR_ALGO_GEMV_ADDSUB.
+constexpr int64_t kAddSubMaxM = 0;
 
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

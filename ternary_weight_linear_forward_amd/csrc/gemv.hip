@@ -196,6 +196,16 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
     }
     const uint32_t lane_off = static_cast<uint32_t>(g) * 256u + static_cast<uint32_t>(i) * 16u;
     const uint32_t last_kb_off = static_cast<uint32_t>(KB - 1) * 256u + static_cast<uint32_t>(i) * 16u;
+    // rescale factors of this lane's 4 output tokens, loaded before the product
+    float sc[4];
+    {
+        const float gamma = *gamma_p;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int64_t mm = static_cast<int64_t>(blockIdx.y) * 16 + 4 * g + rr;
+            sc[rr] = mm < M ? token_scale(gamma, beta[mm]) : 0.0f;
+        }
+    }
 
     v4i acc[TW];
 #pragma unroll
@@ -259,7 +269,6 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
 #pragma unroll
     for (int t = 0; t < TW; ++t) red[t][wave][lane] = acc[t];
     __syncthreads();
-    const float gamma = *gamma_p;
     // tile t is finished by wave t % KS (KS may be smaller than TW)
     for (int t = wave; t < TW; t += KS) {
         const int64_t tile = tile0 + t;
@@ -271,7 +280,7 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const int64_t mm = static_cast<int64_t>(blockIdx.y) * 16 + 4 * g + rr;
-            if (mm < M && n < N) store_out(Y, y_dtype, ldy, mm, n, tot[rr], token_scale(gamma, beta[mm]));
+            if (mm < M && n < N) store_out(Y, y_dtype, ldy, mm, n, tot[rr], sc[rr]);
         }
     }
 }
@@ -304,6 +313,16 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const uint8_t *__restrict
     const int64_t m_a = static_cast<int64_t>(blockIdx.y) * 16 + i;
     const int64_t G = gridDim.x;
     const int ntiles = static_cast<int>((NT - blockIdx.x + G - 1) / G); // tiles of this workgroup (<= TMAX)
+    // rescale factors of this lane's 4 output tokens, loaded before the product
+    float sc[4];
+    {
+        const float gamma = *gamma_p;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int64_t mm = static_cast<int64_t>(blockIdx.y) * 16 + 4 * g + rr;
+            sc[rr] = mm < M ? token_scale(gamma, beta[mm]) : 0.0f;
+        }
+    }
 
     // activation operands of this wave's k-steps, loaded once (zero past K)
     v4i a[SPW][NMF];
@@ -359,7 +378,6 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const uint8_t *__restrict
         for (int rr = 0; rr < 4; ++rr) red[((t * KS + wave) * 4 + rr) * 64 + lane] = acc[t][rr];
     }
     __syncthreads();
-    const float gamma = *gamma_p;
     // output group (t, rr): tokens 4g + rr of this token group, weight row i of tile t
     for (int task = wave; task < ntiles * 4; task += KS) {
         const int t = task >> 2, rr = task & 3;
@@ -367,7 +385,11 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const uint8_t *__restrict
         for (int w = 0; w < KS; ++w) tot += red[((t * KS + w) * 4 + rr) * 64 + lane];
         const int64_t n = (blockIdx.x + t * G) * 16 + i;
         const int64_t mm = static_cast<int64_t>(blockIdx.y) * 16 + 4 * g + rr;
-        if (mm < M && n < N) store_out(Y, y_dtype, ldy, mm, n, tot, token_scale(gamma, beta[mm]));
+        float s_rr = sc[0];
+        s_rr = rr == 1 ? sc[1] : s_rr;
+        s_rr = rr == 2 ? sc[2] : s_rr;
+        s_rr = rr == 3 ? sc[3] : s_rr;
+        if (mm < M && n < N) store_out(Y, y_dtype, ldy, mm, n, tot, s_rr);
     }
 }
 
@@ -422,6 +444,12 @@ __global__ __launch_bounds__(1024) void k_gemv_addsub(const uint8_t *__restrict_
         }
     }
 
+    float sc[MT]; // rescale factors, loaded before the product
+    {
+        const float gamma = *gamma_p;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) sc[t] = t < M ? token_scale(gamma, beta[t]) : 0.0f;
+    }
     int acc[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[t] = 0;
@@ -478,7 +506,6 @@ __global__ __launch_bounds__(1024) void k_gemv_addsub(const uint8_t *__restrict_
     for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
     __syncthreads();
     if (wave != 0) return;
-    const float gamma = *gamma_p;
     const int64_t n = tile * 16 + r;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -488,7 +515,7 @@ __global__ __launch_bounds__(1024) void k_gemv_addsub(const uint8_t *__restrict_
             total += red[w][t][lane];
             qs += qsum_part[w][t];
         }
-        if (n < N) store_out(Y, y_dtype, ldy, t, n, total - qs, token_scale(gamma, beta[t]));
+        if (n < N) store_out(Y, y_dtype, ldy, t, n, total - qs, sc[t]);
     }
 }
 
