@@ -13,6 +13,12 @@ throughput is reported separately under "weight_prep").  Steps rotate over
 copies of the packed weights totalling >= 1 GiB so that neither the L2 nor
 the 256 MB Infinity Cache serves them.  Each step is a captured HIP graph.
 
+--workload stack_3b_26 times one token step (batch 16) through 26 decoder
+layers of the 3B model's BitLinears, 104 forwards with all weights resident:
+per layer qkv (9600 x 3200), o (3200 x 3200) reading the first 3200 columns
+of qkv's output, gate_up (17280 x 3200), down (3200 x 8640) reading the first
+8640 columns of gate_up's output; down's output feeds the next layer.
+
 One JSON line is printed.  'value' is packed-weight GB/s over the whole step
 (wall clock around K replays); 'roofline' reports the dominant kernel from a
 replay in which every launch of it is bracketed by HIP events; 'cpu_baseline'
@@ -73,12 +79,20 @@ def main():
     print(f"[bench] workload={wl.name} batches={batches} layout={args.layout}", file=sys.stderr, flush=True)
 
     # ---- weights: quantise + pack on the GPU (timed separately) --------------
+    # The stack has 4 * 26 distinct weight tensors; the other workloads one
+    # tensor per named layer.
+    if wl is workloads.STACK_3B:
+        chain = workloads.stack_chain(workloads.STACK_DEPTH)
+        weight_specs = [(link.layer, workloads.seed_for(wl, link.index, 0)) for link in chain]
+    else:
+        chain = None
+        weight_specs = [(layer, workloads.seed_for(wl, li, 0)) for li, layer in enumerate(wl.layers)]
     layers = []
     prep_ms = 0.0
     prep_bytes = 0
     with torch.cuda.stream(stream):
-        for li, layer in enumerate(wl.layers):
-            w = torch.from_numpy(synth.latent_weights(layer.N, layer.K, seed=workloads.seed_for(wl, li, 0))).to(dev)
+        for layer, seed in weight_specs:
+            w = torch.from_numpy(synth.latent_weights(layer.N, layer.K, seed=seed)).to(dev)
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -98,19 +112,39 @@ def main():
     print(f"[bench] packed set {set_bytes/1e6:.1f} MB x {ncopies} copies", file=sys.stderr, flush=True)
 
     # ---- activations, outputs, workspaces --------------------------------------
+    # A job is one bitlinear_forward: input pointer/dtype/row stride, output.
     act = synth.activations_student_t_bf16 if wl.act_dist == "student_t" else synth.activations_bf16
-    jobs = []
-    for M in batches:
-        for li, L in enumerate(layers):
-            layer = L["layer"]
-            x = act(M, layer.K, seed=workloads.seed_for(wl, li, 1) + M)
-            xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
-            nws = bl.bitlinear_forward_workspace_bytes(M, layer.N, layer.K, layout, bl.BF16)
-            jobs.append({
-                "M": M, "L": L, "x": xd,
+    keep = []
+
+    def make_job(M, L, x_ptr, x_dtype, ldx):
+        layer = L["layer"]
+        nws = bl.bitlinear_forward_workspace_bytes(M, layer.N, layer.K, layout, x_dtype)
+        return {"M": M, "L": L, "x_ptr": x_ptr, "x_dtype": x_dtype, "ldx": ldx,
                 "ws": torch.empty(max(nws, 16), dtype=torch.uint8, device=dev), "nws": nws,
-                "y": torch.empty((M, layer.N), dtype=torch.float32, device=dev),
-            })
+                "y": torch.empty((M, layer.N), dtype=torch.float32, device=dev)}
+
+    def bf16_input(M, K, seed):
+        xd = torch.from_numpy(act(M, K, seed=seed).view(np.int16)).to(dev).view(torch.bfloat16)
+        keep.append(xd)
+        return xd
+
+    jobs = []
+    if chain is not None:
+        # One token step through the stack: link i reads the first K columns
+        # of link i-1's fp32 output and quantises them inside its forward.
+        M = batches[0]
+        x0 = bf16_input(M, chain[0].layer.K, workloads.seed_for(wl, 0, 1))
+        for link, L in zip(chain, layers):
+            if link.index == 0:
+                jobs.append(make_job(M, L, x0.data_ptr(), bl.BF16, x0.stride(0)))
+            else:
+                prev = jobs[-1]["y"]
+                jobs.append(make_job(M, L, prev.data_ptr(), bl.F32, prev.stride(0)))
+    else:
+        for M in batches:
+            for li, L in enumerate(layers):
+                xd = bf16_input(M, L["layer"].K, workloads.seed_for(wl, li, 1) + M)
+                jobs.append(make_job(M, L, xd.data_ptr(), bl.BF16, xd.stride(0)))
     torch.cuda.synchronize()
 
     def launch_job(j, copy):
@@ -118,7 +152,7 @@ def main():
         L = j["L"]
         layer = L["layer"]
         st = bl.bitlinear_forward(L["P"][copy].data_ptr(), layout, L["gamma"].data_ptr(), j["M"], layer.N, layer.K,
-                                  j["x"].data_ptr(), bl.BF16, j["x"].stride(0), None, j["y"].data_ptr(), bl.F32,
+                                  j["x_ptr"], j["x_dtype"], j["ldx"], None, j["y"].data_ptr(), bl.F32,
                                   j["y"].stride(0), j["ws"].data_ptr(), j["nws"], stream.cuda_stream)
         if st:
             raise bl.BitlinearError(st, "bitlinear_forward")
@@ -203,12 +237,12 @@ def main():
                 kind, algo, name = j["plan"]
                 s = stream.cuda_stream
                 if kind == "tiled":
-                    bl.bitlinear_quantize_act_tiled(j["x"].data_ptr(), bl.BF16, j["M"], layer.K, j["x"].stride(0),
+                    bl.bitlinear_quantize_act_tiled(j["x_ptr"], j["x_dtype"], j["M"], layer.K, j["ldx"],
                                                     layout, j["xq"].data_ptr(), j["xq"].numel(),
                                                     j["beta"].data_ptr(), s)
                     xdt = bl.I8_TILED
                 else:
-                    bl.bitlinear_quantize_act(j["x"].data_ptr(), bl.BF16, j["M"], layer.K, j["x"].stride(0),
+                    bl.bitlinear_quantize_act(j["x_ptr"], j["x_dtype"], j["M"], layer.K, j["ldx"],
                                               j["xq"].data_ptr(), j["ldq"], j["beta"].data_ptr(), s)
                     xdt = bl.I8
                 ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -271,7 +305,12 @@ def main():
             "layers": {L["layer"].name: [L["layer"].N, L["layer"].K] for L in layers},
             "batches": list(batches),
             "layout": args.layout,
-            "x_dtype": "bf16",
+            "x_dtype": "bf16" if chain is None else "bf16 stack input, fp32 between links",
+            **({"depth": workloads.STACK_DEPTH,
+                "glue": "qkv -> o reads qkv[:, :3200]; gate_up -> down reads gate_up[:, :8640]; "
+                        "down -> next layer's qkv; per-token int8 requantisation inside every forward"}
+               if chain is not None else {}),
+            "bitlinears_per_step": len(jobs),
             "y_dtype": "f32",
             "weight_copies": ncopies,
             "graph_replay": True,

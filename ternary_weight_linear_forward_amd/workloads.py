@@ -88,3 +88,28 @@ ALL = {w.name: w for w in (TINY, DECODE_3B, PREFILL_3B, LAYERS_70B, STACK_3B)}
 def seed_for(workload: Workload, layer_index: int, tensor: int, copy: int = 0) -> int:
     """Seed of one tensor: the workload base + layer, tensor kind and copy index."""
     return workload.seed + 1000 * copy + 10 * layer_index + tensor
+
+
+@dataclass(frozen=True)
+class StackLink:
+    """One BitLinear of the stack in execution order.  Its input is the first
+    K columns of the previous link's output (width 'ld_in'), or the stack
+    input X0 for the first link."""
+    index: int        # 0 .. 4*depth-1, execution order
+    depth: int        # decoder layer 0 .. depth-1
+    layer: Layer
+    ld_in: int        # row stride of the input (the producer's N; K for X0)
+
+
+def stack_chain(depth: int = STACK_DEPTH) -> list:
+    """The stack's BitLinears: per decoder layer qkv (3200 -> 9600), o reading
+    columns 0..3199 of qkv's output, gate_up (3200 -> 17280), down reading
+    columns 0..8639 of gate_up's output.  down's output feeds the next
+    layer's qkv.  Each link re-quantises its fp32 input per token."""
+    links = []
+    prev_n = STACK_3B.layers[0].K
+    for d in range(depth):
+        for layer in STACK_3B.layers:
+            links.append(StackLink(len(links), d, layer, prev_n))
+            prev_n = layer.N
+    return links
