@@ -199,16 +199,19 @@ def main():
     # bitlinear_forward runs a quantiser kernel, then the product kernel.  To
     # time the product kernel alone the same two steps are issued through the
     # split entry points, in the same way bitlinear_forward dispatches them.
-    def plan(M):
-        if M <= 16 or layout == bl.LAYOUT_B3:
-            if M > 4:
-                return "tiled", bl.ALGO_GEMV_MFMA, f"k_gemv_mfma<{layout},tiled>"
-            return "rowmajor", bl.ALGO_GEMV_MFMA, f"k_gemv_mfma<{layout},rowmajor>"
-        return "rowmajor", bl.ALGO_GEMM_MFMA, "k_gemm_mfma_i2"
+    def plan(M, N, K):
+        algo = bl.bitlinear_auto_algo(M, N, K, layout, bl.BF16)
+        lname = "i2" if layout == bl.LAYOUT_I2 else "b3"
+        if algo == bl.ALGO_GEMV_MFMA:
+            kind = "tiled" if M > 4 and K <= 65536 else "rowmajor"
+            return kind, algo, f"k_gemv_mfma|k_gemv_persist <{lname},{kind}>"
+        if algo == bl.ALGO_GEMM_MFMA:
+            return "rowmajor", algo, "k_gemm_mfma_i2"
+        raise RuntimeError(f"unexpected automatic algorithm {algo}")
 
     for j in jobs:
         layer = j["L"]["layer"]
-        kind, algo, name = plan(j["M"])
+        kind, algo, name = plan(j["M"], layer.N, layer.K)
         j["plan"] = (kind, algo, name)
         if kind == "tiled":
             nb = bl.bitlinear_act_tiled_bytes(j["M"], layer.K, layout)

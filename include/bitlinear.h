@@ -113,6 +113,15 @@ int64_t bitlinear_quantize_weights_workspace_bytes(int64_t N, int64_t K);
 int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int layout, int x_dtype);
 
 /*
+ * The product algorithm bitlinear_forward (algo AUTO) runs for these sizes:
+ * BITLINEAR_ALGO_GEMV_MFMA for pre-tiled input, for M <= 16 and for the b3
+ * layout, and for larger M when the GEMM would launch too few workgroup tiles
+ * to fill the GPU; BITLINEAR_ALGO_GEMM_MFMA otherwise.  Returns -1 for invalid
+ * sizes, layout or dtype.  Host-only; enqueues nothing.
+ */
+int bitlinear_auto_algo(int64_t M, int64_t N, int64_t K, int layout, int x_dtype);
+
+/*
  * Absmean weight ternarisation (LIT-380 Key takeaways bullet 1).
  *   W      fp32 [N x K], row stride ldw >= K (device, read-only).
  *   T      int8 [N x K], row stride K (device, written): values in {-1, 0, +1}.

@@ -18,6 +18,21 @@ constexpr int64_t kMaxElems = int64_t(1) << 40; // keeps per-exponent sums of |W
 // MACs off it), so automatic dispatch never picks add/subtract; it stays
 // available as BITLINEAR_ALGO_GEMV_ADDSUB.
 constexpr int64_t kAddSubMaxM = 0;
+// Fewest GEMM workgroup tiles for which the GEMM beats the matrix-core GEMV
+// (token groups of 16) when there are more than 16 tokens: with fewer tiles
+// most CUs idle (measured on the 70B k/v and q layers at 64 and 176 tokens).
+constexpr int64_t kGemmMinTiles = 128;
+
+// The product kernel of algo AUTO (sizes already validated).
+int auto_algo(int64_t M, int64_t N, int layout, int x_dtype)
+{
+    if (x_dtype == BITLINEAR_I8_TILED) return BITLINEAR_ALGO_GEMV_MFMA;
+    if (M <= 16)
+        return (layout == BITLINEAR_LAYOUT_I2 && M <= kAddSubMaxM) ? BITLINEAR_ALGO_GEMV_ADDSUB
+                                                                   : BITLINEAR_ALGO_GEMV_MFMA;
+    return layout == BITLINEAR_LAYOUT_I2 && bl::gemm_tiles(M, N) >= kGemmMinTiles ? BITLINEAR_ALGO_GEMM_MFMA
+                                                                                 : BITLINEAR_ALGO_GEMV_MFMA;
+}
 
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -103,6 +118,17 @@ int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int l
     if (x_dtype == BITLINEAR_I8 || x_dtype == BITLINEAR_I8_TILED) return 0;
     if (x_dtype != BITLINEAR_F32 && x_dtype != BITLINEAR_BF16) return -1;
     return staged_xq_bytes(M, K, layout) + round_up(4 * M, 256);
+}
+
+int bitlinear_auto_algo(int64_t M, int64_t N, int64_t K, int layout, int x_dtype)
+{
+    if (M < 1 || M > BITLINEAR_MAX_M || N < 1 || N > (int64_t(1) << 31) || K < 1 || K > BITLINEAR_MAX_K ||
+        !valid_layout(layout))
+        return -1;
+    if (x_dtype != BITLINEAR_F32 && x_dtype != BITLINEAR_BF16 && x_dtype != BITLINEAR_I8 &&
+        x_dtype != BITLINEAR_I8_TILED)
+        return -1;
+    return auto_algo(M, N, layout, x_dtype);
 }
 
 int64_t bitlinear_act_tiled_bytes(int64_t M, int64_t K, int layout)
@@ -218,15 +244,7 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
             return BITLINEAR_ERR_INVALID_ARG;
     }
 
-    if (algo == BITLINEAR_ALGO_AUTO) {
-        if (x_dtype == BITLINEAR_I8_TILED)
-            algo = BITLINEAR_ALGO_GEMV_MFMA;
-        else if (M <= 16)
-            algo = (layout == BITLINEAR_LAYOUT_I2 && M <= kAddSubMaxM) ? BITLINEAR_ALGO_GEMV_ADDSUB
-                                                                       : BITLINEAR_ALGO_GEMV_MFMA;
-        else
-            algo = layout == BITLINEAR_LAYOUT_I2 ? BITLINEAR_ALGO_GEMM_MFMA : BITLINEAR_ALGO_GEMV_MFMA;
-    }
+    if (algo == BITLINEAR_ALGO_AUTO) algo = auto_algo(M, N, layout, x_dtype);
     if (algo == BITLINEAR_ALGO_GEMV_ADDSUB && (M > 16 || layout != BITLINEAR_LAYOUT_I2))
         return BITLINEAR_ERR_UNSUPPORTED;
     if (algo == BITLINEAR_ALGO_GEMM_MFMA && layout != BITLINEAR_LAYOUT_I2) return BITLINEAR_ERR_UNSUPPORTED;

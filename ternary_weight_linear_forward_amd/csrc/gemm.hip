@@ -3,28 +3,48 @@
 // At large M the BitLinear product (LIT-380 record, Key takeaways, bullet 4:
 // integer additions of activations selected by ternary weights) is a dense
 // contraction whose arithmetic, not HBM, is the bound: every packed weight is
-// used by thousands of tokens.  So the ternary weights are unpacked once per
-// workgroup into signed int8 tiles in LDS and multiplied with int8 activation
-// tiles by v_mfma_i32_32x32x32_i8.  The epilogue applies
-// y = float(acc) * (gamma * beta_m) / 127.
+// used by hundreds of tokens.  So it runs as v_mfma_i32_32x32x32_i8 on int8
+// activation tiles and signed-byte weight operands unpacked from the 2-bit
+// codes in registers.  The epilogue applies y = float(acc) * (gamma*beta_m)/127.
 //
-// Workgroup tile BM tokens x 128 weight rows, 4 waves in a 2 x 2 grid, each
-// (BM/2) x 64 = (BM/64) x 2 MFMA tiles of 32 x 32.  Per stage 128 weights of
-// k (two k-blocks): the activation tile (BM x 128 bytes) and the unpacked
-// weight tile (128 x 128 bytes) sit in LDS, double-buffered, one barrier per
-// stage; global loads run one stage ahead in registers.  LDS rows are padded
-// to 144 bytes so that the 16-byte operand reads of a wave hit distinct banks.
+// Workgroup tile: BM tokens x BN weight rows, 4 waves in a 2 x 2 grid, each
+// (BM/2) x (BN/2) = MI x NI MFMA tiles of 32 x 32.  A stage covers 128 k (two
+// 64-weight k-blocks).  Both operands of a stage go from global memory
+// straight to LDS (global_load_lds_dwordx4: no registers, no LDS write
+// instructions), into a ring of NST stage buffers; the loads of stage s+NST-1
+// are issued while stage s is multiplied, so NST-1 stages of memory latency
+// are hidden.
+//  * Activations: BM rows of 128 bytes per stage.  The 16-byte unit g of row r
+//    sits at slot g ^ swz(r), so the 32 rows read by one MFMA operand load
+//    spread over all LDS banks.
+//  * Weights: the packed 256-byte chunks (16 rows x 64 weights) of the stage,
+//    copied as they are (BN/16 tiles x 2 k-blocks = BN * 32 bytes).  Each lane
+//    reads the one 32-bit word holding its 16 weights of an operand and
+//    unpacks it with four v_perm_b32.
+// Only s_barrier (no memory fence) separates the stages; the explicit vmcnt
+// wait before it covers this wave's own copies of the stage, and the barrier
+// then covers every wave's.
 #include "common.h"
 #include "launch.h"
 
 namespace bl {
 
 namespace {
-constexpr int BN = 128;       // weight rows per workgroup (8 tiles of 16)
-constexpr int KSTEP = 128;    // k per LDS stage: two 64-weight k-blocks
-constexpr int LDS_ROW = 144;  // 128 bytes of k + 16 bytes of padding
+constexpr int KSTEP = 128;              // k per stage: two 64-weight k-blocks
+constexpr int LDS_RING_BYTES = 150 * 1024; // LDS given to the stage ring (of 160 KB)
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+// Word 3 of a raw buffer resource on gfx9 parts: 32-bit data format, no swizzle.
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
+
+// s_waitcnt immediate that waits for vmcnt <= n and nothing else (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and lgkmcnt at max).
+constexpr int vmcnt_only(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+// ... and also for every LDS read of this wave (lgkmcnt 0)
+constexpr int vmcnt_lgkm0(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14); }
 } // namespace
+
+__device__ __forceinline__ int a_swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 __device__ __forceinline__ v4i gemm_i2_word_signed(uint32_t w)
 {
@@ -36,23 +56,63 @@ __device__ __forceinline__ v4i gemm_i2_word_signed(uint32_t w)
     return r;
 }
 
-template <int BM, int S>
-__global__ __launch_bounds__(256) void k_gemm_mfma_i2(const uint8_t *__restrict__ P, int64_t KB, int64_t NT,
-                                                      const float *__restrict__ gamma_p,
-                                                      const int8_t *__restrict__ Xq, int64_t ldq,
-                                                      const float *__restrict__ beta, int64_t M, int64_t N,
-                                                      int64_t K, void *__restrict__ Y, int y_dtype, int64_t ldy)
+// One wave-wide copy into LDS through a raw buffer resource over [base,
+// base + nbytes): lane i's SZ bytes at byte voff land at dst + SZ * i; reads
+// at or past nbytes return zeros without touching memory.  (The buffer
+// builtins exist only in the device pass.)
+template <int SZ>
+__device__ __forceinline__ void buffer_copy_to_lds(const void *base, int nbytes, lds_void_t *dst, int voff)
 {
-    constexpr int MI = BM / 64;             // 32-row MFMA tiles per wave along M
-    constexpr int NI = 2;                   // 32-column MFMA tiles per wave along N
-    constexpr int A_LOADS = BM * KSTEP / 16 / 256; // 16-byte activation loads per thread per stage
-    __shared__ __attribute__((aligned(16))) int8_t As[2][BM * LDS_ROW];
-    __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * LDS_ROW];
-    __shared__ float scale[BM]; // per-token rescale factors, computed once up front
-    const int tid = threadIdx.x;
+#if defined(__HIP_DEVICE_COMPILE__)
+    // base and nbytes are wave-uniform; say so, so that the resource stays in
+    // scalar registers
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t bu = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32))) << 32) |
+                        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void *>(bu), 0, __builtin_amdgcn_readfirstlane(nbytes), BUF_RSRC_WORD3);
+    if constexpr (SZ == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, voff, 0, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ void stage_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__restrict__ P, int64_t KB,
+                                                               int64_t NT, const float *__restrict__ gamma_p,
+                                                               const int8_t *__restrict__ Xq, int64_t ldq,
+                                                               const float *__restrict__ beta, int64_t M,
+                                                               int64_t N, int64_t K, void *__restrict__ Y,
+                                                               int y_dtype, int64_t ldy)
+{
+    constexpr int NW = WM * WN;                // waves
+    constexpr int MI = BM / WM / 32;           // 32-token MFMA tiles per wave
+    constexpr int NI = BN / WN / 32;           // 32-row MFMA tiles per wave
+    constexpr int A_BYTES = BM * KSTEP;        // activation bytes per stage
+    constexpr int B_BYTES = BN * 32;           // packed weight bytes per stage
+    constexpr int STAGE = A_BYTES + B_BYTES;
+    constexpr int A_ROWS_W = BM / NW;          // activation rows copied by one wave
+    constexpr int A_INST = A_ROWS_W / 8;       // 1 KB copies (8 rows) per wave per stage
+    // weight copies: 16 bytes per lane when every wave gets whole 1 KB copies, else 4
+    constexpr int B_CP = (B_BYTES % (1024 * NW) == 0) ? 16 : 4;
+    constexpr int B_INST = B_BYTES / (64 * B_CP) / NW;
+    constexpr int NST = LDS_RING_BYTES / STAGE < 8 ? LDS_RING_BYTES / STAGE : 8; // ring depth
+    constexpr int LOADS = A_INST + B_INST;     // copies per wave per stage
+    static_assert(MI >= 1 && NI >= 1 && A_INST >= 1 && B_INST >= 1 && NST >= 3, "tile shape");
+    static_assert(B_INST * NW * 64 * B_CP == B_BYTES && (NST - 1) * LOADS < 64, "copy plan");
+    __shared__ __attribute__((aligned(16))) int8_t lds[NST * STAGE];
+
     const int wave = wave_id(), lane = lane_id();
-    const int wm = wave >> 1, wn = wave & 1;
-    const int l32 = lane & 31, kh = lane >> 5; // operand row/column and 16-byte k half
+    const int wm = wave / WN, wn = wave % WN;
+    const int l32 = lane & 31, kh = lane >> 5;
 
     // XCD-aware tile order.  Workgroup ids are dealt round-robin to the 8 XCDs
     // (each with its own L2), so id L runs on XCD L % 8.  Tiles are numbered
@@ -64,58 +124,80 @@ __global__ __launch_bounds__(256) void k_gemm_mfma_i2(const uint8_t *__restrict_
     int64_t t;
     {
         const int64_t per = W / 8, rem = W % 8, x = L % 8, j = L / 8;
-        // XCDs 0 .. rem-1 own per+1 tiles, the others per
         t = x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
     }
     const int64_t m0 = (t / nN) * BM;
     const int64_t n0 = (t % nN) * BN;
     const int64_t nstages = (KB + 1) / 2;
 
-    // Per-thread load sources, computed once.  Activation piece r of a stage:
-    // row (tid + 256 r) / 8, 16-byte column (tid % 8).  Rows past M read row
-    // M - 1 and pieces that start at or past K read offset 0: the products they
-    // feed are discarded or meet packed weights that are 0 (columns past K
-    // carry T = 0), so only the addresses need to be valid; a piece straddling
-    // K reads up to round_up(K, 16) <= ldq.
-    const int8_t *a_row[A_LOADS];
+    // ---- copy sources, fixed for the whole loop ------------------------------
+    // The copies are buffer loads.  The hardware range check of a buffer
+    // resource turns every read past its end into zeros without touching
+    // memory, so rows past M, tiles past NT and the k tail need no clamping.
+    // Rows and tiles that do not exist only feed outputs that are never
+    // stored, and k positions past K meet zero weights (pad codes, or words
+    // replaced in the last stage), so whatever they read is harmless.
+    //
+    // Activation copy j of this wave: row wave*A_ROWS_W + 8j + lane/8, LDS slot
+    // lane%8, which holds the row's 16-byte unit (lane%8) ^ swz(row).
+    int a_voff[A_INST];
 #pragma unroll
-    for (int r = 0; r < A_LOADS; ++r) {
-        const int64_t m = m0 + ((tid + 256 * r) >> 3);
-        a_row[r] = Xq + (m < M ? m : M - 1) * ldq;
+    for (int j = 0; j < A_INST; ++j) {
+        const int row = wave * A_ROWS_W + 8 * j + (lane >> 3);
+        a_voff[j] = static_cast<int>(row * ldq) + ((lane & 7) ^ a_swz(row)) * 16;
     }
-    const int a_col = (tid & 7) * 16;
-    // weight chunk of this thread: row tid % 128 of the tile group, k-block 2 * stage + tid / 128;
-    // tiles past NT read tile NT - 1 (their outputs are never stored)
-    const int64_t b_n = n0 + (tid & 127);
-    const int64_t b_tile = b_n / 16 < NT ? b_n / 16 : NT - 1;
-    const uint8_t *b_ptr = P + (b_tile * KB) * 256 + (b_n % 16) * 16;
-    const int b_half = tid >> 7;
+    // Weight copy j of this wave covers stage chunk c (c = kb2 * BN/16 + tile,
+    // 256 bytes = 16 rows x 16 bytes): with 16-byte copies chunks
+    // 4 (wave*B_INST + j) + lane/16, row lane%16; with 4-byte copies chunk
+    // wave*B_INST + j, row lane/4, word lane%4.
+    int b_voff[B_INST];
+#pragma unroll
+    for (int j = 0; j < B_INST; ++j) {
+        const int c = B_CP == 16 ? (wave * B_INST + j) * 4 + (lane >> 4) : wave * B_INST + j;
+        const int in_chunk = B_CP == 16 ? (lane & 15) * 16 : (lane >> 2) * 16 + (lane & 3) * 4;
+        b_voff[j] = static_cast<int>((c % (BN / 16)) * KB * 256 + (c / (BN / 16)) * 256 + in_chunk);
+    }
+    // Bytes the resources cover from the block's first row / tile: rows m0 ..
+    // min(M, m0+BM)-1, the last one up to column K rounded up to 16 (the range
+    // check drops whole dwords, and the 16-byte-aligned unit holding the row's
+    // last byte never crosses a page); tiles n0/16 .. min(NT, (n0+BN)/16)-1.
+    const int64_t rows = (M - m0 < BM ? M - m0 : BM);
+    const int64_t a_bytes = (rows - 1) * ldq + ((K + 15) & ~int64_t(15));
+    const int64_t tiles = (NT - n0 / 16 < BN / 16 ? NT - n0 / 16 : BN / 16);
+    const int64_t b_bytes = tiles * KB * 256;
+    const int8_t *a_base = Xq + m0 * ldq;
+    const uint8_t *b_base = P + (n0 / 16) * KB * 256;
 
-    v4i a_st[S][A_LOADS];
-    uint4 b_st[S];
-    // Every call issues the same unconditional loads, so the waits before each
-    // use only need the oldest stage.  A k-block past KB reads the last one and
-    // is replaced by zero weights.
-    auto gload = [&](int64_t stg, v4i (&as)[A_LOADS], uint4 &bs) {
-        stg = stg < nstages ? stg : nstages - 1;
-        const int64_t kc = stg * KSTEP + a_col;
-        const int64_t ko = kc < K ? kc : 0;
+    // Issue the copies of stage st into ring slot buf.  Stages past the last
+    // read nothing (their resources are empty) and are never used.
+    auto issue = [&](int64_t st, int buf) {
+        int8_t *sbase = lds + buf * STAGE;
+        const int64_t ka = st * KSTEP, kb = st * 2 * 256;
+        const int na = static_cast<int>(a_bytes > ka ? a_bytes - ka : 0);
+        const int nb = static_cast<int>(b_bytes > kb ? b_bytes - kb : 0);
 #pragma unroll
-        for (int r = 0; r < A_LOADS; ++r) as[r] = *reinterpret_cast<const v4i *>(a_row[r] + ko);
-        const int64_t kb = 2 * stg + b_half;
-        const uint4 w = *reinterpret_cast<const uint4 *>(b_ptr + (kb < KB ? kb : KB - 1) * 256);
-        bs = kb < KB ? w : make_uint4(I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD);
-    };
-    auto lstore = [&](int buf, const v4i (&as)[A_LOADS], const uint4 &bs) {
+        for (int j = 0; j < A_INST; ++j)
+            buffer_copy_to_lds<16>(a_base + ka, na, (lds_void_t *)(sbase + (wave * A_ROWS_W + 8 * j) * KSTEP), a_voff[j]);
 #pragma unroll
-        for (int r = 0; r < A_LOADS; ++r)
-            *reinterpret_cast<v4i *>(&As[buf][((tid + 256 * r) >> 3) * LDS_ROW + a_col]) = as[r];
-        int8_t *row = &Bs[buf][(tid & 127) * LDS_ROW + b_half * 64];
-        *reinterpret_cast<v4i *>(row + 0) = gemm_i2_word_signed(bs.x);
-        *reinterpret_cast<v4i *>(row + 16) = gemm_i2_word_signed(bs.y);
-        *reinterpret_cast<v4i *>(row + 32) = gemm_i2_word_signed(bs.z);
-        *reinterpret_cast<v4i *>(row + 48) = gemm_i2_word_signed(bs.w);
+        for (int j = 0; j < B_INST; ++j)
+            buffer_copy_to_lds<B_CP>(b_base + kb, nb, (lds_void_t *)(sbase + A_BYTES + (wave * B_INST + j) * 64 * B_CP),
+                                     b_voff[j]);
     };
+
+    // ---- operand read offsets within a stage ---------------------------------
+    int a_off[MI][4];
+#pragma unroll
+    for (int a = 0; a < MI; ++a) {
+        const int row = wm * (BM / WM) + a * 32 + l32;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) a_off[a][kk] = row * KSTEP + (((2 * kk + kh) ^ a_swz(row)) * 16);
+    }
+    int b_off[NI];
+#pragma unroll
+    for (int b = 0; b < NI; ++b) {
+        const int nl = wn * (BN / WN) + b * 32 + l32;
+        b_off[b] = A_BYTES + (nl / 16) * 256 + (nl % 16) * 16 + 4 * kh;
+    }
 
     v16i acc[MI][NI];
 #pragma unroll
@@ -125,85 +207,157 @@ __global__ __launch_bounds__(256) void k_gemm_mfma_i2(const uint8_t *__restrict_
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
 
-    auto compute = [&](int buf) {
-        const int8_t *abase = &As[buf][(wm * (BM / 2) + l32) * LDS_ROW + kh * 16];
-        const int8_t *bbase = &Bs[buf][(wn * 64 + l32) * LDS_ROW + kh * 16];
+    // Operands of one stage, read from LDS one stage ahead of their MFMAs so
+    // that LDS latency overlaps the matrix work of the stage before.
+    struct Ops {
+        v4i a[MI][4];       // activation operand of tile a, k-step kk
+        uint32_t w[NI][4];  // packed word of B tile b, k-step kk (16 weights)
+    };
+    auto read_ops = [&](int buf, Ops &o) {
+        const int8_t *sbase = lds + buf * STAGE;
 #pragma unroll
-        for (int kk = 0; kk < KSTEP / 32; ++kk) {
-            v4i af[MI], bf[NI];
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-            for (int a = 0; a < MI; ++a) af[a] = *reinterpret_cast<const v4i *>(abase + a * 32 * LDS_ROW + kk * 32);
+            for (int a = 0; a < MI; ++a) o.a[a][kk] = *reinterpret_cast<const v4i *>(sbase + a_off[a][kk]);
+        // word of k-block kk/2, 16-weight group (kk % 2) * 2 + kh
 #pragma unroll
-            for (int b = 0; b < NI; ++b) bf[b] = *reinterpret_cast<const v4i *>(bbase + b * 32 * LDS_ROW + kk * 32);
+        for (int b = 0; b < NI; ++b)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                o.w[b][kk] = *reinterpret_cast<const uint32_t *>(sbase + b_off[b] + (kk / 2) * (BN / 16) * 256 +
+                                                                 (kk % 2) * 8);
+    };
+    auto mma = [&](const Ops &o, bool hi_valid) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            v4i bf[NI];
+#pragma unroll
+            for (int b = 0; b < NI; ++b) bf[b] = gemm_i2_word_signed((kk < 2 || hi_valid) ? o.w[b][kk] : I2_ZERO_WORD);
 #pragma unroll
             for (int a = 0; a < MI; ++a)
 #pragma unroll
                 for (int b = 0; b < NI; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], acc[a][b], 0, 0, 0);
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[a][kk], bf[b], acc[a][b], 0, 0, 0);
         }
     };
 
-    // the first S - 1 stages are requested up front, stage 0 goes to LDS
+    // The ring holds NST stages.  Before the MFMAs of stage st: stage st's
+    // operands are in registers, stage st+1 has landed in LDS (waited for and
+    // read into the other register set in this step), and stages st+2 ..
+    // st+NST are in flight; stage st+NST goes into the slot stage st has left.
 #pragma unroll
-    for (int j = 0; j < S; ++j)
-        if (j < S - 1 || S == 1) gload(j, a_st[j], b_st[j]);
-    if (tid < BM) {
-        const int64_t m = m0 + tid;
-        scale[tid] = m < M ? token_scale(*gamma_p, beta[m]) : 0.0f;
+    for (int s = 0; s < NST; ++s) issue(s, s);
+    __builtin_amdgcn_s_waitcnt(vmcnt_only((NST - 1) * LOADS));
+    stage_barrier();
+    Ops o0, o1;
+    read_ops(0, o0);
+    int slot = 0; // ring slot of stage st
+    auto step = [&](int64_t st, const Ops &cur, Ops &nxt) {
+        const int nslot = slot == NST - 1 ? 0 : slot + 1;
+        // this wave's copies of stage st+1 are done once at most NST-2 later
+        // stages' copies are outstanding, and its reads of stage st are back;
+        // the barrier extends both to every wave
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0((NST - 2) * LOADS));
+        stage_barrier();
+        issue(st + NST, slot);
+        read_ops(nslot, nxt);
+        mma(cur, 2 * st + 1 < KB);
+        slot = nslot;
+    };
+    int64_t st = 0;
+    for (; st + 1 < nstages; st += 2) {
+        step(st, o0, o1);
+        step(st + 1, o1, o0);
     }
-    lstore(0, a_st[0], b_st[0]);
+    if (st < nstages) step(st, o0, o1);
+
+    // ---- epilogue ------------------------------------------------------------
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0)); // the clamped tail copies still land in LDS
+    stage_barrier();
+    float *scale = reinterpret_cast<float *>(lds);
+    for (int i = threadIdx.x; i < BM; i += 64 * NW) {
+        const int64_t m = m0 + i;
+        scale[i] = m < M ? token_scale(*gamma_p, beta[m]) : 0.0f;
+    }
     __syncthreads();
-    // Stage st sits in LDS buffer st & 1.  At the start of its iteration the
-    // loads of stage st + S - 1 go out (register stage (st + S - 1) % S, free
-    // since its last content went to LDS); after the MFMAs of stage st, stage
-    // st + 1 (register stage (st + 1) % S, requested S - 1 iterations ago) is
-    // written to the other LDS buffer.  With S = 1 the loads of stage st + 1
-    // overlap the MFMAs of stage st only.
-    for (int64_t st0 = 0; st0 < nstages; st0 += S) {
-#pragma unroll
-        for (int j = 0; j < S; ++j) {
-            const int64_t st = st0 + j;
-            if (st >= nstages) break;
-            const int lbuf = static_cast<int>(st & 1);
-            if (S == 1) gload(st + 1, a_st[0], b_st[0]);
-            else gload(st + S - 1, a_st[(j + S - 1) % S], b_st[(j + S - 1) % S]);
-            compute(lbuf);
-            lstore(lbuf ^ 1, a_st[(j + 1) % S], b_st[(j + 1) % S]);
-            __syncthreads();
-        }
-    }
 
     // 32 x 32 output layout: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32
+    auto store_all = [&](auto put) {
 #pragma unroll
-    for (int a = 0; a < MI; ++a)
+        for (int a = 0; a < MI; ++a)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int lrow = wm * (BM / 2) + a * 32 + 8 * (r / 4) + 4 * kh + (r % 4);
-            const int64_t m = m0 + lrow;
-            if (m >= M) continue;
-            const float sc = scale[lrow];
+            for (int r = 0; r < 16; ++r) {
+                const int lrow = wm * (BM / WM) + a * 32 + 8 * (r / 4) + 4 * kh + (r % 4);
+                const int64_t m = m0 + lrow;
+                if (m >= M) continue;
+                const float sc = scale[lrow];
 #pragma unroll
-            for (int b = 0; b < NI; ++b) {
-                const int64_t n = n0 + wn * 64 + b * 32 + l32;
-                if (n < N) store_out(Y, y_dtype, ldy, m, n, acc[a][b][r], sc);
+                for (int b = 0; b < NI; ++b) {
+                    const int64_t n = n0 + wn * (BN / WN) + b * 32 + l32;
+                    if (n < N) put(m * ldy + n, acc[a][b][r], sc);
+                }
             }
-        }
+    };
+    if (y_dtype == DT_F32)
+        store_all([&](int64_t i, int v, float sc) { static_cast<float *>(Y)[i] = static_cast<float>(v) * sc; });
+    else if (y_dtype == DT_BF16)
+        store_all([&](int64_t i, int v, float sc) {
+            static_cast<uint16_t *>(Y)[i] = float_to_bf16_rne(static_cast<float>(v) * sc);
+        });
+    else
+        store_all([&](int64_t i, int v, float) { static_cast<int *>(Y)[i] = v; });
+}
+
+namespace {
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_tile(const GemvArgs &a, hipStream_t stream)
+{
+    const int64_t NT = (a.N + 15) / 16;
+    const int64_t KB = (a.K + 63) / 64;
+    dim3 grid(static_cast<unsigned>((a.N + BN - 1) / BN), static_cast<unsigned>((a.M + BM - 1) / BM));
+    hipLaunchKernelGGL((k_gemm_mfma_i2<BM, BN, WM, WN>), grid, dim3(64 * WM * WN), 0, stream, a.P, KB, NT, a.gamma,
+                       a.Xq, a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
+    return hipGetLastError();
+}
+} // namespace
+
+namespace {
+// Tile shapes on offer, with their measured sustained rates relative to each
+// other (large problems, every CU busy).  A launch costs about
+// ceil(tiles / 256 CUs) rounds of one tile each.
+struct GemmTile {
+    int bm, bn;
+    double rate;
+};
+constexpr GemmTile kTiles[] = {{256, 256, 2.1}, {128, 256, 1.95}, {128, 128, 1.5}};
+constexpr int64_t kCUs = 256;
+
+int best_tile(int64_t M, int64_t N)
+{
+    int best = 0;
+    double best_cost = 0;
+    for (int i = 0; i < 3; ++i) {
+        const int64_t t = ((M + kTiles[i].bm - 1) / kTiles[i].bm) * ((N + kTiles[i].bn - 1) / kTiles[i].bn);
+        const double cost = static_cast<double>((t + kCUs - 1) / kCUs) * kTiles[i].bm * kTiles[i].bn / kTiles[i].rate;
+        if (i == 0 || cost < best_cost) best = i, best_cost = cost;
+    }
+    return best;
+}
+} // namespace
+
+int64_t gemm_tiles(int64_t M, int64_t N)
+{
+    const GemmTile &t = kTiles[best_tile(M, N)];
+    return ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
 }
 
 hipError_t launch_gemm_mfma(const GemvArgs &a, hipStream_t stream)
 {
-    const int64_t NT = (a.N + 15) / 16;
-    const int64_t KB = (a.K + 63) / 64;
-    if (a.M > 128) {
-        dim3 grid(static_cast<unsigned>((a.N + BN - 1) / BN), static_cast<unsigned>((a.M + 255) / 256));
-        hipLaunchKernelGGL((k_gemm_mfma_i2<256, 1>), grid, dim3(256), 0, stream, a.P, KB, NT, a.gamma, a.Xq, a.ldq,
-                           a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
-    } else {
-        dim3 grid(static_cast<unsigned>((a.N + BN - 1) / BN), static_cast<unsigned>((a.M + 127) / 128));
-        hipLaunchKernelGGL((k_gemm_mfma_i2<128, 1>), grid, dim3(256), 0, stream, a.P, KB, NT, a.gamma, a.Xq, a.ldq,
-                           a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
+    switch (best_tile(a.M, a.N)) {
+    case 0: return launch_tile<256, 256, 2, 2>(a, stream);
+    case 1: return launch_tile<128, 256, 2, 4>(a, stream);
+    default: return launch_tile<128, 128, 2, 2>(a, stream);
     }
-    return hipGetLastError();
 }
 
 } // namespace bl

@@ -48,5 +48,8 @@ struct GemvArgs {
 hipError_t launch_gemv_addsub(const GemvArgs &a, hipStream_t stream);
 hipError_t launch_gemv_mfma(const GemvArgs &a, hipStream_t stream);
 hipError_t launch_gemm_mfma(const GemvArgs &a, hipStream_t stream);
+// Workgroup tiles the GEMM would launch for M x N (below a few hundred the
+// GPU is not filled and the matrix-core GEMV is faster).
+int64_t gemm_tiles(int64_t M, int64_t N);
 
 } // namespace bl

@@ -187,3 +187,20 @@ def test_one_hip_runtime_when_loaded_first():
             "assert len(rt) == 1, rt\n")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
+
+
+def test_auto_algo_dispatch():
+    """Host-side dispatch query: the GEMV for few tokens, pre-tiled input and
+    b3; the GEMM only when it fills the GPU with workgroup tiles."""
+    f = bl.bitlinear_auto_algo
+    for M in (1, 4, 16):
+        assert f(M, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMV_MFMA
+    assert f(2048, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMM_MFMA
+    assert f(2048, 3200, 3200, bl.LAYOUT_B3, bl.BF16) == bl.ALGO_GEMV_MFMA
+    assert f(2048, 3200, 3200, bl.LAYOUT_I2, bl.I8_TILED) == bl.ALGO_GEMV_MFMA
+    assert f(176, 1024, 8192, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMV_MFMA  # 16 tiles: GPU mostly idle
+    assert f(176, 8192, 8192, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMM_MFMA
+    assert f(64, 28672, 8192, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMM_MFMA
+    assert f(0, 16, 16, bl.LAYOUT_I2, bl.BF16) == -1
+    assert f(16, 16, 16, 7, bl.BF16) == -1
+    assert f(16, 16, 16, bl.LAYOUT_I2, 9) == -1
