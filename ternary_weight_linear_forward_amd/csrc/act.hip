@@ -9,15 +9,6 @@
 
 namespace bl {
 
-template <int XDT>
-__device__ __forceinline__ float load_x(const void *X, int64_t idx)
-{
-    if constexpr (XDT == DT_F32)
-        return static_cast<const float *>(X)[idx];
-    else
-        return bf16_bits_to_float(static_cast<const uint16_t *>(X)[idx]);
-}
-
 __device__ __forceinline__ float block_max(float v, float *red)
 {
     for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
@@ -28,14 +19,6 @@ __device__ __forceinline__ float block_max(float v, float *red)
     for (int w = 1; w < nw; ++w) r = fmaxf(r, red[w]);
     __syncthreads();
     return r;
-}
-
-__device__ __forceinline__ uint32_t quant_one(float x, float s)
-{
-    float r = __builtin_rintf(x * s);
-    r = r > 127.0f ? 127.0f : r;
-    r = r < -127.0f ? -127.0f : r;
-    return static_cast<uint32_t>(static_cast<int>(r)) & 0xffu;
 }
 
 // Generic path: one workgroup per token row; a thread handles groups of 4
@@ -51,7 +34,7 @@ __global__ __launch_bounds__(256) void k_quant_act(const void *__restrict__ X, i
     float amax = 0.0f;
     for (int64_t k = threadIdx.x; k < K; k += blockDim.x) amax = fmaxf(amax, fabsf(load_x<XDT>(X, base + k)));
     const float b = block_max(amax, red);
-    const float s = b > 0.0f ? 127.0f / b : 0.0f;
+    const float s = token_step(b);
     uint32_t *qrow = reinterpret_cast<uint32_t *>(Xq + m * ldq);
     const int64_t nwords = ldq / 4;
     for (int64_t w = threadIdx.x; w < nwords; w += blockDim.x) {
@@ -102,7 +85,7 @@ __global__ __launch_bounds__(256) void k_quant_act_vec(const void *__restrict__ 
         }
     }
     const float b = block_max(amax, red);
-    const float s = b > 0.0f ? 127.0f / b : 0.0f;
+    const float s = token_step(b);
     int8_t *qrow = Xq + m * ldq;
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
@@ -223,7 +206,7 @@ __global__ __launch_bounds__(256) void k_quant_act_tiled(const void *__restrict_
         for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
     }
     const float b = block_max(amax, red);
-    const float s = b > 0.0f ? 127.0f / b : 0.0f;
+    const float s = token_step(b);
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
         const int64_t p = threadIdx.x + static_cast<int64_t>(j) * blockDim.x;

@@ -55,6 +55,29 @@ __device__ __forceinline__ v4i i2_word_to_signed16(uint32_t w)
     return r;
 }
 
+template <int XDT>
+__device__ __forceinline__ float load_x(const void *X, int64_t idx)
+{
+    if constexpr (XDT == DT_F32)
+        return static_cast<const float *>(X)[idx];
+    else
+        return bf16_bits_to_float(static_cast<const uint16_t *>(X)[idx]);
+}
+
+// Per-token quantisation step: s = 127 / beta (correctly rounded binary32
+// division), or 0 for an all-zero token.
+__device__ __forceinline__ float token_step(float beta) { return beta > 0.0f ? 127.0f / beta : 0.0f; }
+
+// One activation to int8: clamp(rint(x * s), -127, 127), ties to even, as the
+// low byte of the result.
+__device__ __forceinline__ uint32_t quant_one(float x, float s)
+{
+    float r = __builtin_rintf(x * s);
+    r = r > 127.0f ? 127.0f : r;
+    r = r < -127.0f ? -127.0f : r;
+    return static_cast<uint32_t>(static_cast<int>(r)) & 0xffu;
+}
+
 // Per-token rescale factor (gamma * beta) / 127 in binary32.
 __device__ __forceinline__ float token_scale(float gamma, float beta)
 {

@@ -223,6 +223,33 @@ def test_forward_wide_short(layout, M, N, K):
     run_forward_case(M, N, K, bl.ALGO_GEMV_MFMA, layout, seed=M + N + K, y_kinds=("i32", "f32"))
 
 
+@pytest.mark.parametrize("layout", ["i2", "b3"])
+@pytest.mark.parametrize("x_kind", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", [(1, 300, 1024), (7, 1000, 2000), (16, 8200, 3200), (16, 9000, 9984),
+                                   (3, 2048, 9920)])
+def test_forward_gemv_float_input(layout, x_kind, M, N, K):
+    """bf16/fp32 activations of at most 16 tokens through the matrix-core GEMV
+    (per-tile and persistent kernels, K near 10^4)."""
+    log("forward gemv float input", layout, x_kind, M, N, K)
+    run_forward_case(M, N, K, bl.ALGO_GEMV_MFMA, layout, seed=M + N + 3 * K, x_kind=x_kind, y_kinds=("i32", "f32"))
+
+
+def test_forward_gemv_strided_f32():
+    """Rows of a wider fp32 matrix (the stack's o and down inputs): row stride
+    larger than K."""
+    M, N, K, ldx = 16, 640, 800, 1200
+    t = synth.ternary_weights(N, K, seed=91)
+    xw = synth.activations_f32(M, ldx, seed=92)
+    ref = oracle.forward(t, np.float32(0.02), np.ascontiguousarray(xw[:, :K]))
+    P = to_dev(oracle.pack(t, bl.LAYOUT_I2))
+    gamma = to_dev(np.array([0.02], np.float32))
+    xd = to_dev(xw)[:, :K]
+    acc = to_host(bl.forward(P, bl.LAYOUT_I2, gamma, xd, N, K, y_dtype=torch.int32, algo=bl.ALGO_GEMV_MFMA))
+    assert np.array_equal(acc, ref["acc"])
+    y = to_host(bl.forward(P, bl.LAYOUT_I2, gamma, xd, N, K, algo=bl.ALGO_GEMV_MFMA))
+    assert_f32_parity(y, ref["y"])
+
+
 def test_forward_f32_input_tiny():
     run_forward_case(16, 512, 256, bl.ALGO_AUTO, "i2", seed=77, x_kind="f32")
 
