@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--layout", default="i2", choices=["i2", "b3"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device 5 times (a plain copy of known size for scaling "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
 
 
@@ -66,6 +69,17 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_copy": n, "copies": 5}), flush=True)
+        return
 
     from ternary_weight_linear_forward_amd import bitlinear as bl
     from ternary_weight_linear_forward_amd import synth, workloads
@@ -195,79 +209,83 @@ def main():
     value = packed_per_step / (step_ms * 1e-3) / 1e9
     tops = ops_per_step / (step_ms * 1e-3) / 1e12
 
-    # ---- roofline: HIP events around every launch of each product kernel -----
-    # bitlinear_forward runs a quantiser kernel, then the product kernel.  To
-    # time the product kernel alone the same two steps are issued through the
-    # split entry points, in the same way bitlinear_forward dispatches them.
-    def plan(M, N, K):
-        algo = bl.bitlinear_auto_algo(M, N, K, layout, bl.BF16)
-        lname = "i2" if layout == bl.LAYOUT_I2 else "b3"
-        if algo == bl.ALGO_GEMV_MFMA:
-            kind = "tiled" if M > 4 and K <= 65536 else "rowmajor"
-            return kind, algo, f"k_gemv_mfma|k_gemv_persist <{lname},{kind}>"
-        if algo == bl.ALGO_GEMM_MFMA:
-            return "rowmajor", algo, "k_gemm_mfma_i2"
-        raise RuntimeError(f"unexpected automatic algorithm {algo}")
-
+    # ---- roofline: the product kernel of every job, timed on its own ---------
+    # bitlinear_forward runs the activation quantiser, then the product kernel
+    # (bitlinear_product_kernel names it).  Here each job's activations are
+    # quantised once through the split entry point, then a HIP graph of R
+    # back-to-back product launches (rotating over the weight copies) is
+    # replayed between two HIP events on the launch stream; a launch's
+    # duration is the replay time / R.  Durations are summed per kernel name;
+    # the kernel with the most time per step is the dominant one.
+    R = 16
     for j in jobs:
         layer = j["L"]["layer"]
-        kind, algo, name = plan(j["M"], layer.N, layer.K)
-        j["plan"] = (kind, algo, name)
-        if kind == "tiled":
-            nb = bl.bitlinear_act_tiled_bytes(j["M"], layer.K, layout)
-            j["xq"] = torch.empty(nb, dtype=torch.int8, device=dev)
-            j["ldq"] = 0
-        else:
-            j["ldq"] = (layer.K + 63) // 64 * 64
-            j["xq"] = torch.empty((j["M"], j["ldq"]), dtype=torch.int8, device=dev)
-        j["beta"] = torch.empty(j["M"], dtype=torch.float32, device=dev)
+        M = j["M"]
+        algo = bl.bitlinear_auto_algo(M, layer.N, layer.K, layout, j["x_dtype"])
+        j["kernel"] = bl.bitlinear_product_kernel(M, layer.N, layer.K, layout, j["x_dtype"], bl.ALGO_AUTO)
+        tiled = algo == bl.ALGO_GEMV_MFMA and M > 4 and layer.K <= 65536
+        j["beta"] = torch.empty(M, dtype=torch.float32, device=dev)
+        s_ = stream.cuda_stream
+        with torch.cuda.stream(stream):
+            if tiled:
+                nb = bl.bitlinear_act_tiled_bytes(M, layer.K, layout)
+                j["xq"], j["ldq"], xdt = torch.empty(nb, dtype=torch.int8, device=dev), 0, bl.I8_TILED
+                st = bl.bitlinear_quantize_act_tiled(j["x_ptr"], j["x_dtype"], M, layer.K, j["ldx"], layout,
+                                                     j["xq"].data_ptr(), nb, j["beta"].data_ptr(), s_)
+            else:
+                j["ldq"] = (layer.K + 63) // 64 * 64
+                j["xq"], xdt = torch.empty((M, j["ldq"]), dtype=torch.int8, device=dev), bl.I8
+                st = bl.bitlinear_quantize_act(j["x_ptr"], j["x_dtype"], M, layer.K, j["ldx"], j["xq"].data_ptr(),
+                                               j["ldq"], j["beta"].data_ptr(), s_)
+            if st:
+                raise bl.BitlinearError(st, "quantize (instrumented)")
+            assert bl.bitlinear_product_kernel(M, layer.N, layer.K, layout, xdt, algo) == j["kernel"]
 
-    def gemv_bytes(j):
+            def product(copy, j=j, xdt=xdt, algo=algo):
+                L, lay = j["L"], j["L"]["layer"]
+                st = bl.bitlinear_forward_algo(L["P"][copy].data_ptr(), layout, L["gamma"].data_ptr(), j["M"],
+                                               lay.N, lay.K, j["xq"].data_ptr(), xdt, j["ldq"],
+                                               j["beta"].data_ptr(), j["y"].data_ptr(), bl.F32, j["y"].stride(0),
+                                               None, 0, algo, stream.cuda_stream)
+                if st:
+                    raise bl.BitlinearError(st, "forward (instrumented)")
+
+            product(0)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for r in range(R):
+                    product(r % ncopies)
+            j["graph"] = g
+    torch.cuda.synchronize()
+
+    def product_bytes(j):
         layer = j["L"]["layer"]
         return j["L"]["P"][0].numel() + j["M"] * layer.K + 4 * j["M"] + 4 + 4 * j["M"] * layer.N
 
     per_kernel = {}
-    reps = max(1, min(args.steps, ncopies, 4))
+    reps = 5
     with torch.cuda.stream(stream):
-        torch.cuda.synchronize()
-        marks = []
-        if hasattr(torch.cuda, "_sleep"):
-            torch.cuda._sleep(50_000_000)  # hold the stream while the host queues every launch
-        for r in range(reps):
-            for j in jobs:
-                L = j["L"]
-                layer = L["layer"]
-                kind, algo, name = j["plan"]
-                s = stream.cuda_stream
-                if kind == "tiled":
-                    bl.bitlinear_quantize_act_tiled(j["x_ptr"], j["x_dtype"], j["M"], layer.K, j["ldx"],
-                                                    layout, j["xq"].data_ptr(), j["xq"].numel(),
-                                                    j["beta"].data_ptr(), s)
-                    xdt = bl.I8_TILED
-                else:
-                    bl.bitlinear_quantize_act(j["x_ptr"], j["x_dtype"], j["M"], layer.K, j["ldx"],
-                                              j["xq"].data_ptr(), j["ldq"], j["beta"].data_ptr(), s)
-                    xdt = bl.I8
+        for j in jobs:
+            ts = []
+            for _ in range(reps):
                 ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 ea.record(stream)
-                st = bl.bitlinear_forward_algo(L["P"][r % ncopies].data_ptr(), layout, L["gamma"].data_ptr(),
-                                               j["M"], layer.N, layer.K, j["xq"].data_ptr(), xdt, j["ldq"],
-                                               j["beta"].data_ptr(), j["y"].data_ptr(), bl.F32, j["y"].stride(0),
-                                               None, 0, algo, s)
+                j["graph"].replay()
                 eb.record(stream)
-                if st:
-                    raise bl.BitlinearError(st, "forward (instrumented)")
-                marks.append((name, ea, eb, gemv_bytes(j), 2 * j["M"] * layer.N * layer.K))
-        torch.cuda.synchronize()
-    for name, ea, eb, nbytes, nops in marks:
-        d = per_kernel.setdefault(name, {"ms": 0.0, "bytes": 0, "ops": 0, "launches": 0})
-        d["ms"] += ea.elapsed_time(eb)
-        d["bytes"] += nbytes
-        d["ops"] += nops
-        d["launches"] += 1
+                ts.append((ea, eb))
+            torch.cuda.synchronize()
+            j["launch_ms"] = sum(a.elapsed_time(b) for a, b in ts) / (reps * R)
+            d = per_kernel.setdefault(j["kernel"], {"ms": 0.0, "bytes": 0, "ops": 0, "launches": 0, "jobs": []})
+            layer = j["L"]["layer"]
+            d["ms"] += j["launch_ms"]
+            d["bytes"] += product_bytes(j)
+            d["ops"] += 2 * j["M"] * layer.N * layer.K
+            d["launches"] += 1
+            d["jobs"].append(f"{layer.name}@M{j['M']}")
     dom_name, dom = max(per_kernel.items(), key=lambda kv: kv[1]["ms"])
     avg_us = dom["ms"] / dom["launches"] * 1e3
-    bound = "mfma" if dom_name.startswith("k_gemm") else "hbm"
+    bound = "mfma" if "gemm" in dom_name else "hbm"
     if bound == "hbm":
         achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -276,12 +294,13 @@ def main():
         achieved = dom["ops"] / (dom["ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                 "frac": round(achieved / INT8_PEAK_TOPS, 4)}
-    roof.update({"traffic": None, "kernel": dom_name, "avg_launch_us": round(avg_us, 3),
-                 "launches": dom["launches"],
-                 "algorithmic_bytes_per_launch": dom["bytes"] // dom["launches"]})
+    roof.update({"traffic": measured_traffic(wl.name, dom_name), "kernel": dom_name, "avg_launch_us": round(avg_us, 3),
+                 "jobs": dom["jobs"],
+                 "algorithmic_bytes_per_launch": dom["bytes"] // dom["launches"],
+                 "algorithmic_ops_per_launch": dom["ops"] // dom["launches"]})
     kernels = {k: {"avg_us": round(v["ms"] / v["launches"] * 1e3, 3),
                    "GB/s": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1),
-                   "TOPS": round(v["ops"] / (v["ms"] * 1e-3) / 1e12, 2), "launches": v["launches"]}
+                   "TOPS": round(v["ops"] / (v["ms"] * 1e-3) / 1e12, 2), "jobs": len(v["jobs"])}
                for k, v in per_kernel.items()}
     print(f"[bench] per-kernel: {json.dumps(kernels)}", file=sys.stderr, flush=True)
 
@@ -327,6 +346,29 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of 'kernel' from the committed rocprofv3 counter
+    summary (profiles/traffic_*.txt), or None when there is none for this
+    workload and kernel, or when the kernel sources changed since."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "gemm.hip", "common.h"):
+        with open(os.path.join(ROOT, "ternary_weight_linear_forward_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    for path in glob.glob(os.path.join(ROOT, "profiles", "traffic_*.txt")):
+        kv = {}
+        with open(path) as fh:
+            for line in fh:
+                if ": " in line and not line.startswith(("#", " ")):
+                    k, v = line.rstrip("\n").split(": ", 1)
+                    kv[k] = v
+        if kv.get("workload") == workload and kv.get("kernel") == kernel and kv.get("source_sha256") == h.hexdigest():
+            return int(kv["traffic_bytes_per_launch"])
+    return None
 
 
 def cpu_baseline(wl, batches, seconds):

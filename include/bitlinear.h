@@ -122,6 +122,15 @@ int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int l
 int bitlinear_auto_algo(int64_t M, int64_t N, int64_t K, int layout, int x_dtype);
 
 /*
+ * Name of the product kernel a forward with these arguments launches (algo
+ * AUTO resolved as above), as profilers print it without the argument list,
+ * e.g. "bl::k_gemv_persist<0, 1, 8, true>"; NULL for invalid or unsupported
+ * arguments.  The string lives in thread-local storage until the calling
+ * thread's next call.  Host-only; enqueues nothing.
+ */
+const char *bitlinear_product_kernel(int64_t M, int64_t N, int64_t K, int layout, int x_dtype, int algo);
+
+/*
  * Absmean weight ternarisation (LIT-380 Key takeaways bullet 1).
  *   W      fp32 [N x K], row stride ldw >= K (device, read-only).
  *   T      int8 [N x K], row stride K (device, written): values in {-1, 0, +1}.

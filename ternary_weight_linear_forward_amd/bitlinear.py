@@ -64,6 +64,7 @@ _SIGNATURES = {
     "bitlinear_forward_workspace_bytes": ([_I64, _I64, _I64, _INT, _INT], _I64),
     "bitlinear_act_tiled_bytes": ([_I64, _I64, _INT], _I64),
     "bitlinear_auto_algo": ([_I64, _I64, _I64, _INT, _INT], _INT),
+    "bitlinear_product_kernel": ([_I64, _I64, _I64, _INT, _INT, _INT], ctypes.c_char_p),
     "bitlinear_quantize_act_tiled": ([_P, _INT, _I64, _I64, _I64, _INT, _P, _I64, _P, _P], _INT),
     "bitlinear_quantize_weights": ([_P, _I64, _I64, _I64, _P, _P, _P, _I64, _P], _INT),
     "bitlinear_pack": ([_P, _I64, _I64, _I64, _INT, _P, _P], _INT),
@@ -118,6 +119,11 @@ def bitlinear_act_tiled_bytes(M: int, K: int, layout: int) -> int:
 
 def bitlinear_auto_algo(M: int, N: int, K: int, layout: int, x_dtype: int) -> int:
     return _lib.bitlinear_auto_algo(M, N, K, layout, x_dtype)
+
+
+def bitlinear_product_kernel(M: int, N: int, K: int, layout: int, x_dtype: int, algo: int = 0):
+    r = _lib.bitlinear_product_kernel(M, N, K, layout, x_dtype, algo)
+    return None if r is None else r.decode()
 
 
 def bitlinear_quantize_act_tiled(X, x_dtype, M, K, ldx, layout, Xt, xt_bytes, beta, stream) -> int:

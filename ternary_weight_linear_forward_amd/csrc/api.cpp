@@ -131,6 +131,30 @@ int bitlinear_auto_algo(int64_t M, int64_t N, int64_t K, int layout, int x_dtype
     return auto_algo(M, N, layout, x_dtype);
 }
 
+const char *bitlinear_product_kernel(int64_t M, int64_t N, int64_t K, int layout, int x_dtype, int algo)
+{
+    thread_local char name[96];
+    if (bitlinear_auto_algo(M, N, K, layout, x_dtype) < 0 || algo < BITLINEAR_ALGO_AUTO ||
+        algo > BITLINEAR_ALGO_GEMM_MFMA)
+        return nullptr;
+    if (algo == BITLINEAR_ALGO_AUTO) algo = auto_algo(M, N, layout, x_dtype);
+    if ((algo == BITLINEAR_ALGO_GEMV_ADDSUB && (M > 16 || layout != BITLINEAR_LAYOUT_I2)) ||
+        (algo == BITLINEAR_ALGO_GEMM_MFMA && layout != BITLINEAR_LAYOUT_I2) ||
+        (x_dtype == BITLINEAR_I8_TILED && algo != BITLINEAR_ALGO_GEMV_MFMA))
+        return nullptr;
+    if (algo == BITLINEAR_ALGO_GEMV_ADDSUB) {
+        bl::gemv_addsub_kernel_name(M, name, sizeof name);
+    } else if (algo == BITLINEAR_ALGO_GEMM_MFMA) {
+        bl::gemm_kernel_name(M, N, name, sizeof name);
+    } else {
+        // the same choice of activation staging as bitlinear_forward_algo
+        const bool tiled = x_dtype == BITLINEAR_I8_TILED ||
+                           ((x_dtype == BITLINEAR_F32 || x_dtype == BITLINEAR_BF16) && M > 4 && K <= kTiledMaxK);
+        bl::gemv_kernel_name(layout, M, N, K, tiled, name, sizeof name);
+    }
+    return name;
+}
+
 int64_t bitlinear_act_tiled_bytes(int64_t M, int64_t K, int layout)
 {
     if (M < 1 || M > BITLINEAR_MAX_M || K < 1 || K > BITLINEAR_MAX_K || !valid_layout(layout)) return -1;

@@ -24,6 +24,8 @@
 // Only s_barrier (no memory fence) separates the stages; the explicit vmcnt
 // wait before it covers this wave's own copies of the stage, and the barrier
 // then covers every wave's.
+#include <cstdio>
+
 #include "common.h"
 #include "launch.h"
 
@@ -349,6 +351,13 @@ int64_t gemm_tiles(int64_t M, int64_t N)
 {
     const GemmTile &t = kTiles[best_tile(M, N)];
     return ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+}
+
+void gemm_kernel_name(int64_t M, int64_t N, char *buf, size_t n)
+{
+    static const char *const names[] = {"bl::k_gemm_mfma_i2<256, 256, 2, 2>", "bl::k_gemm_mfma_i2<128, 256, 2, 4>",
+                                        "bl::k_gemm_mfma_i2<128, 128, 2, 2>"};
+    snprintf(buf, n, "%s", names[best_tile(M, N)]);
 }
 
 hipError_t launch_gemm_mfma(const GemvArgs &a, hipStream_t stream)

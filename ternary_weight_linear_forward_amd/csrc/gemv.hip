@@ -17,6 +17,8 @@
 //    {0, 1, 2} goes through v_dot4_i32_i8: sum_k c*q adds q where T = 0, 2q
 //    where T = +1 and nothing where T = -1; subtracting sum_k q leaves
 //    sum_{T=+1} q - sum_{T=-1} q exactly.
+#include <cstdio>
+
 #include "common.h"
 #include "launch.h"
 
@@ -570,32 +572,68 @@ static void launch_persist(const GemvArgs &a, int64_t KB, int64_t NT, int64_t KS
                            a.Xq, a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
 }
 
+// Which matrix-core GEMV kernel runs for a shape.  Large layers: persistent
+// workgroups with register-resident activations, when every CU gets at least
+// two row tiles and the k-steps fit 16 waves x 4.  Otherwise one workgroup
+// per TW row tiles, reusing each activation operand over several tiles when
+// there are many tokens (the activations are then a large share of the
+// L2 -> CU traffic) and enough tiles to keep every CU busy.
+struct GemvPlan {
+    bool persist;
+    int spw;    // persistent: k-steps per wave (1, 2 or 4)
+    int tw;     // per-tile kernel: row tiles per workgroup (1, 2 or 4)
+    int64_t KS; // persistent: waves per workgroup
+};
+
+static GemvPlan gemv_plan(int layout, int64_t M, int64_t N, int64_t K)
+{
+    const int64_t NT = (N + 15) / 16;
+    const int64_t KB = layout == LAYOUT_I2 ? (K + 63) / 64 : (K + 79) / 80;
+    const int64_t nsteps = (KB + 3) / 4;
+    const int64_t tgroups = (M + 15) / 16;
+    GemvPlan p{false, 0, 1, 0};
+    if (NT >= 512 * tgroups && nsteps <= 64) {
+        p.persist = true;
+        p.KS = nsteps < 16 ? nsteps : 16;
+        const int64_t spw = (nsteps + p.KS - 1) / p.KS;
+        p.spw = spw <= 1 ? 1 : (spw <= 2 ? 2 : 4);
+        return p;
+    }
+    p.tw = (M > 4 && NT >= 1024) ? 4 : ((M > 4 && NT >= 512) ? 2 : 1);
+    return p;
+}
+
 template <int LAYOUT>
 static void launch_mfma_layout(const GemvArgs &a, hipStream_t stream)
 {
     const int64_t NT = (a.N + 15) / 16;
     const int64_t KB = LAYOUT == LAYOUT_I2 ? (a.K + 63) / 64 : (a.K + 79) / 80;
     const int64_t nsteps = (KB + 3) / 4;
-    // Large layers: persistent workgroups with register-resident activations,
-    // when every CU gets at least two row tiles and the k-steps fit 16 waves x 4.
-    const int64_t tgroups = (a.M + 15) / 16;
-    if (NT >= 512 * tgroups && nsteps <= 64) {
-        const int64_t KS = nsteps < 16 ? nsteps : 16;
-        const int64_t spw = (nsteps + KS - 1) / KS;
-        if (spw <= 1) launch_persist<LAYOUT, 1>(a, KB, NT, KS, stream);
-        else if (spw <= 2) launch_persist<LAYOUT, 2>(a, KB, NT, KS, stream);
-        else launch_persist<LAYOUT, 4>(a, KB, NT, KS, stream);
+    const GemvPlan p = gemv_plan(LAYOUT, a.M, a.N, a.K);
+    if (p.persist) {
+        if (p.spw == 1) launch_persist<LAYOUT, 1>(a, KB, NT, p.KS, stream);
+        else if (p.spw == 2) launch_persist<LAYOUT, 2>(a, KB, NT, p.KS, stream);
+        else launch_persist<LAYOUT, 4>(a, KB, NT, p.KS, stream);
         return;
     }
-    // Reuse each activation operand over several tiles when there are many
-    // tokens (the activations are then a large share of the L2 -> CU traffic)
-    // and enough tiles to keep every CU busy.
-    if (a.M > 4 && NT >= 1024)
-        launch_mfma_tw<LAYOUT, 4>(a, KB, NT, nsteps, stream);
-    else if (a.M > 4 && NT >= 512)
-        launch_mfma_tw<LAYOUT, 2>(a, KB, NT, nsteps, stream);
+    if (p.tw == 4) launch_mfma_tw<LAYOUT, 4>(a, KB, NT, nsteps, stream);
+    else if (p.tw == 2) launch_mfma_tw<LAYOUT, 2>(a, KB, NT, nsteps, stream);
+    else launch_mfma_tw<LAYOUT, 1>(a, KB, NT, nsteps, stream);
+}
+
+void gemv_kernel_name(int layout, int64_t M, int64_t N, int64_t K, bool tiled, char *buf, size_t n)
+{
+    const GemvPlan p = gemv_plan(layout, M, N, K);
+    if (p.persist)
+        snprintf(buf, n, "bl::k_gemv_persist<%d, %d, %d, %s>", layout, p.spw, p.spw >= 4 ? 4 : 8,
+                 tiled ? "true" : "false");
     else
-        launch_mfma_tw<LAYOUT, 1>(a, KB, NT, nsteps, stream);
+        snprintf(buf, n, "bl::k_gemv_mfma<%d, %d, 1, %s>", layout, p.tw, tiled ? "true" : "false");
+}
+
+void gemv_addsub_kernel_name(int64_t M, char *buf, size_t n)
+{
+    snprintf(buf, n, "bl::k_gemv_addsub<%d>", M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : (M <= 8 ? 8 : 16))));
 }
 
 hipError_t launch_gemv_mfma(const GemvArgs &a, hipStream_t stream)

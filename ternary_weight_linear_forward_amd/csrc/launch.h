@@ -52,4 +52,10 @@ hipError_t launch_gemm_mfma(const GemvArgs &a, hipStream_t stream);
 // GPU is not filled and the matrix-core GEMV is faster).
 int64_t gemm_tiles(int64_t M, int64_t N);
 
+// Names (as profilers print them, without the argument list) of the kernel a
+// product launch runs for a shape.
+void gemv_kernel_name(int layout, int64_t M, int64_t N, int64_t K, bool tiled, char *buf, size_t n);
+void gemv_addsub_kernel_name(int64_t M, char *buf, size_t n);
+void gemm_kernel_name(int64_t M, int64_t N, char *buf, size_t n);
+
 } // namespace bl

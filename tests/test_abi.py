@@ -204,3 +204,18 @@ def test_auto_algo_dispatch():
     assert f(0, 16, 16, bl.LAYOUT_I2, bl.BF16) == -1
     assert f(16, 16, 16, 7, bl.BF16) == -1
     assert f(16, 16, 16, bl.LAYOUT_I2, 9) == -1
+
+
+def test_product_kernel_names():
+    """The kernel-name query follows the dispatch: GEMV kernels for few tokens
+    (the persistent one for wide layers), GEMM tiles for prefill, the add/sub
+    kernel on request; None for requests the library rejects."""
+    f = bl.bitlinear_product_kernel
+    assert f(1, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemv_mfma<0, 1, 1, false>"
+    assert f(16, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemv_mfma<0, 1, 1, true>"
+    assert f(16, 3200, 3200, bl.LAYOUT_I2, bl.I8) == "bl::k_gemv_mfma<0, 1, 1, false>"
+    assert f(16, 28672, 8192, bl.LAYOUT_B3, bl.BF16).startswith("bl::k_gemv_persist<1, ")
+    assert f(2048, 3200, 3200, bl.LAYOUT_I2, bl.BF16).startswith("bl::k_gemm_mfma_i2<")
+    assert f(3, 64, 64, bl.LAYOUT_I2, bl.BF16, bl.ALGO_GEMV_ADDSUB) == "bl::k_gemv_addsub<4>"
+    assert f(3, 64, 64, bl.LAYOUT_B3, bl.BF16, bl.ALGO_GEMM_MFMA) is None
+    assert f(0, 64, 64, bl.LAYOUT_I2, bl.BF16) is None
