@@ -199,13 +199,15 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
     const uint32_t lane_off = static_cast<uint32_t>(g) * 256u + static_cast<uint32_t>(i) * 16u;
     const uint32_t last_kb_off = static_cast<uint32_t>(KB - 1) * 256u + static_cast<uint32_t>(i) * 16u;
     // rescale factors of this lane's 4 output tokens, loaded before the product
+    // (clamped loads, then selects: no branch, so the four loads overlap)
     float sc[4];
     {
         const float gamma = *gamma_p;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const int64_t mm = static_cast<int64_t>(blockIdx.y) * 16 + 4 * g + rr;
-            sc[rr] = mm < M ? token_scale(gamma, beta[mm]) : 0.0f;
+            const float v = token_scale(gamma, beta[mm < M ? mm : M - 1]);
+            sc[rr] = mm < M ? v : 0.0f;
         }
     }
 
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
             int64_t s = s0 + static_cast<int64_t>(j) * KS;
-            s = s < nfull ? s : nfull - 1; // a clamped duplicate is never accumulated
+            s = s < nfull ? s : nfull - 1; // (the loop never asks past the last step)
             uint32_t off = static_cast<uint32_t>(s) * 1024u + lane_off;
             if (TILED) off = 4 * s + g < KB ? off : last_kb_off;
 #pragma unroll
@@ -231,28 +233,37 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
                                 : *reinterpret_cast<const v4i *>(xrow + s * STEP_K + 16 * d);
         }
     };
-    auto compute_batch = [&](int64_t s0, const uint4 (&b)[SB][TW], const v4i (&a)[SB][NMF]) {
-#pragma unroll
-        for (int j = 0; j < SB; ++j)
-            if (s0 + static_cast<int64_t>(j) * KS < nfull) gemv_step<LAYOUT, TW, NMF>(b[j], a[j], acc);
+    // (SB = 1: the loop below only computes batches that exist)
+    static_assert(SB == 1, "one k-step per batch");
+    auto compute_batch = [&](int64_t, const uint4 (&b)[SB][TW], const v4i (&a)[SB][NMF]) {
+        gemv_step<LAYOUT, TW, NMF>(b[0], a[0], acc);
     };
     if (wave < nfull) {
         uint4 b0[SB][TW], b1[SB][TW];
         v4i a0[SB][NMF], a1[SB][NMF];
-        int64_t s0 = wave;
+        const int64_t niter = (nfull - 1 - wave) / stride + 1; // k-steps of this wave
+        int64_t s0 = wave, it = 0;
         load_batch(s0, b0, a0);
-        while (true) {
-            const int64_t s1 = s0 + stride;
-            if (s1 < nfull) load_batch(s1, b1, a1);
+        // Two steps per trip, each preceded by the unconditional request of the
+        // next one: every path through the loop has the same loads outstanding,
+        // so the wait before a step's MFMAs covers only that step and the next
+        // stays in flight.  The last one or two steps run after the loop, so no
+        // request goes past this wave's last step.
+        for (; it + 2 < niter; it += 2, s0 += 2 * stride) {
+            load_batch(s0 + stride, b1, a1);
             __builtin_amdgcn_sched_barrier(0);
             compute_batch(s0, b0, a0);
-            if (s1 >= nfull) break;
-            const int64_t s2 = s1 + stride;
-            if (s2 < nfull) load_batch(s2, b0, a0);
+            load_batch(s0 + 2 * stride, b0, a0);
             __builtin_amdgcn_sched_barrier(0);
-            compute_batch(s1, b1, a1);
-            if (s2 >= nfull) break;
-            s0 = s2;
+            compute_batch(s0 + stride, b1, a1);
+        }
+        if (niter - it == 2) {
+            load_batch(s0 + stride, b1, a1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_batch(s0, b0, a0);
+            compute_batch(s0 + stride, b1, a1);
+        } else {
+            compute_batch(s0, b0, a0);
         }
     }
     // the partial k-step of row-major activations, bounds-checked
@@ -297,7 +308,7 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
 // tile meet in LDS and the 4 x TMAX output groups are summed by different
 // waves.  Activations cross L2 once per CU instead of once per tile.
 // ---------------------------------------------------------------------------
-template <int LAYOUT, int SPW, int TMAX, bool TILED>
+template <int LAYOUT, int SPW, int TMAX, bool TILED, bool GUARD>
 __global__ __launch_bounds__(1024) void k_gemv_persist(const uint8_t *__restrict__ P, int64_t KB, int64_t NT,
                                                        const float *__restrict__ gamma_p,
                                                        const int8_t *__restrict__ Xq, int64_t ldq,
@@ -316,38 +327,34 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const uint8_t *__restrict
     const int64_t G = gridDim.x;
     const int ntiles = static_cast<int>((NT - blockIdx.x + G - 1) / G); // tiles of this workgroup (<= TMAX)
     // rescale factors of this lane's 4 output tokens, loaded before the product
+    // (clamped loads, then selects: no branch, so the four loads overlap)
     float sc[4];
     {
         const float gamma = *gamma_p;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const int64_t mm = static_cast<int64_t>(blockIdx.y) * 16 + 4 * g + rr;
-            sc[rr] = mm < M ? token_scale(gamma, beta[mm]) : 0.0f;
+            const float v = token_scale(gamma, beta[mm < M ? mm : M - 1]);
+            sc[rr] = mm < M ? v : 0.0f;
         }
     }
 
-    // activation operands of this wave's k-steps, loaded once (zero past K)
-    v4i a[SPW][NMF];
     uint32_t boff[SPW]; // byte offset of this lane's weight chunk in a tile, per k-step
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
-        const int64_t s = wave + static_cast<int64_t>(j) * KS;
-        const int64_t kb = 4 * s + g;
+        const int64_t kb = 4 * (wave + static_cast<int64_t>(j) * KS) + g;
         boff[j] = static_cast<uint32_t>(kb < KB ? kb : KB - 1) * 256u + static_cast<uint32_t>(i) * 16u;
-#pragma unroll
-        for (int d = 0; d < NMF; ++d) {
-            if (s >= nsteps)
-                a[j][d] = v4i{0, 0, 0, 0};
-            else if (TILED)
-                a[j][d] = *reinterpret_cast<const v4i *>(
-                    Xq + (((static_cast<int64_t>(blockIdx.y) * nsteps + s) * NMF + d) * 64 + lane) * 16);
-            else
-                a[j][d] = load_a16(Xq, ldq, m_a, M, K, kb * KBLK + 16 * d);
-        }
     }
+    // Ring loads.  Unguarded (many tiles per workgroup): tiles past this
+    // workgroup's last one re-read its last tile (just fetched, so from L2)
+    // and are never used; the loads are unconditional, every path has the same
+    // loads outstanding, and the wait before tile t leaves the next D-1 tiles
+    // in flight.  Guarded (a few tiles per workgroup): tiles that do not exist
+    // are skipped, which saves the redundant reads when they would be a large
+    // share of the work.
     auto load_tile = [&](int t, uint4 (&b)[SPW]) {
-        const int64_t tile = blockIdx.x + t * G;
-        const uint8_t *pt = P + (tile < NT ? tile : NT - 1) * KB * 256;
+        const int64_t tile = blockIdx.x + static_cast<int64_t>(t < ntiles ? t : ntiles - 1) * G;
+        const uint8_t *pt = P + tile * KB * 256;
 #pragma unroll
         for (int j = 0; j < SPW; ++j) b[j] = *reinterpret_cast<const uint4 *>(pt + boff[j]);
     };
@@ -356,9 +363,27 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const uint8_t *__restrict
     uint4 b[D][SPW];
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) acc[t] = v4i{0, 0, 0, 0};
+    // activation operands of this wave's k-steps, loaded once (zero past K),
+    // before the first weight tiles: waits are in issue order, so the wait for
+    // tile 0 then leaves tiles 1 .. D-1 in flight
+    v4i a[SPW][NMF];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+        const int64_t s = wave + static_cast<int64_t>(j) * KS;
+        const int64_t sx = s < nsteps ? s : nsteps - 1;
+        const int64_t kb = 4 * sx + g;
+#pragma unroll
+        for (int d = 0; d < NMF; ++d) {
+            v4i v = TILED ? *reinterpret_cast<const v4i *>(
+                                Xq + (((static_cast<int64_t>(blockIdx.y) * nsteps + sx) * NMF + d) * 64 + lane) * 16)
+                          : load_a16(Xq, ldq, m_a, M, K, kb * KBLK + 16 * d);
+            a[j][d] = s < nsteps ? v : v4i{0, 0, 0, 0};
+        }
+    }
+
 #pragma unroll
     for (int t = 0; t < D; ++t)
-        if (t < ntiles) load_tile(t, b[t]);
+        if (!GUARD || t < ntiles) load_tile(t, b[t]);
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
         if (t >= ntiles) break;
@@ -370,7 +395,7 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const uint8_t *__restrict
             gemv_step<LAYOUT, 1, NMF>(bj, a[j], accs);
             acc[t] = accs[0];
         }
-        if (t + D < ntiles) load_tile(t + D, b[t % D]);
+        if (!GUARD || t + D < ntiles) load_tile(t + D, b[t % D]);
     }
     int *red = red_dyn;
 #pragma unroll
@@ -546,43 +571,22 @@ static void launch_mfma_tw(const GemvArgs &a, int64_t KB, int64_t NT, int64_t ns
                            a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
 }
 
-template <int LAYOUT, int SPW>
-static void launch_persist(const GemvArgs &a, int64_t KB, int64_t NT, int64_t KS, hipStream_t stream)
-{
-    constexpr int TMAX = SPW >= 4 ? 4 : 8;
-    const int64_t tgroups = (a.M + 15) / 16;
-    // about one workgroup per CU in total, at most TMAX tiles each
-    int64_t wgs = 256 / tgroups;
-    const int64_t min_wgs = (NT + TMAX - 1) / TMAX;
-    wgs = wgs < min_wgs ? min_wgs : wgs;
-    wgs = wgs > NT ? NT : wgs;
-    const size_t lds = static_cast<size_t>(TMAX) * KS * 4 * 64 * sizeof(int);
-    dim3 grid(static_cast<unsigned>(wgs), static_cast<unsigned>(tgroups)), block(static_cast<unsigned>(KS * 64));
-    // more than 64 KiB of dynamic LDS must be allowed explicitly (a host-side
-    // function attribute; nothing is enqueued)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv_persist<LAYOUT, SPW, TMAX, true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv_persist<LAYOUT, SPW, TMAX, false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (a.tiled)
-        hipLaunchKernelGGL((k_gemv_persist<LAYOUT, SPW, TMAX, true>), grid, block, lds, stream, a.P, KB, NT, a.gamma,
-                           a.Xq, a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
-    else
-        hipLaunchKernelGGL((k_gemv_persist<LAYOUT, SPW, TMAX, false>), grid, block, lds, stream, a.P, KB, NT, a.gamma,
-                           a.Xq, a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
-}
-
 // Which matrix-core GEMV kernel runs for a shape.  Large layers: persistent
 // workgroups with register-resident activations, when every CU gets at least
-// two row tiles and the k-steps fit 16 waves x 4.  Otherwise one workgroup
-// per TW row tiles, reusing each activation operand over several tiles when
-// there are many tokens (the activations are then a large share of the
-// L2 -> CU traffic) and enough tiles to keep every CU busy.
+// two row tiles and the k-steps fit 16 waves x 4 (about one workgroup per CU
+// in total, at most TMAX tiles each; the weight ring is guarded when a
+// workgroup has only a few tiles).  Otherwise one workgroup per TW row tiles,
+// reusing each activation operand over several tiles when there are many
+// tokens (the activations are then a large share of the L2 -> CU traffic)
+// and enough tiles to keep every CU busy.
 struct GemvPlan {
     bool persist;
-    int spw;    // persistent: k-steps per wave (1, 2 or 4)
-    int tw;     // per-tile kernel: row tiles per workgroup (1, 2 or 4)
-    int64_t KS; // persistent: waves per workgroup
+    int spw;     // persistent: k-steps per wave (1, 2 or 4)
+    int tmax;    // persistent: most tiles per workgroup
+    bool guard;  // persistent: ring loads skipped past the workgroup's tiles
+    int64_t KS;  // persistent: waves per workgroup
+    int64_t wgs; // persistent: workgroups per token group
+    int tw;      // per-tile kernel: row tiles per workgroup (1, 2 or 4)
 };
 
 static GemvPlan gemv_plan(int layout, int64_t M, int64_t N, int64_t K)
@@ -591,16 +595,51 @@ static GemvPlan gemv_plan(int layout, int64_t M, int64_t N, int64_t K)
     const int64_t KB = layout == LAYOUT_I2 ? (K + 63) / 64 : (K + 79) / 80;
     const int64_t nsteps = (KB + 3) / 4;
     const int64_t tgroups = (M + 15) / 16;
-    GemvPlan p{false, 0, 1, 0};
+    GemvPlan p{false, 0, 0, false, 0, 0, 1};
     if (NT >= 512 * tgroups && nsteps <= 64) {
         p.persist = true;
         p.KS = nsteps < 16 ? nsteps : 16;
         const int64_t spw = (nsteps + p.KS - 1) / p.KS;
         p.spw = spw <= 1 ? 1 : (spw <= 2 ? 2 : 4);
+        p.tmax = p.spw >= 4 ? 4 : 8;
+        int64_t wgs = 256 / tgroups;
+        const int64_t min_wgs = (NT + p.tmax - 1) / p.tmax;
+        wgs = wgs < min_wgs ? min_wgs : wgs;
+        p.wgs = wgs > NT ? NT : wgs;
+        p.guard = (NT + p.wgs - 1) / p.wgs <= 5;
         return p;
     }
     p.tw = (M > 4 && NT >= 1024) ? 4 : ((M > 4 && NT >= 512) ? 2 : 1);
     return p;
+}
+
+template <int LAYOUT, int SPW, int TMAX, bool TILED, bool GUARD>
+static void launch_persist_kernel(const GemvArgs &a, int64_t KB, int64_t NT, dim3 grid, dim3 block, size_t lds,
+                                  hipStream_t stream)
+{
+    auto *f = &k_gemv_persist<LAYOUT, SPW, TMAX, TILED, GUARD>;
+    // more than 64 KiB of dynamic LDS must be allowed explicitly (a host-side
+    // function attribute; nothing is enqueued)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(f), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(lds));
+    hipLaunchKernelGGL(f, grid, block, lds, stream, a.P, KB, NT, a.gamma, a.Xq, a.ldq, a.beta, a.M, a.N, a.K, a.Y,
+                       a.y_dtype, a.ldy);
+}
+
+template <int LAYOUT, int SPW>
+static void launch_persist(const GemvArgs &a, const GemvPlan &p, int64_t KB, int64_t NT, hipStream_t stream)
+{
+    constexpr int TMAX = SPW >= 4 ? 4 : 8;
+    const int64_t tgroups = (a.M + 15) / 16;
+    const size_t lds = static_cast<size_t>(TMAX) * p.KS * 4 * 64 * sizeof(int);
+    dim3 grid(static_cast<unsigned>(p.wgs), static_cast<unsigned>(tgroups)), block(static_cast<unsigned>(p.KS * 64));
+    if (a.tiled) {
+        if (p.guard) launch_persist_kernel<LAYOUT, SPW, TMAX, true, true>(a, KB, NT, grid, block, lds, stream);
+        else launch_persist_kernel<LAYOUT, SPW, TMAX, true, false>(a, KB, NT, grid, block, lds, stream);
+    } else {
+        if (p.guard) launch_persist_kernel<LAYOUT, SPW, TMAX, false, true>(a, KB, NT, grid, block, lds, stream);
+        else launch_persist_kernel<LAYOUT, SPW, TMAX, false, false>(a, KB, NT, grid, block, lds, stream);
+    }
 }
 
 template <int LAYOUT>
@@ -611,9 +650,9 @@ static void launch_mfma_layout(const GemvArgs &a, hipStream_t stream)
     const int64_t nsteps = (KB + 3) / 4;
     const GemvPlan p = gemv_plan(LAYOUT, a.M, a.N, a.K);
     if (p.persist) {
-        if (p.spw == 1) launch_persist<LAYOUT, 1>(a, KB, NT, p.KS, stream);
-        else if (p.spw == 2) launch_persist<LAYOUT, 2>(a, KB, NT, p.KS, stream);
-        else launch_persist<LAYOUT, 4>(a, KB, NT, p.KS, stream);
+        if (p.spw == 1) launch_persist<LAYOUT, 1>(a, p, KB, NT, stream);
+        else if (p.spw == 2) launch_persist<LAYOUT, 2>(a, p, KB, NT, stream);
+        else launch_persist<LAYOUT, 4>(a, p, KB, NT, stream);
         return;
     }
     if (p.tw == 4) launch_mfma_tw<LAYOUT, 4>(a, KB, NT, nsteps, stream);
@@ -625,8 +664,8 @@ void gemv_kernel_name(int layout, int64_t M, int64_t N, int64_t K, bool tiled, c
 {
     const GemvPlan p = gemv_plan(layout, M, N, K);
     if (p.persist)
-        snprintf(buf, n, "bl::k_gemv_persist<%d, %d, %d, %s>", layout, p.spw, p.spw >= 4 ? 4 : 8,
-                 tiled ? "true" : "false");
+        snprintf(buf, n, "bl::k_gemv_persist<%d, %d, %d, %s, %s>", layout, p.spw, p.tmax, tiled ? "true" : "false",
+                 p.guard ? "true" : "false");
     else
         snprintf(buf, n, "bl::k_gemv_mfma<%d, %d, 1, %s>", layout, p.tw, tiled ? "true" : "false");
 }
