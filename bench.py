@@ -241,12 +241,18 @@ def main():
                 raise bl.BitlinearError(st, "quantize (instrumented)")
             assert bl.bitlinear_product_kernel(M, layer.N, layer.K, layout, xdt, algo) == j["kernel"]
 
-            def product(copy, j=j, xdt=xdt, algo=algo):
+            # int8 input needs no staging; base-3 weights for the GEMM need room
+            # for their i2 rewrite (that pass is then part of the timed launch)
+            nws8 = bl.bitlinear_forward_workspace_bytes(M, layer.N, layer.K, layout, xdt)
+            j["ws8"] = torch.empty(max(nws8, 16), dtype=torch.uint8, device=dev)
+
+            def product(copy, j=j, xdt=xdt, algo=algo, nws8=nws8):
                 L, lay = j["L"], j["L"]["layer"]
                 st = bl.bitlinear_forward_algo(L["P"][copy].data_ptr(), layout, L["gamma"].data_ptr(), j["M"],
                                                lay.N, lay.K, j["xq"].data_ptr(), xdt, j["ldq"],
                                                j["beta"].data_ptr(), j["y"].data_ptr(), bl.F32, j["y"].stride(0),
-                                               None, 0, algo, stream.cuda_stream)
+                                               j["ws8"].data_ptr() if nws8 > 0 else None, nws8, algo,
+                                               stream.cuda_stream)
                 if st:
                     raise bl.BitlinearError(st, "forward (instrumented)")
 

@@ -23,17 +23,6 @@ constexpr int64_t kAddSubMaxM = 0;
 // most CUs idle (measured on the 70B k/v and q layers at 64 and 176 tokens).
 constexpr int64_t kGemmMinTiles = 128;
 
-// The product kernel of algo AUTO (sizes already validated).
-int auto_algo(int64_t M, int64_t N, int layout, int x_dtype)
-{
-    if (x_dtype == BITLINEAR_I8_TILED) return BITLINEAR_ALGO_GEMV_MFMA;
-    if (M <= 16)
-        return (layout == BITLINEAR_LAYOUT_I2 && M <= kAddSubMaxM) ? BITLINEAR_ALGO_GEMV_ADDSUB
-                                                                   : BITLINEAR_ALGO_GEMV_MFMA;
-    return layout == BITLINEAR_LAYOUT_I2 && bl::gemm_tiles(M, N) >= kGemmMinTiles ? BITLINEAR_ALGO_GEMM_MFMA
-                                                                                 : BITLINEAR_ALGO_GEMV_MFMA;
-}
-
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
@@ -78,6 +67,31 @@ int64_t staged_xq_bytes(int64_t M, int64_t K, int layout)
     return round_up(rm > tl ? rm : tl, 256);
 }
 
+
+// Workspace of one forward: the quantised activations and beta (bf16/fp32
+// input), then, for base-3 weights and more than 16 tokens, room for the
+// weights rewritten in the i2 layout that the GEMM reads.
+int64_t staging_bytes(int64_t M, int64_t K, int layout, int x_dtype)
+{
+    if (x_dtype == BITLINEAR_I8 || x_dtype == BITLINEAR_I8_TILED) return 0;
+    return staged_xq_bytes(M, K, layout) + round_up(4 * M, 256);
+}
+int64_t transcode_bytes(int64_t M, int64_t N, int64_t K, int layout)
+{
+    return layout == BITLINEAR_LAYOUT_B3 && M > 16 ? round_up(bitlinear_packed_bytes(N, K, BITLINEAR_LAYOUT_I2), 256)
+                                                   : 0;
+}
+
+// The product kernel of algo AUTO (sizes already validated).
+int auto_algo(int64_t M, int64_t N, int layout, int x_dtype)
+{
+    if (x_dtype == BITLINEAR_I8_TILED) return BITLINEAR_ALGO_GEMV_MFMA;
+    if (M <= 16)
+        return (layout == BITLINEAR_LAYOUT_I2 && M <= kAddSubMaxM) ? BITLINEAR_ALGO_GEMV_ADDSUB
+                                                                   : BITLINEAR_ALGO_GEMV_MFMA;
+    return bl::gemm_tiles(M, N) >= kGemmMinTiles ? BITLINEAR_ALGO_GEMM_MFMA : BITLINEAR_ALGO_GEMV_MFMA;
+}
+
 } // namespace
 
 extern "C" {
@@ -115,9 +129,10 @@ int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int l
 {
     if (M < 1 || M > BITLINEAR_MAX_M || N < 1 || K < 1 || K > BITLINEAR_MAX_K || !valid_layout(layout))
         return -1;
-    if (x_dtype == BITLINEAR_I8 || x_dtype == BITLINEAR_I8_TILED) return 0;
-    if (x_dtype != BITLINEAR_F32 && x_dtype != BITLINEAR_BF16) return -1;
-    return staged_xq_bytes(M, K, layout) + round_up(4 * M, 256);
+    if (x_dtype != BITLINEAR_I8 && x_dtype != BITLINEAR_I8_TILED && x_dtype != BITLINEAR_F32 &&
+        x_dtype != BITLINEAR_BF16)
+        return -1;
+    return staging_bytes(M, K, layout, x_dtype) + transcode_bytes(M, N, K, layout);
 }
 
 int bitlinear_auto_algo(int64_t M, int64_t N, int64_t K, int layout, int x_dtype)
@@ -139,7 +154,7 @@ const char *bitlinear_product_kernel(int64_t M, int64_t N, int64_t K, int layout
         return nullptr;
     if (algo == BITLINEAR_ALGO_AUTO) algo = auto_algo(M, N, layout, x_dtype);
     if ((algo == BITLINEAR_ALGO_GEMV_ADDSUB && (M > 16 || layout != BITLINEAR_LAYOUT_I2)) ||
-        (algo == BITLINEAR_ALGO_GEMM_MFMA && layout != BITLINEAR_LAYOUT_I2) ||
+        (algo == BITLINEAR_ALGO_GEMM_MFMA && layout != BITLINEAR_LAYOUT_I2 && M <= 16) ||
         (x_dtype == BITLINEAR_I8_TILED && algo != BITLINEAR_ALGO_GEMV_MFMA))
         return nullptr;
     if (algo == BITLINEAR_ALGO_GEMV_ADDSUB) {
@@ -271,7 +286,7 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
     if (algo == BITLINEAR_ALGO_AUTO) algo = auto_algo(M, N, layout, x_dtype);
     if (algo == BITLINEAR_ALGO_GEMV_ADDSUB && (M > 16 || layout != BITLINEAR_LAYOUT_I2))
         return BITLINEAR_ERR_UNSUPPORTED;
-    if (algo == BITLINEAR_ALGO_GEMM_MFMA && layout != BITLINEAR_LAYOUT_I2) return BITLINEAR_ERR_UNSUPPORTED;
+    if (algo == BITLINEAR_ALGO_GEMM_MFMA && layout != BITLINEAR_LAYOUT_I2 && M <= 16) return BITLINEAR_ERR_UNSUPPORTED;
     if (x_dtype == BITLINEAR_I8_TILED && algo != BITLINEAR_ALGO_GEMV_MFMA) return BITLINEAR_ERR_UNSUPPORTED;
 
     (void)hipGetLastError();
@@ -316,7 +331,17 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
     switch (algo) {
     case BITLINEAR_ALGO_GEMV_ADDSUB: e = bl::launch_gemv_addsub(a, st); break;
     case BITLINEAR_ALGO_GEMV_MFMA: e = bl::launch_gemv_mfma(a, st); break;
-    default: e = bl::launch_gemm_mfma(a, st); break;
+    default:
+        if (layout == BITLINEAR_LAYOUT_B3) {
+            // the GEMM reads i2: rewrite the base-3 weights into the workspace first
+            uint8_t *p2 = static_cast<uint8_t *>(ws) + staging_bytes(M, K, layout, x_dtype);
+            e = bl::launch_b3_to_i2(P, N, K, p2, st);
+            if (e != hipSuccess) return BITLINEAR_ERR_LAUNCH;
+            a.P = p2;
+            a.layout = BITLINEAR_LAYOUT_I2;
+        }
+        e = bl::launch_gemm_mfma(a, st);
+        break;
     }
     return status_of(e);
 }

@@ -101,6 +101,46 @@ __device__ __forceinline__ void store_out(void *Y, int y_dtype, int64_t ldy, int
     }
 }
 
+// Base-3 digits of bytes b <= 242, two bytes per 16-bit lane: floor(b / 3^(4-t))
+// is (b * m) >> s with (m, s) = (203, 14), (19, 9), (57, 9), (171, 9) for
+// t = 0..3 (exact for every b <= 242, b * m < 2^16); digit t is
+// H_t - 3 H_(t-1), t = 0 the most significant.
+__device__ __forceinline__ uint32_t pk_mul_u16(uint32_t a, uint32_t b)
+{
+    typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+    v2u16 x = __builtin_bit_cast(v2u16, a), y = __builtin_bit_cast(v2u16, b);
+    return __builtin_bit_cast(uint32_t, static_cast<v2u16>(x * y));
+}
+
+__device__ __forceinline__ uint32_t pk_shr_u16(uint32_t a, int s)
+{
+    typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+    v2u16 x = __builtin_bit_cast(v2u16, a);
+    v2u16 sh = {static_cast<unsigned short>(s), static_cast<unsigned short>(s)};
+    return __builtin_bit_cast(uint32_t, static_cast<v2u16>(x >> sh));
+}
+
+__device__ __forceinline__ uint32_t pk_sub_u16(uint32_t a, uint32_t b)
+{
+    typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+    v2u16 x = __builtin_bit_cast(v2u16, a), y = __builtin_bit_cast(v2u16, b);
+    return __builtin_bit_cast(uint32_t, static_cast<v2u16>(x - y));
+}
+
+// digits of the two bytes held in the 16-bit lanes of 'b' (each <= 242)
+__device__ __forceinline__ void b3_digits_pair(uint32_t b, uint32_t c[5])
+{
+    const uint32_t h0 = pk_shr_u16(pk_mul_u16(b, 0x00cb00cbu), 14); // b / 81
+    const uint32_t h1 = pk_shr_u16(pk_mul_u16(b, 0x00130013u), 9);  // b / 27
+    const uint32_t h2 = pk_shr_u16(pk_mul_u16(b, 0x00390039u), 9);  // b / 9
+    const uint32_t h3 = pk_shr_u16(pk_mul_u16(b, 0x00ab00abu), 9);  // b / 3
+    c[0] = h0;
+    c[1] = pk_sub_u16(h1, pk_mul_u16(h0, 0x00030003u));
+    c[2] = pk_sub_u16(h2, pk_mul_u16(h1, 0x00030003u));
+    c[3] = pk_sub_u16(h3, pk_mul_u16(h2, 0x00030003u));
+    c[4] = pk_sub_u16(b, pk_mul_u16(h3, 0x00030003u));
+}
+
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 

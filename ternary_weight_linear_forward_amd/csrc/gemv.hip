@@ -57,49 +57,10 @@ __device__ __forceinline__ v4i i2_word_signed(uint32_t w)
 }
 
 // Base-3 digit t (t = 0 most significant) of each byte of a b3 word, as signed
-// bytes digit - 1.  Two bytes per 16-bit lane: floor(b / 3^(4-t)) is
-// (b * m) >> s with (m, s) = (203, 14), (19, 9), (57, 9), (171, 9) for
-// t = 0..3, exact for every b <= 242 with b * m < 2^16; digit t is
-// H_t - 3 H_(t-1) with H_t = floor(b / 3^(4-t)).
+// bytes digit - 1 (digits from b3_digits_pair, two bytes per 16-bit lane).
 struct B3Digits {
     uint32_t d[5];
 };
-
-__device__ __forceinline__ uint32_t pk_mul_u16(uint32_t a, uint32_t b)
-{
-    typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
-    v2u16 x = __builtin_bit_cast(v2u16, a), y = __builtin_bit_cast(v2u16, b);
-    return __builtin_bit_cast(uint32_t, static_cast<v2u16>(x * y));
-}
-
-__device__ __forceinline__ uint32_t pk_shr_u16(uint32_t a, int s)
-{
-    typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
-    v2u16 x = __builtin_bit_cast(v2u16, a);
-    v2u16 sh = {static_cast<unsigned short>(s), static_cast<unsigned short>(s)};
-    return __builtin_bit_cast(uint32_t, static_cast<v2u16>(x >> sh));
-}
-
-__device__ __forceinline__ uint32_t pk_sub_u16(uint32_t a, uint32_t b)
-{
-    typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
-    v2u16 x = __builtin_bit_cast(v2u16, a), y = __builtin_bit_cast(v2u16, b);
-    return __builtin_bit_cast(uint32_t, static_cast<v2u16>(x - y));
-}
-
-// digits of the two bytes held in the 16-bit lanes of 'b' (each <= 242)
-__device__ __forceinline__ void b3_digits_pair(uint32_t b, uint32_t c[5])
-{
-    const uint32_t h0 = pk_shr_u16(pk_mul_u16(b, 0x00cb00cbu), 14); // b / 81
-    const uint32_t h1 = pk_shr_u16(pk_mul_u16(b, 0x00130013u), 9);  // b / 27
-    const uint32_t h2 = pk_shr_u16(pk_mul_u16(b, 0x00390039u), 9);  // b / 9
-    const uint32_t h3 = pk_shr_u16(pk_mul_u16(b, 0x00ab00abu), 9);  // b / 3
-    c[0] = h0;
-    c[1] = pk_sub_u16(h1, pk_mul_u16(h0, 0x00030003u));
-    c[2] = pk_sub_u16(h2, pk_mul_u16(h1, 0x00030003u));
-    c[3] = pk_sub_u16(h3, pk_mul_u16(h2, 0x00030003u));
-    c[4] = pk_sub_u16(b, pk_mul_u16(h3, 0x00030003u));
-}
 
 __device__ __forceinline__ B3Digits b3_word_signed(uint32_t w)
 {

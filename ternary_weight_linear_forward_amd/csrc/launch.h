@@ -14,6 +14,9 @@ hipError_t launch_quantize_weights(const float *W, int64_t N, int64_t K, int64_t
 hipError_t launch_pack(const int8_t *T, int64_t N, int64_t K, int64_t ldt, int layout, uint8_t *P,
                        hipStream_t stream);
 
+// Rewrite b3-packed weights P3 [N x K] in the i2 layout (P2, i2 packed size).
+hipError_t launch_b3_to_i2(const uint8_t *P3, int64_t N, int64_t K, uint8_t *P2, hipStream_t stream);
+
 hipError_t launch_quant_act(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int8_t *Xq,
                             int64_t ldq, float *beta, hipStream_t stream);
 

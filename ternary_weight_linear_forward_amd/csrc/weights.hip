@@ -207,6 +207,51 @@ __global__ __launch_bounds__(256) void k_pack_b3(const int8_t *__restrict__ T, i
     *reinterpret_cast<uint4 *>(P + idx * 16) = make_uint4(word[0], word[1], word[2], word[3]);
 }
 
+// b3 -> i2 transcode (for the GEMM, which reads i2).  One thread per b3 chunk
+// (row r of tile, block kb3: weights 80 kb3 .. +79).  Digit t of its 16 bytes
+// is the 16 weights k0 = 80 kb3 + 16 t .. k0+15, which is exactly i2 word
+// d = (k0 % 64) / 16 of i2 block kb2 = k0 / 64 (80 and 64 are multiples of
+// 16): the thread decodes the chunk once and writes five i2 words.  i2 words
+// past the b3 blocks (only when 64 * KB2 > 80 * KB3) are padding, T = 0; the
+// thread of the row's last b3 chunk writes them.
+__global__ __launch_bounds__(256) void k_b3_to_i2(const uint8_t *__restrict__ P3, int64_t KB3, int64_t KB2,
+                                                  int64_t nchunks, uint8_t *__restrict__ P2)
+{
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; // (tile * KB3 + kb3) * 16 + r
+    if (idx >= nchunks) return;
+    const int64_t r = idx & 15, tk = idx >> 4;
+    const int64_t tile = tk / KB3, kb3 = tk - tile * KB3;
+    const uint4 c = *reinterpret_cast<const uint4 *>(P3 + idx * 16);
+    const uint32_t bw[4] = {c.x, c.y, c.z, c.w};
+    // word t: byte i = 4q + j of the chunk (weight k0 + i) at bits 8j + 2q
+    uint32_t out[5] = {0, 0, 0, 0, 0};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t lo[5], hi[5];
+        b3_digits_pair(bw[q] & 0x00ff00ffu, lo);        // bytes 0 and 2 of the word
+        b3_digits_pair((bw[q] >> 8) & 0x00ff00ffu, hi); // bytes 1 and 3
+#pragma unroll
+        for (int t = 0; t < 5; ++t) out[t] |= (lo[t] | (hi[t] << 8)) << (2 * q);
+    }
+    uint32_t *row = reinterpret_cast<uint32_t *>(P2) + tile * KB2 * 64 + r * 4; // word (kb2, d) at kb2 * 64 + d
+#pragma unroll
+    for (int t = 0; t < 5; ++t) {
+        const int64_t k0 = kb3 * 80 + 16 * t;
+        if (k0 < KB2 * 64) row[(k0 >> 6) * 64 + ((k0 >> 4) & 3)] = out[t];
+    }
+    if (kb3 == KB3 - 1)
+        for (int64_t k0 = KB3 * 80; k0 < KB2 * 64; k0 += 16) row[(k0 >> 6) * 64 + ((k0 >> 4) & 3)] = I2_ZERO_WORD;
+}
+
+hipError_t launch_b3_to_i2(const uint8_t *P3, int64_t N, int64_t K, uint8_t *P2, hipStream_t stream)
+{
+    const int64_t NT = (N + 15) / 16, KB3 = (K + 79) / 80, KB2 = (K + 63) / 64;
+    const int64_t nchunks = NT * KB3 * 16;
+    hipLaunchKernelGGL(k_b3_to_i2, dim3(static_cast<unsigned>((nchunks + 255) / 256)), dim3(256), 0, stream, P3,
+                       KB3, KB2, nchunks, P2);
+    return hipGetLastError();
+}
+
 static unsigned grid_rows(int64_t N) { return static_cast<unsigned>(N < 65535 ? N : 65535); }
 
 hipError_t launch_quantize_weights(const float *W, int64_t N, int64_t K, int64_t ldw, int8_t *T, float *gamma,

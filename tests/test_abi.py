@@ -127,7 +127,7 @@ def fw(**kw):
     (dict(ws=C), bl.ERR_INVALID_ARG),                               # workspace overlaps X
     (dict(algo=bl.ALGO_GEMV_ADDSUB, M=17), bl.ERR_UNSUPPORTED),
     (dict(algo=bl.ALGO_GEMV_ADDSUB, layout=bl.LAYOUT_B3), bl.ERR_UNSUPPORTED),
-    (dict(algo=bl.ALGO_GEMM_MFMA, layout=bl.LAYOUT_B3), bl.ERR_UNSUPPORTED),
+    (dict(algo=bl.ALGO_GEMM_MFMA, layout=bl.LAYOUT_B3), bl.ERR_UNSUPPORTED),  # b3 GEMM needs M > 16
 ])
 def test_forward_rejects(kw, status):
     assert fw(**kw) == status
@@ -196,7 +196,7 @@ def test_auto_algo_dispatch():
     for M in (1, 4, 16):
         assert f(M, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMV_MFMA
     assert f(2048, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMM_MFMA
-    assert f(2048, 3200, 3200, bl.LAYOUT_B3, bl.BF16) == bl.ALGO_GEMV_MFMA
+    assert f(2048, 3200, 3200, bl.LAYOUT_B3, bl.BF16) == bl.ALGO_GEMM_MFMA  # through an i2 rewrite
     assert f(2048, 3200, 3200, bl.LAYOUT_I2, bl.I8_TILED) == bl.ALGO_GEMV_MFMA
     assert f(176, 1024, 8192, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMV_MFMA  # 16 tiles: GPU mostly idle
     assert f(176, 8192, 8192, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMM_MFMA
@@ -219,3 +219,15 @@ def test_product_kernel_names():
     assert f(3, 64, 64, bl.LAYOUT_I2, bl.BF16, bl.ALGO_GEMV_ADDSUB) == "bl::k_gemv_addsub<4>"
     assert f(3, 64, 64, bl.LAYOUT_B3, bl.BF16, bl.ALGO_GEMM_MFMA) is None
     assert f(0, 64, 64, bl.LAYOUT_I2, bl.BF16) is None
+
+
+def test_b3_gemm_workspace():
+    """Base-3 weights with more than 16 tokens: the workspace also holds the
+    weights rewritten in the i2 layout for the GEMM."""
+    M, N, K = 176, 1000, 3000
+    base = bl.bitlinear_forward_workspace_bytes(M, N, K, bl.LAYOUT_I2, bl.BF16)
+    b3 = bl.bitlinear_forward_workspace_bytes(M, N, K, bl.LAYOUT_B3, bl.BF16)
+    i2 = bl.bitlinear_packed_bytes(N, K, bl.LAYOUT_I2)
+    assert b3 >= base and b3 - bl.bitlinear_forward_workspace_bytes(M, N, K, bl.LAYOUT_B3, bl.I8) < b3
+    assert bl.bitlinear_forward_workspace_bytes(M, N, K, bl.LAYOUT_B3, bl.I8) >= i2
+    assert bl.bitlinear_forward_workspace_bytes(16, N, K, bl.LAYOUT_B3, bl.I8) == 0

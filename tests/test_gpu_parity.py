@@ -198,7 +198,8 @@ def test_forward_small(algo_name, algo, layout, M, N, K):
 
 @pytest.mark.parametrize("algo_name,algo,layout", [("mfma_gemv", bl.ALGO_GEMV_MFMA, "i2"),
                                                    ("mfma_gemv", bl.ALGO_GEMV_MFMA, "b3"),
-                                                   ("gemm", bl.ALGO_GEMM_MFMA, "i2")])
+                                                   ("gemm", bl.ALGO_GEMM_MFMA, "i2"),
+                                                   ("gemm", bl.ALGO_GEMM_MFMA, "b3")])
 @pytest.mark.parametrize("M,N,K", [(17, 40, 100), (64, 96, 512), (130, 257, 700), (256, 128, 64)])
 def test_forward_many_tokens(algo_name, algo, layout, M, N, K):
     log("forward", algo_name, layout, M, N, K)
@@ -212,6 +213,8 @@ def test_gemm_tile_shapes(M, N, K):
     ragged in M and N; an odd number of k-blocks ends in a half stage)."""
     log("forward gemm tiles", M, N, K)
     run_forward_case(M, N, K, bl.ALGO_GEMM_MFMA, "i2", seed=M + 7 * N + K, y_kinds=("i32", "f32"))
+    if M * N <= 1100 * 5000:  # base-3 weights through the i2 rewrite
+        run_forward_case(M, N, K, bl.ALGO_GEMM_MFMA, "b3", seed=M + 7 * N + K + 1, y_kinds=("i32",))
 
 
 @pytest.mark.parametrize("layout", ["i2", "b3"])
