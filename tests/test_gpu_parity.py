@@ -291,6 +291,42 @@ def test_forward_degenerate():
         assert np.array_equal(acc, ref["acc"])
 
 
+@pytest.mark.parametrize("layout", ["i2", "b3"])
+def test_forward_max_k(layout):
+    """K = BITLINEAR_MAX_K: the row-major staging (K beyond the tiled
+    quantiser's range), and the largest accumulator the contract allows,
+    127 * K = 16,646,144 < 2^24, which float(acc) still represents exactly."""
+    M, N, K = 3, 40, bl.MAX_K
+    t = synth.ternary_weights(N, K, seed=101)
+    t[0] = 1                                        # row 0: all +1
+    x = synth.activations_bf16(M, K, seed=102)
+    x[1] = synth.to_bf16_bits(np.full(K, 0.75, np.float32))  # token 1: every q = 127
+    ref = oracle.forward(t, np.float32(0.03), x)
+    assert ref["acc"][1, 0] == 127 * K
+    P = to_dev(oracle.pack(t, LAYOUTS[layout]))
+    gamma = to_dev(np.array([0.03], np.float32))
+    algos = [bl.ALGO_AUTO, bl.ALGO_GEMV_MFMA] + ([bl.ALGO_GEMV_ADDSUB, bl.ALGO_GEMM_MFMA] if layout == "i2" else [])
+    for algo in algos:
+        acc = to_host(bl.forward(P, LAYOUTS[layout], gamma, to_dev(x), N, K, y_dtype=torch.int32, algo=algo))
+        assert np.array_equal(acc, ref["acc"]), algo
+        y = to_host(bl.forward(P, LAYOUTS[layout], gamma, to_dev(x), N, K, algo=algo))
+        assert_f32_parity(y, ref["y"])
+
+
+def test_forward_max_m():
+    """M = BITLINEAR_MAX_M tokens: 4096 token groups for the GEMV, 256-token
+    tiles for the GEMM."""
+    M, N, K = bl.MAX_M, 48, 72
+    t = synth.ternary_weights(N, K, seed=103)
+    x = synth.activations_bf16(M, K, seed=104)
+    ref = oracle.forward(t, np.float32(0.01), x)
+    gamma = to_dev(np.array([0.01], np.float32))
+    for layout, algo in (("i2", bl.ALGO_AUTO), ("i2", bl.ALGO_GEMV_MFMA), ("b3", bl.ALGO_AUTO)):
+        P = to_dev(oracle.pack(t, LAYOUTS[layout]))
+        acc = to_host(bl.forward(P, LAYOUTS[layout], gamma, to_dev(x), N, K, y_dtype=torch.int32, algo=algo))
+        assert np.array_equal(acc, ref["acc"]), (layout, algo)
+
+
 def test_forward_strided_output_and_input():
     M, N, K = 16, 96, 200
     t = synth.ternary_weights(N, K, seed=95)
