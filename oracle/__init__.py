@@ -35,6 +35,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 LAYOUT_I2 = 0
 LAYOUT_B3 = 1
+LAYOUT_B1 = 2
 
 _ERRORS = {
     1: "non-finite input",
@@ -71,6 +72,9 @@ def _load():
         sig = {
             "oracle_absmean": ([P, I, P], ctypes.c_int),
             "oracle_ternarize": ([P, I, ctypes.c_float, P], ctypes.c_int),
+            "oracle_binarize": ([P, I, P], ctypes.c_int),
+            "oracle_pack_b1": ([P, I, I, P], ctypes.c_int),
+            "oracle_unpack_b1": ([P, I, I, P], ctypes.c_int),
             "oracle_packed_bytes": ([I, I, ctypes.c_int], ctypes.c_int64),
             "oracle_pack_i2": ([P, I, I, P], ctypes.c_int),
             "oracle_unpack_i2": ([P, I, I, P], ctypes.c_int),
@@ -123,17 +127,37 @@ def quantize_weights(w: np.ndarray):
     return ternarize(w, g), g
 
 
+def binarize(w: np.ndarray) -> np.ndarray:
+    """T = +1 where w >= 0 (including -0), -1 where w < 0: the binary weights of
+    the predecessor variant (HackerPapers digest: the original BitNet used -1
+    or +1; LIT-380 Key takeaways #2: two states against three)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    t = np.empty(w.shape, np.int8)
+    _check(_load().oracle_binarize(_ptr(w), w.size, _ptr(t)))
+    return t
+
+
+def quantize_weights_binary(w: np.ndarray):
+    """(T, gamma) of the binary variant: sign weights, the same absmean scale."""
+    return binarize(w), absmean(w)
+
+
+_PACK = {LAYOUT_I2: ("oracle_pack_i2", "oracle_unpack_i2"), LAYOUT_B3: ("oracle_pack_b3", "oracle_unpack_b3"),
+         LAYOUT_B1: ("oracle_pack_b1", "oracle_unpack_b1")}
+
+
 def packed_bytes(N: int, K: int, layout: int) -> int:
     return int(_load().oracle_packed_bytes(N, K, layout))
 
 
 def pack(t: np.ndarray, layout: int) -> np.ndarray:
-    """Pack T[N x K] into the i2 (2 bits/weight, "GPUs Go Brrr" thread) or b3
-    (5 trits per byte, "How to pack ternary numbers in 8-bit bytes" thread) layout."""
+    """Pack T[N x K] into the i2 (2 bits/weight, "GPUs Go Brrr" thread), b3
+    (5 trits per byte, "How to pack ternary numbers in 8-bit bytes" thread) or,
+    for binary weights, b1 (1 bit per weight) layout."""
     t = np.ascontiguousarray(t, dtype=np.int8)
     N, K = t.shape
     p = np.zeros(packed_bytes(N, K, layout), np.uint8)
-    fn = _load().oracle_pack_i2 if layout == LAYOUT_I2 else _load().oracle_pack_b3
+    fn = getattr(_load(), _PACK[layout][0])
     _check(fn(_ptr(t), N, K, _ptr(p)))
     return p
 
@@ -143,7 +167,7 @@ def unpack(p: np.ndarray, N: int, K: int, layout: int) -> np.ndarray:
     if p.size < packed_bytes(N, K, layout):
         raise OracleError("packed buffer too small")
     t = np.empty((N, K), np.int8)
-    fn = _load().oracle_unpack_i2 if layout == LAYOUT_I2 else _load().oracle_unpack_b3
+    fn = getattr(_load(), _PACK[layout][1])
     _check(fn(_ptr(p), N, K, _ptr(t)))
     return t
 

@@ -149,6 +149,21 @@ int oracle_ternarize(const float *w, int64_t count, float gamma, int8_t *t)
     return ORACLE_OK;
 }
 
+/* Binary weights, the predecessor variant: the original BitNet used weights  */
+/* -1 or +1 (HackerPapers digest of the paper's threads; LIT-380, Key        */
+/* takeaways, bullet 2, contrasts three states with two).  No formula is on   */
+/* the pages; reading: T = sign(w) with w >= 0 (including -0) giving +1, and  */
+/* the same scale gamma = mean|W| as the ternary path.                        */
+/* ------------------------------------------------------------------------ */
+int oracle_binarize(const float *w, int64_t count, int8_t *t)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        if (!isfinite(w[i])) return ORACLE_ERR_NONFINITE;
+        t[i] = w[i] >= 0.0f ? 1 : -1;
+    }
+    return ORACLE_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Packed layouts (a convention of this library; the pages fix none).        */
 /* ------------------------------------------------------------------------ */
@@ -169,6 +184,14 @@ int oracle_ternarize(const float *w, int64_t count, float gamma, int8_t *t)
  * kb*80 + 16t + i (t = 0..4) as sum_t c_t * 3^(4 - t): weight t = 0 is the
  * most significant base-3 digit.  So digit t of bytes 0..15 covers 16
  * consecutive weights.  Values 243..255 are never written.
+ *
+ * "b1" (1 bit per weight, binary weights only): a k-block is 128 weights.  The
+ * chunk of row n and k-block kb starts at byte ((n/16)*KB1 + kb)*256 +
+ * (n%16)*16, KB1 = ceil(K/128).  Its word d (d = 0..3) holds weights
+ * kb*128 + 32d + 4s + j (s = 0..7, j = 0..3) at bit 8j + s: 1 for +1, 0 for
+ * -1.  Bits past K (and rows past N) are 0; binary weights have no zero, so
+ * those positions carry a weight and the product must meet zero activations
+ * there.
  */
 static int8_t t_at(const int8_t *t, int64_t N, int64_t K, int64_t n, int64_t k)
 {
@@ -178,7 +201,7 @@ static int8_t t_at(const int8_t *t, int64_t N, int64_t K, int64_t n, int64_t k)
 int64_t oracle_packed_bytes(int64_t N, int64_t K, int layout)
 {
     int64_t NT = (N + 15) / 16;
-    int64_t KB = layout == 0 ? (K + 63) / 64 : (K + 79) / 80;
+    int64_t KB = layout == 0 ? (K + 63) / 64 : (layout == 1 ? (K + 79) / 80 : (K + 127) / 128);
     return NT * KB * 256;
 }
 
@@ -248,6 +271,41 @@ int oracle_unpack_b3(const uint8_t *p, int64_t N, int64_t K, int8_t *t)
             unsigned digit = byte;
             for (int d = 4; d > (int)(r / 16); --d) digit /= 3;
             t[n * K + k] = (int8_t)((int)(digit % 3) - 1);
+        }
+    return ORACLE_OK;
+}
+
+int oracle_pack_b1(const int8_t *t, int64_t N, int64_t K, uint8_t *p)
+{
+    int64_t NT = (N + 15) / 16, KB = (K + 127) / 128;
+    for (int64_t n = 0; n < NT * 16; ++n)
+        for (int64_t kb = 0; kb < KB; ++kb) {
+            uint8_t *chunk = p + ((n / 16) * KB + kb) * 256 + (n % 16) * 16;
+            for (int d = 0; d < 4; ++d)
+                for (int j = 0; j < 4; ++j) {
+                    unsigned byte = 0;
+                    for (int s = 0; s < 8; ++s) {
+                        int64_t k = kb * 128 + 32 * d + 4 * s + j;
+                        if (n >= N || k >= K) continue; /* padding: bit 0 */
+                        int8_t v = t[n * K + k];
+                        if (v != 1 && v != -1) return ORACLE_ERR_ARG;
+                        byte |= (unsigned)(v == 1) << s;
+                    }
+                    chunk[4 * d + j] = (uint8_t)byte;
+                }
+        }
+    return ORACLE_OK;
+}
+
+int oracle_unpack_b1(const uint8_t *p, int64_t N, int64_t K, int8_t *t)
+{
+    int64_t KB = (K + 127) / 128;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t kb = k / 128, r = k % 128;
+            int d = (int)(r / 32), s = (int)((r % 32) / 4), j = (int)(r % 4);
+            uint8_t byte = p[((n / 16) * KB + kb) * 256 + (n % 16) * 16 + 4 * d + j];
+            t[n * K + k] = (byte >> s) & 1u ? 1 : -1;
         }
     return ORACLE_OK;
 }

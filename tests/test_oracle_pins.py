@@ -404,3 +404,78 @@ def test_forward_tracks_the_linear_layer():
     ref = x.astype(np.float64) @ w.astype(np.float64).T
     corr = np.corrcoef(y.reshape(-1), ref.reshape(-1))[0, 1]
     assert corr > 0.7
+
+
+# ---------------------------------------------------------------------------
+# Binary variant (weights -1 or +1) and its 1-bit layout
+# ---------------------------------------------------------------------------
+def test_binarize_hand_vector():
+    v = HV["binarize_signs"]
+    w = np.array(v["W"], np.float32)
+    assert np.signbit(w[3])  # the vector holds a negative zero
+    assert oracle.binarize(w).tolist() == v["T"]
+
+
+def test_binarize_invariants():
+    w = synth.latent_weights(64, 300, seed=211)
+    t = oracle.binarize(w)
+    assert set(np.unique(t).tolist()) <= {-1, 1}
+    assert np.array_equal(oracle.binarize(-w), -t)          # no zeros in a Gaussian draw
+    assert np.array_equal(oracle.binarize(w * np.float32(2.0 ** 17)), t)
+    assert np.array_equal(t == 1, w >= 0)
+    t2, g = oracle.quantize_weights_binary(w)
+    assert np.array_equal(t2, t) and g == oracle.absmean(w)  # the same scale as the ternary path
+    # a symmetric distribution: the +1 share is 1/2 within 4 sigma
+    share = (t == 1).mean()
+    assert abs(share - 0.5) < 4 * np.sqrt(0.25 / t.size)
+
+
+def test_binarize_rejects_nonfinite():
+    with pytest.raises(oracle.OracleError):
+        oracle.binarize(np.array([1.0, np.nan], np.float32))
+
+
+def test_pack_b1_hand_words():
+    v = HV["pack_b1_words"]
+    for case in v["cases"]:
+        t = -np.ones((1, v["K"]), np.int8)
+        if case["plus_ones"] == "all":
+            t[:] = 1
+        else:
+            t[0, case["plus_ones"]] = 1
+        p = oracle.pack(t, oracle.LAYOUT_B1)
+        assert p.size == 256                      # one tile x one 128-weight block x 16 bytes
+        words = p[:16].view("<u4")
+        assert hex(int(words[0])) == case["word0_hex"], case
+        assert not words[1:].any()                # weights 32..127 are padding: bits 0
+        assert not p[16:].any()                   # rows 1..15 of the tile: padding
+    b = v["second_block"]
+    t = -np.ones((1, b["K"]), np.int8)
+    t[0, b["plus_ones"]] = 1
+    p = oracle.pack(t, oracle.LAYOUT_B1)
+    assert p.size == 512
+    assert not p[:16].any()
+    assert hex(int(p[256:272].view("<u4")[0])) == b["chunk1_word0_hex"]
+
+
+def test_pack_b1_round_trip_and_sizes():
+    for N, K in [(1, 1), (17, 127), (33, 300), (16, 8192)]:
+        t = synth.ternary_weights(N, K, seed=N + K)
+        t = np.where(t >= 0, 1, -1).astype(np.int8)
+        p = oracle.pack(t, oracle.LAYOUT_B1)
+        assert p.size == ((N + 15) // 16) * 16 * ((K + 127) // 128) * 16
+        assert np.array_equal(oracle.unpack(p, N, K, oracle.LAYOUT_B1), t)
+    assert oracle.packed_bytes(16, 8192, oracle.LAYOUT_B1) == 16 * 1024  # 1 bit per weight
+    with pytest.raises(oracle.OracleError):
+        oracle.pack(np.zeros((1, 8), np.int8), oracle.LAYOUT_B1)       # no zero in binary weights
+
+
+def test_binary_product_is_add_sub():
+    """acc = sum of q where T = +1 minus sum where T = -1, with no multiply."""
+    M, N, K = 5, 9, 200
+    t = oracle.binarize(synth.latent_weights(N, K, seed=213))
+    q, _ = oracle.quantize_act(synth.activations_f32(M, K, seed=214))
+    acc = oracle.matmul(q, t)
+    qs = q.astype(np.int64)
+    want = np.array([[qs[m][t[n] == 1].sum() - qs[m][t[n] == -1].sum() for n in range(N)] for m in range(M)])
+    assert np.array_equal(acc, want)
