@@ -52,7 +52,8 @@ def parse():
     ap.add_argument("--workload", default="decode_3b",
                     choices=["decode_3b", "prefill_3b", "llama70b_layers", "stack_3b_26"])
     ap.add_argument("--batches", default=None, help="comma list overriding the workload's batch sizes")
-    ap.add_argument("--layout", default="i2", choices=["i2", "b3"])
+    ap.add_argument("--layout", default="i2", choices=["i2", "b3", "b1"],
+                    help="packed weight layout; b1 runs the binary-weight variant (sign quantiser)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -85,7 +86,8 @@ def main():
     from ternary_weight_linear_forward_amd import synth, workloads
 
     wl = workloads.ALL[args.workload]
-    layout = bl.LAYOUT_I2 if args.layout == "i2" else bl.LAYOUT_B3
+    layout = {"i2": bl.LAYOUT_I2, "b3": bl.LAYOUT_B3, "b1": bl.LAYOUT_B1}[args.layout]
+    weight_quant = bl.binarize_weights if layout == bl.LAYOUT_B1 else bl.quantize_weights
     batches = tuple(int(b) for b in args.batches.split(",")) if args.batches else wl.batches
     dev = torch.device("cuda")
     torch.cuda.set_device(0)
@@ -110,7 +112,7 @@ def main():
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            T, gamma = bl.quantize_weights(w, stream=stream)
+            T, gamma = weight_quant(w, stream=stream)
             P = bl.pack(T, layout, stream=stream)
             e1.record(stream)
             torch.cuda.synchronize()
@@ -333,6 +335,7 @@ def main():
             "layers": {L["layer"].name: [L["layer"].N, L["layer"].K] for L in layers},
             "batches": list(batches),
             "layout": args.layout,
+            "weights": "binary {-1, +1}" if layout == bl.LAYOUT_B1 else "ternary {-1, 0, +1}",
             "x_dtype": "bf16" if chain is None else "bf16 stack input, fp32 between links",
             **({"depth": workloads.STACK_DEPTH,
                 "glue": "qkv -> o reads qkv[:, :3200]; gate_up -> down reads gate_up[:, :8640]; "

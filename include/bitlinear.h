@@ -67,7 +67,8 @@ typedef enum {
 
 typedef enum {
     BITLINEAR_LAYOUT_I2 = 0, /* 2 bits per weight                     */
-    BITLINEAR_LAYOUT_B3 = 1  /* base 3, 5 weights per byte            */
+    BITLINEAR_LAYOUT_B3 = 1, /* base 3, 5 weights per byte            */
+    BITLINEAR_LAYOUT_B1 = 2  /* 1 bit per weight, binary weights only */
 } bitlinear_layout_t;
 
 typedef enum {
@@ -85,7 +86,7 @@ int bitlinear_version(void);
 
 /*
  * Packed layouts (this library's convention; the pages fix none).
- * Both store code c = T + 1 in {0, 1, 2} and pad with T = 0 (rows up to a
+ * I2 and B3 store code c = T + 1 in {0, 1, 2} and pad with T = 0 (rows up to a
  * multiple of 16, columns up to a whole k-block).  Rows are grouped in tiles
  * of 16.  Inside a tile, 16-byte chunks are ordered by k-block, then by row:
  * the chunk of row n and k-block kb starts at byte
@@ -98,6 +99,11 @@ int bitlinear_version(void);
  *       holds weights kb*80 + 16t + i (t = 0..4) as sum_t c_t * 3^(4-t)
  *       (t = 0 most significant), so base-3 digit t of the 16 bytes covers 16
  *       consecutive weights; values 243..255 never occur.
+ *   B1: binary weights T in {-1, +1} only.  A k-block is 128 weights,
+ *       KB = ceil(K / 128).  Word d (0..3) of a chunk holds weights
+ *       kb*128 + 32d + 4s + j (s in 0..7, j in 0..3) at bit 8j+s: 1 for +1,
+ *       0 for -1.  Padding bits are 0 (a weight of -1 that the product meets
+ *       with zero activations).
  * Returns the byte size of P, or -1 if N, K or layout is invalid.
  */
 int64_t bitlinear_packed_bytes(int64_t N, int64_t K, int layout);
@@ -114,9 +120,10 @@ int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int l
 
 /*
  * The product algorithm bitlinear_forward (algo AUTO) runs for these sizes:
- * BITLINEAR_ALGO_GEMV_MFMA for pre-tiled input, for M <= 16 and for the b3
- * layout, and for larger M when the GEMM would launch too few workgroup tiles
- * to fill the GPU; BITLINEAR_ALGO_GEMM_MFMA otherwise.  Returns -1 for invalid
+ * BITLINEAR_ALGO_GEMV_MFMA for pre-tiled input, for M <= 16, and for larger
+ * M when the GEMM would launch too few workgroup tiles to fill the GPU;
+ * BITLINEAR_ALGO_GEMM_MFMA otherwise (b3 and b1 weights are first rewritten
+ * as i2 in the workspace).  Returns -1 for invalid
  * sizes, layout or dtype.  Host-only; enqueues nothing.
  */
 int bitlinear_auto_algo(int64_t M, int64_t N, int64_t K, int layout, int x_dtype);
@@ -144,10 +151,21 @@ int bitlinear_quantize_weights(const float *W, int64_t N, int64_t K, int64_t ldw
                                float *gamma, void *ws, int64_t ws_bytes, void *stream);
 
 /*
+ * Binary weights of the original BitNet, the predecessor the 1.58-bit method
+ * extends with a zero state (LIT-380 Key takeaways bullet 2; HackerPapers
+ * digest).  Arguments, workspace and gamma as bitlinear_quantize_weights;
+ * T[n][k] = +1 where W[n][k] >= 0 (also -0), else -1.  Pack T with
+ * BITLINEAR_LAYOUT_B1 (or I2 / B3, which hold any ternary values).
+ */
+int bitlinear_binarize_weights(const float *W, int64_t N, int64_t K, int64_t ldw, int8_t *T,
+                               float *gamma, void *ws, int64_t ws_bytes, void *stream);
+
+/*
  * Pack ternary weights T int8 [N x K] (row stride ldt >= K, values in
  * {-1, 0, +1}) into P (bitlinear_packed_bytes(N, K, layout) bytes, 16-byte
  * aligned).  Every byte of P is written, padding included.  Values of T
- * outside {-1, 0, +1} are outside the contract.
+ * outside {-1, 0, +1} are outside the contract, and so is T = 0 for
+ * BITLINEAR_LAYOUT_B1 (it is packed as -1).
  */
 int bitlinear_pack(const int8_t *T, int64_t N, int64_t K, int64_t ldt, int layout, uint8_t *P,
                    void *stream);
@@ -166,8 +184,9 @@ int bitlinear_quantize_act(const void *X, int x_dtype, int64_t M, int64_t K, int
 /*
  * Tiled activation layout (this library's convention): the int8 activations
  * as the operands of the matrix-core product, 1 KiB per operand.  With
- * S = 256 weights per k-step for I2 (320 for B3), F = 4 operands per k-step
- * for I2 (5 for B3), nsteps = ceil(K / S) and G = ceil(M / 16) token groups,
+ * S = 256 weights per k-step for I2 (320 for B3, 512 for B1), F = 4 operands
+ * per k-step for I2 (5 for B3, 8 for B1), nsteps = ceil(K / S) and
+ * G = ceil(M / 16) token groups,
  * q[m][k] with m = 16*tg + i, k = s*S + g*(S/4) + 16*d + e (g in 0..3,
  * d in 0..F-1, e in 0..15) is stored at byte
  *     (((tg * nsteps + s) * F + d) * 64 + g * 16 + i) * 16 + e

@@ -47,7 +47,7 @@ if len(_hip_runtimes_loaded()) > 1:
 # --- enums (bitlinear.h) ---------------------------------------------------
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_DEVICE = range(6)
 F32, BF16, I8, I32, I8_TILED = range(5)
-LAYOUT_I2, LAYOUT_B3 = 0, 1
+LAYOUT_I2, LAYOUT_B3, LAYOUT_B1 = 0, 1, 2
 ALGO_AUTO, ALGO_GEMV_ADDSUB, ALGO_GEMV_MFMA, ALGO_GEMM_MFMA = range(4)
 MAX_K = 131072
 MAX_M = 65536
@@ -67,6 +67,7 @@ _SIGNATURES = {
     "bitlinear_product_kernel": ([_I64, _I64, _I64, _INT, _INT, _INT], ctypes.c_char_p),
     "bitlinear_quantize_act_tiled": ([_P, _INT, _I64, _I64, _I64, _INT, _P, _I64, _P, _P], _INT),
     "bitlinear_quantize_weights": ([_P, _I64, _I64, _I64, _P, _P, _P, _I64, _P], _INT),
+    "bitlinear_binarize_weights": ([_P, _I64, _I64, _I64, _P, _P, _P, _I64, _P], _INT),
     "bitlinear_pack": ([_P, _I64, _I64, _I64, _INT, _P, _P], _INT),
     "bitlinear_quantize_act": ([_P, _INT, _I64, _I64, _I64, _P, _I64, _P, _P], _INT),
     "bitlinear_forward": ([_P, _INT, _P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P, _INT, _I64, _P, _I64, _P], _INT),
@@ -134,6 +135,10 @@ def bitlinear_quantize_weights(W, N, K, ldw, T, gamma, ws, ws_bytes, stream) -> 
     return _lib.bitlinear_quantize_weights(W, N, K, ldw, T, gamma, ws, ws_bytes, stream)
 
 
+def bitlinear_binarize_weights(W, N, K, ldw, T, gamma, ws, ws_bytes, stream) -> int:
+    return _lib.bitlinear_binarize_weights(W, N, K, ldw, T, gamma, ws, ws_bytes, stream)
+
+
 def bitlinear_pack(T, N, K, ldt, layout, P, stream) -> int:
     return _lib.bitlinear_pack(T, N, K, ldt, layout, P, stream)
 
@@ -175,19 +180,27 @@ def _ptr(t) -> int | None:
     return None if t is None else int(t.data_ptr())
 
 
-def quantize_weights(W, stream=None):
-    """Latent fp32 W [N x K] (cuda) -> (T int8 [N x K], gamma fp32 [1])."""
+def _weight_quant(entry, W, stream):
     torch = _torch()
     N, K = W.shape
     T = torch.empty((N, K), dtype=torch.int8, device=W.device)
     gamma = torch.empty(1, dtype=torch.float32, device=W.device)
     nws = bitlinear_quantize_weights_workspace_bytes(N, K)
     if nws < 0:
-        raise BitlinearError(ERR_INVALID_ARG, "quantize_weights")
+        raise BitlinearError(ERR_INVALID_ARG, entry.__name__)
     ws = torch.empty(nws, dtype=torch.uint8, device=W.device)
-    _check(bitlinear_quantize_weights(_ptr(W), N, K, W.stride(0), _ptr(T), _ptr(gamma), _ptr(ws), nws,
-                                      _stream(stream)), "bitlinear_quantize_weights")
+    _check(entry(_ptr(W), N, K, W.stride(0), _ptr(T), _ptr(gamma), _ptr(ws), nws, _stream(stream)), entry.__name__)
     return T, gamma
+
+
+def quantize_weights(W, stream=None):
+    """Latent fp32 W [N x K] (cuda) -> ternary (T int8 [N x K], gamma fp32 [1])."""
+    return _weight_quant(bitlinear_quantize_weights, W, stream)
+
+
+def binarize_weights(W, stream=None):
+    """Latent fp32 W [N x K] (cuda) -> binary (T int8 [N x K] in {-1, +1}, gamma fp32 [1])."""
+    return _weight_quant(bitlinear_binarize_weights, W, stream)
 
 
 def pack(T, layout: int = LAYOUT_I2, stream=None):

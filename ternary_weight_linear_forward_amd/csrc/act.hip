@@ -165,7 +165,8 @@ __global__ __launch_bounds__(256) void k_quant_act_tiled(const void *__restrict_
     constexpr int ES = XDT == DT_F32 ? 4 : 2;
     __shared__ float red[16];
     const int64_t m = blockIdx.x;
-    const int64_t step_k = layout == LAYOUT_I2 ? 256 : 320, kblk = step_k / 4, nmf = layout == LAYOUT_I2 ? 4 : 5;
+    const int64_t step_k = layout == LAYOUT_I2 ? 256 : (layout == LAYOUT_B3 ? 320 : 512), kblk = step_k / 4;
+    const int64_t nmf = layout == LAYOUT_I2 ? 4 : (layout == LAYOUT_B3 ? 5 : 8);
     const int64_t npieces = nsteps * step_k / 16;
     const int64_t tg = m / 16, i = m % 16;
     const bool live_row = m < M;

@@ -54,7 +54,10 @@ bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
 
 int status_of(hipError_t e) { return e == hipSuccess ? BITLINEAR_OK : BITLINEAR_ERR_LAUNCH; }
 
-bool valid_layout(int layout) { return layout == BITLINEAR_LAYOUT_I2 || layout == BITLINEAR_LAYOUT_B3; }
+bool valid_layout(int layout)
+{
+    return layout == BITLINEAR_LAYOUT_I2 || layout == BITLINEAR_LAYOUT_B3 || layout == BITLINEAR_LAYOUT_B1;
+}
 
 // Staged activations of the fused quantiser: row-major Xq [M x round_up(K, 64)]
 // or the tiled layout, whichever is larger, then beta [M].
@@ -78,7 +81,7 @@ int64_t staging_bytes(int64_t M, int64_t K, int layout, int x_dtype)
 }
 int64_t transcode_bytes(int64_t M, int64_t N, int64_t K, int layout)
 {
-    return layout == BITLINEAR_LAYOUT_B3 && M > 16 ? round_up(bitlinear_packed_bytes(N, K, BITLINEAR_LAYOUT_I2), 256)
+    return layout != BITLINEAR_LAYOUT_I2 && M > 16 ? round_up(bitlinear_packed_bytes(N, K, BITLINEAR_LAYOUT_I2), 256)
                                                    : 0;
 }
 
@@ -115,7 +118,9 @@ int64_t bitlinear_packed_bytes(int64_t N, int64_t K, int layout)
 {
     if (N < 1 || K < 1 || K > BITLINEAR_MAX_K || N > kMaxElems || !valid_layout(layout)) return -1;
     const int64_t NT = (N + 15) / 16;
-    const int64_t KB = layout == BITLINEAR_LAYOUT_I2 ? (K + 63) / 64 : (K + 79) / 80;
+    const int64_t KB = layout == BITLINEAR_LAYOUT_I2 ? (K + 63) / 64
+                       : layout == BITLINEAR_LAYOUT_B3 ? (K + 79) / 80
+                                                       : (K + 127) / 128;
     return NT * KB * 256;
 }
 
@@ -176,8 +181,9 @@ int64_t bitlinear_act_tiled_bytes(int64_t M, int64_t K, int layout)
     return bl::tiled_bytes(M, K, layout);
 }
 
-int bitlinear_quantize_weights(const float *W, int64_t N, int64_t K, int64_t ldw, int8_t *T, float *gamma,
-                               void *ws, int64_t ws_bytes, void *stream)
+// Shared argument checks of the two weight quantisers.
+static int check_weight_quant(const float *W, int64_t N, int64_t K, int64_t ldw, const int8_t *T,
+                              const float *gamma, const void *ws, int64_t ws_bytes)
 {
     if (!W || !T || !gamma) return BITLINEAR_ERR_INVALID_ARG;
     if (N < 1 || K < 1 || ldw < K || N > kMaxElems / K) return BITLINEAR_ERR_INVALID_ARG;
@@ -190,6 +196,23 @@ int bitlinear_quantize_weights(const float *W, int64_t N, int64_t K, int64_t ldw
     if (overlap(sw, st) || overlap(sw, sg) || overlap(st, sg) || overlap(sws, sw) || overlap(sws, st) ||
         overlap(sws, sg))
         return BITLINEAR_ERR_INVALID_ARG;
+    return BITLINEAR_OK;
+}
+
+int bitlinear_binarize_weights(const float *W, int64_t N, int64_t K, int64_t ldw, int8_t *T, float *gamma,
+                               void *ws, int64_t ws_bytes, void *stream)
+{
+    const int st = check_weight_quant(W, N, K, ldw, T, gamma, ws, ws_bytes);
+    if (st != BITLINEAR_OK) return st;
+    (void)hipGetLastError();
+    return status_of(bl::launch_binarize_weights(W, N, K, ldw, T, gamma, ws, as_stream(stream)));
+}
+
+int bitlinear_quantize_weights(const float *W, int64_t N, int64_t K, int64_t ldw, int8_t *T, float *gamma,
+                               void *ws, int64_t ws_bytes, void *stream)
+{
+    const int st = check_weight_quant(W, N, K, ldw, T, gamma, ws, ws_bytes);
+    if (st != BITLINEAR_OK) return st;
     (void)hipGetLastError();
     return status_of(bl::launch_quantize_weights(W, N, K, ldw, T, gamma, ws, as_stream(stream)));
 }
@@ -332,10 +355,10 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
     case BITLINEAR_ALGO_GEMV_ADDSUB: e = bl::launch_gemv_addsub(a, st); break;
     case BITLINEAR_ALGO_GEMV_MFMA: e = bl::launch_gemv_mfma(a, st); break;
     default:
-        if (layout == BITLINEAR_LAYOUT_B3) {
-            // the GEMM reads i2: rewrite the base-3 weights into the workspace first
+        if (layout != BITLINEAR_LAYOUT_I2) {
+            // the GEMM reads i2: rewrite the b3 / b1 weights into the workspace first
             uint8_t *p2 = static_cast<uint8_t *>(ws) + staging_bytes(M, K, layout, x_dtype);
-            e = bl::launch_b3_to_i2(P, N, K, p2, st);
+            e = layout == BITLINEAR_LAYOUT_B3 ? bl::launch_b3_to_i2(P, N, K, p2, st) : bl::launch_b1_to_i2(P, N, K, p2, st);
             if (e != hipSuccess) return BITLINEAR_ERR_LAUNCH;
             a.P = p2;
             a.layout = BITLINEAR_LAYOUT_I2;

@@ -10,7 +10,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 // dtype / layout codes of the C ABI (bitlinear.h).
 enum { DT_F32 = 0, DT_BF16 = 1, DT_I8 = 2, DT_I32 = 3 };
-enum { LAYOUT_I2 = 0, LAYOUT_B3 = 1 };
+enum { LAYOUT_I2 = 0, LAYOUT_B3 = 1, LAYOUT_B1 = 2 };
 
 // A chunk is 16 bytes: one row's weights for one k-block; a tile is 16 rows.
 constexpr int TILE_ROWS = 16;

@@ -98,6 +98,22 @@ template <>
 struct StepShape<LAYOUT_B3> {
     static constexpr int NMF = 5, KBLK = 80;
 };
+template <>
+struct StepShape<LAYOUT_B1> {
+    static constexpr int NMF = 8, KBLK = 128;
+};
+
+// Signed weights of half h of a b1 word (16 binary weights 16h .. 16h+15 of
+// the word's 32, natural k order): (w >> (4h + s)) & 0x01010101 holds the bits
+// of weights 16h + 4s .. +3 as bytes, and v_perm_b32 maps 0 -> -1, 1 -> +1.
+__device__ __forceinline__ v4i b1_half_signed(uint32_t w, int h)
+{
+    v4i r;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        r[s] = static_cast<int>(__builtin_amdgcn_perm(0u, 0x000001ffu, (w >> (4 * h + s)) & 0x01010101u));
+    return r;
+}
 
 // One k-step of TW tiles: unpack the weight chunks and accumulate.
 template <int LAYOUT, int TW, int NMF>
@@ -110,6 +126,11 @@ __device__ __forceinline__ void gemv_step(const uint4 (&b)[TW], const v4i (&a)[N
 #pragma unroll
             for (int d = 0; d < 4; ++d)
                 acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d], i2_word_signed(wd[d]), acc[t], 0, 0, 0);
+        } else if constexpr (LAYOUT == LAYOUT_B1) {
+#pragma unroll
+            for (int d = 0; d < 8; ++d)
+                acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d], b1_half_signed(wd[d / 2], d % 2), acc[t], 0, 0,
+                                                               0);
         } else {
             B3Digits dg[4];
 #pragma unroll
@@ -145,8 +166,10 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
     // activations are zero-padded, so every k-step runs unchecked: a weight
     // chunk past the last k-block (address clamped) meets zero activations.
     const int64_t nfull = TILED ? nsteps : K / STEP_K;
-    const uint4 zero_chunk = LAYOUT == LAYOUT_I2 ? make_uint4(I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD)
-                                                 : make_uint4(0x79797979u, 0x79797979u, 0x79797979u, 0x79797979u);
+    // (b1 has no zero weight: its past-the-end chunk meets zero activations)
+    const uint4 zero_chunk = LAYOUT == LAYOUT_I2   ? make_uint4(I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD)
+                             : LAYOUT == LAYOUT_B3 ? make_uint4(0x79797979u, 0x79797979u, 0x79797979u, 0x79797979u)
+                                                   : make_uint4(0u, 0u, 0u, 0u);
     // Tokens past M and tiles past NT read valid rows (clamped); their results are never stored.
     const int64_t m_a = static_cast<int64_t>(blockIdx.y) * 16 + i;
     const int8_t *xrow = TILED ? Xq + (static_cast<int64_t>(blockIdx.y) * nsteps * NMF * 64 + lane) * 16
@@ -553,7 +576,7 @@ struct GemvPlan {
 static GemvPlan gemv_plan(int layout, int64_t M, int64_t N, int64_t K)
 {
     const int64_t NT = (N + 15) / 16;
-    const int64_t KB = layout == LAYOUT_I2 ? (K + 63) / 64 : (K + 79) / 80;
+    const int64_t KB = layout == LAYOUT_I2 ? (K + 63) / 64 : (layout == LAYOUT_B3 ? (K + 79) / 80 : (K + 127) / 128);
     const int64_t nsteps = (KB + 3) / 4;
     const int64_t tgroups = (M + 15) / 16;
     GemvPlan p{false, 0, 0, false, 0, 0, 1};
@@ -607,7 +630,7 @@ template <int LAYOUT>
 static void launch_mfma_layout(const GemvArgs &a, hipStream_t stream)
 {
     const int64_t NT = (a.N + 15) / 16;
-    const int64_t KB = LAYOUT == LAYOUT_I2 ? (a.K + 63) / 64 : (a.K + 79) / 80;
+    const int64_t KB = (a.K + StepShape<LAYOUT>::KBLK - 1) / StepShape<LAYOUT>::KBLK;
     const int64_t nsteps = (KB + 3) / 4;
     const GemvPlan p = gemv_plan(LAYOUT, a.M, a.N, a.K);
     if (p.persist) {
@@ -640,8 +663,10 @@ hipError_t launch_gemv_mfma(const GemvArgs &a, hipStream_t stream)
 {
     if (a.layout == LAYOUT_I2)
         launch_mfma_layout<LAYOUT_I2>(a, stream);
-    else
+    else if (a.layout == LAYOUT_B3)
         launch_mfma_layout<LAYOUT_B3>(a, stream);
+    else
+        launch_mfma_layout<LAYOUT_B1>(a, stream);
     return hipGetLastError();
 }
 

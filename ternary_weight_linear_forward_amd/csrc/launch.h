@@ -16,13 +16,20 @@ hipError_t launch_pack(const int8_t *T, int64_t N, int64_t K, int64_t ldt, int l
 
 // Rewrite b3-packed weights P3 [N x K] in the i2 layout (P2, i2 packed size).
 hipError_t launch_b3_to_i2(const uint8_t *P3, int64_t N, int64_t K, uint8_t *P2, hipStream_t stream);
+// Rewrite b1-packed (binary) weights P1 [N x K] in the i2 layout; positions
+// past K become T = 0.
+hipError_t launch_b1_to_i2(const uint8_t *P1, int64_t N, int64_t K, uint8_t *P2, hipStream_t stream);
+// Binary weights: gamma = mean|W| as for the ternary path, T = +1 where
+// w >= 0, else -1.
+hipError_t launch_binarize_weights(const float *W, int64_t N, int64_t K, int64_t ldw, int8_t *T, float *gamma,
+                                   void *ws, hipStream_t stream);
 
 hipError_t launch_quant_act(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int8_t *Xq,
                             int64_t ldq, float *beta, hipStream_t stream);
 
 // Tiled activation layout: see bitlinear_act_tiled_bytes in bitlinear.h.
-inline int64_t tiled_step_k(int layout) { return layout == 0 ? 256 : 320; }
-inline int64_t tiled_nmf(int layout) { return layout == 0 ? 4 : 5; }
+inline int64_t tiled_step_k(int layout) { return layout == 0 ? 256 : (layout == 1 ? 320 : 512); }
+inline int64_t tiled_nmf(int layout) { return layout == 0 ? 4 : (layout == 1 ? 5 : 8); }
 inline int64_t tiled_nsteps(int64_t K, int layout) { return (K + tiled_step_k(layout) - 1) / tiled_step_k(layout); }
 inline int64_t tiled_bytes(int64_t M, int64_t K, int layout)
 {

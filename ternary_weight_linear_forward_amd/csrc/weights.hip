@@ -155,6 +155,17 @@ __global__ __launch_bounds__(256) void k_ternarize(const float *__restrict__ W, 
     }
 }
 
+// Binary weights (the predecessor variant, weights -1 or +1): T = +1 where
+// w >= 0 (including -0), -1 where w < 0.
+__global__ __launch_bounds__(256) void k_binarize(const float *__restrict__ W, int64_t N, int64_t K, int64_t ldw,
+                                                  int8_t *__restrict__ T)
+{
+    for (int64_t n = blockIdx.y; n < N; n += gridDim.y)
+        for (int64_t k = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; k < K;
+             k += static_cast<int64_t>(gridDim.x) * 256)
+            T[n * K + k] = W[n * ldw + k] >= 0.0f ? 1 : -1;
+}
+
 // i2 packing: one thread per (row n, k-block kb) writes one 16-byte chunk.
 // Consecutive threads write consecutive chunks of a tile.
 __global__ __launch_bounds__(256) void k_pack_i2(const int8_t *__restrict__ T, int64_t N, int64_t K,
@@ -252,10 +263,78 @@ hipError_t launch_b3_to_i2(const uint8_t *P3, int64_t N, int64_t K, uint8_t *P2,
     return hipGetLastError();
 }
 
+// b1 packing: one thread per (row n, 128-weight block kb); word d holds
+// weights kb*128 + 32d + 4s + j at bit 8j + s (1 for T > 0, else 0); bits
+// past K or N are 0.
+__global__ __launch_bounds__(256) void k_pack_b1(const int8_t *__restrict__ T, int64_t N, int64_t K,
+                                                 int64_t ldt, int64_t KB, int64_t nchunks,
+                                                 uint8_t *__restrict__ P)
+{
+    int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= nchunks) return;
+    int64_t tile = idx / (KB * 16);
+    int64_t rem = idx % (KB * 16);
+    int64_t kb = rem / 16, r = rem % 16;
+    int64_t n = tile * 16 + r;
+    uint32_t word[4];
+    for (int d = 0; d < 4; ++d) {
+        uint32_t w = 0;
+        for (int s = 0; s < 8; ++s)
+            for (int j = 0; j < 4; ++j) {
+                int64_t k = kb * 128 + 32 * d + 4 * s + j;
+                if (n < N && k < K && T[n * ldt + k] > 0) w |= 1u << (8 * j + s);
+            }
+        word[d] = w;
+    }
+    *reinterpret_cast<uint4 *>(P + idx * 16) = make_uint4(word[0], word[1], word[2], word[3]);
+}
+
+// b1 -> i2 transcode (for the GEMM): one thread per i2 word, 16 weights
+// k0 .. k0+15 (k0 = 64 kb2 + 16 d).  They are half h = (k0 % 32) / 16 of b1
+// word q = (k0 % 128) / 32 of block k0 / 128: weight 4s + j of the i2 word is
+// bit 8j + 4h + s of that b1 word, and its code is 2 (T = +1) or 0 (T = -1).
+// Positions at or past K become code 1 (T = 0): binary padding carries a
+// weight, i2 padding must not.
+__global__ __launch_bounds__(256) void k_b1_to_i2(const uint8_t *__restrict__ P1, int64_t KB1, int64_t KB2,
+                                                  int64_t K, int64_t nwords, uint8_t *__restrict__ P2)
+{
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; // ((tile*KB2 + kb2)*16 + r)*4 + d
+    if (idx >= nwords) return;
+    const int d = static_cast<int>(idx & 3);
+    const int64_t chunk = idx >> 2, r = chunk & 15, tk = chunk >> 4;
+    const int64_t tile = tk / KB2, kb2 = tk - tile * KB2;
+    const int64_t k0 = kb2 * 64 + 16 * d;
+    const int64_t kb1 = k0 >> 7;
+    const int q = static_cast<int>((k0 >> 5) & 3), h = static_cast<int>((k0 >> 4) & 1);
+    const uint32_t w = reinterpret_cast<const uint32_t *>(P1)[((tile * KB1 + kb1) * 16 + r) * 4 + q];
+    uint32_t out = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) out |= ((w >> (4 * h + s)) & 0x01010101u) << (2 * s + 1); // code 2 or 0
+    if (k0 + 16 > K) { // the block straddles K: positions past it become T = 0 (code 1)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            if (k0 + e >= K) {
+                const int sh = 8 * (e % 4) + 2 * (e / 4);
+                out = (out & ~(3u << sh)) | (1u << sh);
+            }
+    }
+    reinterpret_cast<uint32_t *>(P2)[idx] = out;
+}
+
+hipError_t launch_b1_to_i2(const uint8_t *P1, int64_t N, int64_t K, uint8_t *P2, hipStream_t stream)
+{
+    const int64_t NT = (N + 15) / 16, KB1 = (K + 127) / 128, KB2 = (K + 63) / 64;
+    const int64_t nwords = NT * KB2 * 16 * 4;
+    hipLaunchKernelGGL(k_b1_to_i2, dim3(static_cast<unsigned>((nwords + 255) / 256)), dim3(256), 0, stream, P1, KB1,
+                       KB2, K, nwords, P2);
+    return hipGetLastError();
+}
+
 static unsigned grid_rows(int64_t N) { return static_cast<unsigned>(N < 65535 ? N : 65535); }
 
-hipError_t launch_quantize_weights(const float *W, int64_t N, int64_t K, int64_t ldw, int8_t *T, float *gamma,
-                                   void *ws, hipStream_t stream)
+// gamma = mean|W| (exact, one rounding): bucket sums, then one wave finishes.
+static void launch_absmean(const float *W, int64_t N, int64_t K, int64_t ldw, float *gamma, void *ws,
+                           hipStream_t stream)
 {
     unsigned long long *buckets = static_cast<unsigned long long *>(ws);
     hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(256), 0, stream, buckets, 256);
@@ -266,9 +345,27 @@ hipError_t launch_quantize_weights(const float *W, int64_t N, int64_t K, int64_t
     unsigned gy = static_cast<unsigned>(N < want_rows ? N : want_rows);
     hipLaunchKernelGGL(k_abs_buckets, dim3(gx, gy), dim3(256), 0, stream, W, N, K, ldw, buckets);
     hipLaunchKernelGGL(k_gamma_finalize, dim3(1), dim3(64), 0, stream, buckets, N * K, gamma);
+}
+
+static dim3 elementwise_grid(int64_t N, int64_t K)
+{
     int64_t kb = (K + 255) / 256;
-    unsigned tx = static_cast<unsigned>(kb < 1024 ? kb : 1024);
-    hipLaunchKernelGGL(k_ternarize, dim3(tx, grid_rows(N)), dim3(256), 0, stream, W, N, K, ldw, gamma, T);
+    return dim3(static_cast<unsigned>(kb < 1024 ? kb : 1024), grid_rows(N));
+}
+
+hipError_t launch_quantize_weights(const float *W, int64_t N, int64_t K, int64_t ldw, int8_t *T, float *gamma,
+                                   void *ws, hipStream_t stream)
+{
+    launch_absmean(W, N, K, ldw, gamma, ws, stream);
+    hipLaunchKernelGGL(k_ternarize, elementwise_grid(N, K), dim3(256), 0, stream, W, N, K, ldw, gamma, T);
+    return hipGetLastError();
+}
+
+hipError_t launch_binarize_weights(const float *W, int64_t N, int64_t K, int64_t ldw, int8_t *T, float *gamma,
+                                   void *ws, hipStream_t stream)
+{
+    launch_absmean(W, N, K, ldw, gamma, ws, stream);
+    hipLaunchKernelGGL(k_binarize, elementwise_grid(N, K), dim3(256), 0, stream, W, N, K, ldw, T);
     return hipGetLastError();
 }
 
@@ -276,13 +373,15 @@ hipError_t launch_pack(const int8_t *T, int64_t N, int64_t K, int64_t ldt, int l
                        hipStream_t stream)
 {
     int64_t NT = (N + 15) / 16;
-    int64_t KB = layout == LAYOUT_I2 ? (K + 63) / 64 : (K + 79) / 80;
+    int64_t KB = layout == LAYOUT_I2 ? (K + 63) / 64 : (layout == LAYOUT_B3 ? (K + 79) / 80 : (K + 127) / 128);
     int64_t nchunks = NT * KB * 16;
     unsigned blocks = static_cast<unsigned>((nchunks + 255) / 256);
     if (layout == LAYOUT_I2)
         hipLaunchKernelGGL(k_pack_i2, dim3(blocks), dim3(256), 0, stream, T, N, K, ldt, KB, nchunks, P);
-    else
+    else if (layout == LAYOUT_B3)
         hipLaunchKernelGGL(k_pack_b3, dim3(blocks), dim3(256), 0, stream, T, N, K, ldt, KB, nchunks, P);
+    else
+        hipLaunchKernelGGL(k_pack_b1, dim3(blocks), dim3(256), 0, stream, T, N, K, ldt, KB, nchunks, P);
     return hipGetLastError();
 }
 

@@ -60,6 +60,11 @@ def ternary_weights(N: int, K: int, seed: int, p_zero: float = 0.31) -> np.ndarr
     return t.astype(np.int8)
 
 
+def binary_weights(N: int, K: int, seed: int) -> np.ndarray:
+    """Random binary T[N x K] in {-1, +1}, equally likely."""
+    return np.where(rng(seed).random((N, K)) < 0.5, -1, 1).astype(np.int8)
+
+
 def int8_activations(M: int, K: int, seed: int) -> np.ndarray:
     """Random int8 activations in [-127, 127]."""
     return rng(seed).integers(-127, 128, size=(M, K), dtype=np.int16).astype(np.int8)

@@ -44,6 +44,8 @@ def test_size_queries():
     assert bl.bitlinear_packed_bytes(3200, 3200, bl.LAYOUT_I2) == 3200 * 3200 // 4
     assert bl.bitlinear_packed_bytes(28672, 8192, bl.LAYOUT_B3) == 28672 * 103 * 16
     assert bl.bitlinear_packed_bytes(17, 65, bl.LAYOUT_I2) == 2 * 2 * 256
+    assert bl.bitlinear_packed_bytes(3200, 3200, bl.LAYOUT_B1) == 3200 * 25 * 16
+    assert bl.bitlinear_packed_bytes(17, 129, bl.LAYOUT_B1) == 2 * 2 * 256
     assert bl.bitlinear_packed_bytes(0, 4, bl.LAYOUT_I2) == -1
     assert bl.bitlinear_packed_bytes(4, bl.MAX_K + 1, bl.LAYOUT_I2) == -1
     assert bl.bitlinear_packed_bytes(4, 4, 7) == -1
@@ -73,6 +75,16 @@ def test_quantize_weights_rejects(kw, status):
     assert qw(**kw) == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), bl.ERR_INVALID_ARG), (dict(N=0), bl.ERR_INVALID_ARG), (dict(ldw=63), bl.ERR_INVALID_ARG),
+    (dict(ws_bytes=2047), bl.ERR_WORKSPACE), (dict(T=A + 64), bl.ERR_INVALID_ARG),
+])
+def test_binarize_weights_rejects(kw, status):
+    a = dict(W=A, N=64, K=64, ldw=64, T=B, gamma=C, ws=D, ws_bytes=2048, stream=None)
+    a.update(kw)
+    assert bl.bitlinear_binarize_weights(**a) == status
+
+
 def pk(**kw):
     a = dict(T=A, N=64, K=64, ldt=64, layout=bl.LAYOUT_I2, P=B, stream=None)
     a.update(kw)
@@ -80,7 +92,7 @@ def pk(**kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(T=None), dict(P=None), dict(layout=2), dict(N=0), dict(K=0), dict(K=bl.MAX_K + 1, ldt=bl.MAX_K + 1),
+    dict(T=None), dict(P=None), dict(layout=3), dict(layout=-1), dict(N=0), dict(K=0), dict(K=bl.MAX_K + 1, ldt=bl.MAX_K + 1),
     dict(ldt=10), dict(P=B + 4), dict(P=A + 16),
 ])
 def test_pack_rejects(kw):
@@ -197,6 +209,8 @@ def test_auto_algo_dispatch():
         assert f(M, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMV_MFMA
     assert f(2048, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMM_MFMA
     assert f(2048, 3200, 3200, bl.LAYOUT_B3, bl.BF16) == bl.ALGO_GEMM_MFMA  # through an i2 rewrite
+    assert f(2048, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == bl.ALGO_GEMM_MFMA
+    assert f(16, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == bl.ALGO_GEMV_MFMA
     assert f(2048, 3200, 3200, bl.LAYOUT_I2, bl.I8_TILED) == bl.ALGO_GEMV_MFMA
     assert f(176, 1024, 8192, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMV_MFMA  # 16 tiles: GPU mostly idle
     assert f(176, 8192, 8192, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMM_MFMA
@@ -218,6 +232,8 @@ def test_product_kernel_names():
     assert f(2048, 3200, 3200, bl.LAYOUT_I2, bl.BF16).startswith("bl::k_gemm_mfma_i2<")
     assert f(3, 64, 64, bl.LAYOUT_I2, bl.BF16, bl.ALGO_GEMV_ADDSUB) == "bl::k_gemv_addsub<4>"
     assert f(3, 64, 64, bl.LAYOUT_B3, bl.BF16, bl.ALGO_GEMM_MFMA) is None
+    assert f(1, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == "bl::k_gemv_mfma<2, 1, 1, false>"
+    assert f(3, 64, 64, bl.LAYOUT_B1, bl.BF16, bl.ALGO_GEMV_ADDSUB) is None
     assert f(0, 64, 64, bl.LAYOUT_I2, bl.BF16) is None
 
 
@@ -231,3 +247,5 @@ def test_b3_gemm_workspace():
     assert b3 >= base and b3 - bl.bitlinear_forward_workspace_bytes(M, N, K, bl.LAYOUT_B3, bl.I8) < b3
     assert bl.bitlinear_forward_workspace_bytes(M, N, K, bl.LAYOUT_B3, bl.I8) >= i2
     assert bl.bitlinear_forward_workspace_bytes(16, N, K, bl.LAYOUT_B3, bl.I8) == 0
+    assert bl.bitlinear_forward_workspace_bytes(M, N, K, bl.LAYOUT_B1, bl.I8) >= i2
+    assert bl.bitlinear_forward_workspace_bytes(16, N, K, bl.LAYOUT_B1, bl.I8) == 0
