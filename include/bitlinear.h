@@ -96,9 +96,12 @@ int bitlinear_version(void);
  *       at bits 8j+2s .. 8j+2s+1, so (word >> 2s) & 0x03030303 gives the
  *       codes of 4 consecutive weights, one per byte.
  *   B3: a k-block is 80 weights, KB = ceil(K / 80).  Byte i (0..15) of a chunk
- *       holds weights kb*80 + 16t + i (t = 0..4) as sum_t c_t * 3^(4-t)
- *       (t = 0 most significant), so base-3 digit t of the 16 bytes covers 16
- *       consecutive weights; values 243..255 never occur.
+ *       holds weights kb*80 + 16t + i (t = 0..4): with v = sum_t c_t * 3^(4-t)
+ *       (t = 0 most significant), the byte is ceil(256 * v / 243), v / 243 as
+ *       an 8-bit fraction rounded up (v = floor(243 * byte / 256)), so that
+ *       digit t is floor(byte * 3^(t+1) / 256) - 3 * floor(byte * 3^t / 256).
+ *       Base-3 digit t of the 16 bytes covers 16 consecutive weights; 13 of
+ *       the 256 byte values never occur.  Padding (T = 0) is the byte 128.
  *   B1: binary weights T in {-1, +1} only.  A k-block is 128 weights,
  *       KB = ceil(K / 128).  Word d (0..3) of a chunk holds weights
  *       kb*128 + 32d + 4s + j (s in 0..7, j in 0..3) at bit 8j+s: 1 for +1,

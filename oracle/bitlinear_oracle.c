@@ -181,9 +181,12 @@ int oracle_binarize(const float *w, int64_t count, int8_t *t)
  * "b3" (base 3, 5 weights per byte): a k-block is 80 weights.  The chunk of
  * row n and k-block kb starts at byte ((n/16)*KB3 + kb)*256 + (n%16)*16,
  * KB3 = ceil(K/80).  Its byte i (i = 0..15) holds the five weights
- * kb*80 + 16t + i (t = 0..4) as sum_t c_t * 3^(4 - t): weight t = 0 is the
- * most significant base-3 digit.  So digit t of bytes 0..15 covers 16
- * consecutive weights.  Values 243..255 are never written.
+ * kb*80 + 16t + i (t = 0..4) as the base-3 number v = sum_t c_t * 3^(4 - t)
+ * (weight t = 0 the most significant digit), stored as the byte
+ * ceil(256 * v / 243): v / 243 as an 8-bit fixed-point fraction, rounded up.
+ * The map is one-to-one (v = floor(243 * byte / 256) recovers v), so 243 of
+ * the 256 byte values occur.  Digit t of bytes 0..15 covers 16 consecutive
+ * weights.
  *
  * "b1" (1 bit per weight, binary weights only): a k-block is 128 weights.  The
  * chunk of row n and k-block kb starts at byte ((n/16)*KB1 + kb)*256 +
@@ -254,7 +257,7 @@ int oracle_pack_b3(const int8_t *t, int64_t N, int64_t K, uint8_t *p)
                     if (v < -1 || v > 1) return ORACLE_ERR_ARG;
                     byte = byte * 3 + (unsigned)(v + 1);
                 }
-                chunk[i] = (uint8_t)byte;
+                chunk[i] = (uint8_t)((256 * byte + 242) / 243); /* ceil(256 v / 243) */
             }
         }
     return ORACLE_OK;
@@ -267,8 +270,9 @@ int oracle_unpack_b3(const uint8_t *p, int64_t N, int64_t K, int8_t *t)
         for (int64_t k = 0; k < K; ++k) {
             int64_t kb = k / 80, r = k % 80;
             unsigned byte = p[((n / 16) * KB + kb) * 256 + (n % 16) * 16 + r % 16];
-            if (byte > 242) return ORACLE_ERR_CODE;
-            unsigned digit = byte;
+            unsigned v = (243 * byte) / 256;
+            if ((256 * v + 242) / 243 != byte) return ORACLE_ERR_CODE; /* not a b3 byte */
+            unsigned digit = v;
             for (int d = 4; d > (int)(r / 16); --d) digit /= 3;
             t[n * K + k] = (int8_t)((int)(digit % 3) - 1);
         }

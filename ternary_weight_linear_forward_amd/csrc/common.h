@@ -19,8 +19,6 @@ constexpr int I2_KBLOCK = 64;
 constexpr int B3_KBLOCK = 80;
 // Word of four "T = 0" codes (c = 1 in every 2-bit field): padding for i2.
 constexpr uint32_t I2_ZERO_WORD = 0x55555555u;
-// Byte of five "T = 0" codes in base 3: 1*81 + 1*27 + 1*9 + 1*3 + 1.
-constexpr uint32_t B3_ZERO_BYTE = 121u;
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b)
 {
@@ -101,10 +99,7 @@ __device__ __forceinline__ void store_out(void *Y, int y_dtype, int64_t ldy, int
     }
 }
 
-// Base-3 digits of bytes b <= 242, two bytes per 16-bit lane: floor(b / 3^(4-t))
-// is (b * m) >> s with (m, s) = (203, 14), (19, 9), (57, 9), (171, 9) for
-// t = 0..3 (exact for every b <= 242, b * m < 2^16); digit t is
-// H_t - 3 H_(t-1), t = 0 the most significant.
+// Lane-wise product of two pairs of 16-bit integers (low 16 bits kept).
 __device__ __forceinline__ uint32_t pk_mul_u16(uint32_t a, uint32_t b)
 {
     typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
@@ -112,34 +107,51 @@ __device__ __forceinline__ uint32_t pk_mul_u16(uint32_t a, uint32_t b)
     return __builtin_bit_cast(uint32_t, static_cast<v2u16>(x * y));
 }
 
-__device__ __forceinline__ uint32_t pk_shr_u16(uint32_t a, int s)
+// Base-3 digits of the four b3 bytes of w.  A b3 byte holds the five-digit
+// base-3 number v (digit 0 most significant) as u = ceil(256 v / 243), the
+// fixed-point fraction v / 243 rounded up.  Then H_t = floor(u 3^t / 256) is
+// the number formed by the leading t digits (an exhaustive check over the 243
+// values confirms it), so digit t is H_{t+1} - 3 H_t.  The products u 3^t fit
+// 16-bit lanes (u 3^5 < 2^16), two bytes per instruction, and their high
+// bytes are gathered into one word per t with v_perm_b32.  Because the result
+// of X_{t+1} - 3 X_t is a whole word of byte digits 0..2, the subtraction is
+// exact on the packed word.  d[t] byte j = digit t of byte j of w.
+struct B3Digits {
+    uint32_t d[5];
+};
+
+__device__ __forceinline__ B3Digits b3_word_digits(uint32_t w)
 {
-    typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
-    v2u16 x = __builtin_bit_cast(v2u16, a);
-    v2u16 sh = {static_cast<unsigned short>(s), static_cast<unsigned short>(s)};
-    return __builtin_bit_cast(uint32_t, static_cast<v2u16>(x >> sh));
+    const uint32_t even = w & 0x00ff00ffu;                         // bytes 0 and 2
+    const uint32_t odd = __builtin_amdgcn_perm(0u, w, 0x0c030c01u); // bytes 1 and 3
+    uint32_t X[6];
+    uint32_t p3 = 1;
+#pragma unroll
+    for (int t = 1; t <= 5; ++t) {
+        p3 *= 3;
+        const uint32_t ze = pk_mul_u16(even, p3 * 0x00010001u), zo = pk_mul_u16(odd, p3 * 0x00010001u);
+        X[t] = __builtin_amdgcn_perm(zo, ze, 0x07030501u); // high byte of each lane, bytes in order
+    }
+    B3Digits r;
+    r.d[0] = X[1];
+#pragma unroll
+    for (int t = 1; t < 5; ++t) {
+        // 3 X_t as one full-rate shift-add: written as a multiply or as
+        // x + (x << 1), the compiler forms a quarter-rate v_mad_u64_u32
+        uint32_t x3;
+        asm("v_lshl_add_u32 %0, %1, 1, %1" : "=v"(x3) : "v"(X[t]));
+        r.d[t] = X[t + 1] - x3;
+    }
+    return r;
 }
 
-__device__ __forceinline__ uint32_t pk_sub_u16(uint32_t a, uint32_t b)
-{
-    typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
-    v2u16 x = __builtin_bit_cast(v2u16, a), y = __builtin_bit_cast(v2u16, b);
-    return __builtin_bit_cast(uint32_t, static_cast<v2u16>(x - y));
-}
+// The b3 byte of five "T = 0" weights: v = 121 (all digits 1), stored as
+// ceil(256 * 121 / 243) = 128; four of them make the padding word.
+constexpr uint32_t B3_ZERO_WORD = 0x80808080u;
 
-// digits of the two bytes held in the 16-bit lanes of 'b' (each <= 242)
-__device__ __forceinline__ void b3_digits_pair(uint32_t b, uint32_t c[5])
-{
-    const uint32_t h0 = pk_shr_u16(pk_mul_u16(b, 0x00cb00cbu), 14); // b / 81
-    const uint32_t h1 = pk_shr_u16(pk_mul_u16(b, 0x00130013u), 9);  // b / 27
-    const uint32_t h2 = pk_shr_u16(pk_mul_u16(b, 0x00390039u), 9);  // b / 9
-    const uint32_t h3 = pk_shr_u16(pk_mul_u16(b, 0x00ab00abu), 9);  // b / 3
-    c[0] = h0;
-    c[1] = pk_sub_u16(h1, pk_mul_u16(h0, 0x00030003u));
-    c[2] = pk_sub_u16(h2, pk_mul_u16(h1, 0x00030003u));
-    c[3] = pk_sub_u16(h3, pk_mul_u16(h2, 0x00030003u));
-    c[4] = pk_sub_u16(b, pk_mul_u16(h3, 0x00030003u));
-}
+// b3 byte of the digits c_0 .. c_4 (c_0 most significant): v = sum c_t 3^(4-t),
+// stored as ceil(256 v / 243).
+__device__ __forceinline__ uint32_t b3_encode(uint32_t v) { return (256u * v + 242u) / 243u; }
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }

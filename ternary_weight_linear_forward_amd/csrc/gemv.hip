@@ -56,23 +56,6 @@ __device__ __forceinline__ v4i i2_word_signed(uint32_t w)
     return r;
 }
 
-// Base-3 digit t (t = 0 most significant) of each byte of a b3 word, as signed
-// bytes digit - 1 (digits from b3_digits_pair, two bytes per 16-bit lane).
-struct B3Digits {
-    uint32_t d[5];
-};
-
-__device__ __forceinline__ B3Digits b3_word_signed(uint32_t w)
-{
-    uint32_t lo[5], hi[5];
-    b3_digits_pair(w & 0x00ff00ffu, lo);        // bytes 0 and 2
-    b3_digits_pair((w >> 8) & 0x00ff00ffu, hi); // bytes 1 and 3
-    B3Digits r;
-#pragma unroll
-    for (int t = 0; t < 5; ++t) r.d[t] = __builtin_amdgcn_perm(0u, 0x000100ffu, lo[t] | (hi[t] << 8));
-    return r;
-}
-
 // ---------------------------------------------------------------------------
 // MFMA GEMV.  A k-step is 4 consecutive k-blocks (i2: 256 weights, b3: 320).
 // In a k-step, lane l (i = l % 16, g = l / 16) holds the 16-byte chunk of row
@@ -115,6 +98,22 @@ __device__ __forceinline__ v4i b1_half_signed(uint32_t w, int h)
     return r;
 }
 
+// Layouts whose k-step multiplies the unsigned codes c = T + 1 (no per-word
+// conversion to signed bytes); the kernel subtracts sum_k q[m][k] once per
+// output, which is the same for every weight row.
+template <int LAYOUT>
+constexpr bool kOffsetCodes = LAYOUT == LAYOUT_B3;
+
+// sacc[m] += sum of the activations of one k-step, in the MFMA output layout
+// (the product with an all-ones B operand; every weight row gets the same sum).
+template <int NMF>
+__device__ __forceinline__ void act_sum_step(const v4i (&a)[NMF], v4i &sacc)
+{
+    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+#pragma unroll
+    for (int d = 0; d < NMF; ++d) sacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d], ones, sacc, 0, 0, 0);
+}
+
 // One k-step of TW tiles: unpack the weight chunks and accumulate.
 template <int LAYOUT, int TW, int NMF>
 __device__ __forceinline__ void gemv_step(const uint4 (&b)[TW], const v4i (&a)[NMF], v4i (&acc)[TW])
@@ -132,9 +131,10 @@ __device__ __forceinline__ void gemv_step(const uint4 (&b)[TW], const v4i (&a)[N
                 acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d], b1_half_signed(wd[d / 2], d % 2), acc[t], 0, 0,
                                                                0);
         } else {
+            // unsigned digits c = T + 1: the caller subtracts sum_k q (act_sum_step)
             B3Digits dg[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) dg[q] = b3_word_signed(wd[q]);
+            for (int q = 0; q < 4; ++q) dg[q] = b3_word_digits(wd[q]);
 #pragma unroll
             for (int d = 0; d < 5; ++d) {
                 v4i bt = {static_cast<int>(dg[0].d[d]), static_cast<int>(dg[1].d[d]), static_cast<int>(dg[2].d[d]),
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
     const int64_t nfull = TILED ? nsteps : K / STEP_K;
     // (b1 has no zero weight: its past-the-end chunk meets zero activations)
     const uint4 zero_chunk = LAYOUT == LAYOUT_I2   ? make_uint4(I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD)
-                             : LAYOUT == LAYOUT_B3 ? make_uint4(0x79797979u, 0x79797979u, 0x79797979u, 0x79797979u)
+                             : LAYOUT == LAYOUT_B3 ? make_uint4(B3_ZERO_WORD, B3_ZERO_WORD, B3_ZERO_WORD, B3_ZERO_WORD)
                                                    : make_uint4(0u, 0u, 0u, 0u);
     // Tokens past M and tiles past NT read valid rows (clamped); their results are never stored.
     const int64_t m_a = static_cast<int64_t>(blockIdx.y) * 16 + i;
@@ -219,8 +219,10 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
     };
     // (SB = 1: the loop below only computes batches that exist)
     static_assert(SB == 1, "one k-step per batch");
+    v4i sacc = {0, 0, 0, 0}; // sum_k q of the wave's k-steps (offset codes only)
     auto compute_batch = [&](int64_t, const uint4 (&b)[SB][TW], const v4i (&a)[SB][NMF]) {
         gemv_step<LAYOUT, TW, NMF>(b[0], a[0], acc);
+        if constexpr (kOffsetCodes<LAYOUT>) act_sum_step<NMF>(a[0], sacc);
     };
     if (wave < nfull) {
         uint4 b0[SB][TW], b1[SB][TW];
@@ -261,10 +263,11 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
 #pragma unroll
         for (int d = 0; d < NMF; ++d) a[d] = load_a16(Xq, ldq, m_a, M, K, kb * KBLK + 16 * d);
         gemv_step<LAYOUT, TW, NMF>(b, a, acc);
+        if constexpr (kOffsetCodes<LAYOUT>) act_sum_step<NMF>(a, sacc);
     }
 
 #pragma unroll
-    for (int t = 0; t < TW; ++t) red[t][wave][lane] = acc[t];
+    for (int t = 0; t < TW; ++t) red[t][wave][lane] = kOffsetCodes<LAYOUT> ? acc[t] - sacc : acc[t];
     __syncthreads();
     // tile t is finished by wave t % KS (KS may be smaller than TW)
     for (int t = wave; t < TW; t += KS) {
@@ -365,6 +368,12 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const uint8_t *__restrict
         }
     }
 
+    v4i sacc = {0, 0, 0, 0}; // sum_k q of the wave's k-steps (offset codes only)
+    if constexpr (kOffsetCodes<LAYOUT>) {
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) act_sum_step<NMF>(a[j], sacc);
+    }
+
 #pragma unroll
     for (int t = 0; t < D; ++t)
         if (!GUARD || t < ntiles) load_tile(t, b[t]);
@@ -386,7 +395,8 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const uint8_t *__restrict
     for (int t = 0; t < TMAX; ++t) {
         if (t >= ntiles) break;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) red[((t * KS + wave) * 4 + rr) * 64 + lane] = acc[t][rr];
+        for (int rr = 0; rr < 4; ++rr)
+            red[((t * KS + wave) * 4 + rr) * 64 + lane] = kOffsetCodes<LAYOUT> ? acc[t][rr] - sacc[rr] : acc[t][rr];
     }
     __syncthreads();
     // output group (t, rr): tokens 4g + rr of this token group, weight row i of tile t

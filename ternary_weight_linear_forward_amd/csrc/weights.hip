@@ -194,7 +194,8 @@ __global__ __launch_bounds__(256) void k_pack_i2(const int8_t *__restrict__ T, i
 }
 
 // b3 packing: one thread per (row n, 80-weight block kb); byte i holds
-// weights 16t + i (t = 0..4) of the block as a base-3 number, t = 0 most significant.
+// weights 16t + i (t = 0..4) of the block as the base-3 number v (t = 0 most
+// significant), stored as ceil(256 v / 243) (see b3_word_digits).
 __global__ __launch_bounds__(256) void k_pack_b3(const int8_t *__restrict__ T, int64_t N, int64_t K,
                                                  int64_t ldt, int64_t KB, int64_t nchunks,
                                                  uint8_t *__restrict__ P)
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(256) void k_pack_b3(const int8_t *__restrict__ T, i
             int v = (n < N && k < K) ? T[n * ldt + k] : 0;
             b = b * 3u + static_cast<uint32_t>(v + 1);
         }
-        word[i / 4] |= b << (8 * (i % 4));
+        word[i / 4] |= b3_encode(b) << (8 * (i % 4));
     }
     *reinterpret_cast<uint4 *>(P + idx * 16) = make_uint4(word[0], word[1], word[2], word[3]);
 }
@@ -238,11 +239,9 @@ __global__ __launch_bounds__(256) void k_b3_to_i2(const uint8_t *__restrict__ P3
     uint32_t out[5] = {0, 0, 0, 0, 0};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        uint32_t lo[5], hi[5];
-        b3_digits_pair(bw[q] & 0x00ff00ffu, lo);        // bytes 0 and 2 of the word
-        b3_digits_pair((bw[q] >> 8) & 0x00ff00ffu, hi); // bytes 1 and 3
+        const B3Digits dg = b3_word_digits(bw[q]); // byte j of dg.d[t]: digit t of byte 4q + j
 #pragma unroll
-        for (int t = 0; t < 5; ++t) out[t] |= (lo[t] | (hi[t] << 8)) << (2 * q);
+        for (int t = 0; t < 5; ++t) out[t] |= dg.d[t] << (2 * q);
     }
     uint32_t *row = reinterpret_cast<uint32_t *>(P2) + tile * KB2 * 64 + r * 4; // word (kb2, d) at kb2 * 64 + d
 #pragma unroll

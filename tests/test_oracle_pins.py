@@ -188,7 +188,8 @@ def test_pack_b3_hand_bytes():
         t[0, [0, 16, 32, 48, 64]] = grp
         p = oracle.pack(t, oracle.LAYOUT_B3)
         assert p[0] == want
-        assert np.all(p[1:16] == 121) and np.all(p[16:] == 121)
+        pad = v["padding_byte"]
+        assert np.all(p[1:16] == pad) and np.all(p[16:] == pad)
 
 
 def test_pack_b3_bijection_over_all_groups():
@@ -205,11 +206,21 @@ def test_pack_b3_bijection_over_all_groups():
     for kb in range(KB):
         codes.extend(p[kb * 256: kb * 256 + 16].tolist())
     codes = codes[:243]
-    assert sorted(codes) == list(range(243))
-    # first trit most significant: decode by plain base-3 expansion
+    assert len(set(codes)) == 243  # one-to-one
+    # The byte is an 8-bit fixed-point fraction whose base-3 expansion is the
+    # group, first trit first: multiplying the fraction by 3 brings each trit
+    # into the integer part (a different route from the packer's division).
     for g, b in zip(groups, codes):
-        digits = [(b // 3 ** (4 - i)) % 3 - 1 for i in range(5)]
+        x, digits = b, []
+        for _ in range(5):
+            x *= 3
+            digits.append(x // 256 - 1)
+            x %= 256
         assert digits == g.tolist()
+    # and the fraction is the group's value over 243, rounded up to 1/256
+    for g, b in zip(groups, codes):
+        value = sum((c + 1) * 3 ** (4 - i) for i, c in enumerate(g.tolist()))
+        assert value / 243 <= b / 256 < value / 243 + 1 / 256
 
 
 @pytest.mark.parametrize("layout", [oracle.LAYOUT_I2, oracle.LAYOUT_B3])
@@ -253,7 +264,7 @@ def test_unpack_rejects_unused_code():
     with pytest.raises(oracle.OracleError):
         oracle.unpack(p, 1, 4, oracle.LAYOUT_I2)
     p = oracle.pack(np.zeros((1, 4), np.int8), oracle.LAYOUT_B3)
-    p[0] = 243
+    p[0] = 1  # ceil(256 v / 243) skips 1 (v = 0 -> 0, v = 1 -> 2)
     with pytest.raises(oracle.OracleError):
         oracle.unpack(p, 1, 4, oracle.LAYOUT_B3)
 
