@@ -242,6 +242,46 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
                            void *Y, int y_dtype, int64_t ldy, void *ws, int64_t ws_bytes, int algo,
                            void *stream);
 
+/*
+ * Backward pass under the straight-through estimator (the pages quote the
+ * BitNet paper: training lets the gradient bypass the non-differentiable
+ * quantisation functions; HackerPapers digest, comment on the
+ * straight-through estimator).  Reading: rounding and clipping have
+ * derivative 1 and gamma, beta_m are constants, so the layer acts like
+ * y = Xhat @ What^T with What = gamma * T and Xhat[m][k] = q[m][k] * r_m,
+ * r_m = beta_m / 127 rounded to binary32.  Gradients are fp32 [row-major],
+ * accumulated in fp32 (order unspecified; the error is within
+ * (n + 2) * 2^-24 of the sum of the absolute terms, n the contraction length).
+ */
+
+/* Workspace bytes bitlinear_backward_dx needs (b3 / b1 weights are rewritten
+ * as i2 first); 0 for i2, -1 if invalid. */
+int64_t bitlinear_backward_dx_workspace_bytes(int64_t N, int64_t K, int layout);
+
+/*
+ * Gradient with respect to the layer input: dX = gamma * (dY @ T).
+ *   P, layout, gamma  the forward's packed weights [N x K] and scale.
+ *   dY    fp32 [M x N], row stride lddy >= N (device, read-only).
+ *   dX    fp32 [M x K], row stride lddx >= K (device, written).
+ *   ws    >= bitlinear_backward_dx_workspace_bytes(N, K, layout) bytes,
+ *         16-byte aligned (may be NULL when that is 0).
+ */
+int bitlinear_backward_dx(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                          const float *dY, int64_t lddy, float *dX, int64_t lddx, void *ws, int64_t ws_bytes,
+                          void *stream);
+
+/*
+ * Gradient with respect to the latent fp32 weights W (the estimator passes
+ * d/dWhat straight to W): dW = dY^T @ Xhat.
+ *   Xq, ldq, beta  the forward's int8 activations [M x K] (row stride
+ *         ldq >= K) and per-token beta [M], as bitlinear_quantize_act
+ *         writes them.
+ *   dY    fp32 [M x N], row stride lddy >= N.
+ *   dW    fp32 [N x K], row stride lddw >= K (written, not accumulated).
+ */
+int bitlinear_backward_dw(const int8_t *Xq, int64_t ldq, const float *beta, int64_t M, int64_t N, int64_t K,
+                          const float *dY, int64_t lddy, float *dW, int64_t lddw, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

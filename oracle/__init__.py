@@ -15,7 +15,8 @@ pages it follows:
   absmean function ternarises the weights, activations are 8-bit.
 * LIT-380 record, Key takeaways, bullet 4: the product is integer additions.
 * HackerPapers digest, threads "GPUs Go Brrr" (2 bits in practice) and "How to
-  pack ternary numbers in 8-bit bytes" (several trits per byte).
+  pack ternary numbers in 8-bit bytes" (several trits per byte); a comment
+  there quoting the BitNet paper on the straight-through estimator (backward).
 
 Functions with no independent pin are listed as "parity unpinned" in the
 design notes; at present every function here has at least one pin in
@@ -230,6 +231,40 @@ def forward(t: np.ndarray, gamma, x: np.ndarray):
     acc = matmul(q, t)
     y = rescale(acc, beta, gamma)
     return {"q": q, "beta": beta, "acc": acc, "y": y}
+
+
+# ---------------------------------------------------------------------------
+# Backward pass with the straight-through estimator.  The pages quote the
+# BitNet paper: training uses the straight-through estimator, which bypasses
+# the non-differentiable functions (Sign and Clip there; here also the
+# rounding of the absmean and absmax quantisers) when gradients are
+# propagated (HackerPapers digest, comment quoting the BitNet paper on the
+# straight-through estimator).  Reading: each quantiser's derivative is taken
+# as 1 and its scale (gamma, beta_m) as a constant, so the forward acts like
+# the linear map y = Xhat @ What^T of the dequantised operands
+#     What[n, k] = gamma * T[n, k],    Xhat[m, k] = q[m, k] * r_m,
+# r_m = fl32(beta_m / 127), Xhat rounded to binary32 (the same rounding
+# order as the forward's rescale is not needed: Xhat only feeds a gradient).
+# Its gradients are the plain matrix products below, summed in binary64.
+# ---------------------------------------------------------------------------
+def dequantize_act(q: np.ndarray, beta: np.ndarray) -> np.ndarray:
+    """Xhat[m, k] = fl32(q[m, k] * fl32(beta_m / 127))."""
+    r = (np.asarray(beta, np.float32) / np.float32(127.0)).astype(np.float32)
+    return (np.asarray(q, np.float32) * r[:, None]).astype(np.float32)
+
+
+def backward_dx(t: np.ndarray, gamma, dy: np.ndarray) -> np.ndarray:
+    """Gradient with respect to the layer input: dX = dY @ What = gamma *
+    (dY @ T), float64 [M x K].  t: int8 [N x K]; dy: fp32 [M x N]."""
+    dy = np.asarray(dy, np.float64)
+    return float(np.float32(gamma)) * (dy @ np.asarray(t, np.float64))
+
+
+def backward_dw(q: np.ndarray, beta: np.ndarray, dy: np.ndarray) -> np.ndarray:
+    """Gradient with respect to the latent weights W (through the ternariser
+    by the straight-through estimator): dW = dY^T @ Xhat, float64 [N x K]."""
+    xhat = dequantize_act(q, beta).astype(np.float64)
+    return np.asarray(dy, np.float64).T @ xhat
 
 
 def threads_used() -> int:

@@ -71,6 +71,9 @@ _SIGNATURES = {
     "bitlinear_pack": ([_P, _I64, _I64, _I64, _INT, _P, _P], _INT),
     "bitlinear_quantize_act": ([_P, _INT, _I64, _I64, _I64, _P, _I64, _P, _P], _INT),
     "bitlinear_forward": ([_P, _INT, _P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P, _INT, _I64, _P, _I64, _P], _INT),
+    "bitlinear_backward_dx_workspace_bytes": ([_I64, _I64, _INT], _I64),
+    "bitlinear_backward_dx": ([_P, _INT, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P], _INT),
+    "bitlinear_backward_dw": ([_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P], _INT),
     "bitlinear_forward_algo": (
         [_P, _INT, _P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P, _INT, _I64, _P, _I64, _INT, _P], _INT),
 }
@@ -137,6 +140,18 @@ def bitlinear_quantize_weights(W, N, K, ldw, T, gamma, ws, ws_bytes, stream) -> 
 
 def bitlinear_binarize_weights(W, N, K, ldw, T, gamma, ws, ws_bytes, stream) -> int:
     return _lib.bitlinear_binarize_weights(W, N, K, ldw, T, gamma, ws, ws_bytes, stream)
+
+
+def bitlinear_backward_dx_workspace_bytes(N: int, K: int, layout: int) -> int:
+    return _lib.bitlinear_backward_dx_workspace_bytes(N, K, layout)
+
+
+def bitlinear_backward_dx(P, layout, gamma, M, N, K, dY, lddy, dX, lddx, ws, ws_bytes, stream) -> int:
+    return _lib.bitlinear_backward_dx(P, layout, gamma, M, N, K, dY, lddy, dX, lddx, ws, ws_bytes, stream)
+
+
+def bitlinear_backward_dw(Xq, ldq, beta, M, N, K, dY, lddy, dW, lddw, stream) -> int:
+    return _lib.bitlinear_backward_dw(Xq, ldq, beta, M, N, K, dY, lddy, dW, lddw, stream)
 
 
 def bitlinear_pack(T, N, K, ldt, layout, P, stream) -> int:
@@ -269,4 +284,33 @@ def forward(P, layout: int, gamma, X, N: int, K: int | None = None, beta=None, y
     _check(bitlinear_forward_algo(_ptr(P), layout, _ptr(gamma), M, N, K, _ptr(X), xdt, ldx, _ptr(beta),
                                   _ptr(out), _dtype_code(out), out.stride(0), _ptr(ws) if nws > 0 else None,
                                   nws, algo, _stream(stream)), "bitlinear_forward")
+    return out
+
+
+def backward_dx(P, layout: int, gamma, dY, K: int, out=None, stream=None):
+    """Straight-through-estimator input gradient dX = gamma * dY @ T.
+    dY fp32 [M x N] (cuda); returns dX fp32 [M x K]."""
+    torch = _torch()
+    M, N = dY.shape
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=dY.device)
+    nws = bitlinear_backward_dx_workspace_bytes(N, K, layout)
+    if nws < 0:
+        raise BitlinearError(ERR_INVALID_ARG, "backward_dx")
+    ws = torch.empty(nws, dtype=torch.uint8, device=dY.device) if nws > 0 else None
+    _check(bitlinear_backward_dx(_ptr(P), layout, _ptr(gamma), M, N, K, _ptr(dY), dY.stride(0), _ptr(out),
+                                 out.stride(0), _ptr(ws), nws, _stream(stream)), "bitlinear_backward_dx")
+    return out
+
+
+def backward_dw(Xq, beta, dY, K: int, out=None, stream=None):
+    """Straight-through-estimator latent-weight gradient dW = dY^T @ Xhat,
+    from the forward's int8 activations Xq [M x >=K] and beta [M].
+    Returns dW fp32 [N x K]."""
+    torch = _torch()
+    M, N = dY.shape
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float32, device=dY.device)
+    _check(bitlinear_backward_dw(_ptr(Xq), Xq.stride(0), _ptr(beta), M, N, K, _ptr(dY), dY.stride(0), _ptr(out),
+                                 out.stride(0), _stream(stream)), "bitlinear_backward_dw")
     return out

@@ -369,6 +369,63 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
     return status_of(e);
 }
 
+int64_t bitlinear_backward_dx_workspace_bytes(int64_t N, int64_t K, int layout)
+{
+    if (bitlinear_packed_bytes(N, K, layout) < 0) return -1;
+    return layout == BITLINEAR_LAYOUT_I2 ? 0 : round_up(bitlinear_packed_bytes(N, K, BITLINEAR_LAYOUT_I2), 256);
+}
+
+int bitlinear_backward_dx(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                          const float *dY, int64_t lddy, float *dX, int64_t lddx, void *ws, int64_t ws_bytes,
+                          void *stream)
+{
+    if (!P || !gamma || !dY || !dX || !valid_layout(layout)) return BITLINEAR_ERR_INVALID_ARG;
+    if (M < 1 || M > BITLINEAR_MAX_M || N < 1 || K < 1 || K > BITLINEAR_MAX_K || N > kMaxElems / K ||
+        lddy < N || lddx < K)
+        return BITLINEAR_ERR_INVALID_ARG;
+    const int64_t need = bitlinear_backward_dx_workspace_bytes(N, K, layout);
+    if (need > 0 && (!ws || ws_bytes < need)) return BITLINEAR_ERR_WORKSPACE;
+    if (!aligned16(P) || (need > 0 && !aligned16(ws)) || (reinterpret_cast<uintptr_t>(dY) & 3u) ||
+        (reinterpret_cast<uintptr_t>(dX) & 3u) || (reinterpret_cast<uintptr_t>(gamma) & 3u))
+        return BITLINEAR_ERR_INVALID_ARG;
+    const int64_t pb = bitlinear_packed_bytes(N, K, layout);
+    const Span sx = span_of(dX, M, lddx, K, 4), sy = span_of(dY, M, lddy, N, 4), sp = span_of(P, 1, pb, pb, 1),
+               sg = span_of(gamma, 1, 1, 1, 4);
+    if (overlap(sx, sy) || overlap(sx, sp) || overlap(sx, sg)) return BITLINEAR_ERR_INVALID_ARG;
+    if (need > 0) {
+        const Span sw = span_of(ws, 1, need, need, 1);
+        if (overlap(sw, sx) || overlap(sw, sy) || overlap(sw, sp) || overlap(sw, sg)) return BITLINEAR_ERR_INVALID_ARG;
+    }
+    (void)hipGetLastError();
+    hipStream_t st = as_stream(stream);
+    const uint8_t *p2 = P;
+    if (layout != BITLINEAR_LAYOUT_I2) {
+        uint8_t *w2 = static_cast<uint8_t *>(ws);
+        const hipError_t e = layout == BITLINEAR_LAYOUT_B3 ? bl::launch_b3_to_i2(P, N, K, w2, st)
+                                                           : bl::launch_b1_to_i2(P, N, K, w2, st);
+        if (e != hipSuccess) return BITLINEAR_ERR_LAUNCH;
+        p2 = w2;
+    }
+    return status_of(bl::launch_bwd_dx(p2, gamma, M, N, K, dY, lddy, dX, lddx, st));
+}
+
+int bitlinear_backward_dw(const int8_t *Xq, int64_t ldq, const float *beta, int64_t M, int64_t N, int64_t K,
+                          const float *dY, int64_t lddy, float *dW, int64_t lddw, void *stream)
+{
+    if (!Xq || !beta || !dY || !dW) return BITLINEAR_ERR_INVALID_ARG;
+    if (M < 1 || M > BITLINEAR_MAX_M || N < 1 || K < 1 || K > BITLINEAR_MAX_K || N > kMaxElems / K || ldq < K ||
+        lddy < N || lddw < K)
+        return BITLINEAR_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(dY) & 3u) || (reinterpret_cast<uintptr_t>(dW) & 3u) ||
+        (reinterpret_cast<uintptr_t>(beta) & 3u))
+        return BITLINEAR_ERR_INVALID_ARG;
+    const Span sw = span_of(dW, N, lddw, K, 4), sq = span_of(Xq, M, ldq, K, 1), sb = span_of(beta, 1, M, M, 4),
+               sy = span_of(dY, M, lddy, N, 4);
+    if (overlap(sw, sq) || overlap(sw, sb) || overlap(sw, sy)) return BITLINEAR_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return status_of(bl::launch_bwd_dw(Xq, ldq, beta, M, N, K, dY, lddy, dW, lddw, as_stream(stream)));
+}
+
 int bitlinear_forward(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
                       const void *X, int x_dtype, int64_t ldx, const float *beta_in, void *Y, int y_dtype,
                       int64_t ldy, void *ws, int64_t ws_bytes, void *stream)

@@ -62,6 +62,13 @@ hipError_t launch_gemm_mfma(const GemvArgs &a, hipStream_t stream);
 // GPU is not filled and the matrix-core GEMV is faster).
 int64_t gemm_tiles(int64_t M, int64_t N);
 
+// Straight-through-estimator gradients (backward.hip): dX from i2-packed
+// weights, dW from the forward's int8 activations and beta.
+hipError_t launch_bwd_dx(const uint8_t *P2, const float *gamma, int64_t M, int64_t N, int64_t K, const float *dY,
+                         int64_t lddy, float *dX, int64_t lddx, hipStream_t stream);
+hipError_t launch_bwd_dw(const int8_t *Xq, int64_t ldq, const float *beta, int64_t M, int64_t N, int64_t K,
+                         const float *dY, int64_t lddy, float *dW, int64_t lddw, hipStream_t stream);
+
 // Names (as profilers print them, without the argument list) of the kernel a
 // product launch runs for a shape.
 void gemv_kernel_name(int layout, int64_t M, int64_t N, int64_t K, bool tiled, char *buf, size_t n);

@@ -237,6 +237,28 @@ def test_product_kernel_names():
     assert f(0, 64, 64, bl.LAYOUT_I2, bl.BF16) is None
 
 
+def test_backward_rejects():
+    """Argument checks of the two backward entry points (no kernel runs)."""
+    dx = dict(P=A, layout=bl.LAYOUT_I2, gamma=C, M=4, N=64, K=64, dY=B, lddy=64, dX=D, lddx=64, ws=None, ws_bytes=0,
+              stream=None)
+    assert bl.bitlinear_backward_dx(**{**dx, "P": None}) == bl.ERR_INVALID_ARG
+    assert bl.bitlinear_backward_dx(**{**dx, "layout": 3}) == bl.ERR_INVALID_ARG
+    assert bl.bitlinear_backward_dx(**{**dx, "lddy": 63}) == bl.ERR_INVALID_ARG
+    assert bl.bitlinear_backward_dx(**{**dx, "lddx": 63}) == bl.ERR_INVALID_ARG
+    assert bl.bitlinear_backward_dx(**{**dx, "M": 0}) == bl.ERR_INVALID_ARG
+    assert bl.bitlinear_backward_dx(**{**dx, "dX": B + 64}) == bl.ERR_INVALID_ARG  # overlaps dY
+    assert bl.bitlinear_backward_dx(**{**dx, "layout": bl.LAYOUT_B3}) == bl.ERR_WORKSPACE
+    assert bl.bitlinear_backward_dx_workspace_bytes(64, 64, bl.LAYOUT_I2) == 0
+    assert bl.bitlinear_backward_dx_workspace_bytes(64, 64, bl.LAYOUT_B3) == bl.bitlinear_packed_bytes(64, 64, 0)
+    assert bl.bitlinear_backward_dx_workspace_bytes(0, 64, bl.LAYOUT_B3) == -1
+    dw = dict(Xq=A, ldq=64, beta=C, M=4, N=64, K=64, dY=B, lddy=64, dW=D, lddw=64, stream=None)
+    assert bl.bitlinear_backward_dw(**{**dw, "Xq": None}) == bl.ERR_INVALID_ARG
+    assert bl.bitlinear_backward_dw(**{**dw, "ldq": 63}) == bl.ERR_INVALID_ARG
+    assert bl.bitlinear_backward_dw(**{**dw, "lddw": 10}) == bl.ERR_INVALID_ARG
+    assert bl.bitlinear_backward_dw(**{**dw, "dW": B}) == bl.ERR_INVALID_ARG  # overlaps dY
+    assert bl.bitlinear_backward_dw(**{**dw, "beta": C + 2}) == bl.ERR_INVALID_ARG
+
+
 def test_b3_gemm_workspace():
     """Base-3 weights with more than 16 tokens: the workspace also holds the
     weights rewritten in the i2 layout for the GEMM."""

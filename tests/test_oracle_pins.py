@@ -490,3 +490,115 @@ def test_binary_product_is_add_sub():
     qs = q.astype(np.int64)
     want = np.array([[qs[m][t[n] == 1].sum() - qs[m][t[n] == -1].sum() for n in range(N)] for m in range(M)])
     assert np.array_equal(acc, want)
+
+
+# --------------------------------------------------------------------------
+# backward with the straight-through estimator
+# --------------------------------------------------------------------------
+def _surrogate(xhat, what, dy):
+    """f = sum_mn dY[m, n] * (Xhat @ What^T)[m, n], exactly, in rationals:
+    the forward as the linear map the estimator sees."""
+    M, K = len(xhat), len(xhat[0])
+    N = len(what)
+    return sum(dy[m][n] * sum(xhat[m][k] * what[n][k] for k in range(K)) for m in range(M) for n in range(N))
+
+
+def _frac(a):
+    return [[Fraction(float(v)) for v in row] for row in np.asarray(a)]
+
+
+def test_backward_dx_is_the_exact_gradient_of_the_surrogate():
+    """On a tiny case, the change of f under a unit step of Xhat[m, k] (exact
+    rationals: f is linear, so the difference quotient is the derivative)
+    equals dX[m, k]."""
+    r = synth.rng(41)
+    M, N, K = 2, 3, 5
+    t = synth.ternary_weights(N, K, seed=42)
+    gamma = np.float32(0.0371)
+    dy = r.standard_normal((M, N)).astype(np.float32)
+    xhat = r.standard_normal((M, K)).astype(np.float32)
+    what = [[Fraction(float(gamma)) * int(v) for v in row] for row in t]
+    fx, fdy = _frac(xhat), _frac(dy)
+    base = _surrogate(fx, what, fdy)
+    dx = oracle.backward_dx(t, gamma, dy)
+    for m in range(M):
+        for k in range(K):
+            fx[m][k] += 1
+            want = _surrogate(fx, what, fdy) - base
+            fx[m][k] -= 1
+            assert abs(dx[m, k] - float(want)) <= 1e-15 * max(1.0, abs(float(want)))
+
+
+def test_backward_dw_is_the_exact_gradient_of_the_surrogate():
+    """The estimator passes the gradient of What = gamma * T straight to the
+    latent W: a unit step of What[n, k] changes f by dW[n, k]."""
+    M, N, K = 3, 2, 4
+    x = synth.activations_f32(M, K, seed=43)
+    q, beta = oracle.quantize_act(x)
+    dy = synth.activations_f32(M, N, seed=44)
+    what = [[Fraction(float(np.float32(0.02))) * int(v) for v in row] for row in synth.ternary_weights(N, K, 45)]
+    xhat = _frac(oracle.dequantize_act(q, beta))
+    fdy = _frac(dy)
+    base = _surrogate(xhat, what, fdy)
+    dw = oracle.backward_dw(q, beta, dy)
+    for n in range(N):
+        for k in range(K):
+            what[n][k] += 1
+            want = _surrogate(xhat, what, fdy) - base
+            what[n][k] -= 1
+            assert abs(dw[n, k] - float(want)) <= 1e-15 * max(1.0, abs(float(want)))
+
+
+def test_backward_adjoint_identity_with_the_forward():
+    """<dY, y> = <dX, Xhat> = <dW, What> for the forward's own output y (up to
+    the forward's binary32 roundings): the backward is the transpose of the
+    map the forward computes."""
+    M, N, K = 5, 40, 300
+    t = synth.ternary_weights(N, K, seed=46)
+    gamma = np.float32(0.0123)
+    x = synth.activations_bf16(M, K, seed=47)
+    dy = synth.activations_f32(M, N, seed=48)
+    ref = oracle.forward(t, gamma, x)
+    xhat = oracle.dequantize_act(ref["q"], ref["beta"]).astype(np.float64)
+    what = float(gamma) * t.astype(np.float64)
+    lhs = float(np.sum(dy.astype(np.float64) * ref["y"]))
+    scale = float(np.sum(np.abs(dy.astype(np.float64)) * np.abs(ref["y"])))
+    dx = oracle.backward_dx(t, gamma, dy)
+    dw = oracle.backward_dw(ref["q"], ref["beta"], dy)
+    assert abs(lhs - float(np.sum(dx * xhat))) <= 1e-5 * scale
+    assert abs(lhs - float(np.sum(dw * what))) <= 1e-5 * scale
+
+
+def test_backward_closed_forms():
+    """All-ones T: dX rows are gamma times the row sums of dY.  One-hot dY at
+    (m0, n0): dX is gamma * T[n0] in row m0 and zero elsewhere; dW is
+    Xhat[m0] in row n0 and zero elsewhere."""
+    M, N, K = 4, 6, 9
+    gamma = np.float32(0.5)
+    dy = synth.activations_f32(M, N, seed=49)
+    dx = oracle.backward_dx(np.ones((N, K), np.int8), gamma, dy)
+    assert np.allclose(dx, 0.5 * dy.astype(np.float64).sum(axis=1, keepdims=True) * np.ones((1, K)), rtol=0,
+                       atol=1e-14)
+    t = synth.ternary_weights(N, K, seed=50)
+    hot = np.zeros((M, N), np.float32)
+    hot[2, 3] = 1.0
+    dx = oracle.backward_dx(t, gamma, hot)
+    want = np.zeros((M, K))
+    want[2] = 0.5 * t[3]
+    assert np.array_equal(dx, want)
+    q, beta = oracle.quantize_act(synth.activations_f32(M, K, seed=51))
+    dw = oracle.backward_dw(q, beta, hot)
+    want = np.zeros((N, K))
+    want[3] = oracle.dequantize_act(q, beta)[2]
+    assert np.array_equal(dw, want)
+
+
+def test_dequantize_act_hand_vector_and_inverse():
+    """beta = 127: r = 1 and Xhat = q exactly.  Otherwise Xhat * 127 / beta
+    is q up to the two binary32 roundings."""
+    q = np.array([[127, -64, 0, 1, -127]], np.int8)
+    assert np.array_equal(oracle.dequantize_act(q, np.array([127.0], np.float32)), q.astype(np.float32))
+    beta = np.array([2.54], np.float32)
+    xh = oracle.dequantize_act(q, beta).astype(np.float64)
+    back = xh * 127.0 / float(beta[0])
+    assert np.all(np.abs(back - q) <= 2 * 2.0 ** -24 * np.abs(q) + 1e-12)
