@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--batches", default=None, help="comma list overriding the workload's batch sizes")
     ap.add_argument("--layout", default="i2", choices=["i2", "b3", "b1"],
                     help="packed weight layout; b1 runs the binary-weight variant (sign quantiser)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the straight-through-estimator backward (dX and dW) of the workload's forwards "
+                         "instead of the forward, and print its own JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -162,6 +165,10 @@ def main():
                 xd = bf16_input(M, L["layer"].K, workloads.seed_for(wl, li, 1) + M)
                 jobs.append(make_job(M, L, xd.data_ptr(), bl.BF16, xd.stride(0)))
     torch.cuda.synchronize()
+
+    if args.backward:
+        run_backward(args, wl, jobs, layout, ncopies, stream, dev)
+        return
 
     def launch_job(j, copy):
         """The user path: one fused bitlinear_forward (quantiser + product + rescale)."""
@@ -353,6 +360,112 @@ def main():
                         "ms": round(prep_ms, 3)},
         "roofline": roof,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def run_backward(args, wl, jobs, layout, ncopies, stream, dev):
+    """Straight-through-estimator backward of every job: dX = gamma * dY @ T
+    from the packed weights and dW = dY^T @ Xhat from the job's quantised
+    activations, dY ~ N(0, 1) fp32.  Each kernel is timed as a HIP graph of R
+    back-to-back launches (dX rotating over the weight copies) between HIP
+    events on the launch stream."""
+    import torch
+    from ternary_weight_linear_forward_amd import bitlinear as bl
+    from ternary_weight_linear_forward_amd import synth
+
+    R = 8
+    per = {}
+    total_ms = 0.0
+    total_flops = 0
+    for ji, j in enumerate(jobs):
+        L, layer, M = j["L"], j["L"]["layer"], j["M"]
+        with torch.cuda.stream(stream):
+            dy = torch.from_numpy(synth.activations_f32(M, layer.N, seed=1000 + ji)).to(dev)
+            x = torch.empty((M, layer.K), dtype=torch.bfloat16, device=dev)
+            x.view(torch.int16).copy_(torch.from_numpy(synth.activations_bf16(M, layer.K, seed=2000 + ji)
+                                                       .view(np.int16)))
+            xq, beta = bl.quantize_act(x, stream=stream)
+            dx = torch.empty((M, layer.K), dtype=torch.float32, device=dev)
+            dw = torch.empty((layer.N, layer.K), dtype=torch.float32, device=dev)
+            nws = bl.bitlinear_backward_dx_workspace_bytes(layer.N, layer.K, layout)
+            ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+
+            def run_dx(c, L=L, layer=layer, M=M, dy=dy, dx=dx, ws=ws, nws=nws):
+                st = bl.bitlinear_backward_dx(L["P"][c].data_ptr(), layout, L["gamma"].data_ptr(), M, layer.N,
+                                              layer.K, dy.data_ptr(), dy.stride(0), dx.data_ptr(), dx.stride(0),
+                                              ws.data_ptr() if nws > 0 else None, nws, stream.cuda_stream)
+                if st:
+                    raise bl.BitlinearError(st, "backward_dx")
+
+            def run_dw(c, layer=layer, M=M, dy=dy, dw=dw, xq=xq, beta=beta):
+                st = bl.bitlinear_backward_dw(xq.data_ptr(), xq.stride(0), beta.data_ptr(), M, layer.N, layer.K,
+                                              dy.data_ptr(), dy.stride(0), dw.data_ptr(), dw.stride(0),
+                                              stream.cuda_stream)
+                if st:
+                    raise bl.BitlinearError(st, "backward_dw")
+
+            for name, fn, nbytes in (
+                    ("bl::k_bwd_dx", run_dx,
+                     L["P"][0].numel() + 4 * M * layer.N + 4 * M * layer.K
+                     + (2 * bl.bitlinear_packed_bytes(layer.N, layer.K, bl.LAYOUT_I2) if nws > 0 else 0)),
+                    ("bl::k_bwd_dw", run_dw, M * layer.K + 4 * M + 4 * M * layer.N + 4 * layer.N * layer.K)):
+                fn(0)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for r in range(R):
+                        fn(r % ncopies)
+                ts = []
+                for _ in range(3):
+                    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    ea.record(stream)
+                    g.replay()
+                    eb.record(stream)
+                    ts.append((ea, eb))
+                torch.cuda.synchronize()
+                ms = sum(a.elapsed_time(b) for a, b in ts) / (3 * R)
+                flops = 2 * M * layer.N * layer.K
+                d = per.setdefault(name, {"ms": 0.0, "bytes": 0, "flops": 0, "launches": 0, "jobs": []})
+                d["ms"] += ms
+                d["bytes"] += nbytes
+                d["flops"] += flops
+                d["launches"] += 1
+                d["jobs"].append(f"{layer.name}@M{M}:{ms * 1e3:.1f}us")
+                total_ms += ms
+                total_flops += flops
+                del g
+    dom_name, dom = max(per.items(), key=lambda kv: kv[1]["ms"])
+    intensity = dom["flops"] / dom["bytes"]
+    if intensity > FP32_MFMA_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
+        ach = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / FP32_MFMA_PEAK_TFLOPS, 4)}
+    else:
+        ach = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": None, "kernel": dom_name, "avg_launch_us": round(dom["ms"] / dom["launches"] * 1e3, 3)})
+    kernels = {k: {"avg_us": round(v["ms"] / v["launches"] * 1e3, 3),
+                   "GB/s": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1),
+                   "TFLOP/s": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2), "jobs": v["jobs"]}
+               for k, v in per.items()}
+    out = {
+        "metric": "STE backward (dX and dW) effective fp32 TFLOP/s",
+        "value": round(total_flops / (total_ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "ms_per_step": round(total_ms, 5),
+        "higher_is_better": True,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layout": args.layout, "pass": "backward",
+                   "dY": "N(0,1) fp32", "batches": sorted({j["M"] for j in jobs})},
+        "kernels": kernels,
+        "roofline": roof,
     }
     print(json.dumps(out), flush=True)
 
