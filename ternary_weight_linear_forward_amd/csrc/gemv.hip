@@ -98,11 +98,25 @@ __device__ __forceinline__ v4i b1_half_signed(uint32_t w, int h)
     return r;
 }
 
-// Layouts whose k-step multiplies the unsigned codes c = T + 1 (no per-word
-// conversion to signed bytes); the kernel subtracts sum_k q[m][k] once per
-// output, which is the same for every weight row.
+// Layouts whose k-step multiplies unsigned codes, with no per-word conversion
+// to signed bytes: the digits c = T + 1 in {0, 1, 2} for b3, the bit
+// b = (T + 1) / 2 for b1.  Then sum_k q T = acc - S (b3) or 2 acc - S (b1)
+// with S = sum_k q[m][k], the same for every weight row, computed once per
+// wave (act_sum_step).  (i2 keeps the signed form: with its cheap unpack the
+// extra MFMAs of S cancel the saved instructions, measured on the 70B layers.)
 template <int LAYOUT>
-constexpr bool kOffsetCodes = LAYOUT == LAYOUT_B3;
+constexpr bool kOffsetCodes = LAYOUT != LAYOUT_I2;
+
+template <int LAYOUT>
+__device__ __forceinline__ int offset_fix(int acc, int s)
+{
+    return LAYOUT == LAYOUT_B1 ? 2 * acc - s : acc - s;
+}
+template <int LAYOUT>
+__device__ __forceinline__ v4i offset_fix(v4i acc, v4i s)
+{
+    return LAYOUT == LAYOUT_B1 ? 2 * acc - s : acc - s;
+}
 
 // sacc[m] += sum of the activations of one k-step, in the MFMA output layout
 // (the product with an all-ones B operand; every weight row gets the same sum).
@@ -121,10 +135,26 @@ __device__ __forceinline__ void gemv_step(const uint4 (&b)[TW], const v4i (&a)[N
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
         const uint32_t wd[4] = {b[t].x, b[t].y, b[t].z, b[t].w};
-        if constexpr (LAYOUT == LAYOUT_I2) {
+        if constexpr (LAYOUT == LAYOUT_I2 && kOffsetCodes<LAYOUT>) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const v4i bt = {static_cast<int>(wd[d] & 0x03030303u), static_cast<int>((wd[d] >> 2) & 0x03030303u),
+                                static_cast<int>((wd[d] >> 4) & 0x03030303u),
+                                static_cast<int>((wd[d] >> 6) & 0x03030303u)};
+                acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d], bt, acc[t], 0, 0, 0);
+            }
+        } else if constexpr (LAYOUT == LAYOUT_I2) {
 #pragma unroll
             for (int d = 0; d < 4; ++d)
                 acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d], i2_word_signed(wd[d]), acc[t], 0, 0, 0);
+        } else if constexpr (LAYOUT == LAYOUT_B1 && kOffsetCodes<LAYOUT>) {
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                const uint32_t w = wd[d / 2] >> (4 * (d % 2));
+                const v4i bt = {static_cast<int>(w & 0x01010101u), static_cast<int>((w >> 1) & 0x01010101u),
+                                static_cast<int>((w >> 2) & 0x01010101u), static_cast<int>((w >> 3) & 0x01010101u)};
+                acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d], bt, acc[t], 0, 0, 0);
+            }
         } else if constexpr (LAYOUT == LAYOUT_B1) {
 #pragma unroll
             for (int d = 0; d < 8; ++d)
@@ -267,7 +297,7 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
     }
 
 #pragma unroll
-    for (int t = 0; t < TW; ++t) red[t][wave][lane] = kOffsetCodes<LAYOUT> ? acc[t] - sacc : acc[t];
+    for (int t = 0; t < TW; ++t) red[t][wave][lane] = kOffsetCodes<LAYOUT> ? offset_fix<LAYOUT>(acc[t], sacc) : acc[t];
     __syncthreads();
     // tile t is finished by wave t % KS (KS may be smaller than TW)
     for (int t = wave; t < TW; t += KS) {
@@ -396,7 +426,8 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const uint8_t *__restrict
         if (t >= ntiles) break;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
-            red[((t * KS + wave) * 4 + rr) * 64 + lane] = kOffsetCodes<LAYOUT> ? acc[t][rr] - sacc[rr] : acc[t][rr];
+            red[((t * KS + wave) * 4 + rr) * 64 + lane] =
+                kOffsetCodes<LAYOUT> ? offset_fix<LAYOUT>(acc[t][rr], sacc[rr]) : acc[t][rr];
     }
     __syncthreads();
     // output group (t, rr): tokens 4g + rr of this token group, weight row i of tile t
@@ -590,7 +621,9 @@ static GemvPlan gemv_plan(int layout, int64_t M, int64_t N, int64_t K)
     const int64_t nsteps = (KB + 3) / 4;
     const int64_t tgroups = (M + 15) / 16;
     GemvPlan p{false, 0, 0, false, 0, 0, 1};
-    if (NT >= 512 * tgroups && nsteps <= 64) {
+    // (b1 keeps 8 activation operands per k-step: four k-steps per wave would
+    // not fit the registers, so it goes persistent only up to two)
+    if (NT >= 512 * tgroups && nsteps <= (layout == LAYOUT_B1 ? 32 : 64)) {
         p.persist = true;
         p.KS = nsteps < 16 ? nsteps : 16;
         const int64_t spw = (nsteps + p.KS - 1) / p.KS;
@@ -604,6 +637,7 @@ static GemvPlan gemv_plan(int layout, int64_t M, int64_t N, int64_t K)
         return p;
     }
     p.tw = (M > 4 && NT >= 1024) ? 4 : ((M > 4 && NT >= 512) ? 2 : 1);
+    if (layout == LAYOUT_B1) p.tw = 1; // (operands of several tiles would spill)
     return p;
 }
 
