@@ -331,14 +331,15 @@ struct GemmTile {
     int bm, bn;
     double rate;
 };
-constexpr GemmTile kTiles[] = {{256, 256, 2.1}, {128, 256, 1.95}, {128, 128, 1.5}};
+constexpr GemmTile kTiles[] = {{256, 256, 2.1}, {128, 256, 1.95}, {128, 128, 1.5}, {64, 128, 1.0}};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int64_t kCUs = 256;
 
 int best_tile(int64_t M, int64_t N)
 {
     int best = 0;
     double best_cost = 0;
-    for (int i = 0; i < 3; ++i) {
+    for (int i = 0; i < kNumTiles; ++i) {
         const int64_t t = ((M + kTiles[i].bm - 1) / kTiles[i].bm) * ((N + kTiles[i].bn - 1) / kTiles[i].bn);
         const double cost = static_cast<double>((t + kCUs - 1) / kCUs) * kTiles[i].bm * kTiles[i].bn / kTiles[i].rate;
         if (i == 0 || cost < best_cost) best = i, best_cost = cost;
@@ -356,7 +357,7 @@ int64_t gemm_tiles(int64_t M, int64_t N)
 void gemm_kernel_name(int64_t M, int64_t N, char *buf, size_t n)
 {
     static const char *const names[] = {"bl::k_gemm_mfma_i2<256, 256, 2, 2>", "bl::k_gemm_mfma_i2<128, 256, 2, 4>",
-                                        "bl::k_gemm_mfma_i2<128, 128, 2, 2>"};
+                                        "bl::k_gemm_mfma_i2<128, 128, 2, 2>", "bl::k_gemm_mfma_i2<64, 128, 2, 2>"};
     snprintf(buf, n, "%s", names[best_tile(M, N)]);
 }
 
@@ -365,7 +366,8 @@ hipError_t launch_gemm_mfma(const GemvArgs &a, hipStream_t stream)
     switch (best_tile(a.M, a.N)) {
     case 0: return launch_tile<256, 256, 2, 2>(a, stream);
     case 1: return launch_tile<128, 256, 2, 4>(a, stream);
-    default: return launch_tile<128, 128, 2, 2>(a, stream);
+    case 2: return launch_tile<128, 128, 2, 2>(a, stream);
+    default: return launch_tile<64, 128, 2, 2>(a, stream);
     }
 }
 

@@ -206,11 +206,11 @@ def test_forward_many_tokens(algo_name, algo, layout, M, N, K):
     run_forward_case(M, N, K, algo, layout, seed=M * 131 + N + K)
 
 
-@pytest.mark.parametrize("M,N,K", [(1100, 5000, 200), (4000, 4000, 130), (2048, 3200, 320)],
-                         ids=["tile128x256", "tile256x256_odd_kb", "prefill_rows"])
+@pytest.mark.parametrize("M,N,K", [(1100, 5000, 200), (4000, 4000, 130), (2048, 3200, 320), (150, 6000, 300)],
+                         ids=["tile128x256", "tile256x256_odd_kb", "prefill_rows", "tile64x128_skinny"])
 def test_gemm_tile_shapes(M, N, K):
-    """Sizes whose workgroup-tile choice differs (128x256 and 256x256 tiles,
-    ragged in M and N; an odd number of k-blocks ends in a half stage)."""
+    """Sizes whose workgroup-tile choice differs (128x256, 256x256 and 64x128
+    tiles, ragged in M and N; an odd number of k-blocks ends in a half stage)."""
     log("forward gemm tiles", M, N, K)
     run_forward_case(M, N, K, bl.ALGO_GEMM_MFMA, "i2", seed=M + 7 * N + K, y_kinds=("i32", "f32"))
     if M * N <= 1100 * 5000:  # base-3 weights through the i2 rewrite
