@@ -298,6 +298,7 @@ def main():
             d["ops"] += 2 * j["M"] * layer.N * layer.K
             d["launches"] += 1
             d["jobs"].append(f"{layer.name}@M{j['M']}")
+            d.setdefault("job_us", []).append(f"{layer.name}@M{j['M']}:{j['launch_ms'] * 1e3:.1f}")
     dom_name, dom = max(per_kernel.items(), key=lambda kv: kv[1]["ms"])
     avg_us = dom["ms"] / dom["launches"] * 1e3
     bound = "mfma" if "gemm" in dom_name else "hbm"
@@ -315,7 +316,8 @@ def main():
                  "algorithmic_ops_per_launch": dom["ops"] // dom["launches"]})
     kernels = {k: {"avg_us": round(v["ms"] / v["launches"] * 1e3, 3),
                    "GB/s": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1),
-                   "TOPS": round(v["ops"] / (v["ms"] * 1e-3) / 1e12, 2), "jobs": len(v["jobs"])}
+                   "TOPS": round(v["ops"] / (v["ms"] * 1e-3) / 1e12, 2), "jobs": len(v["jobs"]),
+                   "us_per_job": v["job_us"]}
                for k, v in per_kernel.items()}
     print(f"[bench] per-kernel: {json.dumps(kernels)}", file=sys.stderr, flush=True)
 

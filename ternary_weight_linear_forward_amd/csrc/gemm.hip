@@ -324,14 +324,15 @@ hipError_t launch_tile(const GemvArgs &a, hipStream_t stream)
 } // namespace
 
 namespace {
-// Tile shapes on offer, with their measured sustained rates relative to each
-// other (large problems, every CU busy).  A launch costs about
-// ceil(tiles / 256 CUs) rounds of one tile each.
+// Tile shapes on offer, with their sustained rates relative to each other
+// (measured; for the small tile, fitted to 32-176-token products of the
+// 70B layers, where latency rather than the matrix cores bounds a tile).  A
+// launch costs about ceil(tiles / 256 CUs) rounds of one tile each.
 struct GemmTile {
     int bm, bn;
     double rate;
 };
-constexpr GemmTile kTiles[] = {{256, 256, 2.1}, {128, 256, 1.95}, {128, 128, 1.5}, {64, 128, 1.0}};
+constexpr GemmTile kTiles[] = {{256, 256, 2.1}, {128, 256, 1.95}, {128, 128, 1.5}, {32, 128, 1.1}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int64_t kCUs = 256;
 
@@ -350,14 +351,14 @@ int best_tile(int64_t M, int64_t N)
 
 int64_t gemm_tiles(int64_t M, int64_t N)
 {
-    const GemmTile &t = kTiles[best_tile(M, N)];
-    return ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+    // in units of 64 x 128 (the GEMV / GEMM crossover was measured in these)
+    return ((M + 63) / 64) * ((N + 127) / 128);
 }
 
 void gemm_kernel_name(int64_t M, int64_t N, char *buf, size_t n)
 {
     static const char *const names[] = {"bl::k_gemm_mfma_i2<256, 256, 2, 2>", "bl::k_gemm_mfma_i2<128, 256, 2, 4>",
-                                        "bl::k_gemm_mfma_i2<128, 128, 2, 2>", "bl::k_gemm_mfma_i2<64, 128, 2, 2>"};
+                                        "bl::k_gemm_mfma_i2<128, 128, 2, 2>", "bl::k_gemm_mfma_i2<32, 128, 1, 4>"};
     snprintf(buf, n, "%s", names[best_tile(M, N)]);
 }
 
@@ -367,7 +368,7 @@ hipError_t launch_gemm_mfma(const GemvArgs &a, hipStream_t stream)
     case 0: return launch_tile<256, 256, 2, 2>(a, stream);
     case 1: return launch_tile<128, 256, 2, 4>(a, stream);
     case 2: return launch_tile<128, 128, 2, 2>(a, stream);
-    default: return launch_tile<64, 128, 2, 2>(a, stream);
+    default: return launch_tile<32, 128, 1, 4>(a, stream);
     }
 }
 

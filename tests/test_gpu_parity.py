@@ -206,10 +206,12 @@ def test_forward_many_tokens(algo_name, algo, layout, M, N, K):
     run_forward_case(M, N, K, algo, layout, seed=M * 131 + N + K)
 
 
-@pytest.mark.parametrize("M,N,K", [(1100, 5000, 200), (4000, 4000, 130), (2048, 3200, 320), (150, 6000, 300)],
-                         ids=["tile128x256", "tile256x256_odd_kb", "prefill_rows", "tile64x128_skinny"])
+@pytest.mark.parametrize("M,N,K", [(1100, 5000, 200), (4000, 4000, 130), (2048, 3200, 320), (150, 6000, 300),
+                                   (100, 9000, 200)],
+                         ids=["tile128x256", "tile256x256_odd_kb", "prefill_rows", "tile32x128_skinny",
+                              "tile32x128_one_block"])
 def test_gemm_tile_shapes(M, N, K):
-    """Sizes whose workgroup-tile choice differs (128x256, 256x256 and 64x128
+    """Sizes whose workgroup-tile choice differs (128x256, 256x256 and 32x128
     tiles, ragged in M and N; an odd number of k-blocks ends in a half stage)."""
     log("forward gemm tiles", M, N, K)
     run_forward_case(M, N, K, bl.ALGO_GEMM_MFMA, "i2", seed=M + 7 * N + K, y_kinds=("i32", "f32"))
