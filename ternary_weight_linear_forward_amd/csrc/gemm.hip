@@ -93,7 +93,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
                                                                const int8_t *__restrict__ Xq, int64_t ldq,
                                                                const float *__restrict__ beta, int64_t M,
                                                                int64_t N, int64_t K, void *__restrict__ Y,
-                                                               int y_dtype, int64_t ldy)
+                                                               int y_dtype, int64_t ldy, int n_major)
 {
     constexpr int NW = WM * WN;                // waves
     constexpr int MI = BM / WM / 32;           // 32-token MFMA tiles per wave
@@ -117,19 +117,21 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
     const int l32 = lane & 31, kh = lane >> 5;
 
     // XCD-aware tile order.  Workgroup ids are dealt round-robin to the 8 XCDs
-    // (each with its own L2), so id L runs on XCD L % 8.  Tiles are numbered
-    // M-block-major (t = mb * nN + nb) and XCD x takes the contiguous range of
-    // tile numbers [x * W/8, (x+1) * W/8): the workgroups sharing an XCD work on
-    // the same activation rows and find them in that XCD's L2.
-    const int64_t nN = gridDim.x, W = static_cast<int64_t>(gridDim.x) * gridDim.y;
-    const int64_t L = blockIdx.x + static_cast<int64_t>(gridDim.x) * blockIdx.y;
+    // (each with its own L2), so id L runs on XCD L % 8, and XCD x takes the
+    // contiguous range of tile numbers [x * W/8, (x+1) * W/8).  Tiles are
+    // numbered M-block-major (t = mb * nN + nb: the workgroups sharing an XCD
+    // work on the same activation rows and find them in its L2) or, with
+    // n_major, N-block-major (t = nb * nM + mb: they share weight tiles, which
+    // then cross HBM once; the host picks whichever operand is larger per XCD).
+    const int64_t nN = gridDim.x, nM = gridDim.y, W = nN * nM;
+    const int64_t L = blockIdx.x + nN * blockIdx.y;
     int64_t t;
     {
         const int64_t per = W / 8, rem = W % 8, x = L % 8, j = L / 8;
         t = x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
     }
-    const int64_t m0 = (t / nN) * BM;
-    const int64_t n0 = (t % nN) * BN;
+    const int64_t m0 = (n_major ? t % nM : t / nN) * BM;
+    const int64_t n0 = (n_major ? t / nM : t % nN) * BN;
     const int64_t nstages = (KB + 1) / 2;
 
     // ---- copy sources, fixed for the whole loop ------------------------------
@@ -201,13 +203,20 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
         b_off[b] = A_BYTES + (nl / 16) * 256 + (nl % 16) * 16 + 4 * kh;
     }
 
-    v16i acc[MI][NI];
+    // A wave with fewer than 4 output tiles keeps SPLIT accumulators per tile
+    // (k-step kk adds into copy kk % SPLIT), so that consecutive MFMAs of a
+    // stage do not wait on each other's results; the copies are summed at the
+    // end (exact: integer sums).
+    constexpr int SPLIT = MI * NI >= 4 ? 1 : 4 / (MI * NI);
+    v16i acc[MI][NI][SPLIT];
 #pragma unroll
     for (int a = 0; a < MI; ++a)
 #pragma unroll
         for (int b = 0; b < NI; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
+            for (int c = 0; c < SPLIT; ++c)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[a][b][c][r] = 0;
 
     // Operands of one stage, read from LDS one stage ahead of their MFMAs so
     // that LDS latency overlaps the matrix work of the stage before.
@@ -239,7 +248,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
             for (int a = 0; a < MI; ++a)
 #pragma unroll
                 for (int b = 0; b < NI; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[a][kk], bf[b], acc[a][b], 0, 0, 0);
+                    acc[a][b][kk % SPLIT] = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[a][kk], bf[b],
+                                                                                  acc[a][b][kk % SPLIT], 0, 0, 0);
         }
     };
 
@@ -274,6 +284,12 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
     if (st < nstages) step(st, o0, o1);
 
     // ---- epilogue ------------------------------------------------------------
+#pragma unroll
+    for (int a = 0; a < MI; ++a)
+#pragma unroll
+        for (int b = 0; b < NI; ++b)
+#pragma unroll
+            for (int c = 1; c < SPLIT; ++c) acc[a][b][0] += acc[a][b][c];
     __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0)); // the clamped tail copies still land in LDS
     stage_barrier();
     float *scale = reinterpret_cast<float *>(lds);
@@ -296,7 +312,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
 #pragma unroll
                 for (int b = 0; b < NI; ++b) {
                     const int64_t n = n0 + wn * (BN / WN) + b * 32 + l32;
-                    if (n < N) put(m * ldy + n, acc[a][b][r], sc);
+                    if (n < N) put(m * ldy + n, acc[a][b][0][r], sc);
                 }
             }
     };
@@ -316,9 +332,16 @@ hipError_t launch_tile(const GemvArgs &a, hipStream_t stream)
 {
     const int64_t NT = (a.N + 15) / 16;
     const int64_t KB = (a.K + 63) / 64;
-    dim3 grid(static_cast<unsigned>((a.N + BN - 1) / BN), static_cast<unsigned>((a.M + BM - 1) / BM));
+    const int64_t nN = (a.N + BN - 1) / BN, nM = (a.M + BM - 1) / BM;
+    dim3 grid(static_cast<unsigned>(nN), static_cast<unsigned>(nM));
+    // bytes one XCD reads per tile order: M-block-major: its share of the
+    // activation row blocks plus every weight tile; N-block-major: its share of
+    // the weight tiles plus every activation row
+    const double act = static_cast<double>(a.M) * a.K, wts = static_cast<double>(a.N) * a.K / 4;
+    const double m_major = act / 8 + wts, n_major = wts / 8 + act;
+    const int nmaj = (nM > 1 && n_major < m_major) ? 1 : 0;
     hipLaunchKernelGGL((k_gemm_mfma_i2<BM, BN, WM, WN>), grid, dim3(64 * WM * WN), 0, stream, a.P, KB, NT, a.gamma,
-                       a.Xq, a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
+                       a.Xq, a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy, nmaj);
     return hipGetLastError();
 }
 } // namespace
