@@ -32,7 +32,7 @@
 namespace bl {
 
 namespace {
-constexpr int KSTEP = 128;              // k per stage: two 64-weight k-blocks
+constexpr int KSTEP = 128;              // k per stage half: two 64-weight k-blocks
 constexpr int LDS_RING_BYTES = 150 * 1024; // LDS given to the stage ring (of 160 KB)
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -87,7 +87,7 @@ __device__ __forceinline__ void stage_barrier()
     asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int S>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__restrict__ P, int64_t KB,
                                                                int64_t NT, const float *__restrict__ gamma_p,
                                                                const int8_t *__restrict__ Xq, int64_t ldq,
@@ -98,11 +98,14 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
     constexpr int NW = WM * WN;                // waves
     constexpr int MI = BM / WM / 32;           // 32-token MFMA tiles per wave
     constexpr int NI = BN / WN / 32;           // 32-row MFMA tiles per wave
-    constexpr int A_BYTES = BM * KSTEP;        // activation bytes per stage
-    constexpr int B_BYTES = BN * 32;           // packed weight bytes per stage
+    constexpr int KS_ = KSTEP * S;             // k per stage: S halves of 128
+    constexpr int KK = 4 * S;                  // 32-k MFMA steps per stage
+    constexpr int A_BYTES = BM * KS_;          // activation bytes per stage: [S][BM][128]
+    constexpr int B_BYTES = BN * 32 * S;       // packed weight bytes per stage (2S k-blocks)
     constexpr int STAGE = A_BYTES + B_BYTES;
     constexpr int A_ROWS_W = BM / NW;          // activation rows copied by one wave
-    constexpr int A_INST = A_ROWS_W / 8;       // 1 KB copies (8 rows) per wave per stage
+    constexpr int A_RB = A_ROWS_W / 8;         // 1 KB copies (8 rows of 128 B) per wave per half
+    constexpr int A_INST = A_RB * S;           // ... per stage
     // weight copies: 16 bytes per lane when every wave gets whole 1 KB copies, else 4
     constexpr int B_CP = (B_BYTES % (1024 * NW) == 0) ? 16 : 4;
     constexpr int B_INST = B_BYTES / (64 * B_CP) / NW;
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
     }
     const int64_t m0 = (n_major ? t % nM : t / nN) * BM;
     const int64_t n0 = (n_major ? t / nM : t % nN) * BN;
-    const int64_t nstages = (KB + 1) / 2;
+    const int64_t nstages = (KB + 2 * S - 1) / (2 * S);
 
     // ---- copy sources, fixed for the whole loop ------------------------------
     // The copies are buffer loads.  The hardware range check of a buffer
@@ -142,13 +145,14 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
     // stored, and k positions past K meet zero weights (pad codes, or words
     // replaced in the last stage), so whatever they read is harmless.
     //
-    // Activation copy j of this wave: row wave*A_ROWS_W + 8j + lane/8, LDS slot
-    // lane%8, which holds the row's 16-byte unit (lane%8) ^ swz(row).
+    // Activation copy j of this wave: k-half h = j / A_RB, row
+    // wave*A_ROWS_W + 8 (j % A_RB) + lane/8, LDS slot lane%8 of the half's
+    // 128-byte row, which holds the row's 16-byte unit (lane%8) ^ swz(row).
     int a_voff[A_INST];
 #pragma unroll
     for (int j = 0; j < A_INST; ++j) {
-        const int row = wave * A_ROWS_W + 8 * j + (lane >> 3);
-        a_voff[j] = static_cast<int>(row * ldq) + ((lane & 7) ^ a_swz(row)) * 16;
+        const int row = wave * A_ROWS_W + 8 * (j % A_RB) + (lane >> 3);
+        a_voff[j] = static_cast<int>(row * ldq) + (j / A_RB) * KSTEP + ((lane & 7) ^ a_swz(row)) * 16;
     }
     // Weight copy j of this wave covers stage chunk c (c = kb2 * BN/16 + tile,
     // 256 bytes = 16 rows x 16 bytes): with 16-byte copies chunks
@@ -176,12 +180,15 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
     // read nothing (their resources are empty) and are never used.
     auto issue = [&](int64_t st, int buf) {
         int8_t *sbase = lds + buf * STAGE;
-        const int64_t ka = st * KSTEP, kb = st * 2 * 256;
+        const int64_t ka = st * KS_, kb = st * 2 * S * 256;
         const int na = static_cast<int>(a_bytes > ka ? a_bytes - ka : 0);
         const int nb = static_cast<int>(b_bytes > kb ? b_bytes - kb : 0);
 #pragma unroll
         for (int j = 0; j < A_INST; ++j)
-            buffer_copy_to_lds<16>(a_base + ka, na, (lds_void_t *)(sbase + (wave * A_ROWS_W + 8 * j) * KSTEP), a_voff[j]);
+            buffer_copy_to_lds<16>(a_base + ka, na,
+                                   (lds_void_t *)(sbase + (j / A_RB) * BM * KSTEP +
+                                                  (wave * A_ROWS_W + 8 * (j % A_RB)) * KSTEP),
+                                   a_voff[j]);
 #pragma unroll
         for (int j = 0; j < B_INST; ++j)
             buffer_copy_to_lds<B_CP>(b_base + kb, nb, (lds_void_t *)(sbase + A_BYTES + (wave * B_INST + j) * 64 * B_CP),
@@ -189,12 +196,13 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
     };
 
     // ---- operand read offsets within a stage ---------------------------------
-    int a_off[MI][4];
+    int a_off[MI][KK];
 #pragma unroll
     for (int a = 0; a < MI; ++a) {
         const int row = wm * (BM / WM) + a * 32 + l32;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) a_off[a][kk] = row * KSTEP + (((2 * kk + kh) ^ a_swz(row)) * 16);
+        for (int kk = 0; kk < KK; ++kk)
+            a_off[a][kk] = (kk / 4) * BM * KSTEP + row * KSTEP + (((2 * (kk % 4) + kh) ^ a_swz(row)) * 16);
     }
     int b_off[NI];
 #pragma unroll
@@ -221,29 +229,32 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
     // Operands of one stage, read from LDS one stage ahead of their MFMAs so
     // that LDS latency overlaps the matrix work of the stage before.
     struct Ops {
-        v4i a[MI][4];       // activation operand of tile a, k-step kk
-        uint32_t w[NI][4];  // packed word of B tile b, k-step kk (16 weights)
+        v4i a[MI][KK];       // activation operand of tile a, k-step kk
+        uint32_t w[NI][KK];  // packed word of B tile b, k-step kk (16 weights)
     };
     auto read_ops = [&](int buf, Ops &o) {
         const int8_t *sbase = lds + buf * STAGE;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
             for (int a = 0; a < MI; ++a) o.a[a][kk] = *reinterpret_cast<const v4i *>(sbase + a_off[a][kk]);
         // word of k-block kk/2, 16-weight group (kk % 2) * 2 + kh
 #pragma unroll
         for (int b = 0; b < NI; ++b)
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
+            for (int kk = 0; kk < KK; ++kk)
                 o.w[b][kk] = *reinterpret_cast<const uint32_t *>(sbase + b_off[b] + (kk / 2) * (BN / 16) * 256 +
                                                                  (kk % 2) * 8);
     };
-    auto mma = [&](const Ops &o, bool hi_valid) {
+    // kb_left: k-blocks of the stage that exist (>= 2S except in the last
+    // stage); the words of the others become T = 0
+    auto mma = [&](const Ops &o, int kb_left) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < KK; ++kk) {
             v4i bf[NI];
 #pragma unroll
-            for (int b = 0; b < NI; ++b) bf[b] = gemm_i2_word_signed((kk < 2 || hi_valid) ? o.w[b][kk] : I2_ZERO_WORD);
+            for (int b = 0; b < NI; ++b)
+                bf[b] = gemm_i2_word_signed((kk < 2 || kk / 2 < kb_left) ? o.w[b][kk] : I2_ZERO_WORD);
 #pragma unroll
             for (int a = 0; a < MI; ++a)
 #pragma unroll
@@ -273,7 +284,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
         stage_barrier();
         issue(st + NST, slot);
         read_ops(nslot, nxt);
-        mma(cur, 2 * st + 1 < KB);
+        const int64_t left = KB - 2 * S * st;
+        mma(cur, static_cast<int>(left < 2 * S ? left : 2 * S));
         slot = nslot;
     };
     int64_t st = 0;
@@ -327,7 +339,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
 }
 
 namespace {
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int S>
 hipError_t launch_tile(const GemvArgs &a, hipStream_t stream)
 {
     const int64_t NT = (a.N + 15) / 16;
@@ -340,7 +352,7 @@ hipError_t launch_tile(const GemvArgs &a, hipStream_t stream)
     const double act = static_cast<double>(a.M) * a.K, wts = static_cast<double>(a.N) * a.K / 4;
     const double m_major = act / 8 + wts, n_major = wts / 8 + act;
     const int nmaj = (nM > 1 && n_major < m_major) ? 1 : 0;
-    hipLaunchKernelGGL((k_gemm_mfma_i2<BM, BN, WM, WN>), grid, dim3(64 * WM * WN), 0, stream, a.P, KB, NT, a.gamma,
+    hipLaunchKernelGGL((k_gemm_mfma_i2<BM, BN, WM, WN, S>), grid, dim3(64 * WM * WN), 0, stream, a.P, KB, NT, a.gamma,
                        a.Xq, a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy, nmaj);
     return hipGetLastError();
 }
@@ -352,10 +364,11 @@ namespace {
 // 70B layers, where latency rather than the matrix cores bounds a tile).  A
 // launch costs about ceil(tiles / 256 CUs) rounds of one tile each.
 struct GemmTile {
-    int bm, bn;
+    int bm, bn, wm, wn, s; // tile, wave grid, k halves (of 128) per stage
     double rate;
 };
-constexpr GemmTile kTiles[] = {{256, 256, 2.1}, {128, 256, 1.95}, {128, 128, 1.5}, {32, 128, 1.1}};
+constexpr GemmTile kTiles[] = {
+    {256, 256, 2, 2, 1, 2.1}, {128, 256, 2, 4, 1, 1.95}, {128, 128, 2, 2, 1, 1.5}, {32, 128, 1, 4, 1, 1.1}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int64_t kCUs = 256;
 
@@ -370,6 +383,13 @@ int best_tile(int64_t M, int64_t N)
     }
     return best;
 }
+
+template <int I>
+hipError_t launch_entry(const GemvArgs &a, hipStream_t stream)
+{
+    constexpr GemmTile t = kTiles[I];
+    return launch_tile<t.bm, t.bn, t.wm, t.wn, t.s>(a, stream);
+}
 } // namespace
 
 int64_t gemm_tiles(int64_t M, int64_t N)
@@ -380,18 +400,18 @@ int64_t gemm_tiles(int64_t M, int64_t N)
 
 void gemm_kernel_name(int64_t M, int64_t N, char *buf, size_t n)
 {
-    static const char *const names[] = {"bl::k_gemm_mfma_i2<256, 256, 2, 2>", "bl::k_gemm_mfma_i2<128, 256, 2, 4>",
-                                        "bl::k_gemm_mfma_i2<128, 128, 2, 2>", "bl::k_gemm_mfma_i2<32, 128, 1, 4>"};
-    snprintf(buf, n, "%s", names[best_tile(M, N)]);
+    const GemmTile &t = kTiles[best_tile(M, N)];
+    snprintf(buf, n, "bl::k_gemm_mfma_i2<%d, %d, %d, %d, %d>", t.bm, t.bn, t.wm, t.wn, t.s);
 }
 
 hipError_t launch_gemm_mfma(const GemvArgs &a, hipStream_t stream)
 {
+    static_assert(kNumTiles == 4, "one case per tile shape");
     switch (best_tile(a.M, a.N)) {
-    case 0: return launch_tile<256, 256, 2, 2>(a, stream);
-    case 1: return launch_tile<128, 256, 2, 4>(a, stream);
-    case 2: return launch_tile<128, 128, 2, 2>(a, stream);
-    default: return launch_tile<32, 128, 1, 4>(a, stream);
+    case 0: return launch_entry<0>(a, stream);
+    case 1: return launch_entry<1>(a, stream);
+    case 2: return launch_entry<2>(a, stream);
+    default: return launch_entry<3>(a, stream);
     }
 }
 

@@ -229,11 +229,11 @@ def test_product_kernel_names():
     assert f(16, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemv_mfma<0, 1, 1, true>"
     assert f(16, 3200, 3200, bl.LAYOUT_I2, bl.I8) == "bl::k_gemv_mfma<0, 1, 1, false>"
     assert f(16, 28672, 8192, bl.LAYOUT_B3, bl.BF16).startswith("bl::k_gemv_persist<1, ")
-    assert f(2048, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemm_mfma_i2<128, 256, 2, 4>"
-    assert f(64, 28672, 8192, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemm_mfma_i2<32, 128, 1, 4>"
-    assert f(100, 9000, 200, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemm_mfma_i2<32, 128, 1, 4>"
+    assert f(2048, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemm_mfma_i2<128, 256, 2, 4, 1>"
+    assert f(64, 28672, 8192, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemm_mfma_i2<32, 128, 1, 4, 1>"
+    assert f(100, 9000, 200, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemm_mfma_i2<32, 128, 1, 4, 1>"
     assert f(64, 8192, 8192, bl.LAYOUT_I2, bl.BF16).startswith("bl::k_gemv_mfma<")  # too few tiles
-    assert f(150, 6000, 300, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemm_mfma_i2<32, 128, 1, 4>"
+    assert f(150, 6000, 300, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemm_mfma_i2<32, 128, 1, 4, 1>"
     assert f(3, 64, 64, bl.LAYOUT_I2, bl.BF16, bl.ALGO_GEMV_ADDSUB) == "bl::k_gemv_addsub<4>"
     assert f(3, 64, 64, bl.LAYOUT_B3, bl.BF16, bl.ALGO_GEMM_MFMA) is None
     assert f(1, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == "bl::k_gemv_mfma<2, 1, 1, false>"
