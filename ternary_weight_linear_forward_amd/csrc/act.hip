@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void k_quant_act(const void *__restrict__ X, i
 // thread issues all its 16-byte loads of the row first (one memory round
 // trip), keeps them in registers for the max and for the rounding.
 template <int XDT, int VPT>
-__global__ __launch_bounds__(256) void k_quant_act_vec(const void *__restrict__ X, int64_t K, int64_t ldx,
+__global__ __launch_bounds__(1024) void k_quant_act_vec(const void *__restrict__ X, int64_t K, int64_t ldx,
                                                        int8_t *__restrict__ Xq, int64_t ldq,
                                                        float *__restrict__ beta)
 {
@@ -122,8 +122,12 @@ static bool launch_vec(const void *X, int64_t M, int64_t K, int64_t ldx, int8_t 
     constexpr int EPV = XDT == DT_F32 ? 4 : 8;
     constexpr int ES = XDT == DT_F32 ? 4 : 2;
     if (K % EPV || (ldx * ES) % 16 || (reinterpret_cast<uintptr_t>(X) & 15)) return false;
-    const int64_t vpt = (K / EPV + 255) / 256;
-    dim3 grid(static_cast<unsigned>(M)), block(256);
+    // about one 16-byte vector per thread (up to 1024 threads): the row's
+    // loads all go out at once and each thread rounds only a few elements
+    const int64_t nvec = K / EPV;
+    const int64_t threads = nvec <= 64 ? 64 : (nvec >= 1024 ? 1024 : (nvec + 63) / 64 * 64);
+    const int64_t vpt = (nvec + threads - 1) / threads;
+    dim3 grid(static_cast<unsigned>(M)), block(static_cast<unsigned>(threads));
     if (vpt <= 1) hipLaunchKernelGGL((k_quant_act_vec<XDT, 1>), grid, block, 0, stream, X, K, ldx, Xq, ldq, beta);
     else if (vpt <= 2) hipLaunchKernelGGL((k_quant_act_vec<XDT, 2>), grid, block, 0, stream, X, K, ldx, Xq, ldq, beta);
     else if (vpt <= 4) hipLaunchKernelGGL((k_quant_act_vec<XDT, 4>), grid, block, 0, stream, X, K, ldx, Xq, ldq, beta);
