@@ -583,7 +583,10 @@ static void launch_mfma_tw(const GemvArgs &a, int64_t KB, int64_t NT, int64_t ns
     const int64_t want_waves = 256 * 16;
     int64_t KS = (want_waves + groups * tgroups - 1) / (groups * tgroups);
     KS = KS < 1 ? 1 : KS;
-    KS = KS > 16 ? 16 : KS;
+    // at most 10 waves: with fewer, larger waves the cross-wave reduction is
+    // shorter (measured 5-9 % faster than 13-16 waves on 3200- and 1024-row
+    // layers, K = 3200 to 8640)
+    KS = KS > 10 ? 10 : KS;
     KS = KS > nsteps ? nsteps : KS;
     dim3 grid(static_cast<unsigned>(groups), static_cast<unsigned>(tgroups));
     dim3 block(static_cast<unsigned>(KS * 64));
