@@ -75,7 +75,7 @@ typedef enum {
     BITLINEAR_ALGO_AUTO = 0,        /* pick by M and layout                                 */
     BITLINEAR_ALGO_GEMV_ADDSUB = 1, /* vector-ALU add/subtract GEMV, M <= 16                */
     BITLINEAR_ALGO_GEMV_MFMA = 2,   /* 16-token int8 matrix-core tiles, any M (token groups) */
-    BITLINEAR_ALGO_GEMM_MFMA = 3    /* LDS-tiled int8 matrix-core GEMM, any M (i2 layout)   */
+    BITLINEAR_ALGO_GEMM_MFMA = 3    /* LDS-tiled int8 matrix-core GEMM: i2 and b3 any M, b1 M > 16 */
 } bitlinear_algo_t;
 
 /* Static description of a status code (never NULL). */
@@ -116,8 +116,9 @@ int64_t bitlinear_quantize_weights_workspace_bytes(int64_t N, int64_t K);
 
 /*
  * Workspace bytes bitlinear_forward needs for these sizes (-1 if invalid).
- * Covers the staged int8 activations of the fused quantiser (x_dtype F32 or
- * BF16) and any split-K partial sums.
+ * Covers the staged int8 activations and beta of the fused quantiser (x_dtype
+ * F32 or BF16) and, for b1 weights with M > 16, their i2 rewrite that the
+ * GEMM reads.
  */
 int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int layout, int x_dtype);
 
@@ -125,8 +126,8 @@ int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int l
  * The product algorithm bitlinear_forward (algo AUTO) runs for these sizes:
  * BITLINEAR_ALGO_GEMV_MFMA for pre-tiled input, for M <= 16, and for larger
  * M when the GEMM would launch too few workgroup tiles to fill the GPU;
- * BITLINEAR_ALGO_GEMM_MFMA otherwise (b3 and b1 weights are first rewritten
- * as i2 in the workspace).  Returns -1 for invalid
+ * BITLINEAR_ALGO_GEMM_MFMA otherwise (it decodes b3 weights itself; b1
+ * weights are first rewritten as i2 in the workspace).  Returns -1 for invalid
  * sizes, layout or dtype.  Host-only; enqueues nothing.
  */
 int bitlinear_auto_algo(int64_t M, int64_t N, int64_t K, int layout, int x_dtype);

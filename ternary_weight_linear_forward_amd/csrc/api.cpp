@@ -70,19 +70,25 @@ int64_t staged_xq_bytes(int64_t M, int64_t K, int layout)
     return round_up(rm > tl ? rm : tl, 256);
 }
 
-
 // Workspace of one forward: the quantised activations and beta (bf16/fp32
-// input), then, for base-3 weights and more than 16 tokens, room for the
-// weights rewritten in the i2 layout that the GEMM reads.
+// input), then, with more than 16 tokens and weights the GEMM rewrites as i2
+// (gemm_rewrites), room for that rewrite.
 int64_t staging_bytes(int64_t M, int64_t K, int layout, int x_dtype)
 {
     if (x_dtype == BITLINEAR_I8 || x_dtype == BITLINEAR_I8_TILED) return 0;
     return staged_xq_bytes(M, K, layout) + round_up(4 * M, 256);
 }
+// The GEMM reads i2 weights or decodes b3 itself; b1 weights, and b3 weights
+// of shapes where the decode would repeat over many token blocks, are
+// rewritten as i2 first.
+bool gemm_rewrites(int64_t M, int64_t N, int layout)
+{
+    return layout == BITLINEAR_LAYOUT_B1 || (layout == BITLINEAR_LAYOUT_B3 && !bl::gemm_b3_native(M, N));
+}
 int64_t transcode_bytes(int64_t M, int64_t N, int64_t K, int layout)
 {
-    return layout != BITLINEAR_LAYOUT_I2 && M > 16 ? round_up(bitlinear_packed_bytes(N, K, BITLINEAR_LAYOUT_I2), 256)
-                                                   : 0;
+    return M > 16 && gemm_rewrites(M, N, layout) ? round_up(bitlinear_packed_bytes(N, K, BITLINEAR_LAYOUT_I2), 256)
+                                                 : 0;
 }
 
 // The product kernel of algo AUTO (sizes already validated).
@@ -159,13 +165,13 @@ const char *bitlinear_product_kernel(int64_t M, int64_t N, int64_t K, int layout
         return nullptr;
     if (algo == BITLINEAR_ALGO_AUTO) algo = auto_algo(M, N, layout, x_dtype);
     if ((algo == BITLINEAR_ALGO_GEMV_ADDSUB && (M > 16 || layout != BITLINEAR_LAYOUT_I2)) ||
-        (algo == BITLINEAR_ALGO_GEMM_MFMA && layout != BITLINEAR_LAYOUT_I2 && M <= 16) ||
+        (algo == BITLINEAR_ALGO_GEMM_MFMA && layout == BITLINEAR_LAYOUT_B1 && M <= 16) ||
         (x_dtype == BITLINEAR_I8_TILED && algo != BITLINEAR_ALGO_GEMV_MFMA))
         return nullptr;
     if (algo == BITLINEAR_ALGO_GEMV_ADDSUB) {
         bl::gemv_addsub_kernel_name(M, name, sizeof name);
     } else if (algo == BITLINEAR_ALGO_GEMM_MFMA) {
-        bl::gemm_kernel_name(M, N, name, sizeof name);
+        bl::gemm_kernel_name(gemm_rewrites(M, N, layout) ? BITLINEAR_LAYOUT_I2 : layout, M, N, name, sizeof name);
     } else {
         // the same choice of activation staging as bitlinear_forward_algo
         const bool tiled = x_dtype == BITLINEAR_I8_TILED ||
@@ -309,7 +315,7 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
     if (algo == BITLINEAR_ALGO_AUTO) algo = auto_algo(M, N, layout, x_dtype);
     if (algo == BITLINEAR_ALGO_GEMV_ADDSUB && (M > 16 || layout != BITLINEAR_LAYOUT_I2))
         return BITLINEAR_ERR_UNSUPPORTED;
-    if (algo == BITLINEAR_ALGO_GEMM_MFMA && layout != BITLINEAR_LAYOUT_I2 && M <= 16) return BITLINEAR_ERR_UNSUPPORTED;
+    if (algo == BITLINEAR_ALGO_GEMM_MFMA && layout == BITLINEAR_LAYOUT_B1 && M <= 16) return BITLINEAR_ERR_UNSUPPORTED;
     if (x_dtype == BITLINEAR_I8_TILED && algo != BITLINEAR_ALGO_GEMV_MFMA) return BITLINEAR_ERR_UNSUPPORTED;
 
     (void)hipGetLastError();
@@ -355,8 +361,8 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
     case BITLINEAR_ALGO_GEMV_ADDSUB: e = bl::launch_gemv_addsub(a, st); break;
     case BITLINEAR_ALGO_GEMV_MFMA: e = bl::launch_gemv_mfma(a, st); break;
     default:
-        if (layout != BITLINEAR_LAYOUT_I2) {
-            // the GEMM reads i2: rewrite the b3 / b1 weights into the workspace first
+        if (gemm_rewrites(M, N, layout)) {
+            // rewrite the weights as i2 into the workspace first
             uint8_t *p2 = static_cast<uint8_t *>(ws) + staging_bytes(M, K, layout, x_dtype);
             e = layout == BITLINEAR_LAYOUT_B3 ? bl::launch_b3_to_i2(P, N, K, p2, st) : bl::launch_b1_to_i2(P, N, K, p2, st);
             if (e != hipSuccess) return BITLINEAR_ERR_LAUNCH;

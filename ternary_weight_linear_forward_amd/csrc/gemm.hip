@@ -21,6 +21,19 @@
 //    copied as they are (BN/16 tiles x 2 k-blocks = BN * 32 bytes).  Each lane
 //    reads the one 32-bit word holding its 16 weights of an operand and
 //    unpacks it with four v_perm_b32.
+//
+// Base-3 weights (k_gemm_mfma_b3) are decoded in the same place, so the GEMM
+// reads the 20 % smaller b3 bytes and nothing is rewritten first.  A stage
+// covers two 80-weight k-blocks (160 k) and lane half kh (lanes 32 kh ..
+// 32 kh + 31) owns block kh of it: the lane reads its weight row's 16-byte
+// chunk row with one 128-bit LDS read, and digit t of those 16 bytes is the
+// 16 consecutive weights of MFMA k-step t (t = 0..4), in natural k order.  So
+// the activations stay row-major: 160 bytes per row per stage, copied as
+// consecutive 16-byte units (row stride 160 bytes spreads a 32-row operand
+// read over the banks without a swizzle), and lane (token, kh) takes unit
+// 5 kh + t of its row at k-step t.  Digits come from the fixed-point byte
+// (H_t = floor(u 3^t / 256), digit t = H_(t+1) - 3 H_t) and become signed
+// bytes with one v_perm_b32 each.
 // Only s_barrier (no memory fence) separates the stages; the explicit vmcnt
 // wait before it covers this wave's own copies of the stage, and the barrier
 // then covers every wave's.
@@ -33,6 +46,7 @@ namespace bl {
 
 namespace {
 constexpr int KSTEP = 128;              // k per stage half: two 64-weight k-blocks
+constexpr int B3_ROW = 160;             // b3: k per stage, two 80-weight k-blocks
 constexpr int LDS_RING_BYTES = 150 * 1024; // LDS given to the stage ring (of 160 KB)
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -87,31 +101,35 @@ __device__ __forceinline__ void stage_barrier()
     asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int S>
-__global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__restrict__ P, int64_t KB,
-                                                               int64_t NT, const float *__restrict__ gamma_p,
-                                                               const int8_t *__restrict__ Xq, int64_t ldq,
-                                                               const float *__restrict__ beta, int64_t M,
-                                                               int64_t N, int64_t K, void *__restrict__ Y,
-                                                               int y_dtype, int64_t ldy, int n_major)
+template <int LAYOUT, int BM, int BN, int WM, int WN, int S>
+__device__ __forceinline__ void gemm_body(const uint8_t *__restrict__ P, int64_t KB, int64_t NT,
+                                          const float *__restrict__ gamma_p, const int8_t *__restrict__ Xq,
+                                          int64_t ldq, const float *__restrict__ beta, int64_t M, int64_t N,
+                                          int64_t K, void *__restrict__ Y, int y_dtype, int64_t ldy, int n_major)
 {
+    constexpr bool B3 = LAYOUT == LAYOUT_B3;
+    static_assert(LAYOUT == LAYOUT_I2 || (B3 && S == 1), "i2 with S halves of 128 k, or b3 with 160 k");
     constexpr int NW = WM * WN;                // waves
     constexpr int MI = BM / WM / 32;           // 32-token MFMA tiles per wave
     constexpr int NI = BN / WN / 32;           // 32-row MFMA tiles per wave
-    constexpr int KS_ = KSTEP * S;             // k per stage: S halves of 128
-    constexpr int KK = 4 * S;                  // 32-k MFMA steps per stage
-    constexpr int A_BYTES = BM * KS_;          // activation bytes per stage: [S][BM][128]
+    constexpr int ROW = B3 ? B3_ROW : KSTEP;   // activation bytes per row per stage half
+    constexpr int KS_ = ROW * S;               // k per stage
+    constexpr int KK = B3 ? 5 : 4 * S;         // 32-k MFMA steps per stage
+    constexpr int NWORD = B3 ? 4 : KK;         // packed words per weight operand row per stage
+    constexpr int A_BYTES = BM * KS_;          // activation bytes per stage: [S][BM][ROW]
     constexpr int B_BYTES = BN * 32 * S;       // packed weight bytes per stage (2S k-blocks)
     constexpr int STAGE = A_BYTES + B_BYTES;
-    constexpr int A_ROWS_W = BM / NW;          // activation rows copied by one wave
-    constexpr int A_RB = A_ROWS_W / 8;         // 1 KB copies (8 rows of 128 B) per wave per half
-    constexpr int A_INST = A_RB * S;           // ... per stage
+    constexpr int A_ROWS_W = BM / NW;          // i2: activation rows copied by one wave
+    constexpr int A_RB = A_ROWS_W / 8;         // i2: 1 KB copies (8 rows of 128 B) per wave per half
+    constexpr int A_COPIES = A_BYTES / 1024;   // b3: 1 KB copies per stage, dealt round-robin
+    constexpr int A_INST = B3 ? (A_COPIES + NW - 1) / NW : A_RB * S; // copies per wave per stage
     // weight copies: 16 bytes per lane when every wave gets whole 1 KB copies, else 4
     constexpr int B_CP = (B_BYTES % (1024 * NW) == 0) ? 16 : 4;
     constexpr int B_INST = B_BYTES / (64 * B_CP) / NW;
     constexpr int NST = LDS_RING_BYTES / STAGE < 8 ? LDS_RING_BYTES / STAGE : 8; // ring depth
     constexpr int LOADS = A_INST + B_INST;     // copies per wave per stage
     static_assert(MI >= 1 && NI >= 1 && A_INST >= 1 && B_INST >= 1 && NST >= 3, "tile shape");
+    static_assert(!B3 || A_COPIES * 1024 == A_BYTES, "b3 activation stage in whole 1 KB copies");
     static_assert(B_INST * NW * 64 * B_CP == B_BYTES && (NST - 1) * LOADS < 64, "copy plan");
     __shared__ __attribute__((aligned(16))) int8_t lds[NST * STAGE];
 
@@ -148,11 +166,24 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
     // Activation copy j of this wave: k-half h = j / A_RB, row
     // wave*A_ROWS_W + 8 (j % A_RB) + lane/8, LDS slot lane%8 of the half's
     // 128-byte row, which holds the row's 16-byte unit (lane%8) ^ swz(row).
-    int a_voff[A_INST];
+    //
+    // b3: copy c (c = wave * A_INST + j, taken modulo A_COPIES: the last waves
+    // repeat a few copies, which write the same bytes again) moves units
+    // 64 c + lane of the stage, unit U = 10 row + g holding bytes 16 g .. 16 g
+    // + 15 of the row's 160.
+    int a_voff[A_INST], a_dst[A_INST];
 #pragma unroll
     for (int j = 0; j < A_INST; ++j) {
-        const int row = wave * A_ROWS_W + 8 * (j % A_RB) + (lane >> 3);
-        a_voff[j] = static_cast<int>(row * ldq) + (j / A_RB) * KSTEP + ((lane & 7) ^ a_swz(row)) * 16;
+        if constexpr (B3) {
+            const int c = (wave * A_INST + j) % A_COPIES;
+            const int u = c * 64 + lane;
+            a_voff[j] = static_cast<int>((u / 10) * ldq) + (u % 10) * 16;
+            a_dst[j] = c * 1024;
+        } else {
+            const int row = wave * A_ROWS_W + 8 * (j % A_RB) + (lane >> 3);
+            a_voff[j] = static_cast<int>(row * ldq) + (j / A_RB) * KSTEP + ((lane & 7) ^ a_swz(row)) * 16;
+            a_dst[j] = (j / A_RB) * BM * KSTEP + (wave * A_ROWS_W + 8 * (j % A_RB)) * KSTEP;
+        }
     }
     // Weight copy j of this wave covers stage chunk c (c = kb2 * BN/16 + tile,
     // 256 bytes = 16 rows x 16 bytes): with 16-byte copies chunks
@@ -185,10 +216,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
         const int nb = static_cast<int>(b_bytes > kb ? b_bytes - kb : 0);
 #pragma unroll
         for (int j = 0; j < A_INST; ++j)
-            buffer_copy_to_lds<16>(a_base + ka, na,
-                                   (lds_void_t *)(sbase + (j / A_RB) * BM * KSTEP +
-                                                  (wave * A_ROWS_W + 8 * (j % A_RB)) * KSTEP),
-                                   a_voff[j]);
+            buffer_copy_to_lds<16>(a_base + ka, na, (lds_void_t *)(sbase + a_dst[j]), a_voff[j]);
 #pragma unroll
         for (int j = 0; j < B_INST; ++j)
             buffer_copy_to_lds<B_CP>(b_base + kb, nb, (lds_void_t *)(sbase + A_BYTES + (wave * B_INST + j) * 64 * B_CP),
@@ -202,13 +230,17 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
         const int row = wm * (BM / WM) + a * 32 + l32;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-            a_off[a][kk] = (kk / 4) * BM * KSTEP + row * KSTEP + (((2 * (kk % 4) + kh) ^ a_swz(row)) * 16);
+            a_off[a][kk] = B3 ? (row * 10 + 5 * kh + kk) * 16
+                              : (kk / 4) * BM * KSTEP + row * KSTEP + (((2 * (kk % 4) + kh) ^ a_swz(row)) * 16);
     }
+    // i2: word (kk % 2) * 2 + kh of the row in k-block kk / 2 (added in
+    // read_ops); b3: the whole chunk row of k-block kh
     int b_off[NI];
 #pragma unroll
     for (int b = 0; b < NI; ++b) {
         const int nl = wn * (BN / WN) + b * 32 + l32;
-        b_off[b] = A_BYTES + (nl / 16) * 256 + (nl % 16) * 16 + 4 * kh;
+        b_off[b] = B3 ? A_BYTES + (kh * (BN / 16) + nl / 16) * 256 + (nl % 16) * 16
+                      : A_BYTES + (nl / 16) * 256 + (nl % 16) * 16 + 4 * kh;
     }
 
     // A wave with fewer than 4 output tiles keeps SPLIT accumulators per tile
@@ -229,8 +261,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
     // Operands of one stage, read from LDS one stage ahead of their MFMAs so
     // that LDS latency overlaps the matrix work of the stage before.
     struct Ops {
-        v4i a[MI][KK];       // activation operand of tile a, k-step kk
-        uint32_t w[NI][KK];  // packed word of B tile b, k-step kk (16 weights)
+        v4i a[MI][KK];         // activation operand of tile a, k-step kk
+        uint32_t w[NI][NWORD]; // i2: packed word of B tile b, k-step kk; b3: the chunk row's words
     };
     auto read_ops = [&](int buf, Ops &o) {
         const int8_t *sbase = lds + buf * STAGE;
@@ -238,29 +270,63 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
         for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
             for (int a = 0; a < MI; ++a) o.a[a][kk] = *reinterpret_cast<const v4i *>(sbase + a_off[a][kk]);
-        // word of k-block kk/2, 16-weight group (kk % 2) * 2 + kh
+        if constexpr (B3) {
 #pragma unroll
-        for (int b = 0; b < NI; ++b)
+            for (int b = 0; b < NI; ++b) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(sbase + b_off[b]);
+                o.w[b][0] = v.x;
+                o.w[b][1] = v.y;
+                o.w[b][2] = v.z;
+                o.w[b][3] = v.w;
+            }
+        } else {
+            // word of k-block kk/2, 16-weight group (kk % 2) * 2 + kh
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                o.w[b][kk] = *reinterpret_cast<const uint32_t *>(sbase + b_off[b] + (kk / 2) * (BN / 16) * 256 +
-                                                                 (kk % 2) * 8);
+            for (int b = 0; b < NI; ++b)
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    o.w[b][kk] = *reinterpret_cast<const uint32_t *>(sbase + b_off[b] + (kk / 2) * (BN / 16) * 256 +
+                                                                     (kk % 2) * 8);
+        }
     };
     // kb_left: k-blocks of the stage that exist (>= 2S except in the last
     // stage); the words of the others become T = 0
     auto mma = [&](const Ops &o, int kb_left) {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            v4i bf[NI];
+        if constexpr (B3) {
+            // k-block kh exists unless kb_left == 1; a missing block's words
+            // become the all-zero-weight word before decoding
+            v4i bf[NI][5];
 #pragma unroll
             for (int b = 0; b < NI; ++b)
-                bf[b] = gemm_i2_word_signed((kk < 2 || kk / 2 < kb_left) ? o.w[b][kk] : I2_ZERO_WORD);
 #pragma unroll
-            for (int a = 0; a < MI; ++a)
+                for (int q = 0; q < 4; ++q) {
+                    const B3Digits dg = b3_word_digits(kh < kb_left ? o.w[b][q] : B3_ZERO_WORD);
+#pragma unroll
+                    for (int t = 0; t < 5; ++t)
+                        bf[b][t][q] = static_cast<int>(__builtin_amdgcn_perm(0u, 0x000100ffu, dg.d[t]));
+                }
+#pragma unroll
+            for (int t = 0; t < 5; ++t)
+#pragma unroll
+                for (int a = 0; a < MI; ++a)
+#pragma unroll
+                    for (int b = 0; b < NI; ++b)
+                        acc[a][b][t % SPLIT] = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[a][t], bf[b][t],
+                                                                                     acc[a][b][t % SPLIT], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                v4i bf[NI];
 #pragma unroll
                 for (int b = 0; b < NI; ++b)
-                    acc[a][b][kk % SPLIT] = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[a][kk], bf[b],
-                                                                                  acc[a][b][kk % SPLIT], 0, 0, 0);
+                    bf[b] = gemm_i2_word_signed((kk < 2 || kk / 2 < kb_left) ? o.w[b][kk] : I2_ZERO_WORD);
+#pragma unroll
+                for (int a = 0; a < MI; ++a)
+#pragma unroll
+                    for (int b = 0; b < NI; ++b)
+                        acc[a][b][kk % SPLIT] = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[a][kk], bf[b],
+                                                                                      acc[a][b][kk % SPLIT], 0, 0, 0);
+            }
         }
     };
 
@@ -338,22 +404,49 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
         store_all([&](int64_t i, int v, float) { static_cast<int *>(Y)[i] = v; });
 }
 
-namespace {
 template <int BM, int BN, int WM, int WN, int S>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__restrict__ P, int64_t KB,
+                                                               int64_t NT, const float *__restrict__ gamma_p,
+                                                               const int8_t *__restrict__ Xq, int64_t ldq,
+                                                               const float *__restrict__ beta, int64_t M,
+                                                               int64_t N, int64_t K, void *__restrict__ Y,
+                                                               int y_dtype, int64_t ldy, int n_major)
+{
+    gemm_body<LAYOUT_I2, BM, BN, WM, WN, S>(P, KB, NT, gamma_p, Xq, ldq, beta, M, N, K, Y, y_dtype, ldy, n_major);
+}
+
+template <int BM, int BN, int WM, int WN, int S>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_b3(const uint8_t *__restrict__ P, int64_t KB,
+                                                               int64_t NT, const float *__restrict__ gamma_p,
+                                                               const int8_t *__restrict__ Xq, int64_t ldq,
+                                                               const float *__restrict__ beta, int64_t M,
+                                                               int64_t N, int64_t K, void *__restrict__ Y,
+                                                               int y_dtype, int64_t ldy, int n_major)
+{
+    gemm_body<LAYOUT_B3, BM, BN, WM, WN, S>(P, KB, NT, gamma_p, Xq, ldq, beta, M, N, K, Y, y_dtype, ldy, n_major);
+}
+
+namespace {
+template <int LAYOUT, int BM, int BN, int WM, int WN, int S>
 hipError_t launch_tile(const GemvArgs &a, hipStream_t stream)
 {
     const int64_t NT = (a.N + 15) / 16;
-    const int64_t KB = (a.K + 63) / 64;
+    const int64_t KB = LAYOUT == LAYOUT_B3 ? (a.K + 79) / 80 : (a.K + 63) / 64;
     const int64_t nN = (a.N + BN - 1) / BN, nM = (a.M + BM - 1) / BM;
     dim3 grid(static_cast<unsigned>(nN), static_cast<unsigned>(nM));
     // bytes one XCD reads per tile order: M-block-major: its share of the
     // activation row blocks plus every weight tile; N-block-major: its share of
     // the weight tiles plus every activation row
-    const double act = static_cast<double>(a.M) * a.K, wts = static_cast<double>(a.N) * a.K / 4;
+    const double act = static_cast<double>(a.M) * a.K,
+                 wts = static_cast<double>(a.N) * a.K / (LAYOUT == LAYOUT_B3 ? 5 : 4);
     const double m_major = act / 8 + wts, n_major = wts / 8 + act;
     const int nmaj = (nM > 1 && n_major < m_major) ? 1 : 0;
-    hipLaunchKernelGGL((k_gemm_mfma_i2<BM, BN, WM, WN, S>), grid, dim3(64 * WM * WN), 0, stream, a.P, KB, NT, a.gamma,
-                       a.Xq, a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy, nmaj);
+    if constexpr (LAYOUT == LAYOUT_B3)
+        hipLaunchKernelGGL((k_gemm_mfma_b3<BM, BN, WM, WN, S>), grid, dim3(64 * WM * WN), 0, stream, a.P, KB, NT,
+                           a.gamma, a.Xq, a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy, nmaj);
+    else
+        hipLaunchKernelGGL((k_gemm_mfma_i2<BM, BN, WM, WN, S>), grid, dim3(64 * WM * WN), 0, stream, a.P, KB, NT,
+                           a.gamma, a.Xq, a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy, nmaj);
     return hipGetLastError();
 }
 } // namespace
@@ -366,20 +459,24 @@ namespace {
 struct GemmTile {
     int bm, bn, wm, wn, s; // tile, wave grid, k halves (of 128) per stage
     double rate;
+    bool b3; // offered for b3 weights (the b3 decode of a 128 x 128 wave tile spills registers)
 };
-constexpr GemmTile kTiles[] = {
-    {256, 256, 2, 2, 1, 2.1}, {128, 256, 2, 4, 1, 1.95}, {128, 128, 2, 2, 1, 1.5}, {32, 128, 1, 4, 1, 1.1}};
+constexpr GemmTile kTiles[] = {{256, 256, 2, 2, 1, 2.1, false},
+                               {128, 256, 2, 4, 1, 1.95, true},
+                               {128, 128, 2, 2, 1, 1.5, true},
+                               {32, 128, 1, 4, 1, 1.1, true}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int64_t kCUs = 256;
 
-int best_tile(int64_t M, int64_t N)
+int best_tile(int layout, int64_t M, int64_t N)
 {
-    int best = 0;
+    int best = -1;
     double best_cost = 0;
     for (int i = 0; i < kNumTiles; ++i) {
+        if (layout == LAYOUT_B3 && !kTiles[i].b3) continue;
         const int64_t t = ((M + kTiles[i].bm - 1) / kTiles[i].bm) * ((N + kTiles[i].bn - 1) / kTiles[i].bn);
         const double cost = static_cast<double>((t + kCUs - 1) / kCUs) * kTiles[i].bm * kTiles[i].bn / kTiles[i].rate;
-        if (i == 0 || cost < best_cost) best = i, best_cost = cost;
+        if (best < 0 || cost < best_cost) best = i, best_cost = cost;
     }
     return best;
 }
@@ -388,7 +485,9 @@ template <int I>
 hipError_t launch_entry(const GemvArgs &a, hipStream_t stream)
 {
     constexpr GemmTile t = kTiles[I];
-    return launch_tile<t.bm, t.bn, t.wm, t.wn, t.s>(a, stream);
+    if constexpr (t.b3)
+        if (a.layout == LAYOUT_B3) return launch_tile<LAYOUT_B3, t.bm, t.bn, t.wm, t.wn, t.s>(a, stream);
+    return launch_tile<LAYOUT_I2, t.bm, t.bn, t.wm, t.wn, t.s>(a, stream);
 }
 } // namespace
 
@@ -398,16 +497,23 @@ int64_t gemm_tiles(int64_t M, int64_t N)
     return ((M + 63) / 64) * ((N + 127) / 128);
 }
 
-void gemm_kernel_name(int64_t M, int64_t N, char *buf, size_t n)
+bool gemm_b3_native(int64_t M, int64_t N)
 {
-    const GemmTile &t = kTiles[best_tile(M, N)];
-    snprintf(buf, n, "bl::k_gemm_mfma_i2<%d, %d, %d, %d, %d>", t.bm, t.bn, t.wm, t.wn, t.s);
+    const GemmTile &t = kTiles[best_tile(LAYOUT_B3, M, N)];
+    return (M + t.bm - 1) / t.bm <= 2;
+}
+
+void gemm_kernel_name(int layout, int64_t M, int64_t N, char *buf, size_t n)
+{
+    const GemmTile &t = kTiles[best_tile(layout, M, N)];
+    snprintf(buf, n, "bl::k_gemm_mfma_%s<%d, %d, %d, %d, %d>", layout == LAYOUT_B3 ? "b3" : "i2", t.bm, t.bn, t.wm,
+             t.wn, t.s);
 }
 
 hipError_t launch_gemm_mfma(const GemvArgs &a, hipStream_t stream)
 {
     static_assert(kNumTiles == 4, "one case per tile shape");
-    switch (best_tile(a.M, a.N)) {
+    switch (best_tile(a.layout, a.M, a.N)) {
     case 0: return launch_entry<0>(a, stream);
     case 1: return launch_entry<1>(a, stream);
     case 2: return launch_entry<2>(a, stream);

@@ -57,10 +57,17 @@ struct GemvArgs {
 
 hipError_t launch_gemv_addsub(const GemvArgs &a, hipStream_t stream);
 hipError_t launch_gemv_mfma(const GemvArgs &a, hipStream_t stream);
-hipError_t launch_gemm_mfma(const GemvArgs &a, hipStream_t stream);
+hipError_t launch_gemm_mfma(const GemvArgs &a, hipStream_t stream); // i2 or b3 weights
 // Size of an M x N product in 64 x 128 output tiles: below about 128 of them
 // the matrix-core GEMV is faster than the GEMM (measured on the 70B layers).
 int64_t gemm_tiles(int64_t M, int64_t N);
+// Whether the GEMM decodes b3 weights itself for this shape.  Every M-block of
+// a workgroup tile decodes its weight tiles again (about 30 VALU instructions
+// per 20 weights), so with more than two M-blocks one rewrite of the weights
+// as i2 (a single pass) and the i2 GEMM are faster (measured on the 70B
+// layers: gate at 64 tokens 45 us native against 60 us, q and down at 176
+// tokens the other way round).
+bool gemm_b3_native(int64_t M, int64_t N);
 
 // Straight-through-estimator gradients (backward.hip): dX from i2-packed
 // weights, dW from the forward's int8 activations and beta.
@@ -73,6 +80,6 @@ hipError_t launch_bwd_dw(const int8_t *Xq, int64_t ldq, const float *beta, int64
 // product launch runs for a shape.
 void gemv_kernel_name(int layout, int64_t M, int64_t N, int64_t K, bool tiled, char *buf, size_t n);
 void gemv_addsub_kernel_name(int64_t M, char *buf, size_t n);
-void gemm_kernel_name(int64_t M, int64_t N, char *buf, size_t n);
+void gemm_kernel_name(int layout, int64_t M, int64_t N, char *buf, size_t n);
 
 } // namespace bl

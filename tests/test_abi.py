@@ -139,7 +139,7 @@ def fw(**kw):
     (dict(ws=C), bl.ERR_INVALID_ARG),                               # workspace overlaps X
     (dict(algo=bl.ALGO_GEMV_ADDSUB, M=17), bl.ERR_UNSUPPORTED),
     (dict(algo=bl.ALGO_GEMV_ADDSUB, layout=bl.LAYOUT_B3), bl.ERR_UNSUPPORTED),
-    (dict(algo=bl.ALGO_GEMM_MFMA, layout=bl.LAYOUT_B3), bl.ERR_UNSUPPORTED),  # b3 GEMM needs M > 16
+    (dict(algo=bl.ALGO_GEMM_MFMA, layout=bl.LAYOUT_B1), bl.ERR_UNSUPPORTED),  # b1 GEMM needs M > 16
 ])
 def test_forward_rejects(kw, status):
     assert fw(**kw) == status
@@ -208,8 +208,8 @@ def test_auto_algo_dispatch():
     for M in (1, 4, 16):
         assert f(M, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMV_MFMA
     assert f(2048, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMM_MFMA
-    assert f(2048, 3200, 3200, bl.LAYOUT_B3, bl.BF16) == bl.ALGO_GEMM_MFMA  # through an i2 rewrite
-    assert f(2048, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == bl.ALGO_GEMM_MFMA
+    assert f(2048, 3200, 3200, bl.LAYOUT_B3, bl.BF16) == bl.ALGO_GEMM_MFMA  # decoded inside the GEMM
+    assert f(2048, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == bl.ALGO_GEMM_MFMA  # through an i2 rewrite
     assert f(16, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == bl.ALGO_GEMV_MFMA
     assert f(2048, 3200, 3200, bl.LAYOUT_I2, bl.I8_TILED) == bl.ALGO_GEMV_MFMA
     assert f(176, 1024, 8192, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMV_MFMA  # 16 tiles: GPU mostly idle
@@ -235,7 +235,16 @@ def test_product_kernel_names():
     assert f(64, 8192, 8192, bl.LAYOUT_I2, bl.BF16).startswith("bl::k_gemv_mfma<")  # too few tiles
     assert f(150, 6000, 300, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemm_mfma_i2<32, 128, 1, 4, 1>"
     assert f(3, 64, 64, bl.LAYOUT_I2, bl.BF16, bl.ALGO_GEMV_ADDSUB) == "bl::k_gemv_addsub<4>"
-    assert f(3, 64, 64, bl.LAYOUT_B3, bl.BF16, bl.ALGO_GEMM_MFMA) is None
+    assert f(3, 64, 64, bl.LAYOUT_B3, bl.BF16, bl.ALGO_GEMM_MFMA) == "bl::k_gemm_mfma_b3<32, 128, 1, 4, 1>"
+    assert f(3, 64, 64, bl.LAYOUT_B1, bl.BF16, bl.ALGO_GEMM_MFMA) is None
+    # b3 is decoded in the GEMM (tiles other than 256 x 256) when a weight tile
+    # meets at most two token blocks, else rewritten as i2; b1 always is
+    assert f(64, 28672, 8192, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemm_mfma_b3<32, 128, 1, 4, 1>"
+    assert f(176, 28672, 8192, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemm_mfma_b3<128, 256, 2, 4, 1>"
+    assert f(176, 8192, 8192, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemm_mfma_i2<32, 128, 1, 4, 1>"
+    assert f(2048, 3200, 3200, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemm_mfma_i2<128, 256, 2, 4, 1>"
+    assert f(4000, 4000, 130, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemm_mfma_i2<256, 256, 2, 2, 1>"
+    assert f(2048, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == "bl::k_gemm_mfma_i2<128, 256, 2, 4, 1>"
     assert f(1, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == "bl::k_gemv_mfma<2, 1, 1, false>"
     assert f(3, 64, 64, bl.LAYOUT_B1, bl.BF16, bl.ALGO_GEMV_ADDSUB) is None
     assert f(0, 64, 64, bl.LAYOUT_I2, bl.BF16) is None
@@ -263,15 +272,17 @@ def test_backward_rejects():
     assert bl.bitlinear_backward_dw(**{**dw, "beta": C + 2}) == bl.ERR_INVALID_ARG
 
 
-def test_b3_gemm_workspace():
-    """Base-3 weights with more than 16 tokens: the workspace also holds the
-    weights rewritten in the i2 layout for the GEMM."""
-    M, N, K = 176, 1000, 3000
-    base = bl.bitlinear_forward_workspace_bytes(M, N, K, bl.LAYOUT_I2, bl.BF16)
-    b3 = bl.bitlinear_forward_workspace_bytes(M, N, K, bl.LAYOUT_B3, bl.BF16)
+def test_gemm_weight_workspace():
+    """Workspace for the weights: none where the GEMM decodes b3 itself (at
+    most two token blocks per weight tile); room for the i2 rewrite of b3
+    weights with more token blocks and of b1 weights, with more than 16
+    tokens."""
+    N, K = 1000, 3000
+    ws = bl.bitlinear_forward_workspace_bytes
     i2 = bl.bitlinear_packed_bytes(N, K, bl.LAYOUT_I2)
-    assert b3 >= base and b3 - bl.bitlinear_forward_workspace_bytes(M, N, K, bl.LAYOUT_B3, bl.I8) < b3
-    assert bl.bitlinear_forward_workspace_bytes(M, N, K, bl.LAYOUT_B3, bl.I8) >= i2
-    assert bl.bitlinear_forward_workspace_bytes(16, N, K, bl.LAYOUT_B3, bl.I8) == 0
-    assert bl.bitlinear_forward_workspace_bytes(M, N, K, bl.LAYOUT_B1, bl.I8) >= i2
+    assert ws(64, N, K, bl.LAYOUT_B3, bl.I8) == 0
+    assert ws(64, N, K, bl.LAYOUT_B3, bl.BF16) == ws(64, 1, K, bl.LAYOUT_B3, bl.BF16)  # nothing sized by N
+    assert ws(176, N, K, bl.LAYOUT_B3, bl.I8) >= i2
+    assert ws(16, N, K, bl.LAYOUT_B3, bl.I8) == 0
+    assert ws(64, N, K, bl.LAYOUT_B1, bl.I8) >= i2
     assert bl.bitlinear_forward_workspace_bytes(16, N, K, bl.LAYOUT_B1, bl.I8) == 0

@@ -86,7 +86,7 @@ def test_tiny_config_full_pipeline():
     for name, lay in LAYOUTS.items():
         P = bl.pack(T, lay)
         assert np.array_equal(to_host(P), oracle.pack(t_ref, lay))
-        for algo in ((bl.ALGO_AUTO, bl.ALGO_GEMV_MFMA) if name == "b3" else
+        for algo in ((bl.ALGO_AUTO, bl.ALGO_GEMV_MFMA, bl.ALGO_GEMM_MFMA) if name == "b3" else
                      (bl.ALGO_AUTO, bl.ALGO_GEMV_ADDSUB, bl.ALGO_GEMV_MFMA, bl.ALGO_GEMM_MFMA)):
             acc = to_host(bl.forward(P, lay, gamma, to_dev(x), layer.N, layer.K, y_dtype=torch.int32, algo=algo))
             assert np.array_equal(acc, ref["acc"])

@@ -163,7 +163,7 @@ FWD_SHAPES = [  # (M, N, K)
 ]
 ALGOS_SMALL = [("addsub", bl.ALGO_GEMV_ADDSUB, "i2"), ("mfma_gemv", bl.ALGO_GEMV_MFMA, "i2"),
                ("mfma_gemv", bl.ALGO_GEMV_MFMA, "b3"), ("gemm", bl.ALGO_GEMM_MFMA, "i2"),
-               ("auto", bl.ALGO_AUTO, "i2"), ("auto", bl.ALGO_AUTO, "b3")]
+               ("gemm", bl.ALGO_GEMM_MFMA, "b3"), ("auto", bl.ALGO_AUTO, "i2"), ("auto", bl.ALGO_AUTO, "b3")]
 
 
 def run_forward_case(M, N, K, algo, layout, seed, x_kind="bf16", y_kinds=("i32", "f32", "bf16")):
@@ -215,8 +215,54 @@ def test_gemm_tile_shapes(M, N, K):
     tiles, ragged in M and N; an odd number of k-blocks ends in a half stage)."""
     log("forward gemm tiles", M, N, K)
     run_forward_case(M, N, K, bl.ALGO_GEMM_MFMA, "i2", seed=M + 7 * N + K, y_kinds=("i32", "f32"))
-    if M * N <= 1100 * 5000:  # base-3 weights through the i2 rewrite
+    if M * N <= 1100 * 5000:  # base-3 weights, decoded inside the GEMM
         run_forward_case(M, N, K, bl.ALGO_GEMM_MFMA, "b3", seed=M + 7 * N + K + 1, y_kinds=("i32",))
+
+
+# (M, N, K) for the base-3 GEMM, whose stage is two 80-weight k-blocks:
+# one block (a half stage), exactly one stage, an odd block count (the last
+# stage half empty), K inside a block (pad bytes), K < 16, many stages, and
+# each b3 tile shape (32 x 128, 128 x 128, 128 x 256), ragged in M and N.
+# With more than two token blocks per weight tile the weights are rewritten
+# as i2 and the i2 kernel runs instead (the last four shapes).
+B3_GEMM_SHAPES = [(33, 200, 80, "b3"), (40, 130, 160, "b3"), (64, 257, 240, "b3"), (64, 300, 1001, "b3"),
+                  (17, 16, 7, "b3"), (64, 2000, 3200, "b3"), (129, 13500, 170, "b3"), (200, 26500, 250, "b3"),
+                  (100, 96, 1001, "i2"), (300, 520, 3200, "i2"), (700, 9000, 333, "i2"), (2048, 3200, 320, "i2")]
+
+
+@pytest.mark.parametrize("M,N,K,kernel", B3_GEMM_SHAPES)
+def test_gemm_b3(M, N, K, kernel):
+    kname = bl.bitlinear_product_kernel(M, N, K, bl.LAYOUT_B3, bl.BF16, bl.ALGO_GEMM_MFMA)
+    log("forward gemm b3", M, N, K, kname)
+    assert kname.startswith(f"bl::k_gemm_mfma_{kernel}<")
+    run_forward_case(M, N, K, bl.ALGO_GEMM_MFMA, "b3", seed=3 * M + N + 11 * K, y_kinds=("i32", "f32"))
+
+
+@pytest.mark.parametrize("K", [80, 240, 1001])
+def test_gemm_b3_int8_tight_rows(K):
+    """Pre-quantised rows only 16-byte padded: the last stage's 160-byte
+    activation reads run into the next row or past the buffer, where the
+    weights are zero (pad bytes, or a missing k-block's zero word)."""
+    M, N = 50, 300
+    assert bl.bitlinear_product_kernel(M, N, K, bl.LAYOUT_B3, bl.I8, bl.ALGO_GEMM_MFMA).startswith("bl::k_gemm_mfma_b3<")
+    t = synth.ternary_weights(N, K, seed=K + 5)
+    x = synth.activations_bf16(M, K, seed=K + 6)
+    ref = oracle.forward(t, np.float32(0.02), x)
+    Xq, beta = bl.quantize_act(to_dev(x))
+    ld = (K + 15) // 16 * 16
+    xt = torch.zeros((M, ld), dtype=torch.int8, device="cuda")
+    xt[:, :K] = Xq[:, :K]
+    assert xt.stride(0) == ld
+    P = to_dev(oracle.pack(t, bl.LAYOUT_B3))
+    gamma = to_dev(np.array([0.02], np.float32))
+    acc = to_host(bl.forward(P, bl.LAYOUT_B3, gamma, xt, N, K, beta=beta, y_dtype=torch.int32,
+                             algo=bl.ALGO_GEMM_MFMA))
+    assert np.array_equal(acc, ref["acc"])
+    # the same with garbage (not zero) bytes between K and the row stride
+    xt[:, K:] = 77
+    acc = to_host(bl.forward(P, bl.LAYOUT_B3, gamma, xt, N, K, beta=beta, y_dtype=torch.int32,
+                             algo=bl.ALGO_GEMM_MFMA))
+    assert np.array_equal(acc, ref["acc"])
 
 
 @pytest.mark.parametrize("layout", ["i2", "b3"])
