@@ -453,18 +453,21 @@ hipError_t launch_tile(const GemvArgs &a, hipStream_t stream)
 
 namespace {
 // Tile shapes on offer, with their sustained rates relative to each other
-// (measured; for the small tile, fitted to 32-176-token products of the
-// 70B layers, where latency rather than the matrix cores bounds a tile).  A
-// launch costs about ceil(tiles / 256 CUs) rounds of one tile each.
+// (measured; for the small tiles, fitted to 32-176-token products of the
+// 70B layers, where latency or the b3 decode rather than the matrix cores
+// bounds a tile).  A launch costs about ceil(tiles / 256 CUs) rounds of one
+// tile each.  The 64 x 128 tile serves b3 only: at 64 tokens it decodes each
+// weight tile once instead of twice.
 struct GemmTile {
     int bm, bn, wm, wn, s; // tile, wave grid, k halves (of 128) per stage
     double rate;
-    bool b3; // offered for b3 weights (the b3 decode of a 128 x 128 wave tile spills registers)
+    bool i2, b3; // offered for i2 / b3 weights (the b3 decode of a 128 x 128 wave tile spills registers)
 };
-constexpr GemmTile kTiles[] = {{256, 256, 2, 2, 1, 2.1, false},
-                               {128, 256, 2, 4, 1, 1.95, true},
-                               {128, 128, 2, 2, 1, 1.5, true},
-                               {32, 128, 1, 4, 1, 1.1, true}};
+constexpr GemmTile kTiles[] = {{256, 256, 2, 2, 1, 2.1, true, false},
+                               {128, 256, 2, 4, 1, 1.95, true, true},
+                               {128, 128, 2, 2, 1, 1.5, true, true},
+                               {32, 128, 1, 4, 1, 1.1, true, true},
+                               {64, 128, 1, 4, 1, 1.3, false, true}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int64_t kCUs = 256;
 
@@ -473,7 +476,7 @@ int best_tile(int layout, int64_t M, int64_t N)
     int best = -1;
     double best_cost = 0;
     for (int i = 0; i < kNumTiles; ++i) {
-        if (layout == LAYOUT_B3 && !kTiles[i].b3) continue;
+        if (layout == LAYOUT_B3 ? !kTiles[i].b3 : !kTiles[i].i2) continue;
         const int64_t t = ((M + kTiles[i].bm - 1) / kTiles[i].bm) * ((N + kTiles[i].bn - 1) / kTiles[i].bn);
         const double cost = static_cast<double>((t + kCUs - 1) / kCUs) * kTiles[i].bm * kTiles[i].bn / kTiles[i].rate;
         if (best < 0 || cost < best_cost) best = i, best_cost = cost;
@@ -487,7 +490,8 @@ hipError_t launch_entry(const GemvArgs &a, hipStream_t stream)
     constexpr GemmTile t = kTiles[I];
     if constexpr (t.b3)
         if (a.layout == LAYOUT_B3) return launch_tile<LAYOUT_B3, t.bm, t.bn, t.wm, t.wn, t.s>(a, stream);
-    return launch_tile<LAYOUT_I2, t.bm, t.bn, t.wm, t.wn, t.s>(a, stream);
+    if constexpr (t.i2) return launch_tile<LAYOUT_I2, t.bm, t.bn, t.wm, t.wn, t.s>(a, stream);
+    return hipErrorInvalidValue; // not reached: best_tile offers the tile only for its layouts
 }
 } // namespace
 
@@ -512,12 +516,13 @@ void gemm_kernel_name(int layout, int64_t M, int64_t N, char *buf, size_t n)
 
 hipError_t launch_gemm_mfma(const GemvArgs &a, hipStream_t stream)
 {
-    static_assert(kNumTiles == 4, "one case per tile shape");
+    static_assert(kNumTiles == 5, "one case per tile shape");
     switch (best_tile(a.layout, a.M, a.N)) {
     case 0: return launch_entry<0>(a, stream);
     case 1: return launch_entry<1>(a, stream);
     case 2: return launch_entry<2>(a, stream);
-    default: return launch_entry<3>(a, stream);
+    case 3: return launch_entry<3>(a, stream);
+    default: return launch_entry<4>(a, stream);
     }
 }
 

@@ -239,7 +239,7 @@ def test_product_kernel_names():
     assert f(3, 64, 64, bl.LAYOUT_B1, bl.BF16, bl.ALGO_GEMM_MFMA) is None
     # b3 is decoded in the GEMM (tiles other than 256 x 256) when a weight tile
     # meets at most two token blocks, else rewritten as i2; b1 always is
-    assert f(64, 28672, 8192, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemm_mfma_b3<32, 128, 1, 4, 1>"
+    assert f(64, 28672, 8192, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemm_mfma_b3<64, 128, 1, 4, 1>"  # b3 only
     assert f(176, 28672, 8192, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemm_mfma_b3<128, 256, 2, 4, 1>"
     assert f(176, 8192, 8192, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemm_mfma_i2<32, 128, 1, 4, 1>"
     assert f(2048, 3200, 3200, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemm_mfma_i2<128, 256, 2, 4, 1>"

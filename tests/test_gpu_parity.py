@@ -222,11 +222,13 @@ def test_gemm_tile_shapes(M, N, K):
 # (M, N, K) for the base-3 GEMM, whose stage is two 80-weight k-blocks:
 # one block (a half stage), exactly one stage, an odd block count (the last
 # stage half empty), K inside a block (pad bytes), K < 16, many stages, and
-# each b3 tile shape (32 x 128, 128 x 128, 128 x 256), ragged in M and N.
+# each b3 tile shape (32 x 128, 64 x 128, 128 x 128, 128 x 256), ragged in M
+# and N.
 # With more than two token blocks per weight tile the weights are rewritten
 # as i2 and the i2 kernel runs instead (the last four shapes).
 B3_GEMM_SHAPES = [(33, 200, 80, "b3"), (40, 130, 160, "b3"), (64, 257, 240, "b3"), (64, 300, 1001, "b3"),
                   (17, 16, 7, "b3"), (64, 2000, 3200, "b3"), (129, 13500, 170, "b3"), (200, 26500, 250, "b3"),
+                  (64, 20000, 100, "b3"), (50, 20000, 250, "b3"),
                   (100, 96, 1001, "i2"), (300, 520, 3200, "i2"), (700, 9000, 333, "i2"), (2048, 3200, 320, "i2")]
 
 
