@@ -220,18 +220,31 @@ def main():
 
     # ---- roofline: the product kernel of every job, timed on its own ---------
     # bitlinear_forward runs the activation quantiser, then the product kernel
-    # (bitlinear_product_kernel names it).  Here each job's activations are
-    # quantised once through the split entry point, then a HIP graph of R
-    # back-to-back product launches (rotating over the weight copies) is
-    # replayed between two HIP events on the launch stream; a launch's
-    # duration is the replay time / R.  Durations are summed per kernel name;
-    # the kernel with the most time per step is the dominant one.
+    # (bitlinear_product_kernel names it), or, for 1-4 tokens, one GEMV with
+    # the quantiser inside.  For the first kind each job's activations are
+    # quantised once through the split entry point and the product kernel is
+    # timed alone; the one-launch forwards are timed as called.  A HIP graph
+    # of R back-to-back launches (rotating over the weight copies) is replayed
+    # between two HIP events on the launch stream; a launch's duration is the
+    # replay time / R.  Durations are summed per kernel name; the kernel with
+    # the most time per step is the dominant one.
     R = 16
     for j in jobs:
         layer = j["L"]["layer"]
         M = j["M"]
         algo = bl.bitlinear_auto_algo(M, layer.N, layer.K, layout, j["x_dtype"])
         j["kernel"] = bl.bitlinear_product_kernel(M, layer.N, layer.K, layout, j["x_dtype"], bl.ALGO_AUTO)
+        j["fused"] = j["kernel"].startswith("bl::k_gemv_fq<")
+        if j["fused"]:
+            with torch.cuda.stream(stream):
+                launch_job(j, 0)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for r in range(R):
+                        launch_job(j, r % ncopies)
+            j["graph"] = g
+            continue
         tiled = algo == bl.ALGO_GEMV_MFMA and M > 4 and layer.K <= 65536
         j["beta"] = torch.empty(M, dtype=torch.float32, device=dev)
         s_ = stream.cuda_stream
@@ -275,8 +288,11 @@ def main():
     torch.cuda.synchronize()
 
     def product_bytes(j):
+        # packed weights, the activations as the kernel reads them (int8 and
+        # beta, or the fp32 / bf16 rows of a one-launch forward), gamma, Y
         layer = j["L"]["layer"]
-        return j["L"]["P"][0].numel() + j["M"] * layer.K + 4 * j["M"] + 4 + 4 * j["M"] * layer.N
+        x = j["M"] * layer.K * (4 if j["x_dtype"] == bl.F32 else 2) if j["fused"] else j["M"] * layer.K + 4 * j["M"]
+        return j["L"]["P"][0].numel() + x + 4 + 4 * j["M"] * layer.N
 
     per_kernel = {}
     reps = 5

@@ -172,6 +172,9 @@ const char *bitlinear_product_kernel(int64_t M, int64_t N, int64_t K, int layout
         bl::gemv_addsub_kernel_name(M, name, sizeof name);
     } else if (algo == BITLINEAR_ALGO_GEMM_MFMA) {
         bl::gemm_kernel_name(gemm_rewrites(M, N, layout) ? BITLINEAR_LAYOUT_I2 : layout, M, N, name, sizeof name);
+    } else if (algo == BITLINEAR_ALGO_GEMV_MFMA && bl::gemv_fq_shape(layout, M, N, K, x_dtype)) {
+        // the quantiser inside the GEMV (for 16-byte aligned rows)
+        bl::gemv_fq_kernel_name(layout, M, N, K, x_dtype, name, sizeof name);
     } else {
         // the same choice of activation staging as bitlinear_forward_algo
         const bool tiled = x_dtype == BITLINEAR_I8_TILED ||
@@ -331,6 +334,13 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
     a.y_dtype = y_dtype;
     a.ldy = ldy;
     a.tiled = false;
+    if (!x_int8 && algo == BITLINEAR_ALGO_GEMV_MFMA && bl::gemv_fq_ok(layout, M, N, K, x_dtype, X, ldx)) {
+        // 1-4 tokens: the GEMV quantises the activations itself (one launch)
+        a.Xq = nullptr;
+        a.ldq = 0;
+        a.beta = nullptr;
+        return status_of(bl::launch_gemv_fq(a, X, x_dtype, ldx, st));
+    }
     if (x_int8) {
         a.Xq = static_cast<const int8_t *>(X);
         a.ldq = ldx;

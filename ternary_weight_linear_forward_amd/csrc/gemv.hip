@@ -316,6 +316,274 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// Decode GEMV with the per-token quantiser inside, for 1 to 4 tokens given as
+// fp32 or bf16 rows (16-byte aligned).  The work split is k_gemv_mfma's with
+// one row tile per workgroup: wave w owns the k-steps w, w + KS, ... (at most
+// SPW of them), and every workgroup quantises the few KB of activations
+// itself, so the forward is one launch instead of quantiser + GEMV.
+//  1. Each wave issues the loads of its own activations (4 tokens x STEP_K
+//     values per k-step, as 16-value units, unit u = lane + 64 j: token
+//     u / CH, chunk u % CH) and then of its weight chunks, all before the
+//     first wait.  Waits count loads in issue order, so the activations are
+//     waited for without waiting for the weights.
+//  2. beta_m = max |x_mk| of the wave's values, across the wave by shuffles
+//     and across the waves through LDS (one barrier).
+//  3. The values are rounded with the quantiser's own arithmetic (token_step,
+//     quant_one: bit-identical to bitlinear_quantize_act) and pass through a
+//     per-wave LDS area into the MFMA operand layout: lane (i, g), operand d
+//     takes token i's 16 values at chunk NMF g + d of the k-step.
+//  4. The k-step products, the cross-wave sum and the rescale follow as in
+//     k_gemv_mfma.
+// ---------------------------------------------------------------------------
+constexpr int FQ_MAX_WAVES = 10;
+constexpr int FQ_MAX_SPW = 4;
+
+__device__ __forceinline__ uint4 buffer_load_16(const void *base, int nbytes, int voff)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, nbytes, 0x00020000);
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+#else
+    (void)base, (void)nbytes, (void)voff;
+    return make_uint4(0u, 0u, 0u, 0u);
+#endif
+}
+
+// Maximum of a non-negative value over the wave, in every lane: running
+// maxima within rows of 16 lanes (DPP row shifts; lanes shifted in from
+// outside the row read 0), then row 15's value broadcast into the next rows
+// (row_bcast:15, row_bcast:31), and lane 63's result read back.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max_step(float x)
+{
+    const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, true);
+    return fmaxf(x, __int_as_float(y));
+}
+
+__device__ __forceinline__ float wave_max_nonneg(float v)
+{
+    v = dpp_max_step<0x111, 0xf>(v); // row_shr:1
+    v = dpp_max_step<0x112, 0xf>(v); // row_shr:2
+    v = dpp_max_step<0x114, 0xf>(v); // row_shr:4
+    v = dpp_max_step<0x118, 0xf>(v); // row_shr:8
+    v = dpp_max_step<0x142, 0xa>(v); // row_bcast:15
+    v = dpp_max_step<0x143, 0xc>(v); // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+template <int LAYOUT, int XDT, int SPW, int MT>
+__global__ __launch_bounds__(64 * FQ_MAX_WAVES) void k_gemv_fq(const uint8_t *__restrict__ P, int64_t KB, int64_t NT,
+                                                              const float *__restrict__ gamma_p,
+                                                              const void *__restrict__ X, int64_t ldx, int xbytes,
+                                                              int64_t M, int64_t N, int64_t K, void *__restrict__ Y,
+                                                              int y_dtype, int64_t ldy)
+{
+    using S = StepShape<LAYOUT>;
+    constexpr int NMF = S::NMF, KBLK = S::KBLK;
+    constexpr int STEP_K = 4 * KBLK;
+    constexpr int CH = STEP_K / 16;                // 16-value chunks per token per k-step (i2 16, b3 20, b1 32)
+    constexpr int NUW = (SPW * MT * CH + 63) / 64; // unit slots per lane (MT: tokens the kernel takes, 4 or 16)
+    constexpr int ES = XDT == DT_F32 ? 4 : 2;      // bytes per value
+    constexpr int VL = ES;                         // 16-byte loads per unit (16 values)
+    __shared__ v4i qbuf[FQ_MAX_WAVES][SPW][MT * CH];
+    __shared__ float wmax[FQ_MAX_WAVES][MT];
+    __shared__ v4i red[FQ_MAX_WAVES][64];
+    const int KS = blockDim.x >> 6;
+    const int wave = wave_id(), lane = lane_id();
+    const int i = lane & 15, g = lane >> 4;
+    const int64_t tile = blockIdx.x;
+    const int64_t nsteps = (KB + 3) / 4;
+    const uint4 zero_chunk = LAYOUT == LAYOUT_I2   ? make_uint4(I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD)
+                             : LAYOUT == LAYOUT_B3 ? make_uint4(B3_ZERO_WORD, B3_ZERO_WORD, B3_ZERO_WORD, B3_ZERO_WORD)
+                                                   : make_uint4(0u, 0u, 0u, 0u);
+    // this wave's k-steps wave + j KS (j < nj), and its (k-step, token, chunk)
+    // units: unit u = (j M + token) CH + chunk, dealt to lane u % 64
+    int nj = 0;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) nj += wave + static_cast<int64_t>(j) * KS < nsteps ? 1 : 0;
+    const int mtok = static_cast<int>(M);
+    const int nunits = nj * mtok * CH;
+    const int ldx32 = static_cast<int>(ldx); // (the whole activation range is below 2^31 bytes)
+    const int K32 = static_cast<int>(K);
+
+    // ---- 1. loads: activations first, then weights (no branch, clamped) ----
+    // Dead unit slots and values past K read an in-bounds place and are
+    // zeroed below.  The activation resource ends at the last row's value K
+    // rounded up to 16 bytes: reads past it return zeros.
+    // unit slot n of this lane: its k-step slot j, token, chunk c, first k and
+    // the number of its values before K (0 for a dead slot); recomputed where
+    // needed rather than kept in registers
+    struct Unit {
+        int j, tok, c, k0, nv;
+    };
+    auto unit = [&](int n) {
+        Unit r;
+        const int u = lane + 64 * n;
+        const bool live = u < nunits;
+        const int uu = live ? u : 0;
+        const int t = uu / CH; // t = j M + token
+        r.c = uu - t * CH;
+        // t / M without a division for M = 1..4 ((t * 0xAAAB) >> 17 is t / 3
+        // below 2^15); 16-token groups divide (M up to 16)
+        r.j = MT == 4 ? (mtok == 1 ? t : (mtok == 2 ? t >> 1 : (mtok == 4 ? t >> 2 : static_cast<int>((t * 0xAAABu) >> 17))))
+                      : t / mtok;
+        r.tok = t - r.j * mtok;
+        r.k0 = (wave + r.j * KS) * STEP_K + 16 * r.c;
+        const int left = K32 - r.k0;
+        r.nv = live ? (left <= 0 ? 0 : (left < 16 ? left : 16)) : 0;
+        return r;
+    };
+    uint4 xv[NUW][VL];
+#pragma unroll
+    for (int n = 0; n < NUW; ++n) {
+        const Unit un = unit(n);
+        const int off = (un.tok * ldx32 + (un.k0 < K32 ? un.k0 : 0)) * ES;
+#pragma unroll
+        for (int v = 0; v < VL; ++v) xv[n][v] = buffer_load_16(X, xbytes, off + 16 * v);
+    }
+    uint4 wb[SPW];
+    {
+        const uint8_t *pt = P + tile * KB * 256;
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+            const int64_t st = wave + static_cast<int64_t>(j) * KS;
+            const int64_t kb = 4 * (st < nsteps ? st : nsteps - 1) + g;
+            const uint4 v = *reinterpret_cast<const uint4 *>(pt + (kb < KB ? kb : KB - 1) * 256 + i * 16);
+            wb[j] = kb < KB ? v : zero_chunk;
+        }
+    }
+    const float gamma = *gamma_p;
+    // keep every load above this point: the compiler would otherwise sink the
+    // weight loads below the activation work and serialise the round trips
+    __builtin_amdgcn_sched_barrier(0);
+
+    // the 16-value unit as 16 dwords of binary32 bits (bf16: value e is the
+    // upper or lower half of dword e / 2)
+    auto bits = [&](int n, int e) -> uint32_t {
+        const uint4 q = xv[n][XDT == DT_F32 ? e / 4 : e / 8];
+        const int w = XDT == DT_F32 ? e % 4 : (e % 8) / 2;
+        const uint32_t d = w == 0 ? q.x : (w == 1 ? q.y : (w == 2 ? q.z : q.w));
+        if constexpr (XDT == DT_F32) return d;
+        else return (e & 1) ? (d & 0xffff0000u) : (d << 16);
+    };
+
+    // ---- 2. per-token absmax ----
+    // zero the values at or past K of the unit that holds K, and whole dead
+    // slots (a lane-divergent branch, taken by few lanes)
+#pragma unroll
+    for (int n = 0; n < NUW; ++n) {
+        const int nv = unit(n).nv;
+        if (nv < 16) {
+#pragma unroll
+            for (int v = 0; v < VL; ++v) {
+                uint32_t w4[4] = {xv[n][v].x, xv[n][v].y, xv[n][v].z, xv[n][v].w};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int e0 = (XDT == DT_F32 ? 4 : 8) * v + (XDT == DT_F32 ? 1 : 2) * w; // first value of the dword
+                    uint32_t keep;
+                    if constexpr (XDT == DT_F32) keep = e0 < nv ? 0xffffffffu : 0u;
+                    else keep = (e0 < nv ? 0x0000ffffu : 0u) | (e0 + 1 < nv ? 0xffff0000u : 0u);
+                    w4[w] &= keep;
+                }
+                xv[n][v] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+            }
+        }
+    }
+    float amax[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) amax[t] = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NUW; ++n) {
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(__uint_as_float(bits(n, e))));
+        const int tok = unit(n).tok;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) amax[t] = tok == t ? fmaxf(amax[t], m) : amax[t];
+    }
+    // every lane holds every token's wave maximum; lane t writes token t's
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        const float b = wave_max_nonneg(amax[t]);
+        if (lane == t) wmax[wave][t] = b;
+    }
+    __syncthreads();
+    // lane t holds beta of token t % MT; other tokens' come by a lane shuffle
+    float beta_lane;
+    {
+        const int t = lane & (MT - 1);
+        float b = wmax[0][t];
+        for (int w = 1; w < KS; ++w) b = fmaxf(b, wmax[w][t]);
+        beta_lane = b;
+    }
+    // (a lane shuffle: call it only where every lane of the wave is active)
+    auto beta_of = [&](int t) { return __shfl(beta_lane, t); };
+
+    // ---- 3. round to int8 and regroup through this wave's LDS area ----
+    // q = rint(fl32(x s)) as quant_one computes it: every |x| <= beta, so
+    // |fl32(x s)| <= 127 (1 + 2^-24)^2 < 127.5 and the clamp never acts;
+    // adding 1.5 * 2^23 (a separate, correctly rounded add: the build does
+    // not contract) rounds to an integer with ties to even, which then sits
+    // in the low bits of the sum (two's complement in its low byte).
+#pragma unroll
+    for (int n = 0; n < NUW; ++n) {
+        const Unit un = unit(n);
+        const float st = token_step(beta_of(un.tok));
+        if (lane + 64 * n >= nunits) continue;
+        uint32_t w4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t b[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v = __uint_as_float(bits(n, 4 * q + e)) * st;
+                b[e] = __float_as_uint(v + 12582912.0f);
+            }
+            const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
+            const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);
+            w4[q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        }
+        qbuf[wave][un.j][un.tok * CH + un.c] = v4i{static_cast<int>(w4[0]), static_cast<int>(w4[1]),
+                                                   static_cast<int>(w4[2]), static_cast<int>(w4[3])};
+    }
+    // the other lanes of this wave read what it wrote: order the LDS accesses
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // operand d of lane (i, g): token i's chunk NMF g + d (tokens past M, and
+    // past MT, read copies or stale data: their outputs are never stored)
+    v4i a[SPW][NMF];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+#pragma unroll
+        for (int d = 0; d < NMF; ++d) a[j][d] = qbuf[wave][j][(i & (MT - 1)) * CH + NMF * g + d];
+
+    // ---- 4. products, cross-wave sum, rescale ----
+    v4i acc[1] = {v4i{0, 0, 0, 0}};
+    v4i sacc = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+        if (j >= nj) break;
+        const uint4 b[1] = {wb[j]};
+        gemv_step<LAYOUT, 1, NMF>(b, a[j], acc);
+        if constexpr (kOffsetCodes<LAYOUT>) act_sum_step<NMF>(a[j], sacc);
+    }
+    red[wave][lane] = kOffsetCodes<LAYOUT> ? offset_fix<LAYOUT>(acc[0], sacc) : acc[0];
+    float sc[4]; // rescale of tokens 4g .. 4g + 3 (shuffled while all lanes are active)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) sc[rr] = token_scale(gamma, beta_of(4 * g + rr));
+    __syncthreads();
+    if (wave != 0 || 4 * g >= M) return; // lane (i, g) holds tokens 4g .. 4g + 3
+    v4i tot = red[0][lane];
+    for (int w = 1; w < KS; ++w) tot += red[w][lane];
+    const int64_t n = tile * 16 + i;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+        if (4 * g + rr < M && n < N) store_out(Y, y_dtype, ldy, 4 * g + rr, n, tot[rr], sc[rr]);
+}
+
+// ---------------------------------------------------------------------------
 // Persistent MFMA GEMV for large layers.  About one workgroup per CU, KS
 // waves; wave w owns the k-steps w, w + KS, ... (at most SPW of them): it loads
 // their activation operands into registers once and then streams the packed
@@ -689,6 +957,97 @@ static void launch_mfma_layout(const GemvArgs &a, hipStream_t stream)
     if (p.tw == 4) launch_mfma_tw<LAYOUT, 4>(a, KB, NT, nsteps, stream);
     else if (p.tw == 2) launch_mfma_tw<LAYOUT, 2>(a, KB, NT, nsteps, stream);
     else launch_mfma_tw<LAYOUT, 1>(a, KB, NT, nsteps, stream);
+}
+
+// Shape of the fused-quantiser GEMV (k_gemv_fq): 1 to 4 tokens of fp32 /
+// bf16 input on shapes the per-tile kernel takes (not the persistent one),
+// with the per-tile kernel's wave count and at most FQ_MAX_SPW k-steps per
+// wave.  Alignment is checked separately (gemv_fq_ok).
+struct FqPlan {
+    bool ok;
+    int64_t KS; // waves per workgroup
+    int spw;    // k-steps per wave (1, 2 or 4)
+    int mt;     // tokens the kernel takes (4)
+};
+
+static FqPlan fq_plan(int layout, int64_t M, int64_t N, int64_t K, int x_dtype)
+{
+    FqPlan f{false, 0, 0, 4};
+    // (16-token groups were measured slower than quantiser + GEMV: every
+    // workgroup rounds all 16 x K values again; 2x on the 3B q layer)
+    if (M < 1 || M > 4 || (x_dtype != DT_F32 && x_dtype != DT_BF16)) return f;
+    const GemvPlan gp = gemv_plan(layout, M, N, K);
+    if (gp.persist || gp.tw != 1) return f;
+    const int64_t NT = (N + 15) / 16;
+    const int64_t kblk = layout == LAYOUT_I2 ? 64 : (layout == LAYOUT_B3 ? 80 : 128);
+    const int64_t nsteps = ((K + kblk - 1) / kblk + 3) / 4;
+    int64_t KS = (256 * 16 + NT - 1) / NT;
+    KS = KS < 1 ? 1 : (KS > FQ_MAX_WAVES ? FQ_MAX_WAVES : KS);
+    KS = KS > nsteps ? nsteps : KS;
+    const int64_t spw = (nsteps + KS - 1) / KS;
+    // (b1 holds 8 operands per k-step: four k-steps per wave spill)
+    if (spw > (layout == LAYOUT_B1 ? 2 : FQ_MAX_SPW)) return f;
+    f.ok = true;
+    f.KS = KS;
+    f.spw = spw <= 1 ? 1 : (spw <= 2 ? 2 : 4);
+    return f;
+}
+
+bool gemv_fq_shape(int layout, int64_t M, int64_t N, int64_t K, int x_dtype)
+{
+    return fq_plan(layout, M, N, K, x_dtype).ok;
+}
+
+bool gemv_fq_ok(int layout, int64_t M, int64_t N, int64_t K, int x_dtype, const void *X, int64_t ldx)
+{
+    if (!gemv_fq_shape(layout, M, N, K, x_dtype)) return false;
+    const int64_t es = x_dtype == DT_F32 ? 4 : 2;
+    if ((reinterpret_cast<uintptr_t>(X) & 15u) || (ldx * es) % 16) return false;
+    return ((M - 1) * ldx + K) * es + 15 <= 0x7fffffff; // the buffer resource's byte range
+}
+
+template <int LAYOUT, int XDT>
+static void launch_fq_x(const GemvArgs &a, const void *X, int64_t ldx, const FqPlan &f, hipStream_t stream)
+{
+    const int64_t NT = (a.N + 15) / 16;
+    const int64_t KB = (a.K + StepShape<LAYOUT>::KBLK - 1) / StepShape<LAYOUT>::KBLK;
+    constexpr int64_t ES = XDT == DT_F32 ? 4 : 2;
+    const int xbytes = static_cast<int>((((a.M - 1) * ldx + a.K) * ES + 15) & ~int64_t(15));
+    dim3 grid(static_cast<unsigned>(NT)), block(static_cast<unsigned>(f.KS * 64));
+    if (f.spw == 1) {
+        hipLaunchKernelGGL((k_gemv_fq<LAYOUT, XDT, 1, 4>), grid, block, 0, stream, a.P, KB, NT, a.gamma, X, ldx, xbytes,
+                           a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
+    } else if (f.spw == 2) {
+        hipLaunchKernelGGL((k_gemv_fq<LAYOUT, XDT, 2, 4>), grid, block, 0, stream, a.P, KB, NT, a.gamma, X, ldx, xbytes,
+                           a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
+    } else if constexpr (LAYOUT != LAYOUT_B1) {
+        hipLaunchKernelGGL((k_gemv_fq<LAYOUT, XDT, 4, 4>), grid, block, 0, stream, a.P, KB, NT, a.gamma, X, ldx, xbytes,
+                           a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
+    }
+}
+
+template <int LAYOUT>
+static void launch_fq_layout(const GemvArgs &a, const void *X, int x_dtype, int64_t ldx, const FqPlan &f,
+                             hipStream_t stream)
+{
+    if (x_dtype == DT_F32) launch_fq_x<LAYOUT, DT_F32>(a, X, ldx, f, stream);
+    else launch_fq_x<LAYOUT, DT_BF16>(a, X, ldx, f, stream);
+}
+
+hipError_t launch_gemv_fq(const GemvArgs &a, const void *X, int x_dtype, int64_t ldx, hipStream_t stream)
+{
+    const FqPlan f = fq_plan(a.layout, a.M, a.N, a.K, x_dtype);
+    if (!f.ok) return hipErrorInvalidValue;
+    if (a.layout == LAYOUT_I2) launch_fq_layout<LAYOUT_I2>(a, X, x_dtype, ldx, f, stream);
+    else if (a.layout == LAYOUT_B3) launch_fq_layout<LAYOUT_B3>(a, X, x_dtype, ldx, f, stream);
+    else launch_fq_layout<LAYOUT_B1>(a, X, x_dtype, ldx, f, stream);
+    return hipGetLastError();
+}
+
+void gemv_fq_kernel_name(int layout, int64_t M, int64_t N, int64_t K, int x_dtype, char *buf, size_t n)
+{
+    const FqPlan f = fq_plan(layout, M, N, K, x_dtype);
+    snprintf(buf, n, "bl::k_gemv_fq<%d, %d, %d, %d>", layout, x_dtype, f.spw, f.mt);
 }
 
 void gemv_kernel_name(int layout, int64_t M, int64_t N, int64_t K, bool tiled, char *buf, size_t n)

@@ -57,6 +57,13 @@ struct GemvArgs {
 
 hipError_t launch_gemv_addsub(const GemvArgs &a, hipStream_t stream);
 hipError_t launch_gemv_mfma(const GemvArgs &a, hipStream_t stream);
+// The matrix-core GEMV with the activation quantiser inside (k_gemv_fq): the
+// whole forward in one launch for 1 to 4 tokens of fp32 / bf16 input X (rows
+// of ldx values); a.Xq, a.ldq and a.beta are unused.  gemv_fq_shape: the
+// shape qualifies; gemv_fq_ok: the shape and X's alignment and extent do.
+bool gemv_fq_shape(int layout, int64_t M, int64_t N, int64_t K, int x_dtype);
+bool gemv_fq_ok(int layout, int64_t M, int64_t N, int64_t K, int x_dtype, const void *X, int64_t ldx);
+hipError_t launch_gemv_fq(const GemvArgs &a, const void *X, int x_dtype, int64_t ldx, hipStream_t stream);
 hipError_t launch_gemm_mfma(const GemvArgs &a, hipStream_t stream); // i2 or b3 weights
 // Size of an M x N product in 64 x 128 output tiles: below about 128 of them
 // the matrix-core GEMV is faster than the GEMM (measured on the 70B layers).
@@ -80,6 +87,7 @@ hipError_t launch_bwd_dw(const int8_t *Xq, int64_t ldq, const float *beta, int64
 // product launch runs for a shape.
 void gemv_kernel_name(int layout, int64_t M, int64_t N, int64_t K, bool tiled, char *buf, size_t n);
 void gemv_addsub_kernel_name(int64_t M, char *buf, size_t n);
+void gemv_fq_kernel_name(int layout, int64_t M, int64_t N, int64_t K, int x_dtype, char *buf, size_t n);
 void gemm_kernel_name(int layout, int64_t M, int64_t N, char *buf, size_t n);
 
 } // namespace bl
