@@ -234,7 +234,7 @@ def main():
         M = j["M"]
         algo = bl.bitlinear_auto_algo(M, layer.N, layer.K, layout, j["x_dtype"])
         j["kernel"] = bl.bitlinear_product_kernel(M, layer.N, layer.K, layout, j["x_dtype"], bl.ALGO_AUTO)
-        j["fused"] = j["kernel"].startswith("bl::k_gemv_fq<")
+        j["fused"] = j["kernel"].startswith(("bl::k_gemv_fq<", "bl::k_gemv_persist_fq<"))
         if j["fused"]:
             with torch.cuda.stream(stream):
                 launch_job(j, 0)

@@ -316,26 +316,24 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Decode GEMV with the per-token quantiser inside, for 1 to 4 tokens given as
-// fp32 or bf16 rows (16-byte aligned).  The work split is k_gemv_mfma's with
-// one row tile per workgroup: wave w owns the k-steps w, w + KS, ... (at most
-// SPW of them), and every workgroup quantises the few KB of activations
-// itself, so the forward is one launch instead of quantiser + GEMV.
-//  1. Each wave issues the loads of its own activations (4 tokens x STEP_K
-//     values per k-step, as 16-value units, unit u = lane + 64 j: token
-//     u / CH, chunk u % CH) and then of its weight chunks, all before the
-//     first wait.  Waits count loads in issue order, so the activations are
-//     waited for without waiting for the weights.
-//  2. beta_m = max |x_mk| of the wave's values, across the wave by shuffles
-//     and across the waves through LDS (one barrier).
-//  3. The values are rounded with the quantiser's own arithmetic (token_step,
-//     quant_one: bit-identical to bitlinear_quantize_act) and pass through a
-//     per-wave LDS area into the MFMA operand layout: lane (i, g), operand d
-//     takes token i's 16 values at chunk NMF g + d of the k-step.
-//  4. The k-step products, the cross-wave sum and the rescale follow as in
-//     k_gemv_mfma.
+// The per-token quantiser inside the decode GEMVs, for 1 to 4 tokens given as
+// fp32 or bf16 rows (16-byte aligned): every workgroup quantises the few KB of
+// activations itself, so the forward is one launch instead of quantiser +
+// GEMV.  In each wave (owning k-steps wave + j KS, j < nj):
+//  1. fq_load issues the loads of the wave's own activations (4 tokens x
+//     STEP_K values per k-step, as 16-value units: unit u = (j M + token) CH
+//     + chunk, dealt to lane u % 64), then the caller issues its weight
+//     loads, all before the first wait.  Waits count loads in issue order,
+//     so the activations are waited for without waiting for the weights.
+//  2. fq_quantise: beta_m = max |x_mk| of the wave's values, across the wave
+//     by DPP and across the waves through LDS (one barrier); the values are
+//     rounded exactly as the quantiser rounds them (bit-identical to
+//     bitlinear_quantize_act) and pass through a per-wave LDS area into the
+//     MFMA operand layout: lane (i, g), operand d takes token i's 16 values
+//     at chunk NMF g + d of the k-step.
+//  3. The kernel's own products, cross-wave sum and rescale.
 // ---------------------------------------------------------------------------
-constexpr int FQ_MAX_WAVES = 10;
+constexpr int FQ_MAX_WAVES = 10; // per-tile kernel
 constexpr int FQ_MAX_SPW = 4;
 
 __device__ __forceinline__ uint4 buffer_load_16(const void *base, int nbytes, int voff)
@@ -373,22 +371,169 @@ __device__ __forceinline__ float wave_max_nonneg(float v)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-template <int LAYOUT, int XDT, int SPW, int MT>
+// This lane's activation units (see above) and their geometry.
+template <int LAYOUT, int XDT, int SPW>
+struct FqUnits {
+    static constexpr int NMF = StepShape<LAYOUT>::NMF;
+    static constexpr int STEP_K = 4 * StepShape<LAYOUT>::KBLK;
+    static constexpr int CH = STEP_K / 16;               // 16-value chunks per token per k-step (i2 16, b3 20, b1 32)
+    static constexpr int UNITS = 4 * CH;                 // units per k-step (4 tokens)
+    static constexpr int NUW = (SPW * UNITS + 63) / 64;  // unit slots per lane
+    static constexpr int ES = XDT == DT_F32 ? 4 : 2;     // bytes per value
+    static constexpr int VL = ES;                        // 16-byte loads per unit (16 values)
+    int lane, wave, KS, mtok, nunits, K32, ldx32;
+
+    struct Unit {
+        int j, tok, c, k0, nv; // k-step slot, token, chunk, first k, values before K (0: dead slot)
+    };
+    // recomputed where needed rather than kept in registers
+    __device__ __forceinline__ Unit unit(int n) const
+    {
+        Unit r;
+        const int u = lane + 64 * n;
+        const bool live = u < nunits;
+        const int uu = live ? u : 0;
+        const int t = uu / CH; // t = j M + token
+        r.c = uu - t * CH;
+        // t / M for M = 1..4 without a division ((t * 0xAAAB) >> 17 is t / 3 below 2^15)
+        r.j = mtok == 1 ? t : (mtok == 2 ? t >> 1 : (mtok == 4 ? t >> 2 : static_cast<int>((t * 0xAAABu) >> 17)));
+        r.tok = t - r.j * mtok;
+        r.k0 = (wave + r.j * KS) * STEP_K + 16 * r.c;
+        const int left = K32 - r.k0;
+        r.nv = live ? (left <= 0 ? 0 : (left < 16 ? left : 16)) : 0;
+        return r;
+    }
+};
+
+// Issue this lane's activation loads.  Dead unit slots and values past K read
+// an in-bounds place (zeroed later); the resource ends at the last row's value
+// K rounded up to 16 bytes (xbytes), and reads past it return zeros.
+template <class FU>
+__device__ __forceinline__ void fq_load(const FU &U, const void *X, int xbytes, uint4 (&xv)[FU::NUW][FU::VL])
+{
+#pragma unroll
+    for (int n = 0; n < FU::NUW; ++n) {
+        const auto un = U.unit(n);
+        const int off = (un.tok * U.ldx32 + (un.k0 < U.K32 ? un.k0 : 0)) * FU::ES;
+#pragma unroll
+        for (int v = 0; v < FU::VL; ++v) xv[n][v] = buffer_load_16(X, xbytes, off + 16 * v);
+    }
+}
+
+// Absmax, rounding and regroup (every wave of the workgroup must call it: it
+// holds a barrier).  qbuf: this wave's LDS area, SPW x UNITS units; wmax:
+// [waves][4].  Fills a[j][d] for the wave's k-steps j < nj and returns, in lane
+// t, beta of token t % 4 (a lane shuffle of the result gives any token's).
+template <class FU, int SPW>
+__device__ __forceinline__ float fq_quantise(const FU &U, uint4 (&xv)[FU::NUW][FU::VL], v4i *qbuf, float (*wmax)[4],
+                                             v4i (&a)[SPW][FU::NMF])
+{
+    constexpr int XF32 = FU::ES == 4;
+    const int lane = U.lane, wave = U.wave;
+    // the 16-value unit as 16 binary32 bit patterns (bf16: value e is the
+    // upper or lower half of dword e / 2)
+    auto bits = [&](int n, int e) -> uint32_t {
+        const uint4 q = xv[n][XF32 ? e / 4 : e / 8];
+        const int w = XF32 ? e % 4 : (e % 8) / 2;
+        const uint32_t d = w == 0 ? q.x : (w == 1 ? q.y : (w == 2 ? q.z : q.w));
+        if constexpr (XF32) return d;
+        else return (e & 1) ? (d & 0xffff0000u) : (d << 16);
+    };
+    // zero the values at or past K of the unit that holds K, and whole dead
+    // slots (a lane-divergent branch, taken by few lanes)
+#pragma unroll
+    for (int n = 0; n < FU::NUW; ++n) {
+        const int nv = U.unit(n).nv;
+        if (nv < 16) {
+#pragma unroll
+            for (int v = 0; v < FU::VL; ++v) {
+                uint32_t w4[4] = {xv[n][v].x, xv[n][v].y, xv[n][v].z, xv[n][v].w};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int e0 = (XF32 ? 4 : 8) * v + (XF32 ? 1 : 2) * w; // first value of the dword
+                    uint32_t keep;
+                    if constexpr (XF32) keep = e0 < nv ? 0xffffffffu : 0u;
+                    else keep = (e0 < nv ? 0x0000ffffu : 0u) | (e0 + 1 < nv ? 0xffff0000u : 0u);
+                    w4[w] &= keep;
+                }
+                xv[n][v] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+            }
+        }
+    }
+    float amax[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int n = 0; n < FU::NUW; ++n) {
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(__uint_as_float(bits(n, e))));
+        const int tok = U.unit(n).tok;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) amax[t] = tok == t ? fmaxf(amax[t], m) : amax[t];
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const float b = wave_max_nonneg(amax[t]);
+        if (lane == t) wmax[wave][t] = b;
+    }
+    __syncthreads();
+    float beta_lane;
+    {
+        const int t = lane & 3;
+        float b = wmax[0][t];
+        for (int w = 1; w < U.KS; ++w) b = fmaxf(b, wmax[w][t]);
+        beta_lane = b;
+    }
+    // q = rint(fl32(x s)) as quant_one computes it: every |x| <= beta, so
+    // |fl32(x s)| <= 127 (1 + 2^-24)^2 < 127.5 and the clamp never acts;
+    // adding 1.5 * 2^23 (a separate, correctly rounded add: the build does
+    // not contract) rounds to an integer with ties to even, which then sits
+    // in the low bits of the sum (two's complement in its low byte).
+#pragma unroll
+    for (int n = 0; n < FU::NUW; ++n) {
+        const auto un = U.unit(n);
+        const float st = token_step(__shfl(beta_lane, un.tok)); // (every lane active here)
+        if (lane + 64 * n >= U.nunits) continue;
+        uint32_t w4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t b[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v = __uint_as_float(bits(n, 4 * q + e)) * st;
+                b[e] = __float_as_uint(v + 12582912.0f);
+            }
+            const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
+            const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);
+            w4[q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        }
+        qbuf[un.j * FU::UNITS + un.tok * FU::CH + un.c] = v4i{static_cast<int>(w4[0]), static_cast<int>(w4[1]),
+                                                             static_cast<int>(w4[2]), static_cast<int>(w4[3])};
+    }
+    // the other lanes of this wave read what it wrote: order the LDS accesses
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // operand d of lane (i, g): token i's chunk NMF g + d (tokens past M and
+    // 4..15 read copies or stale data: their outputs are never stored)
+    const int i = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+#pragma unroll
+        for (int d = 0; d < FU::NMF; ++d) a[j][d] = qbuf[j * FU::UNITS + (i & 3) * FU::CH + FU::NMF * g + d];
+    return beta_lane;
+}
+
+// One row tile per workgroup (the k_gemv_mfma split, TW = 1), KS <= 10 waves.
+template <int LAYOUT, int XDT, int SPW>
 __global__ __launch_bounds__(64 * FQ_MAX_WAVES) void k_gemv_fq(const uint8_t *__restrict__ P, int64_t KB, int64_t NT,
                                                               const float *__restrict__ gamma_p,
                                                               const void *__restrict__ X, int64_t ldx, int xbytes,
                                                               int64_t M, int64_t N, int64_t K, void *__restrict__ Y,
                                                               int y_dtype, int64_t ldy)
 {
-    using S = StepShape<LAYOUT>;
-    constexpr int NMF = S::NMF, KBLK = S::KBLK;
-    constexpr int STEP_K = 4 * KBLK;
-    constexpr int CH = STEP_K / 16;                // 16-value chunks per token per k-step (i2 16, b3 20, b1 32)
-    constexpr int NUW = (SPW * MT * CH + 63) / 64; // unit slots per lane (MT: tokens the kernel takes, 4 or 16)
-    constexpr int ES = XDT == DT_F32 ? 4 : 2;      // bytes per value
-    constexpr int VL = ES;                         // 16-byte loads per unit (16 values)
-    __shared__ v4i qbuf[FQ_MAX_WAVES][SPW][MT * CH];
-    __shared__ float wmax[FQ_MAX_WAVES][MT];
+    using FU = FqUnits<LAYOUT, XDT, SPW>;
+    constexpr int NMF = FU::NMF;
+    __shared__ v4i qbuf[FQ_MAX_WAVES][SPW * FU::UNITS];
+    __shared__ float wmax[FQ_MAX_WAVES][4];
     __shared__ v4i red[FQ_MAX_WAVES][64];
     const int KS = blockDim.x >> 6;
     const int wave = wave_id(), lane = lane_id();
@@ -398,51 +543,14 @@ __global__ __launch_bounds__(64 * FQ_MAX_WAVES) void k_gemv_fq(const uint8_t *__
     const uint4 zero_chunk = LAYOUT == LAYOUT_I2   ? make_uint4(I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD, I2_ZERO_WORD)
                              : LAYOUT == LAYOUT_B3 ? make_uint4(B3_ZERO_WORD, B3_ZERO_WORD, B3_ZERO_WORD, B3_ZERO_WORD)
                                                    : make_uint4(0u, 0u, 0u, 0u);
-    // this wave's k-steps wave + j KS (j < nj), and its (k-step, token, chunk)
-    // units: unit u = (j M + token) CH + chunk, dealt to lane u % 64
     int nj = 0;
 #pragma unroll
     for (int j = 0; j < SPW; ++j) nj += wave + static_cast<int64_t>(j) * KS < nsteps ? 1 : 0;
-    const int mtok = static_cast<int>(M);
-    const int nunits = nj * mtok * CH;
-    const int ldx32 = static_cast<int>(ldx); // (the whole activation range is below 2^31 bytes)
-    const int K32 = static_cast<int>(K);
+    const FU U{lane, wave, KS, static_cast<int>(M), nj * static_cast<int>(M) * FU::CH, static_cast<int>(K),
+               static_cast<int>(ldx)};
 
-    // ---- 1. loads: activations first, then weights (no branch, clamped) ----
-    // Dead unit slots and values past K read an in-bounds place and are
-    // zeroed below.  The activation resource ends at the last row's value K
-    // rounded up to 16 bytes: reads past it return zeros.
-    // unit slot n of this lane: its k-step slot j, token, chunk c, first k and
-    // the number of its values before K (0 for a dead slot); recomputed where
-    // needed rather than kept in registers
-    struct Unit {
-        int j, tok, c, k0, nv;
-    };
-    auto unit = [&](int n) {
-        Unit r;
-        const int u = lane + 64 * n;
-        const bool live = u < nunits;
-        const int uu = live ? u : 0;
-        const int t = uu / CH; // t = j M + token
-        r.c = uu - t * CH;
-        // t / M without a division for M = 1..4 ((t * 0xAAAB) >> 17 is t / 3
-        // below 2^15); 16-token groups divide (M up to 16)
-        r.j = MT == 4 ? (mtok == 1 ? t : (mtok == 2 ? t >> 1 : (mtok == 4 ? t >> 2 : static_cast<int>((t * 0xAAABu) >> 17))))
-                      : t / mtok;
-        r.tok = t - r.j * mtok;
-        r.k0 = (wave + r.j * KS) * STEP_K + 16 * r.c;
-        const int left = K32 - r.k0;
-        r.nv = live ? (left <= 0 ? 0 : (left < 16 ? left : 16)) : 0;
-        return r;
-    };
-    uint4 xv[NUW][VL];
-#pragma unroll
-    for (int n = 0; n < NUW; ++n) {
-        const Unit un = unit(n);
-        const int off = (un.tok * ldx32 + (un.k0 < K32 ? un.k0 : 0)) * ES;
-#pragma unroll
-        for (int v = 0; v < VL; ++v) xv[n][v] = buffer_load_16(X, xbytes, off + 16 * v);
-    }
+    uint4 xv[FU::NUW][FU::VL];
+    fq_load(U, X, xbytes, xv);
     uint4 wb[SPW];
     {
         const uint8_t *pt = P + tile * KB * 256;
@@ -459,107 +567,9 @@ __global__ __launch_bounds__(64 * FQ_MAX_WAVES) void k_gemv_fq(const uint8_t *__
     // weight loads below the activation work and serialise the round trips
     __builtin_amdgcn_sched_barrier(0);
 
-    // the 16-value unit as 16 dwords of binary32 bits (bf16: value e is the
-    // upper or lower half of dword e / 2)
-    auto bits = [&](int n, int e) -> uint32_t {
-        const uint4 q = xv[n][XDT == DT_F32 ? e / 4 : e / 8];
-        const int w = XDT == DT_F32 ? e % 4 : (e % 8) / 2;
-        const uint32_t d = w == 0 ? q.x : (w == 1 ? q.y : (w == 2 ? q.z : q.w));
-        if constexpr (XDT == DT_F32) return d;
-        else return (e & 1) ? (d & 0xffff0000u) : (d << 16);
-    };
-
-    // ---- 2. per-token absmax ----
-    // zero the values at or past K of the unit that holds K, and whole dead
-    // slots (a lane-divergent branch, taken by few lanes)
-#pragma unroll
-    for (int n = 0; n < NUW; ++n) {
-        const int nv = unit(n).nv;
-        if (nv < 16) {
-#pragma unroll
-            for (int v = 0; v < VL; ++v) {
-                uint32_t w4[4] = {xv[n][v].x, xv[n][v].y, xv[n][v].z, xv[n][v].w};
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const int e0 = (XDT == DT_F32 ? 4 : 8) * v + (XDT == DT_F32 ? 1 : 2) * w; // first value of the dword
-                    uint32_t keep;
-                    if constexpr (XDT == DT_F32) keep = e0 < nv ? 0xffffffffu : 0u;
-                    else keep = (e0 < nv ? 0x0000ffffu : 0u) | (e0 + 1 < nv ? 0xffff0000u : 0u);
-                    w4[w] &= keep;
-                }
-                xv[n][v] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-            }
-        }
-    }
-    float amax[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) amax[t] = 0.0f;
-#pragma unroll
-    for (int n = 0; n < NUW; ++n) {
-        float m = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(__uint_as_float(bits(n, e))));
-        const int tok = unit(n).tok;
-#pragma unroll
-        for (int t = 0; t < MT; ++t) amax[t] = tok == t ? fmaxf(amax[t], m) : amax[t];
-    }
-    // every lane holds every token's wave maximum; lane t writes token t's
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        const float b = wave_max_nonneg(amax[t]);
-        if (lane == t) wmax[wave][t] = b;
-    }
-    __syncthreads();
-    // lane t holds beta of token t % MT; other tokens' come by a lane shuffle
-    float beta_lane;
-    {
-        const int t = lane & (MT - 1);
-        float b = wmax[0][t];
-        for (int w = 1; w < KS; ++w) b = fmaxf(b, wmax[w][t]);
-        beta_lane = b;
-    }
-    // (a lane shuffle: call it only where every lane of the wave is active)
-    auto beta_of = [&](int t) { return __shfl(beta_lane, t); };
-
-    // ---- 3. round to int8 and regroup through this wave's LDS area ----
-    // q = rint(fl32(x s)) as quant_one computes it: every |x| <= beta, so
-    // |fl32(x s)| <= 127 (1 + 2^-24)^2 < 127.5 and the clamp never acts;
-    // adding 1.5 * 2^23 (a separate, correctly rounded add: the build does
-    // not contract) rounds to an integer with ties to even, which then sits
-    // in the low bits of the sum (two's complement in its low byte).
-#pragma unroll
-    for (int n = 0; n < NUW; ++n) {
-        const Unit un = unit(n);
-        const float st = token_step(beta_of(un.tok));
-        if (lane + 64 * n >= nunits) continue;
-        uint32_t w4[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            uint32_t b[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float v = __uint_as_float(bits(n, 4 * q + e)) * st;
-                b[e] = __float_as_uint(v + 12582912.0f);
-            }
-            const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
-            const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);
-            w4[q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-        }
-        qbuf[wave][un.j][un.tok * CH + un.c] = v4i{static_cast<int>(w4[0]), static_cast<int>(w4[1]),
-                                                   static_cast<int>(w4[2]), static_cast<int>(w4[3])};
-    }
-    // the other lanes of this wave read what it wrote: order the LDS accesses
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    // operand d of lane (i, g): token i's chunk NMF g + d (tokens past M, and
-    // past MT, read copies or stale data: their outputs are never stored)
     v4i a[SPW][NMF];
-#pragma unroll
-    for (int j = 0; j < SPW; ++j)
-#pragma unroll
-        for (int d = 0; d < NMF; ++d) a[j][d] = qbuf[wave][j][(i & (MT - 1)) * CH + NMF * g + d];
+    const float beta_lane = fq_quantise<FU, SPW>(U, xv, &qbuf[wave][0], wmax, a);
 
-    // ---- 4. products, cross-wave sum, rescale ----
     v4i acc[1] = {v4i{0, 0, 0, 0}};
     v4i sacc = {0, 0, 0, 0};
 #pragma unroll
@@ -572,15 +582,15 @@ __global__ __launch_bounds__(64 * FQ_MAX_WAVES) void k_gemv_fq(const uint8_t *__
     red[wave][lane] = kOffsetCodes<LAYOUT> ? offset_fix<LAYOUT>(acc[0], sacc) : acc[0];
     float sc[4]; // rescale of tokens 4g .. 4g + 3 (shuffled while all lanes are active)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) sc[rr] = token_scale(gamma, beta_of(4 * g + rr));
+    for (int rr = 0; rr < 4; ++rr) sc[rr] = token_scale(gamma, __shfl(beta_lane, (4 * g + rr) & 3));
     __syncthreads();
-    if (wave != 0 || 4 * g >= M) return; // lane (i, g) holds tokens 4g .. 4g + 3
+    if (wave != 0 || g != 0) return; // tokens 0..3: lanes of g = 0
     v4i tot = red[0][lane];
     for (int w = 1; w < KS; ++w) tot += red[w][lane];
     const int64_t n = tile * 16 + i;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-        if (4 * g + rr < M && n < N) store_out(Y, y_dtype, ldy, 4 * g + rr, n, tot[rr], sc[rr]);
+        if (rr < M && n < N) store_out(Y, y_dtype, ldy, rr, n, tot[rr], sc[rr]);
 }
 
 // ---------------------------------------------------------------------------
@@ -710,6 +720,114 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const uint8_t *__restrict
         s_rr = rr == 2 ? sc[2] : s_rr;
         s_rr = rr == 3 ? sc[3] : s_rr;
         if (mm < M && n < N) store_out(Y, y_dtype, ldy, mm, n, tot, s_rr);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_gemv_persist with the activation quantiser inside (1 to 4 tokens of fp32 /
+// bf16 rows; see fq_load / fq_quantise): the wave's activation loads, then
+// the first D weight tiles of the ring, then the rounding while those are in
+// flight.
+// ---------------------------------------------------------------------------
+constexpr int FQ_PERSIST_WAVES = 16;
+
+template <int LAYOUT, int XDT, int SPW, int TMAX, bool GUARD>
+__global__ __launch_bounds__(1024) void k_gemv_persist_fq(const uint8_t *__restrict__ P, int64_t KB, int64_t NT,
+                                                          const float *__restrict__ gamma_p,
+                                                          const void *__restrict__ X, int64_t ldx, int xbytes,
+                                                          int64_t M, int64_t N, int64_t K, void *__restrict__ Y,
+                                                          int y_dtype, int64_t ldy)
+{
+    using FU = FqUnits<LAYOUT, XDT, SPW>;
+    constexpr int NMF = FU::NMF;
+    constexpr int D = SPW >= 4 ? 2 : (SPW >= 2 ? 3 : 4);
+    extern __shared__ int red_dyn[]; // [TMAX][KS][4][64]
+    __shared__ v4i qbuf[FQ_PERSIST_WAVES][SPW * FU::UNITS];
+    __shared__ float wmax[FQ_PERSIST_WAVES][4];
+    const int KS = blockDim.x >> 6;
+    const int wave = wave_id(), lane = lane_id();
+    const int i = lane & 15, g = lane >> 4;
+    const int64_t nsteps = (KB + 3) / 4;
+    const int64_t G = gridDim.x;
+    const int ntiles = static_cast<int>((NT - blockIdx.x + G - 1) / G); // tiles of this workgroup (<= TMAX)
+    int nj = 0;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) nj += wave + static_cast<int64_t>(j) * KS < nsteps ? 1 : 0;
+    const FU U{lane, wave, KS, static_cast<int>(M), nj * static_cast<int>(M) * FU::CH, static_cast<int>(K),
+               static_cast<int>(ldx)};
+
+    uint4 xv[FU::NUW][FU::VL];
+    fq_load(U, X, xbytes, xv);
+
+    uint32_t boff[SPW]; // byte offset of this lane's weight chunk in a tile, per k-step
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+        const int64_t kb = 4 * (wave + static_cast<int64_t>(j) * KS) + g;
+        boff[j] = static_cast<uint32_t>(kb < KB ? kb : KB - 1) * 256u + static_cast<uint32_t>(i) * 16u;
+    }
+    auto load_tile = [&](int t, uint4 (&b)[SPW]) {
+        const int64_t tile = blockIdx.x + static_cast<int64_t>(t < ntiles ? t : ntiles - 1) * G;
+        const uint8_t *pt = P + tile * KB * 256;
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) b[j] = *reinterpret_cast<const uint4 *>(pt + boff[j]);
+    };
+    v4i acc[TMAX];
+    uint4 b[D][SPW];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) acc[t] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < D; ++t)
+        if (!GUARD || t < ntiles) load_tile(t, b[t]);
+    const float gamma = *gamma_p;
+    // keep every load above this point (see k_gemv_fq)
+    __builtin_amdgcn_sched_barrier(0);
+
+    v4i a[SPW][NMF];
+    const float beta_lane = fq_quantise<FU, SPW>(U, xv, &qbuf[wave][0], wmax, a);
+    float sc[4]; // rescale of tokens 4g .. 4g + 3 (shuffled while all lanes are active)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) sc[rr] = token_scale(gamma, __shfl(beta_lane, (4 * g + rr) & 3));
+    v4i sacc = {0, 0, 0, 0}; // sum_k q of the wave's k-steps (offset codes only)
+    if constexpr (kOffsetCodes<LAYOUT>) {
+#pragma unroll
+        for (int j = 0; j < SPW; ++j)
+            if (j < nj) act_sum_step<NMF>(a[j], sacc);
+    }
+
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+        if (t >= ntiles) break;
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+            if (j >= nj) break;
+            const uint4 bj[1] = {b[t % D][j]};
+            v4i accs[1] = {acc[t]};
+            gemv_step<LAYOUT, 1, NMF>(bj, a[j], accs);
+            acc[t] = accs[0];
+        }
+        if (!GUARD || t + D < ntiles) load_tile(t + D, b[t % D]);
+    }
+    int *red = red_dyn;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+        if (t >= ntiles) break;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            red[((t * KS + wave) * 4 + rr) * 64 + lane] =
+                kOffsetCodes<LAYOUT> ? offset_fix<LAYOUT>(acc[t][rr], sacc[rr]) : acc[t][rr];
+    }
+    __syncthreads();
+    // output group (t, rr): token 4g + rr, weight row i of tile t (tokens < 4: g = 0)
+    for (int task = wave; task < ntiles * 4; task += KS) {
+        const int t = task >> 2, rr = task & 3;
+        int tot = 0;
+        for (int w = 0; w < KS; ++w) tot += red[((t * KS + w) * 4 + rr) * 64 + lane];
+        const int64_t n = (blockIdx.x + t * G) * 16 + i;
+        float s_rr = sc[0];
+        s_rr = rr == 1 ? sc[1] : s_rr;
+        s_rr = rr == 2 ? sc[2] : s_rr;
+        s_rr = rr == 3 ? sc[3] : s_rr;
+        if (g == 0 && rr < M && n < N) store_out(Y, y_dtype, ldy, rr, n, tot, s_rr);
     }
 }
 
@@ -959,34 +1077,54 @@ static void launch_mfma_layout(const GemvArgs &a, hipStream_t stream)
     else launch_mfma_tw<LAYOUT, 1>(a, KB, NT, nsteps, stream);
 }
 
-// Shape of the fused-quantiser GEMV (k_gemv_fq): 1 to 4 tokens of fp32 /
-// bf16 input on shapes the per-tile kernel takes (not the persistent one),
-// with the per-tile kernel's wave count and at most FQ_MAX_SPW k-steps per
-// wave.  Alignment is checked separately (gemv_fq_ok).
+// The GEMV with the quantiser inside: 1 to 4 tokens of fp32 / bf16 input,
+// on the shapes and launch geometry of the kernel the int8 path would run:
+// the per-tile kernel with one tile per workgroup (k_gemv_fq, at most 10
+// waves, at most FQ_MAX_SPW k-steps per wave, b1 2) or the persistent one
+// (k_gemv_persist_fq, at most 2 k-steps per wave, b1 1), so that nothing
+// spills, and LDS for the rounding areas and the persistent kernel's partial
+// sums within the 160 KB of a CU.  Alignment
+// is checked separately (gemv_fq_ok).
 struct FqPlan {
     bool ok;
+    bool persist;
     int64_t KS; // waves per workgroup
     int spw;    // k-steps per wave (1, 2 or 4)
-    int mt;     // tokens the kernel takes (4)
+    GemvPlan gp; // the persistent kernel's geometry
 };
 
 static FqPlan fq_plan(int layout, int64_t M, int64_t N, int64_t K, int x_dtype)
 {
-    FqPlan f{false, 0, 0, 4};
+    FqPlan f{false, false, 0, 0, {}};
     // (16-token groups were measured slower than quantiser + GEMV: every
     // workgroup rounds all 16 x K values again; 2x on the 3B q layer)
     if (M < 1 || M > 4 || (x_dtype != DT_F32 && x_dtype != DT_BF16)) return f;
     const GemvPlan gp = gemv_plan(layout, M, N, K);
-    if (gp.persist || gp.tw != 1) return f;
     const int64_t NT = (N + 15) / 16;
     const int64_t kblk = layout == LAYOUT_I2 ? 64 : (layout == LAYOUT_B3 ? 80 : 128);
     const int64_t nsteps = ((K + kblk - 1) / kblk + 3) / 4;
+    const int64_t units = 4 * (4 * kblk / 16); // rounding units per k-step
+    const int64_t max_spw = layout == LAYOUT_B1 ? 2 : FQ_MAX_SPW;
+    if (gp.persist) {
+        // (the weight ring and TMAX accumulators leave registers for at
+        // most two k-steps per wave, one for b1)
+        if (gp.spw > (layout == LAYOUT_B1 ? 1 : 2)) return f;
+        const int64_t lds = static_cast<int64_t>(gp.tmax) * gp.KS * 4 * 64 * 4 +
+                            FQ_PERSIST_WAVES * gp.spw * units * 16 + FQ_PERSIST_WAVES * 4 * 4;
+        if (lds > 160 * 1024) return f;
+        f.ok = true;
+        f.persist = true;
+        f.KS = gp.KS;
+        f.spw = gp.spw;
+        f.gp = gp;
+        return f;
+    }
+    if (gp.tw != 1) return f;
     int64_t KS = (256 * 16 + NT - 1) / NT;
     KS = KS < 1 ? 1 : (KS > FQ_MAX_WAVES ? FQ_MAX_WAVES : KS);
     KS = KS > nsteps ? nsteps : KS;
     const int64_t spw = (nsteps + KS - 1) / KS;
-    // (b1 holds 8 operands per k-step: four k-steps per wave spill)
-    if (spw > (layout == LAYOUT_B1 ? 2 : FQ_MAX_SPW)) return f;
+    if (spw > max_spw) return f;
     f.ok = true;
     f.KS = KS;
     f.spw = spw <= 1 ? 1 : (spw <= 2 ? 2 : 4);
@@ -1006,6 +1144,30 @@ bool gemv_fq_ok(int layout, int64_t M, int64_t N, int64_t K, int x_dtype, const 
     return ((M - 1) * ldx + K) * es + 15 <= 0x7fffffff; // the buffer resource's byte range
 }
 
+template <int LAYOUT, int XDT, int SPW, int TMAX, bool GUARD>
+static void launch_persist_fq_kernel(const GemvArgs &a, const void *X, int64_t ldx, int xbytes, int64_t KB,
+                                     int64_t NT, const FqPlan &f, hipStream_t stream)
+{
+    auto *fn = &k_gemv_persist_fq<LAYOUT, XDT, SPW, TMAX, GUARD>;
+    const size_t lds = static_cast<size_t>(TMAX) * f.KS * 4 * 64 * sizeof(int);
+    // more than 64 KiB of LDS must be allowed explicitly (a host-side function
+    // attribute; nothing is enqueued)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(lds));
+    dim3 grid(static_cast<unsigned>(f.gp.wgs)), block(static_cast<unsigned>(f.KS * 64));
+    hipLaunchKernelGGL(fn, grid, block, lds, stream, a.P, KB, NT, a.gamma, X, ldx, xbytes, a.M, a.N, a.K, a.Y,
+                       a.y_dtype, a.ldy);
+}
+
+template <int LAYOUT, int XDT, int SPW>
+static void launch_persist_fq(const GemvArgs &a, const void *X, int64_t ldx, int xbytes, int64_t KB, int64_t NT,
+                              const FqPlan &f, hipStream_t stream)
+{
+    constexpr int TMAX = SPW >= 4 ? 4 : 8;
+    if (f.gp.guard) launch_persist_fq_kernel<LAYOUT, XDT, SPW, TMAX, true>(a, X, ldx, xbytes, KB, NT, f, stream);
+    else launch_persist_fq_kernel<LAYOUT, XDT, SPW, TMAX, false>(a, X, ldx, xbytes, KB, NT, f, stream);
+}
+
 template <int LAYOUT, int XDT>
 static void launch_fq_x(const GemvArgs &a, const void *X, int64_t ldx, const FqPlan &f, hipStream_t stream)
 {
@@ -1013,15 +1175,20 @@ static void launch_fq_x(const GemvArgs &a, const void *X, int64_t ldx, const FqP
     const int64_t KB = (a.K + StepShape<LAYOUT>::KBLK - 1) / StepShape<LAYOUT>::KBLK;
     constexpr int64_t ES = XDT == DT_F32 ? 4 : 2;
     const int xbytes = static_cast<int>((((a.M - 1) * ldx + a.K) * ES + 15) & ~int64_t(15));
+    if (f.persist) {
+        if (f.spw == 1) launch_persist_fq<LAYOUT, XDT, 1>(a, X, ldx, xbytes, KB, NT, f, stream);
+        else if constexpr (LAYOUT != LAYOUT_B1) launch_persist_fq<LAYOUT, XDT, 2>(a, X, ldx, xbytes, KB, NT, f, stream);
+        return;
+    }
     dim3 grid(static_cast<unsigned>(NT)), block(static_cast<unsigned>(f.KS * 64));
     if (f.spw == 1) {
-        hipLaunchKernelGGL((k_gemv_fq<LAYOUT, XDT, 1, 4>), grid, block, 0, stream, a.P, KB, NT, a.gamma, X, ldx, xbytes,
+        hipLaunchKernelGGL((k_gemv_fq<LAYOUT, XDT, 1>), grid, block, 0, stream, a.P, KB, NT, a.gamma, X, ldx, xbytes,
                            a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
     } else if (f.spw == 2) {
-        hipLaunchKernelGGL((k_gemv_fq<LAYOUT, XDT, 2, 4>), grid, block, 0, stream, a.P, KB, NT, a.gamma, X, ldx, xbytes,
+        hipLaunchKernelGGL((k_gemv_fq<LAYOUT, XDT, 2>), grid, block, 0, stream, a.P, KB, NT, a.gamma, X, ldx, xbytes,
                            a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
     } else if constexpr (LAYOUT != LAYOUT_B1) {
-        hipLaunchKernelGGL((k_gemv_fq<LAYOUT, XDT, 4, 4>), grid, block, 0, stream, a.P, KB, NT, a.gamma, X, ldx, xbytes,
+        hipLaunchKernelGGL((k_gemv_fq<LAYOUT, XDT, 4>), grid, block, 0, stream, a.P, KB, NT, a.gamma, X, ldx, xbytes,
                            a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
     }
 }
@@ -1047,7 +1214,11 @@ hipError_t launch_gemv_fq(const GemvArgs &a, const void *X, int x_dtype, int64_t
 void gemv_fq_kernel_name(int layout, int64_t M, int64_t N, int64_t K, int x_dtype, char *buf, size_t n)
 {
     const FqPlan f = fq_plan(layout, M, N, K, x_dtype);
-    snprintf(buf, n, "bl::k_gemv_fq<%d, %d, %d, %d>", layout, x_dtype, f.spw, f.mt);
+    if (f.persist)
+        snprintf(buf, n, "bl::k_gemv_persist_fq<%d, %d, %d, %d, %s>", layout, x_dtype, f.spw, f.gp.tmax,
+                 f.gp.guard ? "true" : "false");
+    else
+        snprintf(buf, n, "bl::k_gemv_fq<%d, %d, %d>", layout, x_dtype, f.spw);
 }
 
 void gemv_kernel_name(int layout, int64_t M, int64_t N, int64_t K, bool tiled, char *buf, size_t n)

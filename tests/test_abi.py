@@ -226,11 +226,13 @@ def test_product_kernel_names():
     kernel on request; None for requests the library rejects."""
     f = bl.bitlinear_product_kernel
     # 1-4 tokens of float input: the GEMV with the quantiser inside (aligned rows)
-    assert f(1, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemv_fq<0, 1, 2, 4>"
-    assert f(4, 3200, 8640, bl.LAYOUT_I2, bl.F32) == "bl::k_gemv_fq<0, 0, 4, 4>"
-    assert f(1, 3200, 3200, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemv_fq<1, 1, 1, 4>"
+    assert f(1, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemv_fq<0, 1, 2>"
+    assert f(4, 3200, 8640, bl.LAYOUT_I2, bl.F32) == "bl::k_gemv_fq<0, 0, 4>"
+    assert f(1, 3200, 3200, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemv_fq<1, 1, 1>"
     assert f(1, 3200, 3200, bl.LAYOUT_I2, bl.I8) == "bl::k_gemv_mfma<0, 1, 1, false>"
-    assert f(1, 8640, 3200, bl.LAYOUT_I2, bl.BF16).startswith("bl::k_gemv_persist<0, ")
+    assert f(1, 8640, 3200, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemv_persist_fq<0, 1, 1, 8, true>"
+    assert f(1, 8640, 3200, bl.LAYOUT_I2, bl.I8).startswith("bl::k_gemv_persist<0, ")
+    assert f(1, 28672, 8192, bl.LAYOUT_I2, bl.BF16).startswith("bl::k_gemv_persist<0, ")  # LDS: two launches
     assert f(16, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemv_mfma<0, 1, 1, true>"
     assert f(5, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemv_mfma<0, 1, 1, true>"  # one launch only up to 4 tokens
     assert f(16, 3200, 3200, bl.LAYOUT_I2, bl.I8) == "bl::k_gemv_mfma<0, 1, 1, false>"
@@ -251,7 +253,7 @@ def test_product_kernel_names():
     assert f(2048, 3200, 3200, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemm_mfma_i2<128, 256, 2, 4, 1>"
     assert f(4000, 4000, 130, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemm_mfma_i2<256, 256, 2, 2, 1>"
     assert f(2048, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == "bl::k_gemm_mfma_i2<128, 256, 2, 4, 1>"
-    assert f(1, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == "bl::k_gemv_fq<2, 1, 1, 4>"
+    assert f(1, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == "bl::k_gemv_fq<2, 1, 1>"
     assert f(1, 3200, 3200, bl.LAYOUT_B1, bl.I8) == "bl::k_gemv_mfma<2, 1, 1, false>"
     assert f(3, 64, 64, bl.LAYOUT_B1, bl.BF16, bl.ALGO_GEMV_ADDSUB) is None
     assert f(0, 64, 64, bl.LAYOUT_I2, bl.BF16) is None

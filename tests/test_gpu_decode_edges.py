@@ -119,6 +119,9 @@ FQ_CASES = [  # (layout, M, N, K)
     ("i2", 1, 50, 16), ("b3", 1, 3200, 3200), ("b3", 4, 333, 1001), ("b3", 2, 100, 80), ("b1", 1, 3200, 3200),
     ("b1", 3, 500, 1000), ("b1", 4, 64, 128),
     ("b3", 4, 3200, 8640), ("b1", 4, 3200, 8640),
+    # wide layers: the persistent kernel with the quantiser inside
+    ("i2", 1, 8640, 3200), ("i2", 4, 8640, 3200), ("i2", 3, 9000, 77), ("b3", 2, 8640, 1001), ("b3", 4, 8640, 3200),
+    ("b1", 1, 8640, 3200), ("b1", 3, 9000, 77),
 ]
 
 
@@ -128,7 +131,7 @@ def test_fused_quant_gemv(layout, M, N, K, xk):
     xdt = bl.BF16 if xk == "bf16" else bl.F32
     kname = bl.bitlinear_product_kernel(M, N, K, LAYOUTS[layout], xdt)
     log("fused quant gemv", layout, M, N, K, xk, kname)
-    assert kname.startswith("bl::k_gemv_fq<"), kname
+    assert kname.startswith(("bl::k_gemv_fq<", "bl::k_gemv_persist_fq<")), kname
     t = weights(layout, N, K, seed=M * 7 + N + K)
     x = (synth.activations_bf16 if xk == "bf16" else synth.activations_f32)(M, K, seed=N + 3 * K)
     # rows padded to 16 bytes (the one-launch path needs aligned rows)
