@@ -115,6 +115,84 @@ __global__ __launch_bounds__(1024) void k_quant_act_vec(const void *__restrict__
     if (threadIdx.x == 0) beta[m] = b;
 }
 
+// Many tokens (prefill): one wave per token row, 4 rows per workgroup.  A
+// lane issues all its 16-byte loads of the row (VPL of them) first, the row
+// maximum is a DPP reduction inside the wave (no barrier), and the lane
+// rounds and stores its own vectors.  Many more rows are in flight per CU
+// than with a workgroup per row.  Same arithmetic as k_quant_act_vec.
+constexpr int ROWS_WAVES = 4;
+template <int XDT, int VPL>
+__global__ __launch_bounds__(64 * ROWS_WAVES) void k_quant_act_rows(const void *__restrict__ X, int64_t M, int64_t K,
+                                                                    int64_t ldx, int8_t *__restrict__ Xq, int64_t ldq,
+                                                                    float *__restrict__ beta)
+{
+    constexpr int EPV = XDT == DT_F32 ? 4 : 8; // elements per 16-byte vector
+    const int64_t m = static_cast<int64_t>(blockIdx.x) * ROWS_WAVES + wave_id();
+    if (m >= M) return; // (whole wave: the reduction below stays within one row)
+    const int lane = lane_id();
+    const int64_t nvec = K / EPV;
+    const uint4 *row = reinterpret_cast<const uint4 *>(static_cast<const char *>(X) +
+                                                       m * ldx * (XDT == DT_F32 ? 4 : 2));
+    uint4 v[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+        const int64_t vi = lane + 64 * static_cast<int64_t>(j);
+        v[j] = vi < nvec ? row[vi] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    // |x| as bit patterns: non-negative binary32 / bfloat16 values order like
+    // their bits, so the maximum is an unsigned integer maximum (bf16: two
+    // halves at a time), with no unpacking to floats
+    float amax;
+    if constexpr (XDT == DT_F32) {
+        uint32_t mb = 0;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mb = max(mb, u[e] & 0x7fffffffu);
+        }
+        amax = __uint_as_float(mb);
+    } else {
+        typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+        us2 mb = {0, 0};
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mb = __builtin_elementwise_max(mb, __builtin_bit_cast(us2, u[e] & 0x7fff7fffu));
+        }
+        amax = __uint_as_float(static_cast<uint32_t>(mb[0] > mb[1] ? mb[0] : mb[1]) << 16);
+    }
+    const float b = wave_max_nonneg(amax);
+    const float s = token_step(b);
+    int8_t *qrow = Xq + m * ldq;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+        const int64_t vi = lane + 64 * static_cast<int64_t>(j);
+        if (vi >= nvec) continue;
+        const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        if constexpr (XDT == DT_F32) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w |= quant_one(__uint_as_float(u[e]), s) << (8 * e);
+            reinterpret_cast<uint32_t *>(qrow)[vi] = w;
+        } else {
+            uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                w0 |= quant_one(__uint_as_float(u[e] << 16), s) << (16 * e);
+                w0 |= quant_one(__uint_as_float(u[e] & 0xffff0000u), s) << (16 * e + 8);
+                w1 |= quant_one(__uint_as_float(u[e + 2] << 16), s) << (16 * e);
+                w1 |= quant_one(__uint_as_float(u[e + 2] & 0xffff0000u), s) << (16 * e + 8);
+            }
+            reinterpret_cast<uint2 *>(qrow)[vi] = make_uint2(w0, w1);
+        }
+    }
+    // zero the row padding [K, ldq)
+    for (int64_t k = K + 4 * lane; k < ldq; k += 4 * 64) *reinterpret_cast<uint32_t *>(qrow + k) = 0u;
+    if (lane == 0) beta[m] = b;
+}
+
 template <int XDT>
 static bool launch_vec(const void *X, int64_t M, int64_t K, int64_t ldx, int8_t *Xq, int64_t ldq, float *beta,
                        hipStream_t stream)
@@ -122,9 +200,22 @@ static bool launch_vec(const void *X, int64_t M, int64_t K, int64_t ldx, int8_t 
     constexpr int EPV = XDT == DT_F32 ? 4 : 8;
     constexpr int ES = XDT == DT_F32 ? 4 : 2;
     if (K % EPV || (ldx * ES) % 16 || (reinterpret_cast<uintptr_t>(X) & 15)) return false;
+    const int64_t nvec = K / EPV;
+    // many tokens: a wave per row, when a lane's share of the row fits its
+    // registers (K up to 6144 fp32 / 12288 bf16)
+    if (M >= 64 && nvec <= 64 * 24) {
+        const int64_t vpl = (nvec + 63) / 64;
+        dim3 grid(static_cast<unsigned>((M + ROWS_WAVES - 1) / ROWS_WAVES)), block(64 * ROWS_WAVES);
+        if (vpl <= 4) hipLaunchKernelGGL((k_quant_act_rows<XDT, 4>), grid, block, 0, stream, X, M, K, ldx, Xq, ldq, beta);
+        else if (vpl <= 8) hipLaunchKernelGGL((k_quant_act_rows<XDT, 8>), grid, block, 0, stream, X, M, K, ldx, Xq, ldq, beta);
+        else if (vpl <= 12) hipLaunchKernelGGL((k_quant_act_rows<XDT, 12>), grid, block, 0, stream, X, M, K, ldx, Xq, ldq, beta);
+        else if (vpl <= 16) hipLaunchKernelGGL((k_quant_act_rows<XDT, 16>), grid, block, 0, stream, X, M, K, ldx, Xq, ldq, beta);
+        else if (vpl <= 20) hipLaunchKernelGGL((k_quant_act_rows<XDT, 20>), grid, block, 0, stream, X, M, K, ldx, Xq, ldq, beta);
+        else hipLaunchKernelGGL((k_quant_act_rows<XDT, 24>), grid, block, 0, stream, X, M, K, ldx, Xq, ldq, beta);
+        return true;
+    }
     // about one 16-byte vector per thread (up to 1024 threads): the row's
     // loads all go out at once and each thread rounds only a few elements
-    const int64_t nvec = K / EPV;
     const int64_t threads = nvec <= 64 ? 64 : (nvec >= 1024 ? 1024 : (nvec + 63) / 64 * 64);
     const int64_t vpt = (nvec + threads - 1) / threads;
     dim3 grid(static_cast<unsigned>(M)), block(static_cast<unsigned>(threads));

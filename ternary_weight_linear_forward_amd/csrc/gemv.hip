@@ -349,28 +349,6 @@ __device__ __forceinline__ uint4 buffer_load_16(const void *base, int nbytes, in
 #endif
 }
 
-// Maximum of a non-negative value over the wave, in every lane: running
-// maxima within rows of 16 lanes (DPP row shifts; lanes shifted in from
-// outside the row read 0), then row 15's value broadcast into the next rows
-// (row_bcast:15, row_bcast:31), and lane 63's result read back.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_max_step(float x)
-{
-    const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, true);
-    return fmaxf(x, __int_as_float(y));
-}
-
-__device__ __forceinline__ float wave_max_nonneg(float v)
-{
-    v = dpp_max_step<0x111, 0xf>(v); // row_shr:1
-    v = dpp_max_step<0x112, 0xf>(v); // row_shr:2
-    v = dpp_max_step<0x114, 0xf>(v); // row_shr:4
-    v = dpp_max_step<0x118, 0xf>(v); // row_shr:8
-    v = dpp_max_step<0x142, 0xa>(v); // row_bcast:15
-    v = dpp_max_step<0x143, 0xc>(v); // row_bcast:31
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
 // This lane's activation units (see above) and their geometry.
 template <int LAYOUT, int XDT, int SPW>
 struct FqUnits {

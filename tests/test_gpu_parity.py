@@ -94,6 +94,24 @@ def act_cases():
     x[2] = (x[2] * 1e-40).astype(np.float32)         # subnormal row
     x[3] = np.float32(-3.0)                          # constant row
     yield "f32_edges", x
+    # 64 tokens or more: a wave per row (k_quant_act_rows), the same bits
+    yield "bf16_prefill_2048x3200", synth.activations_student_t_bf16(2048, 3200, seed=17)
+    yield "f32_100x2048", synth.activations_f32(100, 2048, seed=18)
+    yield "bf16_70x12288", synth.activations_bf16(70, 12288, seed=19)
+    yield "bf16_65x12296_vec_path", synth.activations_bf16(65, 12296, seed=20)
+    x = synth.activations_f32(67, 300, seed=21)      # 67 rows: the last workgroup partly empty
+    x[0] = 0.0
+    x[1, :7] = [127.0, 2.5, -2.5, 0.5, -0.5, 1.5, -127.0]
+    x[1, 7:] = 0.0
+    x[2] = (x[2] * 1e-40).astype(np.float32)
+    x[3] = np.float32(-3.0)
+    x[4] = np.float32(-0.0)
+    x[66, 5] = np.float32(3e38)
+    yield "f32_edges_67x300", x
+    xb = synth.activations_bf16(64, 1000, seed=22)
+    xb[7] = 0x8000                                   # bf16 -0.0 row
+    xb[9, 3] = 0x7f7f                                # bf16 largest finite
+    yield "bf16_edges_64x1000", xb
 
 
 @pytest.mark.parametrize("name,x", list(act_cases()), ids=[c[0] for c in act_cases()])
