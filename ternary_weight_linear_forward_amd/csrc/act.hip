@@ -9,9 +9,11 @@
 
 namespace bl {
 
+// Maximum of non-negative values over the workgroup (whole waves, every lane
+// active): DPP within each wave, then LDS across the waves.
 __device__ __forceinline__ float block_max(float v, float *red)
 {
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    v = wave_max_nonneg(v);
     const int nw = blockDim.x >> 6;
     if (lane_id() == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -249,11 +251,12 @@ hipError_t launch_quant_act(const void *X, int x_dtype, int64_t M, int64_t K, in
 namespace bl {
 
 // Tiled activation layout (bitlinear.h): one workgroup per token row m of the
-// G*16 padded rows.  A thread owns whole 16-element pieces of the row (16
-// consecutive k: one 16-byte operand slice), loads them all before the max,
-// then quantises from registers and stores each piece with one 16-byte store.
+// G*16 padded rows, up to 1024 threads.  A thread owns whole 16-element
+// pieces of the row (16 consecutive k: one 16-byte operand slice; about one
+// piece per thread), loads them all before the max, then quantises from
+// registers and stores each piece with one 16-byte store.
 template <int XDT, int PPT>
-__global__ __launch_bounds__(256) void k_quant_act_tiled(const void *__restrict__ X, int64_t M, int64_t K,
+__global__ __launch_bounds__(1024) void k_quant_act_tiled(const void *__restrict__ X, int64_t M, int64_t K,
                                                          int64_t ldx, int layout, int64_t nsteps,
                                                          int8_t *__restrict__ Xt, float *__restrict__ beta)
 {
@@ -324,14 +327,16 @@ static bool launch_tiled_ppt(const void *X, int64_t M, int64_t K, int64_t ldx, i
 {
     const int64_t nsteps = tiled_nsteps(K, layout);
     const int64_t npieces = nsteps * tiled_step_k(layout) / 16;
-    const int64_t ppt = (npieces + 255) / 256;
-    dim3 grid(static_cast<unsigned>((M + 15) / 16 * 16)), block(256);
+    const int64_t threads = npieces >= 1024 ? 1024 : (npieces + 63) / 64 * 64;
+    const int64_t ppt = (npieces + threads - 1) / threads;
+    dim3 grid(static_cast<unsigned>((M + 15) / 16 * 16)), block(static_cast<unsigned>(threads));
 #define BL_TILED(N) hipLaunchKernelGGL((k_quant_act_tiled<XDT, N>), grid, block, 0, stream, X, M, K, ldx, layout, nsteps, Xt, beta)
+    // (K <= 65536 for the tiled layout: at most 4096 pieces for i2 and b1,
+    // 4100 for b3, whose last few take the 8-piece variant)
     if (ppt <= 1) BL_TILED(1);
     else if (ppt <= 2) BL_TILED(2);
     else if (ppt <= 4) BL_TILED(4);
     else if (ppt <= 8) BL_TILED(8);
-    else if (ppt <= 16) BL_TILED(16);
     else return false;
 #undef BL_TILED
     return true;

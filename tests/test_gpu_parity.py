@@ -146,7 +146,7 @@ def untile(xt: np.ndarray, M: int, K: int, layout: str) -> np.ndarray:
 
 @pytest.mark.parametrize("layout", ["i2", "b3"])
 @pytest.mark.parametrize("M,K,kind", [(16, 256, "f32"), (5, 3200, "bf16"), (20, 333, "bf16"), (1, 80, "f32"),
-                                      (33, 8192, "bf16"), (3, 28672, "bf16")])
+                                      (33, 8192, "bf16"), (3, 28672, "bf16"), (5, 65500, "f32"), (2, 65536, "bf16")])
 def test_quantize_act_tiled(layout, M, K, kind):
     log("quantize_act_tiled", layout, M, K, kind)
     x = synth.activations_f32(M, K, seed=M + K) if kind == "f32" else synth.activations_bf16(M, K, seed=M + K)
