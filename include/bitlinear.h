@@ -136,8 +136,12 @@ int bitlinear_auto_algo(int64_t M, int64_t N, int64_t K, int layout, int x_dtype
  * Name of the product kernel a forward with these arguments launches (algo
  * AUTO resolved as above), as profilers print it without the argument list,
  * e.g. "bl::k_gemv_persist<0, 1, 8, true>"; NULL for invalid or unsupported
- * arguments.  The string lives in thread-local storage until the calling
- * thread's next call.  Host-only; enqueues nothing.
+ * arguments.  For 1 to 4 tokens of F32 / BF16 input it names the GEMV that
+ * quantises the activations itself ("bl::k_gemv_fq<...>" or
+ * "bl::k_gemv_persist_fq<...>"), which a forward runs when X and its rows
+ * are 16-byte aligned (otherwise: the quantiser, then the int8 GEMV).  The
+ * string lives in thread-local storage until the calling thread's next call.
+ * Host-only; enqueues nothing.
  */
 const char *bitlinear_product_kernel(int64_t M, int64_t N, int64_t K, int layout, int x_dtype, int algo);
 
@@ -216,9 +220,11 @@ int bitlinear_quantize_act_tiled(const void *X, int x_dtype, int64_t M, int64_t 
  * BitLinear forward: Y = rescale(quant(X) (x) T^T), T given packed in P.
  *   P        packed weights of T [N x K] in 'layout' (16-byte aligned).
  *   gamma    1 fp32 (device): the weight scale returned by quantize_weights.
- *   X        x_dtype F32 or BF16: quantised per token inside the call (the
- *            quantiser is fused with the product; its int8 output is staged
- *            in ws).  x_dtype I8: X is already quantised (16-byte aligned,
+ *   X        x_dtype F32 or BF16: quantised per token inside the call.  For
+ *            1 to 4 tokens on GEMV shapes, with X and ldx * element size
+ *            16-byte aligned, the GEMV quantises the rows itself (one
+ *            launch, ws untouched); otherwise the quantiser runs first and
+ *            its int8 output is staged in ws.  x_dtype I8: X is already quantised (16-byte aligned,
  *            ldx % 16 == 0, M rows of ldx bytes readable) and beta_in (fp32
  *            [M], device) gives beta.  x_dtype I8_TILED: X is
  *            bitlinear_act_tiled_bytes(M, K, layout) bytes in the tiled
