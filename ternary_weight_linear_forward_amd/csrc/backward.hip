@@ -20,154 +20,216 @@ namespace bl {
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
-// dX = gamma * dY @ T.  Workgroup: one token group (16 tokens, blockIdx.y)
-// and one 64-column k-block (blockIdx.x); its W waves split the N row tiles
-// (wave w takes tiles w, w+W, ...).  For a 16-row tile the wave multiplies
-// 4 row groups x 4 column groups: A = dY[16 tokens x 4 rows] (lane l: token
-// l%16, row l/16), B = T[4 rows x 16 columns] (lane l: row l/16, column
-// l%16, decoded from the packed word), D = dX[16 tokens x 16 columns] per
-// column group.  The W partial tiles meet in LDS; wave d stores column
-// group d, scaled by gamma.
+// Both gradients are C[p][q] = sum_t A[t][p] B[t][q] over a contraction index
+// t, computed by one body: a workgroup owns a 128 x 128 tile of C, 4 waves of
+// 64 x 64 (4 x 4 MFMA tiles of 16 x 16, v_mfma_f32_16x16x4f32), and the
+// contraction runs in stages of 32.  A stage's A [32 x 128] and B [32 x 128]
+// sit in LDS as fp32, double-buffered: each thread fetches its share of
+// stage s+1 from global memory into registers before the waves multiply
+// stage s, and writes it to the other buffer after.
+//   dW[n][k] = sum_m dY[m][n] Xhat[m][k]:   t = token, A = dY, B = Xhat
+//   dX[m][k] = gamma sum_n dY[m][n] T[n][k]: t = weight row, A = dY^T, B = T
+// MFMA operands: A tile i of a wave takes rows p = wp + 4 li + i (lane l:
+// li = l % 16, contraction row l / 16 of the k-step), B tile j columns
+// q = wq + 4 li + j, so a lane's four A (and four B) values of a k-step are
+// one 16-byte LDS read.  LDS rows are 144 floats apart: the 4 contraction
+// rows of a read fall in different banks.
 // ---------------------------------------------------------------------------
-constexpr int DX_MAX_WAVES = 8;
+constexpr int MM_T = 128;  // output tile edge
+constexpr int MM_S = 32;   // contraction rows per stage
+constexpr int MM_LD = 144; // LDS row stride in floats
 
-__global__ __launch_bounds__(64 * DX_MAX_WAVES) void k_bwd_dx(const uint8_t *__restrict__ P, int64_t KB,
-                                                             int64_t NT, const float *__restrict__ gamma_p,
-                                                             const float *__restrict__ dY, int64_t lddy, int64_t M,
-                                                             int64_t N, int64_t K, float *__restrict__ dX,
-                                                             int64_t lddx)
+template <class Stage>
+__device__ __forceinline__ void bwd_mm_body(const Stage &st, float (*sa)[MM_S][MM_LD], float (*sb)[MM_S][MM_LD],
+                                            int64_t nst, v4f (&acc)[4][4])
 {
-    __shared__ v4f red[DX_MAX_WAVES][4][64];
-    const int nw = blockDim.x >> 6;
     const int wave = wave_id(), lane = lane_id();
     const int li = lane & 15, lg = lane >> 4;
-    const int64_t kb = blockIdx.x;
-    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 16;
-    const int64_t ma = m0 + li; // token of this lane's A element
-    const bool mvalid = ma < M;
-    const float *dyrow = dY + (mvalid ? ma : 0) * lddy;
-    // column 16d + li of a chunk word d: li = 4s + j sits at bits 8j + 2s
-    const int sh = 8 * (li & 3) + 2 * (li >> 2);
-
-    v4f acc[4];
+    const int wp = (wave >> 1) * 64, wq = (wave & 1) * 64;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) acc[d] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t tile = wave; tile < NT; tile += nw) {
-        const uint8_t *cb = P + (tile * KB + kb) * 256;
-        uint4 ch[4];
-        float a[4];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            ch[rg] = *reinterpret_cast<const uint4 *>(cb + (4 * rg + lg) * 16);
-            const int64_t n = tile * 16 + 4 * rg + lg;
-            a[rg] = (mvalid && n < N) ? dyrow[n] : 0.0f;
-        }
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            const uint32_t w[4] = {ch[rg].x, ch[rg].y, ch[rg].z, ch[rg].w};
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const float b = static_cast<float>(static_cast<int>((w[d] >> sh) & 3u) - 1);
-                acc[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rg], b, acc[d], 0, 0, 0);
-            }
-        }
-    }
-#pragma unroll
-    for (int d = 0; d < 4; ++d) red[wave][d][lane] = acc[d];
+        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    typename Stage::Regs r;
+    st.fetch(0, r);
+    st.stash(r, sa[0], sb[0]);
     __syncthreads();
-    const float gamma = *gamma_p;
-    // D layout: lane l holds tokens 4 * (l/16) + r, column l%16 of the group
-    for (int d = wave; d < 4; d += nw) {
-        v4f tot = red[0][d][lane];
-        for (int w = 1; w < nw; ++w) tot += red[w][d][lane];
-        const int64_t k = kb * 64 + 16 * d + li;
+    for (int64_t s = 0; s < nst; ++s) {
+        const int buf = static_cast<int>(s & 1);
+        if (s + 1 < nst) st.fetch(s + 1, r); // in flight during the multiply
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t m = m0 + 4 * lg + r;
-            if (m < M && k < K) dX[m * lddx + k] = gamma * tot[r];
+        for (int ks = 0; ks < MM_S / 4; ++ks) {
+            const int t = 4 * ks + lg;
+            const float4 a4 = *reinterpret_cast<const float4 *>(&sa[buf][t][wp + 4 * li]);
+            const float4 b4 = *reinterpret_cast<const float4 *>(&sb[buf][t][wq + 4 * li]);
+            const float a[4] = {a4.x, a4.y, a4.z, a4.w}, b[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
         }
+        if (s + 1 < nst) st.stash(r, sa[buf ^ 1], sb[buf ^ 1]); // last read two stages ago
+        __syncthreads();
     }
 }
 
-// ---------------------------------------------------------------------------
-// dW = dY^T @ Xhat.  Workgroup: 64 rows n x 64 columns k of dW, 4 waves of
-// 32 x 32 (2 x 2 MFMA tiles); the contraction runs over the tokens, 4 per
-// MFMA, 4 MFMA k-steps (16 tokens) per loop trip with all their loads issued
-// first.  A = dY^T[16 rows x 4 tokens] (lane l: row l%16, token l/16),
-// B = Xhat[4 tokens x 16 columns] (lane l: token l/16, column l%16), with
-// Xhat = float(q) * r_m and r_m = beta_m / 127 rounded to binary32.
-// ---------------------------------------------------------------------------
+// Store a 128 x 128 tile: C[p][q] of wave tile (i, j), register r of lane l
+// is p = wp + 4 (4 (l / 16) + r) + i, q = wq + 4 (l % 16) + j.
+template <class Put>
+__device__ __forceinline__ void bwd_mm_store(const v4f (&acc)[4][4], int64_t p0, int64_t q0, int64_t P, int64_t Q, Put put)
+{
+    const int wave = wave_id(), lane = lane_id();
+    const int li = lane & 15, lg = lane >> 4;
+    const int64_t wp = p0 + (wave >> 1) * 64, wq = q0 + (wave & 1) * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t p = wp + 4 * (4 * lg + r) + i;
+            if (p >= P) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t q = wq + 4 * li + j;
+                if (q < Q) put(p, q, acc[i][j][r]);
+            }
+        }
+}
+
+// dX stage: A[t][p] = dY[m0 + p][n] (n = nb + t) staged transposed: thread
+// (p = tid / 2, half h = tid % 2) loads 16 consecutive n of token row p;
+// B[t][q] = T[nb + t][k0 + q] from the packed i2 words: thread (t = tid / 8,
+// c = tid % 8) unpacks the one word holding weights k0 + 16 c .. + 15 of row
+// nb + t.
+struct DxStage {
+    const uint8_t *P;
+    int64_t KB, M, N, K, lddy, m0, k0, nst;
+    const float *dY;
+    struct Regs {
+        float a[16];
+        uint32_t w;
+    };
+    __device__ __forceinline__ void fetch(int64_t s, Regs &r) const
+    {
+        const int tid = threadIdx.x;
+        const int64_t nb = s * MM_S;
+        {
+            const int64_t m = m0 + (tid >> 1), n = nb + 16 * (tid & 1);
+            const bool mv = m < M;
+            const float *row = dY + (mv ? m : 0) * lddy;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) r.a[e] = (mv && n + e < N) ? row[n + e] : 0.0f;
+        }
+        {
+            const int64_t n = nb + (tid >> 3), k = k0 + 16 * (tid & 7);
+            const bool v = n < N && k < K;
+            const int64_t nc = v ? n : 0, kc = v ? k : 0;
+            r.w = v ? *reinterpret_cast<const uint32_t *>(P + ((nc / 16) * KB + kc / 64) * 256 + (nc % 16) * 16 +
+                                                         ((kc % 64) / 16) * 4)
+                    : I2_ZERO_WORD;
+        }
+    }
+    __device__ __forceinline__ void stash(const Regs &r, float (*sa)[MM_LD], float (*sb)[MM_LD]) const
+    {
+        const int tid = threadIdx.x;
+        const int p = tid >> 1, t0 = 16 * (tid & 1);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sa[t0 + e][p] = r.a[e];
+        // weight 4s + j of the word sits at bits 8j + 2s (code c = T + 1);
+        // positions past K hold the zero code (padding) or the zero word
+        const int t = tid >> 3, c = 16 * (tid & 7);
+        float v[16];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[4 * s + j] = static_cast<float>(static_cast<int>((r.w >> (8 * j + 2 * s)) & 3u) - 1);
+#pragma unroll
+        for (int e = 0; e < 16; e += 4) *reinterpret_cast<float4 *>(&sb[t][c + e]) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+    }
+};
+
+// dW stage: A[t][p] = dY[mb + t][n0 + p], B[t][q] = Xhat[mb + t][k0 + q] =
+// float(q) * r_m, r_m = beta_m / 127 rounded to binary32: thread (t =
+// tid / 8, c = tid % 8) loads 16 consecutive values of each.
+struct DwStage {
+    const int8_t *Xq;
+    const float *beta, *dY;
+    int64_t ldq, lddy, M, N, K, n0, k0;
+    struct Regs {
+        float a[16], r;
+        int8_t x[16];
+    };
+    __device__ __forceinline__ void fetch(int64_t s, Regs &g) const
+    {
+        const int tid = threadIdx.x;
+        const int64_t m = s * MM_S + (tid >> 3);
+        const int c = 16 * (tid & 7);
+        const bool mv = m < M;
+        const int64_t mc = mv ? m : 0;
+        g.r = mv ? beta[mc] / 127.0f : 0.0f;
+        const float *yrow = dY + mc * lddy;
+        const int8_t *xrow = Xq + mc * ldq;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            g.a[e] = (mv && n0 + c + e < N) ? yrow[n0 + c + e] : 0.0f;
+            g.x[e] = (mv && k0 + c + e < K) ? xrow[k0 + c + e] : static_cast<int8_t>(0);
+        }
+    }
+    __device__ __forceinline__ void stash(const Regs &g, float (*sa)[MM_LD], float (*sb)[MM_LD]) const
+    {
+        const int tid = threadIdx.x;
+        const int t = tid >> 3, c = 16 * (tid & 7);
+#pragma unroll
+        for (int e = 0; e < 16; e += 4) {
+            *reinterpret_cast<float4 *>(&sa[t][c + e]) = make_float4(g.a[e], g.a[e + 1], g.a[e + 2], g.a[e + 3]);
+            *reinterpret_cast<float4 *>(&sb[t][c + e]) =
+                make_float4(static_cast<float>(g.x[e]) * g.r, static_cast<float>(g.x[e + 1]) * g.r,
+                            static_cast<float>(g.x[e + 2]) * g.r, static_cast<float>(g.x[e + 3]) * g.r);
+        }
+    }
+};
+
+__global__ __launch_bounds__(256) void k_bwd_dx(const uint8_t *__restrict__ P, int64_t KB,
+                                               const float *__restrict__ gamma_p, const float *__restrict__ dY,
+                                               int64_t lddy, int64_t M, int64_t N, int64_t K, float *__restrict__ dX,
+                                               int64_t lddx)
+{
+    __shared__ float sa[2][MM_S][MM_LD];
+    __shared__ float sb[2][MM_S][MM_LD];
+    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * MM_T, k0 = static_cast<int64_t>(blockIdx.x) * MM_T;
+    const DxStage st{P, KB, M, N, K, lddy, m0, k0, (N + MM_S - 1) / MM_S, dY};
+    v4f acc[4][4];
+    bwd_mm_body(st, sa, sb, st.nst, acc);
+    const float gamma = *gamma_p;
+    bwd_mm_store(acc, m0, k0, M, K, [&](int64_t m, int64_t k, float v) { dX[m * lddx + k] = gamma * v; });
+}
+
 __global__ __launch_bounds__(256) void k_bwd_dw(const int8_t *__restrict__ Xq, int64_t ldq,
                                                const float *__restrict__ beta, const float *__restrict__ dY,
                                                int64_t lddy, int64_t M, int64_t N, int64_t K, float *__restrict__ dW,
                                                int64_t lddw)
 {
-    constexpr int U = 4; // MFMA k-steps (of 4 tokens) per trip
-    const int wave = wave_id(), lane = lane_id();
-    const int li = lane & 15, lg = lane >> 4;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * 64 + (wave >> 1) * 32;
-    const int64_t k0 = static_cast<int64_t>(blockIdx.x) * 64 + (wave & 1) * 32;
-    int64_t nn[2], kk[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        nn[i] = n0 + 16 * i + li;
-        kk[i] = k0 + 16 * i + li;
-    }
-    v4f acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t mb = 0; mb < M; mb += 4 * U) {
-        float a[U][2], b[U][2];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t m = mb + 4 * u + lg;
-            const bool mv = m < M;
-            const int64_t mc = mv ? m : 0;
-            const float r = mv ? beta[mc] / 127.0f : 0.0f;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) a[u][i] = (mv && nn[i] < N) ? dY[mc * lddy + nn[i]] : 0.0f;
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                b[u][j] = (mv && kk[j] < K) ? static_cast<float>(Xq[mc * ldq + kk[j]]) * r : 0.0f;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
-    }
-    // D layout: lane l holds rows 4 * (l/16) + r, column l%16 of the tile
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t n = n0 + 16 * i + 4 * lg + r;
-            if (n >= N) continue;
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                if (kk[j] < K) dW[n * lddw + kk[j]] = acc[i][j][r];
-        }
+    __shared__ float sa[2][MM_S][MM_LD];
+    __shared__ float sb[2][MM_S][MM_LD];
+    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * MM_T, k0 = static_cast<int64_t>(blockIdx.x) * MM_T;
+    const DwStage st{Xq, beta, dY, ldq, lddy, M, N, K, n0, k0};
+    v4f acc[4][4];
+    bwd_mm_body(st, sa, sb, (M + MM_S - 1) / MM_S, acc);
+    bwd_mm_store(acc, n0, k0, N, K, [&](int64_t n, int64_t k, float v) { dW[n * lddw + k] = v; });
 }
 
 hipError_t launch_bwd_dx(const uint8_t *P2, const float *gamma, int64_t M, int64_t N, int64_t K, const float *dY,
                          int64_t lddy, float *dX, int64_t lddx, hipStream_t stream)
 {
-    const int64_t NT = (N + 15) / 16, KB = (K + 63) / 64;
-    const int64_t nw = NT < DX_MAX_WAVES ? NT : DX_MAX_WAVES;
-    dim3 grid(static_cast<unsigned>(KB), static_cast<unsigned>((M + 15) / 16));
-    hipLaunchKernelGGL(k_bwd_dx, grid, dim3(static_cast<unsigned>(64 * nw)), 0, stream, P2, KB, NT, gamma, dY, lddy,
-                       M, N, K, dX, lddx);
+    const int64_t KB = (K + 63) / 64;
+    dim3 grid(static_cast<unsigned>((K + MM_T - 1) / MM_T), static_cast<unsigned>((M + MM_T - 1) / MM_T));
+    hipLaunchKernelGGL(k_bwd_dx, grid, dim3(256), 0, stream, P2, KB, gamma, dY, lddy, M, N, K, dX, lddx);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dw(const int8_t *Xq, int64_t ldq, const float *beta, int64_t M, int64_t N, int64_t K,
                          const float *dY, int64_t lddy, float *dW, int64_t lddw, hipStream_t stream)
 {
-    dim3 grid(static_cast<unsigned>((K + 63) / 64), static_cast<unsigned>((N + 63) / 64));
+    dim3 grid(static_cast<unsigned>((K + MM_T - 1) / MM_T), static_cast<unsigned>((N + MM_T - 1) / MM_T));
     hipLaunchKernelGGL(k_bwd_dw, grid, dim3(256), 0, stream, Xq, ldq, beta, dY, lddy, M, N, K, dW, lddw);
     return hipGetLastError();
 }
