@@ -74,9 +74,12 @@ __device__ __forceinline__ void bwd_mm_body(const Stage &st, float (*sa)[MM_S][M
 }
 
 // Store a 128 x 128 tile: C[p][q] of wave tile (i, j), register r of lane l
-// is p = wp + 4 (4 (l / 16) + r) + i, q = wq + 4 (l % 16) + j.
-template <class Put>
-__device__ __forceinline__ void bwd_mm_store(const v4f (&acc)[4][4], int64_t p0, int64_t q0, int64_t P, int64_t Q, Put put)
+// is p = wp + 4 (4 (l / 16) + r) + i, q = wq + 4 (l % 16) + j, so the four
+// tiles j of a lane are 4 consecutive columns: one 16-byte store where the
+// row is 16-byte aligned (vec) and all four are in range.
+template <class Put, class Put4>
+__device__ __forceinline__ void bwd_mm_store(const v4f (&acc)[4][4], int64_t p0, int64_t q0, int64_t P, int64_t Q,
+                                             bool vec, Put put, Put4 put4)
 {
     const int wave = wave_id(), lane = lane_id();
     const int li = lane & 15, lg = lane >> 4;
@@ -87,6 +90,10 @@ __device__ __forceinline__ void bwd_mm_store(const v4f (&acc)[4][4], int64_t p0,
         for (int r = 0; r < 4; ++r) {
             const int64_t p = wp + 4 * (4 * lg + r) + i;
             if (p >= P) continue;
+            if (vec && wq + 4 * li + 3 < Q) {
+                put4(p, wq + 4 * li, make_float4(acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]));
+                continue;
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t q = wq + 4 * li + j;
@@ -200,7 +207,12 @@ __global__ __launch_bounds__(256) void k_bwd_dx(const uint8_t *__restrict__ P, i
     v4f acc[4][4];
     bwd_mm_body(st, sa, sb, st.nst, acc);
     const float gamma = *gamma_p;
-    bwd_mm_store(acc, m0, k0, M, K, [&](int64_t m, int64_t k, float v) { dX[m * lddx + k] = gamma * v; });
+    const bool vec = (reinterpret_cast<uintptr_t>(dX) & 15) == 0 && (lddx & 3) == 0;
+    bwd_mm_store(
+        acc, m0, k0, M, K, vec, [&](int64_t m, int64_t k, float v) { dX[m * lddx + k] = gamma * v; },
+        [&](int64_t m, int64_t k, float4 v) {
+            *reinterpret_cast<float4 *>(dX + m * lddx + k) = make_float4(gamma * v.x, gamma * v.y, gamma * v.z, gamma * v.w);
+        });
 }
 
 __global__ __launch_bounds__(256) void k_bwd_dw(const int8_t *__restrict__ Xq, int64_t ldq,
@@ -214,14 +226,173 @@ __global__ __launch_bounds__(256) void k_bwd_dw(const int8_t *__restrict__ Xq, i
     const DwStage st{Xq, beta, dY, ldq, lddy, M, N, K, n0, k0};
     v4f acc[4][4];
     bwd_mm_body(st, sa, sb, (M + MM_S - 1) / MM_S, acc);
-    bwd_mm_store(acc, n0, k0, N, K, [&](int64_t n, int64_t k, float v) { dW[n * lddw + k] = v; });
+    const bool vec = (reinterpret_cast<uintptr_t>(dW) & 15) == 0 && (lddw & 3) == 0;
+    bwd_mm_store(
+        acc, n0, k0, N, K, vec, [&](int64_t n, int64_t k, float v) { dW[n * lddw + k] = v; },
+        [&](int64_t n, int64_t k, float4 v) { *reinterpret_cast<float4 *>(dW + n * lddw + k) = v; });
 }
+
+// ---------------------------------------------------------------------------
+// Few tokens (the 128 x 128 tiles below would leave most CUs idle).
+// dX = gamma * dY @ T.  Workgroup: one token group (16 tokens, blockIdx.y)
+// and one 64-column k-block (blockIdx.x); its W waves split the N row tiles
+// (wave w takes tiles w, w+W, ...).  For a 16-row tile the wave multiplies
+// 4 row groups x 4 column groups: A = dY[16 tokens x 4 rows] (lane l: token
+// l%16, row l/16), B = T[4 rows x 16 columns] (lane l: row l/16, column
+// l%16, decoded from the packed word), D = dX[16 tokens x 16 columns] per
+// column group.  The W partial tiles meet in LDS; wave d stores column
+// group d, scaled by gamma.
+// ---------------------------------------------------------------------------
+constexpr int DX_MAX_WAVES = 8;
+
+__global__ __launch_bounds__(64 * DX_MAX_WAVES) void k_bwd_dx_few(const uint8_t *__restrict__ P, int64_t KB,
+                                                             int64_t NT, const float *__restrict__ gamma_p,
+                                                             const float *__restrict__ dY, int64_t lddy, int64_t M,
+                                                             int64_t N, int64_t K, float *__restrict__ dX,
+                                                             int64_t lddx)
+{
+    __shared__ v4f red[DX_MAX_WAVES][4][64];
+    const int nw = blockDim.x >> 6;
+    const int wave = wave_id(), lane = lane_id();
+    const int li = lane & 15, lg = lane >> 4;
+    const int64_t kb = blockIdx.x;
+    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 16;
+    const int64_t ma = m0 + li; // token of this lane's A element
+    const bool mvalid = ma < M;
+    const float *dyrow = dY + (mvalid ? ma : 0) * lddy;
+    // column 16d + li of a chunk word d: li = 4s + j sits at bits 8j + 2s
+    const int sh = 8 * (li & 3) + 2 * (li >> 2);
+
+    v4f acc[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) acc[d] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t tile = wave; tile < NT; tile += nw) {
+        const uint8_t *cb = P + (tile * KB + kb) * 256;
+        uint4 ch[4];
+        float a[4];
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            ch[rg] = *reinterpret_cast<const uint4 *>(cb + (4 * rg + lg) * 16);
+            const int64_t n = tile * 16 + 4 * rg + lg;
+            a[rg] = (mvalid && n < N) ? dyrow[n] : 0.0f;
+        }
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const uint32_t w[4] = {ch[rg].x, ch[rg].y, ch[rg].z, ch[rg].w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const float b = static_cast<float>(static_cast<int>((w[d] >> sh) & 3u) - 1);
+                acc[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rg], b, acc[d], 0, 0, 0);
+            }
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) red[wave][d][lane] = acc[d];
+    __syncthreads();
+    const float gamma = *gamma_p;
+    // D layout: lane l holds tokens 4 * (l/16) + r, column l%16 of the group
+    for (int d = wave; d < 4; d += nw) {
+        v4f tot = red[0][d][lane];
+        for (int w = 1; w < nw; ++w) tot += red[w][d][lane];
+        const int64_t k = kb * 64 + 16 * d + li;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t m = m0 + 4 * lg + r;
+            if (m < M && k < K) dX[m * lddx + k] = gamma * tot[r];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dW = dY^T @ Xhat.  Workgroup: 64 rows n x 64 columns k of dW, 4 waves of
+// 32 x 32 (2 x 2 MFMA tiles); the contraction runs over the tokens, 4 per
+// MFMA, 4 MFMA k-steps (16 tokens) per loop trip with all their loads issued
+// first.  A = dY^T[16 rows x 4 tokens] (lane l: row l%16, token l/16),
+// B = Xhat[4 tokens x 16 columns] (lane l: token l/16, column l%16), with
+// Xhat = float(q) * r_m and r_m = beta_m / 127 rounded to binary32.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_bwd_dw_few(const int8_t *__restrict__ Xq, int64_t ldq,
+                                               const float *__restrict__ beta, const float *__restrict__ dY,
+                                               int64_t lddy, int64_t M, int64_t N, int64_t K, float *__restrict__ dW,
+                                               int64_t lddw)
+{
+    constexpr int U = 4; // MFMA k-steps (of 4 tokens) per trip
+    const int wave = wave_id(), lane = lane_id();
+    const int li = lane & 15, lg = lane >> 4;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * 64 + (wave >> 1) * 32;
+    const int64_t k0 = static_cast<int64_t>(blockIdx.x) * 64 + (wave & 1) * 32;
+    int64_t nn[2], kk[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        nn[i] = n0 + 16 * i + li;
+        kk[i] = k0 + 16 * i + li;
+    }
+    v4f acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t mb = 0; mb < M; mb += 4 * U) {
+        float a[U][2], b[U][2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t m = mb + 4 * u + lg;
+            const bool mv = m < M;
+            const int64_t mc = mv ? m : 0;
+            const float r = mv ? beta[mc] / 127.0f : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) a[u][i] = (mv && nn[i] < N) ? dY[mc * lddy + nn[i]] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                b[u][j] = (mv && kk[j] < K) ? static_cast<float>(Xq[mc * ldq + kk[j]]) * r : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
+    }
+    // D layout: lane l holds rows 4 * (l/16) + r, column l%16 of the tile
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t n = n0 + 16 * i + 4 * lg + r;
+            if (n >= N) continue;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                if (kk[j] < K) dW[n * lddw + kk[j]] = acc[i][j][r];
+        }
+}
+
+// The 128 x 128 dX tiles number ceil(M / 128) ceil(K / 128); below one per
+// CU the small-batch kernel, whose workgroups cover 16 tokens x 64 columns,
+// keeps more of the chip busy.  dW always has ceil(N / 128) ceil(K / 128)
+// tiles; its small-batch kernel only avoids staging 32 tokens of which most
+// are padding.
+static bool bwd_dx_few(int64_t M, int64_t K)
+{
+    return ((M + MM_T - 1) / MM_T) * ((K + MM_T - 1) / MM_T) < 256;
+}
+
+static bool bwd_dw_few(int64_t M) { return M < MM_S; }
 
 hipError_t launch_bwd_dx(const uint8_t *P2, const float *gamma, int64_t M, int64_t N, int64_t K, const float *dY,
                          int64_t lddy, float *dX, int64_t lddx, hipStream_t stream)
 {
     const int64_t KB = (K + 63) / 64;
-    dim3 grid(static_cast<unsigned>((K + MM_T - 1) / MM_T), static_cast<unsigned>((M + MM_T - 1) / MM_T));
+    const int64_t mt = (M + MM_T - 1) / MM_T, kt = (K + MM_T - 1) / MM_T;
+    if (bwd_dx_few(M, K)) {
+        const int64_t NT = (N + 15) / 16;
+        const int64_t nw = NT < DX_MAX_WAVES ? NT : DX_MAX_WAVES;
+        dim3 grid(static_cast<unsigned>(KB), static_cast<unsigned>((M + 15) / 16));
+        hipLaunchKernelGGL(k_bwd_dx_few, grid, dim3(static_cast<unsigned>(64 * nw)), 0, stream, P2, KB, NT, gamma, dY,
+                           lddy, M, N, K, dX, lddx);
+        return hipGetLastError();
+    }
+    dim3 grid(static_cast<unsigned>(kt), static_cast<unsigned>(mt));
     hipLaunchKernelGGL(k_bwd_dx, grid, dim3(256), 0, stream, P2, KB, gamma, dY, lddy, M, N, K, dX, lddx);
     return hipGetLastError();
 }
@@ -229,6 +400,11 @@ hipError_t launch_bwd_dx(const uint8_t *P2, const float *gamma, int64_t M, int64
 hipError_t launch_bwd_dw(const int8_t *Xq, int64_t ldq, const float *beta, int64_t M, int64_t N, int64_t K,
                          const float *dY, int64_t lddy, float *dW, int64_t lddw, hipStream_t stream)
 {
+    if (bwd_dw_few(M)) {
+        dim3 grid(static_cast<unsigned>((K + 63) / 64), static_cast<unsigned>((N + 63) / 64));
+        hipLaunchKernelGGL(k_bwd_dw_few, grid, dim3(256), 0, stream, Xq, ldq, beta, dY, lddy, M, N, K, dW, lddw);
+        return hipGetLastError();
+    }
     dim3 grid(static_cast<unsigned>((K + MM_T - 1) / MM_T), static_cast<unsigned>((N + MM_T - 1) / MM_T));
     hipLaunchKernelGGL(k_bwd_dw, grid, dim3(256), 0, stream, Xq, ldq, beta, dY, lddy, M, N, K, dW, lddw);
     return hipGetLastError();

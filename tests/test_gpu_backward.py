@@ -4,7 +4,9 @@ dW = dY^T @ Xhat from the forward's int8 activations and beta, against the
 oracle's binary64 products.  Both GPU results are fp32 sums in an unspecified
 order, so the bar is the summation bound: |got - want| <= (n + 2) * 2^-24 *
 sum |terms| per element (n the contraction length), plus bit-exact zeros
-where every term is zero."""
+where every term is zero.  Batches below 32 tokens (dW), or with fewer than
+256 tiles of 128 x 128 (dX), take the small-batch kernels; the rest the
+tiled ones, with 16-byte stores on aligned rows and single ones otherwise."""
 import numpy as np
 import pytest
 
@@ -42,7 +44,7 @@ def weights(layout, N, K, seed):
 
 @pytest.mark.parametrize("layout", ["i2", "b3", "b1"])
 @pytest.mark.parametrize("M,N,K", [(1, 3200, 3200), (4, 130, 333), (16, 8640, 3200), (17, 100, 64), (3, 48, 1),
-                                   (300, 257, 700), (1024, 1000, 3200)])
+                                   (300, 257, 700), (1024, 1000, 3200), (1100, 130, 3900), (1030, 70, 4001)])
 def test_backward_dx(layout, M, N, K):
     log("backward dx", layout, M, N, K)
     t = weights(layout, N, K, seed=M + 3 * N + K)
@@ -56,7 +58,7 @@ def test_backward_dx(layout, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 3200, 3200), (4, 130, 333), (16, 8640, 3200), (17, 100, 65), (5, 1, 7),
-                                   (300, 257, 700), (2048, 640, 1024)])
+                                   (300, 257, 700), (2048, 640, 1024), (33, 100, 65), (40, 129, 1030)])
 def test_backward_dw(M, N, K):
     log("backward dw", M, N, K)
     x = synth.activations_bf16(M, K, seed=M + K)
