@@ -427,10 +427,10 @@ def run_backward(args, wl, jobs, layout, ncopies, stream, dev):
                     raise bl.BitlinearError(st, "backward_dw")
 
             for name, fn, nbytes in (
-                    ("bl::k_bwd_dx", run_dx,
+                    (bl.bitlinear_backward_kernel(M, layer.N, layer.K, 0), run_dx,
                      L["P"][0].numel() + 4 * M * layer.N + 4 * M * layer.K
                      + (2 * bl.bitlinear_packed_bytes(layer.N, layer.K, bl.LAYOUT_I2) if nws > 0 else 0)),
-                    ("bl::k_bwd_dw", run_dw, M * layer.K + 4 * M + 4 * M * layer.N + 4 * layer.N * layer.K)):
+                    (bl.bitlinear_backward_kernel(M, layer.N, layer.K, 1), run_dw, M * layer.K + 4 * M + 4 * M * layer.N + 4 * layer.N * layer.K)):
                 fn(0)
                 torch.cuda.synchronize()
                 g = torch.cuda.CUDAGraph()

@@ -289,6 +289,14 @@ int bitlinear_backward_dx(const uint8_t *P, int layout, const float *gamma, int6
 int bitlinear_backward_dw(const int8_t *Xq, int64_t ldq, const float *beta, int64_t M, int64_t N, int64_t K,
                           const float *dY, int64_t lddy, float *dW, int64_t lddw, void *stream);
 
+/*
+ * Name of the kernel a backward call with these sizes launches (which = 0:
+ * bitlinear_backward_dx, 1: bitlinear_backward_dw), e.g. "bl::k_bwd_dx" or,
+ * for small batches, "bl::k_bwd_dx_few"; NULL for sizes or a 'which' the
+ * calls reject.  A static string; host-only, enqueues nothing.
+ */
+const char *bitlinear_backward_kernel(int64_t M, int64_t N, int64_t K, int which);
+
 #ifdef __cplusplus
 }
 #endif

@@ -72,6 +72,7 @@ _SIGNATURES = {
     "bitlinear_quantize_act": ([_P, _INT, _I64, _I64, _I64, _P, _I64, _P, _P], _INT),
     "bitlinear_forward": ([_P, _INT, _P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P, _INT, _I64, _P, _I64, _P], _INT),
     "bitlinear_backward_dx_workspace_bytes": ([_I64, _I64, _INT], _I64),
+    "bitlinear_backward_kernel": ([_I64, _I64, _I64, _INT], ctypes.c_char_p),
     "bitlinear_backward_dx": ([_P, _INT, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P], _INT),
     "bitlinear_backward_dw": ([_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P], _INT),
     "bitlinear_forward_algo": (
@@ -127,6 +128,11 @@ def bitlinear_auto_algo(M: int, N: int, K: int, layout: int, x_dtype: int) -> in
 
 def bitlinear_product_kernel(M: int, N: int, K: int, layout: int, x_dtype: int, algo: int = 0):
     r = _lib.bitlinear_product_kernel(M, N, K, layout, x_dtype, algo)
+    return None if r is None else r.decode()
+
+
+def bitlinear_backward_kernel(M: int, N: int, K: int, which: int):
+    r = _lib.bitlinear_backward_kernel(M, N, K, which)
     return None if r is None else r.decode()
 
 

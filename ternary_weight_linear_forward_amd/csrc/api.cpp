@@ -425,6 +425,14 @@ int bitlinear_backward_dx(const uint8_t *P, int layout, const float *gamma, int6
     return status_of(bl::launch_bwd_dx(p2, gamma, M, N, K, dY, lddy, dX, lddx, st));
 }
 
+const char *bitlinear_backward_kernel(int64_t M, int64_t N, int64_t K, int which)
+{
+    if (M < 1 || M > BITLINEAR_MAX_M || N < 1 || K < 1 || K > BITLINEAR_MAX_K || N > kMaxElems / K ||
+        (which != 0 && which != 1))
+        return nullptr;
+    return bl::bwd_kernel_name(which == 0, M, K);
+}
+
 int bitlinear_backward_dw(const int8_t *Xq, int64_t ldq, const float *beta, int64_t M, int64_t N, int64_t K,
                           const float *dY, int64_t lddy, float *dW, int64_t lddw, void *stream)
 {

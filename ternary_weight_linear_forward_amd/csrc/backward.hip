@@ -379,6 +379,12 @@ static bool bwd_dx_few(int64_t M, int64_t K)
 
 static bool bwd_dw_few(int64_t M) { return M < MM_S; }
 
+const char *bwd_kernel_name(bool dx, int64_t M, int64_t K)
+{
+    if (dx) return bwd_dx_few(M, K) ? "bl::k_bwd_dx_few" : "bl::k_bwd_dx";
+    return bwd_dw_few(M) ? "bl::k_bwd_dw_few" : "bl::k_bwd_dw";
+}
+
 hipError_t launch_bwd_dx(const uint8_t *P2, const float *gamma, int64_t M, int64_t N, int64_t K, const float *dY,
                          int64_t lddy, float *dX, int64_t lddx, hipStream_t stream)
 {

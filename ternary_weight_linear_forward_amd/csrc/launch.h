@@ -78,6 +78,9 @@ bool gemm_b3_native(int64_t M, int64_t N);
 
 // Straight-through-estimator gradients (backward.hip): dX from i2-packed
 // weights, dW from the forward's int8 activations and beta.
+// Name of the kernel bitlinear_backward_dx (dx) or _dw (!dx) launches for M
+// tokens and K columns.
+const char *bwd_kernel_name(bool dx, int64_t M, int64_t K);
 hipError_t launch_bwd_dx(const uint8_t *P2, const float *gamma, int64_t M, int64_t N, int64_t K, const float *dY,
                          int64_t lddy, float *dX, int64_t lddx, hipStream_t stream);
 hipError_t launch_bwd_dw(const int8_t *Xq, int64_t ldq, const float *beta, int64_t M, int64_t N, int64_t K,

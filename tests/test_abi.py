@@ -220,6 +220,20 @@ def test_auto_algo_dispatch():
     assert f(16, 16, 16, bl.LAYOUT_I2, 9) == -1
 
 
+def test_backward_kernel_names():
+    """dX takes the small-batch kernel while its 128 x 128 tiles number fewer
+    than 256, dW below 32 tokens; None for sizes the calls reject."""
+    f = bl.bitlinear_backward_kernel
+    assert f(1, 3200, 3200, 0) == "bl::k_bwd_dx_few"
+    assert f(2048, 3200, 3200, 0) == "bl::k_bwd_dx"  # 16 x 25 = 400 tiles
+    assert f(1280, 3200, 3200, 0) == "bl::k_bwd_dx_few"  # 10 x 25 = 250 tiles
+    assert f(1408, 3200, 3200, 0) == "bl::k_bwd_dx"  # 11 x 25 = 275 tiles
+    assert f(176, 8192, 8192, 0) == "bl::k_bwd_dx_few"
+    assert f(31, 3200, 3200, 1) == "bl::k_bwd_dw_few"
+    assert f(32, 3200, 3200, 1) == "bl::k_bwd_dw"
+    assert f(0, 3200, 3200, 0) is None and f(4, 3200, 3200, 2) is None and f(4, 0, 3200, 1) is None
+
+
 def test_product_kernel_names():
     """The kernel-name query follows the dispatch: GEMV kernels for few tokens
     (the persistent one for wide layers), GEMM tiles for prefill, the add/sub
