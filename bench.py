@@ -409,7 +409,7 @@ def run_backward(args, wl, jobs, layout, ncopies, stream, dev):
             xq, beta = bl.quantize_act(x, stream=stream)
             dx = torch.empty((M, layer.K), dtype=torch.float32, device=dev)
             dw = torch.empty((layer.N, layer.K), dtype=torch.float32, device=dev)
-            nws = bl.bitlinear_backward_dx_workspace_bytes(layer.N, layer.K, layout)
+            nws = bl.bitlinear_backward_dx_workspace_bytes(M, layer.N, layer.K, layout)
             ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
 
             def run_dx(c, L=L, layer=layer, M=M, dy=dy, dx=dx, ws=ws, nws=nws):
@@ -429,7 +429,7 @@ def run_backward(args, wl, jobs, layout, ncopies, stream, dev):
             for name, fn, nbytes in (
                     (bl.bitlinear_backward_kernel(M, layer.N, layer.K, 0), run_dx,
                      L["P"][0].numel() + 4 * M * layer.N + 4 * M * layer.K
-                     + (2 * bl.bitlinear_packed_bytes(layer.N, layer.K, bl.LAYOUT_I2) if nws > 0 else 0)),
+                     + (2 * bl.bitlinear_packed_bytes(layer.N, layer.K, bl.LAYOUT_I2) if layout != bl.LAYOUT_I2 else 0)),
                     (bl.bitlinear_backward_kernel(M, layer.N, layer.K, 1), run_dw, M * layer.K + 4 * M + 4 * M * layer.N + 4 * layer.N * layer.K)):
                 fn(0)
                 torch.cuda.synchronize()

@@ -261,17 +261,23 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
  * (n + 2) * 2^-24 of the sum of the absolute terms, n the contraction length).
  */
 
-/* Workspace bytes bitlinear_backward_dx needs (b3 / b1 weights are rewritten
- * as i2 first); 0 for i2, -1 if invalid. */
-int64_t bitlinear_backward_dx_workspace_bytes(int64_t N, int64_t K, int layout);
+/* Workspace bytes bitlinear_backward_dx needs for M tokens: room for the i2
+ * rewrite of b3 / b1 weights, and, for small batches whose weight rows are
+ * split over workgroups, the splits' fp32 partial sums (at most 16 x M x K
+ * floats); 0 when neither applies, -1 if invalid. */
+int64_t bitlinear_backward_dx_workspace_bytes(int64_t M, int64_t N, int64_t K, int layout);
 
 /*
  * Gradient with respect to the layer input: dX = gamma * (dY @ T).
  *   P, layout, gamma  the forward's packed weights [N x K] and scale.
  *   dY    fp32 [M x N], row stride lddy >= N (device, read-only).
  *   dX    fp32 [M x K], row stride lddx >= K (device, written).
- *   ws    >= bitlinear_backward_dx_workspace_bytes(N, K, layout) bytes,
- *         16-byte aligned (may be NULL when that is 0).
+ *   ws    >= bitlinear_backward_dx_workspace_bytes(M, N, K, layout) bytes,
+ *         16-byte aligned (may be NULL when that is 0); contents on entry
+ *         are ignored.
+ * Small batches split the weight rows over workgroups; the splits' partial
+ * sums are added in a fixed order by a second kernel, so results are
+ * deterministic.
  */
 int bitlinear_backward_dx(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
                           const float *dY, int64_t lddy, float *dX, int64_t lddx, void *ws, int64_t ws_bytes,
@@ -290,10 +296,11 @@ int bitlinear_backward_dw(const int8_t *Xq, int64_t ldq, const float *beta, int6
                           const float *dY, int64_t lddy, float *dW, int64_t lddw, void *stream);
 
 /*
- * Name of the kernel a backward call with these sizes launches (which = 0:
- * bitlinear_backward_dx, 1: bitlinear_backward_dw), e.g. "bl::k_bwd_dx" or,
- * for small batches, "bl::k_bwd_dx_few"; NULL for sizes or a 'which' the
- * calls reject.  A static string; host-only, enqueues nothing.
+ * Name of the main kernel a backward call with these sizes launches (which =
+ * 0: bitlinear_backward_dx, 1: bitlinear_backward_dw), e.g. "bl::k_bwd_dx"
+ * or, for small batches, "bl::k_bwd_dx_few" (followed by "bl::k_bwd_dx_sum"
+ * when it splits the weight rows); NULL for sizes or a 'which' the calls
+ * reject.  A static string; host-only, enqueues nothing.
  */
 const char *bitlinear_backward_kernel(int64_t M, int64_t N, int64_t K, int which);
 

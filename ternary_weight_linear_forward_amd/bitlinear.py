@@ -71,7 +71,7 @@ _SIGNATURES = {
     "bitlinear_pack": ([_P, _I64, _I64, _I64, _INT, _P, _P], _INT),
     "bitlinear_quantize_act": ([_P, _INT, _I64, _I64, _I64, _P, _I64, _P, _P], _INT),
     "bitlinear_forward": ([_P, _INT, _P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P, _INT, _I64, _P, _I64, _P], _INT),
-    "bitlinear_backward_dx_workspace_bytes": ([_I64, _I64, _INT], _I64),
+    "bitlinear_backward_dx_workspace_bytes": ([_I64, _I64, _I64, _INT], _I64),
     "bitlinear_backward_kernel": ([_I64, _I64, _I64, _INT], ctypes.c_char_p),
     "bitlinear_backward_dx": ([_P, _INT, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P], _INT),
     "bitlinear_backward_dw": ([_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P], _INT),
@@ -148,8 +148,8 @@ def bitlinear_binarize_weights(W, N, K, ldw, T, gamma, ws, ws_bytes, stream) -> 
     return _lib.bitlinear_binarize_weights(W, N, K, ldw, T, gamma, ws, ws_bytes, stream)
 
 
-def bitlinear_backward_dx_workspace_bytes(N: int, K: int, layout: int) -> int:
-    return _lib.bitlinear_backward_dx_workspace_bytes(N, K, layout)
+def bitlinear_backward_dx_workspace_bytes(M: int, N: int, K: int, layout: int) -> int:
+    return _lib.bitlinear_backward_dx_workspace_bytes(M, N, K, layout)
 
 
 def bitlinear_backward_dx(P, layout, gamma, M, N, K, dY, lddy, dX, lddx, ws, ws_bytes, stream) -> int:
@@ -300,7 +300,7 @@ def backward_dx(P, layout: int, gamma, dY, K: int, out=None, stream=None):
     M, N = dY.shape
     if out is None:
         out = torch.empty((M, K), dtype=torch.float32, device=dY.device)
-    nws = bitlinear_backward_dx_workspace_bytes(N, K, layout)
+    nws = bitlinear_backward_dx_workspace_bytes(M, N, K, layout)
     if nws < 0:
         raise BitlinearError(ERR_INVALID_ARG, "backward_dx")
     ws = torch.empty(nws, dtype=torch.uint8, device=dY.device) if nws > 0 else None

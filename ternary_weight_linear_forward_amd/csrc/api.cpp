@@ -118,7 +118,7 @@ const char *bitlinear_status_string(int status)
     }
 }
 
-int bitlinear_version(void) { return 100; }
+int bitlinear_version(void) { return 101; }
 
 int64_t bitlinear_packed_bytes(int64_t N, int64_t K, int layout)
 {
@@ -385,10 +385,16 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
     return status_of(e);
 }
 
-int64_t bitlinear_backward_dx_workspace_bytes(int64_t N, int64_t K, int layout)
+// i2 rewrite of b3 / b1 weights, then the small-batch dX's partial tiles
+static int64_t bwd_dx_rewrite_bytes(int64_t N, int64_t K, int layout)
 {
-    if (bitlinear_packed_bytes(N, K, layout) < 0) return -1;
     return layout == BITLINEAR_LAYOUT_I2 ? 0 : round_up(bitlinear_packed_bytes(N, K, BITLINEAR_LAYOUT_I2), 256);
+}
+
+int64_t bitlinear_backward_dx_workspace_bytes(int64_t M, int64_t N, int64_t K, int layout)
+{
+    if (M < 1 || M > BITLINEAR_MAX_M || bitlinear_packed_bytes(N, K, layout) < 0 || N > kMaxElems / K) return -1;
+    return bwd_dx_rewrite_bytes(N, K, layout) + bl::bwd_dx_partial_bytes(M, N, K);
 }
 
 int bitlinear_backward_dx(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
@@ -399,7 +405,7 @@ int bitlinear_backward_dx(const uint8_t *P, int layout, const float *gamma, int6
     if (M < 1 || M > BITLINEAR_MAX_M || N < 1 || K < 1 || K > BITLINEAR_MAX_K || N > kMaxElems / K ||
         lddy < N || lddx < K)
         return BITLINEAR_ERR_INVALID_ARG;
-    const int64_t need = bitlinear_backward_dx_workspace_bytes(N, K, layout);
+    const int64_t need = bitlinear_backward_dx_workspace_bytes(M, N, K, layout);
     if (need > 0 && (!ws || ws_bytes < need)) return BITLINEAR_ERR_WORKSPACE;
     if (!aligned16(P) || (need > 0 && !aligned16(ws)) || (reinterpret_cast<uintptr_t>(dY) & 3u) ||
         (reinterpret_cast<uintptr_t>(dX) & 3u) || (reinterpret_cast<uintptr_t>(gamma) & 3u))
@@ -422,7 +428,9 @@ int bitlinear_backward_dx(const uint8_t *P, int layout, const float *gamma, int6
         if (e != hipSuccess) return BITLINEAR_ERR_LAUNCH;
         p2 = w2;
     }
-    return status_of(bl::launch_bwd_dx(p2, gamma, M, N, K, dY, lddy, dX, lddx, st));
+    float *part = need > 0 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + bwd_dx_rewrite_bytes(N, K, layout))
+                           : nullptr;
+    return status_of(bl::launch_bwd_dx(p2, gamma, M, N, K, dY, lddy, dX, lddx, part, st));
 }
 
 const char *bitlinear_backward_kernel(int64_t M, int64_t N, int64_t K, int which)

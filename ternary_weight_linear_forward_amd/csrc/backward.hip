@@ -233,23 +233,27 @@ __global__ __launch_bounds__(256) void k_bwd_dw(const int8_t *__restrict__ Xq, i
 }
 
 // ---------------------------------------------------------------------------
-// Few tokens (the 128 x 128 tiles below would leave most CUs idle).
-// dX = gamma * dY @ T.  Workgroup: one token group (16 tokens, blockIdx.y)
-// and one 64-column k-block (blockIdx.x); its W waves split the N row tiles
-// (wave w takes tiles w, w+W, ...).  For a 16-row tile the wave multiplies
-// 4 row groups x 4 column groups: A = dY[16 tokens x 4 rows] (lane l: token
-// l%16, row l/16), B = T[4 rows x 16 columns] (lane l: row l/16, column
-// l%16, decoded from the packed word), D = dX[16 tokens x 16 columns] per
-// column group.  The W partial tiles meet in LDS; wave d stores column
-// group d, scaled by gamma.
+// Few tokens (the 128 x 128 tiles above would leave most CUs idle).
+// dX = gamma * dY @ T.  Workgroup: one token group (16 tokens, blockIdx.y),
+// one 64-column k-block (blockIdx.x) and one split of the weight-row tiles
+// (blockIdx.z: tiles z * TPS .. min(NT, (z+1) * TPS) - 1); its W waves share
+// the split's tiles (wave w takes every W-th).  For a 16-row tile the wave
+// multiplies 4 row groups x 4 column groups: A = dY[16 tokens x 4 rows]
+// (lane l: token l%16, row l/16), B = T[4 rows x 16 columns] (lane l: row
+// l/16, column l%16, decoded from the packed word), D = dX[16 tokens x 16
+// columns] per column group.  The W partial tiles meet in LDS; wave d stores
+// column group d to out + z * zstride, times gamma when the tiles are not
+// split (scale), else unscaled for k_bwd_dx_sum.
 // ---------------------------------------------------------------------------
 constexpr int DX_MAX_WAVES = 8;
 
 __global__ __launch_bounds__(64 * DX_MAX_WAVES) void k_bwd_dx_few(const uint8_t *__restrict__ P, int64_t KB,
-                                                             int64_t NT, const float *__restrict__ gamma_p,
-                                                             const float *__restrict__ dY, int64_t lddy, int64_t M,
-                                                             int64_t N, int64_t K, float *__restrict__ dX,
-                                                             int64_t lddx)
+                                                                 int64_t NT, int64_t TPS,
+                                                                 const float *__restrict__ gamma_p, int scale,
+                                                                 const float *__restrict__ dY, int64_t lddy,
+                                                                 int64_t M, int64_t N, int64_t K,
+                                                                 float *__restrict__ out, int64_t ldo,
+                                                                 int64_t zstride)
 {
     __shared__ v4f red[DX_MAX_WAVES][4][64];
     const int nw = blockDim.x >> 6;
@@ -257,6 +261,8 @@ __global__ __launch_bounds__(64 * DX_MAX_WAVES) void k_bwd_dx_few(const uint8_t 
     const int li = lane & 15, lg = lane >> 4;
     const int64_t kb = blockIdx.x;
     const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 16;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.z) * TPS;
+    const int64_t t1 = t0 + TPS < NT ? t0 + TPS : NT;
     const int64_t ma = m0 + li; // token of this lane's A element
     const bool mvalid = ma < M;
     const float *dyrow = dY + (mvalid ? ma : 0) * lddy;
@@ -266,7 +272,7 @@ __global__ __launch_bounds__(64 * DX_MAX_WAVES) void k_bwd_dx_few(const uint8_t 
     v4f acc[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) acc[d] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t tile = wave; tile < NT; tile += nw) {
+    for (int64_t tile = t0 + wave; tile < t1; tile += nw) {
         const uint8_t *cb = P + (tile * KB + kb) * 256;
         uint4 ch[4];
         float a[4];
@@ -289,7 +295,8 @@ __global__ __launch_bounds__(64 * DX_MAX_WAVES) void k_bwd_dx_few(const uint8_t 
 #pragma unroll
     for (int d = 0; d < 4; ++d) red[wave][d][lane] = acc[d];
     __syncthreads();
-    const float gamma = *gamma_p;
+    const float g = scale ? *gamma_p : 1.0f;
+    float *o = out + static_cast<int64_t>(blockIdx.z) * zstride;
     // D layout: lane l holds tokens 4 * (l/16) + r, column l%16 of the group
     for (int d = wave; d < 4; d += nw) {
         v4f tot = red[0][d][lane];
@@ -298,8 +305,24 @@ __global__ __launch_bounds__(64 * DX_MAX_WAVES) void k_bwd_dx_few(const uint8_t 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t m = m0 + 4 * lg + r;
-            if (m < M && k < K) dX[m * lddx + k] = gamma * tot[r];
+            if (m < M && k < K) o[m * ldo + k] = g * tot[r];
         }
+    }
+}
+
+// dX[m][k] = gamma * sum over the S splits of part[z][m][k], z in order
+// (part: S blocks of M x K, row stride K).
+__global__ __launch_bounds__(256) void k_bwd_dx_sum(const float *__restrict__ part, int64_t S, int64_t M, int64_t K,
+                                                   const float *__restrict__ gamma_p, float *__restrict__ dX,
+                                                   int64_t lddx)
+{
+    const float gamma = *gamma_p;
+    const int64_t MK = M * K;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < MK;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        float t = part[i];
+        for (int64_t z = 1; z < S; ++z) t += part[z * MK + i];
+        dX[(i / K) * lddx + i % K] = gamma * t;
     }
 }
 
@@ -379,6 +402,25 @@ static bool bwd_dx_few(int64_t M, int64_t K)
 
 static bool bwd_dw_few(int64_t M) { return M < MM_S; }
 
+// Splits of the weight-row tiles for the small-batch dX: enough workgroups
+// for about two per CU, at most 16 splits, at least 8 tiles (one per wave)
+// per split.  Splits write partial tiles that k_bwd_dx_sum adds in order.
+int64_t bwd_dx_splits(int64_t M, int64_t N, int64_t K)
+{
+    if (!bwd_dx_few(M, K)) return 1;
+    const int64_t wgs = ((K + 63) / 64) * ((M + 15) / 16), NT = (N + 15) / 16;
+    int64_t s = (2 * 256 + wgs - 1) / wgs;
+    if (s > 16) s = 16;
+    if (s > NT / 8) s = NT / 8;
+    return s < 1 ? 1 : s;
+}
+
+int64_t bwd_dx_partial_bytes(int64_t M, int64_t N, int64_t K)
+{
+    const int64_t s = bwd_dx_splits(M, N, K);
+    return s > 1 ? s * M * K * 4 : 0;
+}
+
 const char *bwd_kernel_name(bool dx, int64_t M, int64_t K)
 {
     if (dx) return bwd_dx_few(M, K) ? "bl::k_bwd_dx_few" : "bl::k_bwd_dx";
@@ -386,18 +428,29 @@ const char *bwd_kernel_name(bool dx, int64_t M, int64_t K)
 }
 
 hipError_t launch_bwd_dx(const uint8_t *P2, const float *gamma, int64_t M, int64_t N, int64_t K, const float *dY,
-                         int64_t lddy, float *dX, int64_t lddx, hipStream_t stream)
+                         int64_t lddy, float *dX, int64_t lddx, float *part, hipStream_t stream)
 {
     const int64_t KB = (K + 63) / 64;
-    const int64_t mt = (M + MM_T - 1) / MM_T, kt = (K + MM_T - 1) / MM_T;
     if (bwd_dx_few(M, K)) {
-        const int64_t NT = (N + 15) / 16;
-        const int64_t nw = NT < DX_MAX_WAVES ? NT : DX_MAX_WAVES;
-        dim3 grid(static_cast<unsigned>(KB), static_cast<unsigned>((M + 15) / 16));
-        hipLaunchKernelGGL(k_bwd_dx_few, grid, dim3(static_cast<unsigned>(64 * nw)), 0, stream, P2, KB, NT, gamma, dY,
-                           lddy, M, N, K, dX, lddx);
+        const int64_t NT = (N + 15) / 16, S = bwd_dx_splits(M, N, K);
+        const int64_t TPS = (NT + S - 1) / S;
+        const int64_t nw = TPS < DX_MAX_WAVES ? TPS : DX_MAX_WAVES;
+        dim3 grid(static_cast<unsigned>(KB), static_cast<unsigned>((M + 15) / 16), static_cast<unsigned>(S));
+        if (S == 1) {
+            hipLaunchKernelGGL(k_bwd_dx_few, grid, dim3(static_cast<unsigned>(64 * nw)), 0, stream, P2, KB, NT, TPS,
+                               gamma, 1, dY, lddy, M, N, K, dX, lddx, int64_t(0));
+            return hipGetLastError();
+        }
+        hipLaunchKernelGGL(k_bwd_dx_few, grid, dim3(static_cast<unsigned>(64 * nw)), 0, stream, P2, KB, NT, TPS,
+                           gamma, 0, dY, lddy, M, N, K, part, K, M * K);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t blocks = (M * K + 255) / 256;
+        hipLaunchKernelGGL(k_bwd_dx_sum, dim3(static_cast<unsigned>(blocks < 1024 ? blocks : 1024)), dim3(256), 0,
+                           stream, part, S, M, K, gamma, dX, lddx);
         return hipGetLastError();
     }
+    const int64_t mt = (M + MM_T - 1) / MM_T, kt = (K + MM_T - 1) / MM_T;
     dim3 grid(static_cast<unsigned>(kt), static_cast<unsigned>(mt));
     hipLaunchKernelGGL(k_bwd_dx, grid, dim3(256), 0, stream, P2, KB, gamma, dY, lddy, M, N, K, dX, lddx);
     return hipGetLastError();

@@ -81,8 +81,13 @@ bool gemm_b3_native(int64_t M, int64_t N);
 // Name of the kernel bitlinear_backward_dx (dx) or _dw (!dx) launches for M
 // tokens and K columns.
 const char *bwd_kernel_name(bool dx, int64_t M, int64_t K);
+// Splits of the weight rows the small-batch dX kernel uses, and the bytes of
+// their partial tiles (0 when it does not split).
+int64_t bwd_dx_splits(int64_t M, int64_t N, int64_t K);
+int64_t bwd_dx_partial_bytes(int64_t M, int64_t N, int64_t K);
+// part: bwd_dx_partial_bytes(M, N, K) bytes, 16-byte aligned (unused if 0).
 hipError_t launch_bwd_dx(const uint8_t *P2, const float *gamma, int64_t M, int64_t N, int64_t K, const float *dY,
-                         int64_t lddy, float *dX, int64_t lddx, hipStream_t stream);
+                         int64_t lddy, float *dX, int64_t lddx, float *part, hipStream_t stream);
 hipError_t launch_bwd_dw(const int8_t *Xq, int64_t ldq, const float *beta, int64_t M, int64_t N, int64_t K,
                          const float *dY, int64_t lddy, float *dW, int64_t lddw, hipStream_t stream);
 

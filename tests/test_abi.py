@@ -284,9 +284,20 @@ def test_backward_rejects():
     assert bl.bitlinear_backward_dx(**{**dx, "M": 0}) == bl.ERR_INVALID_ARG
     assert bl.bitlinear_backward_dx(**{**dx, "dX": B + 64}) == bl.ERR_INVALID_ARG  # overlaps dY
     assert bl.bitlinear_backward_dx(**{**dx, "layout": bl.LAYOUT_B3}) == bl.ERR_WORKSPACE
-    assert bl.bitlinear_backward_dx_workspace_bytes(64, 64, bl.LAYOUT_I2) == 0
-    assert bl.bitlinear_backward_dx_workspace_bytes(64, 64, bl.LAYOUT_B3) == bl.bitlinear_packed_bytes(64, 64, 0)
-    assert bl.bitlinear_backward_dx_workspace_bytes(0, 64, bl.LAYOUT_B3) == -1
+    assert bl.bitlinear_backward_dx_workspace_bytes(4, 64, 64, bl.LAYOUT_I2) == 0
+    assert bl.bitlinear_backward_dx_workspace_bytes(4, 64, 64, bl.LAYOUT_B3) == bl.bitlinear_packed_bytes(64, 64, 0)
+    assert bl.bitlinear_backward_dx_workspace_bytes(4, 0, 64, bl.LAYOUT_B3) == -1
+    assert bl.bitlinear_backward_dx_workspace_bytes(0, 64, 64, bl.LAYOUT_I2) == -1
+    # small batches split the weight rows (at least 8 row tiles per split, at
+    # most 16 splits, about 512 workgroups) and keep fp32 partials per split
+    ws = bl.bitlinear_backward_dx_workspace_bytes
+    assert ws(1, 3200, 3200, bl.LAYOUT_I2) == 11 * 1 * 3200 * 4  # 50 workgroups -> 11 splits
+    assert ws(16, 8640, 3200, bl.LAYOUT_I2) == 11 * 16 * 3200 * 4
+    assert ws(5, 1000, 130, bl.LAYOUT_I2) == 7 * 5 * 130 * 4  # 63 row tiles -> 7 splits
+    assert ws(1, 64, 64, bl.LAYOUT_I2) == 0  # 4 row tiles: no split
+    assert ws(2048, 3200, 3200, bl.LAYOUT_I2) == 0  # tiled kernel
+    assert ws(1, 3200, 3200, bl.LAYOUT_B1) == (bl.bitlinear_packed_bytes(3200, 3200, 0) + 255) // 256 * 256 \
+        + 11 * 3200 * 4
     dw = dict(Xq=A, ldq=64, beta=C, M=4, N=64, K=64, dY=B, lddy=64, dW=D, lddw=64, stream=None)
     assert bl.bitlinear_backward_dw(**{**dw, "Xq": None}) == bl.ERR_INVALID_ARG
     assert bl.bitlinear_backward_dw(**{**dw, "ldq": 63}) == bl.ERR_INVALID_ARG

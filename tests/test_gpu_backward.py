@@ -5,8 +5,9 @@ oracle's binary64 products.  Both GPU results are fp32 sums in an unspecified
 order, so the bar is the summation bound: |got - want| <= (n + 2) * 2^-24 *
 sum |terms| per element (n the contraction length), plus bit-exact zeros
 where every term is zero.  Batches below 32 tokens (dW), or with fewer than
-256 tiles of 128 x 128 (dX), take the small-batch kernels; the rest the
-tiled ones, with 16-byte stores on aligned rows and single ones otherwise."""
+256 tiles of 128 x 128 (dX), take the small-batch kernels (dX splitting the
+weight rows over workgroups when it has few of them); the rest the tiled
+ones, with 16-byte stores on aligned rows and single ones otherwise."""
 import numpy as np
 import pytest
 
@@ -44,7 +45,8 @@ def weights(layout, N, K, seed):
 
 @pytest.mark.parametrize("layout", ["i2", "b3", "b1"])
 @pytest.mark.parametrize("M,N,K", [(1, 3200, 3200), (4, 130, 333), (16, 8640, 3200), (17, 100, 64), (3, 48, 1),
-                                   (300, 257, 700), (1024, 1000, 3200), (1100, 130, 3900), (1030, 70, 4001)])
+                                   (300, 257, 700), (1024, 1000, 3200), (1100, 130, 3900), (1030, 70, 4001),
+                                   (5, 1000, 130), (2, 520, 4100)])
 def test_backward_dx(layout, M, N, K):
     log("backward dx", layout, M, N, K)
     t = weights(layout, N, K, seed=M + 3 * N + K)
