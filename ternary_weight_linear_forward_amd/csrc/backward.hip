@@ -310,20 +310,28 @@ __global__ __launch_bounds__(64 * DX_MAX_WAVES) void k_bwd_dx_few(const uint8_t 
     }
 }
 
-// dX[m][k] = gamma * sum over the S splits of part[z][m][k], z in order
-// (part: S blocks of M x K, row stride K).
-__global__ __launch_bounds__(256) void k_bwd_dx_sum(const float *__restrict__ part, int64_t S, int64_t M, int64_t K,
+// dX[m][k] = gamma * sum over the S <= DX_MAX_SPLITS splits of part[z][m][k],
+// z in order (part: S blocks of M x K, row stride K).  Thread: column k =
+// blockIdx.x * 256 + tid of token m = blockIdx.y; its S loads are all issued
+// before the sum.
+constexpr int DX_MAX_SPLITS = 16;
+
+__global__ __launch_bounds__(256) void k_bwd_dx_sum(const float *__restrict__ part, int S, int64_t M, int64_t K,
                                                    const float *__restrict__ gamma_p, float *__restrict__ dX,
                                                    int64_t lddx)
 {
-    const float gamma = *gamma_p;
+    const int64_t k = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x, m = blockIdx.y;
+    if (k >= K) return;
+    const float *p = part + m * K + k;
     const int64_t MK = M * K;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < MK;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        float t = part[i];
-        for (int64_t z = 1; z < S; ++z) t += part[z * MK + i];
-        dX[(i / K) * lddx + i % K] = gamma * t;
-    }
+    float v[DX_MAX_SPLITS];
+#pragma unroll
+    for (int z = 0; z < DX_MAX_SPLITS; ++z) v[z] = z < S ? p[z * MK] : 0.0f;
+    float t = v[0];
+#pragma unroll
+    for (int z = 1; z < DX_MAX_SPLITS; ++z)
+        if (z < S) t += v[z];
+    dX[m * lddx + k] = *gamma_p * t;
 }
 
 // ---------------------------------------------------------------------------
@@ -410,7 +418,7 @@ int64_t bwd_dx_splits(int64_t M, int64_t N, int64_t K)
     if (!bwd_dx_few(M, K)) return 1;
     const int64_t wgs = ((K + 63) / 64) * ((M + 15) / 16), NT = (N + 15) / 16;
     int64_t s = (2 * 256 + wgs - 1) / wgs;
-    if (s > 16) s = 16;
+    if (s > DX_MAX_SPLITS) s = DX_MAX_SPLITS;
     if (s > NT / 8) s = NT / 8;
     return s < 1 ? 1 : s;
 }
@@ -445,9 +453,8 @@ hipError_t launch_bwd_dx(const uint8_t *P2, const float *gamma, int64_t M, int64
                            gamma, 0, dY, lddy, M, N, K, part, K, M * K);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const int64_t blocks = (M * K + 255) / 256;
-        hipLaunchKernelGGL(k_bwd_dx_sum, dim3(static_cast<unsigned>(blocks < 1024 ? blocks : 1024)), dim3(256), 0,
-                           stream, part, S, M, K, gamma, dX, lddx);
+        hipLaunchKernelGGL(k_bwd_dx_sum, dim3(static_cast<unsigned>((K + 255) / 256), static_cast<unsigned>(M)),
+                           dim3(256), 0, stream, part, static_cast<int>(S), M, K, gamma, dX, lddx);
         return hipGetLastError();
     }
     const int64_t mt = (M + MM_T - 1) / MM_T, kt = (K + MM_T - 1) / MM_T;
