@@ -51,7 +51,7 @@ extern "C" {
 typedef enum {
     BITLINEAR_OK = 0,
     BITLINEAR_ERR_INVALID_ARG = 1, /* null pointer, bad size, stride, enum or alignment */
-    BITLINEAR_ERR_UNSUPPORTED = 2, /* valid request this build does not implement       */
+    BITLINEAR_ERR_UNSUPPORTED = 2, /* valid request this library does not implement     */
     BITLINEAR_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required        */
     BITLINEAR_ERR_LAUNCH = 4,      /* a kernel launch failed                            */
     BITLINEAR_ERR_DEVICE = 5       /* no usable gfx950 device on the current HIP device  */
