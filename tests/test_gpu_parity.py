@@ -218,7 +218,7 @@ def test_forward_small(algo_name, algo, layout, M, N, K):
                                                    ("mfma_gemv", bl.ALGO_GEMV_MFMA, "b3"),
                                                    ("gemm", bl.ALGO_GEMM_MFMA, "i2"),
                                                    ("gemm", bl.ALGO_GEMM_MFMA, "b3")])
-@pytest.mark.parametrize("M,N,K", [(17, 40, 100), (64, 96, 512), (130, 257, 700), (256, 128, 64)])
+@pytest.mark.parametrize("M,N,K", [(17, 40, 100), (64, 96, 512), (130, 257, 700), (256, 128, 64), (40, 2000, 300)])
 def test_forward_many_tokens(algo_name, algo, layout, M, N, K):
     log("forward", algo_name, layout, M, N, K)
     run_forward_case(M, N, K, algo, layout, seed=M * 131 + N + K)
