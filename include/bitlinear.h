@@ -24,7 +24,8 @@
  * Conventions for every entry point:
  *   - Matrices are row-major.  W and T are [N x K] (out x in, like
  *     nn.Linear.weight), X and Xq are [M x K], Y is [M x N].  "ld*" arguments
- *     are row strides in elements.
+ *     are row strides in elements, at most 2^40, with (rows - 1) * ld at most
+ *     2^44 (larger strides are rejected as invalid arguments).
  *   - All array pointers are DEVICE pointers owned by the caller.  The library
  *     never allocates, frees or synchronises; it keeps no mutable global state.
  *   - 'stream' is a hipStream_t passed as void* (NULL = the default stream).

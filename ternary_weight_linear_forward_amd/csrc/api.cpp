@@ -52,6 +52,12 @@ Span span_of(const void *p, int64_t rows, int64_t ld, int64_t cols, int elem)
 
 bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
 
+// Row strides are bounded so that no offset (rows - 1) * ld * 4 bytes, on the
+// host or in a kernel, can overflow 64 bits: ld <= 2^40 elements and the
+// rows span at most 2^44 elements.
+constexpr int64_t kMaxLd = int64_t(1) << 40, kMaxSpan = int64_t(1) << 44;
+bool stride_ok(int64_t rows, int64_t ld) { return ld <= kMaxLd && rows - 1 <= kMaxSpan / ld; }
+
 int status_of(hipError_t e) { return e == hipSuccess ? BITLINEAR_OK : BITLINEAR_ERR_LAUNCH; }
 
 bool valid_layout(int layout)
@@ -195,7 +201,7 @@ static int check_weight_quant(const float *W, int64_t N, int64_t K, int64_t ldw,
                               const float *gamma, const void *ws, int64_t ws_bytes)
 {
     if (!W || !T || !gamma) return BITLINEAR_ERR_INVALID_ARG;
-    if (N < 1 || K < 1 || ldw < K || N > kMaxElems / K) return BITLINEAR_ERR_INVALID_ARG;
+    if (N < 1 || K < 1 || ldw < K || N > kMaxElems / K || !stride_ok(N, ldw)) return BITLINEAR_ERR_INVALID_ARG;
     const int64_t need = bitlinear_quantize_weights_workspace_bytes(N, K);
     if (!ws || ws_bytes < need) return BITLINEAR_ERR_WORKSPACE;
     if (!aligned16(ws) || (reinterpret_cast<uintptr_t>(W) & 3u) || (reinterpret_cast<uintptr_t>(gamma) & 3u))
@@ -229,7 +235,8 @@ int bitlinear_quantize_weights(const float *W, int64_t N, int64_t K, int64_t ldw
 int bitlinear_pack(const int8_t *T, int64_t N, int64_t K, int64_t ldt, int layout, uint8_t *P, void *stream)
 {
     if (!T || !P || !valid_layout(layout)) return BITLINEAR_ERR_INVALID_ARG;
-    if (N < 1 || K < 1 || K > BITLINEAR_MAX_K || ldt < K || N > kMaxElems / K) return BITLINEAR_ERR_INVALID_ARG;
+    if (N < 1 || K < 1 || K > BITLINEAR_MAX_K || ldt < K || N > kMaxElems / K || !stride_ok(N, ldt))
+        return BITLINEAR_ERR_INVALID_ARG;
     if (!aligned16(P)) return BITLINEAR_ERR_INVALID_ARG;
     const int64_t pb = bitlinear_packed_bytes(N, K, layout);
     if (overlap(span_of(T, N, ldt, K, 1), span_of(P, 1, pb, pb, 1))) return BITLINEAR_ERR_INVALID_ARG;
@@ -242,7 +249,8 @@ int bitlinear_quantize_act(const void *X, int x_dtype, int64_t M, int64_t K, int
 {
     if (!X || !Xq || !beta) return BITLINEAR_ERR_INVALID_ARG;
     if (x_dtype != BITLINEAR_F32 && x_dtype != BITLINEAR_BF16) return BITLINEAR_ERR_INVALID_ARG;
-    if (M < 1 || M > BITLINEAR_MAX_M || K < 1 || K > BITLINEAR_MAX_K || ldx < K || ldq < K || ldq % 16)
+    if (M < 1 || M > BITLINEAR_MAX_M || K < 1 || K > BITLINEAR_MAX_K || ldx < K || ldq < K || ldq % 16 ||
+        !stride_ok(M, ldx) || !stride_ok(M, ldq))
         return BITLINEAR_ERR_INVALID_ARG;
     if (!aligned16(Xq) || (reinterpret_cast<uintptr_t>(X) % dtype_size(x_dtype)) ||
         (reinterpret_cast<uintptr_t>(beta) & 3u))
@@ -259,7 +267,8 @@ int bitlinear_quantize_act_tiled(const void *X, int x_dtype, int64_t M, int64_t 
 {
     if (!X || !Xt || !beta || !valid_layout(layout)) return BITLINEAR_ERR_INVALID_ARG;
     if (x_dtype != BITLINEAR_F32 && x_dtype != BITLINEAR_BF16) return BITLINEAR_ERR_INVALID_ARG;
-    if (M < 1 || M > BITLINEAR_MAX_M || K < 1 || K > BITLINEAR_MAX_K || ldx < K) return BITLINEAR_ERR_INVALID_ARG;
+    if (M < 1 || M > BITLINEAR_MAX_M || K < 1 || K > BITLINEAR_MAX_K || ldx < K || !stride_ok(M, ldx))
+        return BITLINEAR_ERR_INVALID_ARG;
     const int64_t need = bl::tiled_bytes(M, K, layout);
     if (xt_bytes < need) return BITLINEAR_ERR_INVALID_ARG;
     if (!aligned16(Xt) || (reinterpret_cast<uintptr_t>(X) % dtype_size(x_dtype)) ||
@@ -286,7 +295,8 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
     const bool x_int8 = x_dtype == BITLINEAR_I8 || x_dtype == BITLINEAR_I8_TILED;
     if (y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_BF16 && y_dtype != BITLINEAR_I32)
         return BITLINEAR_ERR_INVALID_ARG;
-    if ((x_dtype != BITLINEAR_I8_TILED && ldx < K) || ldy < N) return BITLINEAR_ERR_INVALID_ARG;
+    if ((x_dtype != BITLINEAR_I8_TILED && (ldx < K || !stride_ok(M, ldx))) || ldy < N || !stride_ok(M, ldy))
+        return BITLINEAR_ERR_INVALID_ARG;
     if (algo < BITLINEAR_ALGO_AUTO || algo > BITLINEAR_ALGO_GEMM_MFMA) return BITLINEAR_ERR_INVALID_ARG;
     if (x_int8 != (beta_in != nullptr)) return BITLINEAR_ERR_INVALID_ARG;
     if (!aligned16(P) || (reinterpret_cast<uintptr_t>(gamma) & 3u) ||
@@ -403,7 +413,7 @@ int bitlinear_backward_dx(const uint8_t *P, int layout, const float *gamma, int6
 {
     if (!P || !gamma || !dY || !dX || !valid_layout(layout)) return BITLINEAR_ERR_INVALID_ARG;
     if (M < 1 || M > BITLINEAR_MAX_M || N < 1 || K < 1 || K > BITLINEAR_MAX_K || N > kMaxElems / K ||
-        lddy < N || lddx < K)
+        lddy < N || lddx < K || !stride_ok(M, lddy) || !stride_ok(M, lddx))
         return BITLINEAR_ERR_INVALID_ARG;
     const int64_t need = bitlinear_backward_dx_workspace_bytes(M, N, K, layout);
     if (need > 0 && (!ws || ws_bytes < need)) return BITLINEAR_ERR_WORKSPACE;
@@ -446,7 +456,7 @@ int bitlinear_backward_dw(const int8_t *Xq, int64_t ldq, const float *beta, int6
 {
     if (!Xq || !beta || !dY || !dW) return BITLINEAR_ERR_INVALID_ARG;
     if (M < 1 || M > BITLINEAR_MAX_M || N < 1 || K < 1 || K > BITLINEAR_MAX_K || N > kMaxElems / K || ldq < K ||
-        lddy < N || lddw < K)
+        lddy < N || lddw < K || !stride_ok(M, ldq) || !stride_ok(M, lddy) || !stride_ok(N, lddw))
         return BITLINEAR_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(dY) & 3u) || (reinterpret_cast<uintptr_t>(dW) & 3u) ||
         (reinterpret_cast<uintptr_t>(beta) & 3u))

@@ -66,6 +66,7 @@ def qw(**kw):
     (dict(W=None), bl.ERR_INVALID_ARG), (dict(T=None), bl.ERR_INVALID_ARG), (dict(gamma=None), bl.ERR_INVALID_ARG),
     (dict(N=0), bl.ERR_INVALID_ARG), (dict(K=-1), bl.ERR_INVALID_ARG), (dict(ldw=63), bl.ERR_INVALID_ARG),
     (dict(N=1 << 21, K=1 << 20, ldw=1 << 20), bl.ERR_INVALID_ARG),
+    (dict(ldw=(1 << 40) + 64), bl.ERR_INVALID_ARG),             # stride bound
     (dict(ws=None), bl.ERR_WORKSPACE), (dict(ws_bytes=2047), bl.ERR_WORKSPACE),
     (dict(ws=D + 8), bl.ERR_INVALID_ARG), (dict(W=A + 2), bl.ERR_INVALID_ARG),
     (dict(T=A + 64), bl.ERR_INVALID_ARG),       # T overlaps W
@@ -93,7 +94,7 @@ def pk(**kw):
 
 @pytest.mark.parametrize("kw", [
     dict(T=None), dict(P=None), dict(layout=3), dict(layout=-1), dict(N=0), dict(K=0), dict(K=bl.MAX_K + 1, ldt=bl.MAX_K + 1),
-    dict(ldt=10), dict(P=B + 4), dict(P=A + 16),
+    dict(ldt=10), dict(P=B + 4), dict(P=A + 16), dict(ldt=(1 << 40) + 64),
 ])
 def test_pack_rejects(kw):
     assert pk(**kw) == bl.ERR_INVALID_ARG
@@ -109,6 +110,7 @@ def qa(**kw):
     dict(X=None), dict(Xq=None), dict(beta=None), dict(x_dtype=bl.I8), dict(x_dtype=bl.I32), dict(M=0),
     dict(M=bl.MAX_M + 1), dict(K=0), dict(K=bl.MAX_K + 1, ldx=bl.MAX_K + 1, ldq=bl.MAX_K + 16), dict(ldx=99),
     dict(ldq=104), dict(ldq=96), dict(Xq=B + 8), dict(X=A + 1), dict(beta=C + 2), dict(Xq=A + 32),
+    dict(ldx=1 << 41), dict(ldq=1 << 42),  # strides beyond 2^40 elements
 ])
 def test_quantize_act_rejects(kw):
     assert qa(**kw) == bl.ERR_INVALID_ARG
@@ -128,6 +130,8 @@ def fw(**kw):
     (dict(K=bl.MAX_K + 1, ldx=bl.MAX_K + 1), bl.ERR_INVALID_ARG), (dict(x_dtype=bl.I32), bl.ERR_INVALID_ARG),
     (dict(y_dtype=bl.I8), bl.ERR_INVALID_ARG), (dict(ldx=63), bl.ERR_INVALID_ARG), (dict(ldy=63), bl.ERR_INVALID_ARG),
     (dict(algo=9), bl.ERR_INVALID_ARG), (dict(algo=-1), bl.ERR_INVALID_ARG),
+    (dict(ldx=1 << 41), bl.ERR_INVALID_ARG), (dict(ldy=1 << 41), bl.ERR_INVALID_ARG),  # stride bound
+    (dict(M=40000, ldy=1 << 30), bl.ERR_INVALID_ARG),               # rows x stride beyond 2^44
     (dict(x_dtype=bl.I8), bl.ERR_INVALID_ARG),                      # I8 needs beta_in
     (dict(beta_in=A + 0x100000), bl.ERR_INVALID_ARG),               # bf16 must not pass beta_in
     (dict(x_dtype=bl.I8, beta_in=B + 64, ldx=72), bl.ERR_INVALID_ARG),  # I8 rows must be 16-aligned
@@ -281,6 +285,8 @@ def test_backward_rejects():
     assert bl.bitlinear_backward_dx(**{**dx, "layout": 3}) == bl.ERR_INVALID_ARG
     assert bl.bitlinear_backward_dx(**{**dx, "lddy": 63}) == bl.ERR_INVALID_ARG
     assert bl.bitlinear_backward_dx(**{**dx, "lddx": 63}) == bl.ERR_INVALID_ARG
+    assert bl.bitlinear_backward_dx(**{**dx, "lddx": 1 << 41}) == bl.ERR_INVALID_ARG  # stride bound
+    assert bl.bitlinear_backward_dx(**{**dx, "lddy": 1 << 42}) == bl.ERR_INVALID_ARG
     assert bl.bitlinear_backward_dx(**{**dx, "M": 0}) == bl.ERR_INVALID_ARG
     assert bl.bitlinear_backward_dx(**{**dx, "dX": B + 64}) == bl.ERR_INVALID_ARG  # overlaps dY
     assert bl.bitlinear_backward_dx(**{**dx, "layout": bl.LAYOUT_B3}) == bl.ERR_WORKSPACE
