@@ -244,9 +244,10 @@ def test_product_kernel_names():
     kernel on request; None for requests the library rejects."""
     f = bl.bitlinear_product_kernel
     # 1-4 tokens of float input: the GEMV with the quantiser inside (aligned rows)
-    assert f(1, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemv_fq<0, 1, 2>"
+    assert f(1, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemv_fq<0, 1, 1>"  # 13 waves of one k-step
     assert f(4, 3200, 8640, bl.LAYOUT_I2, bl.F32) == "bl::k_gemv_fq<0, 0, 4>"
     assert f(1, 3200, 3200, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemv_fq<1, 1, 1>"
+    assert f(1, 3200, 8640, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemv_fq<1, 1, 2>"  # 16 waves of two
     assert f(1, 3200, 3200, bl.LAYOUT_I2, bl.I8) == "bl::k_gemv_mfma<0, 1, 1, false>"
     assert f(1, 8640, 3200, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemv_persist_fq<0, 1, 1, 8, true>"
     assert f(1, 8640, 3200, bl.LAYOUT_I2, bl.I8).startswith("bl::k_gemv_persist<0, ")
