@@ -1058,7 +1058,8 @@ static void launch_mfma_layout(const GemvArgs &a, hipStream_t stream)
 // The GEMV with the quantiser inside: 1 to 4 tokens of fp32 / bf16 input,
 // on the shapes and launch geometry of the kernel the int8 path would run:
 // the per-tile kernel with one tile per workgroup (k_gemv_fq, at most 10
-// waves, at most FQ_MAX_SPW k-steps per wave, b1 2) or the persistent one
+// waves, or up to FQ_MAX_WAVES where that shortens the per-wave template, at
+// most FQ_MAX_SPW k-steps per wave, b1 2) or the persistent one
 // (k_gemv_persist_fq, at most 2 k-steps per wave, b1 1), so that nothing
 // spills, and LDS for the rounding areas and the persistent kernel's partial
 // sums within the 160 KB of a CU.  Alignment
