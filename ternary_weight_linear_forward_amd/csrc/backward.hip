@@ -310,6 +310,73 @@ __global__ __launch_bounds__(64 * DX_MAX_WAVES) void k_bwd_dx_few(const uint8_t 
     }
 }
 
+// One token (MT = 1; the template also holds 2 and 4, measured slower than
+// k_bwd_dx_few at 4 tokens: 18 against 11.6 us for the 3B q layer): the
+// 16-token MFMA tiles above would be 15/16 padding, so the product runs on the
+// vector ALU (3B q 11.7 -> 9.6 us, 70B gate 106 -> 71 us).  Workgroup: one 64-column k-block
+// (blockIdx.x) and one split of the weight-row tiles (blockIdx.z, as in
+// k_bwd_dx_few), 4 waves taking every 4th tile of the split.  Lane l owns
+// word d = l % 4 of chunk row r = l / 4, i.e. weight row tile * 16 + r and
+// the 16 columns 16 d .. 16 d + 15 of the k-block (column 16 d + 4 s + j at
+// bits 8 j + 2 s, code T + 1), and adds T * dY[m][row] into 16 sums per
+// token.  The 16 row lanes of each word are then summed by shuffles, the 4
+// waves through LDS, and the block's 64 columns stored like k_bwd_dx_few's.
+template <int MT>
+__global__ __launch_bounds__(256) void k_bwd_dx_vec(const uint8_t *__restrict__ P, int64_t KB, int64_t NT,
+                                                   int64_t TPS, const float *__restrict__ gamma_p, int scale,
+                                                   const float *__restrict__ dY, int64_t lddy, int64_t M,
+                                                   int64_t N, int64_t K, float *__restrict__ out, int64_t ldo,
+                                                   int64_t zstride)
+{
+    __shared__ float red[4][MT][64];
+    const int wave = wave_id(), lane = lane_id();
+    const int r = lane >> 2, d = lane & 3;
+    const int64_t kb = blockIdx.x;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.z) * TPS;
+    const int64_t t1 = t0 + TPS < NT ? t0 + TPS : NT;
+    float acc[MT][16];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int c = 0; c < 16; ++c) acc[m][c] = 0.0f;
+    for (int64_t tile = t0 + wave; tile < t1; tile += 4) {
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(P + (tile * KB + kb) * 256 + r * 16 + d * 4);
+        const int64_t n = tile * 16 + r;
+        float y[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) y[m] = (m < M && n < N) ? dY[m * lddy + n] : 0.0f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float t = static_cast<float>(static_cast<int>((w >> (8 * j + 2 * s)) & 3u) - 1);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) acc[m][4 * s + j] += t * y[m];
+            }
+    }
+    // sum over the 16 row lanes of each word (lane bits 2..5)
+#pragma unroll
+    for (int off = 4; off < 64; off <<= 1)
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int c = 0; c < 16; ++c) acc[m][c] += __shfl_xor(acc[m][c], off);
+    if (r == 0) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int c = 0; c < 16; ++c) red[wave][m][16 * d + c] = acc[m][c];
+    }
+    __syncthreads();
+    const float g = scale ? *gamma_p : 1.0f;
+    float *o = out + static_cast<int64_t>(blockIdx.z) * zstride;
+    for (int e = threadIdx.x; e < MT * 64; e += 256) {
+        const int m = e / 64, c = e % 64;
+        const int64_t k = kb * 64 + c;
+        if (m < M && k < K) o[m * ldo + k] = g * (red[0][m][c] + red[1][m][c] + red[2][m][c] + red[3][m][c]);
+    }
+}
+
 // dX[m][k] = gamma * sum over the S <= DX_MAX_SPLITS splits of part[z][m][k],
 // z in order (part: S blocks of M x K, row stride K).  Thread: column k =
 // blockIdx.x * 256 + tid of token m = blockIdx.y; its S loads are all issued
@@ -431,7 +498,7 @@ int64_t bwd_dx_partial_bytes(int64_t M, int64_t N, int64_t K)
 
 const char *bwd_kernel_name(bool dx, int64_t M, int64_t K)
 {
-    if (dx) return bwd_dx_few(M, K) ? "bl::k_bwd_dx_few" : "bl::k_bwd_dx";
+    if (dx) return !bwd_dx_few(M, K) ? "bl::k_bwd_dx" : (M == 1 ? "bl::k_bwd_dx_vec" : "bl::k_bwd_dx_few");
     return bwd_dw_few(M) ? "bl::k_bwd_dw_few" : "bl::k_bwd_dw";
 }
 
@@ -444,6 +511,18 @@ hipError_t launch_bwd_dx(const uint8_t *P2, const float *gamma, int64_t M, int64
         const int64_t TPS = (NT + S - 1) / S;
         const int64_t nw = TPS < DX_MAX_WAVES ? TPS : DX_MAX_WAVES;
         dim3 grid(static_cast<unsigned>(KB), static_cast<unsigned>((M + 15) / 16), static_cast<unsigned>(S));
+        if (M == 1) {
+            float *o = S == 1 ? dX : part;
+            const int64_t ldo = S == 1 ? lddx : K, zs = S == 1 ? 0 : M * K;
+            const int sc = S == 1 ? 1 : 0;
+            hipLaunchKernelGGL(k_bwd_dx_vec<1>, grid, dim3(256), 0, stream, P2, KB, NT, TPS, gamma, sc, dY, lddy, M, N,
+                               K, o, ldo, zs);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess || S == 1) return e;
+            hipLaunchKernelGGL(k_bwd_dx_sum, dim3(static_cast<unsigned>((K + 255) / 256), static_cast<unsigned>(M)),
+                               dim3(256), 0, stream, part, static_cast<int>(S), M, K, gamma, dX, lddx);
+            return hipGetLastError();
+        }
         if (S == 1) {
             hipLaunchKernelGGL(k_bwd_dx_few, grid, dim3(static_cast<unsigned>(64 * nw)), 0, stream, P2, KB, NT, TPS,
                                gamma, 1, dY, lddy, M, N, K, dX, lddx, int64_t(0));

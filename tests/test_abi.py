@@ -226,9 +226,12 @@ def test_auto_algo_dispatch():
 
 def test_backward_kernel_names():
     """dX takes the small-batch kernel while its 128 x 128 tiles number fewer
-    than 256, dW below 32 tokens; None for sizes the calls reject."""
+    than 256 (the vector-ALU one for one token), dW below 32 tokens; None
+    for sizes the calls reject."""
     f = bl.bitlinear_backward_kernel
-    assert f(1, 3200, 3200, 0) == "bl::k_bwd_dx_few"
+    assert f(1, 3200, 3200, 0) == "bl::k_bwd_dx_vec"  # one token: vector ALU
+    assert f(2, 3200, 3200, 0) == "bl::k_bwd_dx_few"
+    assert f(1, 100, 40000, 0) == "bl::k_bwd_dx"  # 313 column tiles
     assert f(2048, 3200, 3200, 0) == "bl::k_bwd_dx"  # 16 x 25 = 400 tiles
     assert f(1280, 3200, 3200, 0) == "bl::k_bwd_dx_few"  # 10 x 25 = 250 tiles
     assert f(1408, 3200, 3200, 0) == "bl::k_bwd_dx"  # 11 x 25 = 275 tiles

@@ -75,14 +75,16 @@ def test_backward_dw(M, N, K):
     assert_sum_bound(got, want, abs_terms, M)
 
 
-def test_backward_strided_and_zero_rows():
+@pytest.mark.parametrize("M", [6, 3, 1])
+def test_backward_strided_and_zero_rows(M):
     """Row strides wider than the rows; a zero gradient row and a zero
     activation token give exact zeros."""
-    M, N, K = 6, 200, 300
+    N, K = 200, 300
     t = synth.ternary_weights(N, K, seed=61)
     gamma = np.float32(0.05)
     dyw = synth.activations_f32(M, N + 13, seed=62)
-    dyw[2] = 0.0
+    if M > 2:
+        dyw[2] = 0.0
     dy = np.ascontiguousarray(dyw[:, :N])
     P = to_dev(oracle.pack(t, bl.LAYOUT_I2))
     out = torch.full((M, K + 5), float("nan"), dtype=torch.float32, device="cuda")
@@ -92,9 +94,10 @@ def test_backward_strided_and_zero_rows():
     want = oracle.backward_dx(t, gamma, dy)
     abs_terms = float(gamma) * (np.abs(dy.astype(np.float64)) @ np.abs(t.astype(np.float64)))
     assert_sum_bound(got[:, :K], want, abs_terms, N)
-    assert np.all(got[2, :K] == 0)
+    if M > 2:
+        assert np.all(got[2, :K] == 0)
     x = synth.activations_bf16(M, K, seed=63)
-    x[4] = 0
+    x[min(4, M - 1)] = 0
     q, beta = oracle.quantize_act(x)
     Xq, beta_d = bl.quantize_act(to_dev(x))
     got = to_host(bl.backward_dw(Xq, beta_d, to_dev(dyw)[:, :N], K))
