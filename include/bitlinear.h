@@ -301,8 +301,9 @@ int bitlinear_backward_dw(const int8_t *Xq, int64_t ldq, const float *beta, int6
  * 0: bitlinear_backward_dx, 1: bitlinear_backward_dw), e.g. "bl::k_bwd_dx"
  * or, for small batches, "bl::k_bwd_dx_few" ("bl::k_bwd_dx_vec" for one
  * token; either is followed by "bl::k_bwd_dx_sum" when it splits the weight
- * rows); NULL for sizes or a 'which' the calls reject.  A static string;
- * host-only, enqueues nothing.
+ * rows) and "bl::k_bwd_dw_few" ("bl::k_bwd_dw_vec" for one token); NULL for
+ * sizes or a 'which' the calls reject.  A static string; host-only,
+ * enqueues nothing.
  */
 const char *bitlinear_backward_kernel(int64_t M, int64_t N, int64_t K, int which);
 

@@ -236,6 +236,8 @@ def test_backward_kernel_names():
     assert f(1280, 3200, 3200, 0) == "bl::k_bwd_dx_few"  # 10 x 25 = 250 tiles
     assert f(1408, 3200, 3200, 0) == "bl::k_bwd_dx"  # 11 x 25 = 275 tiles
     assert f(176, 8192, 8192, 0) == "bl::k_bwd_dx_few"
+    assert f(1, 3200, 3200, 1) == "bl::k_bwd_dw_vec"  # one token: an outer product
+    assert f(2, 3200, 3200, 1) == "bl::k_bwd_dw_few"
     assert f(31, 3200, 3200, 1) == "bl::k_bwd_dw_few"
     assert f(32, 3200, 3200, 1) == "bl::k_bwd_dw"
     assert f(0, 3200, 3200, 0) is None and f(4, 3200, 3200, 2) is None and f(4, 0, 3200, 1) is None

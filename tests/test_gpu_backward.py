@@ -60,7 +60,7 @@ def test_backward_dx(layout, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 3200, 3200), (4, 130, 333), (16, 8640, 3200), (17, 100, 65), (5, 1, 7),
-                                   (300, 257, 700), (2048, 640, 1024), (33, 100, 65), (40, 129, 1030), (3, 70, 1000)])
+                                   (300, 257, 700), (2048, 640, 1024), (33, 100, 65), (40, 129, 1030), (3, 70, 1000), (1, 70, 333), (1, 9, 1030)])
 def test_backward_dw(M, N, K):
     log("backward dw", M, N, K)
     x = synth.activations_bf16(M, K, seed=M + K)
