@@ -299,7 +299,7 @@ int bitlinear_backward_dw(const int8_t *Xq, int64_t ldq, const float *beta, int6
 /*
  * Name of the main kernel a backward call with these sizes launches (which =
  * 0: bitlinear_backward_dx, 1: bitlinear_backward_dw), e.g. "bl::k_bwd_dx"
- * or, for small batches, "bl::k_bwd_dx_few" ("bl::k_bwd_dx_vec" for one
+ * or, for small batches, "bl::k_bwd_dx_few" ("bl::k_bwd_dx_vec<1>" for one
  * token; either is followed by "bl::k_bwd_dx_sum" when it splits the weight
  * rows) and "bl::k_bwd_dw_few" ("bl::k_bwd_dw_vec" for one token); NULL for
  * sizes or a 'which' the calls reject.  A static string; host-only,

@@ -548,7 +548,7 @@ int64_t bwd_dx_partial_bytes(int64_t M, int64_t N, int64_t K)
 
 const char *bwd_kernel_name(bool dx, int64_t M, int64_t K)
 {
-    if (dx) return !bwd_dx_few(M, K) ? "bl::k_bwd_dx" : (M == 1 ? "bl::k_bwd_dx_vec" : "bl::k_bwd_dx_few");
+    if (dx) return !bwd_dx_few(M, K) ? "bl::k_bwd_dx" : (M == 1 ? "bl::k_bwd_dx_vec<1>" : "bl::k_bwd_dx_few");
     return M == 1 ? "bl::k_bwd_dw_vec" : (bwd_dw_few(M) ? "bl::k_bwd_dw_few" : "bl::k_bwd_dw");
 }
 

@@ -229,7 +229,7 @@ def test_backward_kernel_names():
     than 256 (the vector-ALU one for one token), dW below 32 tokens; None
     for sizes the calls reject."""
     f = bl.bitlinear_backward_kernel
-    assert f(1, 3200, 3200, 0) == "bl::k_bwd_dx_vec"  # one token: vector ALU
+    assert f(1, 3200, 3200, 0) == "bl::k_bwd_dx_vec<1>"  # one token: vector ALU
     assert f(2, 3200, 3200, 0) == "bl::k_bwd_dx_few"
     assert f(1, 100, 40000, 0) == "bl::k_bwd_dx"  # 313 column tiles
     assert f(2048, 3200, 3200, 0) == "bl::k_bwd_dx"  # 16 x 25 = 400 tiles
