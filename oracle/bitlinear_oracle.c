@@ -324,8 +324,22 @@ void oracle_bf16_to_f32(const uint16_t *x, int64_t count, float *out)
 }
 
 /*
- * beta_m = max_k |x_mk|; s_m = 127 / beta_m (0 when beta_m == 0);
- * q_mk = clamp(rint(x_mk * s_m), -127, 127).  x is [M x K] with row stride ldx.
+ * beta_m = max_k |x_mk|, and q_mk = clamp(rint(x_mk * (127 / beta_m)), -127,
+ * 127) with ties to even, evaluated in binary32 as follows.  Let 2^e be the
+ * power of two with 1 <= beta_m / 2^e < 2, and write b = beta_m / 2^e and
+ * x~ = x_mk / 2^e (exact real numbers).  Then
+ *     s = RN32(127 / b)          (one correctly rounded division per token)
+ *     q = clamp(rint(RN32(x~ * s)), -127, 127).
+ * Dividing a whole row by 2^e leaves every ratio x / beta unchanged, so q is
+ * the same for a row and for the row scaled by any power of two (as long as
+ * the scaled row is still exact in binary32).  Wherever 127 / beta_m is a
+ * finite binary32 (beta_m >= 127 / FLT_MAX, about 3.7e-37) this is the same
+ * as RN32(x * RN32(127 / beta_m)), because then RN32(127 / beta_m) = s / 2^e
+ * exactly; for smaller beta_m that form would overflow to infinity, this one
+ * does not.  beta_m = 0 (an all-zero row) gives q = 0.
+ * x is [M x K] with row stride ldx; the rounding is done in binary64, where
+ * x~ and the product x~ * s (24 x 24 significant bits) are exact, and the
+ * product is rounded once to binary32.
  */
 int oracle_quant_act(const float *x, int64_t M, int64_t K, int64_t ldx, int8_t *q, float *beta)
 {
@@ -337,14 +351,24 @@ int oracle_quant_act(const float *x, int64_t M, int64_t K, int64_t ldx, int8_t *
             float a = fabsf(row[k]);
             if (a > b) b = a;
         }
-        float s = b > 0.0f ? 127.0f / b : 0.0f;
+        beta[m] = b;
+        if (b == 0.0f) {
+            for (int64_t k = 0; k < K; ++k) q[m * K + k] = 0;
+            continue;
+        }
+        int E;
+        (void)frexpf(b, &E);               /* b = f * 2^E, 0.5 <= f < 1 */
+        const int e = E - 1;               /* 1 <= b / 2^e < 2          */
+        const float bn = ldexpf(b, -e);    /* exact: b's significand    */
+        const float s = 127.0f / bn;       /* in (63.5, 127]            */
         for (int64_t k = 0; k < K; ++k) {
-            float r = rintf(row[k] * s);
+            const double xn = ldexp((double)row[k], -e); /* exact in binary64 */
+            const float v = (float)(xn * (double)s);     /* exact product, one rounding */
+            float r = rintf(v);
             if (r > 127.0f) r = 127.0f;
             if (r < -127.0f) r = -127.0f;
             q[m * K + k] = (int8_t)r;
         }
-        beta[m] = b;
     }
     return ORACLE_OK;
 }

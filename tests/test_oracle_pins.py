@@ -298,6 +298,71 @@ def test_act_quant_invariants():
         assert np.array_equal(bs, (beta * np.float32(2.0 ** k)).astype(np.float32))
 
 
+def _numpy_quant_where_finite(x):
+    """The quantiser in plain numpy float32 arithmetic, valid where 127 / beta
+    is a finite binary32: q = clip(rint(x * (127 / beta)), -127, 127)."""
+    x = np.asarray(x, np.float32)
+    beta = np.abs(x).max(axis=1)
+    assert np.all((beta == 0) | (beta >= np.float32(127) / np.finfo(np.float32).max))
+    with np.errstate(divide="ignore"):
+        s = np.where(beta > 0, np.float32(127) / beta, np.float32(0)).astype(np.float32)
+    q = np.clip(np.rint((x * s[:, None]).astype(np.float32)), -127, 127)
+    return q.astype(np.int8), beta
+
+
+def test_act_quant_matches_numpy_at_ordinary_scales():
+    x = synth.activations_f32(12, 700, seed=45)
+    x[2, :7] = [127.0, 2.5, -2.5, 0.5, -0.5, 1.5, -127.0]
+    x[2, 7:] = 0.0
+    q, beta = oracle.quantize_act(x)
+    qn, bn = _numpy_quant_where_finite(x)
+    assert np.array_equal(q, qn) and np.array_equal(beta, bn)
+
+
+def test_act_quant_power_of_two_invariance_over_the_whole_exponent_range():
+    # Rows of integers n * 2^k, |n| < 2^12, are exact binary32 values for
+    # every k in [-149, 115], from subnormal rows to rows near the largest
+    # finite value.  Scaling a row by a power of two must leave q unchanged
+    # and scale beta exactly, including where 127 / beta overflows binary32
+    # (beta < 127 / FLT_MAX, about 3.7e-37).
+    r = synth.rng(46)
+    n = r.integers(-4095, 4096, size=(5, 97)).astype(np.int64)
+    n[0, 3] = 4095                  # the largest integer as the absmax
+    n[1] = np.where(n[1] % 7 == 0, 0, n[1])
+    n[2, :] = 0
+    n[2, 10] = -1                   # a single nonzero of magnitude 1
+    n[3, 0] = 2048                  # absmax a power of two
+    n[3, 1:] = np.clip(n[3, 1:], -2048, 2048)
+    q0, b0 = oracle.quantize_act(n.astype(np.float32))
+    qn, bn = _numpy_quant_where_finite(n.astype(np.float32))
+    assert np.array_equal(q0, qn) and np.array_equal(b0, bn)
+    for k in range(-149, 116):
+        xk = np.ldexp(n.astype(np.float64), k)
+        x = xk.astype(np.float32)
+        assert np.array_equal(x.astype(np.float64), xk)  # the scaled rows are exact
+        q, beta = oracle.quantize_act(x)
+        assert np.array_equal(q, q0), k
+        assert np.array_equal(beta.astype(np.float64), np.ldexp(b0.astype(np.float64), k)), k
+
+
+def test_act_quant_tiny_rows_against_their_scaled_copies():
+    # Rows whose beta lies below 127 / FLT_MAX: q must equal that of the same
+    # row scaled up by 2^100 (where numpy's plain formula is finite), and a zero
+    # element must give 0 (no infinite scale, no NaN).
+    x = np.array([[1e-38, 3e-39, -5e-39, 0.0]], np.float32)
+    q, beta = oracle.quantize_act(x)
+    assert q[0].tolist() == [127, 38, -64, 0] and beta[0] == np.float32(1e-38)
+    r = synth.rng(47)
+    rows = (r.standard_normal((8, 300)) * np.exp2(r.integers(-146, -122, (8, 1)))).astype(np.float32)
+    rows[1, :5] = 0.0
+    up = np.ldexp(rows.astype(np.float64), 100).astype(np.float32)
+    assert np.array_equal(up.astype(np.float64), np.ldexp(rows.astype(np.float64), 100))
+    q, beta = oracle.quantize_act(rows)
+    qn, _ = _numpy_quant_where_finite(up)
+    assert np.array_equal(q, qn)
+    assert np.all(np.abs(q[np.arange(8), np.abs(rows).argmax(axis=1)].astype(int)) == 127)
+
+
 def test_act_quant_bf16_input_is_widened_exactly():
     xb = synth.activations_bf16(4, 64, seed=42)
     q1, b1 = oracle.quantize_act(xb)
