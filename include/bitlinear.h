@@ -17,7 +17,11 @@
  *   gamma   = mean |W| over the whole tensor, exact, rounded once to binary32;
  *   T       = clamp(rint(W / gamma), -1, +1), IEEE division, ties to even;
  *   beta_m  = max_k |x_mk| (per token);
- *   q_mk    = clamp(rint(x_mk * (127 / beta_m)), -127, 127), ties to even;
+ *   q_mk    = clamp(rint(x_mk * (127 / beta_m)), -127, 127), ties to even,
+ *             in binary32 at the power-of-two scale of the row where beta_m
+ *             lies in [1, 2) (one rounded division 127 / b per token, one
+ *             rounded product per element), so a row and its 2^k multiple
+ *             give the same q, tiny rows included;
  *   acc_mn  = sum_k q_mk * T_nk, exact in int32;
  *   y_mn    = float(acc_mn) * ((gamma * beta_m) / 127), binary32.
  *
@@ -170,6 +174,10 @@ int bitlinear_binarize_weights(const float *W, int64_t N, int64_t K, int64_t ldw
                                float *gamma, void *ws, int64_t ws_bytes, void *stream);
 
 /*
+ * Packing of the ternary weights: 1.58 bits of information per weight, stored
+ * as 2 bits in practice (HackerPapers digest, thread "GPUs Go Brrr") or five
+ * ternary digits to a byte (thread "How to pack ternary numbers in 8-bit
+ * bytes"); the layouts are this library's convention (see above).
  * Pack ternary weights T int8 [N x K] (row stride ldt >= K, values in
  * {-1, 0, +1}) into P (bitlinear_packed_bytes(N, K, layout) bytes, 16-byte
  * aligned).  Every byte of P is written, padding included.  Values of T
@@ -218,7 +226,11 @@ int bitlinear_quantize_act_tiled(const void *X, int x_dtype, int64_t M, int64_t 
                                  int8_t *Xt, int64_t xt_bytes, float *beta, void *stream);
 
 /*
- * BitLinear forward: Y = rescale(quant(X) (x) T^T), T given packed in P.
+ * BitLinear forward, the drop-in replacement of nn.Linear (LIT-380 record, Key
+ * takeaways, bullet 1: ternary weights from the absmean function, 8-bit
+ * activations), whose product is integer additions and subtractions only
+ * (bullet 4), computed exactly in int32 and rescaled by gamma * beta_m / 127:
+ * Y = rescale(quant(X) (x) T^T), T given packed in P.
  *   P        packed weights of T [N x K] in 'layout' (16-byte aligned).
  *   gamma    1 fp32 (device): the weight scale returned by quantize_weights.
  *   X        x_dtype F32 or BF16: quantised per token inside the call.  For
@@ -244,11 +256,33 @@ int bitlinear_forward(const uint8_t *P, int layout, const float *gamma, int64_t 
                       int64_t ldy, void *ws, int64_t ws_bytes, void *stream);
 
 /* Same as bitlinear_forward with an explicit kernel choice (bitlinear_algo_t);
- * returns BITLINEAR_ERR_UNSUPPORTED if that kernel cannot take these sizes. */
+ * returns BITLINEAR_ERR_UNSUPPORTED if that kernel cannot take these sizes
+ * (among them: BITLINEAR_ALGO_GEMM_MFMA on int8 rows whose stride makes the
+ * rows of one 256-token tile span 2^31 bytes or more; AUTO takes the GEMV
+ * there). */
 int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N,
                            int64_t K, const void *X, int x_dtype, int64_t ldx, const float *beta_in,
                            void *Y, int y_dtype, int64_t ldy, void *ws, int64_t ws_bytes, int algo,
                            void *stream);
+
+/*
+ * bitlinear_forward_algo that also returns the quantiser's outputs, for a
+ * backward pass that needs them (bitlinear_backward_dw takes Xq and beta).
+ *   Xq_out   int8 [M x K] (device, written), row stride ldxq >= K with
+ *            ldxq % 16 == 0, 16-byte aligned; bytes K .. ldxq-1 of each row
+ *            are written with 0.  NULL: not requested.
+ *   beta_out fp32 [M] (device, written): beta_m.  NULL iff Xq_out is NULL.
+ * Both must be NULL when x_dtype is I8 or I8_TILED (the caller already holds
+ * them).  When requested, the quantiser writes them and the product reads
+ * them as int8 input: the workspace is then the one of x_dtype I8
+ * (bitlinear_forward_workspace_bytes(M, N, K, layout, BITLINEAR_I8)), and Y
+ * is bit-identical to bitlinear_forward's.  Neither may overlap another
+ * buffer of the call.
+ */
+int bitlinear_forward_ex(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                         const void *X, int x_dtype, int64_t ldx, const float *beta_in, void *Y, int y_dtype,
+                         int64_t ldy, int8_t *Xq_out, int64_t ldxq, float *beta_out, void *ws, int64_t ws_bytes,
+                         int algo, void *stream);
 
 /*
  * Backward pass under the straight-through estimator (the pages quote the

@@ -77,6 +77,9 @@ _SIGNATURES = {
     "bitlinear_backward_dw": ([_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P], _INT),
     "bitlinear_forward_algo": (
         [_P, _INT, _P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P, _INT, _I64, _P, _I64, _INT, _P], _INT),
+    "bitlinear_forward_ex": (
+        [_P, _INT, _P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P, _INT, _I64, _P, _I64, _P, _P, _I64, _INT, _P],
+        _INT),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -178,6 +181,12 @@ def bitlinear_forward_algo(P, layout, gamma, M, N, K, X, x_dtype, ldx, beta_in, 
                            algo, stream) -> int:
     return _lib.bitlinear_forward_algo(P, layout, gamma, M, N, K, X, x_dtype, ldx, beta_in, Y, y_dtype, ldy, ws,
                                        ws_bytes, algo, stream)
+
+
+def bitlinear_forward_ex(P, layout, gamma, M, N, K, X, x_dtype, ldx, beta_in, Y, y_dtype, ldy, Xq_out, ldxq,
+                         beta_out, ws, ws_bytes, algo, stream) -> int:
+    return _lib.bitlinear_forward_ex(P, layout, gamma, M, N, K, X, x_dtype, ldx, beta_in, Y, y_dtype, ldy, Xq_out,
+                                     ldxq, beta_out, ws, ws_bytes, algo, stream)
 
 
 # --- torch-tensor helpers (allocation + marshalling) ------------------------
@@ -291,6 +300,28 @@ def forward(P, layout: int, gamma, X, N: int, K: int | None = None, beta=None, y
                                   _ptr(out), _dtype_code(out), out.stride(0), _ptr(ws) if nws > 0 else None,
                                   nws, algo, _stream(stream)), "bitlinear_forward")
     return out
+
+
+def forward_with_quant(P, layout: int, gamma, X, N: int, K: int | None = None, y_dtype=None,
+                       algo: int = ALGO_AUTO, stream=None):
+    """BitLinear forward on fp32/bf16 X [M x >=K] that also returns the
+    quantiser's outputs: (Y [M x N], Xq int8 [M x ldq], beta fp32 [M]) with
+    ldq = K rounded up to 16 (bitlinear_forward_ex)."""
+    torch = _torch()
+    M = X.shape[0]
+    K = X.shape[1] if K is None else K
+    ldq = (K + 15) // 16 * 16
+    out = torch.empty((M, N), dtype=y_dtype or torch.float32, device=X.device)
+    Xq = torch.empty((M, ldq), dtype=torch.int8, device=X.device)
+    beta = torch.empty(M, dtype=torch.float32, device=X.device)
+    nws = bitlinear_forward_workspace_bytes(M, N, K, layout, I8)
+    if nws < 0:
+        raise BitlinearError(ERR_INVALID_ARG, "forward_with_quant")
+    ws = torch.empty(nws, dtype=torch.uint8, device=X.device) if nws > 0 else None
+    _check(bitlinear_forward_ex(_ptr(P), layout, _ptr(gamma), M, N, K, _ptr(X), _dtype_code(X), X.stride(0), None,
+                                _ptr(out), _dtype_code(out), out.stride(0), _ptr(Xq), ldq, _ptr(beta), _ptr(ws), nws,
+                                algo, _stream(stream)), "bitlinear_forward_ex")
+    return out, Xq, beta
 
 
 def backward_dx(P, layout: int, gamma, dY, K: int, out=None, stream=None):

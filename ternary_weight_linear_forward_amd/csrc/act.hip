@@ -1,9 +1,11 @@
 // act.hip -- per-token absmax int8 quantisation of BitLinear activations.
 //
 // LIT-380 record (dmarx anthology), Key takeaways, bullet 1: activations are
-// 8-bit.  Reading: per token m, beta_m = max_k |x_mk|, s_m = 127 / beta_m
-// (correctly rounded binary32 division; s_m = 0 when beta_m = 0), and
-// q_mk = clamp(rint(x_mk * s_m), -127, 127) with ties to even.
+// 8-bit.  Reading: per token m, beta_m = max_k |x_mk| and
+// q_mk = clamp(rint(x_mk * (127 / beta_m)), -127, 127) with ties to even, in
+// binary32 with the row taken to the power-of-two scale where beta_m lies in
+// [1, 2) (token_quant in common.h: one correctly rounded division per token,
+// one rounding of each product; q = 0 for an all-zero row).
 #include "common.h"
 #include "launch.h"
 
@@ -36,7 +38,7 @@ __global__ __launch_bounds__(256) void k_quant_act(const void *__restrict__ X, i
     float amax = 0.0f;
     for (int64_t k = threadIdx.x; k < K; k += blockDim.x) amax = fmaxf(amax, fabsf(load_x<XDT>(X, base + k)));
     const float b = block_max(amax, red);
-    const float s = token_step(b);
+    const TokenQuant s = token_quant(b);
     uint32_t *qrow = reinterpret_cast<uint32_t *>(Xq + m * ldq);
     const int64_t nwords = ldq / 4;
     for (int64_t w = threadIdx.x; w < nwords; w += blockDim.x) {
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(1024) void k_quant_act_vec(const void *__restrict__
         }
     }
     const float b = block_max(amax, red);
-    const float s = token_step(b);
+    const TokenQuant s = token_quant(b);
     int8_t *qrow = Xq + m * ldq;
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void k_quant_act_rows(const void *
         amax = __uint_as_float(static_cast<uint32_t>(mb[0] > mb[1] ? mb[0] : mb[1]) << 16);
     }
     const float b = wave_max_nonneg(amax);
-    const float s = token_step(b);
+    const TokenQuant s = token_quant(b);
     int8_t *qrow = Xq + m * ldq;
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(1024) void k_quant_act_tiled(const void *__restrict
         for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
     }
     const float b = block_max(amax, red);
-    const float s = token_step(b);
+    const TokenQuant s = token_quant(b);
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
         const int64_t p = threadIdx.x + static_cast<int64_t>(j) * blockDim.x;

@@ -97,6 +97,17 @@ int64_t transcode_bytes(int64_t M, int64_t N, int64_t K, int layout)
                                                  : 0;
 }
 
+// The GEMM addresses the activation rows of one workgroup tile (at most 256
+// rows) with 32-bit offsets from the tile's first row (buffer resources), so
+// those rows must span less than 2^31 bytes.  Staged activations always do;
+// caller-quantised rows with a huge stride may not.
+constexpr int64_t kGemmMaxTileRows = 256;
+bool gemm_offsets_fit(int64_t M, int64_t K, int64_t ldq)
+{
+    const int64_t rows = M < kGemmMaxTileRows ? M : kGemmMaxTileRows;
+    return (rows - 1) * ldq + round_up(K, 16) <= int64_t(INT32_MAX);
+}
+
 // The product kernel of algo AUTO (sizes already validated).
 int auto_algo(int64_t M, int64_t N, int layout, int x_dtype)
 {
@@ -282,9 +293,10 @@ int bitlinear_quantize_act_tiled(const void *X, int x_dtype, int64_t M, int64_t 
     return status_of(bl::launch_quant_act_tiled(X, x_dtype, M, K, ldx, layout, Xt, beta, as_stream(stream)));
 }
 
-int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
-                           const void *X, int x_dtype, int64_t ldx, const float *beta_in, void *Y, int y_dtype,
-                           int64_t ldy, void *ws, int64_t ws_bytes, int algo, void *stream)
+static int forward_impl(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                        const void *X, int x_dtype, int64_t ldx, const float *beta_in, void *Y, int y_dtype,
+                        int64_t ldy, void *ws, int64_t ws_bytes, int8_t *Xq_out, int64_t ldxq, float *beta_out,
+                        int algo, void *stream)
 {
     if (!P || !gamma || !X || !Y || !valid_layout(layout)) return BITLINEAR_ERR_INVALID_ARG;
     if (M < 1 || M > BITLINEAR_MAX_M || N < 1 || N > (int64_t(1) << 31) || K < 1 || K > BITLINEAR_MAX_K)
@@ -299,6 +311,12 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
         return BITLINEAR_ERR_INVALID_ARG;
     if (algo < BITLINEAR_ALGO_AUTO || algo > BITLINEAR_ALGO_GEMM_MFMA) return BITLINEAR_ERR_INVALID_ARG;
     if (x_int8 != (beta_in != nullptr)) return BITLINEAR_ERR_INVALID_ARG;
+    // quantiser outputs: both or neither, only for fp32 / bf16 input
+    const bool q_out = Xq_out != nullptr;
+    if (q_out != (beta_out != nullptr) || (q_out && x_int8)) return BITLINEAR_ERR_INVALID_ARG;
+    if (q_out && (ldxq < K || ldxq % 16 || !stride_ok(M, ldxq) || !aligned16(Xq_out) ||
+                  (reinterpret_cast<uintptr_t>(beta_out) & 3u)))
+        return BITLINEAR_ERR_INVALID_ARG;
     if (!aligned16(P) || (reinterpret_cast<uintptr_t>(gamma) & 3u) ||
         (reinterpret_cast<uintptr_t>(X) % dtype_size(x_dtype)) ||
         (reinterpret_cast<uintptr_t>(Y) % dtype_size(y_dtype)))
@@ -308,7 +326,8 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
     if (x_dtype == BITLINEAR_I8_TILED && (!aligned16(X) || (reinterpret_cast<uintptr_t>(beta_in) & 3u)))
         return BITLINEAR_ERR_INVALID_ARG;
 
-    const int64_t need = bitlinear_forward_workspace_bytes(M, N, K, layout, x_dtype);
+    // with the quantiser's outputs requested the product reads them (as I8 input)
+    const int64_t need = bitlinear_forward_workspace_bytes(M, N, K, layout, q_out ? BITLINEAR_I8 : x_dtype);
     if (need > 0 && (!ws || ws_bytes < need)) return BITLINEAR_ERR_WORKSPACE;
     if (need > 0 && !aligned16(ws)) return BITLINEAR_ERR_INVALID_ARG;
 
@@ -324,8 +343,27 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
         if (overlap(sw, sp) || overlap(sw, sx) || overlap(sw, sy) || overlap(sw, sg))
             return BITLINEAR_ERR_INVALID_ARG;
     }
+    if (q_out) {
+        const Span sq = span_of(Xq_out, M, ldxq, ldxq, 1), sb = span_of(beta_out, 1, M, M, 4);
+        const Span others[] = {sp, sx, sy, sg};
+        for (const Span &o : others)
+            if (overlap(sq, o) || overlap(sb, o)) return BITLINEAR_ERR_INVALID_ARG;
+        if (overlap(sq, sb)) return BITLINEAR_ERR_INVALID_ARG;
+        if (need > 0) {
+            const Span sw = span_of(ws, 1, need, need, 1);
+            if (overlap(sw, sq) || overlap(sw, sb)) return BITLINEAR_ERR_INVALID_ARG;
+        }
+    }
 
-    if (algo == BITLINEAR_ALGO_AUTO) algo = auto_algo(M, N, layout, x_dtype);
+    const int64_t ldq_user = x_dtype == BITLINEAR_I8 ? ldx : (q_out ? ldxq : 0);
+    const bool user_rows = x_dtype == BITLINEAR_I8 || q_out;
+    if (algo == BITLINEAR_ALGO_GEMM_MFMA && user_rows && !gemm_offsets_fit(M, K, ldq_user))
+        return BITLINEAR_ERR_UNSUPPORTED;
+    if (algo == BITLINEAR_ALGO_AUTO) {
+        algo = auto_algo(M, N, layout, q_out ? BITLINEAR_I8 : x_dtype);
+        if (algo == BITLINEAR_ALGO_GEMM_MFMA && user_rows && !gemm_offsets_fit(M, K, ldq_user))
+            algo = BITLINEAR_ALGO_GEMV_MFMA; // 64-bit row addressing
+    }
     if (algo == BITLINEAR_ALGO_GEMV_ADDSUB && (M > 16 || layout != BITLINEAR_LAYOUT_I2))
         return BITLINEAR_ERR_UNSUPPORTED;
     if (algo == BITLINEAR_ALGO_GEMM_MFMA && layout == BITLINEAR_LAYOUT_B1 && M <= 16) return BITLINEAR_ERR_UNSUPPORTED;
@@ -344,14 +382,24 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
     a.y_dtype = y_dtype;
     a.ldy = ldy;
     a.tiled = false;
-    if (!x_int8 && algo == BITLINEAR_ALGO_GEMV_MFMA && bl::gemv_fq_ok(layout, M, N, K, x_dtype, X, ldx)) {
+    if (q_out) {
+        // the quantiser writes the caller's buffers; the product reads them
+        const hipError_t e = bl::launch_quant_act(X, x_dtype, M, K, ldx, Xq_out, ldxq, beta_out, st);
+        if (e != hipSuccess) return BITLINEAR_ERR_LAUNCH;
+        X = Xq_out;
+        x_dtype = BITLINEAR_I8;
+        ldx = ldxq;
+        beta_in = beta_out;
+    }
+    const bool x_int8_now = x_dtype == BITLINEAR_I8 || x_dtype == BITLINEAR_I8_TILED;
+    if (!x_int8_now && algo == BITLINEAR_ALGO_GEMV_MFMA && bl::gemv_fq_ok(layout, M, N, K, x_dtype, X, ldx)) {
         // 1-4 tokens: the GEMV quantises the activations itself (one launch)
         a.Xq = nullptr;
         a.ldq = 0;
         a.beta = nullptr;
         return status_of(bl::launch_gemv_fq(a, X, x_dtype, ldx, st));
     }
-    if (x_int8) {
+    if (x_int8_now) {
         a.Xq = static_cast<const int8_t *>(X);
         a.ldq = ldx;
         a.beta = beta_in;
@@ -393,6 +441,23 @@ int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int
         break;
     }
     return status_of(e);
+}
+
+int bitlinear_forward_algo(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                           const void *X, int x_dtype, int64_t ldx, const float *beta_in, void *Y, int y_dtype,
+                           int64_t ldy, void *ws, int64_t ws_bytes, int algo, void *stream)
+{
+    return forward_impl(P, layout, gamma, M, N, K, X, x_dtype, ldx, beta_in, Y, y_dtype, ldy, ws, ws_bytes, nullptr,
+                        0, nullptr, algo, stream);
+}
+
+int bitlinear_forward_ex(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                         const void *X, int x_dtype, int64_t ldx, const float *beta_in, void *Y, int y_dtype,
+                         int64_t ldy, int8_t *Xq_out, int64_t ldxq, float *beta_out, void *ws, int64_t ws_bytes,
+                         int algo, void *stream)
+{
+    return forward_impl(P, layout, gamma, M, N, K, X, x_dtype, ldx, beta_in, Y, y_dtype, ldy, ws, ws_bytes, Xq_out,
+                        ldxq, beta_out, algo, stream);
 }
 
 // i2 rewrite of b3 / b1 weights, then the small-batch dX's partial tiles

@@ -62,15 +62,39 @@ __device__ __forceinline__ float load_x(const void *X, int64_t idx)
         return bf16_bits_to_float(static_cast<const uint16_t *>(X)[idx]);
 }
 
-// Per-token quantisation step: s = 127 / beta (correctly rounded binary32
-// division), or 0 for an all-zero token.
-__device__ __forceinline__ float token_step(float beta) { return beta > 0.0f ? 127.0f / beta : 0.0f; }
+// Per-token quantisation of a row with absmax beta: q = clamp(rint(x * (127 /
+// beta)), -127, 127), ties to even, evaluated as RN32(x~ * RN32(127 / b)) with
+// b = beta / 2^e in [1, 2) and x~ = x / 2^e.  Dividing the row by a power of
+// two does not change x / beta, so q is the same for a row and for the row
+// scaled by 2^k.  Wherever 127 / beta is a finite binary32 (beta >= 2^-96 is
+// enough) that equals RN32(x * RN32(127 / beta)): then pre = 1.  Below, 127 /
+// beta would overflow (for beta < 127 / FLT_MAX), so x and beta are first
+// multiplied by pre = 2^64, exactly (x <= beta < 2^-96), which brings beta
+// into [2^-85, 2^-32) where the division is finite; the product x * pre * s
+// is then the same real number as x~ * RN32(127 / b), rounded once.
+struct TokenQuant {
+    float pre; // 1 or 2^64, exact
+    float s;   // RN32(127 / (beta * pre)), or 0 for beta = 0
+};
 
-// One activation to int8: clamp(rint(x * s), -127, 127), ties to even, as the
-// low byte of the result.
-__device__ __forceinline__ uint32_t quant_one(float x, float s)
+__device__ __forceinline__ TokenQuant token_quant(float beta)
 {
-    float r = __builtin_rintf(x * s);
+    const float pre = beta < 0x1p-96f ? 0x1p64f : 1.0f;
+    TokenQuant t;
+    t.pre = pre;
+    t.s = beta > 0.0f ? 127.0f / (beta * pre) : 0.0f;
+    return t;
+}
+
+// RN32(x * pre * s): x * pre is exact, so this is one rounding of the real
+// product.  |result| <= 127 (1 + 2^-24)^2 < 127.5 for |x| <= beta.
+__device__ __forceinline__ float token_scaled(float x, TokenQuant t) { return (x * t.pre) * t.s; }
+
+// One activation to int8: clamp(rint(x * pre * s), -127, 127), ties to even,
+// as the low byte of the result.
+__device__ __forceinline__ uint32_t quant_one(float x, TokenQuant t)
+{
+    float r = __builtin_rintf(token_scaled(x, t));
     r = r > 127.0f ? 127.0f : r;
     r = r < -127.0f ? -127.0f : r;
     return static_cast<uint32_t>(static_cast<int>(r)) & 0xffu;

@@ -461,15 +461,16 @@ __device__ __forceinline__ float fq_quantise(const FU &U, uint4 (&xv)[FU::NUW][F
         for (int w = 1; w < U.KS; ++w) b = fmaxf(b, wmax[w][t]);
         beta_lane = b;
     }
-    // q = rint(fl32(x s)) as quant_one computes it: every |x| <= beta, so
-    // |fl32(x s)| <= 127 (1 + 2^-24)^2 < 127.5 and the clamp never acts;
+    // q = rint(fl32(x pre s)) as quant_one computes it: every |x| <= beta, so
+    // |fl32(x pre s)| <= 127 (1 + 2^-24)^2 < 127.5 and the clamp never acts
+    // (s is finite for every beta: token_quant);
     // adding 1.5 * 2^23 (a separate, correctly rounded add: the build does
     // not contract) rounds to an integer with ties to even, which then sits
     // in the low bits of the sum (two's complement in its low byte).
 #pragma unroll
     for (int n = 0; n < FU::NUW; ++n) {
         const auto un = U.unit(n);
-        const float st = token_step(__shfl(beta_lane, un.tok)); // (every lane active here)
+        const TokenQuant st = token_quant(__shfl(beta_lane, un.tok)); // (every lane active here)
         if (lane + 64 * n >= U.nunits) continue;
         uint32_t w4[4];
 #pragma unroll
@@ -477,7 +478,7 @@ __device__ __forceinline__ float fq_quantise(const FU &U, uint4 (&xv)[FU::NUW][F
             uint32_t b[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float v = __uint_as_float(bits(n, 4 * q + e)) * st;
+                const float v = token_scaled(__uint_as_float(bits(n, 4 * q + e)), st);
                 b[e] = __float_as_uint(v + 12582912.0f);
             }
             const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);

@@ -187,6 +187,49 @@ def test_forward_tiled_rejects(kw, status):
     assert fw(**kw) == status
 
 
+def fx(**kw):
+    a = dict(P=A, layout=bl.LAYOUT_I2, gamma=B, M=4, N=64, K=64, X=C, x_dtype=bl.BF16, ldx=64, beta_in=None,
+             Y=D, y_dtype=bl.F32, ldy=64, Xq_out=E, ldxq=64, beta_out=E + 0x100000, ws=None, ws_bytes=0,
+             algo=bl.ALGO_AUTO, stream=None)
+    a.update(kw)
+    return bl.bitlinear_forward_ex(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(beta_out=None), bl.ERR_INVALID_ARG),                       # both or neither
+    (dict(Xq_out=None), bl.ERR_INVALID_ARG),
+    (dict(x_dtype=bl.I8, beta_in=B + 64), bl.ERR_INVALID_ARG),       # int8 input: nothing to return
+    (dict(ldxq=48), bl.ERR_INVALID_ARG),                             # ldxq < K
+    (dict(ldxq=72), bl.ERR_INVALID_ARG),                             # ldxq % 16
+    (dict(Xq_out=E + 8), bl.ERR_INVALID_ARG),                        # alignment
+    (dict(beta_out=E + 0x100002), bl.ERR_INVALID_ARG),
+    (dict(Xq_out=D), bl.ERR_INVALID_ARG),                            # overlaps Y
+    (dict(Xq_out=C), bl.ERR_INVALID_ARG),                            # overlaps X
+    (dict(beta_out=E + 16), bl.ERR_INVALID_ARG),                     # overlaps Xq_out
+    (dict(beta_out=B), bl.ERR_INVALID_ARG),                          # overlaps gamma
+])
+def test_forward_ex_rejects(kw, status):
+    assert fx(**kw) == status
+
+
+def test_forward_ex_workspace_is_the_int8_one():
+    # with the quantiser's outputs requested the product reads them: a bf16
+    # forward needs only the int8 workspace (none for i2 weights)
+    assert bl.bitlinear_forward_workspace_bytes(4, 64, 64, bl.LAYOUT_I2, bl.I8) == 0
+    assert fx(ws=None, ws_bytes=0, Xq_out=None, beta_out=None) == bl.ERR_WORKSPACE
+
+
+def test_gemm_rejects_row_offsets_beyond_32_bits():
+    # The GEMM addresses the rows of one 256-token tile with 32-bit offsets:
+    # caller-quantised rows of stride 2^24 bytes span 255 * 2^24 + K > 2^31
+    X = 0x1000000000  # far from every other fake buffer
+    kw = dict(x_dtype=bl.I8, X=X, ldx=1 << 24, beta_in=B + 64, M=300, N=4096, K=64, ldy=4096, ws=None, ws_bytes=0)
+    assert fw(algo=bl.ALGO_GEMM_MFMA, **kw) == bl.ERR_UNSUPPORTED
+    assert fw(algo=bl.ALGO_GEMM_MFMA, **dict(kw, ldx=1 << 20)) != bl.ERR_UNSUPPORTED  # 255 * 2^20 fits
+    assert fx(algo=bl.ALGO_GEMM_MFMA, M=300, N=4096, ldy=4096, X=X, ldx=64, ldxq=1 << 24,
+              Xq_out=0x3000000000, beta_out=0x2000000000) == bl.ERR_UNSUPPORTED
+
+
 def test_forward_plain_entry_validates_too():
     assert bl.bitlinear_forward(None, 0, B, 4, 64, 64, C, bl.BF16, 64, None, D, bl.F32, 64, E, 1 << 20, None) \
         == bl.ERR_INVALID_ARG

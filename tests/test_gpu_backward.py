@@ -104,3 +104,32 @@ def test_backward_strided_and_zero_rows(M):
     want = oracle.backward_dw(q, beta, dy)
     abs_terms = np.abs(dy.astype(np.float64)).T @ np.abs(oracle.dequantize_act(q, beta).astype(np.float64))
     assert_sum_bound(got, want, abs_terms, M)
+
+
+@pytest.mark.parametrize("xk", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", [(1, 3200, 3200), (4, 700, 1000), (16, 8640, 3200), (300, 640, 1000)])
+def test_forward_quant_outputs_feed_backward_dw(M, N, K, xk):
+    """bitlinear_forward_ex returns the quantiser's int8 activations and beta
+    next to Y: they equal the oracle's, Y equals the plain forward's bit for
+    bit, and bitlinear_backward_dw takes them without a second quantiser pass."""
+    log("forward_ex quant outputs -> backward_dw", M, N, K, xk)
+    t = synth.ternary_weights(N, K, seed=M + N + K)
+    x = (synth.activations_bf16 if xk == "bf16" else synth.activations_f32)(M, K, seed=M * K)
+    xf = synth.bf16_bits_to_f32(x) if xk == "bf16" else x
+    gamma = np.float32(0.0173)
+    ref = oracle.forward(t, gamma, xf)
+    P = to_dev(oracle.pack(t, bl.LAYOUT_I2))
+    g = to_dev(np.array([gamma], np.float32))
+    xd = to_dev(x)
+    y, Xq, beta = bl.forward_with_quant(P, bl.LAYOUT_I2, g, xd, N, K)
+    assert np.array_equal(to_host(Xq)[:, :K], ref["q"]) and not to_host(Xq)[:, K:].any()
+    assert np.array_equal(to_host(beta).view(np.uint32), ref["beta"].view(np.uint32))
+    y_plain = to_host(bl.forward(P, bl.LAYOUT_I2, g, xd, N, K))
+    assert np.array_equal(to_host(y).view(np.uint32), y_plain.view(np.uint32))
+    assert np.array_equal(to_host(y).view(np.uint32), ref["y"].view(np.uint32))
+    dy = synth.activations_f32(M, N, seed=M + 2 * N)
+    want = oracle.backward_dw(ref["q"], ref["beta"], dy)
+    xhat = oracle.dequantize_act(ref["q"], ref["beta"]).astype(np.float64)
+    abs_terms = np.abs(dy.astype(np.float64)).T @ np.abs(xhat)
+    got = to_host(bl.backward_dw(Xq, beta, to_dev(dy), K))
+    assert_sum_bound(got, want, abs_terms, M)

@@ -1,9 +1,8 @@
 """GPU parity at the full layer sizes of the pages' 3B and 70B models, with the
-kernels the benchmark times (automatic dispatch).  The weight path (gamma, T,
-packed bytes) and the activation quantiser are compared in full; the product
-and rescale on a sample of output columns that the oracle computes one by one,
-plus a property that holds for every element (the fp32 output is the rescale
-of the int32 output)."""
+kernels the benchmark times (automatic dispatch).  Everything is compared in
+full: gamma, T and the packed bytes of every layer, and the int32
+accumulators and fp32 outputs of every forward, element by element, against
+the oracle's (its integer product runs on every host core)."""
 import numpy as np
 import pytest
 
@@ -13,7 +12,7 @@ import oracle  # noqa: E402
 from ternary_weight_linear_forward_amd import bitlinear as bl  # noqa: E402
 from ternary_weight_linear_forward_amd import synth, workloads  # noqa: E402
 
-from gpu_helpers import assert_f32_parity, f32_bits, to_dev, to_host  # noqa: E402
+from gpu_helpers import assert_f32_parity, f32_bits, to_dev, to_host  # noqa: F401  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 LAYOUTS = {"i2": bl.LAYOUT_I2, "b3": bl.LAYOUT_B3}
@@ -61,16 +60,23 @@ def check_forward(wl, li, M, layout, act="normal"):
     P = packed[layout]
     acc = to_host(bl.forward(P, LAYOUTS[layout], gamma, xd, layer.N, layer.K, y_dtype=torch.int32))
     y = to_host(bl.forward(P, LAYOUTS[layout], gamma, xd, layer.N, layer.K, y_dtype=torch.float32))
-    q, beta = oracle.quantize_act(x)
-    # sampled columns: both ends, every tile boundary region, random interior
-    r = synth.rng(seed)
-    cols = np.unique(np.concatenate([[0, 15, 16, layer.N - 1], r.integers(0, layer.N, 60)]))
-    acc_ref = oracle.matmul(q, t_ref[cols])
-    assert np.array_equal(acc[:, cols], acc_ref)
-    assert_f32_parity(y[:, cols], oracle.rescale(acc_ref, beta, g_ref))
-    # every element: the fp32 output is the rescale of the exact accumulator
-    assert np.array_equal(f32_bits(y), f32_bits(oracle.rescale(acc, beta, g_ref)))
+    ref = _reference(wl, li, M, x, t_ref, g_ref)
+    assert np.array_equal(acc, ref["acc"]), f"acc differs at {np.argwhere(acc != ref['acc'])[:5]}"
+    assert_f32_parity(y, ref["y"])
     assert np.abs(acc.astype(np.int64)).max() <= 127 * layer.K
+
+
+_ref_cache = {}
+
+
+def _reference(wl, li, M, x, t_ref, g_ref):
+    """The oracle's forward of one (layer, M), kept while the same layer is
+    checked in another layout."""
+    key = (wl.name, li, M)
+    if key not in _ref_cache:
+        _ref_cache.clear()
+        _ref_cache[key] = oracle.forward(t_ref, g_ref, x)
+    return _ref_cache[key]
 
 
 def test_tiny_config_full_pipeline():
@@ -97,8 +103,8 @@ def test_tiny_config_full_pipeline():
     assert np.array_equal(f32_bits(to_host(beta)), f32_bits(ref["beta"]))
 
 
-@pytest.mark.parametrize("li", [0, 4, 6], ids=["q_3200x3200", "gate_8640x3200", "down_3200x8640"])
 @pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("li", range(7), ids=[l.name for l in workloads.DECODE_3B.layers])
 def test_decode_3b(li, M):
     check_forward(workloads.DECODE_3B, li, M, "i2")
 
@@ -108,8 +114,8 @@ def test_prefill_3b(li):
     check_forward(workloads.PREFILL_3B, li, 2048, "i2", act="student_t")
 
 
-@pytest.mark.parametrize("li", [0, 1, 4, 6], ids=["q_8192", "k_1024x8192", "gate_28672x8192", "down_8192x28672"])
-def test_llama70b(li):
+@pytest.mark.parametrize("M", [1, 16, 64, 176])
+@pytest.mark.parametrize("li", range(7), ids=[l.name for l in workloads.LAYERS_70B.layers])
+def test_llama70b(li, M):
     for layout in ("i2", "b3"):
-        for M in (1, 16, 64, 176):
-            check_forward(workloads.LAYERS_70B, li, M, layout)
+        check_forward(workloads.LAYERS_70B, li, M, layout)

@@ -96,3 +96,31 @@ def test_stack_graph_replay_matches_eager(stack2):
             g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(f32_bits(to_host(outs[-1])), f32_bits(want)), f"replay {r}"
+
+
+_carry = {}
+
+
+@pytest.mark.parametrize("depth", range(workloads.STACK_DEPTH))
+def test_stack_all_layers_teacher_forced(depth):
+    """All 26 decoder layers (104 links) of the stack, in order: each layer
+    starts from the GPU output of the layer before, and each of its four links
+    is compared in full with the oracle on the same fp32 input."""
+    chain = workloads.stack_chain()
+    links = chain[4 * depth: 4 * depth + 4]
+    if depth == 0:
+        x = to_dev(synth.activations_bf16(M, links[0].layer.K, seed=workloads.seed_for(workloads.STACK_3B, 0, 1)))
+    elif _carry.get("depth") == depth - 1:
+        x = _carry["x"]
+    else:
+        pytest.skip("starts from the previous layer's output: run the layers in order")
+    print("stack layer", depth, flush=True)
+    weights = _stack_weights(links)
+    ins, ys = _run_chain(links, weights, x)
+    torch.cuda.synchronize()
+    for link, (P, gamma, (t_ref, g_ref)), xin, y in zip(links, weights, ins, ys):
+        assert to_host(gamma).view(np.uint32)[0] == np.float32(g_ref).view(np.uint32), link
+        x_host = to_host(xin)
+        ref = oracle.forward(t_ref, g_ref, synth.bf16_bits_to_f32(x_host) if x_host.dtype == np.uint16 else x_host)
+        assert_f32_parity(to_host(y), ref["y"])
+    _carry.update(depth=depth, x=ys[-1])
