@@ -285,6 +285,58 @@ int bitlinear_forward_ex(const uint8_t *P, int layout, const float *gamma, int64
                          int algo, void *stream);
 
 /*
+ * Grouped forward: several BitLinears in one call, the way a decode step runs
+ * the layers of a model (q, k, v and o; gate, up and down).  Each BitLinear's
+ * weights are only a few MB, so alone its product cannot fill the chip before
+ * its launch ends, while on stock GPUs the packed-weight stream is the whole
+ * cost (LIT-380 record, closing section "Standing in the anthology").  Here
+ * every job of at most 16 tokens becomes part of one quantiser launch (every
+ * distinct input) and one product launch (every layer); other jobs run as
+ * bitlinear_forward would run them, after it, on the same stream.
+ *
+ * Job j computes exactly what bitlinear_forward computes for
+ *   P, gamma    packed weights of T [N x K] in the call's 'layout' and their
+ *               scale (as bitlinear_forward);
+ *   X, ldx      activations [M x K] of the call's x_dtype (F32 or BF16), row
+ *               stride ldx >= K;
+ *   Y, ldy      output [M x N] of the call's y_dtype, row stride ldy >= N;
+ * with the same results bit for bit.  Jobs with the same X, M, K and ldx
+ * (e.g. q, k and v) share one quantisation.  No Y may overlap any other
+ * buffer of any job.  At most BITLINEAR_MAX_GROUP jobs.
+ */
+#define BITLINEAR_MAX_GROUP 32
+
+typedef struct {
+    const uint8_t *P;
+    const float *gamma;
+    const void *X;
+    void *Y;
+    int64_t M, N, K;
+    int64_t ldx, ldy;
+} bitlinear_job_t;
+
+/* Workspace bytes of bitlinear_forward_grouped for these jobs (host-side,
+ * reads jobs only), or -1 for invalid arguments. */
+int64_t bitlinear_forward_grouped_workspace_bytes(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype);
+
+/*
+ *   jobs     host array of njobs (1 .. BITLINEAR_MAX_GROUP) descriptions; the
+ *            call reads it before it returns (the device pointers in it are
+ *            used by the enqueued work).
+ *   ws       >= bitlinear_forward_grouped_workspace_bytes(...) bytes,
+ *            16-byte aligned, overlapping no job buffer.
+ * Every job is validated before anything is enqueued (the checks of
+ * bitlinear_forward); the first failure is returned.
+ */
+int bitlinear_forward_grouped(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype, int y_dtype,
+                              void *ws, int64_t ws_bytes, void *stream);
+
+/* Name of the product kernel of the grouped launch for these jobs (as
+ * profilers print it, e.g. "bl::k_group_gemv<0, 1, 8>"), or NULL when no job
+ * is grouped or the arguments are invalid.  Thread-local storage; host-only. */
+const char *bitlinear_grouped_kernel(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype);
+
+/*
  * Backward pass under the straight-through estimator (the pages quote the
  * BitNet paper: training lets the gradient bypass the non-differentiable
  * quantisation functions; HackerPapers digest, comment on the

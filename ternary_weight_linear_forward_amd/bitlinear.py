@@ -56,6 +56,16 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _INT = ctypes.c_int
 
+class Job(ctypes.Structure):
+    """bitlinear_job_t: one BitLinear of a grouped forward (device pointers)."""
+    _fields_ = [("P", ctypes.c_void_p), ("gamma", ctypes.c_void_p), ("X", ctypes.c_void_p), ("Y", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("ldx", ctypes.c_int64),
+                ("ldy", ctypes.c_int64)]
+
+
+MAX_GROUP = 32
+_JOBS = ctypes.POINTER(Job)
+
 _SIGNATURES = {
     "bitlinear_status_string": ([_INT], ctypes.c_char_p),
     "bitlinear_version": ([], _INT),
@@ -77,6 +87,9 @@ _SIGNATURES = {
     "bitlinear_backward_dw": ([_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P], _INT),
     "bitlinear_forward_algo": (
         [_P, _INT, _P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P, _INT, _I64, _P, _I64, _INT, _P], _INT),
+    "bitlinear_forward_grouped_workspace_bytes": ([_JOBS, _INT, _INT, _INT], _I64),
+    "bitlinear_forward_grouped": ([_JOBS, _INT, _INT, _INT, _INT, _P, _I64, _P], _INT),
+    "bitlinear_grouped_kernel": ([_JOBS, _INT, _INT, _INT], ctypes.c_char_p),
     "bitlinear_forward_ex": (
         [_P, _INT, _P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P, _INT, _I64, _P, _I64, _P, _P, _I64, _INT, _P],
         _INT),
@@ -187,6 +200,28 @@ def bitlinear_forward_ex(P, layout, gamma, M, N, K, X, x_dtype, ldx, beta_in, Y,
                          beta_out, ws, ws_bytes, algo, stream) -> int:
     return _lib.bitlinear_forward_ex(P, layout, gamma, M, N, K, X, x_dtype, ldx, beta_in, Y, y_dtype, ldy, Xq_out,
                                      ldxq, beta_out, ws, ws_bytes, algo, stream)
+
+
+def job_array(jobs) -> ctypes.Array:
+    """A ctypes array of Job from a sequence of Job (or of field dicts)."""
+    arr = (Job * max(len(jobs), 1))()
+    for i, j in enumerate(jobs):
+        arr[i] = j if isinstance(j, Job) else Job(**j)
+    return arr
+
+
+def bitlinear_forward_grouped_workspace_bytes(jobs, njobs: int, layout: int, x_dtype: int) -> int:
+    return _lib.bitlinear_forward_grouped_workspace_bytes(jobs, njobs, layout, x_dtype)
+
+
+def bitlinear_forward_grouped(jobs, njobs: int, layout: int, x_dtype: int, y_dtype: int, ws, ws_bytes: int,
+                              stream) -> int:
+    return _lib.bitlinear_forward_grouped(jobs, njobs, layout, x_dtype, y_dtype, ws, ws_bytes, stream)
+
+
+def bitlinear_grouped_kernel(jobs, njobs: int, layout: int, x_dtype: int):
+    r = _lib.bitlinear_grouped_kernel(jobs, njobs, layout, x_dtype)
+    return None if r is None else r.decode()
 
 
 # --- torch-tensor helpers (allocation + marshalling) ------------------------
@@ -322,6 +357,42 @@ def forward_with_quant(P, layout: int, gamma, X, N: int, K: int | None = None, y
                                 _ptr(out), _dtype_code(out), out.stride(0), _ptr(Xq), ldq, _ptr(beta), _ptr(ws), nws,
                                 algo, _stream(stream)), "bitlinear_forward_ex")
     return out, Xq, beta
+
+
+def grouped_jobs(specs, y_dtype=None, outs=None):
+    """Job array and outputs for forward_grouped.  specs: sequence of (P, gamma,
+    X, N) or (P, gamma, X, N, K) with X [M x >=K] fp32/bf16 (cuda)."""
+    torch = _torch()
+    jobs, ys = [], []
+    for idx, sp in enumerate(specs):
+        P, gamma, X, N = sp[:4]
+        K = sp[4] if len(sp) > 4 else X.shape[1]
+        M = X.shape[0]
+        Y = outs[idx] if outs is not None else torch.empty((M, N), dtype=y_dtype or torch.float32, device=X.device)
+        ys.append(Y)
+        jobs.append(Job(P=_ptr(P), gamma=_ptr(gamma), X=_ptr(X), Y=_ptr(Y), M=M, N=N, K=K, ldx=X.stride(0),
+                        ldy=Y.stride(0)))
+    return job_array(jobs), ys
+
+
+def forward_grouped(specs, layout: int = LAYOUT_I2, y_dtype=None, ws=None, outs=None, stream=None):
+    """Several BitLinear forwards in one grouped call (bitlinear_forward_grouped).
+    specs as grouped_jobs; every X must have the same dtype.  Returns the list
+    of outputs Y [M x N]."""
+    torch = _torch()
+    if not specs:
+        return []
+    xdt = _dtype_code(specs[0][2])
+    arr, ys = grouped_jobs(specs, y_dtype, outs)
+    n = len(specs)
+    nws = bitlinear_forward_grouped_workspace_bytes(arr, n, layout, xdt)
+    if nws < 0:
+        raise BitlinearError(ERR_INVALID_ARG, "forward_grouped")
+    if nws > 0 and (ws is None or ws.numel() < nws):
+        ws = torch.empty(nws, dtype=torch.uint8, device=specs[0][2].device)
+    _check(bitlinear_forward_grouped(arr, n, layout, xdt, _dtype_code(ys[0]), _ptr(ws) if nws > 0 else None, nws,
+                                     _stream(stream)), "bitlinear_forward_grouped")
+    return ys
 
 
 def backward_dx(P, layout: int, gamma, dY, K: int, out=None, stream=None):

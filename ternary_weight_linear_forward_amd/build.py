@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbitlinear.so")
-SOURCES = ["api.cpp", "weights.hip", "act.hip", "gemv.hip", "gemm.hip", "backward.hip"]
+SOURCES = ["api.cpp", "weights.hip", "act.hip", "gemv.hip", "group.hip", "gemm.hip", "backward.hip"]
 
 
 def hipcc() -> str:

@@ -258,13 +258,11 @@ namespace bl {
 // piece per thread), loads them all before the max, then quantises from
 // registers and stores each piece with one 16-byte store.
 template <int XDT, int PPT>
-__global__ __launch_bounds__(1024) void k_quant_act_tiled(const void *__restrict__ X, int64_t M, int64_t K,
-                                                         int64_t ldx, int layout, int64_t nsteps,
-                                                         int8_t *__restrict__ Xt, float *__restrict__ beta)
+__device__ __forceinline__ void quant_tiled_row(const void *__restrict__ X, int64_t M, int64_t K, int64_t ldx,
+                                                int layout, int64_t nsteps, int8_t *__restrict__ Xt,
+                                                float *__restrict__ beta, int64_t m, float *red)
 {
     constexpr int ES = XDT == DT_F32 ? 4 : 2;
-    __shared__ float red[16];
-    const int64_t m = blockIdx.x;
     const int64_t step_k = layout == LAYOUT_I2 ? 256 : (layout == LAYOUT_B3 ? 320 : 512), kblk = step_k / 4;
     const int64_t nmf = layout == LAYOUT_I2 ? 4 : (layout == LAYOUT_B3 ? 5 : 8);
     const int64_t npieces = nsteps * step_k / 16;
@@ -321,6 +319,57 @@ __global__ __launch_bounds__(1024) void k_quant_act_tiled(const void *__restrict
         *reinterpret_cast<uint4 *>(Xt + off) = make_uint4(w[0], w[1], w[2], w[3]);
     }
     if (threadIdx.x == 0 && live_row) beta[m] = b;
+}
+
+template <int XDT, int PPT>
+__global__ __launch_bounds__(1024) void k_quant_act_tiled(const void *__restrict__ X, int64_t M, int64_t K,
+                                                         int64_t ldx, int layout, int64_t nsteps,
+                                                         int8_t *__restrict__ Xt, float *__restrict__ beta)
+{
+    __shared__ float red[16];
+    quant_tiled_row<XDT, PPT>(X, M, K, ldx, layout, nsteps, Xt, beta, blockIdx.x, red);
+}
+
+// Several inputs in one launch (the grouped forward): one workgroup per real
+// token row of every input (no padding rows: the grouped GEMV never reads
+// tokens past M), each quantised as k_quant_act_tiled quantises it.
+template <int XDT, int PPT>
+__global__ __launch_bounds__(1024) void k_group_quant_tiled(const GroupQuantArgs args)
+{
+    __shared__ float red[16];
+    int u = 0;
+    for (int t = 1; t < args.ninputs; ++t) u = static_cast<int>(blockIdx.x) >= args.in[t].row0 ? t : u;
+    const GroupInput &in = args.in[u];
+    quant_tiled_row<XDT, PPT>(in.X, in.M, in.K, in.ldx, args.layout, in.nsteps, in.Xt, in.beta,
+                              static_cast<int64_t>(blockIdx.x) - in.row0, red);
+}
+
+template <int XDT>
+static bool launch_group_quant_x(const GroupQuantArgs &args, int rows, int64_t max_npieces, hipStream_t stream)
+{
+    const int64_t threads = max_npieces >= 1024 ? 1024 : (max_npieces + 63) / 64 * 64;
+    const int64_t ppt = (max_npieces + threads - 1) / threads;
+    dim3 grid(static_cast<unsigned>(rows)), block(static_cast<unsigned>(threads));
+    if (ppt <= 1) hipLaunchKernelGGL((k_group_quant_tiled<XDT, 1>), grid, block, 0, stream, args);
+    else if (ppt <= 2) hipLaunchKernelGGL((k_group_quant_tiled<XDT, 2>), grid, block, 0, stream, args);
+    else if (ppt <= 4) hipLaunchKernelGGL((k_group_quant_tiled<XDT, 4>), grid, block, 0, stream, args);
+    else if (ppt <= 8) hipLaunchKernelGGL((k_group_quant_tiled<XDT, 8>), grid, block, 0, stream, args);
+    else return false;
+    return true;
+}
+
+hipError_t launch_group_quant(const GroupQuantArgs &args, int x_dtype, hipStream_t stream)
+{
+    int rows = 0;
+    int64_t max_np = 1;
+    for (int u = 0; u < args.ninputs; ++u) {
+        rows = args.in[u].row0 + args.in[u].M;
+        const int64_t np = args.in[u].nsteps * tiled_step_k(args.layout) / 16;
+        max_np = np > max_np ? np : max_np;
+    }
+    const bool ok = x_dtype == DT_F32 ? launch_group_quant_x<DT_F32>(args, rows, max_np, stream)
+                                      : launch_group_quant_x<DT_BF16>(args, rows, max_np, stream);
+    return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 
 template <int XDT>

@@ -460,6 +460,218 @@ int bitlinear_forward_ex(const uint8_t *P, int layout, const float *gamma, int64
                         ldxq, beta_out, algo, stream);
 }
 
+// ---- grouped forward --------------------------------------------------------
+namespace {
+
+// Whether a job runs inside the grouped launch (else as its own forward).
+bool group_eligible(const bitlinear_job_t &j, int layout)
+{
+    const int64_t kblk = layout == BITLINEAR_LAYOUT_I2 ? 64 : (layout == BITLINEAR_LAYOUT_B3 ? 80 : 128);
+    const int64_t nsteps = ((j.K + kblk - 1) / kblk + 3) / 4;
+    return j.M <= 16 && nsteps <= bl::group_max_nsteps(layout) && j.N <= (int64_t(1) << 30);
+}
+
+// The distinct inputs of the grouped jobs: jobs with the same X, M, K and ldx
+// share one quantisation.  in_of[j]: the input of job j (-1: not grouped).
+struct GroupInputs {
+    int n = 0;
+    int first_job[BITLINEAR_MAX_GROUP];
+    int in_of[BITLINEAR_MAX_GROUP];
+};
+
+GroupInputs group_inputs(const bitlinear_job_t *jobs, int njobs, int layout)
+{
+    GroupInputs g;
+    for (int j = 0; j < njobs; ++j) {
+        g.in_of[j] = -1;
+        if (!group_eligible(jobs[j], layout)) continue;
+        for (int u = 0; u < g.n; ++u) {
+            const bitlinear_job_t &o = jobs[g.first_job[u]];
+            if (o.X == jobs[j].X && o.M == jobs[j].M && o.K == jobs[j].K && o.ldx == jobs[j].ldx) g.in_of[j] = u;
+        }
+        if (g.in_of[j] < 0) {
+            g.first_job[g.n] = j;
+            g.in_of[j] = g.n++;
+        }
+    }
+    return g;
+}
+
+int64_t group_input_bytes(const bitlinear_job_t &j, int layout)
+{
+    return round_up(bl::tiled_bytes(j.M, j.K, layout), 256) + round_up(4 * j.M, 256);
+}
+
+int64_t grouped_ws_bytes(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype, const GroupInputs &g)
+{
+    int64_t total = 0, single = 0;
+    for (int u = 0; u < g.n; ++u) total += group_input_bytes(jobs[g.first_job[u]], layout);
+    for (int j = 0; j < njobs; ++j)
+        if (g.in_of[j] < 0) {
+            const bitlinear_job_t &J = jobs[j];
+            const int64_t b = bitlinear_forward_workspace_bytes(J.M, J.N, J.K, layout, x_dtype);
+            single = b > single ? b : single;
+        }
+    return total + round_up(single, 256);
+}
+
+// Argument checks of one job (the same as bitlinear_forward's for F32 / BF16
+// input), plus: its output overlaps no buffer of any job.
+int check_job(const bitlinear_job_t *jobs, int njobs, int j, int layout, int x_dtype, int y_dtype)
+{
+    const bitlinear_job_t &J = jobs[j];
+    if (!J.P || !J.gamma || !J.X || !J.Y) return BITLINEAR_ERR_INVALID_ARG;
+    if (J.M < 1 || J.M > BITLINEAR_MAX_M || J.N < 1 || J.N > (int64_t(1) << 31) || J.K < 1 || J.K > BITLINEAR_MAX_K)
+        return BITLINEAR_ERR_INVALID_ARG;
+    if (J.ldx < J.K || !stride_ok(J.M, J.ldx) || J.ldy < J.N || !stride_ok(J.M, J.ldy))
+        return BITLINEAR_ERR_INVALID_ARG;
+    if (!aligned16(J.P) || (reinterpret_cast<uintptr_t>(J.gamma) & 3u) ||
+        (reinterpret_cast<uintptr_t>(J.X) % dtype_size(x_dtype)) ||
+        (reinterpret_cast<uintptr_t>(J.Y) % dtype_size(y_dtype)))
+        return BITLINEAR_ERR_INVALID_ARG;
+    const Span sy = span_of(J.Y, J.M, J.ldy, J.N, dtype_size(y_dtype));
+    for (int o = 0; o < njobs; ++o) {
+        const bitlinear_job_t &O = jobs[o];
+        if (!O.P || !O.gamma || !O.X || O.M < 1 || O.N < 1 || O.K < 1 || O.ldx < O.K) return BITLINEAR_ERR_INVALID_ARG;
+        const int64_t pb = bitlinear_packed_bytes(O.N, O.K, layout);
+        if (pb < 0) return BITLINEAR_ERR_INVALID_ARG;
+        if (overlap(sy, span_of(O.P, 1, pb, pb, 1)) || overlap(sy, span_of(O.gamma, 1, 1, 1, 4)) ||
+            overlap(sy, span_of(O.X, O.M, O.ldx, O.K, dtype_size(x_dtype))))
+            return BITLINEAR_ERR_INVALID_ARG;
+        if (o != j && O.Y && O.M >= 1 && O.N >= 1 && O.ldy >= O.N &&
+            overlap(sy, span_of(O.Y, O.M, O.ldy, O.N, dtype_size(y_dtype))))
+            return BITLINEAR_ERR_INVALID_ARG;
+    }
+    return BITLINEAR_OK;
+}
+
+bool group_args_ok(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype, int y_dtype)
+{
+    return jobs && njobs >= 1 && njobs <= BITLINEAR_MAX_GROUP && valid_layout(layout) &&
+           (x_dtype == BITLINEAR_F32 || x_dtype == BITLINEAR_BF16) &&
+           (y_dtype == BITLINEAR_F32 || y_dtype == BITLINEAR_BF16 || y_dtype == BITLINEAR_I32);
+}
+
+// The device-side description of the grouped jobs and their inputs, carved
+// out of the workspace.
+void group_build(const bitlinear_job_t *jobs, int njobs, int layout, int y_dtype, const GroupInputs &g, void *ws,
+                 bl::GroupQuantArgs &qa, bl::GroupGemvArgs &ga)
+{
+    char *p = static_cast<char *>(ws);
+    qa.ninputs = g.n;
+    qa.layout = layout;
+    int rows = 0;
+    for (int u = 0; u < g.n; ++u) {
+        const bitlinear_job_t &J = jobs[g.first_job[u]];
+        bl::GroupInput &in = qa.in[u];
+        in.X = J.X;
+        in.ldx = J.ldx;
+        in.M = static_cast<int>(J.M);
+        in.K = static_cast<int>(J.K);
+        in.nsteps = static_cast<int>(bl::tiled_nsteps(J.K, layout));
+        in.row0 = rows;
+        rows += in.M;
+        in.Xt = reinterpret_cast<int8_t *>(p);
+        in.beta = reinterpret_cast<float *>(p + round_up(bl::tiled_bytes(J.M, J.K, layout), 256));
+        p += group_input_bytes(J, layout);
+    }
+    ga.njobs = 0;
+    ga.y_dtype = y_dtype;
+    for (int j = 0; j < njobs; ++j) {
+        if (g.in_of[j] < 0) continue;
+        const bitlinear_job_t &J = jobs[j];
+        bl::GroupJob &d = ga.job[ga.njobs++];
+        const int64_t kblk = layout == BITLINEAR_LAYOUT_I2 ? 64 : (layout == BITLINEAR_LAYOUT_B3 ? 80 : 128);
+        d.P = J.P;
+        d.gamma = J.gamma;
+        d.Xt = qa.in[g.in_of[j]].Xt;
+        d.beta = qa.in[g.in_of[j]].beta;
+        d.Y = J.Y;
+        d.ldy = J.ldy;
+        d.M = static_cast<int>(J.M);
+        d.N = static_cast<int>(J.N);
+        d.KB = static_cast<int>((J.K + kblk - 1) / kblk);
+        d.nsteps = (d.KB + 3) / 4;
+        d.wg0 = d.nwg = 0;
+    }
+}
+
+} // namespace
+
+int64_t bitlinear_forward_grouped_workspace_bytes(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype)
+{
+    if (!group_args_ok(jobs, njobs, layout, x_dtype, BITLINEAR_F32)) return -1;
+    for (int j = 0; j < njobs; ++j)
+        if (jobs[j].M < 1 || jobs[j].M > BITLINEAR_MAX_M || jobs[j].N < 1 || jobs[j].K < 1 ||
+            jobs[j].K > BITLINEAR_MAX_K)
+            return -1;
+    return grouped_ws_bytes(jobs, njobs, layout, x_dtype, group_inputs(jobs, njobs, layout));
+}
+
+const char *bitlinear_grouped_kernel(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype)
+{
+    thread_local char name[96];
+    if (bitlinear_forward_grouped_workspace_bytes(jobs, njobs, layout, x_dtype) < 0) return nullptr;
+    const GroupInputs g = group_inputs(jobs, njobs, layout);
+    if (g.n == 0) return nullptr;
+    thread_local bl::GroupQuantArgs tqa;
+    thread_local bl::GroupGemvArgs tga;
+    group_build(jobs, njobs, layout, BITLINEAR_F32, g, nullptr, tqa, tga);
+    const bl::GroupPlan plan = bl::group_plan(tga, layout);
+    bl::group_gemv_kernel_name(layout, plan.spw, name, sizeof name);
+    return name;
+}
+
+int bitlinear_forward_grouped(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype, int y_dtype,
+                              void *ws, int64_t ws_bytes, void *stream)
+{
+    if (!group_args_ok(jobs, njobs, layout, x_dtype, y_dtype)) return BITLINEAR_ERR_INVALID_ARG;
+    for (int j = 0; j < njobs; ++j) {
+        const int st = check_job(jobs, njobs, j, layout, x_dtype, y_dtype);
+        if (st != BITLINEAR_OK) return st;
+    }
+    const GroupInputs g = group_inputs(jobs, njobs, layout);
+    const int64_t need = grouped_ws_bytes(jobs, njobs, layout, x_dtype, g);
+    if (need > 0 && (!ws || ws_bytes < need)) return BITLINEAR_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(ws)) return BITLINEAR_ERR_INVALID_ARG;
+    if (need > 0) {
+        const Span sw = span_of(ws, 1, need, need, 1);
+        for (int j = 0; j < njobs; ++j) {
+            const bitlinear_job_t &J = jobs[j];
+            const int64_t pb = bitlinear_packed_bytes(J.N, J.K, layout);
+            if (overlap(sw, span_of(J.P, 1, pb, pb, 1)) || overlap(sw, span_of(J.gamma, 1, 1, 1, 4)) ||
+                overlap(sw, span_of(J.X, J.M, J.ldx, J.K, dtype_size(x_dtype))) ||
+                overlap(sw, span_of(J.Y, J.M, J.ldy, J.N, dtype_size(y_dtype))))
+                return BITLINEAR_ERR_INVALID_ARG;
+        }
+    }
+    (void)hipGetLastError();
+    hipStream_t st = as_stream(stream);
+    int64_t group_bytes = 0;
+    if (g.n > 0) {
+        bl::GroupQuantArgs qa;
+        bl::GroupGemvArgs ga;
+        group_build(jobs, njobs, layout, y_dtype, g, ws, qa, ga);
+        for (int u = 0; u < g.n; ++u) group_bytes += group_input_bytes(jobs[g.first_job[u]], layout);
+        const bl::GroupPlan plan = bl::group_plan(ga, layout);
+        if (bl::launch_group_quant(qa, x_dtype, st) != hipSuccess) return BITLINEAR_ERR_LAUNCH;
+        if (bl::launch_group_gemv(ga, plan, layout, st) != hipSuccess) return BITLINEAR_ERR_LAUNCH;
+    }
+    // the jobs the grouped launch does not take, one forward each (their
+    // workspace follows the grouped inputs'; they run one after another)
+    void *rest = static_cast<char *>(ws) + group_bytes;
+    for (int j = 0; j < njobs; ++j) {
+        if (g.in_of[j] >= 0) continue;
+        const bitlinear_job_t &J = jobs[j];
+        const int64_t nb = bitlinear_forward_workspace_bytes(J.M, J.N, J.K, layout, x_dtype);
+        const int s = forward_impl(J.P, layout, J.gamma, J.M, J.N, J.K, J.X, x_dtype, J.ldx, nullptr, J.Y, y_dtype,
+                                   J.ldy, nb > 0 ? rest : nullptr, nb, nullptr, 0, nullptr, BITLINEAR_ALGO_AUTO,
+                                   stream);
+        if (s != BITLINEAR_OK) return s;
+    }
+    return BITLINEAR_OK;
+}
+
 // i2 rewrite of b3 / b1 weights, then the small-batch dX's partial tiles
 static int64_t bwd_dx_rewrite_bytes(int64_t N, int64_t K, int layout)
 {

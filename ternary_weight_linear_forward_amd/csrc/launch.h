@@ -39,6 +39,57 @@ inline int64_t tiled_bytes(int64_t M, int64_t K, int layout)
 hipError_t launch_quant_act_tiled(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int layout,
                                   int8_t *Xt, float *beta, hipStream_t stream);
 
+// ---- grouped forward (several BitLinears of at most 16 tokens) ------------
+constexpr int GROUP_MAX_INPUTS = 32;
+constexpr int GROUP_MAX_JOBS = 32;
+
+// One distinct input of the group: X [M x K] (row stride ldx), quantised per
+// token into the tiled layout Xt (token group 0; only the M real rows are
+// written) and beta [M].  row0: its first row among all inputs' rows.
+struct GroupInput {
+    const void *X;
+    int8_t *Xt;
+    float *beta;
+    int64_t ldx;
+    int M, K, nsteps, row0;
+};
+struct GroupQuantArgs {
+    int ninputs, layout;
+    GroupInput in[GROUP_MAX_INPUTS];
+};
+// Quantise every input of the group (one launch).
+hipError_t launch_group_quant(const GroupQuantArgs &args, int x_dtype, hipStream_t stream);
+
+// One BitLinear of the group: packed weights P of [N x K] (KB k-blocks,
+// nsteps k-steps), its tiled int8 activations and beta, output Y (row stride
+// ldy).  Workgroups wg0 .. wg0 + nwg - 1 take its row tiles in contiguous
+// ranges.
+struct GroupJob {
+    const uint8_t *P;
+    const float *gamma;
+    const int8_t *Xt;
+    const float *beta;
+    void *Y;
+    int64_t ldy;
+    int M, N, KB, nsteps, wg0, nwg;
+};
+struct GroupGemvArgs {
+    int njobs, y_dtype;
+    GroupJob job[GROUP_MAX_JOBS];
+};
+// Largest k-step count a grouped job may have, its row tiles per workgroup,
+// and the plan of a launch (workgroups per job are filled in by the plan).
+int group_max_nsteps(int layout);
+constexpr int GROUP_STAGE_TILES = 32;
+struct GroupPlan {
+    int waves; // per workgroup
+    int spw;   // k-steps per wave (template)
+    int wgs;   // workgroups in all
+};
+GroupPlan group_plan(GroupGemvArgs &args, int layout);
+hipError_t launch_group_gemv(const GroupGemvArgs &args, const GroupPlan &plan, int layout, hipStream_t stream);
+void group_gemv_kernel_name(int layout, int spw, char *buf, size_t n);
+
 // Product + rescale on int8 activations Xq [M x K] (row stride ldq, 16-byte
 // aligned rows) with per-token beta.
 struct GemvArgs {

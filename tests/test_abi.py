@@ -375,3 +375,73 @@ def test_gemm_weight_workspace():
     assert ws(16, N, K, bl.LAYOUT_B3, bl.I8) == 0
     assert ws(64, N, K, bl.LAYOUT_B1, bl.I8) >= i2
     assert bl.bitlinear_forward_workspace_bytes(16, N, K, bl.LAYOUT_B1, bl.I8) == 0
+
+
+def _jobs(n=3, over=None):
+    over = over or {}
+    base = []
+    for j in range(n):
+        d = dict(P=A + 0x1000000 * j, gamma=B + 64 * j, X=C, Y=D + 0x1000000 * j, M=1, N=3200, K=3200, ldx=3200,
+                 ldy=3200)
+        d.update(over.get(j, {}))
+        base.append(d)
+    return bl.job_array(base), n
+
+
+def test_grouped_workspace_bytes():
+    arr, n = _jobs(3)  # one shared input: tiled 13 k-steps x 4 operands x 1 KiB, beta 256 B
+    assert bl.bitlinear_forward_grouped_workspace_bytes(arr, n, bl.LAYOUT_I2, bl.BF16) == 13 * 4 * 1024 + 256
+    arr, n = _jobs(2, {1: dict(X=C + 0x100000)})  # two distinct inputs
+    assert bl.bitlinear_forward_grouped_workspace_bytes(arr, n, bl.LAYOUT_I2, bl.BF16) == 2 * (13 * 4 * 1024 + 256)
+    # a job of 64 tokens runs as its own forward: its workspace is added
+    arr, n = _jobs(2, {1: dict(X=C + 0x100000, M=64)})
+    one = bl.bitlinear_forward_workspace_bytes(64, 3200, 3200, bl.LAYOUT_I2, bl.BF16)
+    assert bl.bitlinear_forward_grouped_workspace_bytes(arr, n, bl.LAYOUT_I2, bl.BF16) == \
+        13 * 4 * 1024 + 256 + (one + 255) // 256 * 256
+    assert bl.bitlinear_forward_grouped_workspace_bytes(arr, n, bl.LAYOUT_I2, bl.I8) == -1
+    assert bl.bitlinear_forward_grouped_workspace_bytes(arr, 0, bl.LAYOUT_I2, bl.BF16) == -1
+    assert bl.bitlinear_forward_grouped_workspace_bytes(arr, bl.MAX_GROUP + 1, bl.LAYOUT_I2, bl.BF16) == -1
+
+
+def test_grouped_kernel_name():
+    arr, n = _jobs(3)
+    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) == "bl::k_group_gemv<0, 1, 8>"
+    arr, n = _jobs(2, {1: dict(K=8640, ldx=8640, X=C + 0x100000)})  # 34 k-steps on 16 waves: 3 per wave
+    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) == "bl::k_group_gemv<0, 3, 3>"
+    arr, n = _jobs(1, {0: dict(M=17)})
+    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) is None
+
+
+def gfw(arr, n, **kw):
+    a = dict(layout=bl.LAYOUT_I2, x_dtype=bl.BF16, y_dtype=bl.F32, ws=E, ws_bytes=1 << 24, stream=None)
+    a.update(kw)
+    return bl.bitlinear_forward_grouped(arr, n, **a)
+
+
+@pytest.mark.parametrize("over,kw,status", [
+    ({}, dict(layout=7), bl.ERR_INVALID_ARG),
+    ({}, dict(x_dtype=bl.I8), bl.ERR_INVALID_ARG),
+    ({}, dict(y_dtype=bl.I8), bl.ERR_INVALID_ARG),
+    ({1: dict(P=None)}, {}, bl.ERR_INVALID_ARG),
+    ({2: dict(M=0)}, {}, bl.ERR_INVALID_ARG),
+    ({0: dict(ldx=3199)}, {}, bl.ERR_INVALID_ARG),
+    ({0: dict(ldy=3199)}, {}, bl.ERR_INVALID_ARG),
+    ({1: dict(P=A + 0x1000008)}, {}, bl.ERR_INVALID_ARG),            # P alignment
+    ({1: dict(Y=C)}, {}, bl.ERR_INVALID_ARG),                        # Y overlaps a job's X
+    ({1: dict(Y=D)}, {}, bl.ERR_INVALID_ARG),                        # Y overlaps another job's Y
+    ({1: dict(Y=A + 0x2000000)}, {}, bl.ERR_INVALID_ARG),            # Y overlaps another job's P
+    ({}, dict(ws=None, ws_bytes=0), bl.ERR_WORKSPACE),
+    ({}, dict(ws_bytes=1000), bl.ERR_WORKSPACE),
+    ({}, dict(ws=E + 8), bl.ERR_INVALID_ARG),
+    ({}, dict(ws=C), bl.ERR_INVALID_ARG),                            # workspace overlaps X
+])
+def test_grouped_rejects(over, kw, status):
+    arr, n = _jobs(3, over)
+    assert gfw(arr, n, **kw) == status
+
+
+def test_grouped_rejects_bad_counts():
+    arr, n = _jobs(3)
+    assert gfw(arr, 0) == bl.ERR_INVALID_ARG
+    assert gfw(arr, bl.MAX_GROUP + 1) == bl.ERR_INVALID_ARG
+    assert gfw(None, 1) == bl.ERR_INVALID_ARG
