@@ -330,26 +330,24 @@ __global__ __launch_bounds__(1024) void k_quant_act_tiled(const void *__restrict
     quant_tiled_row<XDT, PPT>(X, M, K, ldx, layout, nsteps, Xt, beta, blockIdx.x, red);
 }
 
-// Several inputs in one launch (the grouped forward): one workgroup per real
-// token row of every input (no padding rows: the grouped GEMV never reads
-// tokens past M), each quantised as k_quant_act_tiled quantises it.
+// Several inputs in one launch (the grouped forward): workgroup (m, u)
+// quantises real token row m of input u (no padding rows: the grouped GEMV
+// never reads tokens past M), as k_quant_act_tiled quantises it.
 template <int XDT, int PPT>
 __global__ __launch_bounds__(1024) void k_group_quant_tiled(const GroupQuantArgs args)
 {
     __shared__ float red[16];
-    int u = 0;
-    for (int t = 1; t < args.ninputs; ++t) u = static_cast<int>(blockIdx.x) >= args.in[t].row0 ? t : u;
-    const GroupInput &in = args.in[u];
-    quant_tiled_row<XDT, PPT>(in.X, in.M, in.K, in.ldx, args.layout, in.nsteps, in.Xt, in.beta,
-                              static_cast<int64_t>(blockIdx.x) - in.row0, red);
+    const GroupInput &in = args.in[blockIdx.y];
+    if (static_cast<int>(blockIdx.x) >= in.M) return; // (whole workgroup)
+    quant_tiled_row<XDT, PPT>(in.X, in.M, in.K, in.ldx, args.layout, in.nsteps, in.Xt, in.beta, blockIdx.x, red);
 }
 
 template <int XDT>
-static bool launch_group_quant_x(const GroupQuantArgs &args, int rows, int64_t max_npieces, hipStream_t stream)
+static bool launch_group_quant_x(const GroupQuantArgs &args, int max_m, int64_t max_npieces, hipStream_t stream)
 {
     const int64_t threads = max_npieces >= 1024 ? 1024 : (max_npieces + 63) / 64 * 64;
     const int64_t ppt = (max_npieces + threads - 1) / threads;
-    dim3 grid(static_cast<unsigned>(rows)), block(static_cast<unsigned>(threads));
+    dim3 grid(static_cast<unsigned>(max_m), static_cast<unsigned>(args.ninputs)), block(static_cast<unsigned>(threads));
     if (ppt <= 1) hipLaunchKernelGGL((k_group_quant_tiled<XDT, 1>), grid, block, 0, stream, args);
     else if (ppt <= 2) hipLaunchKernelGGL((k_group_quant_tiled<XDT, 2>), grid, block, 0, stream, args);
     else if (ppt <= 4) hipLaunchKernelGGL((k_group_quant_tiled<XDT, 4>), grid, block, 0, stream, args);
@@ -360,15 +358,15 @@ static bool launch_group_quant_x(const GroupQuantArgs &args, int rows, int64_t m
 
 hipError_t launch_group_quant(const GroupQuantArgs &args, int x_dtype, hipStream_t stream)
 {
-    int rows = 0;
+    int max_m = 1;
     int64_t max_np = 1;
     for (int u = 0; u < args.ninputs; ++u) {
-        rows = args.in[u].row0 + args.in[u].M;
+        max_m = args.in[u].M > max_m ? args.in[u].M : max_m;
         const int64_t np = args.in[u].nsteps * tiled_step_k(args.layout) / 16;
         max_np = np > max_np ? np : max_np;
     }
-    const bool ok = x_dtype == DT_F32 ? launch_group_quant_x<DT_F32>(args, rows, max_np, stream)
-                                      : launch_group_quant_x<DT_BF16>(args, rows, max_np, stream);
+    const bool ok = x_dtype == DT_F32 ? launch_group_quant_x<DT_F32>(args, max_m, max_np, stream)
+                                      : launch_group_quant_x<DT_BF16>(args, max_m, max_np, stream);
     return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 

@@ -569,7 +569,6 @@ void group_build(const bitlinear_job_t *jobs, int njobs, int layout, int y_dtype
         in.M = static_cast<int>(J.M);
         in.K = static_cast<int>(J.K);
         in.nsteps = static_cast<int>(bl::tiled_nsteps(J.K, layout));
-        in.row0 = rows;
         rows += in.M;
         in.Xt = reinterpret_cast<int8_t *>(p);
         in.beta = reinterpret_cast<float *>(p + round_up(bl::tiled_bytes(J.M, J.K, layout), 256));
@@ -653,9 +652,26 @@ int bitlinear_forward_grouped(const bitlinear_job_t *jobs, int njobs, int layout
         bl::GroupGemvArgs ga;
         group_build(jobs, njobs, layout, y_dtype, g, ws, qa, ga);
         for (int u = 0; u < g.n; ++u) group_bytes += group_input_bytes(jobs[g.first_job[u]], layout);
-        const bl::GroupPlan plan = bl::group_plan(ga, layout);
         if (bl::launch_group_quant(qa, x_dtype, st) != hipSuccess) return BITLINEAR_ERR_LAUNCH;
-        if (bl::launch_group_gemv(ga, plan, layout, st) != hipSuccess) return BITLINEAR_ERR_LAUNCH;
+        // one product launch, or several when the jobs need more workgroups
+        // than one launch maps (each job needs one per GROUP_STAGE_TILES tiles)
+        bl::GroupGemvArgs part;
+        part.y_dtype = ga.y_dtype;
+        part.njobs = 0;
+        int need_wgs = 0;
+        for (int j = 0; j <= ga.njobs; ++j) {
+            const int nwg = j < ga.njobs ? ((ga.job[j].N + 15) / 16 + bl::GROUP_STAGE_TILES - 1) / bl::GROUP_STAGE_TILES : 0;
+            if (part.njobs > 0 && (j == ga.njobs || need_wgs + nwg > bl::GROUP_MAX_WGS / 2 - 16)) {
+                const bl::GroupPlan plan = bl::group_plan(part, layout);
+                if (bl::launch_group_gemv(part, plan, layout, st) != hipSuccess) return BITLINEAR_ERR_LAUNCH;
+                part.njobs = 0;
+                need_wgs = 0;
+            }
+            if (j < ga.njobs) {
+                part.job[part.njobs++] = ga.job[j];
+                need_wgs += nwg;
+            }
+        }
     }
     // the jobs the grouped launch does not take, one forward each (their
     // workspace follows the grouped inputs'; they run one after another)

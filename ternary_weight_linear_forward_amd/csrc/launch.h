@@ -45,13 +45,14 @@ constexpr int GROUP_MAX_JOBS = 32;
 
 // One distinct input of the group: X [M x K] (row stride ldx), quantised per
 // token into the tiled layout Xt (token group 0; only the M real rows are
-// written) and beta [M].  row0: its first row among all inputs' rows.
+// written) and beta [M].  The grouped quantiser's grid is (largest M, inputs):
+// workgroup (m, u) quantises row m of input u (none when m >= M).
 struct GroupInput {
     const void *X;
     int8_t *Xt;
     float *beta;
     int64_t ldx;
-    int M, K, nsteps, row0;
+    int M, K, nsteps;
 };
 struct GroupQuantArgs {
     int ninputs, layout;
@@ -62,8 +63,8 @@ hipError_t launch_group_quant(const GroupQuantArgs &args, int x_dtype, hipStream
 
 // One BitLinear of the group: packed weights P of [N x K] (KB k-blocks,
 // nsteps k-steps), its tiled int8 activations and beta, output Y (row stride
-// ldy).  Workgroups wg0 .. wg0 + nwg - 1 take its row tiles in contiguous
-// ranges.
+// ldy).  Workgroups wg0 .. wg0 + nwg - 1 of the grouped GEMV's grid serve
+// it; jobidx (four 8-bit job indices per word) maps a workgroup to its job.
 struct GroupJob {
     const uint8_t *P;
     const float *gamma;
@@ -73,18 +74,20 @@ struct GroupJob {
     int64_t ldy;
     int M, N, KB, nsteps, wg0, nwg;
 };
+constexpr int GROUP_MAX_WGS = 512; // workgroups of one grouped launch
 struct GroupGemvArgs {
     int njobs, y_dtype;
+    uint32_t jobidx[GROUP_MAX_WGS / 4];
     GroupJob job[GROUP_MAX_JOBS];
 };
 // Largest k-step count a grouped job may have, its row tiles per workgroup,
 // and the plan of a launch (workgroups per job are filled in by the plan).
 int group_max_nsteps(int layout);
-constexpr int GROUP_STAGE_TILES = 32;
+constexpr int GROUP_STAGE_TILES = 24;
 struct GroupPlan {
     int waves; // per workgroup
     int spw;   // k-steps per wave (template)
-    int wgs;   // workgroups in all
+    int wgs;   // workgroups in all (at most GROUP_MAX_WGS; 0: too many)
 };
 GroupPlan group_plan(GroupGemvArgs &args, int layout);
 hipError_t launch_group_gemv(const GroupGemvArgs &args, const GroupPlan &plan, int layout, hipStream_t stream);

@@ -405,9 +405,9 @@ def test_grouped_workspace_bytes():
 
 def test_grouped_kernel_name():
     arr, n = _jobs(3)
-    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) == "bl::k_group_gemv<0, 1, 8>"
+    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) == "bl::k_group_gemv<0>"
     arr, n = _jobs(2, {1: dict(K=8640, ldx=8640, X=C + 0x100000)})  # 34 k-steps on 16 waves: 3 per wave
-    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) == "bl::k_group_gemv<0, 3, 3>"
+    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) == "bl::k_group_gemv<0>"
     arr, n = _jobs(1, {0: dict(M=17)})
     assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) is None
 

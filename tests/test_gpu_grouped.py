@@ -155,3 +155,10 @@ def test_grouped_graph_replay():
         torch.cuda.synchronize()
         for o, w in zip(outs, want):
             assert np.array_equal(to_host(o).view(np.uint32), w.view(np.uint32)), r
+
+
+def test_grouped_split_over_several_launches():
+    # 4096 row tiles per job: more workgroups than one grouped launch maps, so
+    # the jobs are spread over several product launches
+    shapes = [(2, 65536, 64, 0), (1, 65536, 130, 1), (4, 65536, 64, 0)]
+    Case("i2", shapes, seed=37).check(("i32", "f32"))
