@@ -332,7 +332,7 @@ int bitlinear_forward_grouped(const bitlinear_job_t *jobs, int njobs, int layout
                               void *ws, int64_t ws_bytes, void *stream);
 
 /* Name of the product kernel of the grouped launch for these jobs (as
- * profilers print it, e.g. "bl::k_group_gemv<0>"), or NULL when no job
+ * profilers print it, e.g. "bl::k_group_gemv<0, 1>" (the quantiser inside, bf16 input) or "bl::k_group_gemv<0, 2>" (quantised by k_group_quant_tiled first)), or NULL when no job
  * is grouped or the arguments are invalid.  Thread-local storage; host-only. */
 const char *bitlinear_grouped_kernel(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype);
 

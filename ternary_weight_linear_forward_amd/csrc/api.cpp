@@ -497,6 +497,22 @@ GroupInputs group_inputs(const bitlinear_job_t *jobs, int njobs, int layout)
     return g;
 }
 
+// Whether the grouped launch quantises the activations itself: every grouped
+// job has 1 to 4 tokens of 16-byte aligned rows whose bytes a 32-bit buffer
+// range covers.
+bool group_fused(const bitlinear_job_t *jobs, int njobs, int x_dtype, const GroupInputs &g)
+{
+    if (g.n == 0) return false;
+    const int64_t es = x_dtype == BITLINEAR_F32 ? 4 : 2;
+    for (int j = 0; j < njobs; ++j) {
+        if (g.in_of[j] < 0) continue;
+        const bitlinear_job_t &J = jobs[j];
+        if (J.M > 4 || !aligned16(J.X) || (J.ldx * es) % 16 || ((J.M - 1) * J.ldx + J.K) * es + 15 > INT32_MAX)
+            return false;
+    }
+    return true;
+}
+
 int64_t group_input_bytes(const bitlinear_job_t &j, int layout)
 {
     return round_up(bl::tiled_bytes(j.M, j.K, layout), 256) + round_up(4 * j.M, 256);
@@ -505,7 +521,8 @@ int64_t group_input_bytes(const bitlinear_job_t &j, int layout)
 int64_t grouped_ws_bytes(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype, const GroupInputs &g)
 {
     int64_t total = 0, single = 0;
-    for (int u = 0; u < g.n; ++u) total += group_input_bytes(jobs[g.first_job[u]], layout);
+    if (!group_fused(jobs, njobs, x_dtype, g))
+        for (int u = 0; u < g.n; ++u) total += group_input_bytes(jobs[g.first_job[u]], layout);
     for (int j = 0; j < njobs; ++j)
         if (g.in_of[j] < 0) {
             const bitlinear_job_t &J = jobs[j];
@@ -557,10 +574,10 @@ bool group_args_ok(const bitlinear_job_t *jobs, int njobs, int layout, int x_dty
 void group_build(const bitlinear_job_t *jobs, int njobs, int layout, int y_dtype, const GroupInputs &g, void *ws,
                  bl::GroupQuantArgs &qa, bl::GroupGemvArgs &ga)
 {
+    // (ws is NULL when the grouped launch quantises inside: no input areas)
     char *p = static_cast<char *>(ws);
     qa.ninputs = g.n;
     qa.layout = layout;
-    int rows = 0;
     for (int u = 0; u < g.n; ++u) {
         const bitlinear_job_t &J = jobs[g.first_job[u]];
         bl::GroupInput &in = qa.in[u];
@@ -569,10 +586,9 @@ void group_build(const bitlinear_job_t *jobs, int njobs, int layout, int y_dtype
         in.M = static_cast<int>(J.M);
         in.K = static_cast<int>(J.K);
         in.nsteps = static_cast<int>(bl::tiled_nsteps(J.K, layout));
-        rows += in.M;
-        in.Xt = reinterpret_cast<int8_t *>(p);
-        in.beta = reinterpret_cast<float *>(p + round_up(bl::tiled_bytes(J.M, J.K, layout), 256));
-        p += group_input_bytes(J, layout);
+        in.Xt = p ? reinterpret_cast<int8_t *>(p) : nullptr;
+        in.beta = p ? reinterpret_cast<float *>(p + round_up(bl::tiled_bytes(J.M, J.K, layout), 256)) : nullptr;
+        if (p) p += group_input_bytes(J, layout);
     }
     ga.njobs = 0;
     ga.y_dtype = y_dtype;
@@ -585,6 +601,9 @@ void group_build(const bitlinear_job_t *jobs, int njobs, int layout, int y_dtype
         d.gamma = J.gamma;
         d.Xt = qa.in[g.in_of[j]].Xt;
         d.beta = qa.in[g.in_of[j]].beta;
+        d.X = J.X;
+        d.ldx = J.ldx;
+        d.K = static_cast<int>(J.K);
         d.Y = J.Y;
         d.ldy = J.ldy;
         d.M = static_cast<int>(J.M);
@@ -613,11 +632,8 @@ const char *bitlinear_grouped_kernel(const bitlinear_job_t *jobs, int njobs, int
     if (bitlinear_forward_grouped_workspace_bytes(jobs, njobs, layout, x_dtype) < 0) return nullptr;
     const GroupInputs g = group_inputs(jobs, njobs, layout);
     if (g.n == 0) return nullptr;
-    thread_local bl::GroupQuantArgs tqa;
-    thread_local bl::GroupGemvArgs tga;
-    group_build(jobs, njobs, layout, BITLINEAR_F32, g, nullptr, tqa, tga);
-    const bl::GroupPlan plan = bl::group_plan(tga, layout);
-    bl::group_gemv_kernel_name(layout, plan.spw, name, sizeof name);
+    bl::group_gemv_kernel_name(layout, group_fused(jobs, njobs, x_dtype, g) ? x_dtype : BITLINEAR_I8, name,
+                               sizeof name);
     return name;
 }
 
@@ -650,9 +666,13 @@ int bitlinear_forward_grouped(const bitlinear_job_t *jobs, int njobs, int layout
     if (g.n > 0) {
         bl::GroupQuantArgs qa;
         bl::GroupGemvArgs ga;
-        group_build(jobs, njobs, layout, y_dtype, g, ws, qa, ga);
-        for (int u = 0; u < g.n; ++u) group_bytes += group_input_bytes(jobs[g.first_job[u]], layout);
-        if (bl::launch_group_quant(qa, x_dtype, st) != hipSuccess) return BITLINEAR_ERR_LAUNCH;
+        const bool fused = group_fused(jobs, njobs, x_dtype, g);
+        group_build(jobs, njobs, layout, y_dtype, g, fused ? nullptr : ws, qa, ga);
+        if (!fused) {
+            for (int u = 0; u < g.n; ++u) group_bytes += group_input_bytes(jobs[g.first_job[u]], layout);
+            if (bl::launch_group_quant(qa, x_dtype, st) != hipSuccess) return BITLINEAR_ERR_LAUNCH;
+        }
+        const int gemv_x = fused ? x_dtype : BITLINEAR_I8;
         // one product launch, or several when the jobs need more workgroups
         // than one launch maps (each job needs one per GROUP_STAGE_TILES tiles)
         bl::GroupGemvArgs part;
@@ -663,7 +683,7 @@ int bitlinear_forward_grouped(const bitlinear_job_t *jobs, int njobs, int layout
             const int nwg = j < ga.njobs ? ((ga.job[j].N + 15) / 16 + bl::GROUP_STAGE_TILES - 1) / bl::GROUP_STAGE_TILES : 0;
             if (part.njobs > 0 && (j == ga.njobs || need_wgs + nwg > bl::GROUP_MAX_WGS / 2 - 16)) {
                 const bl::GroupPlan plan = bl::group_plan(part, layout);
-                if (bl::launch_group_gemv(part, plan, layout, st) != hipSuccess) return BITLINEAR_ERR_LAUNCH;
+                if (bl::launch_group_gemv(part, plan, layout, gemv_x, st) != hipSuccess) return BITLINEAR_ERR_LAUNCH;
                 part.njobs = 0;
                 need_wgs = 0;
             }

@@ -27,6 +27,7 @@
 
 #include "common.h"
 #include "gemv_core.h"
+#include "fq_core.h"
 #include "launch.h"
 
 namespace bl {
@@ -62,36 +63,84 @@ __device__ __forceinline__ void lds_barrier()
 // spilling (about 8-12 KB per wave).
 constexpr int group_depth(int layout, int spw)
 {
-    return layout == LAYOUT_I2 ? (spw == 1 ? 10 : (spw == 2 ? 5 : 3))
+    return layout == LAYOUT_I2 ? (spw == 1 ? 10 : (spw == 2 ? 4 : 2))
            : layout == LAYOUT_B3 ? (spw == 1 ? 8 : (spw == 2 ? 4 : 2))
                                  : (spw == 1 ? 5 : 2);
 }
 
+// Raw buffer load of 16 bytes at byte voff of [base, base + nbytes): reads at
+// or past nbytes return zeros without touching memory.  base and nbytes are
+// wave-uniform.
+__device__ __forceinline__ uint4 group_buffer_load(const void *base, int nbytes, uint32_t voff)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, nbytes, 0x00020000);
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+#else
+    (void)base, (void)nbytes, (void)voff;
+    return make_uint4(0u, 0u, 0u, 0u);
+#endif
+}
+
+// i2 k-step with the 2-bit codes c = T + 1 masked in place.  Word d of the
+// lane's chunk holds weight 16d + 4s + j at bits 8j + 2s, so (w & 0x03030303)
+// are the codes of weights 16d + j, (w & 0x0c0c0c0c) 4 x the codes of weights
+// 16d + 4 + j, (w & 0x30303030) 16 x those of 16d + 8 + j and ((w >> 2) &
+// 0x30303030) 16 x those of 16d + 12 + j: 5 instructions per word, with no
+// conversion to signed bytes.  MFMA s multiplies the four words' field s with
+// the activations of the same weights (operand at[s], dword d = activations
+// 16d + 4s .. 16d + 4s + 3, a transpose of the natural operands) into an
+// accumulator of its own scale: sum_k q c = acc1 + acc4 / 4 + acc16 / 16,
+// every quotient exact, and sum_k q T = that - sum_k q.
+struct I2ScaledAcc {
+    v4i a1, a4, a16a, a16b;
+};
+
+__device__ __forceinline__ void i2_scaled_step(const uint4 &w, const v4i (&at)[4], I2ScaledAcc &acc)
+{
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    v4i b0, b1, b2, b3;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        b0[d] = static_cast<int>(wd[d] & 0x03030303u);
+        b1[d] = static_cast<int>(wd[d] & 0x0c0c0c0cu);
+        b2[d] = static_cast<int>(wd[d] & 0x30303030u);
+        b3[d] = static_cast<int>((wd[d] >> 2) & 0x30303030u);
+    }
+    acc.a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(at[0], b0, acc.a1, 0, 0, 0);
+    acc.a4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(at[1], b1, acc.a4, 0, 0, 0);
+    acc.a16a = __builtin_amdgcn_mfma_i32_16x16x64_i8(at[2], b2, acc.a16a, 0, 0, 0);
+    acc.a16b = __builtin_amdgcn_mfma_i32_16x16x64_i8(at[3], b3, acc.a16b, 0, 0, 0);
+}
+
+// LDS of the workgroup: the tile sums, and for the quantiser inside (1 to 4
+// tokens of fp32 / bf16 input) the per-wave rounding areas and maxima.
+struct GroupLds {
+    int (*sums)[4][64]; // [GROUP_STAGE_TILES][rr][lane]
+    v4i *qbuf;          // [waves][SPW * units per k-step] (quantiser inside)
+    float (*wmax)[4];   // [waves][4] (quantiser inside)
+};
+
 // One job's share of a workgroup: this wave's k-steps (nj of them, at most
-// SPW) of the row tiles lb, lb + nwg, ... (ntiles of them), D tiles of weight
-// loads in flight; each tile's partial sums go into sums[t] by LDS atomics.
-template <int LAYOUT, int SPW, int D, class Z>
-__device__ __forceinline__ void group_job_tiles(const GroupJob &J, int KS, int wave, int lane, int nj, int lb,
-                                                int ntiles, int (*sums)[4][64], const Z &zero_sums)
+// SPW; 0 for a wave without one) of the row tiles lb, lb + nwg, ... (ntiles
+// of them), D tiles of weight loads in flight; each tile's partial sums go
+// into sums[t] by LDS atomics.  XDT: DT_I8 reads the activations quantised
+// by k_group_quant_tiled (tiled layout, beta given); DT_F32 / DT_BF16 reads
+// the job's 1 to 4 tokens of X and quantises them inside (fq_quantise: beta
+// across the waves, exactly as the quantiser) and returns beta of token
+// lane % 4 in every lane.  Every wave of the workgroup calls this once: it
+// holds one barrier.
+template <int LAYOUT, int SPW, int D, int XDT>
+__device__ __forceinline__ float group_job_tiles(const GroupJob &J, int KS, int wave, int lane, int nj, int lb,
+                                                 int ntiles, const GroupLds &L)
 {
     using S = StepShape<LAYOUT>;
     constexpr int NMF = S::NMF;
     const int M = J.M, KB = J.KB, nsteps = J.nsteps;
     const int i = lane & 15, g = lane >> 4;
-    // activation operands of this wave's k-steps, once.  Lanes of tokens
-    // past M read token 0's bytes (the same cache lines) and drop them.
-    v4i a[SPW][NMF];
-    const int lane_a = i < M ? lane : (lane & ~15);
-#pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-        const int s = wave + j * KS;
-        const int sx = s < nsteps ? s : nsteps - 1;
-#pragma unroll
-        for (int d = 0; d < NMF; ++d) {
-            const v4i v = *reinterpret_cast<const v4i *>(J.Xt + ((static_cast<int64_t>(sx) * NMF + d) * 64 + lane_a) * 16);
-            a[j][d] = (s < nsteps && i < M) ? v : v4i{0, 0, 0, 0};
-        }
-    }
+
     // weight chunk offsets in a tile, per k-step (a chunk past the last
     // k-block re-reads the last one: it meets zero activations)
     uint32_t boff[SPW];
@@ -101,30 +150,82 @@ __device__ __forceinline__ void group_job_tiles(const GroupJob &J, int KS, int w
         const int kb = 4 * (s < nsteps ? s : nsteps - 1) + g;
         boff[j] = static_cast<uint32_t>(kb < KB ? kb : KB - 1) * 256u + static_cast<uint32_t>(i) * 16u;
     }
-    const int64_t tile_bytes = static_cast<int64_t>(KB) * 256;
-    const uint8_t *P0 = J.P + static_cast<int64_t>(lb) * tile_bytes;
-    const int64_t stride_bytes = static_cast<int64_t>(J.nwg) * tile_bytes;
-    // Ring loads are unconditional (tiles past the workgroup's last re-read
-    // that one, just fetched): every path has the same loads outstanding, so
-    // the wait before tile t's products leaves the next D - 1 in flight.
+    const uint32_t tile_bytes = static_cast<uint32_t>(KB) * 256u;
+    const uint32_t stride_bytes = static_cast<uint32_t>(J.nwg) * tile_bytes;
+    const int job_bytes = static_cast<int>(static_cast<int64_t>((J.N + 15) >> 4) * tile_bytes);
+    // Ring loads are unconditional, so every path has the same loads
+    // outstanding and the wait before tile t's products leaves the next D - 1
+    // in flight.  Tiles past the workgroup's last and k-steps past the wave's
+    // last ask for bytes past the job's end: the buffer returns zeros without
+    // touching memory.
     auto load_tile = [&](int t, uint4 (&b)[SPW]) {
-        const uint8_t *pt = P0 + static_cast<int64_t>(t < ntiles ? t : ntiles - 1) * stride_bytes;
+        const uint32_t toff = t < ntiles ? static_cast<uint32_t>(lb) * tile_bytes + static_cast<uint32_t>(t) * stride_bytes
+                                         : 0x80000000u;
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) b[j] = *reinterpret_cast<const uint4 *>(pt + boff[j]);
+        for (int j = 0; j < SPW; ++j) b[j] = group_buffer_load(J.P, job_bytes, j < nj ? toff + boff[j] : 0x80000000u);
     };
     uint4 b[D][SPW];
+    v4i a[SPW][NMF];
+    float beta_lane = 0.0f;
+    auto zero_sums = [&]() {
+        for (int e = threadIdx.x; e < ntiles * 4 * 64; e += blockDim.x) (&L.sums[0][0][0])[e] = 0;
+    };
+    if constexpr (XDT == DT_I8) {
+        // activation operands of this wave's k-steps, once.  Lanes of tokens
+        // past M read token 0's bytes (the same cache lines) and drop them.
+        const int lane_a = i < M ? lane : (lane & ~15);
 #pragma unroll
-    for (int d = 0; d < D; ++d) load_tile(d, b[d]);
-    // with the first loads in flight: clear the tile sums (every wave of the
-    // workgroup takes this barrier once before its first atomic)
-    zero_sums();
-
-    v4i sacc = {0, 0, 0, 0}; // sum_k q of the wave's k-steps (offset codes only)
-    if constexpr (kOffsetCodes<LAYOUT>) {
+        for (int j = 0; j < SPW; ++j) {
+            const int s = wave + j * KS;
+            const int sx = s < nsteps ? s : nsteps - 1;
 #pragma unroll
-        for (int j = 0; j < SPW; ++j)
-            if (j < nj) act_sum_step<NMF>(a[j], sacc);
+            for (int d = 0; d < NMF; ++d) {
+                const v4i v = *reinterpret_cast<const v4i *>(J.Xt + ((static_cast<int64_t>(sx) * NMF + d) * 64 + lane_a) * 16);
+                a[j][d] = (s < nsteps && i < M) ? v : v4i{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) load_tile(d, b[d]);
+        // with the first loads in flight: clear the tile sums (every wave of
+        // the workgroup takes this barrier once before its first atomic)
+        zero_sums();
+        lds_barrier();
+    } else {
+        // the wave's own activations first, then the weight ring, then the
+        // rounding while the weights are in flight (waits count loads in
+        // issue order); the quantiser's barrier also orders the clearing of
+        // the sums before the first atomic
+        using FU = FqUnits<LAYOUT, XDT, SPW>;
+        const FU U{lane, wave, KS, M, nj * M * FU::CH, J.K, static_cast<int>(J.ldx)};
+        constexpr int ES = XDT == DT_F32 ? 4 : 2;
+        const int xbytes = static_cast<int>((((static_cast<int64_t>(M) - 1) * J.ldx + J.K) * ES + 15) & ~int64_t(15));
+        uint4 xv[FU::NUW][FU::VL];
+        fq_load(U, J.X, xbytes, xv);
+#pragma unroll
+        for (int d = 0; d < D; ++d) load_tile(d, b[d]);
+        zero_sums();
+        __builtin_amdgcn_sched_barrier(0);
+        beta_lane = fq_quantise<FU, SPW>(U, xv, L.qbuf + wave * SPW * FU::UNITS, L.wmax, a);
     }
+    // i2: the operands transposed for the masked codes (i2_scaled_step)
+    if constexpr (LAYOUT == LAYOUT_I2) {
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+            v4i t[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) t[q][d] = a[j][d][q];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) a[j][q] = t[q];
+        }
+    }
+    if (nj == 0) return beta_lane;
+
+    v4i sacc = {0, 0, 0, 0}; // sum_k q of the wave's k-steps (offset codes)
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+        if (j < nj) act_sum_step<NMF>(a[j], sacc);
     // Unrolled over the most tiles a workgroup takes (a compile-time
     // recursion, so no loop is left): a loop back-edge would make the
     // compiler wait for every load in flight at each trip (it moves ring
@@ -132,28 +233,46 @@ __device__ __forceinline__ void group_job_tiles(const GroupJob &J, int KS, int w
     unroll_while<0, GROUP_STAGE_TILES>([&](auto tc) -> bool {
         constexpr int t = decltype(tc)::value;
         if (t >= ntiles) return false;
-        v4i acc[1] = {v4i{0, 0, 0, 0}};
+        v4i part;
+        if constexpr (LAYOUT == LAYOUT_I2) {
+            I2ScaledAcc acc{{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) {
-            if (j >= nj) break;
-            const uint4 bj[1] = {b[t % D][j]};
-            gemv_step<LAYOUT, 1, NMF>(bj, a[j], acc);
+            for (int j = 0; j < SPW; ++j) {
+                if (j >= nj) break;
+                i2_scaled_step(b[t % D][j], a[j], acc);
+            }
+            part = acc.a1 + (acc.a4 >> 2) + ((acc.a16a + acc.a16b) >> 4) - sacc;
+        } else {
+            v4i acc[1] = {v4i{0, 0, 0, 0}};
+#pragma unroll
+            for (int j = 0; j < SPW; ++j) {
+                if (j >= nj) break;
+                const uint4 bj[1] = {b[t % D][j]};
+                gemv_step<LAYOUT, 1, NMF>(bj, a[j], acc);
+            }
+            part = offset_fix<LAYOUT>(acc[0], sacc);
         }
         if constexpr (t + D < GROUP_STAGE_TILES) load_tile(t + D, b[t % D]);
-        const v4i part = kOffsetCodes<LAYOUT> ? offset_fix<LAYOUT>(acc[0], sacc) : acc[0];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
-            __hip_atomic_fetch_add(&sums[t][rr][lane], part[rr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_add(&L.sums[t][rr][lane], part[rr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         return true;
     });
+    return beta_lane;
 }
 
-template <int LAYOUT>
+// k-steps per wave the fused-quantiser kernel takes for a layout (its
+// rounding area and staged activations share the registers with the ring)
+constexpr int group_fq_max_spw(int layout) { return layout == LAYOUT_I2 ? 3 : 2; }
+
+template <int LAYOUT, int XDT>
 __global__ __launch_bounds__(1024) void k_group_gemv(const GroupGemvArgs args)
 {
     // int32 sums of the workgroup's tiles: [tile][token sub-row rr][lane]
     // (lane (i, g) of tile t: token 4g + rr, weight row i)
     __shared__ int sums[GROUP_STAGE_TILES][4][64];
+    __shared__ float wmax[16][4];
+    extern __shared__ v4i qbuf_dyn[]; // quantiser inside: [waves][spw * units]
 
     // this workgroup's job (one scalar load of the index table, then one
     // batch for the job's fields) and its index among the job's workgroups
@@ -169,27 +288,34 @@ __global__ __launch_bounds__(1024) void k_group_gemv(const GroupGemvArgs args)
     const int spw = (nsteps + KS - 1) / KS;           // the job's k-steps per wave (uniform)
     const int nj = wave < nsteps ? (nsteps - 1 - wave) / KS + 1 : 0; // this wave's
 
-    // gamma and beta of this lane's output tokens 4g .. 4g+3: loaded first,
-    // used only after the product (so no wait on them delays the stream)
-    // (a vector load: a scalar one would be waited for at the first barrier)
+    // gamma and (tiled input) beta of this lane's output tokens 4g .. 4g+3:
+    // loaded first, used only after the product (so no wait on them delays
+    // the stream; gamma by a vector load: a scalar one would be waited for at
+    // the first barrier)
     const float gamma = __hip_atomic_load(J.gamma, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    float bt[4];
+    float bt[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (XDT == DT_I8) {
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        const int m = 4 * g + rr;
-        bt[rr] = J.beta[m < M ? m : M - 1];
+        for (int rr = 0; rr < 4; ++rr) {
+            const int m = 4 * g + rr;
+            bt[rr] = J.beta[m < M ? m : M - 1];
+        }
     }
-    auto zero_sums = [&]() {
+    const GroupLds L{sums, qbuf_dyn, wmax};
+    float beta_lane = 0.0f;
+    if (XDT != DT_I8 || nj > 0) {
+        if (spw <= 1) beta_lane = group_job_tiles<LAYOUT, 1, group_depth(LAYOUT, 1), XDT>(J, KS, wave, lane, nj, lb, ntiles, L);
+        else if (spw == 2) beta_lane = group_job_tiles<LAYOUT, 2, group_depth(LAYOUT, 2), XDT>(J, KS, wave, lane, nj, lb, ntiles, L);
+        else if (LAYOUT == LAYOUT_I2 && spw == 3) beta_lane = group_job_tiles<LAYOUT, LAYOUT == LAYOUT_I2 ? 3 : 2, group_depth(LAYOUT, 3), XDT>(J, KS, wave, lane, nj, lb, ntiles, L);
+        else lds_barrier(); // (not reached: the plan keeps spw within the templates)
+    } else {
         for (int e = threadIdx.x; e < ntiles * 4 * 64; e += blockDim.x) (&sums[0][0][0])[e] = 0;
         lds_barrier();
-    };
-    if (nj > 0) {
-        if (spw <= 1) group_job_tiles<LAYOUT, 1, group_depth(LAYOUT, 1)>(J, KS, wave, lane, nj, lb, ntiles, sums, zero_sums);
-        else if (spw == 2) group_job_tiles<LAYOUT, 2, group_depth(LAYOUT, 2)>(J, KS, wave, lane, nj, lb, ntiles, sums, zero_sums);
-        else if (LAYOUT == LAYOUT_I2 && spw == 3) group_job_tiles<LAYOUT, LAYOUT == LAYOUT_I2 ? 3 : 2, group_depth(LAYOUT, 3)>(J, KS, wave, lane, nj, lb, ntiles, sums, zero_sums);
-        else zero_sums(); // (not reached: the plan keeps spw within the templates)
-    } else {
-        zero_sums();
+    }
+    if constexpr (XDT != DT_I8) {
+        // beta of tokens 4g + rr < 4 (every lane active for the shuffles)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) bt[rr] = __shfl(beta_lane, rr);
     }
     lds_barrier();
     float sc[4]; // rescale factors of tokens 4g .. 4g+3
@@ -253,26 +379,42 @@ GroupPlan group_plan(GroupGemvArgs &args, int layout)
     return p;
 }
 
-template <int LAYOUT>
-static void launch_group_layout(const GroupGemvArgs &args, const GroupPlan &plan, hipStream_t stream)
+template <int LAYOUT, int XDT>
+static void launch_group_x(const GroupGemvArgs &args, const GroupPlan &plan, hipStream_t stream)
 {
-    hipLaunchKernelGGL((k_group_gemv<LAYOUT>), dim3(static_cast<unsigned>(plan.wgs)),
-                       dim3(static_cast<unsigned>(plan.waves * 64)), 0, stream, args);
+    auto *f = &k_group_gemv<LAYOUT, XDT>;
+    // the rounding areas of the quantiser inside: waves x k-steps x 4 tokens
+    // x the k-step's 16-value chunks, 16 bytes each
+    const size_t lds = XDT == DT_I8 ? 0
+                                    : static_cast<size_t>(plan.waves) * plan.spw * 4 * (4 * StepShape<LAYOUT>::KBLK / 16) * 16;
+    if (lds > 0)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(f), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  static_cast<int>(lds));
+    hipLaunchKernelGGL(f, dim3(static_cast<unsigned>(plan.wgs)), dim3(static_cast<unsigned>(plan.waves * 64)), lds,
+                       stream, args);
 }
 
-hipError_t launch_group_gemv(const GroupGemvArgs &args, const GroupPlan &plan, int layout, hipStream_t stream)
+template <int LAYOUT>
+static void launch_group_layout(const GroupGemvArgs &args, const GroupPlan &plan, int x_dtype, hipStream_t stream)
+{
+    if (x_dtype == DT_BF16) launch_group_x<LAYOUT, DT_BF16>(args, plan, stream);
+    else if (x_dtype == DT_F32) launch_group_x<LAYOUT, DT_F32>(args, plan, stream);
+    else launch_group_x<LAYOUT, DT_I8>(args, plan, stream);
+}
+
+hipError_t launch_group_gemv(const GroupGemvArgs &args, const GroupPlan &plan, int layout, int x_dtype,
+                             hipStream_t stream)
 {
     if (plan.wgs < 1 || plan.spw > 3 || (layout != LAYOUT_I2 && plan.spw > 2)) return hipErrorInvalidValue;
-    if (layout == LAYOUT_I2) launch_group_layout<LAYOUT_I2>(args, plan, stream);
-    else if (layout == LAYOUT_B3) launch_group_layout<LAYOUT_B3>(args, plan, stream);
-    else launch_group_layout<LAYOUT_B1>(args, plan, stream);
+    if (layout == LAYOUT_I2) launch_group_layout<LAYOUT_I2>(args, plan, x_dtype, stream);
+    else if (layout == LAYOUT_B3) launch_group_layout<LAYOUT_B3>(args, plan, x_dtype, stream);
+    else launch_group_layout<LAYOUT_B1>(args, plan, x_dtype, stream);
     return hipGetLastError();
 }
 
-void group_gemv_kernel_name(int layout, int spw, char *buf, size_t n)
+void group_gemv_kernel_name(int layout, int x_dtype, char *buf, size_t n)
 {
-    (void)spw;
-    snprintf(buf, n, "bl::k_group_gemv<%d>", layout);
+    snprintf(buf, n, "bl::k_group_gemv<%d, %d>", layout, x_dtype);
 }
 
 } // namespace bl

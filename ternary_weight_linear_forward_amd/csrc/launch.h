@@ -68,11 +68,13 @@ hipError_t launch_group_quant(const GroupQuantArgs &args, int x_dtype, hipStream
 struct GroupJob {
     const uint8_t *P;
     const float *gamma;
-    const int8_t *Xt;
-    const float *beta;
+    const int8_t *Xt;  // quantised activations (tiled; separate quantiser)
+    const float *beta; // their beta
+    const void *X;     // or the fp32 / bf16 rows, quantised inside (1-4 tokens)
+    int64_t ldx;
     void *Y;
     int64_t ldy;
-    int M, N, KB, nsteps, wg0, nwg;
+    int M, N, K, KB, nsteps, wg0, nwg;
 };
 constexpr int GROUP_MAX_WGS = 512; // workgroups of one grouped launch
 struct GroupGemvArgs {
@@ -90,8 +92,12 @@ struct GroupPlan {
     int wgs;   // workgroups in all (at most GROUP_MAX_WGS; 0: too many)
 };
 GroupPlan group_plan(GroupGemvArgs &args, int layout);
-hipError_t launch_group_gemv(const GroupGemvArgs &args, const GroupPlan &plan, int layout, hipStream_t stream);
-void group_gemv_kernel_name(int layout, int spw, char *buf, size_t n);
+// x_dtype DT_I8: the jobs read Xt / beta (k_group_quant_tiled ran first);
+// DT_F32 / DT_BF16: every job has 1 to 4 tokens of 16-byte aligned rows X,
+// quantised inside.
+hipError_t launch_group_gemv(const GroupGemvArgs &args, const GroupPlan &plan, int layout, int x_dtype,
+                             hipStream_t stream);
+void group_gemv_kernel_name(int layout, int x_dtype, char *buf, size_t n);
 
 // Product + rescale on int8 activations Xq [M x K] (row stride ldq, 16-byte
 // aligned rows) with per-token beta.

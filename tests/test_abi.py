@@ -389,12 +389,19 @@ def _jobs(n=3, over=None):
 
 
 def test_grouped_workspace_bytes():
-    arr, n = _jobs(3)  # one shared input: tiled 13 k-steps x 4 operands x 1 KiB, beta 256 B
+    # 1-4 tokens of aligned rows: the product launch quantises them itself, no workspace
+    arr, n = _jobs(3)
+    assert bl.bitlinear_forward_grouped_workspace_bytes(arr, n, bl.LAYOUT_I2, bl.BF16) == 0
+    # 16 tokens: one tiled input (13 k-steps x 4 operands x 1 KiB) and its beta (256 B) per distinct input
+    arr, n = _jobs(3, {0: dict(M=16), 1: dict(M=16), 2: dict(M=16)})
     assert bl.bitlinear_forward_grouped_workspace_bytes(arr, n, bl.LAYOUT_I2, bl.BF16) == 13 * 4 * 1024 + 256
-    arr, n = _jobs(2, {1: dict(X=C + 0x100000)})  # two distinct inputs
+    arr, n = _jobs(2, {0: dict(M=16), 1: dict(M=16, X=C + 0x100000)})  # two distinct inputs
     assert bl.bitlinear_forward_grouped_workspace_bytes(arr, n, bl.LAYOUT_I2, bl.BF16) == 2 * (13 * 4 * 1024 + 256)
+    # unaligned rows (ldx 3201 bf16): quantised by the separate launch
+    arr, n = _jobs(1, {0: dict(ldx=3201)})
+    assert bl.bitlinear_forward_grouped_workspace_bytes(arr, n, bl.LAYOUT_I2, bl.BF16) == 13 * 4 * 1024 + 256
     # a job of 64 tokens runs as its own forward: its workspace is added
-    arr, n = _jobs(2, {1: dict(X=C + 0x100000, M=64)})
+    arr, n = _jobs(2, {0: dict(M=16), 1: dict(X=C + 0x100000, M=64)})
     one = bl.bitlinear_forward_workspace_bytes(64, 3200, 3200, bl.LAYOUT_I2, bl.BF16)
     assert bl.bitlinear_forward_grouped_workspace_bytes(arr, n, bl.LAYOUT_I2, bl.BF16) == \
         13 * 4 * 1024 + 256 + (one + 255) // 256 * 256
@@ -404,12 +411,15 @@ def test_grouped_workspace_bytes():
 
 
 def test_grouped_kernel_name():
-    arr, n = _jobs(3)
-    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) == "bl::k_group_gemv<0>"
-    arr, n = _jobs(2, {1: dict(K=8640, ldx=8640, X=C + 0x100000)})  # 34 k-steps on 16 waves: 3 per wave
-    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) == "bl::k_group_gemv<0>"
+    arr, n = _jobs(3)  # 1 token, aligned bf16 rows: the quantiser inside
+    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) == "bl::k_group_gemv<0, 1>"
+    arr, n = _jobs(2, {1: dict(K=8640, ldx=8640, X=C + 0x100000, M=16)})  # 16 tokens: quantiser launch first
+    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) == "bl::k_group_gemv<0, 2>"
     arr, n = _jobs(1, {0: dict(M=17)})
     assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) is None
+
+
+_M16 = {0: dict(M=16), 1: dict(M=16), 2: dict(M=16)}  # (grouped jobs that need a workspace)
 
 
 def gfw(arr, n, **kw):
@@ -430,10 +440,10 @@ def gfw(arr, n, **kw):
     ({1: dict(Y=C)}, {}, bl.ERR_INVALID_ARG),                        # Y overlaps a job's X
     ({1: dict(Y=D)}, {}, bl.ERR_INVALID_ARG),                        # Y overlaps another job's Y
     ({1: dict(Y=A + 0x2000000)}, {}, bl.ERR_INVALID_ARG),            # Y overlaps another job's P
-    ({}, dict(ws=None, ws_bytes=0), bl.ERR_WORKSPACE),
-    ({}, dict(ws_bytes=1000), bl.ERR_WORKSPACE),
-    ({}, dict(ws=E + 8), bl.ERR_INVALID_ARG),
-    ({}, dict(ws=C), bl.ERR_INVALID_ARG),                            # workspace overlaps X
+    (_M16, dict(ws=None, ws_bytes=0), bl.ERR_WORKSPACE),
+    (_M16, dict(ws_bytes=1000), bl.ERR_WORKSPACE),
+    (_M16, dict(ws=E + 8), bl.ERR_INVALID_ARG),
+    (_M16, dict(ws=C), bl.ERR_INVALID_ARG),                          # workspace overlaps X
 ])
 def test_grouped_rejects(over, kw, status):
     arr, n = _jobs(3, over)

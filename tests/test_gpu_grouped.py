@@ -29,7 +29,7 @@ class Case:
     """Jobs (M, N, K, input id) with seeded weights and inputs; jobs with the
     same input id share one X."""
 
-    def __init__(self, layout, shapes, xk="bf16", seed=0, tiny=False):
+    def __init__(self, layout, shapes, xk="bf16", seed=0, tiny=False, pad=False):
         self.layout, self.xk = layout, xk
         self.t, self.g, self.P, self.gd = [], [], [], []
         self.x_host, self.x_dev = {}, {}
@@ -49,7 +49,17 @@ class Case:
                     xf[::2] *= 2.0 ** -130
                     x = synth.to_bf16_bits(xf.astype(np.float32)) if xk == "bf16" else xf.astype(np.float32)
                 self.x_host[xid] = x
-                self.x_dev[xid] = to_dev(x)
+                if pad:  # rows padded to 16 bytes, passed as a strided view
+                    ld = -(-K * x.itemsize // 16) * 16 // x.itemsize
+                    xw = np.zeros((M, ld), x.dtype)
+                    xw[:, :K] = x
+                    self.x_dev[xid] = to_dev(xw)[:, :K]
+                else:
+                    self.x_dev[xid] = to_dev(x)
+
+    def kernel(self):
+        xdt = bl.BF16 if self.xk == "bf16" else bl.F32
+        return bl.bitlinear_grouped_kernel(bl.grouped_jobs(self.specs())[0], len(self.shapes), LAYOUTS[self.layout], xdt)
 
     def specs(self):
         return [(self.P[j], self.gd[j], self.x_dev[xid], N, K) for j, (M, N, K, xid) in enumerate(self.shapes)]
@@ -162,3 +172,27 @@ def test_grouped_split_over_several_launches():
     # the jobs are spread over several product launches
     shapes = [(2, 65536, 64, 0), (1, 65536, 130, 1), (4, 65536, 64, 0)]
     Case("i2", shapes, seed=37).check(("i32", "f32"))
+
+
+@pytest.mark.parametrize("xk", ["bf16", "f32"])
+@pytest.mark.parametrize("layout", ["i2", "b3", "b1"])
+def test_grouped_quantiser_inside(layout, xk):
+    """1 to 4 tokens in every job, 16-byte aligned rows: the product launch
+    quantises the activations itself (no quantiser launch); ragged K and N,
+    zero, tie and tiny rows."""
+    shapes = [(1, 17, 64, 0), (3, 700, 1001, 1), (4, 1000, 77, 2), (2, 333, 3203, 3), (4, 8640, 3200, 4),
+              (1, 48, 8192, 5), (4, 3200, 3200, 6)]
+    c = Case(layout, shapes, xk=xk, seed=41, pad=True)
+    x = c.x_host[6]
+    xf = synth.bf16_bits_to_f32(x) if x.dtype == np.uint16 else x
+    xf = xf.copy()
+    xf[0] = 0.0                                         # zero token
+    xf[1, :7] = [127.0, 2.5, -2.5, 0.5, -0.5, 1.5, -127.0]
+    xf[1, 7:] = 0.0                                     # ties
+    xf[2] = (xf[2].astype(np.float64) * 2.0 ** -130).astype(np.float32)  # subnormal token
+    c.x_host[6] = synth.to_bf16_bits(xf) if x.dtype == np.uint16 else xf
+    c.x_dev[6] = to_dev(c.x_host[6])
+    kname = c.kernel()
+    log("grouped, quantiser inside", layout, xk, kname)
+    assert kname == f"bl::k_group_gemv<{LAYOUTS[layout]}, {bl.BF16 if xk == 'bf16' else bl.F32}>", kname
+    c.check()
