@@ -1,28 +1,32 @@
 #!/usr/bin/env python3
 """Throughput of the BitLinear forward (BitNet b1.58) on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--mode grouped|single]
 
-A step is one pass of the forward over one batch of synthetic inputs: for the
-default workload (the 3B model's decode layers) every layer of the set
+A step is one pass of the forward over one batch of synthetic inputs.  For the
+default workload (the 3B model's decode layers) that is every layer of the set
 q, k, v, o (3200 x 3200), gate, up (8640 x 3200), down (3200 x 8640) at every
 batch M in {1, 4, 16}: bf16 activations quantised per token to int8, the
-ternary x int8 product from 2-bit packed weights, and the fp32 rescale.
-Weights are ternarised and packed once, before timing (a load-time step; its
-throughput is reported separately under "weight_prep").  Steps rotate over
-copies of the packed weights totalling >= 1 GiB so that neither the L2 nor
-the 256 MB Infinity Cache serves them.  Each step is a captured HIP graph.
+ternary x int8 product from 2-bit packed weights, and the fp32 rescale -- 21
+BitLinear forwards.  With --mode grouped (the default) the seven layers of
+one batch size are one bitlinear_forward_grouped call (3 calls per step);
+--mode single issues 21 bitlinear_forward calls.
+
+Weights are ternarised and packed once, before timing (a load-time step,
+reported under "weight_prep").  Every call of a step reads its own copy of
+the packed weights: the copies rotate over >= 2 GiB, so a copy is read again
+only after 2 GiB of other weights, and neither the L2 nor the 256 MB Infinity
+Cache can serve it.  Steps are captured HIP graphs replayed between HIP
+events on the launch stream.
+
+'roofline' reports the kernel with the most time per step, timed alone (a HIP
+graph of back-to-back launches rotating over every weight copy, between HIP
+events on the launch stream); 'prefill' the 3B prefill GEMM (M = 2048) the
+same way; 'cpu_baseline' the CPU oracle on a bounded sample of the same work.
 
 --workload stack_3b_26 times one token step (batch 16) through 26 decoder
-layers of the 3B model's BitLinears, 104 forwards with all weights resident:
-per layer qkv (9600 x 3200), o (3200 x 3200) reading the first 3200 columns
-of qkv's output, gate_up (17280 x 3200), down (3200 x 8640) reading the first
-8640 columns of gate_up's output; down's output feeds the next layer.
-
-One JSON line is printed.  'value' is packed-weight GB/s over the whole step
-(wall clock around K replays); 'roofline' reports the dominant kernel from a
-replay in which every launch of it is bracketed by HIP events; 'cpu_baseline'
-times the CPU oracle on a bounded sample of the same work.
+layers of the 3B model's BitLinears (104 dependent forwards, all weights
+resident; single calls only).
 """
 from __future__ import annotations
 
@@ -41,7 +45,7 @@ sys.path.insert(0, ROOT)
 METRIC = "packed-weight GB/s + effective ternary TOPS per BitLinear (decode GEMV, prefill GEMM)"
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
-MALL_DEFEAT_BYTES = 1 << 30
+ROTATE_BYTES = 2 << 30
 
 
 def parse():
@@ -51,18 +55,126 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_3b",
                     choices=["decode_3b", "prefill_3b", "llama70b_layers", "stack_3b_26"])
+    ap.add_argument("--mode", default="grouped", choices=["grouped", "single"],
+                    help="grouped: the layers of one batch size in one bitlinear_forward_grouped call; "
+                         "single: one bitlinear_forward per layer")
     ap.add_argument("--batches", default=None, help="comma list overriding the workload's batch sizes")
     ap.add_argument("--layout", default="i2", choices=["i2", "b3", "b1"],
                     help="packed weight layout; b1 runs the binary-weight variant (sign quantiser)")
     ap.add_argument("--backward", action="store_true",
                     help="time the straight-through-estimator backward (dX and dW) of the workload's forwards "
                          "instead of the forward, and print its own JSON line")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill GEMM sub-object")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 5 times (a plain copy of known size for scaling "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Ctx:
+    """Device, launch stream and the library binding."""
+
+    def __init__(self, layout_name):
+        import torch
+
+        from ternary_weight_linear_forward_amd import bitlinear as bl
+
+        self.torch = torch
+        self.bl = bl
+        self.dev = torch.device("cuda")
+        torch.cuda.set_device(0)
+        self.stream = torch.cuda.Stream()
+        self.layout = {"i2": bl.LAYOUT_I2, "b3": bl.LAYOUT_B3, "b1": bl.LAYOUT_B1}[layout_name]
+        self.layout_name = layout_name
+
+    def events(self):
+        t = self.torch
+        return t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+
+
+def prep_weights(ctx, wl, weight_specs):
+    """Quantise and pack every weight tensor on the GPU (timed), then make
+    copies of the packed set totalling >= ROTATE_BYTES."""
+    torch, bl = ctx.torch, ctx.bl
+    from ternary_weight_linear_forward_amd import synth
+
+    weight_quant = bl.binarize_weights if ctx.layout == bl.LAYOUT_B1 else bl.quantize_weights
+    layers, prep_ms, prep_bytes = [], 0.0, 0
+    with torch.cuda.stream(ctx.stream):
+        for layer, seed in weight_specs:
+            w = torch.from_numpy(synth.latent_weights(layer.N, layer.K, seed=seed)).to(ctx.dev)
+            torch.cuda.synchronize()
+            e0, e1 = ctx.events()
+            e0.record(ctx.stream)
+            T, gamma = weight_quant(w, stream=ctx.stream)
+            P = bl.pack(T, ctx.layout, stream=ctx.stream)
+            e1.record(ctx.stream)
+            torch.cuda.synchronize()
+            prep_ms += e0.elapsed_time(e1)
+            prep_bytes += w.numel() * 4
+            layers.append({"layer": layer, "gamma": gamma, "P": [P]})
+            del w, T
+    return layers, prep_ms, prep_bytes
+
+
+def add_copies(ctx, layers, ncopies):
+    for L in layers:
+        L["P"] += [L["P"][0].clone() for _ in range(ncopies - 1)]
+    ctx.torch.cuda.synchronize()
+
+
+def time_graphs(ctx, graphs, steps, warmup):
+    """Replay the step graphs round robin: warm-up, then 'steps' replays
+    between two HIP events on the launch stream.  Returns ms per step."""
+    torch = ctx.torch
+    with torch.cuda.stream(ctx.stream):
+        for k in range(warmup):
+            graphs[k % len(graphs)].replay()
+        torch.cuda.synchronize()
+        e0, e1 = ctx.events()
+        e0.record(ctx.stream)
+        for k in range(steps):
+            graphs[(warmup + k) % len(graphs)].replay()
+        e1.record(ctx.stream)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def capture(ctx, fn):
+    torch = ctx.torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(ctx.stream):
+        with torch.cuda.graph(g, stream=ctx.stream):
+            fn()
+    return g
+
+
+def time_launches(ctx, fn, ncalls, reps=3):
+    """Average duration of one call of fn(i), i = 0 .. ncalls-1 captured back
+    to back in one HIP graph, replayed 'reps' times between HIP events on the
+    launch stream."""
+    torch = ctx.torch
+    with torch.cuda.stream(ctx.stream):
+        fn(0)
+        torch.cuda.synchronize()
+    g = capture(ctx, lambda: [fn(i) for i in range(ncalls)])
+    ts = []
+    with torch.cuda.stream(ctx.stream):
+        g.replay()  # warm
+        for _ in range(reps):
+            ea, eb = ctx.events()
+            ea.record(ctx.stream)
+            g.replay()
+            eb.record(ctx.stream)
+            ts.append((ea, eb))
+        torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ts) / (reps * ncalls)
 
 
 def main():
@@ -85,262 +197,194 @@ def main():
         print(json.dumps({"copy_calibration_bytes_per_copy": n, "copies": 5}), flush=True)
         return
 
-    from ternary_weight_linear_forward_amd import bitlinear as bl
     from ternary_weight_linear_forward_amd import synth, workloads
 
+    ctx = Ctx(args.layout)
+    bl = ctx.bl
     wl = workloads.ALL[args.workload]
-    layout = {"i2": bl.LAYOUT_I2, "b3": bl.LAYOUT_B3, "b1": bl.LAYOUT_B1}[args.layout]
-    weight_quant = bl.binarize_weights if layout == bl.LAYOUT_B1 else bl.quantize_weights
+    layout = ctx.layout
     batches = tuple(int(b) for b in args.batches.split(",")) if args.batches else wl.batches
-    dev = torch.device("cuda")
-    torch.cuda.set_device(0)
-    stream = torch.cuda.Stream()
-    print(f"[bench] workload={wl.name} batches={batches} layout={args.layout}", file=sys.stderr, flush=True)
+    mode = "single" if wl is workloads.STACK_3B else args.mode
+    log(f"workload={wl.name} batches={batches} layout={args.layout} mode={mode}")
 
-    # ---- weights: quantise + pack on the GPU (timed separately) --------------
-    # The stack has 4 * 26 distinct weight tensors; the other workloads one
-    # tensor per named layer.
+    # ---- weights ----------------------------------------------------------------
     if wl is workloads.STACK_3B:
         chain = workloads.stack_chain(workloads.STACK_DEPTH)
-        weight_specs = [(link.layer, workloads.seed_for(wl, link.index, 0)) for link in chain]
+        specs = [(link.layer, workloads.seed_for(wl, link.index, 0)) for link in chain]
     else:
         chain = None
-        weight_specs = [(layer, workloads.seed_for(wl, li, 0)) for li, layer in enumerate(wl.layers)]
-    layers = []
-    prep_ms = 0.0
-    prep_bytes = 0
-    with torch.cuda.stream(stream):
-        for layer, seed in weight_specs:
-            w = torch.from_numpy(synth.latent_weights(layer.N, layer.K, seed=seed)).to(dev)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            T, gamma = weight_quant(w, stream=stream)
-            P = bl.pack(T, layout, stream=stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            prep_ms += e0.elapsed_time(e1)
-            prep_bytes += w.numel() * 4
-            layers.append({"layer": layer, "gamma": gamma, "P": [P]})
-            del w, T
+        specs = [(layer, workloads.seed_for(wl, li, 0)) for li, layer in enumerate(wl.layers)]
+    layers, prep_ms, prep_bytes = prep_weights(ctx, wl, specs)
     set_bytes = sum(L["P"][0].numel() for L in layers)
-    ncopies = max(1, math.ceil(MALL_DEFEAT_BYTES / set_bytes))
-    for L in layers:
-        L["P"] += [L["P"][0].clone() for _ in range(ncopies - 1)]
-    torch.cuda.synchronize()
-    print(f"[bench] packed set {set_bytes/1e6:.1f} MB x {ncopies} copies", file=sys.stderr, flush=True)
 
-    # ---- activations, outputs, workspaces --------------------------------------
-    # A job is one bitlinear_forward: input pointer/dtype/row stride, output.
+    # ---- activations and the calls of a step -------------------------------------
     act = synth.activations_student_t_bf16 if wl.act_dist == "student_t" else synth.activations_bf16
     keep = []
 
-    def make_job(M, L, x_ptr, x_dtype, ldx):
-        layer = L["layer"]
-        nws = bl.bitlinear_forward_workspace_bytes(M, layer.N, layer.K, layout, x_dtype)
-        return {"M": M, "L": L, "x_ptr": x_ptr, "x_dtype": x_dtype, "ldx": ldx,
-                "ws": torch.empty(max(nws, 16), dtype=torch.uint8, device=dev), "nws": nws,
-                "y": torch.empty((M, layer.N), dtype=torch.float32, device=dev)}
-
     def bf16_input(M, K, seed):
-        xd = torch.from_numpy(act(M, K, seed=seed).view(np.int16)).to(dev).view(torch.bfloat16)
+        xd = torch.from_numpy(act(M, K, seed=seed).view(np.int16)).to(ctx.dev).view(torch.bfloat16)
         keep.append(xd)
         return xd
 
+    # A job is one BitLinear forward; a call is what the step issues (one
+    # bitlinear_forward, or one grouped call over the layers of one batch).
     jobs = []
     if chain is not None:
-        # One token step through the stack: link i reads the first K columns
-        # of link i-1's fp32 output and quantises them inside its forward.
         M = batches[0]
         x0 = bf16_input(M, chain[0].layer.K, workloads.seed_for(wl, 0, 1))
         for link, L in zip(chain, layers):
+            y = torch.empty((M, L["layer"].N), dtype=torch.float32, device=ctx.dev)
             if link.index == 0:
-                jobs.append(make_job(M, L, x0.data_ptr(), bl.BF16, x0.stride(0)))
+                jobs.append({"M": M, "L": L, "x": x0, "y": y})
             else:
                 prev = jobs[-1]["y"]
-                jobs.append(make_job(M, L, prev.data_ptr(), bl.F32, prev.stride(0)))
+                jobs.append({"M": M, "L": L, "x": prev[:, :L["layer"].K], "y": y})
     else:
         for M in batches:
             for li, L in enumerate(layers):
-                xd = bf16_input(M, L["layer"].K, workloads.seed_for(wl, li, 1) + M)
-                jobs.append(make_job(M, L, xd.data_ptr(), bl.BF16, xd.stride(0)))
-    torch.cuda.synchronize()
+                jobs.append({"M": M, "L": L, "x": bf16_input(M, L["layer"].K, workloads.seed_for(wl, li, 1) + M),
+                             "y": torch.empty((M, L["layer"].N), dtype=torch.float32, device=ctx.dev)})
+    for j in jobs:
+        lay = j["L"]["layer"]
+        j["x_dtype"] = bl.F32 if j["x"].dtype == torch.float32 else bl.BF16
+        nws = bl.bitlinear_forward_workspace_bytes(j["M"], lay.N, lay.K, layout, j["x_dtype"])
+        j["nws"] = nws
+        j["ws"] = torch.empty(max(nws, 16), dtype=torch.uint8, device=ctx.dev)
+    if mode == "grouped":
+        calls = [[j for j in jobs if j["M"] == M] for M in batches]
+    else:
+        calls = [[j] for j in jobs]
 
-    if args.backward:
-        run_backward(args, wl, jobs, layout, ncopies, stream, dev)
-        return
+    # Weight copies.  Independent layers: call c of step s reads copy
+    # (s * ncalls + c) % ncopies, so consecutive reads of one copy are
+    # ncopies calls, >= ROTATE_BYTES of weights, apart.  The stack: step s
+    # reads copy s % ncopies of all 104 tensors.
+    per_step = sum(j["L"]["P"][0].numel() for j in jobs)
+    bytes_per_call = per_step / len(calls)
+    if chain is None:
+        ncopies = max(len(calls), math.ceil(ROTATE_BYTES / max(bytes_per_call, 1)))
+    else:
+        ncopies = max(2, math.ceil(ROTATE_BYTES / set_bytes))
 
-    def launch_job(j, copy):
-        """The user path: one fused bitlinear_forward (quantiser + product + rescale)."""
-        L = j["L"]
-        layer = L["layer"]
-        st = bl.bitlinear_forward(L["P"][copy].data_ptr(), layout, L["gamma"].data_ptr(), j["M"], layer.N, layer.K,
-                                  j["x_ptr"], j["x_dtype"], j["ldx"], None, j["y"].data_ptr(), bl.F32,
-                                  j["y"].stride(0), j["ws"].data_ptr(), j["nws"], stream.cuda_stream)
+    def copy_of(s, ci):
+        return (s * len(calls) + ci) % ncopies if chain is None else s % ncopies
+
+    add_copies(ctx, layers, ncopies)
+    log(f"packed set {set_bytes / 1e6:.1f} MB x {ncopies} copies; {len(calls)} calls of {len(jobs)} forwards per step")
+
+    def grouped_arrays(call, copy):
+        specs_ = [(j["L"]["P"][copy], j["L"]["gamma"], j["x"], j["L"]["layer"].N, j["L"]["layer"].K) for j in call]
+        arr, _ = bl.grouped_jobs(specs_, outs=[j["y"] for j in call])
+        return arr
+
+    for ci, call in enumerate(calls):
+        if mode == "grouped":
+            arr = grouped_arrays(call, 0)
+            nws = bl.bitlinear_forward_grouped_workspace_bytes(arr, len(call), layout, call[0]["x_dtype"])
+            call_ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=ctx.dev)
+            for j in call:
+                j["call"] = {"ws": call_ws, "nws": nws, "index": ci}
+
+    def launch_call(ci, copy):
+        call = calls[ci]
+        s_ = ctx.stream.cuda_stream
+        if mode == "grouped":
+            arr = grouped_arrays(call, copy)
+            c = call[0]["call"]
+            st = bl.bitlinear_forward_grouped(arr, len(call), layout, call[0]["x_dtype"], bl.F32,
+                                              c["ws"].data_ptr(), c["nws"], s_)
+            if st:
+                raise bl.BitlinearError(st, "bitlinear_forward_grouped")
+            return
+        j = call[0]
+        L, lay = j["L"], j["L"]["layer"]
+        st = bl.bitlinear_forward(L["P"][copy].data_ptr(), layout, L["gamma"].data_ptr(), j["M"], lay.N, lay.K,
+                                  j["x"].data_ptr(), j["x_dtype"], j["x"].stride(0), None, j["y"].data_ptr(), bl.F32,
+                                  j["y"].stride(0), j["ws"].data_ptr() if j["nws"] > 0 else None, j["nws"], s_)
         if st:
             raise bl.BitlinearError(st, "bitlinear_forward")
 
-    def step(copy):
-        for j in jobs:
-            launch_job(j, copy)
+    def step(s):
+        for ci in range(len(calls)):
+            launch_call(ci, copy_of(s, ci))
 
-    # ---- capture one graph per weight copy -----------------------------------
-    graphs = []
-    with torch.cuda.stream(stream):
-        step(0)  # eager warm-up before capture
+    if args.backward:
+        run_backward(args, wl, jobs, layout, ncopies, ctx.stream, ctx.dev)
+        return
+
+    # ---- timed steps -------------------------------------------------------------
+    nsteps_distinct = ncopies // math.gcd(ncopies, len(calls)) if chain is None else ncopies
+    with torch.cuda.stream(ctx.stream):
+        step(0)
         torch.cuda.synchronize()
-        for c in range(ncopies):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                step(c)
-            graphs.append(g)
+    graphs = [capture(ctx, lambda s=s: step(s)) for s in range(nsteps_distinct)]
     torch.cuda.synchronize()
-    print(f"[bench] captured {len(graphs)} graphs of {len(jobs)} forwards", file=sys.stderr, flush=True)
-
-    with torch.cuda.stream(stream):
-        for k in range(args.warmup):
-            graphs[k % ncopies].replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for k in range(args.steps):
-            graphs[(args.warmup + k) % ncopies].replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    step_ms = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] timed {args.steps} steps: {step_ms:.4f} ms/step (wall {wall*1e3/args.steps:.4f})",
-          file=sys.stderr, flush=True)
-
-    packed_per_step = sum(j["L"]["P"][0].numel() for j in jobs)
+    log(f"captured {len(graphs)} step graphs")
+    step_ms = time_graphs(ctx, graphs, args.steps, args.warmup)
+    log(f"timed {args.steps} steps: {step_ms:.4f} ms/step")
     ops_per_step = sum(2 * j["M"] * j["L"]["layer"].N * j["L"]["layer"].K for j in jobs)
-    value = packed_per_step / (step_ms * 1e-3) / 1e9
+    value = per_step / (step_ms * 1e-3) / 1e9
     tops = ops_per_step / (step_ms * 1e-3) / 1e12
 
-    # ---- roofline: the product kernel of every job, timed on its own ---------
-    # bitlinear_forward runs the activation quantiser, then the product kernel
-    # (bitlinear_product_kernel names it), or, for 1-4 tokens, one GEMV with
-    # the quantiser inside.  For the first kind each job's activations are
-    # quantised once through the split entry point and the product kernel is
-    # timed alone; the one-launch forwards are timed as called.  A HIP graph
-    # of R back-to-back launches (rotating over the weight copies) is replayed
-    # between two HIP events on the launch stream; a launch's duration is the
-    # replay time / R.  Durations are summed per kernel name; the kernel with
-    # the most time per step is the dominant one.
-    R = 16
-    for j in jobs:
-        layer = j["L"]["layer"]
-        M = j["M"]
-        algo = bl.bitlinear_auto_algo(M, layer.N, layer.K, layout, j["x_dtype"])
-        j["kernel"] = bl.bitlinear_product_kernel(M, layer.N, layer.K, layout, j["x_dtype"], bl.ALGO_AUTO)
-        j["fused"] = j["kernel"].startswith(("bl::k_gemv_fq<", "bl::k_gemv_persist_fq<"))
-        if j["fused"]:
-            with torch.cuda.stream(stream):
-                launch_job(j, 0)
-                torch.cuda.synchronize()
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    for r in range(R):
-                        launch_job(j, r % ncopies)
-            j["graph"] = g
-            continue
-        tiled = algo == bl.ALGO_GEMV_MFMA and M > 4 and layer.K <= 65536
-        j["beta"] = torch.empty(M, dtype=torch.float32, device=dev)
-        s_ = stream.cuda_stream
-        with torch.cuda.stream(stream):
-            if tiled:
-                nb = bl.bitlinear_act_tiled_bytes(M, layer.K, layout)
-                j["xq"], j["ldq"], xdt = torch.empty(nb, dtype=torch.int8, device=dev), 0, bl.I8_TILED
-                st = bl.bitlinear_quantize_act_tiled(j["x_ptr"], j["x_dtype"], M, layer.K, j["ldx"], layout,
-                                                     j["xq"].data_ptr(), nb, j["beta"].data_ptr(), s_)
-            else:
-                j["ldq"] = (layer.K + 63) // 64 * 64
-                j["xq"], xdt = torch.empty((M, j["ldq"]), dtype=torch.int8, device=dev), bl.I8
-                st = bl.bitlinear_quantize_act(j["x_ptr"], j["x_dtype"], M, layer.K, j["ldx"], j["xq"].data_ptr(),
-                                               j["ldq"], j["beta"].data_ptr(), s_)
-            if st:
-                raise bl.BitlinearError(st, "quantize (instrumented)")
-            assert bl.bitlinear_product_kernel(M, layer.N, layer.K, layout, xdt, algo) == j["kernel"]
-
-            # int8 input needs no staging; base-3 weights for the GEMM need room
-            # for their i2 rewrite (that pass is then part of the timed launch)
-            nws8 = bl.bitlinear_forward_workspace_bytes(M, layer.N, layer.K, layout, xdt)
-            j["ws8"] = torch.empty(max(nws8, 16), dtype=torch.uint8, device=dev)
-
-            def product(copy, j=j, xdt=xdt, algo=algo, nws8=nws8):
-                L, lay = j["L"], j["L"]["layer"]
-                st = bl.bitlinear_forward_algo(L["P"][copy].data_ptr(), layout, L["gamma"].data_ptr(), j["M"],
-                                               lay.N, lay.K, j["xq"].data_ptr(), xdt, j["ldq"],
-                                               j["beta"].data_ptr(), j["y"].data_ptr(), bl.F32, j["y"].stride(0),
-                                               j["ws8"].data_ptr() if nws8 > 0 else None, nws8, algo,
-                                               stream.cuda_stream)
-                if st:
-                    raise bl.BitlinearError(st, "forward (instrumented)")
-
-            product(0)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for r in range(R):
-                    product(r % ncopies)
-            j["graph"] = g
-    torch.cuda.synchronize()
-
-    def product_bytes(j):
-        # packed weights, the activations as the kernel reads them (int8 and
-        # beta, or the fp32 / bf16 rows of a one-launch forward), gamma, Y
-        layer = j["L"]["layer"]
-        x = j["M"] * layer.K * (4 if j["x_dtype"] == bl.F32 else 2) if j["fused"] else j["M"] * layer.K + 4 * j["M"]
-        return j["L"]["P"][0].numel() + x + 4 + 4 * j["M"] * layer.N
-
+    # ---- roofline: every call's kernels timed alone ------------------------------
+    # A call of one launch (a grouped call that quantises inside, or a
+    # one-launch forward) is timed as called.  A call that runs the quantiser
+    # first is timed whole and, for the product kernel alone, with its
+    # activations quantised once beforehand (bitlinear_product_kernel /
+    # bitlinear_grouped_kernel name the kernel).  Graphs of back-to-back calls
+    # rotate over every weight copy.
     per_kernel = {}
-    reps = 5
-    with torch.cuda.stream(stream):
-        for j in jobs:
-            ts = []
-            for _ in range(reps):
-                ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                ea.record(stream)
-                j["graph"].replay()
-                eb.record(stream)
-                ts.append((ea, eb))
-            torch.cuda.synchronize()
-            j["launch_ms"] = sum(a.elapsed_time(b) for a, b in ts) / (reps * R)
-            d = per_kernel.setdefault(j["kernel"], {"ms": 0.0, "bytes": 0, "ops": 0, "launches": 0, "jobs": []})
-            layer = j["L"]["layer"]
-            d["ms"] += j["launch_ms"]
-            d["bytes"] += product_bytes(j)
-            d["ops"] += 2 * j["M"] * layer.N * layer.K
+    call_us = []
+    for ci, call in enumerate(calls):
+        kname, one_launch = call_kernel(ctx, call, mode, layout)
+        ms_call = time_launches(ctx, lambda i, ci=ci: launch_call(ci, i % ncopies), ncopies)
+        call_us.append(round(ms_call * 1e3, 3))
+        if one_launch:
+            ms = ms_call
+        elif mode == "single":
+            ms = time_product_only(ctx, call[0], layout, ncopies)
+        else:
+            ms = None  # the grouped product behind a quantiser launch: counted in the call time only
+        if ms is None:
+            continue
+        d = per_kernel.setdefault(kname, {"ms": 0.0, "bytes": 0, "ops": 0, "launches": 0, "calls": []})
+        d["ms"] += ms
+        d["bytes"] += sum(product_bytes(bl, j, layout, one_launch) for j in call)
+        d["ops"] += sum(2 * j["M"] * j["L"]["layer"].N * j["L"]["layer"].K for j in call)
+        d["launches"] += 1
+        d["calls"].append(f"{'+'.join(j['L']['layer'].name for j in call)}@M{call[0]['M']}:{ms * 1e3:.2f}us")
+    if not per_kernel:  # every call quantises in a launch of its own: the calls themselves
+        for ci, call in enumerate(calls):
+            d = per_kernel.setdefault("grouped call (quantiser + product)",
+                                      {"ms": 0.0, "bytes": 0, "ops": 0, "launches": 0, "calls": []})
+            d["ms"] += call_us[ci] * 1e-3
+            d["bytes"] += sum(product_bytes(bl, j, layout, True) for j in call)
+            d["ops"] += sum(2 * j["M"] * j["L"]["layer"].N * j["L"]["layer"].K for j in call)
             d["launches"] += 1
-            d["jobs"].append(f"{layer.name}@M{j['M']}")
-            d.setdefault("job_us", []).append(f"{layer.name}@M{j['M']}:{j['launch_ms'] * 1e3:.1f}")
+            d["calls"].append(f"M{call[0]['M']}:{call_us[ci]:.2f}us")
     dom_name, dom = max(per_kernel.items(), key=lambda kv: kv[1]["ms"])
     avg_us = dom["ms"] / dom["launches"] * 1e3
     bound = "mfma" if "gemm" in dom_name else "hbm"
-    if bound == "hbm":
-        achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    else:
-        achieved = dom["ops"] / (dom["ms"] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
-                "frac": round(achieved / INT8_PEAK_TOPS, 4)}
-    roof.update({"traffic": measured_traffic(wl.name, dom_name), "kernel": dom_name, "avg_launch_us": round(avg_us, 3),
-                 "jobs": dom["jobs"],
+    roof = roofline(bound, dom)
+    roof.update({"traffic": measured_traffic(wl.name, dom_name), "kernel": dom_name,
+                 "avg_launch_us": round(avg_us, 3), "launches_per_step": dom["launches"], "calls": dom["calls"],
                  "algorithmic_bytes_per_launch": dom["bytes"] // dom["launches"],
-                 "algorithmic_ops_per_launch": dom["ops"] // dom["launches"]})
+                 "algorithmic_ops_per_launch": dom["ops"] // dom["launches"],
+                 "timing": "HIP events on the launch stream around a graph of back-to-back calls over every weight "
+                           "copy"})
     kernels = {k: {"avg_us": round(v["ms"] / v["launches"] * 1e3, 3),
                    "GB/s": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1),
-                   "TOPS": round(v["ops"] / (v["ms"] * 1e-3) / 1e12, 2), "jobs": len(v["jobs"]),
-                   "us_per_job": v["job_us"]}
+                   "TOPS": round(v["ops"] / (v["ms"] * 1e-3) / 1e12, 2), "calls": v["calls"]}
                for k, v in per_kernel.items()}
-    print(f"[bench] per-kernel: {json.dumps(kernels)}", file=sys.stderr, flush=True)
+    log(f"per-kernel: {json.dumps(kernels)}")
 
-    # ---- CPU oracle baseline --------------------------------------------------
+    prefill = None
+    if wl is workloads.DECODE_3B and not args.no_prefill and args.layout == "i2":
+        prefill = run_prefill(ctx, args)
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, batches, args.cpu_seconds)
+        cpu = cpu_baseline(wl, batches, args.cpu_seconds, layout)
 
     out = {
         "metric": METRIC,
@@ -357,7 +401,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": wl.name,
-            "layers": {L["layer"].name: [L["layer"].N, L["layer"].K] for L in layers},
+            "layers": {L["layer"].name: [L["layer"].N, L["layer"].K] for L in layers[:7]},
             "batches": list(batches),
             "layout": args.layout,
             "weights": "binary {-1, +1}" if layout == bl.LAYOUT_B1 else "ternary {-1, 0, +1}",
@@ -367,19 +411,171 @@ def main():
                         "down -> next layer's qkv; per-token int8 requantisation inside every forward"}
                if chain is not None else {}),
             "bitlinears_per_step": len(jobs),
+            "calls_per_step": len(calls),
+            "mode": mode,
             "y_dtype": "f32",
             "weight_copies": ncopies,
+            "rotation_bytes": int(ncopies * (bytes_per_call if chain is None else set_bytes)),
             "graph_replay": True,
         },
         "effective_tops": round(tops, 2),
         "us_per_bitlinear": round(step_ms * 1e3 / len(jobs), 3),
+        "us_per_call": call_us,
         "kernels": kernels,
         "weight_prep": {"GB/s_latent_fp32": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1),
                         "ms": round(prep_ms, 3)},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if prefill is not None:
+        out["prefill"] = prefill
     print(json.dumps(out), flush=True)
+
+
+def roofline(bound, d):
+    if bound == "hbm":
+        achieved = d["bytes"] / (d["ms"] * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    achieved = d["ops"] / (d["ms"] * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / INT8_PEAK_TOPS, 4)}
+
+
+def call_kernel(ctx, call, mode, layout):
+    """(name of the product kernel of a call, whether the call is that one
+    launch)."""
+    bl = ctx.bl
+    if mode == "grouped":
+        specs_ = [(j["L"]["P"][0], j["L"]["gamma"], j["x"], j["L"]["layer"].N, j["L"]["layer"].K) for j in call]
+        arr, _ = bl.grouped_jobs(specs_, outs=[j["y"] for j in call])
+        name = bl.bitlinear_grouped_kernel(arr, len(call), layout, call[0]["x_dtype"])
+        one = name is not None and name.endswith(f", {call[0]['x_dtype']}>")
+        return name, one
+    j = call[0]
+    lay = j["L"]["layer"]
+    name = bl.bitlinear_product_kernel(j["M"], lay.N, lay.K, layout, j["x_dtype"], bl.ALGO_AUTO)
+    return name, name.startswith(("bl::k_gemv_fq<", "bl::k_gemv_persist_fq<"))
+
+
+def product_bytes(bl, j, layout, one_launch):
+    """Algorithmic bytes of one job's product: packed weights, the activations
+    as the kernel reads them (the fp32 / bf16 rows when it quantises them
+    itself, else int8 and beta), gamma, and the fp32 output."""
+    lay = j["L"]["layer"]
+    es = 4 if j["x_dtype"] == bl.F32 else 2
+    x = j["M"] * lay.K * es if one_launch else j["M"] * lay.K + 4 * j["M"]
+    return bl.bitlinear_packed_bytes(lay.N, lay.K, layout) + x + 4 + 4 * j["M"] * lay.N
+
+
+def time_product_only(ctx, j, layout, ncopies):
+    """The product kernel of a single forward alone: its activations quantised
+    once beforehand (through the split entry points), then the forward on
+    int8 input, rotating over the weight copies."""
+    torch, bl = ctx.torch, ctx.bl
+    L, lay, M = j["L"], j["L"]["layer"], j["M"]
+    algo = bl.bitlinear_auto_algo(M, lay.N, lay.K, layout, j["x_dtype"])
+    tiled = algo == bl.ALGO_GEMV_MFMA and M > 4 and lay.K <= 65536
+    beta = torch.empty(M, dtype=torch.float32, device=ctx.dev)
+    s_ = ctx.stream.cuda_stream
+    with torch.cuda.stream(ctx.stream):
+        if tiled:
+            nb = bl.bitlinear_act_tiled_bytes(M, lay.K, layout)
+            xq, ldq, xdt = torch.empty(nb, dtype=torch.int8, device=ctx.dev), 0, bl.I8_TILED
+            st = bl.bitlinear_quantize_act_tiled(j["x"].data_ptr(), j["x_dtype"], M, lay.K, j["x"].stride(0), layout,
+                                                 xq.data_ptr(), nb, beta.data_ptr(), s_)
+        else:
+            ldq = (lay.K + 63) // 64 * 64
+            xq, xdt = torch.empty((M, ldq), dtype=torch.int8, device=ctx.dev), bl.I8
+            st = bl.bitlinear_quantize_act(j["x"].data_ptr(), j["x_dtype"], M, lay.K, j["x"].stride(0), xq.data_ptr(),
+                                           ldq, beta.data_ptr(), s_)
+        if st:
+            raise bl.BitlinearError(st, "quantize (instrumented)")
+    nws8 = bl.bitlinear_forward_workspace_bytes(M, lay.N, lay.K, layout, xdt)
+    ws8 = torch.empty(max(nws8, 16), dtype=torch.uint8, device=ctx.dev)
+
+    def product(i):
+        st = bl.bitlinear_forward_algo(L["P"][i % ncopies].data_ptr(), layout, L["gamma"].data_ptr(), M, lay.N,
+                                       lay.K, xq.data_ptr(), xdt, ldq, beta.data_ptr(), j["y"].data_ptr(), bl.F32,
+                                       j["y"].stride(0), ws8.data_ptr() if nws8 > 0 else None, nws8, algo, s_)
+        if st:
+            raise bl.BitlinearError(st, "forward (instrumented)")
+
+    return time_launches(ctx, product, ncopies)
+
+
+def run_prefill(ctx, args):
+    """The 3B prefill GEMM (M = 2048, Student-t activations, i2): a step of
+    its three forwards (quantiser + GEMM each), and the GEMM kernel alone on
+    pre-quantised int8 activations, rotating over weight copies of >= 2 GiB."""
+    torch, bl = ctx.torch, ctx.bl
+    from ternary_weight_linear_forward_amd import synth, workloads
+
+    wl = workloads.PREFILL_3B
+    M = wl.batches[0]
+    layers, _, _ = prep_weights(ctx, wl, [(layer, workloads.seed_for(wl, li, 0)) for li, layer in enumerate(wl.layers)])
+    set_bytes = sum(L["P"][0].numel() for L in layers)
+    ncopies = max(2, math.ceil(ROTATE_BYTES / set_bytes))
+    add_copies(ctx, layers, ncopies)
+    jobs = []
+    for li, L in enumerate(layers):
+        lay = L["layer"]
+        x = synth.activations_student_t_bf16(M, lay.K, seed=workloads.seed_for(wl, li, 1) + M)
+        xd = torch.from_numpy(x.view(np.int16)).to(ctx.dev).view(torch.bfloat16)
+        nws = bl.bitlinear_forward_workspace_bytes(M, lay.N, lay.K, ctx.layout, bl.BF16)
+        jobs.append({"M": M, "L": L, "x": xd, "x_dtype": bl.BF16, "nws": nws,
+                     "ws": torch.empty(max(nws, 16), dtype=torch.uint8, device=ctx.dev),
+                     "y": torch.empty((M, lay.N), dtype=torch.float32, device=ctx.dev)})
+
+    def fwd(j, copy):
+        L, lay = j["L"], j["L"]["layer"]
+        st = bl.bitlinear_forward(L["P"][copy].data_ptr(), ctx.layout, L["gamma"].data_ptr(), M, lay.N, lay.K,
+                                  j["x"].data_ptr(), bl.BF16, j["x"].stride(0), None, j["y"].data_ptr(), bl.F32,
+                                  j["y"].stride(0), j["ws"].data_ptr(), j["nws"], ctx.stream.cuda_stream)
+        if st:
+            raise bl.BitlinearError(st, "bitlinear_forward (prefill)")
+
+    def step(s):
+        for j in jobs:
+            fwd(j, s % ncopies)
+
+    with torch.cuda.stream(ctx.stream):
+        step(0)
+        torch.cuda.synchronize()
+    graphs = [capture(ctx, lambda s=s: step(s)) for s in range(ncopies)]
+    step_ms = time_graphs(ctx, graphs, max(5, args.steps // 5), 2)
+    ops = sum(2 * M * j["L"]["layer"].N * j["L"]["layer"].K for j in jobs)
+    packed = sum(j["L"]["P"][0].numel() for j in jobs)
+    d = {"ms": 0.0, "bytes": 0, "ops": 0, "launches": 0, "calls": []}
+    kname = None
+    for j in jobs:
+        lay = j["L"]["layer"]
+        kname = bl.bitlinear_product_kernel(M, lay.N, lay.K, ctx.layout, bl.I8, bl.ALGO_AUTO)
+        ms = time_product_only(ctx, j, ctx.layout, ncopies)
+        d["ms"] += ms
+        d["ops"] += 2 * M * lay.N * lay.K
+        d["bytes"] += product_bytes(bl, j, ctx.layout, False)
+        d["launches"] += 1
+        d["calls"].append(f"{lay.name}@M{M}:{ms * 1e3:.2f}us")
+    roof = roofline("mfma", d)
+    roof.update({"traffic": None, "kernel": kname, "avg_launch_us": round(d["ms"] / d["launches"] * 1e3, 3),
+                 "launches_per_step": d["launches"], "calls": d["calls"],
+                 "algorithmic_ops_per_launch": d["ops"] // d["launches"],
+                 "timing": "HIP events on the launch stream around a graph of back-to-back GEMMs over every weight "
+                           "copy (activations quantised beforehand)"})
+    log(f"prefill: {step_ms:.4f} ms/step, GEMM {json.dumps(roof)}")
+    return {
+        "workload": wl.name,
+        "metric": "effective ternary TOPS of the prefill step (quantiser + GEMM + rescale per layer)",
+        "value": round(ops / (step_ms * 1e-3) / 1e12, 2),
+        "unit": "TOPS",
+        "ms_per_step": round(step_ms, 5),
+        "packed_weight_GB/s": round(packed / (step_ms * 1e-3) / 1e9, 2),
+        "config": {"M": M, "layers": {j["L"]["layer"].name: [j["L"]["layer"].N, j["L"]["layer"].K] for j in jobs},
+                   "activations": "Student-t(4) bf16", "layout": "i2", "weight_copies": ncopies},
+        "roofline": roof,
+        "cpu_baseline": cpu_baseline(wl, wl.batches, max(args.cpu_seconds / 2, 3.0), ctx.layout, rows=64),
+    }
 
 
 FP32_MFMA_PEAK_TFLOPS = 157.3
@@ -496,7 +692,7 @@ def measured_traffic(workload, kernel):
     import hashlib
 
     h = hashlib.sha256()
-    for f in ("gemv.hip", "gemm.hip", "common.h"):
+    for f in ("group.hip", "gemv_core.h", "fq_core.h", "gemv.hip", "gemm.hip", "common.h"):
         with open(os.path.join(ROOT, "ternary_weight_linear_forward_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     for path in glob.glob(os.path.join(ROOT, "profiles", "traffic_*.txt")):
@@ -511,11 +707,24 @@ def measured_traffic(workload, kernel):
     return None
 
 
-def cpu_baseline(wl, batches, seconds):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, batches, seconds, layout, rows=None):
     """The CPU oracle, untuned, on a bounded sample of the same work: whole
-    layers of the workload (quantise the activations, exact product, rescale),
-    cycling through the step's (batch, layer) pairs until about 'seconds' of
-    CPU time has passed.  Reported in the same unit (packed-weight GB/s)."""
+    layers of the workload (quantise the activations, exact product, rescale)
+    -- or, with 'rows', the first 'rows' tokens of each -- cycling through the
+    step's (batch, layer) pairs until about 'seconds' of CPU time has passed.
+    Reported in the unit of the GPU figure it stands beside (packed-weight
+    GB/s for decode, effective TOPS with rows)."""
     import oracle
 
     from ternary_weight_linear_forward_amd import synth, workloads
@@ -525,6 +734,7 @@ def cpu_baseline(wl, batches, seconds):
     pairs = [(M, li) for M in batches for li in range(len(wl.layers))]
     tern = {}
     done_bytes = 0
+    done_ops = 0
     done = []
     t_total = 0.0
     i = 0
@@ -535,17 +745,22 @@ def cpu_baseline(wl, batches, seconds):
             w = synth.latent_weights(layer.N, layer.K, seed=workloads.seed_for(wl, li, 0))
             tern[li] = oracle.quantize_weights(w)
         t, g = tern[li]
-        x = act(M, layer.K, seed=workloads.seed_for(wl, li, 1) + M)
+        m = M if rows is None else min(M, rows)
+        x = act(M, layer.K, seed=workloads.seed_for(wl, li, 1) + M)[:m]
         t0 = time.perf_counter()
         oracle.forward(t, g, x)
         t_total += time.perf_counter() - t0
-        done_bytes += bl.bitlinear_packed_bytes(layer.N, layer.K, bl.LAYOUT_I2)
-        done.append(f"{layer.name}@M{M}")
+        done_bytes += bl.bitlinear_packed_bytes(layer.N, layer.K, layout)
+        done_ops += 2 * m * layer.N * layer.K
+        done.append(f"{layer.name}@M{m}")
         i += 1
-    return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": oracle.threads_used(),
-            "kind": "oracle",
-            "sample": f"{len(done)} BitLinear forwards ({', '.join(done[:8])}{', ...' if len(done) > 8 else ''}) "
-                      f"in {t_total:.1f} s"}
+    sample = (f"{len(done)} BitLinear forwards ({', '.join(done[:8])}{', ...' if len(done) > 8 else ''}) "
+              f"in {t_total:.1f} s")
+    base = {"cores": oracle.threads_used(), "cpu_model": cpu_model(), "kind": "oracle", "sample": sample}
+    if rows is None:
+        return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", **base}
+    return {"value": round(done_ops / t_total / 1e12, 5), "unit": "TOPS", **base,
+            "note": f"first {rows} tokens of each forward"}
 
 
 if __name__ == "__main__":

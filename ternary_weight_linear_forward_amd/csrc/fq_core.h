@@ -95,9 +95,16 @@ __device__ __forceinline__ void fq_load(const FU &U, const void *X, int xbytes, 
 // holds a barrier).  qbuf: this wave's LDS area, SPW x UNITS units; wmax:
 // [waves][4].  Fills a[j][d] for the wave's k-steps j < nj and returns, in lane
 // t, beta of token t % 4 (a lane shuffle of the result gives any token's).
-template <class FU, int SPW>
+// after_barrier() runs in every wave right after the barrier (the grouped GEMV
+// issues its weight loads there, once every wave of the workgroup holds its
+// activations).
+struct FqNoHook {
+    __device__ void operator()() const {}
+};
+
+template <class FU, int SPW, class Hook = FqNoHook>
 __device__ __forceinline__ float fq_quantise(const FU &U, uint4 (&xv)[FU::NUW][FU::VL], v4i *qbuf, float (*wmax)[4],
-                                             v4i (&a)[SPW][FU::NMF])
+                                             v4i (&a)[SPW][FU::NMF], const Hook &after_barrier = Hook())
 {
     constexpr int XF32 = FU::ES == 4;
     const int lane = U.lane, wave = U.wave;
@@ -147,6 +154,7 @@ __device__ __forceinline__ float fq_quantise(const FU &U, uint4 (&xv)[FU::NUW][F
         if (lane == t) wmax[wave][t] = b;
     }
     __syncthreads();
+    after_barrier();
     float beta_lane;
     {
         const int t = lane & 3;

@@ -49,6 +49,16 @@ __device__ __forceinline__ void unroll_while(F &&f)
     }
 }
 
+// Settle loaded registers: the compiler waits for their loads here (and only
+// here), and later code sees the values of this empty statement, with no
+// load pending behind them.  Without it, code that uses them after the
+// weight ring has been issued may be given waits that also count ring loads.
+__device__ __forceinline__ void settle(uint4 &x)
+{
+    asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+}
+__device__ __forceinline__ void settle(v4i &x) { asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3])); }
+
 __device__ __forceinline__ void lds_barrier()
 {
     asm volatile("" ::: "memory");
@@ -184,17 +194,27 @@ __device__ __forceinline__ float group_job_tiles(const GroupJob &J, int KS, int 
                 a[j][d] = (s < nsteps && i < M) ? v : v4i{0, 0, 0, 0};
             }
         }
+        // Every wave of the workgroup holds its activations before any wave
+        // asks for weights: the loads of one CU are served in order, and
+        // activations asked for after another wave's weight ring would wait
+        // behind it.  The barrier also orders the clearing of the sums
+        // before the first atomic.
 #pragma unroll
-        for (int d = 0; d < D; ++d) load_tile(d, b[d]);
-        // with the first loads in flight: clear the tile sums (every wave of
-        // the workgroup takes this barrier once before its first atomic)
+        for (int j = 0; j < SPW; ++j)
+#pragma unroll
+            for (int d = 0; d < NMF; ++d) settle(a[j][d]);
         zero_sums();
         lds_barrier();
+#pragma unroll
+        for (int d = 0; d < D; ++d) load_tile(d, b[d]);
     } else {
-        // the wave's own activations first, then the weight ring, then the
-        // rounding while the weights are in flight (waits count loads in
-        // issue order); the quantiser's barrier also orders the clearing of
-        // the sums before the first atomic
+        // The wave's own activations, held by every wave of the workgroup
+        // before any wave asks for weights (the loads of one CU are served in
+        // order, so activations asked for after another wave's weight ring
+        // would wait behind it): the weight ring is issued right after the
+        // quantiser's barrier, and the rounding runs while it is in flight.
+        // The barrier also orders the clearing of the sums before the first
+        // atomic.
         using FU = FqUnits<LAYOUT, XDT, SPW>;
         const FU U{lane, wave, KS, M, nj * M * FU::CH, J.K, static_cast<int>(J.ldx)};
         constexpr int ES = XDT == DT_F32 ? 4 : 2;
@@ -202,10 +222,14 @@ __device__ __forceinline__ float group_job_tiles(const GroupJob &J, int KS, int 
         uint4 xv[FU::NUW][FU::VL];
         fq_load(U, J.X, xbytes, xv);
 #pragma unroll
-        for (int d = 0; d < D; ++d) load_tile(d, b[d]);
+        for (int n = 0; n < FU::NUW; ++n)
+#pragma unroll
+            for (int v = 0; v < FU::VL; ++v) settle(xv[n][v]);
         zero_sums();
-        __builtin_amdgcn_sched_barrier(0);
-        beta_lane = fq_quantise<FU, SPW>(U, xv, L.qbuf + wave * SPW * FU::UNITS, L.wmax, a);
+        beta_lane = fq_quantise<FU, SPW>(U, xv, L.qbuf + wave * SPW * FU::UNITS, L.wmax, a, [&]() {
+#pragma unroll
+            for (int d = 0; d < D; ++d) load_tile(d, b[d]);
+        });
     }
     // i2: the operands transposed for the masked codes (i2_scaled_step)
     if constexpr (LAYOUT == LAYOUT_I2) {
