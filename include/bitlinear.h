@@ -59,7 +59,8 @@ typedef enum {
     BITLINEAR_ERR_UNSUPPORTED = 2, /* valid request this library does not implement     */
     BITLINEAR_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required        */
     BITLINEAR_ERR_LAUNCH = 4,      /* a kernel launch failed                            */
-    BITLINEAR_ERR_DEVICE = 5       /* no usable gfx950 device on the current HIP device  */
+    BITLINEAR_ERR_DEVICE = 5,      /* no usable gfx950 device on the current HIP device  */
+    BITLINEAR_ERR_SCRATCH = 6      /* bitlinear_forward_noalloc: needs more than its scratch */
 } bitlinear_status_t;
 
 typedef enum {
@@ -283,6 +284,29 @@ int bitlinear_forward_ex(const uint8_t *P, int layout, const float *gamma, int64
                          const void *X, int x_dtype, int64_t ldx, const float *beta_in, void *Y, int y_dtype,
                          int64_t ldy, int8_t *Xq_out, int64_t ldxq, float *beta_out, void *ws, int64_t ws_bytes,
                          int algo, void *stream);
+
+/*
+ * bitlinear_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops,
+ * harnesses that forbid allocation).  Arguments and results are those of
+ * bitlinear_forward (algo AUTO); the workspace that call would take
+ * (bitlinear_forward_workspace_bytes(M, N, K, layout, x_dtype) bytes: the
+ * staged int8 activations, and for b3 / b1 weights in the GEMM their i2
+ * rewrite) is a static device array of BITLINEAR_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends.  The
+ * call allocates nothing and frees nothing; it looks the array's address up
+ * once per device, on its first call there (make that first call outside
+ * graph capture).  Every call on one GPU uses the same array: calls that
+ * overlap in time on one GPU (different streams, or host threads, without
+ * ordering) race and give undefined results; calls ordered on one stream are
+ * safe.  No byte of the array needs to start at any value.
+ * Returns BITLINEAR_ERR_SCRATCH, before anything is enqueued, when the
+ * workspace would exceed the array.
+ */
+#define BITLINEAR_NOALLOC_SCRATCH_BYTES (64u << 20)
+int bitlinear_forward_noalloc(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                              const void *X, int x_dtype, int64_t ldx, const float *beta_in, void *Y, int y_dtype,
+                              int64_t ldy, void *stream);
 
 /*
  * Grouped forward: several BitLinears in one call, the way a decode step runs

@@ -45,7 +45,8 @@ if len(_hip_runtimes_loaded()) > 1:
                       f"({', '.join(_hip_runtimes_loaded())}); import torch before loading libbitlinear")
 
 # --- enums (bitlinear.h) ---------------------------------------------------
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_DEVICE = range(6)
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_DEVICE, ERR_SCRATCH = range(7)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 F32, BF16, I8, I32, I8_TILED = range(5)
 LAYOUT_I2, LAYOUT_B3, LAYOUT_B1 = 0, 1, 2
 ALGO_AUTO, ALGO_GEMV_ADDSUB, ALGO_GEMV_MFMA, ALGO_GEMM_MFMA = range(4)
@@ -87,6 +88,7 @@ _SIGNATURES = {
     "bitlinear_backward_dw": ([_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P], _INT),
     "bitlinear_forward_algo": (
         [_P, _INT, _P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P, _INT, _I64, _P, _I64, _INT, _P], _INT),
+    "bitlinear_forward_noalloc": ([_P, _INT, _P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P, _INT, _I64, _P], _INT),
     "bitlinear_forward_grouped_workspace_bytes": ([_JOBS, _INT, _INT, _INT], _I64),
     "bitlinear_forward_grouped": ([_JOBS, _INT, _INT, _INT, _INT, _P, _I64, _P], _INT),
     "bitlinear_grouped_kernel": ([_JOBS, _INT, _INT, _INT], ctypes.c_char_p),
@@ -208,6 +210,11 @@ def job_array(jobs) -> ctypes.Array:
     for i, j in enumerate(jobs):
         arr[i] = j if isinstance(j, Job) else Job(**j)
     return arr
+
+
+def bitlinear_forward_noalloc(P, layout, gamma, M, N, K, X, x_dtype, ldx, beta_in, Y, y_dtype, ldy, stream) -> int:
+    return _lib.bitlinear_forward_noalloc(P, layout, gamma, M, N, K, X, x_dtype, ldx, beta_in, Y, y_dtype, ldy,
+                                          stream)
 
 
 def bitlinear_forward_grouped_workspace_bytes(jobs, njobs: int, layout: int, x_dtype: int) -> int:

@@ -9,6 +9,14 @@
 
 #include "launch.h"
 
+#include <atomic>
+
+// Allocation-free forwards (bitlinear_forward_noalloc): the workspace is this
+// file-scope device array, one per GPU the library runs on, held until the
+// process ends.  In host code 'scratch' is only a stand-in for the symbol;
+// its device address comes from hipGetSymbolAddress (scratch_ptr below).
+static __device__ __align__(256) uint8_t scratch[BITLINEAR_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40; // keeps per-exponent sums of |W| below 2^64
@@ -131,6 +139,7 @@ const char *bitlinear_status_string(int status)
     case BITLINEAR_ERR_WORKSPACE: return "workspace missing or too small";
     case BITLINEAR_ERR_LAUNCH: return "kernel launch failed";
     case BITLINEAR_ERR_DEVICE: return "no usable gfx950 device";
+    case BITLINEAR_ERR_SCRATCH: return "request needs more than the allocation-free scratch (BITLINEAR_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }
@@ -296,7 +305,7 @@ int bitlinear_quantize_act_tiled(const void *X, int x_dtype, int64_t M, int64_t 
 static int forward_impl(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
                         const void *X, int x_dtype, int64_t ldx, const float *beta_in, void *Y, int y_dtype,
                         int64_t ldy, void *ws, int64_t ws_bytes, int8_t *Xq_out, int64_t ldxq, float *beta_out,
-                        int algo, void *stream)
+                        int algo, void *stream, bool check_only = false)
 {
     if (!P || !gamma || !X || !Y || !valid_layout(layout)) return BITLINEAR_ERR_INVALID_ARG;
     if (M < 1 || M > BITLINEAR_MAX_M || N < 1 || N > (int64_t(1) << 31) || K < 1 || K > BITLINEAR_MAX_K)
@@ -328,8 +337,9 @@ static int forward_impl(const uint8_t *P, int layout, const float *gamma, int64_
 
     // with the quantiser's outputs requested the product reads them (as I8 input)
     const int64_t need = bitlinear_forward_workspace_bytes(M, N, K, layout, q_out ? BITLINEAR_I8 : x_dtype);
-    if (need > 0 && (!ws || ws_bytes < need)) return BITLINEAR_ERR_WORKSPACE;
-    if (need > 0 && !aligned16(ws)) return BITLINEAR_ERR_INVALID_ARG;
+    // (check_only: every check but the workspace's, which the caller owns)
+    if (!check_only && need > 0 && (!ws || ws_bytes < need)) return BITLINEAR_ERR_WORKSPACE;
+    if (need > 0 && ws && !aligned16(ws)) return BITLINEAR_ERR_INVALID_ARG;
 
     const int64_t pb = bitlinear_packed_bytes(N, K, layout);
     const int64_t xt = bl::tiled_bytes(M, K, layout);
@@ -338,7 +348,7 @@ static int forward_impl(const uint8_t *P, int layout, const float *gamma, int64_
                sy = span_of(Y, M, ldy, N, dtype_size(y_dtype)), sg = span_of(gamma, 1, 1, 1, 4);
     if (overlap(sy, sp) || overlap(sy, sx) || overlap(sy, sg)) return BITLINEAR_ERR_INVALID_ARG;
     if (beta_in && overlap(sy, span_of(beta_in, 1, M, M, 4))) return BITLINEAR_ERR_INVALID_ARG;
-    if (need > 0) {
+    if (need > 0 && ws) {
         const Span sw = span_of(ws, 1, need, need, 1);
         if (overlap(sw, sp) || overlap(sw, sx) || overlap(sw, sy) || overlap(sw, sg))
             return BITLINEAR_ERR_INVALID_ARG;
@@ -349,7 +359,7 @@ static int forward_impl(const uint8_t *P, int layout, const float *gamma, int64_
         for (const Span &o : others)
             if (overlap(sq, o) || overlap(sb, o)) return BITLINEAR_ERR_INVALID_ARG;
         if (overlap(sq, sb)) return BITLINEAR_ERR_INVALID_ARG;
-        if (need > 0) {
+        if (need > 0 && ws) {
             const Span sw = span_of(ws, 1, need, need, 1);
             if (overlap(sw, sq) || overlap(sw, sb)) return BITLINEAR_ERR_INVALID_ARG;
         }
@@ -368,6 +378,7 @@ static int forward_impl(const uint8_t *P, int layout, const float *gamma, int64_
         return BITLINEAR_ERR_UNSUPPORTED;
     if (algo == BITLINEAR_ALGO_GEMM_MFMA && layout == BITLINEAR_LAYOUT_B1 && M <= 16) return BITLINEAR_ERR_UNSUPPORTED;
     if (x_dtype == BITLINEAR_I8_TILED && algo != BITLINEAR_ALGO_GEMV_MFMA) return BITLINEAR_ERR_UNSUPPORTED;
+    if (check_only) return BITLINEAR_OK;
 
     (void)hipGetLastError();
     hipStream_t st = as_stream(stream);
@@ -706,6 +717,47 @@ int bitlinear_forward_grouped(const bitlinear_job_t *jobs, int njobs, int layout
         if (s != BITLINEAR_OK) return s;
     }
     return BITLINEAR_OK;
+}
+
+// ---- allocation-free forward ------------------------------------------------
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+
+// The device address of 'scratch' on the current device, looked up once per
+// device (each GPU holds its own copy of the array at its own address).
+void *scratch_ptr()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch[dev].store(p, std::memory_order_release);
+    return p;
+}
+
+} // namespace
+
+int bitlinear_forward_noalloc(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                              const void *X, int x_dtype, int64_t ldx, const float *beta_in, void *Y, int y_dtype,
+                              int64_t ldy, void *stream)
+{
+    const int64_t need = bitlinear_forward_workspace_bytes(M, N, K, layout, x_dtype);
+    if (need < 0) return BITLINEAR_ERR_INVALID_ARG;
+    // every argument check first (on the host; nothing is enqueued)
+    const int st = forward_impl(P, layout, gamma, M, N, K, X, x_dtype, ldx, beta_in, Y, y_dtype, ldy, nullptr, 0,
+                                nullptr, 0, nullptr, BITLINEAR_ALGO_AUTO, stream, true);
+    if (st != BITLINEAR_OK) return st;
+    if (need > int64_t(BITLINEAR_NOALLOC_SCRATCH_BYTES)) return BITLINEAR_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (need > 0) {
+        ws = scratch_ptr();
+        if (!ws) return BITLINEAR_ERR_DEVICE;
+    }
+    return forward_impl(P, layout, gamma, M, N, K, X, x_dtype, ldx, beta_in, Y, y_dtype, ldy, ws, need, nullptr, 0,
+                        nullptr, BITLINEAR_ALGO_AUTO, stream);
 }
 
 // i2 rewrite of b3 / b1 weights, then the small-batch dX's partial tiles

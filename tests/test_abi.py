@@ -455,3 +455,14 @@ def test_grouped_rejects_bad_counts():
     assert gfw(arr, 0) == bl.ERR_INVALID_ARG
     assert gfw(arr, bl.MAX_GROUP + 1) == bl.ERR_INVALID_ARG
     assert gfw(None, 1) == bl.ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_before_any_device_call():
+    # a workspace beyond the allocation-free scratch is refused on the host
+    assert bl.bitlinear_forward_workspace_bytes(1024, 16, 131072, bl.LAYOUT_I2, bl.BF16) > bl.NOALLOC_SCRATCH_BYTES
+    st = bl.bitlinear_forward_noalloc(A, bl.LAYOUT_I2, B, 1024, 16, 131072, C, bl.BF16, 131072, None, E, bl.F32, 16,
+                                      None)
+    assert st == bl.ERR_SCRATCH
+    assert "scratch" in bl.bitlinear_status_string(bl.ERR_SCRATCH)
+    assert bl.bitlinear_forward_noalloc(None, bl.LAYOUT_I2, B, 4, 64, 64, C, bl.BF16, 64, None, D, bl.F32, 64,
+                                        None) == bl.ERR_INVALID_ARG
