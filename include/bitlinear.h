@@ -123,8 +123,8 @@ int64_t bitlinear_quantize_weights_workspace_bytes(int64_t N, int64_t K);
 /*
  * Workspace bytes bitlinear_forward needs for these sizes (-1 if invalid).
  * Covers the staged int8 activations and beta of the fused quantiser (x_dtype
- * F32 or BF16) and, for b1 weights with M > 16, their i2 rewrite that the
- * GEMM reads.
+ * F32 or BF16); 0 for pre-quantised input.  Weights are read in their own
+ * layout and never rewritten.
  */
 int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int layout, int x_dtype);
 
@@ -132,8 +132,8 @@ int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int l
  * The product algorithm bitlinear_forward (algo AUTO) runs for these sizes:
  * BITLINEAR_ALGO_GEMV_MFMA for pre-tiled input, for M <= 16, and for larger
  * M when the GEMM would launch too few workgroup tiles to fill the GPU;
- * BITLINEAR_ALGO_GEMM_MFMA otherwise (it decodes b3 weights itself; b1
- * weights are first rewritten as i2 in the workspace).  Returns -1 for invalid
+ * BITLINEAR_ALGO_GEMM_MFMA otherwise (it decodes b3 and b1 weights itself).
+ * Returns -1 for invalid
  * sizes, layout or dtype.  Host-only; enqueues nothing.
  */
 int bitlinear_auto_algo(int64_t M, int64_t N, int64_t K, int layout, int x_dtype);
@@ -187,6 +187,24 @@ int bitlinear_binarize_weights(const float *W, int64_t N, int64_t K, int64_t ldw
  */
 int bitlinear_pack(const int8_t *T, int64_t N, int64_t K, int64_t ldt, int layout, uint8_t *P,
                    void *stream);
+
+/*
+ * Load-time rewrite of packed weights as i2 (a format change of the same
+ * ternary values; the 2-bit form is the one the HackerPapers digest's thread
+ * "GPUs Go Brrr" stores).  No forward rewrites weights: the products read b3
+ * and b1 bytes themselves, and a caller that keeps a b3 / b1 layer mainly for
+ * many-token products, where the base-3 digit decode costs more than the i2
+ * unpack, can call this once when it loads the layer and pass the i2 copy
+ * (layout I2) to those forwards instead.
+ *   P     packed [N x K] in layout B3 or B1 (device, read-only, 16-byte aligned).
+ *   P2    bitlinear_packed_bytes(N, K, I2) bytes (device, written, 16-byte
+ *         aligned, not overlapping P): every byte, padding included, equals
+ *         what bitlinear_pack writes for the same T with layout I2.
+ * Returns INVALID_ARG for a null or misaligned pointer, layout I2 or an
+ * unknown layout, N < 1, K out of [1, BITLINEAR_MAX_K], N * K >= 2^40, or
+ * overlapping buffers; LAUNCH if the launch fails.  Enqueued on stream.
+ */
+int bitlinear_transcode_i2(const uint8_t *P, int layout, int64_t N, int64_t K, uint8_t *P2, void *stream);
 
 /*
  * Per-token absmax int8 activation quantisation (LIT-380 Key takeaways
@@ -291,8 +309,7 @@ int bitlinear_forward_ex(const uint8_t *P, int layout, const float *gamma, int64
  * harnesses that forbid allocation).  Arguments and results are those of
  * bitlinear_forward (algo AUTO); the workspace that call would take
  * (bitlinear_forward_workspace_bytes(M, N, K, layout, x_dtype) bytes: the
- * staged int8 activations, and for b3 / b1 weights in the GEMM their i2
- * rewrite) is a static device array of BITLINEAR_NOALLOC_SCRATCH_BYTES that
+ * staged int8 activations and beta) is a static device array of BITLINEAR_NOALLOC_SCRATCH_BYTES that
  * the library holds on every GPU it runs on until the process ends.  The
  * call allocates nothing and frees nothing; it looks the array's address up
  * once per device, on its first call there (make that first call outside

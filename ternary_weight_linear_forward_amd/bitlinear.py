@@ -80,6 +80,7 @@ _SIGNATURES = {
     "bitlinear_quantize_weights": ([_P, _I64, _I64, _I64, _P, _P, _P, _I64, _P], _INT),
     "bitlinear_binarize_weights": ([_P, _I64, _I64, _I64, _P, _P, _P, _I64, _P], _INT),
     "bitlinear_pack": ([_P, _I64, _I64, _I64, _INT, _P, _P], _INT),
+    "bitlinear_transcode_i2": ([_P, _INT, _I64, _I64, _P, _P], _INT),
     "bitlinear_quantize_act": ([_P, _INT, _I64, _I64, _I64, _P, _I64, _P, _P], _INT),
     "bitlinear_forward": ([_P, _INT, _P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P, _INT, _I64, _P, _I64, _P], _INT),
     "bitlinear_backward_dx_workspace_bytes": ([_I64, _I64, _I64, _INT], _I64),
@@ -180,6 +181,10 @@ def bitlinear_backward_dw(Xq, ldq, beta, M, N, K, dY, lddy, dW, lddw, stream) ->
 
 def bitlinear_pack(T, N, K, ldt, layout, P, stream) -> int:
     return _lib.bitlinear_pack(T, N, K, ldt, layout, P, stream)
+
+
+def bitlinear_transcode_i2(P, layout, N, K, P2, stream) -> int:
+    return _lib.bitlinear_transcode_i2(P, layout, N, K, P2, stream)
 
 
 def bitlinear_quantize_act(X, x_dtype, M, K, ldx, Xq, ldq, beta, stream) -> int:
@@ -285,6 +290,17 @@ def pack(T, layout: int = LAYOUT_I2, stream=None):
     P = torch.empty(nbytes, dtype=torch.uint8, device=T.device)
     _check(bitlinear_pack(_ptr(T), N, K, T.stride(0), layout, _ptr(P), _stream(stream)), "bitlinear_pack")
     return P
+
+
+def transcode_i2(P, layout: int, N: int, K: int, stream=None):
+    """Packed b3 / b1 weights P (cuda) -> the same weights packed as i2 (a load-time step)."""
+    torch = _torch()
+    nbytes = bitlinear_packed_bytes(N, K, LAYOUT_I2)
+    if nbytes < 0:
+        raise BitlinearError(ERR_INVALID_ARG, "transcode_i2")
+    P2 = torch.empty(nbytes, dtype=torch.uint8, device=P.device)
+    _check(bitlinear_transcode_i2(_ptr(P), layout, N, K, _ptr(P2), _stream(stream)), "bitlinear_transcode_i2")
+    return P2
 
 
 def quantize_act(X, stream=None):

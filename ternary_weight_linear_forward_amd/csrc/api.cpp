@@ -85,24 +85,12 @@ int64_t staged_xq_bytes(int64_t M, int64_t K, int layout)
 }
 
 // Workspace of one forward: the quantised activations and beta (bf16/fp32
-// input), then, with more than 16 tokens and weights the GEMM rewrites as i2
-// (gemm_rewrites), room for that rewrite.
+// input).  Every product reads the caller's packed weights in their own
+// layout (the GEMM decodes b3 and b1 itself): no forward writes weights.
 int64_t staging_bytes(int64_t M, int64_t K, int layout, int x_dtype)
 {
     if (x_dtype == BITLINEAR_I8 || x_dtype == BITLINEAR_I8_TILED) return 0;
     return staged_xq_bytes(M, K, layout) + round_up(4 * M, 256);
-}
-// The GEMM reads i2 weights or decodes b3 itself; b1 weights, and b3 weights
-// of shapes where the decode would repeat over many token blocks, are
-// rewritten as i2 first.
-bool gemm_rewrites(int64_t M, int64_t N, int layout)
-{
-    return layout == BITLINEAR_LAYOUT_B1 || (layout == BITLINEAR_LAYOUT_B3 && !bl::gemm_b3_native(M, N));
-}
-int64_t transcode_bytes(int64_t M, int64_t N, int64_t K, int layout)
-{
-    return M > 16 && gemm_rewrites(M, N, layout) ? round_up(bitlinear_packed_bytes(N, K, BITLINEAR_LAYOUT_I2), 256)
-                                                 : 0;
 }
 
 // The GEMM addresses the activation rows of one workgroup tile (at most 256
@@ -169,7 +157,7 @@ int64_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K, int l
     if (x_dtype != BITLINEAR_I8 && x_dtype != BITLINEAR_I8_TILED && x_dtype != BITLINEAR_F32 &&
         x_dtype != BITLINEAR_BF16)
         return -1;
-    return staging_bytes(M, K, layout, x_dtype) + transcode_bytes(M, N, K, layout);
+    return staging_bytes(M, K, layout, x_dtype);
 }
 
 int bitlinear_auto_algo(int64_t M, int64_t N, int64_t K, int layout, int x_dtype)
@@ -191,13 +179,12 @@ const char *bitlinear_product_kernel(int64_t M, int64_t N, int64_t K, int layout
         return nullptr;
     if (algo == BITLINEAR_ALGO_AUTO) algo = auto_algo(M, N, layout, x_dtype);
     if ((algo == BITLINEAR_ALGO_GEMV_ADDSUB && (M > 16 || layout != BITLINEAR_LAYOUT_I2)) ||
-        (algo == BITLINEAR_ALGO_GEMM_MFMA && layout == BITLINEAR_LAYOUT_B1 && M <= 16) ||
         (x_dtype == BITLINEAR_I8_TILED && algo != BITLINEAR_ALGO_GEMV_MFMA))
         return nullptr;
     if (algo == BITLINEAR_ALGO_GEMV_ADDSUB) {
         bl::gemv_addsub_kernel_name(M, name, sizeof name);
     } else if (algo == BITLINEAR_ALGO_GEMM_MFMA) {
-        bl::gemm_kernel_name(gemm_rewrites(M, N, layout) ? BITLINEAR_LAYOUT_I2 : layout, M, N, name, sizeof name);
+        bl::gemm_kernel_name(layout, M, N, name, sizeof name);
     } else if (algo == BITLINEAR_ALGO_GEMV_MFMA && bl::gemv_fq_shape(layout, M, N, K, x_dtype)) {
         // the quantiser inside the GEMV (for 16-byte aligned rows)
         bl::gemv_fq_kernel_name(layout, M, N, K, x_dtype, name, sizeof name);
@@ -262,6 +249,19 @@ int bitlinear_pack(const int8_t *T, int64_t N, int64_t K, int64_t ldt, int layou
     if (overlap(span_of(T, N, ldt, K, 1), span_of(P, 1, pb, pb, 1))) return BITLINEAR_ERR_INVALID_ARG;
     (void)hipGetLastError();
     return status_of(bl::launch_pack(T, N, K, ldt, layout, P, as_stream(stream)));
+}
+
+int bitlinear_transcode_i2(const uint8_t *P, int layout, int64_t N, int64_t K, uint8_t *P2, void *stream)
+{
+    if (!P || !P2 || (layout != BITLINEAR_LAYOUT_B3 && layout != BITLINEAR_LAYOUT_B1)) return BITLINEAR_ERR_INVALID_ARG;
+    if (N < 1 || K < 1 || K > BITLINEAR_MAX_K || N > kMaxElems / K) return BITLINEAR_ERR_INVALID_ARG;
+    if (!aligned16(P) || !aligned16(P2)) return BITLINEAR_ERR_INVALID_ARG;
+    const int64_t pb = bitlinear_packed_bytes(N, K, layout), p2b = bitlinear_packed_bytes(N, K, BITLINEAR_LAYOUT_I2);
+    if (overlap(span_of(P, 1, pb, pb, 1), span_of(P2, 1, p2b, p2b, 1))) return BITLINEAR_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    hipStream_t st = as_stream(stream);
+    return status_of(layout == BITLINEAR_LAYOUT_B3 ? bl::launch_b3_to_i2(P, N, K, P2, st)
+                                                   : bl::launch_b1_to_i2(P, N, K, P2, st));
 }
 
 int bitlinear_quantize_act(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int8_t *Xq,
@@ -376,7 +376,6 @@ static int forward_impl(const uint8_t *P, int layout, const float *gamma, int64_
     }
     if (algo == BITLINEAR_ALGO_GEMV_ADDSUB && (M > 16 || layout != BITLINEAR_LAYOUT_I2))
         return BITLINEAR_ERR_UNSUPPORTED;
-    if (algo == BITLINEAR_ALGO_GEMM_MFMA && layout == BITLINEAR_LAYOUT_B1 && M <= 16) return BITLINEAR_ERR_UNSUPPORTED;
     if (x_dtype == BITLINEAR_I8_TILED && algo != BITLINEAR_ALGO_GEMV_MFMA) return BITLINEAR_ERR_UNSUPPORTED;
     if (check_only) return BITLINEAR_OK;
 
@@ -439,16 +438,7 @@ static int forward_impl(const uint8_t *P, int layout, const float *gamma, int64_
     switch (algo) {
     case BITLINEAR_ALGO_GEMV_ADDSUB: e = bl::launch_gemv_addsub(a, st); break;
     case BITLINEAR_ALGO_GEMV_MFMA: e = bl::launch_gemv_mfma(a, st); break;
-    default:
-        if (gemm_rewrites(M, N, layout)) {
-            // rewrite the weights as i2 into the workspace first
-            uint8_t *p2 = static_cast<uint8_t *>(ws) + staging_bytes(M, K, layout, x_dtype);
-            e = layout == BITLINEAR_LAYOUT_B3 ? bl::launch_b3_to_i2(P, N, K, p2, st) : bl::launch_b1_to_i2(P, N, K, p2, st);
-            if (e != hipSuccess) return BITLINEAR_ERR_LAUNCH;
-            a.P = p2;
-            a.layout = BITLINEAR_LAYOUT_I2;
-        }
-        e = bl::launch_gemm_mfma(a, st);
+    default: e = bl::launch_gemm_mfma(a, st);
         break;
     }
     return status_of(e);

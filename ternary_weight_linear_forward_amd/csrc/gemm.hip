@@ -34,6 +34,13 @@
 // 5 kh + t of its row at k-step t.  Digits come from the fixed-point byte
 // (H_t = floor(u 3^t / 256), digit t = H_(t+1) - 3 H_t) and become signed
 // bytes with one v_perm_b32 each.
+//
+// Binary weights (k_gemm_mfma_b1) take the i2 activation staging (128 k per
+// stage) with one 128-weight k-block of 16 bytes per row: the lane reads its
+// row's 16 bytes at once, word kk holds the 32 weights of MFMA k-step kk, and
+// half kh of them (bits 4 kh + s of each byte, s = 0..3) become signed bytes
+// with one v_perm_b32 per dword.  Pad weights are -1, not 0, so the last
+// stage masks the operand bytes at or past K.
 // Only s_barrier (no memory fence) separates the stages; the explicit vmcnt
 // wait before it covers this wave's own copies of the stage, and the barrier
 // then covers every wave's.
@@ -107,8 +114,8 @@ __device__ __forceinline__ void gemm_body(const uint8_t *__restrict__ P, int64_t
                                           int64_t ldq, const float *__restrict__ beta, int64_t M, int64_t N,
                                           int64_t K, void *__restrict__ Y, int y_dtype, int64_t ldy, int n_major)
 {
-    constexpr bool B3 = LAYOUT == LAYOUT_B3;
-    static_assert(LAYOUT == LAYOUT_I2 || (B3 && S == 1), "i2 with S halves of 128 k, or b3 with 160 k");
+    constexpr bool B3 = LAYOUT == LAYOUT_B3, B1 = LAYOUT == LAYOUT_B1;
+    static_assert(LAYOUT == LAYOUT_I2 || ((B3 || B1) && S == 1), "i2 with S halves of 128 k, b3 with 160 k, b1 with 128 k");
     constexpr int NW = WM * WN;                // waves
     constexpr int MI = BM / WM / 32;           // 32-token MFMA tiles per wave
     constexpr int NI = BN / WN / 32;           // 32-row MFMA tiles per wave
@@ -117,7 +124,8 @@ __device__ __forceinline__ void gemm_body(const uint8_t *__restrict__ P, int64_t
     constexpr int KK = B3 ? 5 : 4 * S;         // 32-k MFMA steps per stage
     constexpr int NWORD = B3 ? 4 : KK;         // packed words per weight operand row per stage
     constexpr int A_BYTES = BM * KS_;          // activation bytes per stage: [S][BM][ROW]
-    constexpr int B_BYTES = BN * 32 * S;       // packed weight bytes per stage (2S k-blocks)
+    constexpr int KBS = B1 ? 1 : 2 * S;        // k-blocks per stage
+    constexpr int B_BYTES = BN * 16 * KBS;     // packed weight bytes per stage
     constexpr int STAGE = A_BYTES + B_BYTES;
     constexpr int A_ROWS_W = BM / NW;          // i2: activation rows copied by one wave
     constexpr int A_RB = A_ROWS_W / 8;         // i2: 1 KB copies (8 rows of 128 B) per wave per half
@@ -153,7 +161,7 @@ __device__ __forceinline__ void gemm_body(const uint8_t *__restrict__ P, int64_t
     }
     const int64_t m0 = (n_major ? t % nM : t / nN) * BM;
     const int64_t n0 = (n_major ? t / nM : t % nN) * BN;
-    const int64_t nstages = (KB + 2 * S - 1) / (2 * S);
+    const int64_t nstages = (KB + KBS - 1) / KBS;
 
     // ---- copy sources, fixed for the whole loop ------------------------------
     // The copies are buffer loads.  The hardware range check of a buffer
@@ -211,7 +219,7 @@ __device__ __forceinline__ void gemm_body(const uint8_t *__restrict__ P, int64_t
     // read nothing (their resources are empty) and are never used.
     auto issue = [&](int64_t st, int buf) {
         int8_t *sbase = lds + buf * STAGE;
-        const int64_t ka = st * KS_, kb = st * 2 * S * 256;
+        const int64_t ka = st * KS_, kb = st * KBS * 256;
         const int na = static_cast<int>(a_bytes > ka ? a_bytes - ka : 0);
         const int nb = static_cast<int>(b_bytes > kb ? b_bytes - kb : 0);
 #pragma unroll
@@ -234,13 +242,13 @@ __device__ __forceinline__ void gemm_body(const uint8_t *__restrict__ P, int64_t
                               : (kk / 4) * BM * KSTEP + row * KSTEP + (((2 * (kk % 4) + kh) ^ a_swz(row)) * 16);
     }
     // i2: word (kk % 2) * 2 + kh of the row in k-block kk / 2 (added in
-    // read_ops); b3: the whole chunk row of k-block kh
+    // read_ops); b3: the whole chunk row of k-block kh; b1: the whole chunk row
     int b_off[NI];
 #pragma unroll
     for (int b = 0; b < NI; ++b) {
         const int nl = wn * (BN / WN) + b * 32 + l32;
         b_off[b] = B3 ? A_BYTES + (kh * (BN / 16) + nl / 16) * 256 + (nl % 16) * 16
-                      : A_BYTES + (nl / 16) * 256 + (nl % 16) * 16 + 4 * kh;
+                      : A_BYTES + (nl / 16) * 256 + (nl % 16) * 16 + (B1 ? 0 : 4 * kh);
     }
 
     // A wave with fewer than 4 output tiles keeps SPLIT accumulators per tile
@@ -262,7 +270,7 @@ __device__ __forceinline__ void gemm_body(const uint8_t *__restrict__ P, int64_t
     // that LDS latency overlaps the matrix work of the stage before.
     struct Ops {
         v4i a[MI][KK];         // activation operand of tile a, k-step kk
-        uint32_t w[NI][NWORD]; // i2: packed word of B tile b, k-step kk; b3: the chunk row's words
+        uint32_t w[NI][NWORD]; // i2: packed word of B tile b, k-step kk; b3, b1: the chunk row's words
     };
     auto read_ops = [&](int buf, Ops &o) {
         const int8_t *sbase = lds + buf * STAGE;
@@ -270,7 +278,7 @@ __device__ __forceinline__ void gemm_body(const uint8_t *__restrict__ P, int64_t
         for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
             for (int a = 0; a < MI; ++a) o.a[a][kk] = *reinterpret_cast<const v4i *>(sbase + a_off[a][kk]);
-        if constexpr (B3) {
+        if constexpr (B3 || B1) {
 #pragma unroll
             for (int b = 0; b < NI; ++b) {
                 const uint4 v = *reinterpret_cast<const uint4 *>(sbase + b_off[b]);
@@ -290,9 +298,36 @@ __device__ __forceinline__ void gemm_body(const uint8_t *__restrict__ P, int64_t
         }
     };
     // kb_left: k-blocks of the stage that exist (>= 2S except in the last
-    // stage); the words of the others become T = 0
+    // stage); the words of the others become T = 0.  b1: k_left, the k of the
+    // stage before K (>= 128 except in the last stage).
     auto mma = [&](const Ops &o, int kb_left) {
-        if constexpr (B3) {
+        if constexpr (B1) {
+            const int k_left = kb_left;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                // weights 32 kk + 16 kh + 4 s + j (byte j of dword s) exist when below k_left
+                const int nv = k_left - 32 * kk - 16 * kh;
+                v4i bf[NI];
+#pragma unroll
+                for (int b = 0; b < NI; ++b)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t bits = (o.w[b][kk] >> (4 * kh + q)) & 0x01010101u;
+                        uint32_t v = __builtin_amdgcn_perm(0u, 0x000001ffu, bits);
+                        if (nv < 16) {
+                            const int e = nv - 4 * q; // bytes of this dword that exist
+                            v &= e >= 4 ? 0xffffffffu : (e <= 0 ? 0u : (1u << (8 * e)) - 1u);
+                        }
+                        bf[b][q] = static_cast<int>(v);
+                    }
+#pragma unroll
+                for (int a = 0; a < MI; ++a)
+#pragma unroll
+                    for (int b = 0; b < NI; ++b)
+                        acc[a][b][kk % SPLIT] = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[a][kk], bf[b],
+                                                                                      acc[a][b][kk % SPLIT], 0, 0, 0);
+            }
+        } else if constexpr (B3) {
             // k-block kh exists unless kb_left == 1; a missing block's words
             // become the all-zero-weight word before decoding
             v4i bf[NI][5];
@@ -350,8 +385,13 @@ __device__ __forceinline__ void gemm_body(const uint8_t *__restrict__ P, int64_t
         stage_barrier();
         issue(st + NST, slot);
         read_ops(nslot, nxt);
-        const int64_t left = KB - 2 * S * st;
-        mma(cur, static_cast<int>(left < 2 * S ? left : 2 * S));
+        if constexpr (B1) {
+            const int64_t left = K - KS_ * st;
+            mma(cur, static_cast<int>(left < KS_ ? left : KS_));
+        } else {
+            const int64_t left = KB - KBS * st;
+            mma(cur, static_cast<int>(left < KBS ? left : KBS));
+        }
         slot = nslot;
     };
     int64_t st = 0;
@@ -416,6 +456,17 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_i2(const uint8_t *__
 }
 
 template <int BM, int BN, int WM, int WN, int S>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_b1(const uint8_t *__restrict__ P, int64_t KB,
+                                                               int64_t NT, const float *__restrict__ gamma_p,
+                                                               const int8_t *__restrict__ Xq, int64_t ldq,
+                                                               const float *__restrict__ beta, int64_t M,
+                                                               int64_t N, int64_t K, void *__restrict__ Y,
+                                                               int y_dtype, int64_t ldy, int n_major)
+{
+    gemm_body<LAYOUT_B1, BM, BN, WM, WN, S>(P, KB, NT, gamma_p, Xq, ldq, beta, M, N, K, Y, y_dtype, ldy, n_major);
+}
+
+template <int BM, int BN, int WM, int WN, int S>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_mfma_b3(const uint8_t *__restrict__ P, int64_t KB,
                                                                int64_t NT, const float *__restrict__ gamma_p,
                                                                const int8_t *__restrict__ Xq, int64_t ldq,
@@ -431,18 +482,21 @@ template <int LAYOUT, int BM, int BN, int WM, int WN, int S>
 hipError_t launch_tile(const GemvArgs &a, hipStream_t stream)
 {
     const int64_t NT = (a.N + 15) / 16;
-    const int64_t KB = LAYOUT == LAYOUT_B3 ? (a.K + 79) / 80 : (a.K + 63) / 64;
+    const int64_t KB = LAYOUT == LAYOUT_B3 ? (a.K + 79) / 80 : (LAYOUT == LAYOUT_B1 ? (a.K + 127) / 128 : (a.K + 63) / 64);
     const int64_t nN = (a.N + BN - 1) / BN, nM = (a.M + BM - 1) / BM;
     dim3 grid(static_cast<unsigned>(nN), static_cast<unsigned>(nM));
     // bytes one XCD reads per tile order: M-block-major: its share of the
     // activation row blocks plus every weight tile; N-block-major: its share of
     // the weight tiles plus every activation row
     const double act = static_cast<double>(a.M) * a.K,
-                 wts = static_cast<double>(a.N) * a.K / (LAYOUT == LAYOUT_B3 ? 5 : 4);
+                 wts = static_cast<double>(a.N) * a.K / (LAYOUT == LAYOUT_B3 ? 5 : (LAYOUT == LAYOUT_B1 ? 8 : 4));
     const double m_major = act / 8 + wts, n_major = wts / 8 + act;
     const int nmaj = (nM > 1 && n_major < m_major) ? 1 : 0;
     if constexpr (LAYOUT == LAYOUT_B3)
         hipLaunchKernelGGL((k_gemm_mfma_b3<BM, BN, WM, WN, S>), grid, dim3(64 * WM * WN), 0, stream, a.P, KB, NT,
+                           a.gamma, a.Xq, a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy, nmaj);
+    else if constexpr (LAYOUT == LAYOUT_B1)
+        hipLaunchKernelGGL((k_gemm_mfma_b1<BM, BN, WM, WN, S>), grid, dim3(64 * WM * WN), 0, stream, a.P, KB, NT,
                            a.gamma, a.Xq, a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy, nmaj);
     else
         hipLaunchKernelGGL((k_gemm_mfma_i2<BM, BN, WM, WN, S>), grid, dim3(64 * WM * WN), 0, stream, a.P, KB, NT,
@@ -461,7 +515,7 @@ namespace {
 struct GemmTile {
     int bm, bn, wm, wn, s; // tile, wave grid, k halves (of 128) per stage
     double rate;
-    bool i2, b3; // offered for i2 / b3 weights (the b3 decode of a 128 x 128 wave tile spills registers)
+    bool i2, b3; // offered for i2 and b1 / b3 weights (the b3 decode of a 128 x 128 wave tile spills registers)
 };
 constexpr GemmTile kTiles[] = {{256, 256, 2, 2, 1, 2.1, true, false},
                                {128, 256, 2, 4, 1, 1.95, true, true},
@@ -490,7 +544,10 @@ hipError_t launch_entry(const GemvArgs &a, hipStream_t stream)
     constexpr GemmTile t = kTiles[I];
     if constexpr (t.b3)
         if (a.layout == LAYOUT_B3) return launch_tile<LAYOUT_B3, t.bm, t.bn, t.wm, t.wn, t.s>(a, stream);
-    if constexpr (t.i2) return launch_tile<LAYOUT_I2, t.bm, t.bn, t.wm, t.wn, t.s>(a, stream);
+    if constexpr (t.i2) {
+        if (a.layout == LAYOUT_B1) return launch_tile<LAYOUT_B1, t.bm, t.bn, t.wm, t.wn, t.s>(a, stream);
+        return launch_tile<LAYOUT_I2, t.bm, t.bn, t.wm, t.wn, t.s>(a, stream);
+    }
     return hipErrorInvalidValue; // not reached: best_tile offers the tile only for its layouts
 }
 } // namespace
@@ -501,17 +558,11 @@ int64_t gemm_tiles(int64_t M, int64_t N)
     return ((M + 63) / 64) * ((N + 127) / 128);
 }
 
-bool gemm_b3_native(int64_t M, int64_t N)
-{
-    const GemmTile &t = kTiles[best_tile(LAYOUT_B3, M, N)];
-    return (M + t.bm - 1) / t.bm <= 2;
-}
-
 void gemm_kernel_name(int layout, int64_t M, int64_t N, char *buf, size_t n)
 {
     const GemmTile &t = kTiles[best_tile(layout, M, N)];
-    snprintf(buf, n, "bl::k_gemm_mfma_%s<%d, %d, %d, %d, %d>", layout == LAYOUT_B3 ? "b3" : "i2", t.bm, t.bn, t.wm,
-             t.wn, t.s);
+    snprintf(buf, n, "bl::k_gemm_mfma_%s<%d, %d, %d, %d, %d>",
+             layout == LAYOUT_B3 ? "b3" : (layout == LAYOUT_B1 ? "b1" : "i2"), t.bm, t.bn, t.wm, t.wn, t.s);
 }
 
 hipError_t launch_gemm_mfma(const GemvArgs &a, hipStream_t stream)

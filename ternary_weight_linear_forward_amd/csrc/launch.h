@@ -134,7 +134,6 @@ int64_t gemm_tiles(int64_t M, int64_t N);
 // as i2 (a single pass) and the i2 GEMM are faster (measured on the 70B
 // layers: gate at 64 tokens 45 us native against 60 us, q and down at 176
 // tokens the other way round).
-bool gemm_b3_native(int64_t M, int64_t N);
 
 // Straight-through-estimator gradients (backward.hip): dX from i2-packed
 // weights, dW from the forward's int8 activations and beta.

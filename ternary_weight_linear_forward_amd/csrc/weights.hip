@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void k_pack_b3(const int8_t *__restrict__ T, i
     *reinterpret_cast<uint4 *>(P + idx * 16) = make_uint4(word[0], word[1], word[2], word[3]);
 }
 
-// b3 -> i2 transcode (for the GEMM, which reads i2).  One thread per b3 chunk
+// b3 -> i2 transcode (a load-time step).  One thread per b3 chunk
 // (row r of tile, block kb3: weights 80 kb3 .. +79).  Digit t of its 16 bytes
 // is the 16 weights k0 = 80 kb3 + 16 t .. k0+15, which is exactly i2 word
 // d = (k0 % 64) / 16 of i2 block kb2 = k0 / 64 (80 and 64 are multiples of
@@ -288,14 +288,15 @@ __global__ __launch_bounds__(256) void k_pack_b1(const int8_t *__restrict__ T, i
     *reinterpret_cast<uint4 *>(P + idx * 16) = make_uint4(word[0], word[1], word[2], word[3]);
 }
 
-// b1 -> i2 transcode (for the GEMM): one thread per i2 word, 16 weights
+// b1 -> i2 transcode (a load-time step): one thread per i2 word, 16 weights
 // k0 .. k0+15 (k0 = 64 kb2 + 16 d).  They are half h = (k0 % 32) / 16 of b1
 // word q = (k0 % 128) / 32 of block k0 / 128: weight 4s + j of the i2 word is
 // bit 8j + 4h + s of that b1 word, and its code is 2 (T = +1) or 0 (T = -1).
-// Positions at or past K become code 1 (T = 0): binary padding carries a
-// weight, i2 padding must not.
+// Positions at or past K and rows at or past N become code 1 (T = 0): binary
+// padding carries a weight, i2 padding must not, so the result is byte for
+// byte the i2 packing of the same weights.
 __global__ __launch_bounds__(256) void k_b1_to_i2(const uint8_t *__restrict__ P1, int64_t KB1, int64_t KB2,
-                                                  int64_t K, int64_t nwords, uint8_t *__restrict__ P2)
+                                                  int64_t N, int64_t K, int64_t nwords, uint8_t *__restrict__ P2)
 {
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; // ((tile*KB2 + kb2)*16 + r)*4 + d
     if (idx >= nwords) return;
@@ -317,6 +318,7 @@ __global__ __launch_bounds__(256) void k_b1_to_i2(const uint8_t *__restrict__ P1
                 out = (out & ~(3u << sh)) | (1u << sh);
             }
     }
+    if (tile * 16 + r >= N) out = 0x55555555u; // a padding row
     reinterpret_cast<uint32_t *>(P2)[idx] = out;
 }
 
@@ -325,7 +327,7 @@ hipError_t launch_b1_to_i2(const uint8_t *P1, int64_t N, int64_t K, uint8_t *P2,
     const int64_t NT = (N + 15) / 16, KB1 = (K + 127) / 128, KB2 = (K + 63) / 64;
     const int64_t nwords = NT * KB2 * 16 * 4;
     hipLaunchKernelGGL(k_b1_to_i2, dim3(static_cast<unsigned>((nwords + 255) / 256)), dim3(256), 0, stream, P1, KB1,
-                       KB2, K, nwords, P2);
+                       KB2, N, K, nwords, P2);
     return hipGetLastError();
 }
 

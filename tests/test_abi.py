@@ -143,7 +143,6 @@ def fw(**kw):
     (dict(ws=C), bl.ERR_INVALID_ARG),                               # workspace overlaps X
     (dict(algo=bl.ALGO_GEMV_ADDSUB, M=17), bl.ERR_UNSUPPORTED),
     (dict(algo=bl.ALGO_GEMV_ADDSUB, layout=bl.LAYOUT_B3), bl.ERR_UNSUPPORTED),
-    (dict(algo=bl.ALGO_GEMM_MFMA, layout=bl.LAYOUT_B1), bl.ERR_UNSUPPORTED),  # b1 GEMM needs M > 16
 ])
 def test_forward_rejects(kw, status):
     assert fw(**kw) == status
@@ -256,7 +255,7 @@ def test_auto_algo_dispatch():
         assert f(M, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMV_MFMA
     assert f(2048, 3200, 3200, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMM_MFMA
     assert f(2048, 3200, 3200, bl.LAYOUT_B3, bl.BF16) == bl.ALGO_GEMM_MFMA  # decoded inside the GEMM
-    assert f(2048, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == bl.ALGO_GEMM_MFMA  # through an i2 rewrite
+    assert f(2048, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == bl.ALGO_GEMM_MFMA  # decoded inside the GEMM
     assert f(16, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == bl.ALGO_GEMV_MFMA
     assert f(2048, 3200, 3200, bl.LAYOUT_I2, bl.I8_TILED) == bl.ALGO_GEMV_MFMA
     assert f(176, 1024, 8192, bl.LAYOUT_I2, bl.BF16) == bl.ALGO_GEMV_MFMA  # 16 tiles: GPU mostly idle
@@ -311,15 +310,15 @@ def test_product_kernel_names():
     assert f(150, 6000, 300, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemm_mfma_i2<32, 128, 1, 4, 1>"
     assert f(3, 64, 64, bl.LAYOUT_I2, bl.BF16, bl.ALGO_GEMV_ADDSUB) == "bl::k_gemv_addsub<4>"
     assert f(3, 64, 64, bl.LAYOUT_B3, bl.BF16, bl.ALGO_GEMM_MFMA) == "bl::k_gemm_mfma_b3<32, 128, 1, 4, 1>"
-    assert f(3, 64, 64, bl.LAYOUT_B1, bl.BF16, bl.ALGO_GEMM_MFMA) is None
-    # b3 is decoded in the GEMM (tiles other than 256 x 256) when a weight tile
-    # meets at most two token blocks, else rewritten as i2; b1 always is
+    assert f(3, 64, 64, bl.LAYOUT_B1, bl.BF16, bl.ALGO_GEMM_MFMA) == "bl::k_gemm_mfma_b1<32, 128, 1, 4, 1>"
+    # b3 and b1 are decoded in the GEMM at every token count (b3: tiles other
+    # than 256 x 256)
     assert f(64, 28672, 8192, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemm_mfma_b3<64, 128, 1, 4, 1>"  # b3 only
     assert f(176, 28672, 8192, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemm_mfma_b3<128, 256, 2, 4, 1>"
-    assert f(176, 8192, 8192, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemm_mfma_i2<32, 128, 1, 4, 1>"
-    assert f(2048, 3200, 3200, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemm_mfma_i2<128, 256, 2, 4, 1>"
+    assert f(176, 8192, 8192, bl.LAYOUT_B3, bl.BF16).startswith("bl::k_gemm_mfma_b3<")
+    assert f(2048, 3200, 3200, bl.LAYOUT_B3, bl.BF16) == "bl::k_gemm_mfma_b3<128, 256, 2, 4, 1>"
     assert f(4000, 4000, 130, bl.LAYOUT_I2, bl.BF16) == "bl::k_gemm_mfma_i2<256, 256, 2, 2, 1>"
-    assert f(2048, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == "bl::k_gemm_mfma_i2<128, 256, 2, 4, 1>"
+    assert f(2048, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == "bl::k_gemm_mfma_b1<128, 256, 2, 4, 1>"
     assert f(1, 3200, 3200, bl.LAYOUT_B1, bl.BF16) == "bl::k_gemv_fq<2, 1, 1>"
     assert f(1, 3200, 3200, bl.LAYOUT_B1, bl.I8) == "bl::k_gemv_mfma<2, 1, 1, false>"
     assert f(3, 64, 64, bl.LAYOUT_B1, bl.BF16, bl.ALGO_GEMV_ADDSUB) is None
@@ -362,19 +361,31 @@ def test_backward_rejects():
 
 
 def test_gemm_weight_workspace():
-    """Workspace for the weights: none where the GEMM decodes b3 itself (at
-    most two token blocks per weight tile); room for the i2 rewrite of b3
-    weights with more token blocks and of b1 weights, with more than 16
-    tokens."""
+    """No forward rewrites weights: the products decode b3 and b1 themselves,
+    so pre-quantised input needs no workspace at any token count and nothing
+    in the workspace is sized by N."""
     N, K = 1000, 3000
     ws = bl.bitlinear_forward_workspace_bytes
-    i2 = bl.bitlinear_packed_bytes(N, K, bl.LAYOUT_I2)
-    assert ws(64, N, K, bl.LAYOUT_B3, bl.I8) == 0
-    assert ws(64, N, K, bl.LAYOUT_B3, bl.BF16) == ws(64, 1, K, bl.LAYOUT_B3, bl.BF16)  # nothing sized by N
-    assert ws(176, N, K, bl.LAYOUT_B3, bl.I8) >= i2
-    assert ws(16, N, K, bl.LAYOUT_B3, bl.I8) == 0
-    assert ws(64, N, K, bl.LAYOUT_B1, bl.I8) >= i2
-    assert bl.bitlinear_forward_workspace_bytes(16, N, K, bl.LAYOUT_B1, bl.I8) == 0
+    for layout in (bl.LAYOUT_I2, bl.LAYOUT_B3, bl.LAYOUT_B1):
+        for M in (1, 16, 64, 176, 2048):
+            assert ws(M, N, K, layout, bl.I8) == 0
+            assert ws(M, N, K, layout, bl.BF16) == ws(M, 1, K, layout, bl.BF16) > 0
+
+
+def test_transcode_rejects():
+    """bitlinear_transcode_i2 argument checks (no launch)."""
+    f = bl.bitlinear_transcode_i2
+    ok = dict(P=A, layout=bl.LAYOUT_B3, N=64, K=300, P2=B, stream=None)
+    assert f(**{**ok, "P": None}) == bl.ERR_INVALID_ARG
+    assert f(**{**ok, "P2": None}) == bl.ERR_INVALID_ARG
+    assert f(**{**ok, "layout": bl.LAYOUT_I2}) == bl.ERR_INVALID_ARG
+    assert f(**{**ok, "layout": 7}) == bl.ERR_INVALID_ARG
+    assert f(**{**ok, "N": 0}) == bl.ERR_INVALID_ARG
+    assert f(**{**ok, "K": 0}) == bl.ERR_INVALID_ARG
+    assert f(**{**ok, "K": bl.MAX_K + 1}) == bl.ERR_INVALID_ARG
+    assert f(**{**ok, "P2": B + 4}) == bl.ERR_INVALID_ARG  # misaligned
+    assert f(**{**ok, "P2": A + 256}) == bl.ERR_INVALID_ARG  # overlaps P
+    assert f(**{**ok, "layout": bl.LAYOUT_B1, "P2": A + 16 * 64 * 2}) == bl.ERR_INVALID_ARG
 
 
 def _jobs(n=3, over=None):

@@ -3,7 +3,8 @@ absmean scale; the 1-bit b1 packed layout) against the CPU oracle: the sign
 quantiser and gamma bit-exact, b1 packing byte-exact, the forward's int32
 accumulators exact and its fp32 / bf16 outputs bit-identical, through the
 matrix-core GEMV (row-major and tiled activations, per-tile and persistent
-kernels) and through the GEMM after the b1 -> i2 rewrite."""
+kernels) and through the GEMM, which decodes the bits itself; the load-time
+b1 -> i2 transcode byte-exact."""
 import numpy as np
 import pytest
 
@@ -92,7 +93,7 @@ def test_forward_many_tokens(algo, M, N, K):
 
 def test_forward_gemm_prefill_rows():
     """The GEMM at a prefill shape with several workgroup tiles and a ragged
-    k tail, fed by the b1 -> i2 rewrite in the workspace."""
+    k tail (the -1 pad weights masked in the last stage)."""
     log("b1 gemm", 2048, 3200, 330)
     run_case(2048, 3200, 330, bl.ALGO_AUTO, seed=21, y_kinds=("i32", "f32"))
 
@@ -133,7 +134,7 @@ def test_forward_max_k():
     assert ref["acc"][1, 0] == 127 * K
     P = to_dev(oracle.pack(t, bl.LAYOUT_B1))
     gamma = to_dev(np.array([0.03], np.float32))
-    for algo in (bl.ALGO_AUTO, bl.ALGO_GEMV_MFMA):
+    for algo in (bl.ALGO_AUTO, bl.ALGO_GEMV_MFMA, bl.ALGO_GEMM_MFMA):
         acc = to_host(bl.forward(P, bl.LAYOUT_B1, gamma, to_dev(x), N, K, y_dtype=torch.int32, algo=algo))
         assert np.array_equal(acc, ref["acc"]), algo
 
@@ -151,3 +152,50 @@ def test_binary_chain_end_to_end():
         x = synth.activations_bf16(M, K, seed=25 + M)
         ref = oracle.forward(t_ref, g_ref, x)
         assert_f32_parity(to_host(bl.forward(P, bl.LAYOUT_B1, gamma, to_dev(x), N, K)), ref["y"])
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 50, 100), (5, 17, 65), (16, 100, 333), (16, 256, 128)])
+def test_forward_gemm_few_tokens(M, N, K):
+    """The GEMM at 1-16 tokens (the bits decoded in the GEMM at any M)."""
+    log("b1 gemm few tokens", M, N, K)
+    assert bl.bitlinear_product_kernel(M, N, K, bl.LAYOUT_B1, bl.BF16, bl.ALGO_GEMM_MFMA).startswith("bl::k_gemm_mfma_b1<")
+    run_case(M, N, K, bl.ALGO_GEMM_MFMA, seed=M * 7 + N + K, y_kinds=("i32", "f32"))
+
+
+@pytest.mark.parametrize("M,N,K", [(40, 300, 200), (300, 130, 1000), (2048, 512, 129)])
+def test_forward_gemm_int8_rows_with_junk_past_k(M, N, K):
+    """Caller-quantised int8 rows whose bytes past K (up to the row stride)
+    hold junk: the GEMM reads them with the row, and the -1 pad weights of the
+    last k-block must not meet them (masked operand bytes)."""
+    log("b1 gemm int8 junk", M, N, K)
+    t = synth.binary_weights(N, K, seed=M + N + K)
+    x = synth.activations_bf16(M, K, seed=M + 2 * K)
+    ref = oracle.forward(t, np.float32(0.02), x)
+    q, beta = oracle.quantize_act(synth.bf16_bits_to_f32(x))
+    ldx = (K + 15) // 16 * 16 + 16
+    xq = np.random.default_rng(K).integers(-127, 128, size=(M, ldx), dtype=np.int64).astype(np.int8)
+    xq[:, :K] = q
+    P = to_dev(oracle.pack(t, bl.LAYOUT_B1))
+    gamma = to_dev(np.array([0.02], np.float32))
+    Xd = to_dev(xq)[:, :K]
+    assert bl.bitlinear_product_kernel(M, N, K, bl.LAYOUT_B1, bl.I8, bl.ALGO_GEMM_MFMA).startswith("bl::k_gemm_mfma_b1<")
+    acc = to_host(bl.forward(P, bl.LAYOUT_B1, gamma, Xd, N, K, beta=to_dev(beta), y_dtype=torch.int32,
+                             algo=bl.ALGO_GEMM_MFMA))
+    assert np.array_equal(acc, ref["acc"])
+
+
+@pytest.mark.parametrize("layout", [bl.LAYOUT_B3, bl.LAYOUT_B1], ids=["b3", "b1"])
+@pytest.mark.parametrize("N,K", [(1, 1), (17, 129), (64, 1000), (3200, 8640)])
+def test_transcode_i2(layout, N, K):
+    """The load-time i2 rewrite: byte-exact against packing the same weights
+    as i2, and a forward on it equals the oracle."""
+    log("transcode i2", layout, N, K)
+    t = (synth.binary_weights if layout == bl.LAYOUT_B1 else synth.ternary_weights)(N, K, seed=N + K)
+    P2 = bl.transcode_i2(to_dev(oracle.pack(t, layout)), layout, N, K)
+    assert np.array_equal(to_host(P2), oracle.pack(t, bl.LAYOUT_I2))
+    if N * K <= 64 * 1000:
+        x = synth.activations_bf16(300, K, seed=K)
+        ref = oracle.forward(t, np.float32(0.02), x)
+        acc = to_host(bl.forward(P2, bl.LAYOUT_I2, to_dev(np.array([0.02], np.float32)), to_dev(x), N, K,
+                                 y_dtype=torch.int32))
+        assert np.array_equal(acc, ref["acc"])

@@ -48,7 +48,7 @@ def replay_matches(run, out, noise):
 
 
 @pytest.mark.parametrize("layout,M,N,K", [("i2", 300, 4000, 640), ("b3", 300, 4000, 640), ("b3", 64, 20000, 256)],
-                         ids=["i2_gemm", "b3_rewrite_gemm", "b3_native_gemm"])
+                         ids=["i2_gemm", "b3_gemm_300_tokens", "b3_gemm_64_tokens"])
 def test_prefill_forward_graph_replay(layout, M, N, K):
     log("graph prefill", layout, M, N, K)
     t = synth.ternary_weights(N, K, seed=M + N)

@@ -2,8 +2,8 @@
 two calls in a row, the second with a smaller input, each compared with
 bitlinear_forward on the same inputs (bit-identical) and with the oracle.
 The cases use the scratch array for what bitlinear_forward keeps in its
-workspace: staged int8 activations (16 tokens; unaligned rows), and the i2
-rewrite of binary weights for the GEMM."""
+workspace: the staged int8 activations and beta, for the GEMV (16 tokens;
+unaligned rows) and for the GEMM on binary weights."""
 import numpy as np
 import pytest
 
@@ -38,7 +38,7 @@ CASES = [  # (name, layout, M, N, K, x kind) -- in call order: larger, then smal
 ]
 
 
-@pytest.mark.parametrize("pair", [(0, 1), (2, 3)], ids=["gemv_staged", "gemm_b1_rewrite"])
+@pytest.mark.parametrize("pair", [(0, 1), (2, 3)], ids=["gemv_staged", "gemm_b1_staged"])
 def test_noalloc_matches_forward_two_calls(pair):
     results = []
     for idx in pair:
