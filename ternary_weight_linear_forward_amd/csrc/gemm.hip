@@ -45,6 +45,7 @@
 // wait before it covers this wave's own copies of the stage, and the barrier
 // then covers every wave's.
 #include <cstdio>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -300,12 +301,14 @@ __device__ __forceinline__ void gemm_body(const uint8_t *__restrict__ P, int64_t
     // kb_left: k-blocks of the stage that exist (>= 2S except in the last
     // stage); the words of the others become T = 0.  b1: k_left, the k of the
     // stage before K (>= 128 except in the last stage).
-    auto mma = [&](const Ops &o, int kb_left) {
+    auto mma = [&](const Ops &o, int kb_left, auto last) {
         if constexpr (B1) {
+            // weights 32 kk + 16 kh + 4 q + j (byte j of dword q) exist when
+            // below k_left; only the last stage (peeled off the loop, so the
+            // loop body holds the plain decode alone) masks
             const int k_left = kb_left;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                // weights 32 kk + 16 kh + 4 s + j (byte j of dword s) exist when below k_left
                 const int nv = k_left - 32 * kk - 16 * kh;
                 v4i bf[NI];
 #pragma unroll
@@ -314,7 +317,7 @@ __device__ __forceinline__ void gemm_body(const uint8_t *__restrict__ P, int64_t
                     for (int q = 0; q < 4; ++q) {
                         const uint32_t bits = (o.w[b][kk] >> (4 * kh + q)) & 0x01010101u;
                         uint32_t v = __builtin_amdgcn_perm(0u, 0x000001ffu, bits);
-                        if (nv < 16) {
+                        if constexpr (decltype(last)::value) {
                             const int e = nv - 4 * q; // bytes of this dword that exist
                             v &= e >= 4 ? 0xffffffffu : (e <= 0 ? 0u : (1u << (8 * e)) - 1u);
                         }
@@ -324,8 +327,8 @@ __device__ __forceinline__ void gemm_body(const uint8_t *__restrict__ P, int64_t
                 for (int a = 0; a < MI; ++a)
 #pragma unroll
                     for (int b = 0; b < NI; ++b)
-                        acc[a][b][kk % SPLIT] = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[a][kk], bf[b],
-                                                                                      acc[a][b][kk % SPLIT], 0, 0, 0);
+                        acc[a][b][kk % SPLIT] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                            o.a[a][kk], bf[b], acc[a][b][kk % SPLIT], 0, 0, 0);
             }
         } else if constexpr (B3) {
             // k-block kh exists unless kb_left == 1; a missing block's words
@@ -376,7 +379,7 @@ __device__ __forceinline__ void gemm_body(const uint8_t *__restrict__ P, int64_t
     Ops o0, o1;
     read_ops(0, o0);
     int slot = 0; // ring slot of stage st
-    auto step = [&](int64_t st, const Ops &cur, Ops &nxt) {
+    auto step = [&](int64_t st, const Ops &cur, Ops &nxt, auto last) {
         const int nslot = slot == NST - 1 ? 0 : slot + 1;
         // this wave's copies of stage st+1 are done once at most NST-2 later
         // stages' copies are outstanding, and its reads of stage st are back;
@@ -387,19 +390,36 @@ __device__ __forceinline__ void gemm_body(const uint8_t *__restrict__ P, int64_t
         read_ops(nslot, nxt);
         if constexpr (B1) {
             const int64_t left = K - KS_ * st;
-            mma(cur, static_cast<int>(left < KS_ ? left : KS_));
+            mma(cur, static_cast<int>(left < KS_ ? left : KS_), last);
         } else {
             const int64_t left = KB - KBS * st;
-            mma(cur, static_cast<int>(left < KBS ? left : KBS));
+            mma(cur, static_cast<int>(left < KBS ? left : KBS), last);
         }
         slot = nslot;
     };
     int64_t st = 0;
-    for (; st + 1 < nstages; st += 2) {
-        step(st, o0, o1);
-        step(st + 1, o1, o0);
+    if constexpr (B1) {
+        // the last stage, the only one that can hold pad weights, on its own
+        const std::false_type body{};
+        const std::true_type last{};
+        for (; st + 2 < nstages; st += 2) {
+            step(st, o0, o1, body);
+            step(st + 1, o1, o0, body);
+        }
+        if (st + 1 < nstages) {
+            step(st, o0, o1, body);
+            step(st + 1, o1, o0, last);
+        } else {
+            step(st, o0, o1, last);
+        }
+    } else {
+        const std::false_type any{};
+        for (; st + 1 < nstages; st += 2) {
+            step(st, o0, o1, any);
+            step(st + 1, o1, o0, any);
+        }
+        if (st < nstages) step(st, o0, o1, any);
     }
-    if (st < nstages) step(st, o0, o1);
 
     // ---- epilogue ------------------------------------------------------------
 #pragma unroll
@@ -515,13 +535,14 @@ namespace {
 struct GemmTile {
     int bm, bn, wm, wn, s; // tile, wave grid, k halves (of 128) per stage
     double rate;
-    bool i2, b3; // offered for i2 and b1 / b3 weights (the b3 decode of a 128 x 128 wave tile spills registers)
+    bool i2, b3, b1; // offered for these weights (the b3 decode, and the b1 tail mask, of a 128 x 128 wave
+                     // tile spill registers)
 };
-constexpr GemmTile kTiles[] = {{256, 256, 2, 2, 1, 2.1, true, false},
-                               {128, 256, 2, 4, 1, 1.95, true, true},
-                               {128, 128, 2, 2, 1, 1.5, true, true},
-                               {32, 128, 1, 4, 1, 1.1, true, true},
-                               {64, 128, 1, 4, 1, 1.3, false, true}};
+constexpr GemmTile kTiles[] = {{256, 256, 2, 2, 1, 2.1, true, false, false},
+                               {128, 256, 2, 4, 1, 1.95, true, true, true},
+                               {128, 128, 2, 2, 1, 1.5, true, true, true},
+                               {32, 128, 1, 4, 1, 1.1, true, true, true},
+                               {64, 128, 1, 4, 1, 1.3, false, true, false}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int64_t kCUs = 256;
 
@@ -530,7 +551,7 @@ int best_tile(int layout, int64_t M, int64_t N)
     int best = -1;
     double best_cost = 0;
     for (int i = 0; i < kNumTiles; ++i) {
-        if (layout == LAYOUT_B3 ? !kTiles[i].b3 : !kTiles[i].i2) continue;
+        if (layout == LAYOUT_B3 ? !kTiles[i].b3 : (layout == LAYOUT_B1 ? !kTiles[i].b1 : !kTiles[i].i2)) continue;
         const int64_t t = ((M + kTiles[i].bm - 1) / kTiles[i].bm) * ((N + kTiles[i].bn - 1) / kTiles[i].bn);
         const double cost = static_cast<double>((t + kCUs - 1) / kCUs) * kTiles[i].bm * kTiles[i].bn / kTiles[i].rate;
         if (best < 0 || cost < best_cost) best = i, best_cost = cost;
@@ -544,10 +565,9 @@ hipError_t launch_entry(const GemvArgs &a, hipStream_t stream)
     constexpr GemmTile t = kTiles[I];
     if constexpr (t.b3)
         if (a.layout == LAYOUT_B3) return launch_tile<LAYOUT_B3, t.bm, t.bn, t.wm, t.wn, t.s>(a, stream);
-    if constexpr (t.i2) {
+    if constexpr (t.b1)
         if (a.layout == LAYOUT_B1) return launch_tile<LAYOUT_B1, t.bm, t.bn, t.wm, t.wn, t.s>(a, stream);
-        return launch_tile<LAYOUT_I2, t.bm, t.bn, t.wm, t.wn, t.s>(a, stream);
-    }
+    if constexpr (t.i2) return launch_tile<LAYOUT_I2, t.bm, t.bn, t.wm, t.wn, t.s>(a, stream);
     return hipErrorInvalidValue; // not reached: best_tile offers the tile only for its layouts
 }
 } // namespace
