@@ -125,6 +125,60 @@ __device__ __forceinline__ void i2_scaled_step(const uint4 &w, const v4i (&at)[4
     acc.a16b = __builtin_amdgcn_mfma_i32_16x16x64_i8(at[3], b3, acc.a16b, 0, 0, 0);
 }
 
+// b3 k-step with the digit subtraction moved into the matrix cores.  The
+// fixed-point byte u of five digits (c_0 most significant) gives the levels
+// X_t = floor(u 3^t / 256) (t = 1..5; X_5 is the base-3 value itself) and
+// digit t is X_(t+1) - 3 X_t (b3_word_digits).  Instead of forming the digits,
+// MFMA t multiplies the activations of digit t with X_(t+1) into acc_p and,
+// for t >= 1, with X_t into acc_m: sum_k q c = acc_p - 3 acc_m.  X_5 (up to
+// 242) does not fit a signed byte, so it enters as X_5 - 128 (bit 7 flipped)
+// and 128 times the sum of digit 4's activations is added back (b3_level_fix).
+// Per 4-byte word: 17 instructions (the 16-bit products and one v_perm_b32
+// per level, one xor) instead of 25, and 9 MFMAs per k-step instead of 5.
+struct B3LevelAcc {
+    v4i p, m;
+};
+
+__device__ __forceinline__ void b3_level_step(const uint4 &w, const v4i (&a)[5], B3LevelAcc &acc)
+{
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    v4i X[6];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t even = wd[q] & 0x00ff00ffu;                         // bytes 0 and 2
+        const uint32_t odd = __builtin_amdgcn_perm(0u, wd[q], 0x0c030c01u); // bytes 1 and 3
+        uint32_t p3 = 1;
+#pragma unroll
+        for (int t = 1; t <= 5; ++t) {
+            p3 *= 3;
+            const uint32_t ze = pk_mul_u16(even, p3 * 0x00010001u), zo = pk_mul_u16(odd, p3 * 0x00010001u);
+            const uint32_t x = __builtin_amdgcn_perm(zo, ze, 0x07030501u); // high byte of each lane, in order
+            X[t][q] = static_cast<int>(t == 5 ? x ^ 0x80808080u : x);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 5; ++t) {
+        acc.p = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], X[t + 1], acc.p, 0, 0, 0);
+        if (t >= 1) acc.m = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], X[t], acc.m, 0, 0, 0);
+    }
+}
+
+// 128 sum_k q over digit 4's activations minus sum_k q over all (the offset
+// codes c = T + 1), for the wave's k-steps, in the MFMA output layout.
+template <int SPW>
+__device__ __forceinline__ v4i b3_level_fix(const v4i (&a)[SPW][5], int nj)
+{
+    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    v4i s4 = {0, 0, 0, 0}, all = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+        if (j < nj) {
+            s4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j][4], ones, s4, 0, 0, 0);
+            act_sum_step<5>(a[j], all);
+        }
+    return 128 * s4 - all;
+}
+
 // LDS of the workgroup: the tile sums, and for the quantiser inside (1 to 4
 // tokens of fp32 / bf16 input) the per-wave rounding areas and maxima.
 struct GroupLds {
@@ -246,10 +300,14 @@ __device__ __forceinline__ float group_job_tiles(const GroupJob &J, int KS, int 
     }
     if (nj == 0) return beta_lane;
 
-    v4i sacc = {0, 0, 0, 0}; // sum_k q of the wave's k-steps (offset codes)
+    v4i sacc = {0, 0, 0, 0}; // sum_k q of the wave's k-steps (offset codes); b3: b3_level_fix
+    if constexpr (LAYOUT == LAYOUT_B3) {
+        sacc = b3_level_fix<SPW>(a, nj);
+    } else {
 #pragma unroll
-    for (int j = 0; j < SPW; ++j)
-        if (j < nj) act_sum_step<NMF>(a[j], sacc);
+        for (int j = 0; j < SPW; ++j)
+            if (j < nj) act_sum_step<NMF>(a[j], sacc);
+    }
     // Unrolled over the most tiles a workgroup takes (a compile-time
     // recursion, so no loop is left): a loop back-edge would make the
     // compiler wait for every load in flight at each trip (it moves ring
@@ -266,6 +324,14 @@ __device__ __forceinline__ float group_job_tiles(const GroupJob &J, int KS, int 
                 i2_scaled_step(b[t % D][j], a[j], acc);
             }
             part = acc.a1 + (acc.a4 >> 2) + ((acc.a16a + acc.a16b) >> 4) - sacc;
+        } else if constexpr (LAYOUT == LAYOUT_B3) {
+            B3LevelAcc acc{{0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+            for (int j = 0; j < SPW; ++j) {
+                if (j >= nj) break;
+                b3_level_step(b[t % D][j], a[j], acc);
+            }
+            part = acc.p - 3 * acc.m + sacc;
         } else {
             v4i acc[1] = {v4i{0, 0, 0, 0}};
 #pragma unroll
