@@ -64,6 +64,12 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="time the straight-through-estimator backward (dX and dW) of the workload's forwards "
                          "instead of the forward, and print its own JSON line")
+    ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "addsub"],
+                    help="single mode: the product algorithm of every forward (auto: the library's choice; mfma: "
+                         "the matrix-core GEMV; addsub: the vector-ALU add/subtract GEMV, i2 and M <= 16)")
+    ap.add_argument("--int8-input", action="store_true",
+                    help="feed every forward activations quantised once beforehand (x_dtype I8 with beta), so a "
+                         "step times the product kernels alone (not with --workload stack_3b_26)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill GEMM sub-object")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -205,6 +211,16 @@ def main():
     layout = ctx.layout
     batches = tuple(int(b) for b in args.batches.split(",")) if args.batches else wl.batches
     mode = "single" if wl is workloads.STACK_3B else args.mode
+    algo = {"auto": bl.ALGO_AUTO, "mfma": bl.ALGO_GEMV_MFMA, "addsub": bl.ALGO_GEMV_ADDSUB}[args.algo]
+    if algo != bl.ALGO_AUTO and mode != "single":
+        print("--algo other than auto needs --mode single", file=sys.stderr)
+        sys.exit(2)
+    if args.int8_input and mode != "single":
+        print("--int8-input needs --mode single (a grouped call quantises its float inputs itself)", file=sys.stderr)
+        sys.exit(2)
+    if args.int8_input and wl is workloads.STACK_3B:
+        print("--int8-input does not apply to the stack (its links requantise fp32 outputs)", file=sys.stderr)
+        sys.exit(2)
     log(f"workload={wl.name} batches={batches} layout={args.layout} mode={mode}")
 
     # ---- weights ----------------------------------------------------------------
@@ -247,6 +263,11 @@ def main():
     for j in jobs:
         lay = j["L"]["layer"]
         j["x_dtype"] = bl.F32 if j["x"].dtype == torch.float32 else bl.BF16
+        j["beta"] = None
+        if args.int8_input:
+            with torch.cuda.stream(ctx.stream):
+                j["x"], j["beta"] = bl.quantize_act(j["x"], stream=ctx.stream)
+            j["x_dtype"] = bl.I8
         nws = bl.bitlinear_forward_workspace_bytes(j["M"], lay.N, lay.K, layout, j["x_dtype"])
         j["nws"] = nws
         j["ws"] = torch.empty(max(nws, 16), dtype=torch.uint8, device=ctx.dev)
@@ -298,9 +319,11 @@ def main():
             return
         j = call[0]
         L, lay = j["L"], j["L"]["layer"]
-        st = bl.bitlinear_forward(L["P"][copy].data_ptr(), layout, L["gamma"].data_ptr(), j["M"], lay.N, lay.K,
-                                  j["x"].data_ptr(), j["x_dtype"], j["x"].stride(0), None, j["y"].data_ptr(), bl.F32,
-                                  j["y"].stride(0), j["ws"].data_ptr() if j["nws"] > 0 else None, j["nws"], s_)
+        st = bl.bitlinear_forward_algo(L["P"][copy].data_ptr(), layout, L["gamma"].data_ptr(), j["M"], lay.N, lay.K,
+                                       j["x"].data_ptr(), j["x_dtype"], j["x"].stride(0),
+                                       j["beta"].data_ptr() if j["beta"] is not None else None, j["y"].data_ptr(),
+                                       bl.F32, j["y"].stride(0), j["ws"].data_ptr() if j["nws"] > 0 else None,
+                                       j["nws"], algo, s_)
         if st:
             raise bl.BitlinearError(st, "bitlinear_forward")
 
@@ -336,13 +359,13 @@ def main():
     per_kernel = {}
     call_us = []
     for ci, call in enumerate(calls):
-        kname, one_launch = call_kernel(ctx, call, mode, layout)
+        kname, one_launch = call_kernel(ctx, call, mode, layout, algo)
         ms_call = time_launches(ctx, lambda i, ci=ci: launch_call(ci, i % ncopies), ncopies)
         call_us.append(round(ms_call * 1e3, 3))
         if one_launch:
             ms = ms_call
         elif mode == "single":
-            ms = time_product_only(ctx, call[0], layout, ncopies)
+            ms = time_product_only(ctx, call[0], layout, ncopies, algo)
         else:
             ms = None  # the grouped product behind a quantiser launch: counted in the call time only
         if ms is None:
@@ -413,6 +436,8 @@ def main():
             "bitlinears_per_step": len(jobs),
             "calls_per_step": len(calls),
             "mode": mode,
+            **({"algo": args.algo} if algo != bl.ALGO_AUTO else {}),
+            **({"input": "int8 activations and beta quantised before the timed steps"} if args.int8_input else {}),
             "y_dtype": "f32",
             "weight_copies": ncopies,
             "rotation_bytes": int(ncopies * (bytes_per_call if chain is None else set_bytes)),
@@ -442,7 +467,7 @@ def roofline(bound, d):
             "frac": round(achieved / INT8_PEAK_TOPS, 4)}
 
 
-def call_kernel(ctx, call, mode, layout):
+def call_kernel(ctx, call, mode, layout, algo):
     """(name of the product kernel of a call, whether the call is that one
     launch)."""
     bl = ctx.bl
@@ -454,8 +479,8 @@ def call_kernel(ctx, call, mode, layout):
         return name, one
     j = call[0]
     lay = j["L"]["layer"]
-    name = bl.bitlinear_product_kernel(j["M"], lay.N, lay.K, layout, j["x_dtype"], bl.ALGO_AUTO)
-    return name, name.startswith(("bl::k_gemv_fq<", "bl::k_gemv_persist_fq<"))
+    name = bl.bitlinear_product_kernel(j["M"], lay.N, lay.K, layout, j["x_dtype"], algo)
+    return name, j["x_dtype"] == bl.I8 or name.startswith(("bl::k_gemv_fq<", "bl::k_gemv_persist_fq<"))
 
 
 def product_bytes(bl, j, layout, one_launch):
@@ -464,17 +489,18 @@ def product_bytes(bl, j, layout, one_launch):
     itself, else int8 and beta), gamma, and the fp32 output."""
     lay = j["L"]["layer"]
     es = 4 if j["x_dtype"] == bl.F32 else 2
-    x = j["M"] * lay.K * es if one_launch else j["M"] * lay.K + 4 * j["M"]
+    x = j["M"] * lay.K * es if one_launch and j["x_dtype"] != bl.I8 else j["M"] * lay.K + 4 * j["M"]
     return bl.bitlinear_packed_bytes(lay.N, lay.K, layout) + x + 4 + 4 * j["M"] * lay.N
 
 
-def time_product_only(ctx, j, layout, ncopies):
+def time_product_only(ctx, j, layout, ncopies, algo):
     """The product kernel of a single forward alone: its activations quantised
     once beforehand (through the split entry points), then the forward on
     int8 input, rotating over the weight copies."""
     torch, bl = ctx.torch, ctx.bl
     L, lay, M = j["L"], j["L"]["layer"], j["M"]
-    algo = bl.bitlinear_auto_algo(M, lay.N, lay.K, layout, j["x_dtype"])
+    if algo == bl.ALGO_AUTO:
+        algo = bl.bitlinear_auto_algo(M, lay.N, lay.K, layout, j["x_dtype"])
     tiled = algo == bl.ALGO_GEMV_MFMA and M > 4 and lay.K <= 65536
     beta = torch.empty(M, dtype=torch.float32, device=ctx.dev)
     s_ = ctx.stream.cuda_stream
@@ -551,7 +577,7 @@ def run_prefill(ctx, args):
     for j in jobs:
         lay = j["L"]["layer"]
         kname = bl.bitlinear_product_kernel(M, lay.N, lay.K, ctx.layout, bl.I8, bl.ALGO_AUTO)
-        ms = time_product_only(ctx, j, ctx.layout, ncopies)
+        ms = time_product_only(ctx, j, ctx.layout, ncopies, bl.ALGO_AUTO)
         d["ms"] += ms
         d["ops"] += 2 * M * lay.N * lay.K
         d["bytes"] += product_bytes(bl, j, ctx.layout, False)
