@@ -68,12 +68,14 @@ __device__ __forceinline__ void lds_barrier()
 }
 } // namespace
 
-// Weight tiles in flight per wave for a job of SPW k-steps per wave: as many
-// as the registers left next to the activation operands hold without
-// spilling (about 8-12 KB per wave).
+// Weight tiles in flight per wave for a job of SPW k-steps per wave: at most
+// what the registers left next to the activation operands hold without
+// spilling.  i2 with one k-step per wave keeps 6 of the 10 that would fit:
+// with every tile of a workgroup asked for at once the 3B calls took 13.1 us
+// (one token) against 12.5 us with 5 or 6 in flight, refilled as tiles finish.
 constexpr int group_depth(int layout, int spw)
 {
-    return layout == LAYOUT_I2 ? (spw == 1 ? 10 : (spw == 2 ? 4 : 2))
+    return layout == LAYOUT_I2 ? (spw == 1 ? 6 : (spw == 2 ? 4 : 2))
            : layout == LAYOUT_B3 ? (spw == 1 ? 8 : (spw == 2 ? 4 : 2))
                                  : (spw == 1 ? 5 : 2);
 }
