@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--int8-input", action="store_true",
                     help="feed every forward activations quantised once beforehand (x_dtype I8 with beta), so a "
                          "step times the product kernels alone (not with --workload stack_3b_26)")
+    ap.add_argument("--f1", action="store_true",
+                    help="stack_3b_26: run every link through bitlinear_forward_chain, whose product writes the "
+                         "per-token maxima of the next link's input and whose quantiser takes beta from them")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill GEMM sub-object")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -218,6 +221,9 @@ def main():
     if args.int8_input and mode != "single":
         print("--int8-input needs --mode single (a grouped call quantises its float inputs itself)", file=sys.stderr)
         sys.exit(2)
+    if args.f1 and wl is not workloads.STACK_3B:
+        print("--f1 applies to --workload stack_3b_26", file=sys.stderr)
+        sys.exit(2)
     if args.int8_input and wl is workloads.STACK_3B:
         print("--int8-input does not apply to the stack (its links requantise fp32 outputs)", file=sys.stderr)
         sys.exit(2)
@@ -271,6 +277,17 @@ def main():
         nws = bl.bitlinear_forward_workspace_bytes(j["M"], lay.N, lay.K, layout, j["x_dtype"])
         j["nws"] = nws
         j["ws"] = torch.empty(max(nws, 16), dtype=torch.uint8, device=ctx.dev)
+    if args.f1:
+        # producer-side maxima: link l's product writes them over link l+1's K
+        for ji, j in enumerate(jobs):
+            lay = j["L"]["layer"]
+            j["parts"] = bl.bitlinear_forward_chain_parts(j["M"], lay.N, lay.K, layout)
+            last = ji + 1 == len(jobs)
+            j["pmax"] = None if last else torch.empty(j["parts"] * 16, dtype=torch.float32, device=ctx.dev)
+            j["pmax_cols"] = 0 if last else jobs[ji + 1]["L"]["layer"].K
+        for ji, j in enumerate(jobs):
+            j["pmax_in"] = jobs[ji - 1]["pmax"] if ji > 0 else None
+            j["nparts_in"] = jobs[ji - 1]["parts"] if ji > 0 else 0
     if mode == "grouped":
         calls = [[j for j in jobs if j["M"] == M] for M in batches]
     else:
@@ -319,6 +336,16 @@ def main():
             return
         j = call[0]
         L, lay = j["L"], j["L"]["layer"]
+        if args.f1:
+            st = bl.bitlinear_forward_chain(
+                L["P"][copy].data_ptr(), layout, L["gamma"].data_ptr(), j["M"], lay.N, lay.K, j["x"].data_ptr(),
+                j["x_dtype"], j["x"].stride(0), j["pmax_in"].data_ptr() if j["pmax_in"] is not None else None,
+                j["nparts_in"], j["y"].data_ptr(), bl.F32, j["y"].stride(0),
+                j["pmax"].data_ptr() if j["pmax"] is not None else None, j["pmax_cols"], j["ws"].data_ptr(), j["nws"],
+                s_)
+            if st:
+                raise bl.BitlinearError(st, "bitlinear_forward_chain")
+            return
         st = bl.bitlinear_forward_algo(L["P"][copy].data_ptr(), layout, L["gamma"].data_ptr(), j["M"], lay.N, lay.K,
                                        j["x"].data_ptr(), j["x_dtype"], j["x"].stride(0),
                                        j["beta"].data_ptr() if j["beta"] is not None else None, j["y"].data_ptr(),
@@ -438,6 +465,8 @@ def main():
             "mode": mode,
             **({"algo": args.algo} if algo != bl.ALGO_AUTO else {}),
             **({"input": "int8 activations and beta quantised before the timed steps"} if args.int8_input else {}),
+            **({"f1": "bitlinear_forward_chain: each product writes per-workgroup maxima of the next link's input, "
+                      "the next quantiser takes beta from them"} if args.f1 else {}),
             "y_dtype": "f32",
             "weight_copies": ncopies,
             "rotation_bytes": int(ncopies * (bytes_per_call if chain is None else set_bytes)),

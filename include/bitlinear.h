@@ -326,6 +326,42 @@ int bitlinear_forward_noalloc(const uint8_t *P, int layout, const float *gamma, 
                               int64_t ldy, void *stream);
 
 /*
+ * One link of a chain of BitLinears whose per-token activation maxima come
+ * from the producer: the per-token absmax of the 8-bit activation quantiser
+ * (LIT-380 record, Key takeaways, bullet 1) taken in the epilogue of the
+ * product that writes the activations, the fusion across layers the
+ * HackerPapers digest's thread "Scalable MatMul-Free Language Modeling"
+ * discusses.  The forward of bitlinear_forward (the tiled quantiser, then the
+ * matrix-core GEMV) for M <= 16 tokens of fp32 / bf16 X, with two optional
+ * additions:
+ *   pmax_in, nparts_in  nparts_in x 16 floats (device, read-only) written by
+ *        the previous link's pmax_out over exactly the K columns X holds; beta_m
+ *        is then their maximum over the parts (bit-identical to the absmax of
+ *        the row) and the quantiser makes one pass over X instead of two.
+ *        NULL and 0 for none.
+ *   pmax_out, pmax_cols  bitlinear_forward_chain_parts(M, N, K, layout) x 16
+ *        floats (device, written): entry p * 16 + m is the maximum of |Y[m][n]|
+ *        as stored (fp32 or bf16) over the columns n < pmax_cols that
+ *        workgroup p of the product wrote (0 for tokens m >= M), written with
+ *        plain stores, no atomics.  pmax_cols (1 <= pmax_cols <= N) is the next
+ *        link's K (it reads Y[:, :pmax_cols]).  NULL and 0 for none; y_dtype
+ *        must be F32 or BF16 with pmax_out.
+ * The other arguments, the workspace (bitlinear_forward_workspace_bytes) and
+ * the results are those of bitlinear_forward; outputs are bit-identical to it.
+ * Returns UNSUPPORTED for M > 16 or K > 65536, INVALID_ARG for the argument
+ * errors of bitlinear_forward, a misaligned or overlapping pmax buffer,
+ * pmax_cols out of range, or pmax_in and nparts_in not given together.
+ */
+int bitlinear_forward_chain(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                            const void *X, int x_dtype, int64_t ldx, const float *pmax_in, int64_t nparts_in,
+                            void *Y, int y_dtype, int64_t ldy, float *pmax_out, int64_t pmax_cols, void *ws,
+                            int64_t ws_bytes, void *stream);
+
+/* Parts (workgroups) of bitlinear_forward_chain's product for these sizes: its
+ * pmax_out holds that many x 16 floats.  -1 if M > 16, K > 65536 or invalid. */
+int64_t bitlinear_forward_chain_parts(int64_t M, int64_t N, int64_t K, int layout);
+
+/*
  * Grouped forward: several BitLinears in one call, the way a decode step runs
  * the layers of a model (q, k, v and o; gate, up and down).  Each BitLinear's
  * weights are only a few MB, so alone its product cannot fill the chip before

@@ -80,6 +80,9 @@ _SIGNATURES = {
     "bitlinear_quantize_weights": ([_P, _I64, _I64, _I64, _P, _P, _P, _I64, _P], _INT),
     "bitlinear_binarize_weights": ([_P, _I64, _I64, _I64, _P, _P, _P, _I64, _P], _INT),
     "bitlinear_pack": ([_P, _I64, _I64, _I64, _INT, _P, _P], _INT),
+    "bitlinear_forward_chain": ([_P, _INT, _P, _I64, _I64, _I64, _P, _INT, _I64, _P, _I64, _P, _INT, _I64, _P, _I64,
+                                 _P, _I64, _P], _INT),
+    "bitlinear_forward_chain_parts": ([_I64, _I64, _I64, _INT], _I64),
     "bitlinear_transcode_i2": ([_P, _INT, _I64, _I64, _P, _P], _INT),
     "bitlinear_quantize_act": ([_P, _INT, _I64, _I64, _I64, _P, _I64, _P, _P], _INT),
     "bitlinear_forward": ([_P, _INT, _P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P, _INT, _I64, _P, _I64, _P], _INT),
@@ -181,6 +184,16 @@ def bitlinear_backward_dw(Xq, ldq, beta, M, N, K, dY, lddy, dW, lddw, stream) ->
 
 def bitlinear_pack(T, N, K, ldt, layout, P, stream) -> int:
     return _lib.bitlinear_pack(T, N, K, ldt, layout, P, stream)
+
+
+def bitlinear_forward_chain(P, layout, gamma, M, N, K, X, x_dtype, ldx, pmax_in, nparts_in, Y, y_dtype, ldy, pmax_out,
+                            pmax_cols, ws, ws_bytes, stream) -> int:
+    return _lib.bitlinear_forward_chain(P, layout, gamma, M, N, K, X, x_dtype, ldx, pmax_in, nparts_in, Y, y_dtype,
+                                        ldy, pmax_out, pmax_cols, ws, ws_bytes, stream)
+
+
+def bitlinear_forward_chain_parts(M, N, K, layout) -> int:
+    return _lib.bitlinear_forward_chain_parts(M, N, K, layout)
 
 
 def bitlinear_transcode_i2(P, layout, N, K, P2, stream) -> int:
@@ -290,6 +303,30 @@ def pack(T, layout: int = LAYOUT_I2, stream=None):
     P = torch.empty(nbytes, dtype=torch.uint8, device=T.device)
     _check(bitlinear_pack(_ptr(T), N, K, T.stride(0), layout, _ptr(P), _stream(stream)), "bitlinear_pack")
     return P
+
+
+def forward_chain(P, layout: int, gamma, X, N: int, K: int | None = None, pmax_in=None, pmax_cols: int = 0,
+                  y_dtype=None, out=None, stream=None):
+    """One link of a chain (bitlinear_forward_chain): X [M <= 16 x >=K] fp32/bf16; pmax_in the previous link's
+    partial maxima (or None); with pmax_cols > 0 also returns this link's partial maxima over Y[:, :pmax_cols].
+    Returns (Y, pmax_out or None)."""
+    torch = _torch()
+    M = X.shape[0]
+    K = X.shape[1] if K is None else K
+    if out is None:
+        out = torch.empty((M, N), dtype=y_dtype or torch.float32, device=X.device)
+    xdt = _dtype_code(X)
+    nws = bitlinear_forward_workspace_bytes(M, N, K, layout, xdt)
+    parts = bitlinear_forward_chain_parts(M, N, K, layout)
+    if nws < 0 or parts < 0:
+        raise BitlinearError(ERR_INVALID_ARG, "forward_chain")
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=X.device)
+    pmax_out = torch.empty(parts * 16, dtype=torch.float32, device=X.device) if pmax_cols > 0 else None
+    nparts_in = pmax_in.numel() // 16 if pmax_in is not None else 0
+    _check(bitlinear_forward_chain(_ptr(P), layout, _ptr(gamma), M, N, K, _ptr(X), xdt, X.stride(0), _ptr(pmax_in),
+                                   nparts_in, _ptr(out), _dtype_code(out), out.stride(0), _ptr(pmax_out), pmax_cols,
+                                   _ptr(ws), nws, _stream(stream)), "bitlinear_forward_chain")
+    return out, pmax_out
 
 
 def transcode_i2(P, layout: int, N: int, K: int, stream=None):

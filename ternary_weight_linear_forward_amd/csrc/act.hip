@@ -260,7 +260,8 @@ namespace bl {
 template <int XDT, int PPT>
 __device__ __forceinline__ void quant_tiled_row(const void *__restrict__ X, int64_t M, int64_t K, int64_t ldx,
                                                 int layout, int64_t nsteps, int8_t *__restrict__ Xt,
-                                                float *__restrict__ beta, int64_t m, float *red)
+                                                float *__restrict__ beta, int64_t m, float *red,
+                                                const float *__restrict__ pmax = nullptr, int64_t nparts = 0)
 {
     constexpr int ES = XDT == DT_F32 ? 4 : 2;
     const int64_t step_k = layout == LAYOUT_I2 ? 256 : (layout == LAYOUT_B3 ? 320 : 512), kblk = step_k / 4;
@@ -301,9 +302,16 @@ __device__ __forceinline__ void quant_tiled_row(const void *__restrict__ X, int6
             for (int e = 0; e < 16; ++e)
                 v[j][e] = (live_row && p < npieces && k0 + e < K) ? load_x<XDT>(X, m * ldx + k0 + e) : 0.0f;
         }
+        if (pmax == nullptr) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
+            for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
+        }
     }
+    // producer-side maxima (the previous product's epilogue wrote each of its
+    // workgroups' maximum of |x| per token over exactly these K columns): the
+    // row maximum without a pass over the values
+    if (pmax != nullptr && live_row)
+        for (int64_t p = threadIdx.x; p < nparts; p += blockDim.x) amax = fmaxf(amax, pmax[p * 16 + i]);
     const float b = block_max(amax, red);
     const TokenQuant s = token_quant(b);
 #pragma unroll
@@ -324,10 +332,11 @@ __device__ __forceinline__ void quant_tiled_row(const void *__restrict__ X, int6
 template <int XDT, int PPT>
 __global__ __launch_bounds__(1024) void k_quant_act_tiled(const void *__restrict__ X, int64_t M, int64_t K,
                                                          int64_t ldx, int layout, int64_t nsteps,
-                                                         int8_t *__restrict__ Xt, float *__restrict__ beta)
+                                                         int8_t *__restrict__ Xt, float *__restrict__ beta,
+                                                         const float *__restrict__ pmax, int64_t nparts)
 {
     __shared__ float red[16];
-    quant_tiled_row<XDT, PPT>(X, M, K, ldx, layout, nsteps, Xt, beta, blockIdx.x, red);
+    quant_tiled_row<XDT, PPT>(X, M, K, ldx, layout, nsteps, Xt, beta, blockIdx.x, red, pmax, nparts);
 }
 
 // Several inputs in one launch (the grouped forward): workgroup (m, u)
@@ -372,14 +381,14 @@ hipError_t launch_group_quant(const GroupQuantArgs &args, int x_dtype, hipStream
 
 template <int XDT>
 static bool launch_tiled_ppt(const void *X, int64_t M, int64_t K, int64_t ldx, int layout, int8_t *Xt, float *beta,
-                             hipStream_t stream)
+                             const float *pmax, int64_t nparts, hipStream_t stream)
 {
     const int64_t nsteps = tiled_nsteps(K, layout);
     const int64_t npieces = nsteps * tiled_step_k(layout) / 16;
     const int64_t threads = npieces >= 1024 ? 1024 : (npieces + 63) / 64 * 64;
     const int64_t ppt = (npieces + threads - 1) / threads;
     dim3 grid(static_cast<unsigned>((M + 15) / 16 * 16)), block(static_cast<unsigned>(threads));
-#define BL_TILED(N) hipLaunchKernelGGL((k_quant_act_tiled<XDT, N>), grid, block, 0, stream, X, M, K, ldx, layout, nsteps, Xt, beta)
+#define BL_TILED(N) hipLaunchKernelGGL((k_quant_act_tiled<XDT, N>), grid, block, 0, stream, X, M, K, ldx, layout, nsteps, Xt, beta, pmax, nparts)
     // (K <= 65536 for the tiled layout: at most 4096 pieces for i2 and b1,
     // 4100 for b3, whose last few take the 8-piece variant)
     if (ppt <= 1) BL_TILED(1);
@@ -392,10 +401,10 @@ static bool launch_tiled_ppt(const void *X, int64_t M, int64_t K, int64_t ldx, i
 }
 
 hipError_t launch_quant_act_tiled(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int layout,
-                                  int8_t *Xt, float *beta, hipStream_t stream)
+                                  int8_t *Xt, float *beta, hipStream_t stream, const float *pmax, int64_t nparts)
 {
-    const bool ok = x_dtype == DT_F32 ? launch_tiled_ppt<DT_F32>(X, M, K, ldx, layout, Xt, beta, stream)
-                                      : launch_tiled_ppt<DT_BF16>(X, M, K, ldx, layout, Xt, beta, stream);
+    const bool ok = x_dtype == DT_F32 ? launch_tiled_ppt<DT_F32>(X, M, K, ldx, layout, Xt, beta, pmax, nparts, stream)
+                                      : launch_tiled_ppt<DT_BF16>(X, M, K, ldx, layout, Xt, beta, pmax, nparts, stream);
     return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 

@@ -750,6 +750,73 @@ int bitlinear_forward_noalloc(const uint8_t *P, int layout, const float *gamma, 
                         nullptr, BITLINEAR_ALGO_AUTO, stream);
 }
 
+int64_t bitlinear_forward_chain_parts(int64_t M, int64_t N, int64_t K, int layout)
+{
+    if (M < 1 || M > 16 || N < 1 || N > (int64_t(1) << 31) || K < 1 || K > kTiledMaxK || !valid_layout(layout))
+        return -1;
+    return bl::gemv_mfma_parts(layout, M, N, K);
+}
+
+int bitlinear_forward_chain(const uint8_t *P, int layout, const float *gamma, int64_t M, int64_t N, int64_t K,
+                            const void *X, int x_dtype, int64_t ldx, const float *pmax_in, int64_t nparts_in,
+                            void *Y, int y_dtype, int64_t ldy, float *pmax_out, int64_t pmax_cols, void *ws,
+                            int64_t ws_bytes, void *stream)
+{
+    if (x_dtype != BITLINEAR_F32 && x_dtype != BITLINEAR_BF16) return BITLINEAR_ERR_INVALID_ARG;
+    // every check of the plain forward (workspace alignment and overlaps included)
+    const int st0 = forward_impl(P, layout, gamma, M, N, K, X, x_dtype, ldx, nullptr, Y, y_dtype, ldy, ws, ws_bytes,
+                                 nullptr, 0, nullptr, BITLINEAR_ALGO_GEMV_MFMA, stream, true);
+    if (st0 != BITLINEAR_OK) return st0;
+    if (M > 16 || K > kTiledMaxK) return BITLINEAR_ERR_UNSUPPORTED;
+    const int64_t need = bitlinear_forward_workspace_bytes(M, N, K, layout, x_dtype);
+    if (!ws || ws_bytes < need) return BITLINEAR_ERR_WORKSPACE;
+    if ((pmax_in != nullptr) != (nparts_in > 0) || nparts_in < 0 || (reinterpret_cast<uintptr_t>(pmax_in) & 3u))
+        return BITLINEAR_ERR_INVALID_ARG;
+    const int64_t parts = bl::gemv_mfma_parts(layout, M, N, K);
+    const Span sy = span_of(Y, M, ldy, N, dtype_size(y_dtype)), sw = span_of(ws, 1, need, need, 1);
+    if (pmax_in) {
+        const Span si = span_of(pmax_in, 1, nparts_in * 16, nparts_in * 16, 4);
+        if (overlap(si, sy) || overlap(si, sw)) return BITLINEAR_ERR_INVALID_ARG;
+    }
+    if (pmax_out) {
+        if (y_dtype == BITLINEAR_I32 || pmax_cols < 1 || pmax_cols > N || (reinterpret_cast<uintptr_t>(pmax_out) & 3u))
+            return BITLINEAR_ERR_INVALID_ARG;
+        const int64_t pb = bitlinear_packed_bytes(N, K, layout);
+        const Span so = span_of(pmax_out, 1, parts * 16, parts * 16, 4);
+        const Span others[] = {sy, sw, span_of(P, 1, pb, pb, 1), span_of(X, M, ldx, K, dtype_size(x_dtype)),
+                               span_of(gamma, 1, 1, 1, 4)};
+        for (const Span &o : others)
+            if (overlap(so, o)) return BITLINEAR_ERR_INVALID_ARG;
+        if (pmax_in && overlap(so, span_of(pmax_in, 1, nparts_in * 16, nparts_in * 16, 4)))
+            return BITLINEAR_ERR_INVALID_ARG;
+    } else if (pmax_cols != 0) {
+        return BITLINEAR_ERR_INVALID_ARG;
+    }
+    (void)hipGetLastError();
+    hipStream_t st = as_stream(stream);
+    int8_t *xq = static_cast<int8_t *>(ws);
+    float *beta = reinterpret_cast<float *>(static_cast<char *>(ws) + staged_xq_bytes(M, K, layout));
+    hipError_t e = bl::launch_quant_act_tiled(X, x_dtype, M, K, ldx, layout, xq, beta, st, pmax_in, nparts_in);
+    if (e != hipSuccess) return BITLINEAR_ERR_LAUNCH;
+    bl::GemvArgs a;
+    a.P = P;
+    a.layout = layout;
+    a.gamma = gamma;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.Xq = xq;
+    a.ldq = 0;
+    a.tiled = true;
+    a.beta = beta;
+    a.Y = Y;
+    a.y_dtype = y_dtype;
+    a.ldy = ldy;
+    a.pmax = pmax_out;
+    a.pmax_cols = pmax_out ? pmax_cols : 0;
+    return status_of(bl::launch_gemv_mfma(a, st));
+}
+
 // i2 rewrite of b3 / b1 weights, then the small-batch dX's partial tiles
 static int64_t bwd_dx_rewrite_bytes(int64_t N, int64_t K, int layout)
 {

@@ -123,6 +123,14 @@ __device__ __forceinline__ void store_out(void *Y, int y_dtype, int64_t ldy, int
     }
 }
 
+// |y| of one output element exactly as store_out stores it (fp32 or bf16).
+__device__ __forceinline__ float stored_abs(int y_dtype, int acc, float r)
+{
+    const float y = static_cast<float>(acc) * r;
+    if (y_dtype == DT_F32) return fabsf(y);
+    return __uint_as_float((static_cast<uint32_t>(float_to_bf16_rne(y)) & 0x7fffu) << 16);
+}
+
 // Lane-wise product of two pairs of 16-bit integers (low 16 bits kept).
 __device__ __forceinline__ uint32_t pk_mul_u16(uint32_t a, uint32_t b)
 {

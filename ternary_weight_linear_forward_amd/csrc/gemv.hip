@@ -61,12 +61,37 @@ __device__ __forceinline__ v4i load_a16(const int8_t *__restrict__ Xq, int64_t l
 // up to 16 waves per CU this keeps ~100 KB of weights in flight per CU.  The
 // KS partial tiles are summed through LDS; wave t < TW writes tile t.
 // ---------------------------------------------------------------------------
+// Per-token maxima of |Y| as stored, for the next product's quantiser (the
+// producer side of the per-token absmax): lm[rr] is this lane's maximum for
+// token 4g + rr; the 16 lanes of a group (rows i) combine by shuffles, the
+// waves through LDS, and wave 0 writes the workgroup's 16 maxima to
+// pmax[blockIdx.x * 16 + token] with plain stores (tokens past M hold 0).
+// Every wave of the workgroup must call it (a barrier).
+__device__ __forceinline__ void write_token_maxima(float (&lm)[4], float *__restrict__ pmax, float (*pm)[16])
+{
+    const int wave = wave_id(), lane = lane_id(), KS = blockDim.x >> 6;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) lm[rr] = fmaxf(lm[rr], __shfl_xor(lm[rr], off));
+    if ((lane & 15) == 0)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) pm[wave][4 * (lane >> 4) + rr] = lm[rr];
+    __syncthreads();
+    if (wave == 0 && lane < 16) {
+        float mx = pm[0][lane];
+        for (int w = 1; w < KS; ++w) mx = fmaxf(mx, pm[w][lane]);
+        pmax[static_cast<int64_t>(blockIdx.x) * 16 + lane] = mx;
+    }
+}
+
 template <int LAYOUT, int TW, int SB, bool TILED>
 __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ P, int64_t KB, int64_t NT,
                                                     const float *__restrict__ gamma_p,
                                                     const int8_t *__restrict__ Xq, int64_t ldq,
                                                     const float *__restrict__ beta, int64_t M, int64_t N,
-                                                    int64_t K, void *__restrict__ Y, int y_dtype, int64_t ldy)
+                                                    int64_t K, void *__restrict__ Y, int y_dtype, int64_t ldy,
+                                                    float *__restrict__ pmax, int64_t pmax_cols)
 {
     using S = StepShape<LAYOUT>;
     constexpr int NMF = S::NMF, KBLK = S::KBLK;
@@ -186,6 +211,7 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
     for (int t = 0; t < TW; ++t) red[t][wave][lane] = kOffsetCodes<LAYOUT> ? offset_fix<LAYOUT>(acc[t], sacc) : acc[t];
     __syncthreads();
     // tile t is finished by wave t % KS (KS may be smaller than TW)
+    float lm[4] = {0.0f, 0.0f, 0.0f, 0.0f}; // |Y| maxima per token (pmax)
     for (int t = wave; t < TW; t += KS) {
         const int64_t tile = tile0 + t;
         if (tile >= NT) break;
@@ -196,8 +222,15 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const int64_t mm = static_cast<int64_t>(blockIdx.y) * 16 + 4 * g + rr;
-            if (mm < M && n < N) store_out(Y, y_dtype, ldy, mm, n, tot[rr], sc[rr]);
+            if (mm < M && n < N) {
+                store_out(Y, y_dtype, ldy, mm, n, tot[rr], sc[rr]);
+                if (n < pmax_cols) lm[rr] = fmaxf(lm[rr], stored_abs(y_dtype, tot[rr], sc[rr]));
+            }
         }
+    }
+    if (pmax != nullptr) {
+        __shared__ float pm[16][16];
+        write_token_maxima(lm, pmax, pm);
     }
 }
 
@@ -287,7 +320,8 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const uint8_t *__restrict
                                                        const float *__restrict__ gamma_p,
                                                        const int8_t *__restrict__ Xq, int64_t ldq,
                                                        const float *__restrict__ beta, int64_t M, int64_t N,
-                                                       int64_t K, void *__restrict__ Y, int y_dtype, int64_t ldy)
+                                                       int64_t K, void *__restrict__ Y, int y_dtype, int64_t ldy,
+                                                       float *__restrict__ pmax, int64_t pmax_cols)
 {
     using S = StepShape<LAYOUT>;
     constexpr int NMF = S::NMF, KBLK = S::KBLK;
@@ -388,6 +422,7 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const uint8_t *__restrict
     }
     __syncthreads();
     // output group (t, rr): tokens 4g + rr of this token group, weight row i of tile t
+    float lm[4] = {0.0f, 0.0f, 0.0f, 0.0f}; // |Y| maxima per token (pmax)
     for (int task = wave; task < ntiles * 4; task += KS) {
         const int t = task >> 2, rr = task & 3;
         int tot = 0;
@@ -398,7 +433,18 @@ __global__ __launch_bounds__(1024) void k_gemv_persist(const uint8_t *__restrict
         s_rr = rr == 1 ? sc[1] : s_rr;
         s_rr = rr == 2 ? sc[2] : s_rr;
         s_rr = rr == 3 ? sc[3] : s_rr;
-        if (mm < M && n < N) store_out(Y, y_dtype, ldy, mm, n, tot, s_rr);
+        if (mm < M && n < N) {
+            store_out(Y, y_dtype, ldy, mm, n, tot, s_rr);
+            const float v = n < pmax_cols ? stored_abs(y_dtype, tot, s_rr) : 0.0f;
+            lm[0] = rr == 0 ? fmaxf(lm[0], v) : lm[0];
+            lm[1] = rr == 1 ? fmaxf(lm[1], v) : lm[1];
+            lm[2] = rr == 2 ? fmaxf(lm[2], v) : lm[2];
+            lm[3] = rr == 3 ? fmaxf(lm[3], v) : lm[3];
+        }
+    }
+    if (pmax != nullptr) {
+        __shared__ float pm[16][16];
+        write_token_maxima(lm, pmax, pm);
     }
 }
 
@@ -658,10 +704,10 @@ static void launch_mfma_tw(const GemvArgs &a, int64_t KB, int64_t NT, int64_t ns
     constexpr int SB = 1;
     if (a.tiled)
         hipLaunchKernelGGL((k_gemv_mfma<LAYOUT, TW, SB, true>), grid, block, 0, stream, a.P, KB, NT, a.gamma, a.Xq,
-                           a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
+                           a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy, a.pmax, a.pmax_cols);
     else
         hipLaunchKernelGGL((k_gemv_mfma<LAYOUT, TW, SB, false>), grid, block, 0, stream, a.P, KB, NT, a.gamma, a.Xq,
-                           a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy);
+                           a.ldq, a.beta, a.M, a.N, a.K, a.Y, a.y_dtype, a.ldy, a.pmax, a.pmax_cols);
 }
 
 // Which matrix-core GEMV kernel runs for a shape.  Large layers: persistent
@@ -719,7 +765,7 @@ static void launch_persist_kernel(const GemvArgs &a, int64_t KB, int64_t NT, dim
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(f), hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>(lds));
     hipLaunchKernelGGL(f, grid, block, lds, stream, a.P, KB, NT, a.gamma, a.Xq, a.ldq, a.beta, a.M, a.N, a.K, a.Y,
-                       a.y_dtype, a.ldy);
+                       a.y_dtype, a.ldy, a.pmax, a.pmax_cols);
 }
 
 template <int LAYOUT, int SPW>
@@ -736,6 +782,13 @@ static void launch_persist(const GemvArgs &a, const GemvPlan &p, int64_t KB, int
         if (p.guard) launch_persist_kernel<LAYOUT, SPW, TMAX, false, true>(a, KB, NT, grid, block, lds, stream);
         else launch_persist_kernel<LAYOUT, SPW, TMAX, false, false>(a, KB, NT, grid, block, lds, stream);
     }
+}
+
+int64_t gemv_mfma_parts(int layout, int64_t M, int64_t N, int64_t K)
+{
+    const GemvPlan p = gemv_plan(layout, M, N, K);
+    const int64_t NT = (N + 15) / 16;
+    return p.persist ? p.wgs : (NT + p.tw - 1) / p.tw;
 }
 
 template <int LAYOUT>

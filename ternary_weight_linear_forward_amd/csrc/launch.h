@@ -36,8 +36,11 @@ inline int64_t tiled_bytes(int64_t M, int64_t K, int layout)
     return (M + 15) / 16 * tiled_nsteps(K, layout) * tiled_nmf(layout) * 1024;
 }
 
+// pmax (optional, M <= 16): nparts x 16 producer-side maxima of |x| per token
+// over exactly the K columns; beta is their maximum (no pass over the values).
 hipError_t launch_quant_act_tiled(const void *X, int x_dtype, int64_t M, int64_t K, int64_t ldx, int layout,
-                                  int8_t *Xt, float *beta, hipStream_t stream);
+                                  int8_t *Xt, float *beta, hipStream_t stream, const float *pmax = nullptr,
+                                  int64_t nparts = 0);
 
 // ---- grouped forward (several BitLinears of at most 16 tokens) ------------
 constexpr int GROUP_MAX_INPUTS = 32;
@@ -113,9 +116,17 @@ struct GemvArgs {
     void *Y;
     int y_dtype;
     int64_t ldy;
+    // optional (k_gemv_mfma / k_gemv_persist, one token group): per-workgroup
+    // maxima of |Y| per token over the columns below pmax_cols, written to
+    // pmax[workgroup * 16 + token]
+    float *pmax = nullptr;
+    int64_t pmax_cols = 0;
 };
 
 hipError_t launch_gemv_addsub(const GemvArgs &a, hipStream_t stream);
+// Workgroups along the row tiles of the matrix-core GEMV for one token group
+// (the number of partial maxima it writes with GemvArgs::pmax).
+int64_t gemv_mfma_parts(int layout, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv_mfma(const GemvArgs &a, hipStream_t stream);
 // The matrix-core GEMV with the activation quantiser inside (k_gemv_fq): the
 // whole forward in one launch for 1 to 4 tokens of fp32 / bf16 input X (rows

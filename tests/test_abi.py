@@ -477,3 +477,37 @@ def test_noalloc_rejects_before_any_device_call():
     assert "scratch" in bl.bitlinear_status_string(bl.ERR_SCRATCH)
     assert bl.bitlinear_forward_noalloc(None, bl.LAYOUT_I2, B, 4, 64, 64, C, bl.BF16, 64, None, D, bl.F32, 64,
                                         None) == bl.ERR_INVALID_ARG
+
+
+F_ = 0x70000000  # another far-apart fake address
+
+
+def test_forward_chain_rejects_and_parts():
+    """bitlinear_forward_chain argument checks and the parts query (no launch:
+    every case fails before anything is enqueued)."""
+    f = bl.bitlinear_forward_chain
+    M, N, K = 16, 3200, 3200
+    nws = bl.bitlinear_forward_workspace_bytes(M, N, K, bl.LAYOUT_I2, bl.F32)
+    parts = bl.bitlinear_forward_chain_parts(M, N, K, bl.LAYOUT_I2)
+    assert parts == (N + 15) // 16  # the per-tile GEMV: one workgroup per row tile
+    assert bl.bitlinear_forward_chain_parts(M, 28672, 8192, bl.LAYOUT_I2) <= 256  # persistent
+    assert bl.bitlinear_forward_chain_parts(17, N, K, bl.LAYOUT_I2) == -1
+    assert bl.bitlinear_forward_chain_parts(M, N, 70000, bl.LAYOUT_I2) == -1
+    ok = dict(P=A, layout=bl.LAYOUT_I2, gamma=B, M=M, N=N, K=K, X=C, x_dtype=bl.F32, ldx=K, pmax_in=F_,
+              nparts_in=200, Y=D, y_dtype=bl.F32, ldy=N, pmax_out=F_ + 0x100000, pmax_cols=K, ws=F_ + 0x200000,
+              ws_bytes=nws, stream=None)
+    assert f(**{**ok, "M": 17}) == bl.ERR_UNSUPPORTED
+    assert f(**{**ok, "x_dtype": bl.I8}) == bl.ERR_INVALID_ARG
+    assert f(**{**ok, "ws_bytes": nws - 1}) == bl.ERR_WORKSPACE
+    assert f(**{**ok, "ws": None}) == bl.ERR_WORKSPACE
+    assert f(**{**ok, "nparts_in": 0}) == bl.ERR_INVALID_ARG       # pmax_in without parts
+    assert f(**{**ok, "pmax_in": None}) == bl.ERR_INVALID_ARG      # parts without pmax_in
+    assert f(**{**ok, "pmax_in": F_ + 2}) == bl.ERR_INVALID_ARG     # misaligned
+    assert f(**{**ok, "pmax_in": D}) == bl.ERR_INVALID_ARG         # overlaps Y
+    assert f(**{**ok, "y_dtype": bl.I32}) == bl.ERR_INVALID_ARG    # maxima of raw accumulators
+    assert f(**{**ok, "pmax_cols": 0}) == bl.ERR_INVALID_ARG
+    assert f(**{**ok, "pmax_cols": N + 1}) == bl.ERR_INVALID_ARG
+    assert f(**{**ok, "pmax_out": None}) == bl.ERR_INVALID_ARG     # pmax_cols without pmax_out
+    assert f(**{**ok, "pmax_out": D + 64}) == bl.ERR_INVALID_ARG   # overlaps Y
+    assert f(**{**ok, "pmax_out": F_ + 16}) == bl.ERR_INVALID_ARG   # overlaps pmax_in
+    assert f(**{**ok, "pmax_out": F_ + 0x100002}) == bl.ERR_INVALID_ARG  # misaligned
