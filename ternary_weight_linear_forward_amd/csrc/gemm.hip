@@ -531,7 +531,11 @@ namespace {
 // 70B layers, where latency or the b3 decode rather than the matrix cores
 // bounds a tile).  A launch costs about ceil(tiles / 256 CUs) rounds of one
 // tile each.  The 64 x 128 tile serves b3 only: at 64 tokens it decodes each
-// weight tile once instead of twice.
+// weight tile once instead of twice.  The 160 x 256 tile (4 waves of 160 x
+// 64, one wave per SIMD) is slower per tile but packs 2048 x 8640 into two
+// full rounds (442 tiles) where 128 x 256 needs a third, one-eighth full
+// (544 tiles): 86 -> 76 us there, and the cost model keeps 128 x 256 where
+// the tile count fits one round either way.
 struct GemmTile {
     int bm, bn, wm, wn, s; // tile, wave grid, k halves (of 128) per stage
     double rate;
@@ -542,7 +546,8 @@ constexpr GemmTile kTiles[] = {{256, 256, 2, 2, 1, 2.1, true, false, false},
                                {128, 256, 2, 4, 1, 1.95, true, true, true},
                                {128, 128, 2, 2, 1, 1.5, true, true, true},
                                {32, 128, 1, 4, 1, 1.1, true, true, true},
-                               {64, 128, 1, 4, 1, 1.3, false, true, false}};
+                               {64, 128, 1, 4, 1, 1.3, false, true, false},
+                               {160, 256, 1, 4, 1, 1.85, true, false, false}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int64_t kCUs = 256;
 
@@ -587,13 +592,14 @@ void gemm_kernel_name(int layout, int64_t M, int64_t N, char *buf, size_t n)
 
 hipError_t launch_gemm_mfma(const GemvArgs &a, hipStream_t stream)
 {
-    static_assert(kNumTiles == 5, "one case per tile shape");
+    static_assert(kNumTiles == 6, "one case per tile shape");
     switch (best_tile(a.layout, a.M, a.N)) {
     case 0: return launch_entry<0>(a, stream);
     case 1: return launch_entry<1>(a, stream);
     case 2: return launch_entry<2>(a, stream);
     case 3: return launch_entry<3>(a, stream);
-    default: return launch_entry<4>(a, stream);
+    case 4: return launch_entry<4>(a, stream);
+    default: return launch_entry<5>(a, stream);
     }
 }
 

@@ -225,13 +225,14 @@ def test_forward_many_tokens(algo_name, algo, layout, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1100, 5000, 200), (4000, 4000, 130), (2048, 3200, 320), (150, 6000, 300),
-                                   (100, 9000, 200)],
+                                   (100, 9000, 200), (1000, 8640, 330), (2048, 8640, 200)],
                          ids=["tile128x256", "tile256x256_odd_kb", "prefill_rows", "tile32x128_skinny",
-                              "tile32x128_one_block"])
+                              "tile32x128_one_block", "tile160x256_ragged", "tile160x256_prefill_rows"])
 def test_gemm_tile_shapes(M, N, K):
-    """Sizes whose workgroup-tile choice differs (128x256, 256x256 and 32x128
-    tiles, ragged in M and N; an odd number of k-blocks ends in a half stage)."""
-    log("forward gemm tiles", M, N, K)
+    """Sizes whose workgroup-tile choice differs (128x256, 256x256, 160x256 and
+    32x128 tiles, ragged in M and N; an odd number of k-blocks ends in a half
+    stage)."""
+    log("forward gemm tiles", M, N, K, bl.bitlinear_product_kernel(M, N, K, bl.LAYOUT_I2, bl.BF16, bl.ALGO_GEMM_MFMA))
     run_forward_case(M, N, K, bl.ALGO_GEMM_MFMA, "i2", seed=M + 7 * N + K, y_kinds=("i32", "f32"))
     if M * N <= 1100 * 5000:  # base-3 weights, decoded inside the GEMM
         run_forward_case(M, N, K, bl.ALGO_GEMM_MFMA, "b3", seed=M + 7 * N + K + 1, y_kinds=("i32",))
