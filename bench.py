@@ -59,14 +59,17 @@ def parse():
                     help="grouped: the layers of one batch size in one bitlinear_forward_grouped call; "
                          "single: one bitlinear_forward per layer")
     ap.add_argument("--batches", default=None, help="comma list overriding the workload's batch sizes")
+    ap.add_argument("--layers", default=None,
+                    help="comma list of the workload's layer names to keep (e.g. q,k,v,o); not for the stack")
     ap.add_argument("--layout", default="i2", choices=["i2", "b3", "b1"],
                     help="packed weight layout; b1 runs the binary-weight variant (sign quantiser)")
     ap.add_argument("--backward", action="store_true",
                     help="time the straight-through-estimator backward (dX and dW) of the workload's forwards "
                          "instead of the forward, and print its own JSON line")
     ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "addsub"],
-                    help="single mode: the product algorithm of every forward (auto: the library's choice; mfma: "
-                         "the matrix-core GEMV; addsub: the vector-ALU add/subtract GEMV, i2 and M <= 16)")
+                    help="the product algorithm of every forward (auto: the library's choice; mfma: the "
+                         "matrix-core GEMV; addsub: the vector-ALU add/subtract GEMV, i2, M <= 16 in single mode "
+                         "and M = 1 (--batches 1) in grouped mode)")
     ap.add_argument("--int8-input", action="store_true",
                     help="feed every forward activations quantised once beforehand (x_dtype I8 with beta), so a "
                          "step times the product kernels alone (not with --workload stack_3b_26)")
@@ -215,11 +218,14 @@ def main():
     batches = tuple(int(b) for b in args.batches.split(",")) if args.batches else wl.batches
     mode = "single" if wl is workloads.STACK_3B else args.mode
     algo = {"auto": bl.ALGO_AUTO, "mfma": bl.ALGO_GEMV_MFMA, "addsub": bl.ALGO_GEMV_ADDSUB}[args.algo]
-    if algo != bl.ALGO_AUTO and mode != "single":
-        print("--algo other than auto needs --mode single", file=sys.stderr)
+    if algo == bl.ALGO_GEMV_ADDSUB and mode == "grouped" and (set(batches) != {1} or args.layout != "i2"):
+        print("grouped calls take --algo addsub for i2 at one token only (--batches 1)", file=sys.stderr)
         sys.exit(2)
     if args.int8_input and mode != "single":
         print("--int8-input needs --mode single (a grouped call quantises its float inputs itself)", file=sys.stderr)
+        sys.exit(2)
+    if args.layers and wl is workloads.STACK_3B:
+        print("--layers does not apply to the stack (its links follow each other)", file=sys.stderr)
         sys.exit(2)
     if args.f1 and wl is not workloads.STACK_3B:
         print("--f1 applies to --workload stack_3b_26", file=sys.stderr)
@@ -235,7 +241,12 @@ def main():
         specs = [(link.layer, workloads.seed_for(wl, link.index, 0)) for link in chain]
     else:
         chain = None
-        specs = [(layer, workloads.seed_for(wl, li, 0)) for li, layer in enumerate(wl.layers)]
+        names = args.layers.split(",") if args.layers else [l.name for l in wl.layers]
+        unknown = set(names) - {l.name for l in wl.layers}
+        if unknown:
+            print(f"--layers: {sorted(unknown)} not in {wl.name}", file=sys.stderr)
+            sys.exit(2)
+        specs = [(layer, workloads.seed_for(wl, li, 0)) for li, layer in enumerate(wl.layers) if layer.name in names]
     layers, prep_ms, prep_bytes = prep_weights(ctx, wl, specs)
     set_bytes = sum(L["P"][0].numel() for L in layers)
 
@@ -329,10 +340,10 @@ def main():
         if mode == "grouped":
             arr = grouped_arrays(call, copy)
             c = call[0]["call"]
-            st = bl.bitlinear_forward_grouped(arr, len(call), layout, call[0]["x_dtype"], bl.F32,
-                                              c["ws"].data_ptr(), c["nws"], s_)
+            st = bl.bitlinear_forward_grouped_algo(arr, len(call), layout, call[0]["x_dtype"], bl.F32, algo,
+                                                   c["ws"].data_ptr(), c["nws"], s_)
             if st:
-                raise bl.BitlinearError(st, "bitlinear_forward_grouped")
+                raise bl.BitlinearError(st, "bitlinear_forward_grouped_algo")
             return
         j = call[0]
         L, lay = j["L"], j["L"]["layer"]
@@ -503,8 +514,8 @@ def call_kernel(ctx, call, mode, layout, algo):
     if mode == "grouped":
         specs_ = [(j["L"]["P"][0], j["L"]["gamma"], j["x"], j["L"]["layer"].N, j["L"]["layer"].K) for j in call]
         arr, _ = bl.grouped_jobs(specs_, outs=[j["y"] for j in call])
-        name = bl.bitlinear_grouped_kernel(arr, len(call), layout, call[0]["x_dtype"])
-        one = name is not None and name.endswith(f", {call[0]['x_dtype']}>")
+        name = bl.bitlinear_grouped_kernel_algo(arr, len(call), layout, call[0]["x_dtype"], algo)
+        one = name is not None and (name.endswith(f", {call[0]['x_dtype']}>") or "_addsub<" in name)
         return name, one
     j = call[0]
     lay = j["L"]["layer"]

@@ -409,9 +409,49 @@ int bitlinear_forward_grouped(const bitlinear_job_t *jobs, int njobs, int layout
                               void *ws, int64_t ws_bytes, void *stream);
 
 /* Name of the product kernel of the grouped launch for these jobs (as
- * profilers print it, e.g. "bl::k_group_gemv<0, 1>" (the quantiser inside, bf16 input) or "bl::k_group_gemv<0, 2>" (quantised by k_group_quant_tiled first)), or NULL when no job
- * is grouped or the arguments are invalid.  Thread-local storage; host-only. */
+ * profilers print it, e.g. "bl::k_group_gemv<0, 1>" (the quantiser inside,
+ * bf16 input), "bl::k_group_gemv<0, 2>" (quantised by k_group_quant_tiled
+ * first) or "bl::k_group_gemv_addsub<1>" (the vector-ALU products, see
+ * bitlinear_forward_grouped_algo)), or NULL when no job is grouped or the
+ * arguments are invalid.  Thread-local storage; host-only. */
 const char *bitlinear_grouped_kernel(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype);
+
+/*
+ * bitlinear_forward_grouped with the product algorithm chosen by the caller.
+ * The decode product is a sum of activations with weights in {-1, 0, +1}:
+ * integer additions and subtractions only (LIT-380 record, Key takeaways,
+ * the fourth point).  algo:
+ *   BITLINEAR_ALGO_AUTO          what bitlinear_forward_grouped runs: the
+ *                                vector-ALU products when every grouped job
+ *                                is i2 with one token and inputs the launch
+ *                                quantises itself (measured as fast or
+ *                                faster there), else the matrix cores; jobs
+ *                                left out of the grouped launch run as
+ *                                bitlinear_forward;
+ *   BITLINEAR_ALGO_GEMV_MFMA     the int8 matrix-core products;
+ *   BITLINEAR_ALGO_GEMV_ADDSUB   the products on the vector ALU
+ *                                ("bl::k_group_gemv_addsub<x_dtype>"): packed
+ *                                dot products of the 2-bit codes (T + 1, so
+ *                                no multiplier sees a weight other than 0,
+ *                                1, 2 or 3 times a power of two) with the
+ *                                activations, minus their sum; only for i2
+ *                                jobs of one token each, the grouped ones
+ *                                with inputs the launch quantises itself
+ *                                (16-byte aligned rows), else
+ *                                BITLINEAR_ERR_UNSUPPORTED; jobs the grouped
+ *                                launch leaves out (rows too long) run as
+ *                                bitlinear_forward_algo with this algo;
+ *   BITLINEAR_ALGO_GEMM_MFMA     BITLINEAR_ERR_UNSUPPORTED.
+ * Results are bit-identical across algorithms.  Other arguments, workspace
+ * and errors as bitlinear_forward_grouped; nothing is enqueued on an error.
+ */
+int bitlinear_forward_grouped_algo(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype, int y_dtype,
+                                   int algo, void *ws, int64_t ws_bytes, void *stream);
+
+/* bitlinear_grouped_kernel for bitlinear_forward_grouped_algo with this algo
+ * (NULL also where that call returns BITLINEAR_ERR_UNSUPPORTED). */
+const char *bitlinear_grouped_kernel_algo(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype,
+                                          int algo);
 
 /*
  * Backward pass under the straight-through estimator (the pages quote the

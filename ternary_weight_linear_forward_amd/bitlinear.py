@@ -96,6 +96,8 @@ _SIGNATURES = {
     "bitlinear_forward_grouped_workspace_bytes": ([_JOBS, _INT, _INT, _INT], _I64),
     "bitlinear_forward_grouped": ([_JOBS, _INT, _INT, _INT, _INT, _P, _I64, _P], _INT),
     "bitlinear_grouped_kernel": ([_JOBS, _INT, _INT, _INT], ctypes.c_char_p),
+    "bitlinear_forward_grouped_algo": ([_JOBS, _INT, _INT, _INT, _INT, _INT, _P, _I64, _P], _INT),
+    "bitlinear_grouped_kernel_algo": ([_JOBS, _INT, _INT, _INT, _INT], ctypes.c_char_p),
     "bitlinear_forward_ex": (
         [_P, _INT, _P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P, _INT, _I64, _P, _I64, _P, _P, _I64, _INT, _P],
         _INT),
@@ -246,6 +248,16 @@ def bitlinear_forward_grouped(jobs, njobs: int, layout: int, x_dtype: int, y_dty
 
 def bitlinear_grouped_kernel(jobs, njobs: int, layout: int, x_dtype: int):
     r = _lib.bitlinear_grouped_kernel(jobs, njobs, layout, x_dtype)
+    return None if r is None else r.decode()
+
+
+def bitlinear_forward_grouped_algo(jobs, njobs: int, layout: int, x_dtype: int, y_dtype: int, algo: int, ws,
+                                   ws_bytes: int, stream) -> int:
+    return _lib.bitlinear_forward_grouped_algo(jobs, njobs, layout, x_dtype, y_dtype, algo, ws, ws_bytes, stream)
+
+
+def bitlinear_grouped_kernel_algo(jobs, njobs: int, layout: int, x_dtype: int, algo: int):
+    r = _lib.bitlinear_grouped_kernel_algo(jobs, njobs, layout, x_dtype, algo)
     return None if r is None else r.decode()
 
 
@@ -435,10 +447,11 @@ def grouped_jobs(specs, y_dtype=None, outs=None):
     return job_array(jobs), ys
 
 
-def forward_grouped(specs, layout: int = LAYOUT_I2, y_dtype=None, ws=None, outs=None, stream=None):
-    """Several BitLinear forwards in one grouped call (bitlinear_forward_grouped).
-    specs as grouped_jobs; every X must have the same dtype.  Returns the list
-    of outputs Y [M x N]."""
+def forward_grouped(specs, layout: int = LAYOUT_I2, y_dtype=None, ws=None, outs=None, stream=None,
+                    algo: int = ALGO_AUTO):
+    """Several BitLinear forwards in one grouped call
+    (bitlinear_forward_grouped_algo).  specs as grouped_jobs; every X must have
+    the same dtype.  Returns the list of outputs Y [M x N]."""
     torch = _torch()
     if not specs:
         return []
@@ -450,8 +463,9 @@ def forward_grouped(specs, layout: int = LAYOUT_I2, y_dtype=None, ws=None, outs=
         raise BitlinearError(ERR_INVALID_ARG, "forward_grouped")
     if nws > 0 and (ws is None or ws.numel() < nws):
         ws = torch.empty(nws, dtype=torch.uint8, device=specs[0][2].device)
-    _check(bitlinear_forward_grouped(arr, n, layout, xdt, _dtype_code(ys[0]), _ptr(ws) if nws > 0 else None, nws,
-                                     _stream(stream)), "bitlinear_forward_grouped")
+    _check(bitlinear_forward_grouped_algo(arr, n, layout, xdt, _dtype_code(ys[0]), algo,
+                                          _ptr(ws) if nws > 0 else None, nws, _stream(stream)),
+           "bitlinear_forward_grouped_algo")
     return ys
 
 

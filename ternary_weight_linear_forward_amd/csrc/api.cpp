@@ -20,11 +20,13 @@ static __device__ __align__(256) uint8_t scratch[BITLINEAR_NOALLOC_SCRATCH_BYTES
 namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40; // keeps per-exponent sums of |W| below 2^64
-// Largest M the add/subtract GEMV takes when the kernel is chosen
-// automatically.  Measured on MI355X the matrix-core GEMV is faster at every M
-// (the vector ALU reaches 4 int8 MACs per lane-cycle, the matrix core takes the
-// MACs off it), so automatic dispatch never picks add/subtract; it stays
-// available as BITLINEAR_ALGO_GEMV_ADDSUB.
+// Largest M the single-layer add/subtract GEMV (k_gemv_addsub) takes when the
+// kernel is chosen automatically.  Measured on MI355X the single-layer
+// matrix-core GEMVs are faster at every M (the vector ALU reaches 4 int8 MACs
+// per lane-cycle, the matrix core takes the MACs off it), so automatic
+// dispatch of bitlinear_forward never picks it; it stays available as
+// BITLINEAR_ALGO_GEMV_ADDSUB.  (The grouped forward's add/sub products are
+// another kernel: group_algo.)
 constexpr int64_t kAddSubMaxM = 0;
 // Fewest GEMM workgroup tiles for which the GEMM beats the matrix-core GEMV
 // (token groups of 16) when there are more than 16 tokens: with fewer tiles
@@ -627,26 +629,70 @@ int64_t bitlinear_forward_grouped_workspace_bytes(const bitlinear_job_t *jobs, i
     return grouped_ws_bytes(jobs, njobs, layout, x_dtype, group_inputs(jobs, njobs, layout));
 }
 
-const char *bitlinear_grouped_kernel(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype)
+namespace {
+// The grouped product's algorithm for these (valid) jobs: 1 = the vector-ALU
+// products, 0 = the matrix cores, -1 = the algorithm cannot take them.  The
+// vector-ALU products take i2 jobs of one token each; the grouped launch
+// quantises their inputs itself, and under BITLINEAR_ALGO_GEMV_ADDSUB the
+// jobs it leaves out (rows too long) run on the single-layer add/sub GEMV.
+// AUTO takes them for every group of one-token i2 jobs: measured on ten
+// layer sets of the 3B and 70B models at one token, they were 0.7-5 % faster
+// than the matrix cores in eight (3B q/k/v/o/gate/up 10.08 against 10.61 us,
+// the 70B q/k/v/o/gate/up 32.1 against 32.7 us) and level (within 1.5 %) in
+// the two that mix the 3B down projection (three k-steps per wave) with
+// layers of one (the whole 3B set: 11.38 against 11.34 us).
+int group_algo(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype, const GroupInputs &g, int algo)
+{
+    if (algo == BITLINEAR_ALGO_GEMV_MFMA) return 0;
+    if (algo != BITLINEAR_ALGO_AUTO && algo != BITLINEAR_ALGO_GEMV_ADDSUB) return -1;
+    const bool forced = algo == BITLINEAR_ALGO_GEMV_ADDSUB;
+    bool ok = layout == BITLINEAR_LAYOUT_I2 && (g.n == 0 || group_fused(jobs, njobs, x_dtype, g));
+    for (int j = 0; j < njobs && ok; ++j) {
+        if (!forced && g.in_of[j] < 0) continue; // AUTO: plain forwards choose for themselves
+        if (jobs[j].M != 1) ok = false;
+    }
+    if (forced) return ok ? 1 : -1;
+    return ok && g.n > 0 ? 1 : 0;
+}
+} // namespace
+
+const char *bitlinear_grouped_kernel_algo(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype, int algo)
 {
     thread_local char name[96];
     if (bitlinear_forward_grouped_workspace_bytes(jobs, njobs, layout, x_dtype) < 0) return nullptr;
     const GroupInputs g = group_inputs(jobs, njobs, layout);
     if (g.n == 0) return nullptr;
-    bl::group_gemv_kernel_name(layout, group_fused(jobs, njobs, x_dtype, g) ? x_dtype : BITLINEAR_I8, name,
+    const int a = group_algo(jobs, njobs, layout, x_dtype, g, algo);
+    if (a < 0) return nullptr;
+    bl::group_gemv_kernel_name(layout, group_fused(jobs, njobs, x_dtype, g) ? x_dtype : BITLINEAR_I8, a == 1, name,
                                sizeof name);
     return name;
+}
+
+const char *bitlinear_grouped_kernel(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype)
+{
+    return bitlinear_grouped_kernel_algo(jobs, njobs, layout, x_dtype, BITLINEAR_ALGO_AUTO);
 }
 
 int bitlinear_forward_grouped(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype, int y_dtype,
                               void *ws, int64_t ws_bytes, void *stream)
 {
+    return bitlinear_forward_grouped_algo(jobs, njobs, layout, x_dtype, y_dtype, BITLINEAR_ALGO_AUTO, ws, ws_bytes,
+                                          stream);
+}
+
+int bitlinear_forward_grouped_algo(const bitlinear_job_t *jobs, int njobs, int layout, int x_dtype, int y_dtype,
+                                   int algo, void *ws, int64_t ws_bytes, void *stream)
+{
     if (!group_args_ok(jobs, njobs, layout, x_dtype, y_dtype)) return BITLINEAR_ERR_INVALID_ARG;
+    if (algo < BITLINEAR_ALGO_AUTO || algo > BITLINEAR_ALGO_GEMM_MFMA) return BITLINEAR_ERR_INVALID_ARG;
     for (int j = 0; j < njobs; ++j) {
         const int st = check_job(jobs, njobs, j, layout, x_dtype, y_dtype);
         if (st != BITLINEAR_OK) return st;
     }
     const GroupInputs g = group_inputs(jobs, njobs, layout);
+    const int galgo = group_algo(jobs, njobs, layout, x_dtype, g, algo);
+    if (galgo < 0) return BITLINEAR_ERR_UNSUPPORTED;
     const int64_t need = grouped_ws_bytes(jobs, njobs, layout, x_dtype, g);
     if (need > 0 && (!ws || ws_bytes < need)) return BITLINEAR_ERR_WORKSPACE;
     if (need > 0 && !aligned16(ws)) return BITLINEAR_ERR_INVALID_ARG;
@@ -684,7 +730,8 @@ int bitlinear_forward_grouped(const bitlinear_job_t *jobs, int njobs, int layout
             const int nwg = j < ga.njobs ? ((ga.job[j].N + 15) / 16 + bl::GROUP_STAGE_TILES - 1) / bl::GROUP_STAGE_TILES : 0;
             if (part.njobs > 0 && (j == ga.njobs || need_wgs + nwg > bl::GROUP_MAX_WGS / 2 - 16)) {
                 const bl::GroupPlan plan = bl::group_plan(part, layout);
-                if (bl::launch_group_gemv(part, plan, layout, gemv_x, st) != hipSuccess) return BITLINEAR_ERR_LAUNCH;
+                if (bl::launch_group_gemv(part, plan, layout, gemv_x, st, galgo == 1) != hipSuccess)
+                    return BITLINEAR_ERR_LAUNCH;
                 part.njobs = 0;
                 need_wgs = 0;
             }
@@ -702,7 +749,9 @@ int bitlinear_forward_grouped(const bitlinear_job_t *jobs, int njobs, int layout
         const bitlinear_job_t &J = jobs[j];
         const int64_t nb = bitlinear_forward_workspace_bytes(J.M, J.N, J.K, layout, x_dtype);
         const int s = forward_impl(J.P, layout, J.gamma, J.M, J.N, J.K, J.X, x_dtype, J.ldx, nullptr, J.Y, y_dtype,
-                                   J.ldy, nb > 0 ? rest : nullptr, nb, nullptr, 0, nullptr, BITLINEAR_ALGO_AUTO,
+                                   J.ldy, nb > 0 ? rest : nullptr, nb, nullptr, 0, nullptr,
+                                   algo == BITLINEAR_ALGO_GEMV_ADDSUB ? BITLINEAR_ALGO_GEMV_ADDSUB
+                                                                      : BITLINEAR_ALGO_AUTO,
                                    stream);
         if (s != BITLINEAR_OK) return s;
     }

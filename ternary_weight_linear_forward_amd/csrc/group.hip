@@ -127,6 +127,28 @@ __device__ __forceinline__ void i2_scaled_step(const uint4 &w, const v4i (&at)[4
     acc.a16b = __builtin_amdgcn_mfma_i32_16x16x64_i8(at[3], b3, acc.a16b, 0, 0, 0);
 }
 
+// The same i2 k-step on the vector ALU for one token (the add/subtract form:
+// no multiplier sees a weight other than 0, 1, 2 or 3 times a power of two).
+// ab[d] holds the token's activations of the lane's k-block in the natural
+// operand layout (dword s of operand d = activations 16d + 4s .. 16d + 4s + 3),
+// the same in every lane of a row; field s of word d pairs with dword s of
+// operand d, one v_dot4 each, into accumulators of three scales as above.
+struct I2DotAcc {
+    int p1, p4, p16;
+};
+
+__device__ __forceinline__ void i2_dot_step(const uint4 &w, const v4i (&ab)[4], I2DotAcc &acc)
+{
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        acc.p1 = __builtin_amdgcn_sdot4(static_cast<int>(wd[d] & 0x03030303u), ab[d][0], acc.p1, false);
+        acc.p4 = __builtin_amdgcn_sdot4(static_cast<int>(wd[d] & 0x0c0c0c0cu), ab[d][1], acc.p4, false);
+        acc.p16 = __builtin_amdgcn_sdot4(static_cast<int>(wd[d] & 0x30303030u), ab[d][2], acc.p16, false);
+        acc.p16 = __builtin_amdgcn_sdot4(static_cast<int>((wd[d] >> 2) & 0x30303030u), ab[d][3], acc.p16, false);
+    }
+}
+
 // b3 k-step with the digit subtraction moved into the matrix cores.  The
 // fixed-point byte u of five digits (c_0 most significant) gives the levels
 // X_t = floor(u 3^t / 256) (t = 1..5; X_5 is the base-3 value itself) and
@@ -198,10 +220,11 @@ struct GroupLds {
 // across the waves, exactly as the quantiser) and returns beta of token
 // lane % 4 in every lane.  Every wave of the workgroup calls this once: it
 // holds one barrier.
-template <int LAYOUT, int SPW, int D, int XDT>
+template <int LAYOUT, int SPW, int D, int XDT, bool ADDSUB>
 __device__ __forceinline__ float group_job_tiles(const GroupJob &J, int KS, int wave, int lane, int nj, int lb,
                                                  int ntiles, const GroupLds &L)
 {
+    static_assert(!ADDSUB || LAYOUT == LAYOUT_I2, "the vector-ALU product is written for i2");
     using S = StepShape<LAYOUT>;
     constexpr int NMF = S::NMF;
     const int M = J.M, KB = J.KB, nsteps = J.nsteps;
@@ -294,8 +317,18 @@ __device__ __forceinline__ float group_job_tiles(const GroupJob &J, int KS, int 
             for (int d = 1; d < D; ++d) load_tile(d, b[d]);
         });
     }
-    // i2: the operands transposed for the masked codes (i2_scaled_step)
-    if constexpr (LAYOUT == LAYOUT_I2) {
+    if constexpr (ADDSUB) {
+        // one token (M = 1): every lane of row g takes lane (0, g)'s operands,
+        // token 0's activations of k-block g (DPP row_newbcast:0, lane 0 of
+        // each 16-lane row to the whole row)
+#pragma unroll
+        for (int j = 0; j < SPW; ++j)
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) a[j][d][w] = __builtin_amdgcn_update_dpp(0, a[j][d][w], 0x150, 0xf, 0xf, false);
+    } else if constexpr (LAYOUT == LAYOUT_I2) {
+        // i2: the operands transposed for the masked codes (i2_scaled_step)
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
             v4i t[4];
@@ -310,7 +343,16 @@ __device__ __forceinline__ float group_job_tiles(const GroupJob &J, int KS, int 
     if (nj == 0) return beta_lane;
 
     v4i sacc = {0, 0, 0, 0}; // sum_k q of the wave's k-steps (offset codes); b3: b3_level_fix
-    if constexpr (LAYOUT == LAYOUT_B3) {
+    int qsum = 0;             // add/sub: sum_k q of the lane's k-blocks
+    if constexpr (ADDSUB) {
+#pragma unroll
+        for (int j = 0; j < SPW; ++j)
+            if (j < nj)
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) qsum = __builtin_amdgcn_sdot4(a[j][d][w], 0x01010101, qsum, false);
+    } else if constexpr (LAYOUT == LAYOUT_B3) {
         sacc = b3_level_fix<SPW>(a, nj);
     } else {
 #pragma unroll
@@ -325,7 +367,20 @@ __device__ __forceinline__ float group_job_tiles(const GroupJob &J, int KS, int 
         constexpr int t = decltype(tc)::value;
         if (t >= ntiles) return false;
         v4i part;
-        if constexpr (LAYOUT == LAYOUT_I2) {
+        if constexpr (ADDSUB) {
+            I2DotAcc acc{0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < SPW; ++j) {
+                if (j >= nj) break;
+                i2_dot_step(b[t % D][j], a[j], acc);
+            }
+            // row i, k-block lane g: summed over the waves in sums[t][0][lane]
+            // (the four k-block lanes of a row are added at the store)
+            const int p = acc.p1 + (acc.p4 >> 2) + (acc.p16 >> 4) - qsum;
+            if constexpr (t + D < GROUP_STAGE_TILES) load_tile(t + D, b[t % D]);
+            __hip_atomic_fetch_add(&L.sums[t][0][lane], p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            return true;
+        } else if constexpr (LAYOUT == LAYOUT_I2) {
             I2ScaledAcc acc{{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
             for (int j = 0; j < SPW; ++j) {
@@ -364,14 +419,14 @@ __device__ __forceinline__ float group_job_tiles(const GroupJob &J, int KS, int 
 // rounding area and staged activations share the registers with the ring)
 constexpr int group_fq_max_spw(int layout) { return layout == LAYOUT_I2 ? 3 : 2; }
 
-template <int LAYOUT, int XDT>
-__global__ __launch_bounds__(1024) void k_group_gemv(const GroupGemvArgs args)
+// The grouped launch's workgroup: its job, the products (matrix cores, or the
+// vector ALU for ADDSUB), the rescale and the stores.  L.sums: the int32 sums
+// of the workgroup's tiles, [tile][token sub-row rr][lane] (lane (i, g) of
+// tile t: token 4g + rr, weight row i).
+template <int LAYOUT, int XDT, bool ADDSUB>
+__device__ __forceinline__ void group_gemv_body(const GroupGemvArgs &args, const GroupLds &L)
 {
-    // int32 sums of the workgroup's tiles: [tile][token sub-row rr][lane]
-    // (lane (i, g) of tile t: token 4g + rr, weight row i)
-    __shared__ int sums[GROUP_STAGE_TILES][4][64];
-    __shared__ float wmax[16][4];
-    extern __shared__ v4i qbuf_dyn[]; // quantiser inside: [waves][spw * units]
+    int (*const sums)[4][64] = L.sums;
 
     // this workgroup's job (one scalar load of the index table, then one
     // batch for the job's fields) and its index among the job's workgroups
@@ -400,12 +455,11 @@ __global__ __launch_bounds__(1024) void k_group_gemv(const GroupGemvArgs args)
             bt[rr] = J.beta[m < M ? m : M - 1];
         }
     }
-    const GroupLds L{sums, qbuf_dyn, wmax};
     float beta_lane = 0.0f;
     if (XDT != DT_I8 || nj > 0) {
-        if (spw <= 1) beta_lane = group_job_tiles<LAYOUT, 1, group_depth(LAYOUT, 1), XDT>(J, KS, wave, lane, nj, lb, ntiles, L);
-        else if (spw == 2) beta_lane = group_job_tiles<LAYOUT, 2, group_depth(LAYOUT, 2), XDT>(J, KS, wave, lane, nj, lb, ntiles, L);
-        else if (LAYOUT == LAYOUT_I2 && spw == 3) beta_lane = group_job_tiles<LAYOUT, LAYOUT == LAYOUT_I2 ? 3 : 2, group_depth(LAYOUT, 3), XDT>(J, KS, wave, lane, nj, lb, ntiles, L);
+        if (spw <= 1) beta_lane = group_job_tiles<LAYOUT, 1, group_depth(LAYOUT, 1), XDT, ADDSUB>(J, KS, wave, lane, nj, lb, ntiles, L);
+        else if (spw == 2) beta_lane = group_job_tiles<LAYOUT, 2, group_depth(LAYOUT, 2), XDT, ADDSUB>(J, KS, wave, lane, nj, lb, ntiles, L);
+        else if (LAYOUT == LAYOUT_I2 && spw == 3) beta_lane = group_job_tiles<LAYOUT, LAYOUT == LAYOUT_I2 ? 3 : 2, group_depth(LAYOUT, 3), XDT, ADDSUB>(J, KS, wave, lane, nj, lb, ntiles, L);
         else lds_barrier(); // (not reached: the plan keeps spw within the templates)
     } else {
         for (int e = threadIdx.x; e < ntiles * 4 * 64; e += blockDim.x) (&sums[0][0][0])[e] = 0;
@@ -423,12 +477,37 @@ __global__ __launch_bounds__(1024) void k_group_gemv(const GroupGemvArgs args)
     // rescale and store tile t (weight rows 16 (lb + t nwg) + i)
     for (int t = wave; t < ntiles; t += KS) {
         const int64_t n = static_cast<int64_t>(lb + t * J.nwg) * 16 + i;
+        if constexpr (ADDSUB) { // one token: row i's four k-block lanes
+            if (g == 0 && n < N)
+                store_out(J.Y, args.y_dtype, J.ldy, 0, n, sums[t][0][i] + sums[t][0][i + 16] + sums[t][0][i + 32] + sums[t][0][i + 48], sc[0]);
+            continue;
+        }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const int m = 4 * g + rr;
             if (m < M && n < N) store_out(J.Y, args.y_dtype, J.ldy, m, n, sums[t][rr][lane], sc[rr]);
         }
     }
+}
+
+template <int LAYOUT, int XDT>
+__global__ __launch_bounds__(1024) void k_group_gemv(const GroupGemvArgs args)
+{
+    __shared__ int sums[GROUP_STAGE_TILES][4][64];
+    __shared__ float wmax[16][4];
+    extern __shared__ v4i qbuf_dyn[]; // quantiser inside: [waves][spw * units]
+    group_gemv_body<LAYOUT, XDT, false>(args, GroupLds{sums, qbuf_dyn, wmax});
+}
+
+// The same launch with the i2 products on the vector ALU (i2_dot_step), for
+// jobs of one token each.
+template <int XDT>
+__global__ __launch_bounds__(1024) void k_group_gemv_addsub(const GroupGemvArgs args)
+{
+    __shared__ int sums[GROUP_STAGE_TILES][4][64];
+    __shared__ float wmax[16][4];
+    extern __shared__ v4i qbuf_dyn[];
+    group_gemv_body<LAYOUT_I2, XDT, true>(args, GroupLds{sums, qbuf_dyn, wmax});
 }
 
 int group_max_nsteps(int layout)
@@ -467,19 +546,44 @@ GroupPlan group_plan(GroupGemvArgs &args, int layout)
     const int spw = (max_steps + p.waves - 1) / p.waves;
     p.spw = spw <= 1 ? 1 : (spw <= 2 ? 2 : 3);
     (void)layout;
-    // one workgroup per CU in all, dealt by weight bytes; at least one per
-    // GROUP_STAGE_TILES tiles (the LDS staging of a workgroup's outputs) and
-    // at most one per tile
-    constexpr double kCUs = 256.0;
+    (void)total;
+    // One workgroup per CU in all (256), at least one per GROUP_STAGE_TILES
+    // tiles of a job (the LDS staging of a workgroup's outputs) and at most
+    // one per tile.  The launch lasts as long as its most loaded workgroup,
+    // so the workgroups are dealt one at a time to the job whose workgroups
+    // hold the most weight bytes each (ceil(tiles / n) tiles of KB k-blocks):
+    // that minimises the largest share.  (Shares proportional to the bytes
+    // leave whole tiles over in some workgroups: at the 3B layers the
+    // largest share was 1.14 times the mean, at the 70B q/k/v/o/gate/up 1.19
+    // times (k and v: 3 workgroups of 22 tiles); dealt this way 1.06 and
+    // 1.03 times.)
+    constexpr int kCUs = 256;
+    int nwg[GROUP_MAX_JOBS];
+    int sum = 0;
+    for (int j = 0; j < args.njobs; ++j) {
+        const int NT = (args.job[j].N + 15) / 16;
+        nwg[j] = (NT + GROUP_STAGE_TILES - 1) / GROUP_STAGE_TILES;
+        sum += nwg[j];
+    }
+    for (; sum < kCUs; ++sum) {
+        int best = -1;
+        int64_t best_bytes = 0;
+        for (int j = 0; j < args.njobs; ++j) {
+            const int NT = (args.job[j].N + 15) / 16;
+            if (nwg[j] >= NT) continue;
+            const int64_t b = static_cast<int64_t>((NT + nwg[j] - 1) / nwg[j]) * args.job[j].KB;
+            if (b > best_bytes) {
+                best_bytes = b;
+                best = j;
+            }
+        }
+        if (best < 0) break;
+        ++nwg[best];
+    }
     int wg = 0;
     for (int j = 0; j < args.njobs; ++j) {
         GroupJob &J = args.job[j];
-        const int NT = (J.N + 15) / 16;
-        int n = static_cast<int>(kCUs * NT * J.KB / total + 0.5);
-        const int min_n = (NT + GROUP_STAGE_TILES - 1) / GROUP_STAGE_TILES;
-        n = n < min_n ? min_n : n;
-        n = n > NT ? NT : n;
-        n = n < 1 ? 1 : n;
+        const int n = nwg[j];
         J.wg0 = wg;
         J.nwg = n;
         for (int b = wg; b < wg + n && b < GROUP_MAX_WGS; ++b) {
@@ -493,9 +597,9 @@ GroupPlan group_plan(GroupGemvArgs &args, int layout)
 }
 
 template <int LAYOUT, int XDT>
-static void launch_group_x(const GroupGemvArgs &args, const GroupPlan &plan, hipStream_t stream)
+static void launch_group_x(const GroupGemvArgs &args, const GroupPlan &plan, bool addsub, hipStream_t stream)
 {
-    auto *f = &k_group_gemv<LAYOUT, XDT>;
+    auto *f = addsub && LAYOUT == LAYOUT_I2 ? &k_group_gemv_addsub<XDT> : &k_group_gemv<LAYOUT, XDT>;
     // the rounding areas of the quantiser inside: waves x k-steps x 4 tokens
     // x the k-step's 16-value chunks, 16 bytes each
     const size_t lds = XDT == DT_I8 ? 0
@@ -508,26 +612,37 @@ static void launch_group_x(const GroupGemvArgs &args, const GroupPlan &plan, hip
 }
 
 template <int LAYOUT>
-static void launch_group_layout(const GroupGemvArgs &args, const GroupPlan &plan, int x_dtype, hipStream_t stream)
+static void launch_group_layout(const GroupGemvArgs &args, const GroupPlan &plan, int x_dtype, bool addsub,
+                                hipStream_t stream)
 {
-    if (x_dtype == DT_BF16) launch_group_x<LAYOUT, DT_BF16>(args, plan, stream);
-    else if (x_dtype == DT_F32) launch_group_x<LAYOUT, DT_F32>(args, plan, stream);
-    else launch_group_x<LAYOUT, DT_I8>(args, plan, stream);
+    if (x_dtype == DT_BF16) launch_group_x<LAYOUT, DT_BF16>(args, plan, addsub, stream);
+    else if (x_dtype == DT_F32) launch_group_x<LAYOUT, DT_F32>(args, plan, addsub, stream);
+    else launch_group_x<LAYOUT, DT_I8>(args, plan, addsub, stream);
+}
+
+bool group_addsub_ok(const GroupGemvArgs &args, int layout)
+{
+    if (layout != LAYOUT_I2) return false;
+    for (int j = 0; j < args.njobs; ++j)
+        if (args.job[j].M != 1) return false;
+    return true;
 }
 
 hipError_t launch_group_gemv(const GroupGemvArgs &args, const GroupPlan &plan, int layout, int x_dtype,
-                             hipStream_t stream)
+                             hipStream_t stream, bool addsub)
 {
     if (plan.wgs < 1 || plan.spw > 3 || (layout != LAYOUT_I2 && plan.spw > 2)) return hipErrorInvalidValue;
-    if (layout == LAYOUT_I2) launch_group_layout<LAYOUT_I2>(args, plan, x_dtype, stream);
-    else if (layout == LAYOUT_B3) launch_group_layout<LAYOUT_B3>(args, plan, x_dtype, stream);
-    else launch_group_layout<LAYOUT_B1>(args, plan, x_dtype, stream);
+    if (addsub && !group_addsub_ok(args, layout)) return hipErrorInvalidValue;
+    if (layout == LAYOUT_I2) launch_group_layout<LAYOUT_I2>(args, plan, x_dtype, addsub, stream);
+    else if (layout == LAYOUT_B3) launch_group_layout<LAYOUT_B3>(args, plan, x_dtype, false, stream);
+    else launch_group_layout<LAYOUT_B1>(args, plan, x_dtype, false, stream);
     return hipGetLastError();
 }
 
-void group_gemv_kernel_name(int layout, int x_dtype, char *buf, size_t n)
+void group_gemv_kernel_name(int layout, int x_dtype, bool addsub, char *buf, size_t n)
 {
-    snprintf(buf, n, "bl::k_group_gemv<%d, %d>", layout, x_dtype);
+    if (addsub) snprintf(buf, n, "bl::k_group_gemv_addsub<%d>", x_dtype);
+    else snprintf(buf, n, "bl::k_group_gemv<%d, %d>", layout, x_dtype);
 }
 
 } // namespace bl

@@ -98,9 +98,12 @@ GroupPlan group_plan(GroupGemvArgs &args, int layout);
 // x_dtype DT_I8: the jobs read Xt / beta (k_group_quant_tiled ran first);
 // DT_F32 / DT_BF16: every job has 1 to 4 tokens of 16-byte aligned rows X,
 // quantised inside.
+// addsub: the products on the vector ALU (k_group_gemv_addsub), for i2 jobs of
+// one token each (group_addsub_ok).
 hipError_t launch_group_gemv(const GroupGemvArgs &args, const GroupPlan &plan, int layout, int x_dtype,
-                             hipStream_t stream);
-void group_gemv_kernel_name(int layout, int x_dtype, char *buf, size_t n);
+                             hipStream_t stream, bool addsub = false);
+bool group_addsub_ok(const GroupGemvArgs &args, int layout);
+void group_gemv_kernel_name(int layout, int x_dtype, bool addsub, char *buf, size_t n);
 
 // Product + rescale on int8 activations Xq [M x K] (row stride ldq, 16-byte
 // aligned rows) with per-token beta.

@@ -422,8 +422,21 @@ def test_grouped_workspace_bytes():
 
 
 def test_grouped_kernel_name():
-    arr, n = _jobs(3)  # 1 token, aligned bf16 rows: the quantiser inside
+    arr, n = _jobs(3)  # 1 token, aligned bf16 rows: the quantiser inside, add/sub products
+    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) == "bl::k_group_gemv_addsub<1>"
+    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.F32) == "bl::k_group_gemv_addsub<0>"
+    arr, n = _jobs(3, {2: dict(K=12288, ldx=12288, X=C + 0x100000)})  # three k-steps per wave
+    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) == "bl::k_group_gemv_addsub<1>"
+    arr, n = _jobs(3, {2: dict(ldx=3201, X=C + 0x100000)})  # unaligned rows: quantiser launch, matrix cores
+    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) == "bl::k_group_gemv<0, 2>"
+    arr, n = _jobs(3, {1: dict(M=2)})  # two tokens: the matrix cores
     assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) == "bl::k_group_gemv<0, 1>"
+    arr, n = _jobs(3)
+    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_B3, bl.BF16) == "bl::k_group_gemv<1, 1>"
+    # one token with a row too long for the grouped launch: left to a plain
+    # forward, which does not decide the grouped launch's algorithm
+    arr, n = _jobs(3, {1: dict(K=65536, ldx=65536, X=C + 0x100000)})
+    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) == "bl::k_group_gemv_addsub<1>"
     arr, n = _jobs(2, {1: dict(K=8640, ldx=8640, X=C + 0x100000, M=16)})  # 16 tokens: quantiser launch first
     assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) == "bl::k_group_gemv<0, 2>"
     arr, n = _jobs(1, {0: dict(M=17)})
@@ -466,6 +479,42 @@ def test_grouped_rejects_bad_counts():
     assert gfw(arr, 0) == bl.ERR_INVALID_ARG
     assert gfw(arr, bl.MAX_GROUP + 1) == bl.ERR_INVALID_ARG
     assert gfw(None, 1) == bl.ERR_INVALID_ARG
+
+
+def test_grouped_algo_rejects_and_names():
+    """bitlinear_forward_grouped_algo: the vector-ALU products take only i2
+    jobs of one token each, all grouped and quantised inside; everything else
+    is refused before anything is enqueued (no launch here)."""
+    def call(arr, n, algo, **kw):
+        a = dict(layout=bl.LAYOUT_I2, x_dtype=bl.BF16, y_dtype=bl.F32, ws=E, ws_bytes=1 << 24, stream=None)
+        a.update(kw)
+        return bl.bitlinear_forward_grouped_algo(arr, n, a["layout"], a["x_dtype"], a["y_dtype"], algo, a["ws"],
+                                                 a["ws_bytes"], a["stream"])
+    names = bl.bitlinear_grouped_kernel_algo
+    arr, n = _jobs(3)
+    assert names(arr, n, bl.LAYOUT_I2, bl.BF16, bl.ALGO_GEMV_ADDSUB) == "bl::k_group_gemv_addsub<1>"
+    assert names(arr, n, bl.LAYOUT_I2, bl.F32, bl.ALGO_GEMV_ADDSUB) == "bl::k_group_gemv_addsub<0>"
+    assert names(arr, n, bl.LAYOUT_I2, bl.BF16, bl.ALGO_GEMV_MFMA) == "bl::k_group_gemv<0, 1>"
+    assert names(arr, n, bl.LAYOUT_I2, bl.BF16, bl.ALGO_AUTO) == bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2,
+                                                                                           bl.BF16)
+    assert names(arr, n, bl.LAYOUT_B3, bl.BF16, bl.ALGO_GEMV_ADDSUB) is None
+    assert names(arr, n, bl.LAYOUT_I2, bl.BF16, bl.ALGO_GEMM_MFMA) is None
+    assert call(arr, n, bl.ALGO_GEMV_ADDSUB, layout=bl.LAYOUT_B3) == bl.ERR_UNSUPPORTED
+    assert call(arr, n, bl.ALGO_GEMV_ADDSUB, layout=bl.LAYOUT_B1) == bl.ERR_UNSUPPORTED
+    assert call(arr, n, bl.ALGO_GEMM_MFMA) == bl.ERR_UNSUPPORTED
+    assert call(arr, n, 4) == bl.ERR_INVALID_ARG
+    assert call(arr, n, -1) == bl.ERR_INVALID_ARG
+    assert call(arr, n, bl.ALGO_GEMV_ADDSUB, y_dtype=bl.I8) == bl.ERR_INVALID_ARG  # argument checks first
+    for over in ({1: dict(M=2)},                        # two tokens
+                 {1: dict(M=20, X=C + 0x100000)},       # a job left to a plain forward
+                 {1: dict(ldx=3201, X=C + 0x100000)}):  # rows not 16-byte aligned: quantiser launch
+        arr, n = _jobs(3, over)
+        assert names(arr, n, bl.LAYOUT_I2, bl.BF16, bl.ALGO_GEMV_ADDSUB) is None, over
+        assert call(arr, n, bl.ALGO_GEMV_ADDSUB) == bl.ERR_UNSUPPORTED, over
+    # one token with a row too long for the grouped launch: that job runs on
+    # the single-layer add/sub GEMV, the others in the grouped launch
+    arr, n = _jobs(3, {1: dict(K=65536, ldx=65536, X=C + 0x100000)})
+    assert names(arr, n, bl.LAYOUT_I2, bl.BF16, bl.ALGO_GEMV_ADDSUB) == "bl::k_group_gemv_addsub<1>"
 
 
 def test_noalloc_rejects_before_any_device_call():

@@ -5,7 +5,8 @@ exact, fp32 / bf16 outputs bit-identical).  Covers the decode layer set of the
 3B model at 1, 4 and 16 tokens, inputs shared between jobs (q / k / v), mixed
 token counts, ragged shapes, every layout and input dtype, jobs the grouped
 launch leaves to a plain forward (more than 16 tokens, very long rows), tiny
-activation rows, and replay from a HIP graph."""
+activation rows, replay from a HIP graph, and the vector-ALU (add/subtract)
+products of bitlinear_forward_grouped_algo for one-token i2 jobs."""
 import numpy as np
 import pytest
 
@@ -29,8 +30,8 @@ class Case:
     """Jobs (M, N, K, input id) with seeded weights and inputs; jobs with the
     same input id share one X."""
 
-    def __init__(self, layout, shapes, xk="bf16", seed=0, tiny=False, pad=False):
-        self.layout, self.xk = layout, xk
+    def __init__(self, layout, shapes, xk="bf16", seed=0, tiny=False, pad=False, algo=bl.ALGO_AUTO):
+        self.layout, self.xk, self.algo = layout, xk, algo
         self.t, self.g, self.P, self.gd = [], [], [], []
         self.x_host, self.x_dev = {}, {}
         self.shapes = shapes
@@ -59,7 +60,8 @@ class Case:
 
     def kernel(self):
         xdt = bl.BF16 if self.xk == "bf16" else bl.F32
-        return bl.bitlinear_grouped_kernel(bl.grouped_jobs(self.specs())[0], len(self.shapes), LAYOUTS[self.layout], xdt)
+        return bl.bitlinear_grouped_kernel_algo(bl.grouped_jobs(self.specs())[0], len(self.shapes),
+                                                LAYOUTS[self.layout], xdt, self.algo)
 
     def specs(self):
         return [(self.P[j], self.gd[j], self.x_dev[xid], N, K) for j, (M, N, K, xid) in enumerate(self.shapes)]
@@ -71,7 +73,7 @@ class Case:
             refs.append(oracle.forward(self.t[j], self.g[j], synth.bf16_bits_to_f32(x) if x.dtype == np.uint16 else x))
         for yk in y_kinds:
             ydt = {"i32": torch.int32, "f32": torch.float32, "bf16": torch.bfloat16}[yk]
-            ys = bl.forward_grouped(self.specs(), LAYOUTS[self.layout], y_dtype=ydt)
+            ys = bl.forward_grouped(self.specs(), LAYOUTS[self.layout], y_dtype=ydt, algo=self.algo)
             for j, (y, ref) in enumerate(zip(ys, refs)):
                 y = to_host(y)
                 if yk == "i32":
@@ -91,7 +93,8 @@ def test_grouped_decode_3b_layer_set(M):
     c = Case("i2", decode_layers(M), seed=M)
     kname = bl.bitlinear_grouped_kernel(bl.grouped_jobs(c.specs())[0], 7, bl.LAYOUT_I2, bl.BF16)
     log("grouped decode 3b", M, kname)
-    assert kname.startswith("bl::k_group_gemv<")
+    assert kname == ("bl::k_group_gemv_addsub<1>" if M == 1 else "bl::k_group_gemv<0, 1>" if M == 4
+                     else "bl::k_group_gemv<0, 2>"), kname
     c.check()
 
 
@@ -196,3 +199,58 @@ def test_grouped_quantiser_inside(layout, xk):
     log("grouped, quantiser inside", layout, xk, kname)
     assert kname == f"bl::k_group_gemv<{LAYOUTS[layout]}, {bl.BF16 if xk == 'bf16' else bl.F32}>", kname
     c.check()
+
+
+@pytest.mark.parametrize("xk", ["bf16", "f32"])
+def test_grouped_addsub_decode_3b(xk):
+    """The 3B decode layer set at one token with the products on the vector
+    ALU: the same results as the oracle (and so as the matrix-core products)."""
+    c = Case("i2", decode_layers(1), xk=xk, seed=43, algo=bl.ALGO_GEMV_ADDSUB)
+    kname = c.kernel()
+    log("grouped add/sub decode 3b", xk, kname)
+    assert kname == f"bl::k_group_gemv_addsub<{bl.BF16 if xk == 'bf16' else bl.F32}>", kname
+    c.check()
+
+
+@pytest.mark.parametrize("xk", ["bf16", "f32"])
+def test_grouped_addsub_ragged_and_special_rows(xk):
+    """Ragged K and N, one to three k-steps per wave (K up to 12288), and a
+    zero, a tie and a tiny row, each job one token."""
+    shapes = [(1, 17, 64, 0), (1, 700, 1001, 1), (1, 1000, 77, 2), (1, 333, 3203, 3), (1, 8640, 3200, 4),
+              (1, 48, 8192, 5), (1, 130, 12288, 6), (1, 64, 256, 7), (1, 40, 640, 8), (1, 2000, 3200, 9)]
+    c = Case("i2", shapes, xk=xk, seed=47, pad=True, algo=bl.ALGO_GEMV_ADDSUB)
+    for xid, fill in ((7, "zero"), (8, "ties"), (9, "tiny")):
+        x = c.x_host[xid]
+        xf = (synth.bf16_bits_to_f32(x) if x.dtype == np.uint16 else x).copy()
+        if fill == "zero":
+            xf[:] = 0.0
+        elif fill == "ties":
+            xf[0, :] = 0.0
+            xf[0, :7] = [127.0, 2.5, -2.5, 0.5, -0.5, 1.5, -127.0]
+        else:
+            xf = (xf.astype(np.float64) * 2.0 ** -130).astype(np.float32)
+        c.x_host[xid] = synth.to_bf16_bits(xf) if x.dtype == np.uint16 else xf
+        c.x_dev[xid] = to_dev(c.x_host[xid])
+    log("grouped add/sub ragged", xk, c.kernel())
+    c.check()
+
+
+def test_grouped_addsub_matches_matrix_cores_bitwise():
+    """Both product algorithms of the grouped forward give the same bits."""
+    c = Case("i2", decode_layers(1), seed=53)
+    specs = c.specs()
+    for ydt in (torch.int32, torch.float32, torch.bfloat16):
+        a = bl.forward_grouped(specs, y_dtype=ydt, algo=bl.ALGO_GEMV_ADDSUB)
+        m = bl.forward_grouped(specs, y_dtype=ydt, algo=bl.ALGO_GEMV_MFMA)
+        for ya, ym in zip(a, m):
+            assert torch.equal(ya.view(torch.int16 if ydt == torch.bfloat16 else torch.int32),
+                               ym.view(torch.int16 if ydt == torch.bfloat16 else torch.int32))
+
+
+def test_grouped_addsub_with_a_long_row_left_to_the_plain_gemv():
+    """A one-token job whose row is too long for the grouped launch (112
+    k-steps) runs on the single-layer add/sub GEMV beside the grouped ones."""
+    shapes = [(1, 3200, 3200, 0), (1, 1024, 28672, 1), (1, 8640, 3200, 0)]
+    c = Case("i2", shapes, seed=59, algo=bl.ALGO_GEMV_ADDSUB)
+    log("grouped add/sub with a plain job", c.kernel())
+    c.check(("i32", "f32"))
