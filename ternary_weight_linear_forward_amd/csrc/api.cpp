@@ -467,11 +467,15 @@ int bitlinear_forward_ex(const uint8_t *P, int layout, const float *gamma, int64
 namespace {
 
 // Whether a job runs inside the grouped launch (else as its own forward).
+// The grouped kernel reads a job's packed weights through one buffer range
+// with 32-bit byte offsets (and 2^31 as its out-of-range offset), so the
+// job's packed bytes must stay below 2^31.
 bool group_eligible(const bitlinear_job_t &j, int layout)
 {
     const int64_t kblk = layout == BITLINEAR_LAYOUT_I2 ? 64 : (layout == BITLINEAR_LAYOUT_B3 ? 80 : 128);
     const int64_t nsteps = ((j.K + kblk - 1) / kblk + 3) / 4;
-    return j.M <= 16 && nsteps <= bl::group_max_nsteps(layout) && j.N <= (int64_t(1) << 30);
+    return j.M <= 16 && nsteps <= bl::group_max_nsteps(layout) && j.N <= (int64_t(1) << 30) &&
+           bitlinear_packed_bytes(j.N, j.K, layout) <= INT32_MAX;
 }
 
 // The distinct inputs of the grouped jobs: jobs with the same X, M, K and ldx

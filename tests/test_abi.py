@@ -560,3 +560,20 @@ def test_forward_chain_rejects_and_parts():
     assert f(**{**ok, "pmax_out": D + 64}) == bl.ERR_INVALID_ARG   # overlaps Y
     assert f(**{**ok, "pmax_out": F_ + 16}) == bl.ERR_INVALID_ARG   # overlaps pmax_in
     assert f(**{**ok, "pmax_out": F_ + 0x100002}) == bl.ERR_INVALID_ARG  # misaligned
+
+
+def test_grouped_leaves_out_jobs_beyond_32_bit_offsets():
+    """The grouped launch addresses a job's packed weights with 32-bit byte
+    offsets: a job of 2^31 packed bytes or more runs as its own forward (the
+    single-layer kernels address whole tiles with 64-bit pointers)."""
+    big = dict(N=1 << 27, K=64, ldx=64, ldy=1 << 27)  # 2^27 rows x 16 bytes = 2^31 bytes
+    assert bl.bitlinear_packed_bytes(1 << 27, 64, bl.LAYOUT_I2) == 1 << 31
+    arr, n = _jobs(1, {0: big})
+    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) is None
+    # rows are packed in whole 16-row tiles: 2^27 - 16 rows are 2^31 - 256 bytes, grouped
+    assert bl.bitlinear_packed_bytes((1 << 27) - 1, 64, bl.LAYOUT_I2) == 1 << 31
+    arr, n = _jobs(1, {0: dict(big, N=(1 << 27) - 16, ldy=(1 << 27) - 16)})
+    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_I2, bl.BF16) == "bl::k_group_gemv_addsub<1>"
+    # b3: 2^31 / 16 rows of one 80-weight block
+    arr, n = _jobs(1, {0: dict(big, K=80, ldx=80)})
+    assert bl.bitlinear_grouped_kernel(arr, n, bl.LAYOUT_B3, bl.BF16) is None
