@@ -22,7 +22,9 @@ events on the launch stream.
 'roofline' reports the kernel with the most time per step, timed alone (a HIP
 graph of back-to-back launches rotating over every weight copy, between HIP
 events on the launch stream); 'prefill' the 3B prefill GEMM (M = 2048) the
-same way; 'cpu_baseline' the CPU oracle on a bounded sample of the same work.
+same way, and its per-token activation quantiser alone against HBM
+('prefill.quantiser'); 'cpu_baseline' the CPU oracle on a bounded sample of
+the same work.
 
 --workload stack_3b_26 times one token step (batch 16) through 26 decoder
 layers of the 3B model's BitLinears (104 dependent forwards, all weights
@@ -630,6 +632,8 @@ def run_prefill(ctx, args):
                  "timing": "HIP events on the launch stream around a graph of back-to-back GEMMs over every weight "
                            "copy (activations quantised beforehand)"})
     log(f"prefill: {step_ms:.4f} ms/step, GEMM {json.dumps(roof)}")
+    quant = time_prefill_quantiser(ctx, jobs, M)
+    log(f"prefill quantiser: {json.dumps(quant)}")
     return {
         "workload": wl.name,
         "metric": "effective ternary TOPS of the prefill step (quantiser + GEMM + rescale per layer)",
@@ -640,8 +644,47 @@ def run_prefill(ctx, args):
         "config": {"M": M, "layers": {j["L"]["layer"].name: [j["L"]["layer"].N, j["L"]["layer"].K] for j in jobs},
                    "activations": "Student-t(4) bf16", "layout": "i2", "weight_copies": ncopies},
         "roofline": roof,
+        "quantiser": quant,
         "cpu_baseline": cpu_baseline(wl, wl.batches, max(args.cpu_seconds / 2, 3.0), ctx.layout, rows=64),
     }
+
+
+def time_prefill_quantiser(ctx, jobs, M):
+    """The per-token activation quantiser of each prefill forward, timed alone
+    against HBM: bf16 rows in, int8 rows (K rounded up to 16) and beta out.
+    A graph of back-to-back launches rotates over input and output copies of
+    >= ROTATE_BYTES in all, so that neither L2 nor the Infinity Cache holds
+    them between uses."""
+    torch, bl = ctx.torch, ctx.bl
+    d = {"ms": 0.0, "bytes": 0, "launches": 0, "calls": []}
+    for j in jobs:
+        K = j["L"]["layer"].K
+        ldq = (K + 15) // 16 * 16
+        nbytes = M * K * 2 + M * ldq + 4 * M
+        nc = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        xs = [j["x"]] + [j["x"].clone() for _ in range(nc - 1)]
+        outs = [(torch.empty((M, ldq), dtype=torch.int8, device=ctx.dev),
+                 torch.empty(M, dtype=torch.float32, device=ctx.dev)) for _ in range(nc)]
+
+        def q(i, xs=xs, outs=outs, K=K, ldq=ldq):
+            x, (xq, beta) = xs[i % len(xs)], outs[i % len(outs)]
+            st = bl.bitlinear_quantize_act(x.data_ptr(), bl.BF16, M, K, x.stride(0), xq.data_ptr(), ldq,
+                                           beta.data_ptr(), ctx.stream.cuda_stream)
+            if st:
+                raise bl.BitlinearError(st, "bitlinear_quantize_act (prefill)")
+
+        ms = time_launches(ctx, q, nc)
+        d["ms"] += ms
+        d["bytes"] += nbytes
+        d["launches"] += 1
+        d["calls"].append(f"{j['L']['layer'].name}@M{M}:{ms * 1e3:.2f}us")
+        del xs, outs
+    roof = roofline("hbm", d)
+    roof.update({"avg_launch_us": round(d["ms"] / d["launches"] * 1e3, 3), "launches_per_step": d["launches"],
+                 "calls": d["calls"], "algorithmic_bytes_per_launch": d["bytes"] // d["launches"],
+                 "timing": "HIP events on the launch stream around a graph of back-to-back launches over input "
+                           "and output copies of >= 2 GiB"})
+    return roof
 
 
 FP32_MFMA_PEAK_TFLOPS = 157.3

@@ -170,26 +170,21 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void k_quant_act_rows(const void *
     const float b = wave_max_nonneg(amax);
     const TokenQuant s = token_quant(b);
     int8_t *qrow = Xq + m * ldq;
+    // every |x| <= b, the row's own maximum: the bounded rounding applies
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
         const int64_t vi = lane + 64 * static_cast<int64_t>(j);
         if (vi >= nvec) continue;
         const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
         if constexpr (XDT == DT_F32) {
-            uint32_t w = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w |= quant_one(__uint_as_float(u[e]), s) << (8 * e);
-            reinterpret_cast<uint32_t *>(qrow)[vi] = w;
+            reinterpret_cast<uint32_t *>(qrow)[vi] = quant4_bounded(__uint_as_float(u[0]), __uint_as_float(u[1]),
+                                                                    __uint_as_float(u[2]), __uint_as_float(u[3]), s);
         } else {
-            uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                w0 |= quant_one(__uint_as_float(u[e] << 16), s) << (16 * e);
-                w0 |= quant_one(__uint_as_float(u[e] & 0xffff0000u), s) << (16 * e + 8);
-                w1 |= quant_one(__uint_as_float(u[e + 2] << 16), s) << (16 * e);
-                w1 |= quant_one(__uint_as_float(u[e + 2] & 0xffff0000u), s) << (16 * e + 8);
-            }
-            reinterpret_cast<uint2 *>(qrow)[vi] = make_uint2(w0, w1);
+            auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+            auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
+            reinterpret_cast<uint2 *>(qrow)[vi] =
+                make_uint2(quant4_bounded(lo(u[0]), hi(u[0]), lo(u[1]), hi(u[1]), s),
+                           quant4_bounded(lo(u[2]), hi(u[2]), lo(u[3]), hi(u[3]), s));
         }
     }
     // zero the row padding [K, ldq)

@@ -90,6 +90,23 @@ __device__ __forceinline__ TokenQuant token_quant(float beta)
 // product.  |result| <= 127 (1 + 2^-24)^2 < 127.5 for |x| <= beta.
 __device__ __forceinline__ float token_scaled(float x, TokenQuant t) { return (x * t.pre) * t.s; }
 
+// Four activations of a row whose absmax is beta (every |x| <= beta) to int8,
+// packed in order: the values quant_one gives.  Every |RN32(x pre s)| < 127.5,
+// so the clamp never acts; adding 1.5 * 2^23 (its own correctly rounded add:
+// the build does not contract) rounds to an integer with ties to even, and the
+// low byte of the sum is the int8 in two's complement.  Three v_perm_b32
+// gather the four bytes: about 3.75 instructions per value against 8.
+__device__ __forceinline__ uint32_t quant4_bounded(float x0, float x1, float x2, float x3, TokenQuant t)
+{
+    const uint32_t b0 = __float_as_uint(token_scaled(x0, t) + 12582912.0f);
+    const uint32_t b1 = __float_as_uint(token_scaled(x1, t) + 12582912.0f);
+    const uint32_t b2 = __float_as_uint(token_scaled(x2, t) + 12582912.0f);
+    const uint32_t b3 = __float_as_uint(token_scaled(x3, t) + 12582912.0f);
+    const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u); // q0, q1 in bytes 0, 1
+    const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u); // q2, q3
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
 // One activation to int8: clamp(rint(x * pre * s), -127, 127), ties to even,
 // as the low byte of the result.
 __device__ __forceinline__ uint32_t quant_one(float x, TokenQuant t)
