@@ -112,6 +112,17 @@ def act_cases():
     xb[7] = 0x8000                                   # bf16 -0.0 row
     xb[9, 3] = 0x7f7f                                # bf16 largest finite
     yield "bf16_edges_64x1000", xb
+    # prefill-sized row counts that leave the last workgroup partly empty,
+    # with edge rows among the last ones
+    yield "bf16_1501x3200_ragged", synth.activations_student_t_bf16(1501, 3200, seed=23)
+    x = synth.activations_f32(2053, 1000, seed=24)
+    for r in (0, 2049, 2052):
+        x[r] = 0.0
+        x[r, :7] = [127.0, 2.5, -2.5, 0.5, -0.5, 1.5, -127.0]
+    x[2050] = (x[2050] * 1e-40).astype(np.float32)  # subnormal row
+    x[2051] = np.float32(-0.0)
+    x[5] = (x[5] * 1e-38).astype(np.float32)        # beta below 127 / FLT_MAX
+    yield "f32_edges_2053x1000", x
 
 
 @pytest.mark.parametrize("name,x", list(act_cases()), ids=[c[0] for c in act_cases()])
