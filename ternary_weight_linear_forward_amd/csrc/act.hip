@@ -316,8 +316,17 @@ __device__ __forceinline__ void quant_tiled_row(const void *__restrict__ X, int6
         const int64_t k0 = 16 * p;
         const int64_t st = k0 / step_k, r = k0 % step_k, g = r / kblk, d = (r % kblk) / 16;
         uint32_t w[4] = {0, 0, 0, 0};
+        if (pmax == nullptr) {
+            // beta is this row's own maximum, so every |x| <= beta: the
+            // bounded rounding gives the same bytes
 #pragma unroll
-        for (int e = 0; e < 16; ++e) w[e / 4] |= quant_one(v[j][e], s) << (8 * (e % 4));
+            for (int q = 0; q < 4; ++q)
+                w[q] = quant4_bounded(v[j][4 * q], v[j][4 * q + 1], v[j][4 * q + 2], v[j][4 * q + 3], s);
+        } else {
+            // beta from the producer's maxima: the clamped form
+#pragma unroll
+            for (int e = 0; e < 16; ++e) w[e / 4] |= quant_one(v[j][e], s) << (8 * (e % 4));
+        }
         const int64_t off = (((tg * nsteps + st) * nmf + d) * 64 + g * 16 + i) * 16;
         *reinterpret_cast<uint4 *>(Xt + off) = make_uint4(w[0], w[1], w[2], w[3]);
     }
